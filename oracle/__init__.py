@@ -1,0 +1,22 @@
+"""Plain fp64 CPU oracle of the E2Former-V2 node-centric attention layer.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import, call, link or execute anything under oracle/.
+The product path (atomistic_attention_amd, its HIP library) never does, and the
+oracle imports nothing from the product path: the two share no code.
+
+Parity status per function (what pins it to something other than itself is in
+tests/test_oracle_*.py):
+  so3.real_sh / real_sh_legendre  pinned: scipy complex harmonics, closed forms
+  so3.cg_complex                  pinned: sympy, unitarity
+  so3.coupling_tensor             pinned: equivariance, dot/cross closed forms,
+                                  sparsity rule of the explainer section 2.2
+  so3.wigner_d                    pinned: D^1 = P R P^T, orthogonal, det 1, homomorphism
+  so3.eaas_couple                 pinned: Proposition 4.3 (equals the full CG product)
+  layer.neighbors                 pinned: scipy cKDTree (sets and K-nearest)
+  layer.rbf_bias                  pinned: closed-form values of Gaussians and envelope
+  layer.attention                 pinned: torch scaled_dot_product_attention (l_max = 0),
+                                  one-neighbour and equal-logit special cases
+  layer.layer_forward             pinned: rotation equivariance to 1e-10
+"""
+from . import so3, layer  # noqa: F401
