@@ -1,0 +1,347 @@
+// Fused streaming neighbour attention with the target coupling in its epilogue.
+//
+// E2Former-V2 explainer, section 3.1 (node-centric message passing: the
+// message m_i = sum_j alpha_ij h'_j is formed on the fly, then coupled with the
+// target's own encoding) and section 3.2 (Algorithm 1: online softmax with a
+// running maximum and normaliser, each key/value row read once, accumulation
+// on chip, one target per independent work item, padded neighbours skipped).
+// The distance bias -- distance, Gaussian expansion and cosine envelope
+// computed in the kernel and never written out -- follows the FlashSchNet
+// page, section 2.1; target-owned rows with no atomics follow its section 2.3.
+//
+// Mapping (one 64-lane wave per target atom i; H heads of 8 channels):
+//   * lane = u * 2H + b * H + h: head h, channel half b (channels 8h + 4b .. +4 of
+//     every (l, m) component, so a lane keeps n_comp * 4 fp32 accumulators) and
+//     neighbour slot u of PS = 32 / H slots streamed side by side;
+//   * neighbours are taken 16 at a time; slot u streams S = H / 2 consecutive
+//     pairs of the chunk with its own running max / normaliser / accumulators;
+//   * the distance bias of the 16 pairs for every head is one small product
+//     phi[16 pairs x R] . W_rbf[R x 16 heads] on the matrix cores
+//     (v_mfma_f32_16x16x4_f32, fp32): lane l evaluates phi_k(d_p) for pair
+//     p = l % 16 and k = l / 16 + 4 kk, i.e. every Gaussian exactly once, and the
+//     product lands in the lanes (or, for 16 heads, the lane pair) that need it;
+//   * q . k is a 4-channel partial per lane plus one swap with the other half;
+//   * per chunk: indices come from registers prefetched one chunk ahead, every
+//     key row and half the value rows are requested at once, the bias math runs
+//     while they are in flight, the second half of the value rows is requested
+//     as soon as the first half is consumed;
+//   * at the end the PS partial softmaxes are merged by a butterfly that halves
+//     the channel set at each step (reduce-scatter), leaving every lane whole
+//     channels: the target EAAS coupling then runs lane-locally and the lane
+//     writes its channels of hhat.
+// Value rows are read as 8-byte (fp16) or 16-byte (fp32) pieces; the 2H lanes of
+// a slot cover one contiguous component row of the neighbour.  A 16-bit h'_j row
+// carries one power-of-two scale (in pos4[j].w), folded into the softmax weight
+// of the pair, so each element costs one mixed-precision FMA.
+#include "e2v2_internal.h"
+
+namespace e2v2 {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <bool HB> struct HpRow;
+template <> struct HpRow<true> {     // scaled fp16: 4 channels in one 8-byte load
+    uint2 v;
+    __device__ __forceinline__ void load(const void *base, size_t elem)
+    {
+        v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(base) + elem);
+    }
+    __device__ __forceinline__ float get(int c) const
+    {
+        const uint32_t w = (c >> 1) == 0 ? v.x : v.y;
+        const uint16_t b = (c & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xffffu);
+        return (float)__builtin_bit_cast(_Float16, b);
+    }
+};
+template <> struct HpRow<false> {    // fp32: 4 channels in one 16-byte load
+    float4 a;
+    __device__ __forceinline__ void load(const void *base, size_t elem)
+    {
+        a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + elem);
+    }
+    __device__ __forceinline__ float get(int c) const
+    {
+        return c == 0 ? a.x : c == 1 ? a.y : c == 2 ? a.z : a.w;
+    }
+};
+
+template <int N> struct Log2;
+template <> struct Log2<1> { static constexpr int v = 0; };
+template <> struct Log2<2> { static constexpr int v = 1; };
+template <> struct Log2<4> { static constexpr int v = 2; };
+template <> struct Log2<8> { static constexpr int v = 3; };
+
+__device__ __forceinline__ float pick4(const floatx4 &v, int r)
+{
+    return r == 0 ? v[0] : r == 1 ? v[1] : r == 2 ? v[2] : v[3];
+}
+
+template <int L, bool HB, int H>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_kernel(const AttnArgs A, const EaasCoef tab)
+{
+    constexpr int NC = n_comp(L);
+    constexpr int C = 8 * H;
+    constexpr int PS = 32 / H;          // neighbour slots per wave
+    constexpr int S = H / 2;            // pairs per slot per 16-pair chunk
+    constexpr int P = path_count(L);
+    constexpr int ND = n_dmat(L);
+    constexpr int NB = Log2<PS>::v;
+    constexpr float LOG2E = 1.4426950408889634f;
+    // Value rows are fetched in NPH phases of SP steps, each phase sized to about
+    // 72 registers (one 8- or 16-byte piece per component and step) when a step's
+    // piece is small, else to one step.
+    constexpr int RPR = HB ? 2 : 4;
+    constexpr int BUDGET = NC * RPR <= 18 ? 72 : 40;
+    constexpr int SPF = BUDGET / (NC * RPR) > 0 ? BUDGET / (NC * RPR) : 1;
+    constexpr int SP = SPF >= 8 && S >= 8 ? 8 : SPF >= 4 && S >= 4 ? 4 : SPF >= 2 && S >= 2 ? 2 : 1;
+    constexpr int NPH = S / SP;
+
+    const int lane = threadIdx.x & 63;
+    const int i = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+    const int n = A.n;
+    const int h = lane % H, b = (lane / H) & 1, u = lane / (2 * H);
+    const int kq = lane >> 4, pm = lane & 15;
+    const int R = A.R;
+    const int KK = (R + 3) >> 2;
+    const int cb = 8 * h + 4 * b;       // first channel of this lane
+
+    // B operand of the bias product, W_rbf[k][head] zero-padded to 64 x 16, in LDS.
+    __shared__ float sW[64 * 16];
+    for (int e = threadIdx.x; e < 64 * 16; e += 256) {
+        const int k = e >> 4, hh = (e & 15) % H;
+        sW[e] = (k < R) ? A.w_rbf[k * H + hh] : 0.f;
+    }
+    __syncthreads();
+    if (i >= n) return;                 // whole wave: i is wave-uniform
+
+    const float4 pi4 = A.pos4[i];
+    const float4 qv = *reinterpret_cast<const float4 *>(A.q + (size_t)i * C + cb);
+    const float qscale = LOG2E * 0.35355339059327373f;   // log2(e) / sqrt(8)
+    const int start = __builtin_amdgcn_readfirstlane(A.nbr_start[i]);
+    const int len = __builtin_amdgcn_readfirstlane(A.nbr_len[i]);
+    const float inv_delta = (float)(R - 1) / A.cutoff;
+    const float cos_scale = 0.5f / A.cutoff;             // cos(pi d / rc) = cos(2 pi * d / (2 rc))
+    const float gexp = -0.5f * LOG2E;
+
+    float mu = -1e30f, z = 0.f;
+    float acc[NC][4];
+#pragma unroll
+    for (int e = 0; e < NC; ++e)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[e][c] = 0.f;
+
+    // Prologue: pair pm of the first chunk (index and padded position).
+    int jp = -1;
+    float4 pj = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (pm < len) jp = A.nbr_idx[start + pm];
+    if (jp >= 0 && jp < n) pj = A.pos4[jp];
+
+    for (int c0 = 0; c0 < len; c0 += 16) {
+        // ---- (a) this lane's S neighbours of the chunk and their row scales
+        int js[S];
+        float scl[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int p = u * S + s;
+            const int j = __shfl(jp, p, 64);
+            js[s] = (j >= 0 && j < n) ? j : -1;
+            scl[s] = HB ? __shfl(pj.w, p, 64) : 1.f;
+        }
+        // ---- (b) issue every key row and the first phase of value rows
+        float4 kv[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            kv[s] = *reinterpret_cast<const float4 *>(A.k + (size_t)(js[s] >= 0 ? js[s] : i) * C + cb);
+        HpRow<HB> hv[SP][NC];
+#pragma unroll
+        for (int s = 0; s < SP; ++s) {
+            const size_t rowe = (size_t)(js[s] >= 0 ? js[s] : i) * NC * C + cb;
+#pragma unroll
+            for (int e = 0; e < NC; ++e) hv[s][e].load(A.hp, rowe + (size_t)e * C);
+        }
+        // ---- (c) prefetch the next chunk's index for pair pm
+        int jn = -1;
+        if (c0 + 16 + pm < len) jn = A.nbr_idx[start + c0 + 16 + pm];
+        // ---- (d) pair pm: distance, Gaussians x envelope, bias product on the matrix cores
+        const bool vp = (jp >= 0) && (jp < n);
+        const float dx = pj.x - pi4.x, dy = pj.y - pi4.y, dz = pj.z - pi4.z;
+        const float d = vp ? sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;
+        const float fc = vp ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
+        const float t0 = d * inv_delta - (float)kq;      // (d - mu_k) / Delta for k = kq
+        const float *wrow = sW + kq * 16 + pm;
+        floatx4 bias = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            if (kk < KK) {
+                const float tk = t0 - 4.0f * (float)kk;
+                const float phi = fc * __builtin_amdgcn_exp2f(gexp * tk * tk);
+                bias = __builtin_amdgcn_mfma_f32_16x16x4f32(phi, wrow[64 * kk], bias, 0, 0, 0);
+            }
+        }
+        // bias[r] holds pair 4 (lane / 16) + r for head (lane % 16) % H.
+        float bs[S];
+        if constexpr (H == 16) {            // pairs 8u .. 8u+7: half b holds 4b .. 4b+3, the partner the rest
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float other = __shfl_xor(bias[r], 16, 64);
+                bs[r] = b ? other : bias[r];
+                bs[4 + r] = b ? bias[r] : other;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < S; ++s) bs[s] = pick4(bias, ((u * S) & 3) + s);
+        }
+        // ---- (e) logits (4-channel partial + the other half) and the online-softmax update
+        float sl[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            float qk = qv.x * kv[s].x;
+            qk = fmaf(qv.y, kv[s].y, qk);
+            qk = fmaf(qv.z, kv[s].z, qk);
+            qk = fmaf(qv.w, kv[s].w, qk);
+            qk += __shfl_xor(qk, H, 64);
+            sl[s] = js[s] >= 0 ? fmaf(qk, qscale, bs[s] * LOG2E) : -INFINITY;
+        }
+        float mx = sl[0];
+#pragma unroll
+        for (int s = 1; s < S; ++s) mx = fmaxf(mx, sl[s]);
+        const float mun = fmaxf(mu, mx);
+        const float corr = __builtin_amdgcn_exp2f(mu - mun);
+        float ps[S];
+        float psum = 0.f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            ps[s] = __builtin_amdgcn_exp2f(sl[s] - mun);
+            psum += ps[s];
+            ps[s] *= scl[s];                   // fold the row scale into the weight
+        }
+        z = fmaf(z, corr, psum);
+        mu = mun;
+        // ---- (f) rescale, then accumulate phase by phase; the next chunk's position
+        //          is requested with the last phase
+#pragma unroll
+        for (int e = 0; e < NC; ++e)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[e][c] *= corr;
+        float4 pjn = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph) {
+            if (ph > 0) {
+                __builtin_amdgcn_sched_barrier(0);     // this phase reuses the previous phase's registers
+#pragma unroll
+                for (int s = 0; s < SP; ++s) {
+                    const int st = ph * SP + s;
+                    const size_t rowe = (size_t)(js[st] >= 0 ? js[st] : i) * NC * C + cb;
+#pragma unroll
+                    for (int e = 0; e < NC; ++e) hv[s][e].load(A.hp, rowe + (size_t)e * C);
+                }
+            }
+            if (ph == NPH - 1 && jn >= 0 && jn < n) pjn = A.pos4[jn];
+#pragma unroll
+            for (int e = 0; e < NC; ++e)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    float a = acc[e][c];
+#pragma unroll
+                    for (int s = 0; s < SP; ++s) a = fmaf(ps[ph * SP + s], hv[s][e].get(c), a);
+                    acc[e][c] = a;
+                }
+        }
+        pj = pjn;
+        jp = jn;
+    }
+
+    // ---- merge the PS partial softmaxes (butterfly over the slot bits of the lane)
+    int off = 0;
+#pragma unroll
+    for (int st = 0; st < NB; ++st) {
+        const int bit = NB - 1 - st;
+        const int mask = (2 * H) << bit;
+        const float mo = __shfl_xor(mu, mask, 64);
+        const float mun = fmaxf(mu, mo);
+        const float corr = __builtin_amdgcn_exp2f(mu - mun);
+        mu = mun;
+        z *= corr;
+        z += __shfl_xor(z, mask, 64);
+        const bool upper = ((u >> bit) & 1) != 0;
+        if (st < 2) {                       // 4 -> 2 -> 1 channels
+            const int half = 2 >> st;
+#pragma unroll
+            for (int e = 0; e < NC; ++e)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    if (c < half) {
+                        const float lo = acc[e][c] * corr, hi = acc[e][c + half] * corr;
+                        const float keep = upper ? hi : lo;
+                        const float send = upper ? lo : hi;
+                        acc[e][c] = keep + __shfl_xor(send, mask, 64);
+                    }
+                }
+            off += upper ? half : 0;
+        } else {                            // one channel left: plain sum
+#pragma unroll
+            for (int e = 0; e < NC; ++e) {
+                const float v = acc[e][0] * corr;
+                acc[e][0] = v + __shfl_xor(v, mask, 64);
+            }
+        }
+    }
+    constexpr int NCH = (NB >= 2) ? 1 : (4 >> NB);
+    const bool writer = (NB <= 2) || ((u & 1) == 0);
+    const float invz = z > 0.f ? 1.f / z : 0.f;
+
+    // ---- target coupling (EAAS with the target's own rotation) and store
+    const float *Di = A.dmat + (size_t)i * (ND > 0 ? ND : 1);
+    const bool dir = (pi4.x != 0.f) || (pi4.y != 0.f) || (pi4.z != 0.f);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int ch = cb + off + c;
+        float mv[NC], yv[NC], w[P];
+#pragma unroll
+        for (int e = 0; e < NC; ++e) mv[e] = acc[e][c] * invz;
+        if (writer && A.m_tap) {
+#pragma unroll
+            for (int e = 0; e < NC; ++e) A.m_tap[((size_t)i * NC + e) * C + ch] = mv[e];
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) w[p] = A.w_tgt[p * C + ch];
+        eaas_channel<L>(Di, mv, yv, w, tab, dir);
+        if (writer) {
+#pragma unroll
+            for (int e = 0; e < NC; ++e) A.hhat[((size_t)i * NC + e) * C + ch] = yv[e];
+        }
+    }
+}
+
+template <int L, bool HB>
+static hipError_t launch_attn_lh(const AttnArgs &a, hipStream_t stream)
+{
+    dim3 grid((unsigned)((a.n + 3) / 4)), block(256);
+    const EaasCoef &tab = eaas_table(L);
+    switch (a.H) {
+    case 4: attn_kernel<L, HB, 4><<<grid, block, 0, stream>>>(a, tab); break;
+    case 8: attn_kernel<L, HB, 8><<<grid, block, 0, stream>>>(a, tab); break;
+    case 16: attn_kernel<L, HB, 16><<<grid, block, 0, stream>>>(a, tab); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(int L, int hp_bf16, const AttnArgs &a, hipStream_t stream)
+{
+    if (a.n <= 0) return hipSuccess;
+    switch (L * 2 + (hp_bf16 ? 1 : 0)) {
+    case 0: return launch_attn_lh<0, false>(a, stream);
+    case 1: return launch_attn_lh<0, true>(a, stream);
+    case 2: return launch_attn_lh<1, false>(a, stream);
+    case 3: return launch_attn_lh<1, true>(a, stream);
+    case 4: return launch_attn_lh<2, false>(a, stream);
+    case 5: return launch_attn_lh<2, true>(a, stream);
+    case 6: return launch_attn_lh<3, false>(a, stream);
+    case 7: return launch_attn_lh<3, true>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace e2v2

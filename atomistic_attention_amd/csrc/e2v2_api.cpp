@@ -1,0 +1,523 @@
+// Host side of the e2v2 C ABI: argument validation, workspace layout, kernel
+// launches and the constant tables the kernels take by value.
+//
+// Tables (built once per process):
+//  * EAAS coefficients.  In the frame whose z axis is the position vector the
+//    encoding Y^{l_f}(z) is sqrt(2 l_f + 1) on m_f = 0 and zero elsewhere
+//    (E2Former-V2 explainer, section 2.1), so path (l_i, l_f, l_o) reduces to
+//    out_{m_o} = sqrt(2 l_f + 1) T[m_i, 0, m_o] x~_{m_i} with m_i = +-m_o
+//    (section 2.2).  T is the real-basis Clebsch-Gordan tensor: complex
+//    Condon-Shortley coefficients (Racah's closed formula) conjugated into the
+//    real basis, real part for even l_i + l_f + l_o, imaginary part for odd.
+//  * Wigner-D sampling: 2l+1 fixed directions X per l in {2, 3} and the inverse
+//    of Y^l(X), so a kernel gets D^l(R) = Y^l(R X) Y^l(X)^{-1} from a handful of
+//    harmonic evaluations.  The directions are picked from a Fibonacci sphere
+//    to keep Y^l(X) well conditioned.
+#include <algorithm>
+#include <cmath>
+#include <complex>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/e2v2.h"
+#include "e2v2_internal.h"
+
+namespace e2v2 {
+namespace {
+
+// ---------------------------------------------------------------- Clebsch-Gordan
+double fact(int k)
+{
+    double r = 1.0;
+    for (int i = 2; i <= k; ++i) r *= i;
+    return r;
+}
+
+// <j1 m1; j2 m2 | J M>, Racah's formula (integer momenta, small enough for doubles).
+double cg(int j1, int m1, int j2, int m2, int J, int M)
+{
+    if (m1 + m2 != M || std::abs(m1) > j1 || std::abs(m2) > j2 || std::abs(M) > J) return 0.0;
+    if (J < std::abs(j1 - j2) || J > j1 + j2) return 0.0;
+    const double pre = std::sqrt((2.0 * J + 1.0) * fact(J + j1 - j2) * fact(J - j1 + j2) * fact(j1 + j2 - J) /
+                                 fact(j1 + j2 + J + 1) * fact(J + M) * fact(J - M) * fact(j1 - m1) * fact(j1 + m1) *
+                                 fact(j2 - m2) * fact(j2 + m2));
+    double sum = 0.0;
+    for (int k = 0; k <= j1 + j2 + J; ++k) {
+        const int a[6] = {k, j1 + j2 - J - k, j1 - m1 - k, j2 + m2 - k, J - j2 + m1 + k, J - j1 - m2 + k};
+        bool ok = true;
+        for (int v : a) ok = ok && v >= 0;
+        if (!ok) continue;
+        double den = 1.0;
+        for (int v : a) den *= fact(v);
+        sum += ((k & 1) ? -1.0 : 1.0) / den;
+    }
+    return pre * sum;
+}
+
+// Complex -> real basis: Y_real[m] = sum_mu U(m, mu) Y_complex[mu].
+std::complex<double> U(int l, int m, int mu)
+{
+    const double r2 = 1.0 / std::sqrt(2.0);
+    const double sgn = (std::abs(m) & 1) ? -1.0 : 1.0;
+    if (m == 0) return mu == 0 ? 1.0 : 0.0;
+    if (m > 0) {
+        if (mu == -m) return r2;
+        if (mu == m) return sgn * r2;
+        return 0.0;
+    }
+    if (mu == m) return std::complex<double>(0.0, r2);
+    if (mu == -m) return std::complex<double>(0.0, -sgn * r2);
+    (void)l;
+    return 0.0;
+}
+
+// sqrt(2 lf + 1) * T[m_i, m_f = 0, m_o] in the real basis.
+double eaas_entry(int li, int lf, int lo, int mi, int mo)
+{
+    std::complex<double> acc = 0.0;
+    for (int mu = -std::min(li, lo); mu <= std::min(li, lo); ++mu)   // m_f = 0 forces mu_i = mu_o
+        acc += std::conj(U(li, mi, mu)) * U(lo, mo, mu) * cg(li, mu, lf, 0, lo, mu);
+    const double v = ((li + lf + lo) & 1) ? acc.imag() : acc.real();
+    return std::sqrt(2.0 * lf + 1.0) * v;
+}
+
+// ---------------------------------------------------------------- Wigner-D sampling
+void sh_block(int l, const double *x, double *o)
+{
+    if (l == 2) sh_l2(x[0], x[1], x[2], o);
+    else sh_l3(x[0], x[1], x[2], o);
+}
+
+// Gauss-Jordan inverse with partial pivoting; returns false if singular.
+bool invert(int k, const double *A, double *Ainv)
+{
+    double M[7][14];
+    for (int r = 0; r < k; ++r)
+        for (int c = 0; c < 2 * k; ++c) M[r][c] = c < k ? A[r * k + c] : (c - k == r ? 1.0 : 0.0);
+    for (int c = 0; c < k; ++c) {
+        int piv = c;
+        for (int r = c + 1; r < k; ++r)
+            if (std::fabs(M[r][c]) > std::fabs(M[piv][c])) piv = r;
+        if (std::fabs(M[piv][c]) < 1e-12) return false;
+        for (int cc = 0; cc < 2 * k; ++cc) std::swap(M[c][cc], M[piv][cc]);
+        const double d = M[c][c];
+        for (int cc = 0; cc < 2 * k; ++cc) M[c][cc] /= d;
+        for (int r = 0; r < k; ++r)
+            if (r != c) {
+                const double f = M[r][c];
+                for (int cc = 0; cc < 2 * k; ++cc) M[r][cc] -= f * M[c][cc];
+            }
+    }
+    for (int r = 0; r < k; ++r)
+        for (int c = 0; c < k; ++c) Ainv[r * k + c] = M[r][c + k];
+    return true;
+}
+
+// Pick 2l+1 directions with a well-conditioned Y^l(X) (Frobenius condition number).
+void pick_samples(int l, double (*xs)[3], double *inv)
+{
+    const int k = 2 * l + 1;
+    const int npts = 48;
+    double pts[48][3];
+    const double ga = M_PI * (3.0 - std::sqrt(5.0));
+    for (int i = 0; i < npts; ++i) {
+        const double z = 1.0 - (i + 0.5) * 2.0 / npts, r = std::sqrt(1.0 - z * z);
+        pts[i][0] = r * std::cos(ga * i);
+        pts[i][1] = r * std::sin(ga * i);
+        pts[i][2] = z;
+    }
+    uint64_t s = 0x9E3779B97F4A7C15ull;
+    double best = 1e300;
+    int sel[7], bsel[7] = {0};
+    for (int trial = 0; trial < 4000; ++trial) {
+        for (int a = 0; a < k; ++a) {
+            bool dup;
+            do {
+                s ^= s << 13; s ^= s >> 7; s ^= s << 17;
+                sel[a] = (int)(s % npts);
+                dup = false;
+                for (int b = 0; b < a; ++b) dup = dup || sel[b] == sel[a];
+            } while (dup);
+        }
+        double A[49], Ai[49];
+        for (int c = 0; c < k; ++c) {       // A[m][s] = Y^l_m(x_s)
+            double o[7];
+            sh_block(l, pts[sel[c]], o);
+            for (int m = 0; m < k; ++m) A[m * k + c] = o[m];
+        }
+        if (!invert(k, A, Ai)) continue;
+        double na = 0, ni = 0;
+        for (int e = 0; e < k * k; ++e) { na += A[e] * A[e]; ni += Ai[e] * Ai[e]; }
+        const double cond = std::sqrt(na * ni);
+        if (cond < best) {
+            best = cond;
+            std::copy(sel, sel + k, bsel);
+            std::copy(Ai, Ai + k * k, inv);
+        }
+    }
+    for (int a = 0; a < k; ++a)
+        for (int d = 0; d < 3; ++d) xs[a][d] = pts[bsel[a]][d];
+}
+
+Tables g_tables;
+std::once_flag g_once;
+
+void build_tables()
+{
+    std::memset(&g_tables, 0, sizeof(g_tables));
+    int p = 0;
+    for (int lo = 0; lo <= kMaxL; ++lo)
+        for (int li = 0; li <= kMaxL; ++li)
+            for (int lf = 0; lf <= kMaxL; ++lf) {
+                if (!is_path(li, lf, lo)) continue;
+                const bool odd = (li + lf + lo) & 1;
+                for (int mo = -lo; mo <= lo; ++mo) {
+                    const int mi = odd ? -mo : mo;
+                    if (std::abs(mi) > li) continue;
+                    g_tables.eaas.c[p][mo + lo] = (float)eaas_entry(li, lf, lo, mi, mo);
+                }
+                ++p;
+            }
+    pick_samples(2, g_tables.ds.x2, &g_tables.ds.inv2[0][0]);
+    pick_samples(3, g_tables.ds.x3, &g_tables.ds.inv3[0][0]);
+}
+
+// Path indices depend on lmax (l_o is the outer loop), so the table for a
+// smaller lmax is the lmax = 3 table re-indexed.
+void eaas_for_lmax(int lmax, EaasCoef &out)
+{
+    std::memset(&out, 0, sizeof(out));
+    const Tables &t = host_tables();
+    for (int lo = 0; lo <= lmax; ++lo)
+        for (int li = 0; li <= lmax; ++li)
+            for (int lf = 0; lf <= lmax; ++lf) {
+                if (!is_path(li, lf, lo)) continue;
+                const int src = path_index(kMaxL, li, lf, lo), dst = path_index(lmax, li, lf, lo);
+                for (int e = 0; e < 2 * kMaxL + 1; ++e) out.c[dst][e] = t.eaas.c[src][e];
+            }
+}
+
+EaasCoef g_by_lmax[kMaxL + 1];
+std::once_flag g_once_l;
+
+}  // namespace
+
+const Tables &host_tables()
+{
+    std::call_once(g_once, build_tables);
+    return g_tables;
+}
+
+const EaasCoef &eaas_table(int lmax)
+{
+    std::call_once(g_once_l, [] {
+        for (int l = 0; l <= kMaxL; ++l) eaas_for_lmax(l, g_by_lmax[l]);
+    });
+    return g_by_lmax[lmax];
+}
+
+}  // namespace e2v2
+
+// ============================================================================
+// C ABI
+// ============================================================================
+using namespace e2v2;
+
+namespace {
+thread_local std::string t_err;
+
+e2v2_status fail(e2v2_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+e2v2_status fail(e2v2_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    t_err = buf;
+    return s;
+}
+e2v2_status hip_fail(hipError_t e, const char *where)
+{
+    return fail(E2V2_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Attention workspace layout.
+struct AttnWs {
+    size_t q, k, v, hp, dmat, pos4, hhat, total;
+};
+AttnWs attn_ws(const e2v2_layer_desc &d, int n)
+{
+    const size_t N = (size_t)n, C = (size_t)d.channels, NC = (size_t)n_comp(d.lmax);
+    const size_t s = d.storage == E2V2_BF16 ? 2 : 4;
+    const size_t nd = (size_t)(n_dmat(d.lmax) > 0 ? n_dmat(d.lmax) : 1);
+    AttnWs w{};
+    size_t o = 0;
+    w.q = o; o += al256(N * C * 4);
+    w.k = o; o += al256(N * C * 4);
+    w.v = o; o += al256(N * NC * C * 4);
+    w.hp = o; o += al256(N * NC * C * s);
+    w.dmat = o; o += al256(N * nd * 4);
+    w.pos4 = o; o += al256(N * 16);
+    w.hhat = o; o += al256(N * NC * C * 4);
+    w.total = o + 256;   // slack for re-aligning an unaligned base
+    return w;
+}
+
+e2v2_status check_desc(const e2v2_layer_desc *d)
+{
+    if (!d) return fail(E2V2_ERR_ARG, "desc is NULL");
+    if (d->lmax < 0 || d->lmax > kMaxL) return fail(E2V2_ERR_ARG, "lmax %d outside 0..3", d->lmax);
+    if (d->heads <= 0 || d->channels <= 0 || d->channels % d->heads != 0)
+        return fail(E2V2_ERR_ARG, "channels %d not a positive multiple of heads %d", d->channels, d->heads);
+    if (d->channels / d->heads != 8)
+        return fail(E2V2_ERR_UNSUPPORTED, "channels per head must be 8 (got %d)", d->channels / d->heads);
+    if (d->heads != 4 && d->heads != 8 && d->heads != 16)
+        return fail(E2V2_ERR_UNSUPPORTED, "heads must be 4, 8 or 16 (got %d)", d->heads);
+    if (d->n_rbf < 2 || d->n_rbf > 64) return fail(E2V2_ERR_ARG, "n_rbf %d outside 2..64", d->n_rbf);
+    if (!(d->cutoff > 0.f) || !std::isfinite(d->cutoff)) return fail(E2V2_ERR_ARG, "cutoff must be finite and > 0");
+    if (d->storage != E2V2_FP32 && d->storage != E2V2_BF16) return fail(E2V2_ERR_ARG, "unknown storage dtype %d", d->storage);
+    return E2V2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+const char *e2v2_status_string(e2v2_status s)
+{
+    switch (s) {
+    case E2V2_OK: return "ok";
+    case E2V2_ERR_ARG: return "invalid argument";
+    case E2V2_ERR_CAPACITY: return "insufficient neighbour capacity";
+    case E2V2_ERR_UNSUPPORTED: return "unsupported shape";
+    case E2V2_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *e2v2_last_error(void) { return t_err.c_str(); }
+
+int32_t e2v2_num_paths(int32_t lmax)
+{
+    if (lmax < 0 || lmax > kMaxL) return -1;
+    return path_count(lmax);
+}
+
+e2v2_status e2v2_path_table(int32_t lmax, int32_t *t)
+{
+    if (lmax < 0 || lmax > kMaxL) return fail(E2V2_ERR_ARG, "lmax %d outside 0..3", lmax);
+    if (!t) return fail(E2V2_ERR_ARG, "table pointer is NULL");
+    int p = 0;
+    for (int lo = 0; lo <= lmax; ++lo)
+        for (int li = 0; li <= lmax; ++li)
+            for (int lf = 0; lf <= lmax; ++lf)
+                if (is_path(li, lf, lo)) {
+                    t[3 * p] = li; t[3 * p + 1] = lf; t[3 * p + 2] = lo;
+                    ++p;
+                }
+    return E2V2_OK;
+}
+
+e2v2_status e2v2_eaas_coefficients(int32_t lmax, float *coef)
+{
+    if (lmax < 0 || lmax > kMaxL) return fail(E2V2_ERR_ARG, "lmax %d outside 0..3", lmax);
+    if (!coef) return fail(E2V2_ERR_ARG, "coef is NULL");
+    const EaasCoef &t = eaas_table(lmax);
+    for (int p = 0; p < path_count(lmax); ++p)
+        for (int e = 0; e < 2 * kMaxL + 1; ++e) coef[p * 7 + e] = t.c[p][e];
+    return E2V2_OK;
+}
+
+e2v2_status e2v2_alignment_wigner(int32_t lmax, const double *r, double *d)
+{
+    if (lmax < 0 || lmax > kMaxL) return fail(E2V2_ERR_ARG, "lmax %d outside 0..3", lmax);
+    if (!r || !d) return fail(E2V2_ERR_ARG, "NULL pointer");
+    double D[n_dmat(kMaxL)];
+    wigner_blocks<kMaxL>(r[0], r[1], r[2], host_tables().ds, D);
+    for (int e = 0; e < n_dmat(lmax); ++e) d[e] = D[e];
+    return E2V2_OK;
+}
+
+size_t e2v2_build_neighbors_workspace_bytes(int32_t n, int32_t max_neighbors)
+{
+    if (n < 0) return 0;
+    return neighbors_ws_bytes(n, max_neighbors) + 256;
+}
+
+e2v2_status e2v2_build_neighbors(const float *pos, int32_t n, float cutoff, int32_t K, int32_t *nbr_start,
+                                 int32_t *nbr_len, int32_t *nbr_idx, int64_t capacity, int64_t *nnz_host,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (n < 0 || n == INT32_MAX) return fail(E2V2_ERR_ARG, "n = %d out of range", n);
+    if (!(cutoff > 0.f) || !std::isfinite(cutoff)) return fail(E2V2_ERR_ARG, "cutoff must be finite and > 0");
+    if (K < 0 || K > 4096) return fail(E2V2_ERR_ARG, "max_neighbors %d outside 0..4096", K);
+    if (K == 0 && !nnz_host) return fail(E2V2_ERR_ARG, "nnz_host is required for CSR output");
+    if (capacity < 0) return fail(E2V2_ERR_ARG, "negative capacity");
+    if (K > 0 && capacity < (int64_t)n * K)
+        return fail(E2V2_ERR_ARG, "capacity %lld < n*K = %lld", (long long)capacity, (long long)n * K);
+    if (K > 0 && (int64_t)n * K >= INT32_MAX) return fail(E2V2_ERR_ARG, "n*K exceeds int32 offsets");
+    if (n == 0) {
+        if (nnz_host) *nnz_host = 0;
+        return E2V2_OK;
+    }
+    if (!pos || !nbr_start || !nbr_len || !nbr_idx || !workspace) return fail(E2V2_ERR_ARG, "NULL device pointer");
+    if (!aligned16(pos) || !aligned16(nbr_start) || !aligned16(nbr_len) || !aligned16(nbr_idx))
+        return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    if (workspace_bytes < e2v2_build_neighbors_workspace_bytes(n, K))
+        return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, e2v2_build_neighbors_workspace_bytes(n, K));
+    void *ws = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+    hipError_t e = launch_neighbors_count(pos, n, cutoff, K, ws, workspace_bytes, nbr_len, stream);
+    if (e != hipSuccess) return hip_fail(e, "neighbour grid");
+    if (K == 0) {
+        int64_t *nnz_dev = neighbors_nnz_slot(ws, n);
+        e = launch_neighbors_scan(n, ws, nbr_start, nbr_len, nnz_dev, stream);
+        if (e != hipSuccess) return hip_fail(e, "neighbour scan");
+        int64_t nnz = 0;
+        e = hipMemcpyAsync(&nnz, nnz_dev, sizeof nnz, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "reading nnz");
+        *nnz_host = nnz;
+        if (nnz > capacity)
+            return fail(E2V2_ERR_CAPACITY, "need %lld neighbour slots, capacity %lld", (long long)nnz, (long long)capacity);
+        if (nnz >= INT32_MAX) return fail(E2V2_ERR_CAPACITY, "nnz %lld exceeds int32 offsets", (long long)nnz);
+    }
+    e = launch_neighbors_fill(pos, n, cutoff, K, ws, nbr_start, nbr_len, nbr_idx, stream);
+    if (e != hipSuccess) return hip_fail(e, "neighbour fill");
+    if (K > 0 && nnz_host) {
+        // Sum of the row lengths, read back (the documented synchronising option).
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "synchronise");
+        int32_t *lens = new int32_t[(size_t)n];
+        e = hipMemcpy(lens, nbr_len, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost);
+        int64_t s = 0;
+        for (int i = 0; i < n; ++i) s += lens[i];
+        delete[] lens;
+        if (e != hipSuccess) return hip_fail(e, "reading nbr_len");
+        *nnz_host = s;
+    }
+    return E2V2_OK;
+}
+
+e2v2_status e2v2_eaas_couple(const float *pos, const void *x, e2v2_dtype x_dtype, const float *path_w, int32_t n,
+                             int32_t lmax, int32_t channels, void *y, e2v2_dtype y_dtype, hipStream_t stream)
+{
+    if (lmax < 0 || lmax > kMaxL) return fail(E2V2_ERR_ARG, "lmax %d outside 0..3", lmax);
+    if (channels <= 0 || channels > 256 || channels % 8 != 0)
+        return fail(E2V2_ERR_ARG, "channels %d must be a multiple of 8 in 8..256", channels);
+    if ((x_dtype != E2V2_FP32 && x_dtype != E2V2_BF16) || (y_dtype != E2V2_FP32 && y_dtype != E2V2_BF16))
+        return fail(E2V2_ERR_ARG, "unknown dtype");
+    if (n < 0) return fail(E2V2_ERR_ARG, "n < 0");
+    if (n == 0) return E2V2_OK;
+    if (!pos || !x || !path_w || !y) return fail(E2V2_ERR_ARG, "NULL device pointer");
+    if (!aligned16(pos) || !aligned16(x) || !aligned16(path_w) || !aligned16(y))
+        return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    hipError_t e = launch_eaas(lmax, pos, x, x_dtype == E2V2_BF16, path_w, n, channels, y, y_dtype == E2V2_BF16 ? 1 : 0,
+                               nullptr, nullptr, nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, "eaas kernel");
+    return E2V2_OK;
+}
+
+size_t e2v2_attn_workspace_bytes(const e2v2_layer_desc *desc, int32_t n)
+{
+    if (!desc || n < 0 || desc->lmax < 0 || desc->lmax > kMaxL || desc->channels <= 0) return 0;
+    return attn_ws(*desc, n).total;
+}
+
+e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos, const void *h,
+                                   const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
+                                   const int32_t *nbr_idx, int32_t n, float *out, void *workspace,
+                                   size_t workspace_bytes, const e2v2_taps *taps, hipStream_t stream)
+{
+    e2v2_status st = check_desc(desc);
+    if (st != E2V2_OK) return st;
+    if (n < 0) return fail(E2V2_ERR_ARG, "n < 0");
+    if (n == 0) return E2V2_OK;
+    if (!w) return fail(E2V2_ERR_ARG, "weights is NULL");
+    const void *dev[] = {pos, h, w->w_q, w->w_k, w->w_v, w->w_o, w->w_rbf, w->w_src, w->w_tgt,
+                         nbr_start, nbr_len, nbr_idx, out, workspace};
+    for (const void *p : dev) {
+        if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
+        if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    }
+    const AttnWs L = attn_ws(*desc, n);
+    if (workspace_bytes < L.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, L.total);
+    char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+    const int lmax = desc->lmax, C = desc->channels, NC = n_comp(lmax);
+    const bool bf = desc->storage == E2V2_BF16;
+    const size_t wstride = (size_t)C * C * (bf ? 2 : 4);
+    float *q = reinterpret_cast<float *>(ws + L.q);
+    float *k = reinterpret_cast<float *>(ws + L.k);
+    float *v = reinterpret_cast<float *>(ws + L.v);
+    void *hp = ws + L.hp;
+    float *dmat = reinterpret_cast<float *>(ws + L.dmat);
+    float4 *pos4 = reinterpret_cast<float4 *>(ws + L.pos4);
+    float *hhat = reinterpret_cast<float *>(ws + L.hhat);
+
+    hipEvent_t *ev = taps ? taps->events : nullptr;
+    auto mark = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], stream) : hipSuccess; };
+    hipError_t e = mark(0);
+    if (e != hipSuccess) return hip_fail(e, "recording stage event");
+    // Step 2: projections (q, k from the l = 0 block; v per component with W_V[l]).
+    ProjJob jobs[kMaxL * kMaxL + 2 * kMaxL + 1 + 2];
+    int nj = 0;
+    for (int l = 0; l <= lmax; ++l)
+        for (int m = 0; m < 2 * l + 1; ++m)
+            jobs[nj++] = ProjJob{h, (long long)NC * C, reinterpret_cast<const char *>(w->w_v) + l * wstride, v,
+                                 (long long)NC * C, l * l + m};
+    jobs[nj++] = ProjJob{h, (long long)NC * C, w->w_q, q, (long long)C, 0};
+    jobs[nj++] = ProjJob{h, (long long)NC * C, w->w_k, k, (long long)C, 0};
+    e = launch_proj(jobs, nj, bf, bf, n, C, stream);
+    if (e == hipSuccess) e = mark(1);
+    if (e != hipSuccess) return hip_fail(e, "projection kernel");
+    // Step 3: source coupling h' (EAAS), per-node D blocks and padded positions.
+    e = launch_eaas(lmax, pos, v, 0, w->w_src, n, C, hp, bf ? 2 : 0, taps ? taps->hprime : nullptr, dmat, pos4,
+                    stream);
+    if (e == hipSuccess) e = mark(2);
+    if (e != hipSuccess) return hip_fail(e, "source EAAS kernel");
+    // Steps 4-5: streaming attention + target coupling.
+    AttnArgs a{};
+    a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dmat = dmat;
+    a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx;
+    a.w_rbf = w->w_rbf; a.w_tgt = w->w_tgt; a.hhat = hhat;
+    a.m_tap = taps ? taps->m : nullptr;
+    a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
+    e = launch_attn(lmax, bf, a, stream);
+    if (e == hipSuccess) e = mark(3);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel");
+    // Step 6: output projection.
+    nj = 0;
+    for (int l = 0; l <= lmax; ++l)
+        for (int m = 0; m < 2 * l + 1; ++m)
+            jobs[nj++] = ProjJob{hhat, (long long)NC * C, reinterpret_cast<const char *>(w->w_o) + l * wstride, out,
+                                 (long long)NC * C, l * l + m};
+    e = launch_proj(jobs, nj, 0, bf, n, C, stream);
+    if (e == hipSuccess) e = mark(4);
+    if (e != hipSuccess) return hip_fail(e, "output projection kernel");
+    if (taps) {
+        const size_t N = (size_t)n;
+        struct { void *dst; const void *src; size_t bytes; } cp[] = {
+            {taps->q, q, N * C * 4}, {taps->k, k, N * C * 4}, {taps->v, v, N * NC * C * 4},
+            {taps->hhat, hhat, N * NC * C * 4}};
+        for (auto &c : cp)
+            if (c.dst) {
+                e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, stream);
+                if (e != hipSuccess) return hip_fail(e, "copying taps");
+            }
+    }
+    return E2V2_OK;
+}
+
+e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,
+                              const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx, int32_t n,
+                              float *out, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return e2v2_attn_forward_taps(desc, pos, h, w, nbr_start, nbr_len, nbr_idx, n, out, workspace, workspace_bytes,
+                                  nullptr, stream);
+}
+
+}  // extern "C"

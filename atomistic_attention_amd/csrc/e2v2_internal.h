@@ -1,0 +1,314 @@
+// Internal definitions shared by the e2v2 kernels and the host library.
+//
+// Geometry conventions (E2Former-V2 explainer, section 2.1): every node carries
+// an alignment rotation R with R z = r / |r|; features rotate with the real
+// Wigner-D blocks D^l(R), defined by Y^l(R x) = D^l(R) Y^l(x) for the real,
+// component-normalised spherical harmonics Y.  In the aligned frame the
+// encoding Y^{l_f}(z) has only its m = 0 entry, sqrt(2 l_f + 1), so a tensor
+// product path (l_i, l_f, l_o) becomes a one-to-one map between m values
+// (section 2.2): m_i = m_o for even l_i + l_f + l_o, m_i = -m_o (with a sign
+// carried by the coefficient) for odd.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace e2v2 {
+
+constexpr int kMaxL = 3;
+constexpr int kMaxPaths = 34;
+
+__host__ __device__ constexpr int n_comp(int L) { return (L + 1) * (L + 1); }
+
+// Floats of the concatenated D^1..D^L blocks (row-major each).
+__host__ __device__ constexpr int n_dmat(int L)
+{
+    int s = 0;
+    for (int l = 1; l <= L; ++l) s += (2 * l + 1) * (2 * l + 1);
+    return s;
+}
+__host__ __device__ constexpr int dmat_offset(int l)
+{
+    int s = 0;
+    for (int k = 1; k < l; ++k) s += (2 * k + 1) * (2 * k + 1);
+    return s;
+}
+
+__host__ __device__ constexpr bool is_path(int li, int lf, int lo)
+{
+    return (li - lf <= lo) && (lf - li <= lo) && (lo <= li + lf);
+}
+__host__ __device__ constexpr int path_count(int L)
+{
+    int p = 0;
+    for (int lo = 0; lo <= L; ++lo)
+        for (int li = 0; li <= L; ++li)
+            for (int lf = 0; lf <= L; ++lf)
+                if (is_path(li, lf, lo)) ++p;
+    return p;
+}
+// Index of (li, lf, lo) in the canonical order (l_o, then l_i, then l_f); -1 if absent.
+__host__ __device__ constexpr int path_index(int L, int li, int lf, int lo)
+{
+    int p = 0;
+    for (int a = 0; a <= L; ++a)
+        for (int b = 0; b <= L; ++b)
+            for (int c = 0; c <= L; ++c)
+                if (is_path(b, c, a)) {
+                    if (a == lo && b == li && c == lf) return p;
+                    ++p;
+                }
+    return -1;
+}
+
+// EAAS coefficients: c[p][m_o + l_o] for the single contributing m_i.
+struct EaasCoef {
+    float c[kMaxPaths][2 * kMaxL + 1];
+};
+
+// Sample directions X and inverse encodings Y^l(X)^{-1} for l = 2, 3:
+// D^l(R) = Y^l(R X) Y^l(X)^{-1}, exact because Y^l(R x) = D^l(R) Y^l(x).
+struct DSample {
+    double x2[5][3];
+    double inv2[5][5];
+    double x3[7][3];
+    double inv3[7][7];
+};
+
+struct Tables {
+    EaasCoef eaas;
+    DSample ds;
+};
+
+// Built once per process (thread safe).  host_tables().eaas is indexed in the
+// lmax = 3 path order; eaas_table(lmax) re-indexes it for a smaller lmax.
+const Tables &host_tables();
+const EaasCoef &eaas_table(int lmax);
+
+// ----------------------------------------------------------------------------
+// Real spherical harmonics of a unit vector, l = 2 and l = 3 blocks (closed forms).
+__host__ __device__ inline void sh_l2(double x, double y, double z, double *o)
+{
+    const double s15 = 3.872983346207417, s5 = 2.23606797749979;
+    o[0] = s15 * x * y;
+    o[1] = s15 * y * z;
+    o[2] = 0.5 * s5 * (3.0 * z * z - 1.0);
+    o[3] = s15 * x * z;
+    o[4] = 0.5 * s15 * (x * x - y * y);
+}
+__host__ __device__ inline void sh_l3(double x, double y, double z, double *o)
+{
+    const double a = 2.091650066335189;   // sqrt(35/8)
+    const double b = 10.246950765959598;  // sqrt(105)
+    const double c = 1.620185174601965;   // sqrt(21/8)
+    const double d = 1.3228756555322954;  // sqrt(7)/2
+    o[0] = a * y * (3.0 * x * x - y * y);
+    o[1] = b * x * y * z;
+    o[2] = c * y * (5.0 * z * z - 1.0);
+    o[3] = d * (5.0 * z * z * z - 3.0 * z);
+    o[4] = c * x * (5.0 * z * z - 1.0);
+    o[5] = 0.5 * b * z * (x * x - y * y);
+    o[6] = a * x * (x * x - 3.0 * y * y);
+}
+
+// Alignment rotation R = R_z(alpha) R_y(beta) taking z onto r/|r|, built from the
+// direction cosines (no trigonometric calls).  Returns false for r = 0 (R = I).
+__host__ __device__ inline bool alignment_rotation(double x, double y, double z, double R[3][3])
+{
+    double n2 = x * x + y * y + z * z;
+    if (!(n2 > 0.0)) {
+        for (int a = 0; a < 3; ++a)
+            for (int b = 0; b < 3; ++b) R[a][b] = (a == b) ? 1.0 : 0.0;
+        return false;
+    }
+    double inv = 1.0 / sqrt(n2);
+    x *= inv;
+    y *= inv;
+    z *= inv;
+    double rho = sqrt(x * x + y * y);
+    double ca = 1.0, sa = 0.0;
+    if (rho > 0.0) {
+        ca = x / rho;
+        sa = y / rho;
+    }
+    double cb = z, sb = rho;
+    R[0][0] = ca * cb; R[0][1] = -sa; R[0][2] = ca * sb;
+    R[1][0] = sa * cb; R[1][1] = ca;  R[1][2] = sa * sb;
+    R[2][0] = -sb;     R[2][1] = 0.0; R[2][2] = cb;
+    return true;
+}
+
+// D^1..D^L of the alignment rotation of r, fp64, row-major blocks concatenated.
+template <int L, typename DS>
+__host__ __device__ inline bool wigner_blocks(double x, double y, double z, const DS &ds, double *D)
+{
+    double R[3][3];
+    bool dir = alignment_rotation(x, y, z, R);
+    if (L >= 1) {
+        // D^1 = P R P^T with P: (x, y, z) -> (y, z, x)
+        const int s[3] = {1, 2, 0};
+        for (int a = 0; a < 3; ++a)
+            for (int b = 0; b < 3; ++b) D[a * 3 + b] = R[s[a]][s[b]];
+    }
+    if (L >= 2) {
+        double Y[5][5];   // Y[m][s] = Y^2_m(R x_s)
+        for (int sidx = 0; sidx < 5; ++sidx) {
+            double px = R[0][0] * ds.x2[sidx][0] + R[0][1] * ds.x2[sidx][1] + R[0][2] * ds.x2[sidx][2];
+            double py = R[1][0] * ds.x2[sidx][0] + R[1][1] * ds.x2[sidx][1] + R[1][2] * ds.x2[sidx][2];
+            double pz = R[2][0] * ds.x2[sidx][0] + R[2][1] * ds.x2[sidx][1] + R[2][2] * ds.x2[sidx][2];
+            double o[5];
+            sh_l2(px, py, pz, o);
+            for (int m = 0; m < 5; ++m) Y[m][sidx] = o[m];
+        }
+        double *D2 = D + dmat_offset(2);
+        for (int a = 0; a < 5; ++a)
+            for (int b = 0; b < 5; ++b) {
+                double acc = 0.0;
+                for (int sidx = 0; sidx < 5; ++sidx) acc += Y[a][sidx] * ds.inv2[sidx][b];
+                D2[a * 5 + b] = acc;
+            }
+    }
+    if (L >= 3) {
+        double Y[7][7];
+        for (int sidx = 0; sidx < 7; ++sidx) {
+            double px = R[0][0] * ds.x3[sidx][0] + R[0][1] * ds.x3[sidx][1] + R[0][2] * ds.x3[sidx][2];
+            double py = R[1][0] * ds.x3[sidx][0] + R[1][1] * ds.x3[sidx][1] + R[1][2] * ds.x3[sidx][2];
+            double pz = R[2][0] * ds.x3[sidx][0] + R[2][1] * ds.x3[sidx][1] + R[2][2] * ds.x3[sidx][2];
+            double o[7];
+            sh_l3(px, py, pz, o);
+            for (int m = 0; m < 7; ++m) Y[m][sidx] = o[m];
+        }
+        double *D3 = D + dmat_offset(3);
+        for (int a = 0; a < 7; ++a)
+            for (int b = 0; b < 7; ++b) {
+                double acc = 0.0;
+                for (int sidx = 0; sidx < 7; ++sidx) acc += Y[a][sidx] * ds.inv3[sidx][b];
+                D3[a * 7 + b] = acc;
+            }
+    }
+    return dir;
+}
+
+// ----------------------------------------------------------------------------
+// EAAS on one channel: y = D(R) . P(D(R)^T x) with per-path weights w[p].
+// D: the node's concatenated D^1..D^L (fp32).  `dir` false (r = 0) drops the
+// l_f > 0 paths: the encoding of a zero vector is Y_0 = 1 only.
+template <int L>
+__device__ __forceinline__ void eaas_channel(const float *__restrict__ D, const float (&x)[n_comp(L)],
+                                             float (&y)[n_comp(L)], const float *w, const EaasCoef &tab,
+                                             bool dir)
+{
+    constexpr int NC = n_comp(L);
+    float xt[NC];
+    xt[0] = x[0];
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        const int o = l * l, k = 2 * l + 1;
+        const float *Dl = D + dmat_offset(l);
+#pragma unroll
+        for (int b = 0; b < k; ++b) {
+            float acc = 0.f;
+#pragma unroll
+            for (int a = 0; a < k; ++a) acc = fmaf(Dl[a * k + b], x[o + a], acc);
+            xt[o + b] = acc;
+        }
+    }
+    float loc[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) loc[i] = 0.f;
+    const float fdir = dir ? 1.f : 0.f;
+#pragma unroll
+    for (int lo = 0; lo <= L; ++lo)
+#pragma unroll
+        for (int li = 0; li <= L; ++li)
+#pragma unroll
+            for (int lf = 0; lf <= L; ++lf) {
+                if (!is_path(li, lf, lo)) continue;
+                const int p = path_index(L, li, lf, lo);
+                const bool odd = ((li + lf + lo) & 1) != 0;
+                const int mm = li < lo ? li : lo;
+                const float wp = (lf > 0) ? w[p] * fdir : w[p];
+#pragma unroll
+                for (int mo = -mm; mo <= mm; ++mo) {
+                    if (odd && mo == 0) continue;
+                    const int mi = odd ? -mo : mo;
+                    loc[lo * lo + lo + mo] = fmaf(wp * tab.c[p][mo + lo], xt[li * li + li + mi], loc[lo * lo + lo + mo]);
+                }
+            }
+    y[0] = loc[0];
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        const int o = l * l, k = 2 * l + 1;
+        const float *Dl = D + dmat_offset(l);
+#pragma unroll
+        for (int a = 0; a < k; ++a) {
+            float acc = 0.f;
+#pragma unroll
+            for (int b = 0; b < k; ++b) acc = fmaf(Dl[a * k + b], loc[o + b], acc);
+            y[o + a] = acc;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// bf16 helpers (bit patterns in uint16_t / packed in uint32_t).
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ uint16_t f_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) {               // inf / nan: keep, quiet the nan
+        return uint16_t((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);                       // round to nearest, ties to even
+    return uint16_t(u >> 16);
+}
+
+// ----------------------------------------------------------------------------
+// Launch helpers implemented in the .hip files (all enqueue on `stream`).
+struct NbrWork;   // neighbours.hip
+
+// y_format: 0 fp32, 1 bf16, 2 fp16 with a per-node power-of-two scale written to
+// pos4_out[node].w (pos4_out required).  y_deq (optional) receives the stored
+// values dequantised to fp32.
+hipError_t launch_eaas(int L, const float *pos, const void *x, int x_bf16, const float *path_w, int n, int C,
+                       void *y, int y_format, float *y_deq, float *dmat_out, float4 *pos4_out, hipStream_t stream);
+
+struct ProjJob {
+    const void *a;          // A rows: a + node*a_node_stride + comp*C (elements)
+    long long a_node_stride;
+    const void *b;          // [C][C] weight (in, out)
+    float *out;             // out + node*o_node_stride + comp*C
+    long long o_node_stride;
+    int comp;               // component index of the rows
+};
+hipError_t launch_proj(const ProjJob *jobs, int njobs, int a_bf16, int b_bf16, int n, int C, hipStream_t stream);
+
+struct AttnArgs {
+    const float *q, *k;              // [n][C] fp32
+    const void *hp;                  // [n][NC][C] fp32, or fp16 scaled by pos4[j].w
+    const float4 *pos4;              // [n] (x, y, z, scale of h'_j)
+    const float *dmat;               // [n][n_dmat(L)]
+    const int32_t *nbr_start, *nbr_len, *nbr_idx;
+    const float *w_rbf;              // [R][H]
+    const float *w_tgt;              // [P][C]
+    float *hhat;                     // [n][NC][C] fp32
+    float *m_tap;                    // optional [n][NC][C]
+    int n, C, H, R;
+    float cutoff;
+};
+// hp_f16s: h' is fp16 with per-node scales (else fp32).
+hipError_t launch_attn(int L, int hp_f16s, const AttnArgs &a, hipStream_t stream);
+
+hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, void *ws, size_t ws_bytes,
+                                  int32_t *nbr_len, hipStream_t stream);
+hipError_t launch_neighbors_scan(int n, void *ws, int32_t *nbr_start, int32_t *nbr_len, int64_t *nnz_dev,
+                                 hipStream_t stream);
+hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, void *ws, int32_t *nbr_start,
+                                 int32_t *nbr_len, int32_t *nbr_idx, hipStream_t stream);
+size_t neighbors_ws_bytes(int n, int K);
+int64_t *neighbors_nnz_slot(void *ws, int n);
+
+}  // namespace e2v2

@@ -1,0 +1,158 @@
+// EAAS tensor product of node features with the encoding of the node's own
+// position (E2Former-V2 explainer, section 2.1 pseudocode: alignment rotation,
+// rotate features, sparse re-index, inverse rotation; section 2.3 Proposition
+// 4.3: the result equals the dense SO(3) tensor product).
+//
+// One block of 256 threads covers 256 / C nodes.  The first threads build each
+// node's Wigner-D blocks in fp64 (once per node, shared through LDS); then one
+// thread per (node, channel) applies rotate-in, the m re-index and rotate-out
+// entirely in registers.  Reads and writes are channel-contiguous.
+#include "e2v2_internal.h"
+
+namespace e2v2 {
+
+template <typename T> __device__ __forceinline__ float ld_elem(const T *p, size_t i);
+template <> __device__ __forceinline__ float ld_elem<float>(const float *p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t *p, size_t i) { return bf16_to_f(p[i]); }
+
+// Output formats: fp32, bf16, or fp16 with one power-of-two scale per node
+// (kHpF16S).  The scaled-fp16 form keeps 16 bits per element like bf16 but with
+// an 11-bit significand; the per-node scale s (stored in pos4[node].w) keeps
+// fp32 range: the node's largest magnitude M maps below 2^14, so no element
+// overflows and every element within 2^28 of M stays a normal fp16 number.
+enum { kYF32 = 0, kYBF16 = 1, kYF16S = 2 };
+
+__device__ __forceinline__ uint16_t f_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float f16_to_f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+template <int L, typename TX, int YF>
+__global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos, const TX *__restrict__ x,
+                                                   const float *__restrict__ path_w, int n, int C,
+                                                   void *__restrict__ y_, float *__restrict__ y_deq,
+                                                   float *__restrict__ dmat_out, float4 *__restrict__ pos4_out,
+                                                   const Tables tabs)
+{
+    constexpr int NC = n_comp(L);
+    constexpr int ND = n_dmat(L) > 0 ? n_dmat(L) : 1;
+    constexpr int P = path_count(L);
+    __shared__ float sD[32][ND];
+    __shared__ int sDir[32];
+    __shared__ unsigned sMax[32];
+
+    const int npb = 256 / C;
+    const int t = threadIdx.x;
+    const long long node0 = (long long)blockIdx.x * npb;
+    if (t < 32) sMax[t] = 0u;
+    if (t < npb) {
+        const long long node = node0 + t;
+        if (node < n) {
+            const double px = pos[3 * node + 0], py = pos[3 * node + 1], pz = pos[3 * node + 2];
+            double Dd[ND];
+            const bool dir = wigner_blocks<L>(px, py, pz, tabs.ds, Dd);
+#pragma unroll
+            for (int e = 0; e < n_dmat(L); ++e) {
+                sD[t][e] = (float)Dd[e];
+                if (dmat_out) dmat_out[node * n_dmat(L) + e] = (float)Dd[e];
+            }
+            sDir[t] = dir ? 1 : 0;
+            if (pos4_out && YF != kYF16S) pos4_out[node] = make_float4((float)px, (float)py, (float)pz, 1.f);
+        }
+    }
+    __syncthreads();
+    const int ln = t / C, c = t - ln * C;
+    const long long node = node0 + ln;
+    const bool active = ln < npb && node < n;
+    float yv[NC];
+    const size_t base = (size_t)node * NC * C + c;
+    if (active) {
+        float xv[NC], w[P];
+#pragma unroll
+        for (int e = 0; e < NC; ++e) xv[e] = ld_elem<TX>(x, base + (size_t)e * C);
+#pragma unroll
+        for (int p = 0; p < P; ++p) w[p] = path_w[p * C + c];
+        eaas_channel<L>(&sD[ln][0], xv, yv, w, tabs.eaas, sDir[ln] != 0);
+    }
+    if constexpr (YF == kYF16S) {
+        if (active) {
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < NC; ++e) m = fmaxf(m, fabsf(yv[e]));
+            atomicMax(&sMax[ln], __float_as_uint(m));       // non-negative floats order like their bits
+        }
+        __syncthreads();
+        if (!active) return;
+        const unsigned mb = sMax[ln];
+        unsigned sb = 127u, ib = 127u;                      // scale 1 for zero or non-finite rows
+        if (mb != 0u && mb < 0x7f800000u) {
+            const unsigned b = mb >> 23;                    // M < 2^(b-126); s = 2^(b-140)
+            sb = b > 13u ? b - 13u : 1u;
+            ib = 254u - sb;
+        }
+        const float sc = __uint_as_float(sb << 23), inv = __uint_as_float(ib << 23);
+        uint16_t *y = reinterpret_cast<uint16_t *>(y_);
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+            const uint16_t hb = f_to_f16(yv[e] * inv);
+            y[base + (size_t)e * C] = hb;
+            if (y_deq) y_deq[base + (size_t)e * C] = f16_to_f(hb) * sc;
+        }
+        if (c == 0 && pos4_out)
+            pos4_out[node] = make_float4(pos[3 * node], pos[3 * node + 1], pos[3 * node + 2], sc);
+    } else {
+        if (!active) return;
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+            if (YF == kYBF16) {
+                const uint16_t hb = f_to_bf16(yv[e]);
+                reinterpret_cast<uint16_t *>(y_)[base + (size_t)e * C] = hb;
+                if (y_deq) y_deq[base + (size_t)e * C] = bf16_to_f(hb);
+            } else {
+                reinterpret_cast<float *>(y_)[base + (size_t)e * C] = yv[e];
+                if (y_deq) y_deq[base + (size_t)e * C] = yv[e];
+            }
+        }
+    }
+}
+
+template <int L, typename TX>
+static void launch_eaas_x(dim3 grid, const float *pos, const void *x, const float *path_w, int n, int C, void *y,
+                          int yf, float *y_deq, float *dmat_out, float4 *pos4_out, const Tables &tb, hipStream_t stream)
+{
+    const TX *xp = reinterpret_cast<const TX *>(x);
+    if (yf == kYF16S)
+        eaas_kernel<L, TX, kYF16S><<<grid, 256, 0, stream>>>(pos, xp, path_w, n, C, y, y_deq, dmat_out, pos4_out, tb);
+    else if (yf == kYBF16)
+        eaas_kernel<L, TX, kYBF16><<<grid, 256, 0, stream>>>(pos, xp, path_w, n, C, y, y_deq, dmat_out, pos4_out, tb);
+    else
+        eaas_kernel<L, TX, kYF32><<<grid, 256, 0, stream>>>(pos, xp, path_w, n, C, y, y_deq, dmat_out, pos4_out, tb);
+}
+
+template <int L>
+static hipError_t launch_eaas_l(const float *pos, const void *x, int x_bf16, const float *path_w, int n, int C,
+                                void *y, int yf, float *y_deq, float *dmat_out, float4 *pos4_out, hipStream_t stream)
+{
+    const int npb = 256 / C;
+    dim3 grid((unsigned)((n + npb - 1) / npb));
+    Tables tb = host_tables();
+    tb.eaas = eaas_table(L);
+    if (x_bf16)
+        launch_eaas_x<L, uint16_t>(grid, pos, x, path_w, n, C, y, yf, y_deq, dmat_out, pos4_out, tb, stream);
+    else
+        launch_eaas_x<L, float>(grid, pos, x, path_w, n, C, y, yf, y_deq, dmat_out, pos4_out, tb, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_eaas(int L, const float *pos, const void *x, int x_bf16, const float *path_w, int n, int C,
+                       void *y, int y_format, float *y_deq, float *dmat_out, float4 *pos4_out, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    switch (L) {
+    case 0: return launch_eaas_l<0>(pos, x, x_bf16, path_w, n, C, y, y_format, y_deq, dmat_out, pos4_out, stream);
+    case 1: return launch_eaas_l<1>(pos, x, x_bf16, path_w, n, C, y, y_format, y_deq, dmat_out, pos4_out, stream);
+    case 2: return launch_eaas_l<2>(pos, x, x_bf16, path_w, n, C, y, y_format, y_deq, dmat_out, pos4_out, stream);
+    case 3: return launch_eaas_l<3>(pos, x, x_bf16, path_w, n, C, y, y_format, y_deq, dmat_out, pos4_out, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace e2v2

@@ -1,0 +1,384 @@
+// Cell-list neighbour list (E2Former-V2 explainer, section 3.2: a neighbour cap
+// K with masked padding; section 5.2: the list must be right).  Every candidate
+// pair is decided by the fp64 predicate
+//     dx = (double)x_j - (double)x_i  (likewise dy, dz),
+//     d2 = (dx*dx + dy*dy) + dz*dz < (double)cutoff^2,
+// with no fused multiply-add, so the result is bit-identical to a brute-force
+// search with the same arithmetic.
+//
+// Steps (all on the caller's stream):
+//   1. one block reduces the bounding box and sizes a grid whose cells are at
+//      least (1 + 1e-5) * cutoff wide (so a 27-cell stencil covers every pair
+//      even with rounding in the cell index) and holds at most n + 64 cells;
+//   2. cell index per atom + per-cell counts (integer atomics: counts are exact);
+//   3. exclusive scan of the counts; scatter atoms into cell order;
+//   4. one thread per target (targets taken in cell order, so neighbouring
+//      threads read the same cells) scans the 27 cells:
+//        K = 0: count -> scan -> fill -> sort row by j;
+//        K > 0: keep the K nearest by (d2, j) in a max-heap held in the row
+//               itself (d2 recomputed on demand), then sort by j, pad with -1.
+// Within-cell order depends on atomics, but rows are sets sorted by j and the
+// K-nearest choice uses a total order, so results are deterministic.
+#include "e2v2_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace e2v2 {
+
+struct GridInfo {
+    float lo[3];
+    float inv[3];
+    int dims[3];
+    int ncell;
+};
+
+struct NbrLayout {
+    GridInfo *grid;
+    int32_t *cell_of;
+    int32_t *cell_cnt;     // [maxc + 1]
+    int32_t *cell_start;   // [maxc + 1]
+    int32_t *cell_cur;     // [maxc]
+    int32_t *order;        // [n] atom ids in cell order
+    float4 *spos;          // [n] positions in cell order, w = atom id bits
+    int64_t *nnz;
+    size_t bytes;
+};
+
+static inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+static inline int max_cells(int n) { return n + 64; }
+
+static NbrLayout nbr_layout(void *ws, int n)
+{
+    NbrLayout L{};
+    char *p = reinterpret_cast<char *>(ws);
+    size_t o = 0;
+    const size_t mc = (size_t)max_cells(n);
+    L.grid = reinterpret_cast<GridInfo *>(p + o); o += al256(sizeof(GridInfo));
+    L.nnz = reinterpret_cast<int64_t *>(p + o); o += al256(sizeof(int64_t));
+    L.cell_of = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (size_t)n);
+    L.cell_cnt = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (mc + 1));
+    L.cell_start = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (mc + 1));
+    L.cell_cur = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * mc);
+    L.order = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (size_t)n);
+    L.spos = reinterpret_cast<float4 *>(p + o); o += al256(sizeof(float4) * (size_t)n);
+    L.bytes = o;
+    return L;
+}
+
+size_t neighbors_ws_bytes(int n, int /*K*/) { return nbr_layout(nullptr, n).bytes; }
+int64_t *neighbors_nnz_slot(void *ws, int n) { return nbr_layout(ws, n).nnz; }
+
+// ---------------------------------------------------------------- step 1
+__global__ __launch_bounds__(1024) void k_bbox(const float *__restrict__ pos, int n, float cutoff, int maxc,
+                                               GridInfo *grid, int32_t *cell_cnt)
+{
+    __shared__ float smin[3][1024], smax[3][1024];
+    const int t = threadIdx.x;
+    float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+    for (long long i = t; i < n; i += 1024)
+        for (int d = 0; d < 3; ++d) {
+            const float v = pos[3 * i + d];
+            mn[d] = fminf(mn[d], v);     // fminf/fmaxf ignore NaN
+            mx[d] = fmaxf(mx[d], v);
+        }
+    for (int d = 0; d < 3; ++d) { smin[d][t] = mn[d]; smax[d][t] = mx[d]; }
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+        if (t < s)
+            for (int d = 0; d < 3; ++d) {
+                smin[d][t] = fminf(smin[d][t], smin[d][t + s]);
+                smax[d][t] = fmaxf(smax[d][t], smax[d][t + s]);
+            }
+        __syncthreads();
+    }
+    // clear the cell counters for step 2
+    for (long long c = t; c <= maxc; c += 1024) cell_cnt[c] = 0;
+    if (t == 0) {
+        const float cmin = cutoff * 1.00001f;
+        int dims[3];
+        float ext[3];
+        for (int d = 0; d < 3; ++d) {
+            ext[d] = smax[d][0] - smin[d][0];
+            float k = (ext[d] < 1e30f) ? floorf(ext[d] / cmin) : 1.f;   // false for NaN / inf
+            dims[d] = (k >= 1.f) ? (int)fminf(k, 1024.f) : 1;
+        }
+        while ((long long)dims[0] * dims[1] * dims[2] > maxc) {
+            int a = 0;
+            if (dims[1] > dims[a]) a = 1;
+            if (dims[2] > dims[a]) a = 2;
+            dims[a] = dims[a] * 7 / 8 > 0 ? dims[a] * 7 / 8 : 1;
+        }
+        for (int d = 0; d < 3; ++d) {
+            grid->lo[d] = (smin[d][0] < 1e30f && smin[d][0] > -1e30f) ? smin[d][0] : 0.f;
+            grid->inv[d] = dims[d] > 1 ? (float)dims[d] / ext[d] : 0.f;
+            grid->dims[d] = dims[d];
+        }
+        grid->ncell = dims[0] * dims[1] * dims[2];
+    }
+}
+
+__device__ __forceinline__ int cell_coord(float x, float lo, float inv, int dim)
+{
+    const float t = (x - lo) * inv;
+    if (!(t > 0.f)) return 0;                                // also NaN
+    return t >= (float)(dim - 1) ? dim - 1 : (int)t;
+}
+
+// ---------------------------------------------------------------- step 2
+__global__ void k_cell_assign(const float *__restrict__ pos, int n, const GridInfo *__restrict__ grid,
+                              int32_t *cell_of, int32_t *cell_cnt)
+{
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const GridInfo gi = *grid;
+    const int cx = cell_coord(pos[3 * i + 0], gi.lo[0], gi.inv[0], gi.dims[0]);
+    const int cy = cell_coord(pos[3 * i + 1], gi.lo[1], gi.inv[1], gi.dims[1]);
+    const int cz = cell_coord(pos[3 * i + 2], gi.lo[2], gi.inv[2], gi.dims[2]);
+    const int c = (cz * gi.dims[1] + cy) * gi.dims[0] + cx;
+    cell_of[i] = c;
+    atomicAdd(&cell_cnt[c], 1);
+}
+
+// Exclusive scan of in[0..count) into out[0..count], out[count] = total; one block.
+// If total_out is non-null the total is also stored there as int64.
+__global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, const int *count_dev, int count_arg,
+                                               int32_t *out, int32_t *copy, int64_t *total_out)
+{
+    __shared__ long long part[1024];
+    const int t = threadIdx.x;
+    const int count = count_dev ? *count_dev : count_arg;
+    const long long seg = ((long long)count + 1023) / 1024;
+    const long long b = t * seg, e = (b + seg < count) ? b + seg : count;
+    long long s = 0;
+    for (long long k = b; k < e; ++k) s += in[k];
+    part[t] = s;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const long long v = (t >= d) ? part[t - d] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    long long run = part[t] - s;
+    for (long long k = b; k < e; ++k) {
+        const int32_t v = in[k];
+        out[k] = (int32_t)run;
+        if (copy) copy[k] = (int32_t)run;
+        run += v;
+    }
+    if (t == 1023) {
+        out[count] = (int32_t)part[1023];
+        if (total_out) *total_out = part[1023];
+    }
+}
+
+// ---------------------------------------------------------------- step 3
+__global__ void k_scatter(const float *__restrict__ pos, int n, const int32_t *__restrict__ cell_of,
+                          int32_t *cell_cur, int32_t *order, float4 *spos)
+{
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int slot = atomicAdd(&cell_cur[cell_of[i]], 1);
+    order[slot] = (int32_t)i;
+    spos[slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float((int)i));
+}
+
+// ---------------------------------------------------------------- step 4
+__device__ __forceinline__ double pair_d2(double xi, double yi, double zi, float4 pj)
+{
+    const double dx = (double)pj.x - xi;
+    const double dy = (double)pj.y - yi;
+    const double dz = (double)pj.z - zi;
+    const double xx = dx * dx;   // fp contract is off in this file: each op rounds
+    const double yy = dy * dy;
+    const double zz = dz * dz;
+    const double s = xx + yy;
+    return s + zz;
+}
+__device__ __forceinline__ double d2_of(const float *__restrict__ pos, double xi, double yi, double zi, int j)
+{
+    return pair_d2(xi, yi, zi, make_float4(pos[3 * (size_t)j], pos[3 * (size_t)j + 1], pos[3 * (size_t)j + 2], 0.f));
+}
+
+// Visits every candidate j != i in the 27-cell stencil with d2 < rc2.
+template <typename F>
+__device__ __forceinline__ void for_each_neighbor(int i, double xi, double yi, double zi, float xf, float yf,
+                                                  float zf, double rc2, const GridInfo &gi,
+                                                  const int32_t *__restrict__ cell_start,
+                                                  const float4 *__restrict__ spos, F &&f)
+{
+    const int cx = cell_coord(xf, gi.lo[0], gi.inv[0], gi.dims[0]);
+    const int cy = cell_coord(yf, gi.lo[1], gi.inv[1], gi.dims[1]);
+    const int cz = cell_coord(zf, gi.lo[2], gi.inv[2], gi.dims[2]);
+    for (int z = cz - 1; z <= cz + 1; ++z) {
+        if (z < 0 || z >= gi.dims[2]) continue;
+        for (int y = cy - 1; y <= cy + 1; ++y) {
+            if (y < 0 || y >= gi.dims[1]) continue;
+            for (int x = cx - 1; x <= cx + 1; ++x) {
+                if (x < 0 || x >= gi.dims[0]) continue;
+                const int c = (z * gi.dims[1] + y) * gi.dims[0] + x;
+                const int e = cell_start[c + 1];
+                for (int s = cell_start[c]; s < e; ++s) {
+                    const float4 pj = spos[s];
+                    const int j = __float_as_int(pj.w);
+                    if (j == i) continue;
+                    const double d2 = pair_d2(xi, yi, zi, pj);
+                    if (d2 < rc2) f(j, d2);
+                }
+            }
+        }
+    }
+}
+
+__global__ void k_count(int n, double rc2, const GridInfo *__restrict__ grid, const int32_t *__restrict__ cell_start,
+                        const int32_t *__restrict__ order, const float4 *__restrict__ spos, int32_t *nbr_len)
+{
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n) return;
+    const GridInfo gi = *grid;
+    const float4 pi = spos[t];
+    const int i = order[t];
+    int cnt = 0;
+    for_each_neighbor(i, (double)pi.x, (double)pi.y, (double)pi.z, pi.x, pi.y, pi.z, rc2, gi, cell_start, spos,
+                      [&](int, double) { ++cnt; });
+    nbr_len[i] = cnt;
+}
+
+// In-place heapsort of ints ascending.
+__device__ inline void heapsort_int(int32_t *a, int len)
+{
+    auto sift = [&](int root, int end) {
+        while (true) {
+            int child = 2 * root + 1;
+            if (child >= end) break;
+            if (child + 1 < end && a[child + 1] > a[child]) ++child;
+            if (a[root] >= a[child]) break;
+            const int32_t tmp = a[root]; a[root] = a[child]; a[child] = tmp;
+            root = child;
+        }
+    };
+    for (int r = len / 2 - 1; r >= 0; --r) sift(r, len);
+    for (int end = len - 1; end > 0; --end) {
+        const int32_t tmp = a[0]; a[0] = a[end]; a[end] = tmp;
+        sift(0, end);
+    }
+}
+
+__global__ void k_fill_csr(int n, double rc2, const GridInfo *__restrict__ grid, const int32_t *__restrict__ cell_start,
+                           const int32_t *__restrict__ order, const float4 *__restrict__ spos,
+                           const int32_t *__restrict__ nbr_start, int32_t *nbr_idx)
+{
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n) return;
+    const GridInfo gi = *grid;
+    const float4 pi = spos[t];
+    const int i = order[t];
+    int32_t *row = nbr_idx + nbr_start[i];
+    int cnt = 0;
+    for_each_neighbor(i, (double)pi.x, (double)pi.y, (double)pi.z, pi.x, pi.y, pi.z, rc2, gi, cell_start, spos,
+                      [&](int j, double) { row[cnt++] = j; });
+    heapsort_int(row, cnt);
+}
+
+// Key order for the cap: (d2, j) lexicographic.
+__device__ __forceinline__ bool key_less(double da, int ja, double db, int jb)
+{
+    return da < db || (da == db && ja < jb);
+}
+
+__global__ void k_fill_capped(int n, int K, double rc2, const float *__restrict__ pos, const GridInfo *__restrict__ grid,
+                              const int32_t *__restrict__ cell_start, const int32_t *__restrict__ order,
+                              const float4 *__restrict__ spos, int32_t *nbr_start, int32_t *nbr_len, int32_t *nbr_idx)
+{
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n) return;
+    const GridInfo gi = *grid;
+    const float4 pi = spos[t];
+    const int i = order[t];
+    const double xi = pi.x, yi = pi.y, zi = pi.z;
+    int32_t *row = nbr_idx + (size_t)i * K;
+    // max-heap on (d2, j): row[0] is the farthest kept neighbour
+    auto sift_down = [&](int root, int end) {
+        int32_t rj = row[root];
+        double rd = d2_of(pos, xi, yi, zi, rj);
+        while (true) {
+            int child = 2 * root + 1;
+            if (child >= end) break;
+            int32_t cj = row[child];
+            double cd = d2_of(pos, xi, yi, zi, cj);
+            if (child + 1 < end) {
+                const int32_t c2 = row[child + 1];
+                const double d2v = d2_of(pos, xi, yi, zi, c2);
+                if (key_less(cd, cj, d2v, c2)) { ++child; cj = c2; cd = d2v; }
+            }
+            if (!key_less(rd, rj, cd, cj)) break;
+            row[root] = cj;
+            root = child;
+        }
+        row[root] = rj;
+    };
+    int cnt = 0;
+    for_each_neighbor(i, xi, yi, zi, pi.x, pi.y, pi.z, rc2, gi, cell_start, spos, [&](int j, double d2) {
+        if (cnt < K) {
+            row[cnt] = j;
+            if (cnt + 1 == K)
+                for (int r = K / 2 - 1; r >= 0; --r) sift_down(r, K);
+        } else {
+            const int32_t tj = row[0];
+            if (key_less(d2, j, d2_of(pos, xi, yi, zi, tj), tj)) {
+                row[0] = j;
+                sift_down(0, K);
+            }
+        }
+        ++cnt;
+    });
+    const int len = cnt < K ? cnt : K;
+    heapsort_int(row, len);
+    for (int s = len; s < K; ++s) row[s] = -1;
+    nbr_len[i] = len;
+    nbr_start[i] = (int32_t)((size_t)i * K);
+}
+
+// ---------------------------------------------------------------- host launchers
+static inline unsigned nblk(long long n, int b) { return (unsigned)((n + b - 1) / b); }
+
+hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, void *ws, size_t,
+                                  int32_t *nbr_len, hipStream_t stream)
+{
+    NbrLayout L = nbr_layout(ws, n);
+    const int maxc = max_cells(n);
+    k_bbox<<<1, 1024, 0, stream>>>(pos, n, cutoff, maxc, L.grid, L.cell_cnt);
+    k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt);
+    k_scan<<<1, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, 0, L.cell_start, L.cell_cur, nullptr);
+    k_scatter<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_cur, L.order, L.spos);
+    if (K == 0) {
+        const double rc2 = (double)cutoff * (double)cutoff;
+        k_count<<<nblk(n, 128), 128, 0, stream>>>(n, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_len);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_neighbors_scan(int n, void *ws, int32_t *nbr_start, int32_t *nbr_len, int64_t *nnz_dev,
+                                 hipStream_t stream)
+{
+    // nbr_start needs n + 1 slots for the scan's total; use the layout's cell_start
+    // scratch for the tail-inclusive copy and write the first n into nbr_start.
+    NbrLayout L = nbr_layout(ws, n);
+    k_scan<<<1, 1024, 0, stream>>>(nbr_len, nullptr, n, L.cell_cur, nbr_start, nnz_dev);
+    return hipGetLastError();
+}
+
+hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, void *ws, int32_t *nbr_start,
+                                 int32_t *nbr_len, int32_t *nbr_idx, hipStream_t stream)
+{
+    NbrLayout L = nbr_layout(ws, n);
+    const double rc2 = (double)cutoff * (double)cutoff;
+    if (K == 0)
+        k_fill_csr<<<nblk(n, 128), 128, 0, stream>>>(n, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_idx);
+    else
+        k_fill_capped<<<nblk(n, 128), 128, 0, stream>>>(n, K, rc2, pos, L.grid, L.cell_start, L.order, L.spos,
+                                                         nbr_start, nbr_len, nbr_idx);
+    return hipGetLastError();
+}
+
+}  // namespace e2v2

@@ -23,7 +23,7 @@ import math
 import numpy as np
 
 __all__ = ["LayerConfig", "CONFIGS", "Workload", "make_workload", "num_paths",
-           "path_list", "round_bf16", "bf16_bits", "bf16_from_bits"]
+           "path_list", "round_bf16", "bf16_bits", "bf16_from_bits", "device_arrays"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -127,6 +127,26 @@ class Workload:
         if self.cfg.storage == "bf16":
             return bf16_bits(a)
         return a.astype(np.float32)
+
+
+def device_arrays(wl: Workload, device="cuda") -> dict:
+    """Upload a workload as the library consumes it: positions, path weights and RBF
+    weights fp32; features and projection weights in the storage dtype."""
+    import torch
+
+    dt = torch.bfloat16 if wl.cfg.storage == "bf16" else torch.float32
+
+    def st(a):
+        if dt == torch.bfloat16:
+            return torch.from_numpy(np.ascontiguousarray(bf16_bits(a)).view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    def f(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    return dict(pos=f(wl.pos), h=st(wl.h), dtype=dt,
+                weights=dict(w_q=st(wl.w_q), w_k=st(wl.w_k), w_v=st(wl.w_v), w_o=st(wl.w_o),
+                             w_rbf=f(wl.w_rbf), w_src=f(wl.w_src), w_tgt=f(wl.w_tgt)))
 
 
 def _box_side(cfg: LayerConfig) -> float:

@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of one E2Former-V2 node-centric attention layer forward on one MI355X.
+
+A step is one pass of the whole path over the resident workload: the cell-list
+neighbour build (capped, no host synchronisation) followed by the layer forward
+(projections, source EAAS coupling, fused streaming attention with the target
+coupling, output projection).  The default workload is 32,768 atoms at
+0.1 atoms/A^3 with an 8 A cutoff and a K = 256 neighbour cap, l_max = 2,
+128 channels, 16 heads, 32 RBFs, bf16 storage with fp32 arithmetic.
+
+Prints one JSON line: pairs/s over the whole step (value), steps/s, per-stage
+times, the streaming kernel's achieved algorithmic bandwidth against the HBM
+peak (roofline), and the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host (cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--config c4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "atom-neighbour pairs/s & steps/s per attn layer fwd; % HBM peak (1 MI355X)"
+HBM_PEAK_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "atomistic_attention_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+
+
+def algorithmic_bytes(cfg, nnz: int) -> dict:
+    """Bytes the streaming kernel must move: per pair the neighbour's coupled value
+    row h'_j (storage dtype), its fp32 key row, its index and its position; per
+    target its query, its D blocks, its position, its row bounds and the fp32
+    coupled output row."""
+    C, nc = cfg.channels, cfg.n_comp
+    s = 2 if cfg.storage == "bf16" else 4
+    nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
+    per_pair = nc * C * s + 4 * C + 4 + 12
+    per_node = 4 * C + 4 * nd + 12 + 8 + 4 * nc * C
+    return {"per_pair": per_pair, "per_node": per_node, "total": nnz * per_pair + cfg.n * per_node}
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the streaming kernel from the committed counter runs,
+    if they were taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_targets: int | None = None) -> dict:
+    """The fp64 oracle on a compact ball of targets around the box centre (all of
+    its steps: brute-force neighbours, projections, dense-CG coupling, explicit
+    softmax, target coupling, output projection)."""
+    from oracle import layer as O
+    pos = wl.pos
+    r = np.linalg.norm(pos, axis=1)
+    T = budget_targets or int(os.environ.get("E2V2_CPU_TARGETS", "2500"))
+    tg = np.sort(np.argsort(r, kind="stable")[:T])
+    t0 = time.perf_counter()
+    res = O.layer_forward_workload(wl, targets=tg)
+    dt = time.perf_counter() - t0
+    pairs = int(sum(x.size for x in res["rows"]))
+    threads = int(os.environ.get("OMP_NUM_THREADS", str(len(os.sched_getaffinity(0)))))
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"{T} targets nearest the box centre of the same workload ({pairs} pairs, "
+                      f"{res['src'].size} coupled sources), whole layer incl. brute-force neighbours; "
+                      f"{dt:.1f} s; the neighbour search uses {threads} OpenMP threads, the numpy "
+                      f"tensor products one thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this layer has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from atomistic_attention_amd import binding as B
+    from atomistic_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.load()
+    wl = W.make_workload(args.config)
+    cfg = wl.cfg
+    d = W.device_arrays(wl)
+    dev = d["pos"].device
+    desc = B.make_desc(cfg.lmax, cfg.channels, cfg.heads, cfg.n_rbf, cfg.cutoff, d["dtype"])
+    N, K = cfg.n, cfg.max_neighbors
+    # resident buffers
+    start = torch.empty(N, dtype=torch.int32, device=dev)
+    length = torch.empty(N, dtype=torch.int32, device=dev)
+    s0, l0, i0, nnz = B.e2v2_build_neighbors(d["pos"], cfg.cutoff, K)
+    cap = i0.numel()
+    idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    out = torch.empty(wl.h.shape, dtype=torch.float32, device=dev)
+    nws = torch.empty(B.load().e2v2_build_neighbors_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    aws = torch.empty(B.attn_workspace_bytes(desc, N), dtype=torch.uint8, device=dev)
+    lib = B.load()
+    stream = torch.cuda.current_stream()
+    import ctypes
+
+    def build():
+        if K > 0:
+            st = lib.e2v2_build_neighbors(B._ptr(d["pos"]), N, float(cfg.cutoff), K, B._ptr(start), B._ptr(length),
+                                          B._ptr(idx), cap, None, B._ptr(nws), nws.numel(), B._stream())
+            B._check(st)
+        else:   # CSR needs the nnz read-back (one host synchronisation)
+            n64 = ctypes.c_int64(0)
+            st = lib.e2v2_build_neighbors(B._ptr(d["pos"]), N, float(cfg.cutoff), 0, B._ptr(start), B._ptr(length),
+                                          B._ptr(idx), cap, ctypes.byref(n64), B._ptr(nws), nws.numel(), B._stream())
+            B._check(st)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for row in events:
+        for e in row:
+            e.record(stream)          # creates the underlying events
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        build()
+        B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], start, length, idx, out=out, workspace=aws,
+                            taps={"events": ev[1:]} if ev is not None else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stages = np.array([[events[k][a].elapsed_time(events[k][a + 1]) for a in range(5)] for k in range(args.steps)])
+    mean = stages.mean(axis=0)          # ms: neighbours, projections, source EAAS, attention, output projection
+    ms_step = wall * 1e3 / args.steps
+    nnz = int(length.sum().item())
+    ab = algorithmic_bytes(cfg, nnz)
+    t_attn = mean[3] * 1e-3
+    achieved = ab["total"] / t_attn / 1e9
+    traffic = measured_traffic(cfg.name)
+    layer_ms = float(mean[1:].sum())
+    C, nc, s = cfg.channels, cfg.n_comp, (2 if cfg.storage == "bf16" else 4)
+    nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
+    layer_bytes = (N * nc * C * s + N * C * 8 + N * nc * C * 4            # projections: h in; q, k, v out
+                   + N * nc * C * 4 + N * 12 + N * nc * C * s + N * (4 * nd + 16)   # source EAAS
+                   + ab["total"]                                          # streaming attention + target EAAS
+                   + 2 * N * nc * C * 4)                                  # output projection
+
+    rec = {
+        "metric": METRIC,
+        "value": nnz / (ms_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {N} atoms, {cfg.geometry} at {cfg.density} atoms/A^3, cutoff {cfg.cutoff} A, "
+                        f"cap K={K}, l_max={cfg.lmax}, C={cfg.channels}, {cfg.heads} heads, {cfg.n_rbf} RBFs, "
+                        f"{cfg.storage} storage, fp32 arithmetic",
+            "nnz": nnz,
+            "steps_per_s": 1e3 / ms_step,
+            "stage_ms": {"neighbours": float(mean[0]), "projections": float(mean[1]), "source_eaas": float(mean[2]),
+                         "attention": float(mean[3]), "output_projection": float(mean[4])},
+            "layer_ms_excl_neighbours": layer_ms,
+            "layer_pairs_per_s_excl_neighbours": nnz / (layer_ms * 1e-3),
+            "layer_hbm_frac_excl_neighbours": layer_bytes / (layer_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        },
+        "roofline": {
+            "kernel": "attn_kernel (fused streaming attention + target EAAS)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab["total"],
+            "bytes_per_pair": ab["per_pair"],
+            "bytes_per_target": ab["per_node"],
+            "avg_launch_ms": float(mean[3]),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * e2v2.h -- C ABI of an MI355X (gfx950) implementation of one E2Former-V2-style
+ * node-centric equivariant neighbour-attention layer forward.
+ *
+ * The layer (E2Former-V2 explainer, "E2Former-V2: breaking the computational
+ * bottleneck of equivariant graph neural networks", sections 2-3):
+ *   1. neighbour list within a cutoff (section 3.2: one target per work item,
+ *      padded neighbours masked; section 5.2: verify the list);
+ *   2. per-node projections q = h^0 W_Q, k = h^0 W_K, v^l = h^l W_V[l];
+ *   3. source pre-coupling h'_j = v_j (x) Y(r_j) computed with EAAS
+ *      (section 2.1 alignment rotation, section 2.2 sparse m re-index with the
+ *      even/odd sign rule, section 2.3 Proposition 4.3 exactness);
+ *   4. streaming aggregation m_i = sum_j alpha_ij h'_j with an online softmax
+ *      over q_i . k_j / sqrt(d) plus a Gaussian-RBF x cosine-envelope distance
+ *      bias (section 3.1, section 3.2 Algorithm 1; the bias follows the
+ *      FlashSchNet page, section 2.1);
+ *   5. target coupling hhat_i = m_i (x) Y(r_i) (section 3.1);
+ *   6. output projection out^l = hhat^l W_O[l].
+ *
+ * Conventions shared by every entry point
+ *   - Features are [n][(lmax+1)^2][C], channels fastest; component index of
+ *     (l, m) is l*l + l + m, m = -l..l.  Real spherical harmonics of the unit
+ *     direction, "component" normalised (sum_m Y_lm^2 = 2l+1, Y_00 = 1), real
+ *     form of the complex Condon-Shortley harmonics: Y_1 = sqrt(3) (y, z, x).
+ *   - Tensor-product paths (l_in, l_filter, l_out), all l <= lmax with
+ *     |l_in - l_f| <= l_out <= l_in + l_f, ordered l_out, then l_in, then l_f
+ *     (e2v2_path_table).  Path weights are per path and per channel.
+ *   - Position vectors are taken from the coordinate origin.  A zero position
+ *     has no direction: its encoding is Y_0 = 1, Y_{l>0} = 0.
+ *   - Head h owns channels [h*C/H, (h+1)*C/H) in every component.
+ *   - Pointers named "device" are device memory owned by the caller; the
+ *     library allocates no device memory and keeps no per-call state.  Every
+ *     device pointer must be 16-byte aligned.
+ *   - Every call enqueues work on `stream` and returns without waiting, except
+ *     where a function says it synchronises.
+ *   - Errors are returned as status codes; nothing is enqueued when a call
+ *     returns an argument error.  e2v2_last_error() gives a thread-local
+ *     message for the last failing call on the calling thread.
+ */
+#ifndef E2V2_H
+#define E2V2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    E2V2_OK = 0,
+    E2V2_ERR_ARG = 1,          /* invalid argument, detected before enqueueing anything        */
+    E2V2_ERR_CAPACITY = 2,     /* neighbour storage too small; *nnz_host holds the need          */
+    E2V2_ERR_UNSUPPORTED = 3,  /* valid but not implemented shape (e.g. channels per head != 8) */
+    E2V2_ERR_HIP = 4           /* a HIP runtime call failed; see e2v2_last_error()               */
+} e2v2_status;
+
+typedef enum { E2V2_FP32 = 0, E2V2_BF16 = 1 } e2v2_dtype;
+
+/* One attention layer.  Supported: lmax 0..3; heads 4, 8 or 16 with exactly
+ * 8 channels per head (channels = 8 * heads); n_rbf 2..64; cutoff > 0. */
+typedef struct {
+    int32_t lmax;
+    int32_t channels;
+    int32_t heads;
+    int32_t n_rbf;
+    float cutoff;        /* Angstrom; also the RBF range and the envelope's zero */
+    int32_t storage;     /* e2v2_dtype of h, W_Q, W_K, W_V and W_O.  The coupled values h'
+                            are kept in the workspace as fp32 (fp32 storage) or, for bf16
+                            storage, as fp16 with one power-of-two scale per node */
+} e2v2_layer_desc;
+
+/* Layer weights (device pointers).
+ *   w_q, w_k : [C][C] storage dtype, (in, out) row-major: q = h^0 @ w_q
+ *   w_v, w_o : [lmax+1][C][C] storage dtype, one (in, out) matrix per l
+ *   w_rbf    : [n_rbf][heads] fp32; bias_h(d) = f_c(d) sum_k w_rbf[k][h] phi_k(d),
+ *              phi_k(d) = exp(-(d - mu_k)^2 / (2 D^2)), mu_k = k*cutoff/(n_rbf-1),
+ *              D = cutoff/(n_rbf-1), f_c(d) = (cos(pi d / cutoff) + 1) / 2
+ *   w_src, w_tgt : [n_paths(lmax)][C] fp32 per-path, per-channel weights of the
+ *              source and target tensor products */
+typedef struct {
+    const void *w_q, *w_k, *w_v, *w_o;
+    const float *w_rbf;
+    const float *w_src, *w_tgt;
+} e2v2_weights;
+
+/* Optional copies of the layer's intermediates (device pointers; any may be NULL)
+ * and optional stage timing.  Intended for validation and measurement;
+ * production callers pass NULL taps. */
+typedef struct {
+    float *q;        /* [n][C] fp32                                         */
+    float *k;        /* [n][C] fp32                                         */
+    float *v;        /* [n][(lmax+1)^2][C] fp32                             */
+    float *hprime;   /* [n][(lmax+1)^2][C] fp32: h' as the streaming kernel reads it
+                        (for bf16 storage: its 16-bit form times the node's scale) */
+    float *m;        /* [n][(lmax+1)^2][C] fp32 aggregated message (step 4) */
+    float *hhat;     /* [n][(lmax+1)^2][C] fp32 target-coupled message (step 5) */
+    hipEvent_t *events;  /* host array of 5 caller-created events or NULL: recorded on
+                            `stream` before step 2, after step 2, after step 3, after
+                            steps 4-5 (the streaming kernel) and after step 6 */
+} e2v2_taps;
+
+/* ------------------------------------------------------------------------
+ * Neighbour list (cell list).  E2Former-V2 explainer section 3.2 (neighbour
+ * cap with masked padding), section 5.2 (verify the list); Tessera article
+ * (neighbour topology reused between rebuilds).
+ *
+ * For target i the neighbour set is every j != i with d2 < cutoff^2, where
+ * dx = (double)pos[j].x - (double)pos[i].x (likewise y, z) and
+ * d2 = (dx*dx + dy*dy) + dz*dz, each operation rounded separately in fp64.
+ *   max_neighbors == 0 : CSR.  nbr_start[i] is the exclusive prefix sum of
+ *                        nbr_len; nbr_idx holds nnz entries.  Synchronises
+ *                        `stream` once to read nnz; *nnz_host receives it.
+ *                        If nnz > capacity, returns E2V2_ERR_CAPACITY with
+ *                        *nnz_host = nnz and leaves the outputs undefined.
+ *   max_neighbors == K : row i lives at nbr_idx[i*K .. i*K+K); the K nearest
+ *                        by (d2, j) are kept when more qualify; entries past
+ *                        nbr_len[i] are -1.  nbr_start[i] = i*K.  capacity must
+ *                        be >= n*K.  Does not synchronise unless nnz_host is
+ *                        non-NULL (then it waits and stores sum(nbr_len)).
+ * Rows are sorted by j ascending.  Results are deterministic.
+ *   pos          device [n][3] fp32 (the positions' fp32 values are the truth)
+ *   nbr_start    device [n] int32;  nbr_len device [n] int32
+ *   nbr_idx      device [capacity] int32
+ *   nnz_host     host, may be NULL for K > 0; required for K == 0
+ *   workspace    device scratch of at least
+ *                e2v2_build_neighbors_workspace_bytes(n, max_neighbors) bytes
+ * Limits: 0 <= n < 2^31 - 1, cutoff > 0 finite, 0 <= K <= 4096, total entries
+ * < 2^31.  Non-finite coordinates never fault; such atoms get no neighbours. */
+e2v2_status e2v2_build_neighbors(const float *pos, int32_t n, float cutoff, int32_t max_neighbors,
+                                 int32_t *nbr_start, int32_t *nbr_len, int32_t *nbr_idx,
+                                 int64_t capacity, int64_t *nnz_host,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t e2v2_build_neighbors_workspace_bytes(int32_t n, int32_t max_neighbors);
+
+/* ------------------------------------------------------------------------
+ * EAAS tensor product of features with the encoding of each node's position
+ * (explainer section 2.1 pseudocode eaas_forward(h, r_vec); section 2.2 sparse
+ * re-index; section 2.3 Proposition 4.3):
+ *   y^{l_o}[n][m_o][c] = sum_p path_w[p][c] (x_n (x) Y(r_n))^{(l_i,l_f,l_o)}_{m_o,c}
+ * equal to the dense Clebsch-Gordan product, evaluated as: rotate x into the
+ * frame whose z axis is r_n, re-index m with the even/odd rule (only the
+ * m_f = 0 encoding entry is non-zero there), rotate back.
+ *   pos     device [n][3] fp32;  x device [n][(lmax+1)^2][C] in x_dtype
+ *   path_w  device [n_paths(lmax)][C] fp32
+ *   y       device [n][(lmax+1)^2][C] in y_dtype (fp32, or bf16 rounded to nearest even)
+ * Limits: lmax 0..3, 1 <= channels <= 256, channels % 8 == 0. */
+e2v2_status e2v2_eaas_couple(const float *pos, const void *x, e2v2_dtype x_dtype, const float *path_w,
+                             int32_t n, int32_t lmax, int32_t channels,
+                             void *y, e2v2_dtype y_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * One attention layer forward (steps 2-6 above) over a given neighbour list
+ * (the format e2v2_build_neighbors writes: target i reads
+ * nbr_idx[nbr_start[i] .. nbr_start[i] + nbr_len[i])).  Entries outside
+ * [0, n) are skipped, so -1 padding inside a row is harmless.  A target with
+ * no neighbours gets m = 0 and therefore out = 0.
+ *   h    device [n][(lmax+1)^2][C] storage dtype
+ *   out  device [n][(lmax+1)^2][C] fp32
+ *   workspace  device scratch of at least e2v2_attn_workspace_bytes(desc, n)
+ * No N x K tensor is formed: the streaming kernel reads each neighbour's key
+ * and coupled value once per target and accumulates on chip. */
+e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, const void *h,
+                              const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
+                              const int32_t *nbr_idx, int32_t n, float *out,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Same as e2v2_attn_forward, also copying intermediates into `taps` (host
+ * pointer to a struct of device pointers; NULL behaves like e2v2_attn_forward). */
+e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos, const void *h,
+                                   const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
+                                   const int32_t *nbr_idx, int32_t n, float *out,
+                                   void *workspace, size_t workspace_bytes, const e2v2_taps *taps,
+                                   hipStream_t stream);
+size_t e2v2_attn_workspace_bytes(const e2v2_layer_desc *desc, int32_t n);
+
+/* ------------------------------------------------------------------------
+ * Host-side tables (no GPU needed). */
+int32_t e2v2_num_paths(int32_t lmax);   /* 1, 5, 15, 34 for lmax 0..3; -1 if out of range */
+/* li_lf_lo: host [n_paths][3]. */
+e2v2_status e2v2_path_table(int32_t lmax, int32_t *li_lf_lo);
+/* EAAS coefficients used by the kernels: coef host [n_paths][7]; entry
+ * [p][m_o + l_o] multiplies input m_i = m_o (even l_i+l_f+l_o) or m_i = -m_o
+ * (odd) of the aligned-frame features; it equals sqrt(2 l_f + 1) times the
+ * real coupling tensor at (m_i, m_f = 0, m_o).  Unused slots are 0. */
+e2v2_status e2v2_eaas_coefficients(int32_t lmax, float *coef);
+/* Real Wigner-D blocks D^l(R), l = 1..lmax, of the alignment rotation of r
+ * (R z = r / |r|; the rotation is R_z(alpha) R_y(beta) with no roll), row-major,
+ * concatenated; Y^l(R x) = D^l(R) Y^l(x).  Host reference of what the kernels
+ * compute per node, fp64.  d: host [sum_{l=1..lmax} (2l+1)^2]. */
+e2v2_status e2v2_alignment_wigner(int32_t lmax, const double *r, double *d);
+
+const char *e2v2_status_string(e2v2_status s);
+const char *e2v2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* E2V2_H */

@@ -1,0 +1,114 @@
+"""Whole-layer parity of e2v2_attn_forward against the fp64 oracle, step by step
+(q, k, v, h', m, hhat, out), on the seeded workloads, plus edge cases.
+
+Tolerance: max |gpu - oracle| / RMS(oracle) <= 1e-4 for fp32 storage and
+<= 2e-2 for bf16 storage with fp32 accumulation.  Full-size workloads compare a
+sample of targets that the oracle evaluates one by one, with the same kernels
+and launch configuration as the benchmark."""
+import numpy as np
+import pytest
+import torch
+
+from atomistic_attention_amd import workloads as W
+from oracle import layer as O
+from tests._helpers import bf16_close, csr_from_rows, f32, record, rel_err, tolerance, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _desc(gpu_lib, wl, dt):
+    c = wl.cfg
+    return gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, dt)
+
+
+def _run(gpu_lib, wl, nbr=None, taps=False):
+    c = wl.cfg
+    d = upload(wl)
+    if nbr is None:
+        s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors)
+    else:
+        s, ln, ix = nbr
+    tp = None
+    if taps:
+        N, NC, C = c.n, c.n_comp, c.channels
+        z = lambda *sh, dt=torch.float32: torch.empty(sh, dtype=dt, device="cuda")
+        tp = dict(q=z(N, C), k=z(N, C), v=z(N, NC, C), hprime=z(N, NC, C), m=z(N, NC, C),
+                  hhat=z(N, NC, C))
+    out = gpu_lib.e2v2_attn_forward(_desc(gpu_lib, wl, d["dtype"]), d["pos"], d["h"], d["weights"], s, ln, ix,
+                                    taps=tp)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), ({k: v.float().cpu().numpy() for k, v in tp.items()} if tp else None)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_layer_full_fp32(gpu_lib, name):
+    wl = W.make_workload(name)
+    out, taps = _run(gpu_lib, wl, taps=True)
+    ref = O.layer_forward_workload(wl)
+    src = ref["src"]
+    e = dict(q=rel_err(taps["q"], ref["q"]), k=rel_err(taps["k"][src], ref["k"]),
+             v=rel_err(taps["v"][src], ref["v"]), hprime=rel_err(taps["hprime"][src], ref["hprime"]),
+             m=rel_err(taps["m"], ref["m"]), hhat=rel_err(taps["hhat"], ref["hhat"]), out=rel_err(out, ref["out"]))
+    record(f"layer_full[{name}]", **e)
+    assert e["q"] < 1e-5 and e["k"] < 1e-5 and e["v"] < 1e-5 and e["hprime"] < 1e-5
+    assert e["m"] < 1e-4 and e["hhat"] < 1e-4
+    assert e["out"] < tolerance(wl)
+
+
+@pytest.mark.parametrize("name,ntarget", [("c3", 96), ("c3b", 64), ("c4", 48), ("c5", 48)])
+def test_layer_sampled_bf16(gpu_lib, name, ntarget):
+    wl = W.make_workload(name)
+    out, taps = _run(gpu_lib, wl, taps=True)
+    rng = np.random.default_rng(7)
+    tg = np.sort(rng.choice(wl.cfg.n, ntarget, replace=False))
+    ref = O.layer_forward_workload(wl, targets=tg)
+    src = ref["src"]
+    e = dict(q=rel_err(taps["q"][tg], ref["q"]), v=rel_err(taps["v"][src], ref["v"]),
+             hprime=rel_err(taps["hprime"][src], ref["hprime"]), m=rel_err(taps["m"][tg], ref["m"]),
+             hhat=rel_err(taps["hhat"][tg], ref["hhat"]), out=rel_err(out[tg], ref["out"]))
+    record(f"layer_sampled[{name}]", **e)
+    assert e["q"] < 1e-5 and e["v"] < 1e-5
+    assert bf16_close(taps["hprime"][src], ref["hprime"])          # one bf16 store of h'
+    assert e["m"] < tolerance(wl) and e["hhat"] < tolerance(wl)
+    assert e["out"] < tolerance(wl)
+
+
+def _small(n, L, heads, storage, seed, side=14.0, cutoff=4.5, nrbf=10):
+    cfg = W.LayerConfig("edge", n, "uniform", n / side ** 3, cutoff, 0, L, 8 * heads, heads, nrbf, storage, seed)
+    return W.make_workload(cfg)
+
+
+@pytest.mark.parametrize("L,heads,storage", [(0, 16, "fp32"), (1, 8, "fp32"), (3, 4, "fp32"), (2, 8, "bf16")])
+def test_layer_small_shapes(gpu_lib, L, heads, storage):
+    wl = _small(173, L, heads, storage, 50 + L)
+    out, _ = _run(gpu_lib, wl)
+    ref = O.layer_forward_workload(wl)
+    assert rel_err(out, ref["out"]) < tolerance(wl)
+
+
+def test_isolated_atoms_and_padding(gpu_lib):
+    wl = _small(90, 2, 16, "fp32", 3)
+    wl.pos[5] = [500.0, 0, 0]            # isolated: m = 0 so out = 0
+    wl.pos[6] = [0.0, 0.0, 0.0]          # zero position vector (no direction)
+    rows = O.neighbors(wl.pos, wl.cfg.cutoff)
+    assert rows[5].size == 0
+    ref = O.layer_forward_workload(wl, rows=rows)
+    # the same lists with -1 entries and out-of-range indices mixed in: they are skipped
+    rng = np.random.default_rng(0)
+    padded = []
+    for r in rows:
+        r = list(r)
+        for _ in range(rng.integers(0, 4)):
+            r.insert(int(rng.integers(0, len(r) + 1)), int(rng.choice([-1, 90, 10 ** 6])))
+        padded.append(np.array(r, dtype=np.int32))
+    for lst in (rows, padded):
+        out, _ = _run(gpu_lib, wl, nbr=csr_from_rows(lst))
+        assert np.all(out[5] == 0.0)
+        assert rel_err(out, ref["out"]) < 1e-4
+
+
+def test_layer_deterministic(gpu_lib):
+    wl = W.make_workload("c3", n=4000)
+    a, _ = _run(gpu_lib, wl)
+    b, _ = _run(gpu_lib, wl)
+    assert np.array_equal(a, b)

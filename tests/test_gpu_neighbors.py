@@ -1,0 +1,103 @@
+"""GPU neighbour lists against the oracle's brute-force search: bit-exact rows
+(lengths and indices) on every workload, determinism and edge cases."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from atomistic_attention_amd import workloads as W
+from oracle import layer as O
+from tests._helpers import f32, rows_from_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare(rows_gpu, rows_ref):
+    assert len(rows_gpu) == len(rows_ref)
+    for i, (a, b) in enumerate(zip(rows_gpu, rows_ref)):
+        if not np.array_equal(a, b):
+            raise AssertionError(f"row {i}: gpu {a[:12]}... ({a.size}) vs oracle {b[:12]}... ({b.size})")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_neighbors_bit_exact(gpu_lib, name):
+    wl = W.make_workload(name)
+    c = wl.cfg
+    pos = f32(wl.pos)
+    start, length, idx, nnz = gpu_lib.e2v2_build_neighbors(pos, c.cutoff, c.max_neighbors)
+    torch.cuda.synchronize()
+    ref = O.neighbors(wl.pos, c.cutoff, c.max_neighbors)
+    _compare(rows_from_device(start, length, idx), ref)
+    assert nnz == sum(r.size for r in ref)
+    if c.max_neighbors > 0:
+        K = c.max_neighbors
+        assert np.array_equal(start.cpu().numpy(), np.arange(c.n) * K)
+        full = idx.view(c.n, K).cpu().numpy()
+        ln = length.cpu().numpy()
+        for i in range(0, c.n, max(1, c.n // 500)):
+            assert np.all(full[i, ln[i]:] == -1)
+
+
+def test_neighbors_deterministic(gpu_lib):
+    wl = W.make_workload("c5", n=30000)
+    pos = f32(wl.pos)
+    a = gpu_lib.e2v2_build_neighbors(pos, 8.0, 256)
+    b = gpu_lib.e2v2_build_neighbors(pos, 8.0, 256)
+    torch.cuda.synchronize()
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+
+
+def test_cap_ties_break_by_index(gpu_lib):
+    # cubic lattice: exact distance ties at 1 and sqrt(2); K = 10 keeps the six at 1
+    # and the four lowest-index atoms at sqrt(2)
+    g = np.arange(6, dtype=np.float64)
+    pos = np.stack(np.meshgrid(g, g, g, indexing="ij"), -1).reshape(-1, 3)
+    perm = np.random.default_rng(4).permutation(pos.shape[0])
+    pos = pos[perm]
+    for K in (10, 3, 0):
+        s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(f32(pos), 1.5, K)
+        torch.cuda.synchronize()
+        _compare(rows_from_device(s, ln, ix), O.neighbors(pos, 1.5, K))
+
+
+def test_edge_geometries(gpu_lib):
+    rng = np.random.default_rng(1)
+    cases = {
+        "single": np.zeros((1, 3)),
+        "coincident": np.tile([[1.5, -2.0, 0.25]], (40, 1)),
+        "isolated": np.array([[0, 0, 0], [100, 0, 0], [0, 250, 0], [0.5, 0, 0]], dtype=np.float64),
+        "flat": np.c_[rng.uniform(-20, 20, (500, 2)), np.zeros(500)],
+        "line": np.c_[np.zeros(300), np.zeros(300), rng.uniform(0, 90, 300)],
+        "sparse_far": np.r_[rng.uniform(-5, 5, (200, 3)), rng.uniform(1e5, 1.00001e5, (50, 3))],
+        "nonfinite": np.r_[rng.uniform(-6, 6, (300, 3)), [[np.nan, 0, 0], [np.inf, 1, 1], [0, -np.inf, 2]]],
+    }
+    for name, p in cases.items():
+        p32 = p.astype(np.float32).astype(np.float64)
+        for K in (0, 4):
+            s, ln, ix, nnz = gpu_lib.e2v2_build_neighbors(f32(p32), 2.5, K)
+            torch.cuda.synchronize()
+            ref = O.neighbors(p32, 2.5, K)
+            try:
+                _compare(rows_from_device(s, ln, ix), ref)
+            except AssertionError as e:
+                raise AssertionError(f"{name} K={K}: {e}")
+
+
+def test_capacity_error_reports_need(gpu_lib):
+    lib = gpu_lib.load()
+    wl = W.make_workload("c2")
+    pos = f32(wl.pos)
+    n = wl.cfg.n
+    start = torch.empty(n, dtype=torch.int32, device="cuda")
+    ln = torch.empty(n, dtype=torch.int32, device="cuda")
+    idx = torch.empty(16, dtype=torch.int32, device="cuda")
+    ws = torch.empty(lib.e2v2_build_neighbors_workspace_bytes(n, 0), dtype=torch.uint8, device="cuda")
+    nnz = ctypes.c_int64(-1)
+    st = lib.e2v2_build_neighbors(ctypes.c_void_p(pos.data_ptr()), n, 5.0, 0, ctypes.c_void_p(start.data_ptr()),
+                                  ctypes.c_void_p(ln.data_ptr()), ctypes.c_void_p(idx.data_ptr()), 16,
+                                  ctypes.byref(nnz), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == gpu_lib.E2V2_ERR_CAPACITY
+    assert nnz.value == sum(r.size for r in O.neighbors(wl.pos, 5.0))

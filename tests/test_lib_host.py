@@ -1,0 +1,140 @@
+"""Host-side checks of the HIP library that need no GPU: it loads, exports every
+symbol include/e2v2.h declares, its tables agree with the oracle, and argument
+errors are reported before anything is enqueued."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from atomistic_attention_amd import binding as B
+from atomistic_attention_amd import workloads as W
+from oracle import so3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: errors come first
+FAKE_MIS = ctypes.c_void_p(0x10004)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "e2v2.h")).read()
+    declared = set(re.findall(r"\b(e2v2_[a-z_]+)\s*\(", hdr))
+    assert declared == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_path_table_matches(lib):
+    for L in range(4):
+        assert B.e2v2_path_table(L) == so3.paths(L) == W.path_list(L)
+        assert B.e2v2_num_paths(L) == len(so3.paths(L))
+    assert B.e2v2_num_paths(4) == -1
+
+
+def test_eaas_coefficients_match_oracle(lib):
+    for L in range(4):
+        c = B.e2v2_eaas_coefficients(L)
+        for p, (li, lf, lo) in enumerate(so3.paths(L)):
+            E = math.sqrt(2 * lf + 1) * so3.coupling_tensor(li, lf, lo)[:, lf, :]
+            odd = (li + lf + lo) % 2 == 1
+            for mo in range(-lo, lo + 1):
+                mi = -mo if odd else mo
+                ref = E[mi + li, mo + lo] if abs(mi) <= li else 0.0
+                assert abs(c[p, mo + lo] - ref) < 3e-7, (L, li, lf, lo, mo)
+
+
+def test_alignment_wigner_matches_oracle(lib):
+    rng = np.random.default_rng(8)
+    for r in list(rng.standard_normal((6, 3))) + [np.array([0, 0, -3.0]), np.array([0, 0, 1e-3])]:
+        D = B.e2v2_alignment_wigner(3, r)
+        R = so3.alignment_rotation(r)
+        for l in range(1, 4):
+            assert np.max(np.abs(D[l - 1] - so3.wigner_d(R, l))) < 1e-12
+
+
+def _desc(**kw):
+    d = dict(lmax=2, channels=128, heads=16, n_rbf=32, cutoff=5.0, storage=B.E2V2_BF16)
+    d.update(kw)
+    return B.LayerDesc(d["lmax"], d["channels"], d["heads"], d["n_rbf"], d["cutoff"], d["storage"])
+
+
+def _attn(lib, desc, n=10, ws_bytes=None, ptr=FAKE, weights=None):
+    w = weights or B.Weights(*([ptr] * 7))
+    if ws_bytes is not None:
+        wsb = ws_bytes
+    elif desc is not None:
+        wsb = lib.e2v2_attn_workspace_bytes(ctypes.byref(desc), max(n, 0))
+    else:
+        wsb = 1 << 20
+    return lib.e2v2_attn_forward(ctypes.byref(desc) if desc is not None else None, ptr, ptr, ctypes.byref(w),
+                                 ptr, ptr, ptr, n, ptr, ptr, wsb, None)
+
+
+def test_attn_argument_errors(lib):
+    assert _attn(lib, None) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(lmax=4)) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(lmax=-1)) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(channels=100)) == B.E2V2_ERR_ARG          # not a multiple of heads
+    assert _attn(lib, _desc(channels=256)) == B.E2V2_ERR_UNSUPPORTED  # 16 channels per head
+    assert _attn(lib, _desc(channels=16, heads=2)) == B.E2V2_ERR_UNSUPPORTED
+    assert _attn(lib, _desc(n_rbf=1)) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(n_rbf=65)) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(cutoff=0.0)) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(cutoff=float("nan"))) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(storage=7)) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(), n=-1) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(), ptr=FAKE_MIS) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(), ptr=None) == B.E2V2_ERR_ARG
+    assert _attn(lib, _desc(), ws_bytes=100) == B.E2V2_ERR_ARG
+    assert "workspace" in lib.e2v2_last_error().decode()
+    assert _attn(lib, _desc(), n=0) == B.E2V2_OK                       # nothing to do
+
+
+def test_workspace_sizes(lib):
+    d = _desc()
+    a, b = lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 1000), lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 2000)
+    assert 0 < a < b
+    # q, k fp32 + v fp32 + h' bf16 + D blocks + padded positions + hhat fp32 per node
+    per_node = 128 * 4 * 2 + 9 * 128 * 4 + 9 * 128 * 2 + 34 * 4 + 16 + 9 * 128 * 4
+    assert abs((b - a) / 1000 - per_node) < 2
+    assert lib.e2v2_build_neighbors_workspace_bytes(1000, 0) > 0
+
+
+def test_neighbor_argument_errors(lib):
+    nnz = ctypes.c_int64(0)
+    ws = lib.e2v2_build_neighbors_workspace_bytes(100, 16)
+    call = lambda n=100, rc=5.0, K=16, cap=1600, nz=ctypes.byref(nnz), wsb=ws, ptr=FAKE: lib.e2v2_build_neighbors(
+        ptr, n, rc, K, ptr, ptr, ptr, cap, nz, ptr, wsb, None)
+    assert call(n=-1) == B.E2V2_ERR_ARG
+    assert call(rc=0.0) == B.E2V2_ERR_ARG
+    assert call(rc=float("inf")) == B.E2V2_ERR_ARG
+    assert call(K=-2) == B.E2V2_ERR_ARG
+    assert call(K=5000) == B.E2V2_ERR_ARG
+    assert call(K=0, nz=None) == B.E2V2_ERR_ARG
+    assert call(cap=1599) == B.E2V2_ERR_ARG
+    assert call(wsb=10) == B.E2V2_ERR_ARG
+    assert call(ptr=FAKE_MIS) == B.E2V2_ERR_ARG
+    assert call(n=0) == B.E2V2_OK and nnz.value == 0
+
+
+def test_eaas_argument_errors(lib):
+    f = lambda L=2, C=128, dt=0, n=10, ptr=FAKE: lib.e2v2_eaas_couple(ptr, ptr, dt, ptr, n, L, C, ptr, 0, None)
+    assert f(L=4) == B.E2V2_ERR_ARG
+    assert f(C=12) == B.E2V2_ERR_ARG
+    assert f(C=512) == B.E2V2_ERR_ARG
+    assert f(dt=3) == B.E2V2_ERR_ARG
+    assert f(n=-1) == B.E2V2_ERR_ARG
+    assert f(ptr=FAKE_MIS) == B.E2V2_ERR_ARG
+    assert f(n=0) == B.E2V2_OK
+
+
+def test_status_strings(lib):
+    assert lib.e2v2_status_string(0) == b"ok"
+    assert lib.e2v2_status_string(2) == b"insufficient neighbour capacity"
