@@ -12,11 +12,13 @@
 //      even with rounding in the cell index) and holds at most n + 64 cells;
 //   2. cell index per atom + per-cell counts (integer atomics: counts are exact);
 //   3. exclusive scan of the counts; scatter atoms into cell order;
-//   4. one thread per target (targets taken in cell order, so neighbouring
-//      threads read the same cells) scans the 27 cells:
-//        K = 0: count -> scan -> fill -> sort row by j;
-//        K > 0: keep the K nearest by (d2, j) in a max-heap held in the row
-//               itself (d2 recomputed on demand), then sort by j, pad with -1.
+//   4. one wave per target (targets taken in cell order, so neighbouring waves
+//      read the same cells) scans the 27-cell stencil, compacts the pairs that
+//      pass into LDS and orders them there by rank counting:
+//        K = 0: count -> scan -> fill, rows sorted by j;
+//        K > 0: the K nearest by (d2, j), sorted by j, padded with -1.
+//      Rows with more candidates than the LDS buffer holds are finished by a
+//      per-thread kernel (a max-heap held in the row itself, then a heapsort).
 // Within-cell order depends on atomics, but rows are sets sorted by j and the
 // K-nearest choice uses a total order, so results are deterministic.
 #include "e2v2_internal.h"
@@ -230,20 +232,6 @@ __device__ __forceinline__ void for_each_neighbor(int i, double xi, double yi, d
     }
 }
 
-__global__ void k_count(int n, double rc2, const GridInfo *__restrict__ grid, const int32_t *__restrict__ cell_start,
-                        const int32_t *__restrict__ order, const float4 *__restrict__ spos, int32_t *nbr_len)
-{
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= n) return;
-    const GridInfo gi = *grid;
-    const float4 pi = spos[t];
-    const int i = order[t];
-    int cnt = 0;
-    for_each_neighbor(i, (double)pi.x, (double)pi.y, (double)pi.z, pi.x, pi.y, pi.z, rc2, gi, cell_start, spos,
-                      [&](int, double) { ++cnt; });
-    nbr_len[i] = cnt;
-}
-
 // In-place heapsort of ints ascending.
 __device__ inline void heapsort_int(int32_t *a, int len)
 {
@@ -264,15 +252,18 @@ __device__ inline void heapsort_int(int32_t *a, int len)
     }
 }
 
-__global__ void k_fill_csr(int n, double rc2, const GridInfo *__restrict__ grid, const int32_t *__restrict__ cell_start,
-                           const int32_t *__restrict__ order, const float4 *__restrict__ spos,
-                           const int32_t *__restrict__ nbr_start, int32_t *nbr_idx)
+// Per-thread fills for rows longer than the wave kernels' LDS buffer (kWaveCap).
+__global__ void k_fill_csr(int n, int cap, double rc2, const GridInfo *__restrict__ grid,
+                           const int32_t *__restrict__ cell_start, const int32_t *__restrict__ order,
+                           const float4 *__restrict__ spos, const int32_t *__restrict__ nbr_start,
+                           const int32_t *__restrict__ nbr_len, int32_t *nbr_idx)
 {
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n) return;
+    const int i = order[t];
+    if (nbr_len[i] <= cap) return;
     const GridInfo gi = *grid;
     const float4 pi = spos[t];
-    const int i = order[t];
     int32_t *row = nbr_idx + nbr_start[i];
     int cnt = 0;
     for_each_neighbor(i, (double)pi.x, (double)pi.y, (double)pi.z, pi.x, pi.y, pi.z, rc2, gi, cell_start, spos,
@@ -292,9 +283,10 @@ __global__ void k_fill_capped(int n, int K, double rc2, const float *__restrict_
 {
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n) return;
+    const int i = order[t];
+    if (nbr_len[i] != -1) return;                 // done by k_fill_capped_wave
     const GridInfo gi = *grid;
     const float4 pi = spos[t];
-    const int i = order[t];
     const double xi = pi.x, yi = pi.y, zi = pi.z;
     int32_t *row = nbr_idx + (size_t)i * K;
     // max-heap on (d2, j): row[0] is the farthest kept neighbour
@@ -339,6 +331,183 @@ __global__ void k_fill_capped(int n, int K, double rc2, const float *__restrict_
     nbr_start[i] = (int32_t)((size_t)i * K);
 }
 
+// ---------------------------------------------------------------- step 4, one wave per target
+// A wave scans its target's stencil 64 candidates at a time: for fixed (z, y) the
+// three x-neighbouring cells are adjacent in cell order, so the stencil is 9
+// contiguous ranges of the cell-sorted arrays.  Passing candidates are compacted
+// into LDS (ballot + prefix count) and ordered there by rank counting: the rank
+// of an element is the number of elements with a smaller key, which gives every
+// element its final slot without any data movement between lanes.  Rows longer
+// than the LDS buffer are marked and left to the per-thread kernels above.
+constexpr int kWaveCap = 1024;                 // candidates a wave can hold in LDS
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Number of neighbours of the target at cell-order slot t; with COLLECT the first
+// kWaveCap of them land in cj / cd (unordered).  Returns a wave-uniform count.
+template <bool COLLECT>
+__device__ __forceinline__ int wave_scan(int i, float4 pi, double rc2, const GridInfo &gi,
+                                         const int32_t *__restrict__ cell_start, const float4 *__restrict__ spos,
+                                         int32_t *cj, double *cd, int lane)
+{
+    const double xi = pi.x, yi = pi.y, zi = pi.z;
+    const int cx = cell_coord(pi.x, gi.lo[0], gi.inv[0], gi.dims[0]);
+    const int cy = cell_coord(pi.y, gi.lo[1], gi.inv[1], gi.dims[1]);
+    const int cz = cell_coord(pi.z, gi.lo[2], gi.inv[2], gi.dims[2]);
+    const int x0 = cx > 0 ? cx - 1 : 0, x1 = cx + 1 < gi.dims[0] ? cx + 1 : gi.dims[0] - 1;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    int count = 0;
+    for (int z = cz - 1; z <= cz + 1; ++z) {
+        if (z < 0 || z >= gi.dims[2]) continue;
+        for (int y = cy - 1; y <= cy + 1; ++y) {
+            if (y < 0 || y >= gi.dims[1]) continue;
+            const int rowc = (z * gi.dims[1] + y) * gi.dims[0];
+            const int s0 = cell_start[rowc + x0], s1 = cell_start[rowc + x1 + 1];
+            for (int base = s0; base < s1; base += 64) {
+                const int sidx = base + lane;
+                bool pass = false;
+                int j = -1;
+                double d2 = 0.0;
+                if (sidx < s1) {
+                    const float4 pj = spos[sidx];
+                    j = __float_as_int(pj.w);
+                    if (j != i) {
+                        d2 = pair_d2(xi, yi, zi, pj);
+                        pass = d2 < rc2;
+                    }
+                }
+                const uint64_t m = __ballot(pass);
+                if (COLLECT && pass) {
+                    const int slot = count + __popcll(m & below);
+                    if (slot < kWaveCap) {
+                        cj[slot] = j;
+                        cd[slot] = d2;
+                    }
+                }
+                count += __popcll(m);
+            }
+        }
+    }
+    return count;
+}
+
+// row[rank by j] = j for the first cnt entries of cj (distinct j).
+__device__ __forceinline__ void wave_write_sorted(const int32_t *cj, int cnt, int32_t *row, int lane)
+{
+    for (int e0 = 0; e0 < cnt; e0 += 64) {
+        const int e = e0 + lane;
+        const int je = e < cnt ? cj[e] : INT_MAX;
+        int r = 0;
+        for (int t = 0; t < cnt; ++t) r += cj[t] < je ? 1 : 0;
+        if (e < cnt) row[r] = je;
+    }
+}
+
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_count_wave(int n, double rc2, const GridInfo *__restrict__ grid,
+                                                                    const int32_t *__restrict__ cell_start,
+                                                                    const int32_t *__restrict__ order,
+                                                                    const float4 *__restrict__ spos, int32_t *nbr_len)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)));
+    if (t >= n) return;
+    const GridInfo gi = *grid;
+    const int i = order[t];
+    const int cnt = wave_scan<false>(i, spos[t], rc2, gi, cell_start, spos, nullptr, nullptr, lane);
+    if (lane == 0) nbr_len[i] = cnt;
+}
+
+// CSR rows of at most kWaveCap entries (longer rows: k_fill_csr_long).
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, double rc2, const GridInfo *__restrict__ grid,
+                                                                       const int32_t *__restrict__ cell_start,
+                                                                       const int32_t *__restrict__ order,
+                                                                       const float4 *__restrict__ spos,
+                                                                       const int32_t *__restrict__ nbr_start,
+                                                                       const int32_t *__restrict__ nbr_len, int32_t *nbr_idx)
+{
+    __shared__ int32_t sj[kWavesPerBlock][kWaveCap];
+    __shared__ double sd[kWavesPerBlock][kWaveCap];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerBlock + w));
+    if (t >= n) return;
+    const int i = order[t];
+    if (nbr_len[i] > kWaveCap) return;
+    const GridInfo gi = *grid;
+    const int cnt = wave_scan<true>(i, spos[t], rc2, gi, cell_start, spos, sj[w], sd[w], lane);
+    wave_lds_sync();
+    wave_write_sorted(sj[w], cnt, nbr_idx + nbr_start[i], lane);
+}
+
+// Capped rows: keep the K nearest by (d2, j), written sorted by j and padded with -1.
+// Targets with more than kWaveCap candidates get nbr_len = -1 for k_fill_capped.
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n, int K, double rc2,
+                                                                          const GridInfo *__restrict__ grid,
+                                                                          const int32_t *__restrict__ cell_start,
+                                                                          const int32_t *__restrict__ order,
+                                                                          const float4 *__restrict__ spos,
+                                                                          int32_t *nbr_start, int32_t *nbr_len,
+                                                                          int32_t *nbr_idx)
+{
+    __shared__ int32_t sj[kWavesPerBlock][kWaveCap];
+    __shared__ double sd[kWavesPerBlock][kWaveCap];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerBlock + w));
+    if (t >= n) return;
+    const int i = order[t];
+    const GridInfo gi = *grid;
+    int32_t *cj = sj[w];
+    double *cd = sd[w];
+    const int cnt = wave_scan<true>(i, spos[t], rc2, gi, cell_start, spos, cj, cd, lane);
+    int32_t *row = nbr_idx + (size_t)i * K;
+    if (lane == 0) nbr_start[i] = (int32_t)((size_t)i * K);
+    if (cnt > kWaveCap) {
+        if (lane == 0) nbr_len[i] = -1;
+        return;
+    }
+    wave_lds_sync();
+    int len = cnt;
+    if (cnt <= K) {
+        wave_write_sorted(cj, cnt, row, lane);
+    } else {
+        // (d2, j) rank of every candidate; the K smallest go to slots 0..K-1 of kj
+        int rk[kWaveCap / 64];
+#pragma unroll
+        for (int c = 0; c < kWaveCap / 64; ++c) {
+            rk[c] = K;
+            const int e = c * 64 + lane;
+            if (c * 64 < cnt) {
+                const double de = e < cnt ? cd[e] : INFINITY;
+                const int je = e < cnt ? cj[e] : INT_MAX;
+                int r = 0;
+                for (int tt = 0; tt < cnt; ++tt) {
+                    const double dt = cd[tt];
+                    const int jt = cj[tt];
+                    r += (dt < de || (dt == de && jt < je)) ? 1 : 0;
+                }
+                rk[c] = e < cnt ? r : K;
+            }
+        }
+        wave_lds_sync();
+        int32_t *kj = reinterpret_cast<int32_t *>(cd);   // the distances are no longer needed
+#pragma unroll
+        for (int c = 0; c < kWaveCap / 64; ++c) {
+            const int e = c * 64 + lane;
+            if (e < cnt && rk[c] < K) kj[rk[c]] = cj[e];
+        }
+        wave_lds_sync();
+        wave_write_sorted(kj, K, row, lane);
+        len = K;
+    }
+    for (int sidx = len + lane; sidx < K; sidx += 64) row[sidx] = -1;
+    if (lane == 0) nbr_len[i] = len;
+}
+
 // ---------------------------------------------------------------- host launchers
 static inline unsigned nblk(long long n, int b) { return (unsigned)((n + b - 1) / b); }
 
@@ -353,7 +522,8 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
     k_scatter<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_cur, L.order, L.spos);
     if (K == 0) {
         const double rc2 = (double)cutoff * (double)cutoff;
-        k_count<<<nblk(n, 128), 128, 0, stream>>>(n, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_len);
+        k_count_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(n, rc2, L.grid, L.cell_start, L.order,
+                                                                                L.spos, nbr_len);
     }
     return hipGetLastError();
 }
@@ -373,11 +543,17 @@ hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, v
 {
     NbrLayout L = nbr_layout(ws, n);
     const double rc2 = (double)cutoff * (double)cutoff;
-    if (K == 0)
-        k_fill_csr<<<nblk(n, 128), 128, 0, stream>>>(n, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_idx);
-    else
+    if (K == 0) {
+        k_fill_csr_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(
+            n, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
+        k_fill_csr<<<nblk(n, 128), 128, 0, stream>>>(n, kWaveCap, rc2, L.grid, L.cell_start, L.order, L.spos,
+                                                      nbr_start, nbr_len, nbr_idx);
+    } else {
+        k_fill_capped_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(
+            n, K, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
         k_fill_capped<<<nblk(n, 128), 128, 0, stream>>>(n, K, rc2, pos, L.grid, L.cell_start, L.order, L.spos,
                                                          nbr_start, nbr_len, nbr_idx);
+    }
     return hipGetLastError();
 }
 

@@ -72,10 +72,12 @@ def test_edge_geometries(gpu_lib):
         "line": np.c_[np.zeros(300), np.zeros(300), rng.uniform(0, 90, 300)],
         "sparse_far": np.r_[rng.uniform(-5, 5, (200, 3)), rng.uniform(1e5, 1.00001e5, (50, 3))],
         "nonfinite": np.r_[rng.uniform(-6, 6, (300, 3)), [[np.nan, 0, 0], [np.inf, 1, 1], [0, -np.inf, 2]]],
+        # rows longer than a wave's LDS buffer (1024 candidates) take the per-thread path
+        "dense_blob": np.r_[rng.uniform(-1, 1, (1300, 3)), rng.uniform(-20, 20, (400, 3))],
     }
     for name, p in cases.items():
         p32 = p.astype(np.float32).astype(np.float64)
-        for K in (0, 4):
+        for K in (0, 4, 256, 2000):
             s, ln, ix, nnz = gpu_lib.e2v2_build_neighbors(f32(p32), 2.5, K)
             torch.cuda.synchronize()
             ref = O.neighbors(p32, 2.5, K)
