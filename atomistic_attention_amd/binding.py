@@ -60,17 +60,17 @@ def load(path: str = LIB_PATH):
         raise RuntimeError(f"{path} is missing: build it with `python -m atomistic_attention_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    lib.e2v2_build_neighbors.argtypes = [vp, i32, f32, i32, vp, vp, vp, i64, ctypes.POINTER(i64), vp, sz, vp]
+    lib.e2v2_build_neighbors.argtypes = [vp, i32, f32, i32, vp, vp, vp, i64, ctypes.POINTER(i64), vp, vp, sz, vp]
     lib.e2v2_build_neighbors.restype = ctypes.c_int
     lib.e2v2_build_neighbors_workspace_bytes.argtypes = [i32, i32]
     lib.e2v2_build_neighbors_workspace_bytes.restype = sz
     lib.e2v2_eaas_couple.argtypes = [vp, vp, ctypes.c_int, vp, i32, i32, i32, vp, ctypes.c_int, vp]
     lib.e2v2_eaas_couple.restype = ctypes.c_int
-    lib.e2v2_attn_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, i32,
-                                      vp, vp, sz, vp]
+    lib.e2v2_attn_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, vp,
+                                      i32, vp, vp, sz, vp]
     lib.e2v2_attn_forward.restype = ctypes.c_int
     lib.e2v2_attn_forward_taps.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp,
-                                           i32, vp, vp, sz, ctypes.POINTER(Taps), vp]
+                                           vp, i32, vp, vp, sz, ctypes.POINTER(Taps), vp]
     lib.e2v2_attn_forward_taps.restype = ctypes.c_int
     lib.e2v2_attn_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32]
     lib.e2v2_attn_workspace_bytes.restype = sz
@@ -160,8 +160,10 @@ def e2v2_alignment_wigner(lmax: int, r):
 
 # ------------------------------------------------------------------ device calls
 def e2v2_build_neighbors(pos: torch.Tensor, cutoff: float, max_neighbors: int = 0, capacity: int | None = None,
-                         workspace: torch.Tensor | None = None, stream=None, want_nnz: bool = True):
-    """Neighbour list of pos [n, 3] fp32 (device).  Returns (start, len, idx, nnz)."""
+                         workspace: torch.Tensor | None = None, stream=None, want_nnz: bool = True,
+                         order_out: torch.Tensor | None = None):
+    """Neighbour list of pos [n, 3] fp32 (device).  Returns (start, len, idx, nnz).
+    order_out: optional int32 [n] device tensor receiving the cell-list order."""
     lib = load()
     _dev(pos, torch.float32, "pos")
     n = pos.shape[0]
@@ -180,7 +182,7 @@ def e2v2_build_neighbors(pos: torch.Tensor, cutoff: float, max_neighbors: int = 
         nnz = ctypes.c_int64(-1)
         st = lib.e2v2_build_neighbors(_ptr(pos), n, float(cutoff), max_neighbors, _ptr(start), _ptr(length),
                                       _ptr(idx), cap, ctypes.byref(nnz) if (want_nnz or max_neighbors == 0) else None,
-                                      _ptr(workspace), workspace.numel(), _stream(stream))
+                                      _ptr(order_out), _ptr(workspace), workspace.numel(), _stream(stream))
         if st == E2V2_ERR_CAPACITY and max_neighbors == 0:
             cap = int(nnz.value)
             continue
@@ -216,7 +218,8 @@ def attn_workspace_bytes(desc: LayerDesc, n: int) -> int:
 
 
 def e2v2_attn_forward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len, nbr_idx, out=None,
-                      workspace=None, taps: dict | None = None, stream=None) -> torch.Tensor:
+                      workspace=None, taps: dict | None = None, stream=None,
+                      target_order: torch.Tensor | None = None) -> torch.Tensor:
     """One layer forward.  weights: dict with w_q, w_k, w_v, w_o (storage dtype), w_rbf, w_src, w_tgt (fp32).
     taps: optional dict of preallocated device tensors among q, k, v, hprime, m, hhat, and
     "events": a list of 5 recorded-once torch.cuda.Event objects marking the stage boundaries."""
@@ -231,6 +234,8 @@ def e2v2_attn_forward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len
     _dev(h, sdt, "h")
     for t, nm in ((nbr_start, "nbr_start"), (nbr_len, "nbr_len"), (nbr_idx, "nbr_idx")):
         _dev(t, torch.int32, nm)
+    if target_order is not None:
+        _dev(target_order, torch.int32, "target_order")
     if out is None:
         out = torch.empty(h.shape, dtype=torch.float32, device=h.device)
     wsb = attn_workspace_bytes(desc, n)
@@ -239,8 +244,8 @@ def e2v2_attn_forward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len
     w = Weights(*(_ptr(weights[k]) for k in ("w_q", "w_k", "w_v", "w_o", "w_rbf", "w_src", "w_tgt")))
     if taps is None:
         st = lib.e2v2_attn_forward(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), _ptr(nbr_start),
-                                   _ptr(nbr_len), _ptr(nbr_idx), n, _ptr(out), _ptr(workspace), workspace.numel(),
-                                   _stream(stream))
+                                   _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), n, _ptr(out), _ptr(workspace),
+                                   workspace.numel(), _stream(stream))
     else:
         evs = taps.get("events")
         ev_arr = None
@@ -251,7 +256,7 @@ def e2v2_attn_forward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len
         tp = Taps(*(_ptr(taps.get(k)) for k in ("q", "k", "v", "hprime", "m", "hhat")),
                   ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
         st = lib.e2v2_attn_forward_taps(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), _ptr(nbr_start),
-                                        _ptr(nbr_len), _ptr(nbr_idx), n, _ptr(out), _ptr(workspace),
-                                        workspace.numel(), ctypes.byref(tp), _stream(stream))
+                                        _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), n, _ptr(out),
+                                        _ptr(workspace), workspace.numel(), ctypes.byref(tp), _stream(stream))
     _check(st)
     return out

@@ -98,8 +98,15 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
     constexpr int NPH = S / SP;
 
     const int lane = threadIdx.x & 63;
-    const int i = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+    // Workgroups are handed to the 8 XCDs round robin; give each XCD one contiguous
+    // run of target slots so that, with a spatial target order, the targets one
+    // XCD works on at a time are close together and share rows in its L2.
+    const int nb = gridDim.x, xcd = blockIdx.x & 7, kth = blockIdx.x >> 3;
+    const int lb = xcd * (nb >> 3) + (xcd < (nb & 7) ? xcd : (nb & 7)) + kth;
+    const int slot = __builtin_amdgcn_readfirstlane(lb * 4 + (int)(threadIdx.x >> 6));
     const int n = A.n;
+    int i = slot;
+    if (A.order && slot < n) i = __builtin_amdgcn_readfirstlane(A.order[slot]);
     const int h = lane % H, b = (lane / H) & 1, u = lane / (2 * H);
     const int kq = lane >> 4, pm = lane & 15;
     const int R = A.R;
@@ -113,7 +120,7 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
         sW[e] = (k < R) ? A.w_rbf[k * H + hh] : 0.f;
     }
     __syncthreads();
-    if (i >= n) return;                 // whole wave: i is wave-uniform
+    if (slot >= n || i < 0 || i >= n) return;             // whole wave: i is wave-uniform
 
     const float4 pi4 = A.pos4[i];
     const float4 qv = *reinterpret_cast<const float4 *>(A.q + (size_t)i * C + cb);

@@ -351,7 +351,7 @@ size_t e2v2_build_neighbors_workspace_bytes(int32_t n, int32_t max_neighbors)
 
 e2v2_status e2v2_build_neighbors(const float *pos, int32_t n, float cutoff, int32_t K, int32_t *nbr_start,
                                  int32_t *nbr_len, int32_t *nbr_idx, int64_t capacity, int64_t *nnz_host,
-                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
+                                 int32_t *order, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (n < 0 || n == INT32_MAX) return fail(E2V2_ERR_ARG, "n = %d out of range", n);
     if (!(cutoff > 0.f) || !std::isfinite(cutoff)) return fail(E2V2_ERR_ARG, "cutoff must be finite and > 0");
@@ -366,12 +366,13 @@ e2v2_status e2v2_build_neighbors(const float *pos, int32_t n, float cutoff, int3
         return E2V2_OK;
     }
     if (!pos || !nbr_start || !nbr_len || !nbr_idx || !workspace) return fail(E2V2_ERR_ARG, "NULL device pointer");
-    if (!aligned16(pos) || !aligned16(nbr_start) || !aligned16(nbr_len) || !aligned16(nbr_idx))
+    if (!aligned16(pos) || !aligned16(nbr_start) || !aligned16(nbr_len) || !aligned16(nbr_idx) ||
+        (order && !aligned16(order)))
         return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
     if (workspace_bytes < e2v2_build_neighbors_workspace_bytes(n, K))
         return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, e2v2_build_neighbors_workspace_bytes(n, K));
     void *ws = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
-    hipError_t e = launch_neighbors_count(pos, n, cutoff, K, ws, workspace_bytes, nbr_len, stream);
+    hipError_t e = launch_neighbors_count(pos, n, cutoff, K, ws, workspace_bytes, nbr_len, order, stream);
     if (e != hipSuccess) return hip_fail(e, "neighbour grid");
     if (K == 0) {
         int64_t *nnz_dev = neighbors_nnz_slot(ws, n);
@@ -430,8 +431,9 @@ size_t e2v2_attn_workspace_bytes(const e2v2_layer_desc *desc, int32_t n)
 
 e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos, const void *h,
                                    const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
-                                   const int32_t *nbr_idx, int32_t n, float *out, void *workspace,
-                                   size_t workspace_bytes, const e2v2_taps *taps, hipStream_t stream)
+                                   const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
+                                   void *workspace, size_t workspace_bytes, const e2v2_taps *taps,
+                                   hipStream_t stream)
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
@@ -444,6 +446,7 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
         if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
     }
+    if (target_order && !aligned16(target_order)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
     const AttnWs L = attn_ws(*desc, n);
     if (workspace_bytes < L.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, L.total);
     char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
@@ -482,7 +485,7 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
     // Steps 4-5: streaming attention + target coupling.
     AttnArgs a{};
     a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dmat = dmat;
-    a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx;
+    a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
     a.w_rbf = w->w_rbf; a.w_tgt = w->w_tgt; a.hhat = hhat;
     a.m_tap = taps ? taps->m : nullptr;
     a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
@@ -513,11 +516,12 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
 }
 
 e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,
-                              const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx, int32_t n,
-                              float *out, void *workspace, size_t workspace_bytes, hipStream_t stream)
+                              const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
+                              const int32_t *target_order, int32_t n, float *out, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream)
 {
-    return e2v2_attn_forward_taps(desc, pos, h, w, nbr_start, nbr_len, nbr_idx, n, out, workspace, workspace_bytes,
-                                  nullptr, stream);
+    return e2v2_attn_forward_taps(desc, pos, h, w, nbr_start, nbr_len, nbr_idx, target_order, n, out, workspace,
+                                  workspace_bytes, nullptr, stream);
 }
 
 }  // extern "C"

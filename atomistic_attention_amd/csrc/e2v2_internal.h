@@ -292,6 +292,7 @@ struct AttnArgs {
     const float4 *pos4;              // [n] (x, y, z, scale of h'_j)
     const float *dmat;               // [n][n_dmat(L)]
     const int32_t *nbr_start, *nbr_len, *nbr_idx;
+    const int32_t *order;            // optional processing order of the targets
     const float *w_rbf;              // [R][H]
     const float *w_tgt;              // [P][C]
     float *hhat;                     // [n][NC][C] fp32
@@ -303,7 +304,7 @@ struct AttnArgs {
 hipError_t launch_attn(int L, int hp_f16s, const AttnArgs &a, hipStream_t stream);
 
 hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, void *ws, size_t ws_bytes,
-                                  int32_t *nbr_len, hipStream_t stream);
+                                  int32_t *nbr_len, int32_t *order_out, hipStream_t stream);
 hipError_t launch_neighbors_scan(int n, void *ws, int32_t *nbr_start, int32_t *nbr_len, int64_t *nnz_dev,
                                  hipStream_t stream);
 hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, void *ws, int32_t *nbr_start,

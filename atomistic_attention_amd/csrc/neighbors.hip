@@ -176,12 +176,13 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, c
 
 // ---------------------------------------------------------------- step 3
 __global__ void k_scatter(const float *__restrict__ pos, int n, const int32_t *__restrict__ cell_of,
-                          int32_t *cell_cur, int32_t *order, float4 *spos)
+                          int32_t *cell_cur, int32_t *order, float4 *spos, int32_t *order_out)
 {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const int slot = atomicAdd(&cell_cur[cell_of[i]], 1);
     order[slot] = (int32_t)i;
+    if (order_out) order_out[slot] = (int32_t)i;
     spos[slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float((int)i));
 }
 
@@ -512,14 +513,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
 static inline unsigned nblk(long long n, int b) { return (unsigned)((n + b - 1) / b); }
 
 hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, void *ws, size_t,
-                                  int32_t *nbr_len, hipStream_t stream)
+                                  int32_t *nbr_len, int32_t *order_out, hipStream_t stream)
 {
     NbrLayout L = nbr_layout(ws, n);
     const int maxc = max_cells(n);
     k_bbox<<<1, 1024, 0, stream>>>(pos, n, cutoff, maxc, L.grid, L.cell_cnt);
     k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt);
     k_scan<<<1, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, 0, L.cell_start, L.cell_cur, nullptr);
-    k_scatter<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_cur, L.order, L.spos);
+    k_scatter<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_cur, L.order, L.spos, order_out);
     if (K == 0) {
         const double rc2 = (double)cutoff * (double)cutoff;
         k_count_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(n, rc2, L.grid, L.cell_start, L.order,

@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for hardware-counter runs: 3 layer forwards, then 3 plain device copies of 1 GiB "
+                         "(the copies calibrate the counters' byte units); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this layer has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -115,6 +118,7 @@ def main():
     # resident buffers
     start = torch.empty(N, dtype=torch.int32, device=dev)
     length = torch.empty(N, dtype=torch.int32, device=dev)
+    order = torch.empty(N, dtype=torch.int32, device=dev)
     s0, l0, i0, nnz = B.e2v2_build_neighbors(d["pos"], cfg.cutoff, K)
     cap = i0.numel()
     idx = torch.empty(cap, dtype=torch.int32, device=dev)
@@ -128,12 +132,14 @@ def main():
     def build():
         if K > 0:
             st = lib.e2v2_build_neighbors(B._ptr(d["pos"]), N, float(cfg.cutoff), K, B._ptr(start), B._ptr(length),
-                                          B._ptr(idx), cap, None, B._ptr(nws), nws.numel(), B._stream())
+                                          B._ptr(idx), cap, None, B._ptr(order), B._ptr(nws), nws.numel(),
+                                          B._stream())
             B._check(st)
         else:   # CSR needs the nnz read-back (one host synchronisation)
             n64 = ctypes.c_int64(0)
             st = lib.e2v2_build_neighbors(B._ptr(d["pos"]), N, float(cfg.cutoff), 0, B._ptr(start), B._ptr(length),
-                                          B._ptr(idx), cap, ctypes.byref(n64), B._ptr(nws), nws.numel(), B._stream())
+                                          B._ptr(idx), cap, ctypes.byref(n64), B._ptr(order), B._ptr(nws),
+                                          nws.numel(), B._stream())
             B._check(st)
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
@@ -147,7 +153,20 @@ def main():
             ev[0].record(stream)
         build()
         B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], start, length, idx, out=out, workspace=aws,
-                            taps={"events": ev[1:]} if ev is not None else None)
+                            taps={"events": ev[1:]} if ev is not None else None, target_order=order)
+
+    if args.traffic_probe:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(f"traffic probe: 5 steps of {cfg.name} (1 attention launch each), 3 copies of {x.numel() * 4} bytes",
+              flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

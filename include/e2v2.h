@@ -125,13 +125,17 @@ typedef struct {
  *   nbr_start    device [n] int32;  nbr_len device [n] int32
  *   nbr_idx      device [capacity] int32
  *   nnz_host     host, may be NULL for K > 0; required for K == 0
+ *   order        device [n] int32 or NULL: receives the atoms in cell-list order
+ *                (a permutation of 0..n-1 in which consecutive atoms are spatial
+ *                neighbours); pass it as target_order to e2v2_attn_forward.  The
+ *                order within a cell may differ between calls.
  *   workspace    device scratch of at least
  *                e2v2_build_neighbors_workspace_bytes(n, max_neighbors) bytes
  * Limits: 0 <= n < 2^31 - 1, cutoff > 0 finite, 0 <= K <= 4096, total entries
  * < 2^31.  Non-finite coordinates never fault; such atoms get no neighbours. */
 e2v2_status e2v2_build_neighbors(const float *pos, int32_t n, float cutoff, int32_t max_neighbors,
                                  int32_t *nbr_start, int32_t *nbr_len, int32_t *nbr_idx,
-                                 int64_t capacity, int64_t *nnz_host,
+                                 int64_t capacity, int64_t *nnz_host, int32_t *order,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t e2v2_build_neighbors_workspace_bytes(int32_t n, int32_t max_neighbors);
 
@@ -157,6 +161,11 @@ e2v2_status e2v2_eaas_couple(const float *pos, const void *x, e2v2_dtype x_dtype
  * nbr_idx[nbr_start[i] .. nbr_start[i] + nbr_len[i])).  Entries outside
  * [0, n) are skipped, so -1 padding inside a row is harmless.  A target with
  * no neighbours gets m = 0 and therefore out = 0.
+ *   target_order  device [n] int32 or NULL: the order in which targets are
+ *        processed (a permutation of 0..n-1, e.g. the order written by
+ *        e2v2_build_neighbors).  Results do not depend on it; a spatially
+ *        coherent order lets neighbouring targets share cached neighbour rows.
+ *        Entries outside [0, n) are skipped.
  *   h    device [n][(lmax+1)^2][C] storage dtype
  *   out  device [n][(lmax+1)^2][C] fp32
  *   workspace  device scratch of at least e2v2_attn_workspace_bytes(desc, n)
@@ -164,14 +173,14 @@ e2v2_status e2v2_eaas_couple(const float *pos, const void *x, e2v2_dtype x_dtype
  * and coupled value once per target and accumulates on chip. */
 e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, const void *h,
                               const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
-                              const int32_t *nbr_idx, int32_t n, float *out,
+                              const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Same as e2v2_attn_forward, also copying intermediates into `taps` (host
  * pointer to a struct of device pointers; NULL behaves like e2v2_attn_forward). */
 e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos, const void *h,
                                    const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
-                                   const int32_t *nbr_idx, int32_t n, float *out,
+                                   const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
                                    void *workspace, size_t workspace_bytes, const e2v2_taps *taps,
                                    hipStream_t stream);
 size_t e2v2_attn_workspace_bytes(const e2v2_layer_desc *desc, int32_t n);

@@ -112,3 +112,20 @@ def test_layer_deterministic(gpu_lib):
     a, _ = _run(gpu_lib, wl)
     b, _ = _run(gpu_lib, wl)
     assert np.array_equal(a, b)
+
+
+def test_target_order_does_not_change_results(gpu_lib):
+    """Targets are independent: any processing order (natural, the neighbour
+    builder's cell order, a random permutation) gives bit-identical outputs."""
+    wl = W.make_workload("c4", n=6000)
+    c = wl.cfg
+    d = upload(wl)
+    order = torch.empty(c.n, dtype=torch.int32, device="cuda")
+    s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors, order_out=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(np.sort(order.cpu().numpy()), np.arange(c.n))
+    desc = _desc(gpu_lib, wl, d["dtype"])
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(c.n).astype(np.int32)).cuda()
+    outs = [gpu_lib.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, target_order=o).cpu()
+            for o in (None, order, perm)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])

@@ -99,7 +99,7 @@ def test_capacity_error_reports_need(gpu_lib):
     nnz = ctypes.c_int64(-1)
     st = lib.e2v2_build_neighbors(ctypes.c_void_p(pos.data_ptr()), n, 5.0, 0, ctypes.c_void_p(start.data_ptr()),
                                   ctypes.c_void_p(ln.data_ptr()), ctypes.c_void_p(idx.data_ptr()), 16,
-                                  ctypes.byref(nnz), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                  ctypes.byref(nnz), None, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == gpu_lib.E2V2_ERR_CAPACITY
     assert nnz.value == sum(r.size for r in O.neighbors(wl.pos, 5.0))

@@ -74,7 +74,7 @@ def _attn(lib, desc, n=10, ws_bytes=None, ptr=FAKE, weights=None):
     else:
         wsb = 1 << 20
     return lib.e2v2_attn_forward(ctypes.byref(desc) if desc is not None else None, ptr, ptr, ctypes.byref(w),
-                                 ptr, ptr, ptr, n, ptr, ptr, wsb, None)
+                                 ptr, ptr, ptr, None, n, ptr, ptr, wsb, None)
 
 
 def test_attn_argument_errors(lib):
@@ -111,7 +111,7 @@ def test_neighbor_argument_errors(lib):
     nnz = ctypes.c_int64(0)
     ws = lib.e2v2_build_neighbors_workspace_bytes(100, 16)
     call = lambda n=100, rc=5.0, K=16, cap=1600, nz=ctypes.byref(nnz), wsb=ws, ptr=FAKE: lib.e2v2_build_neighbors(
-        ptr, n, rc, K, ptr, ptr, ptr, cap, nz, ptr, wsb, None)
+        ptr, n, rc, K, ptr, ptr, ptr, cap, nz, None, ptr, wsb, None)
     assert call(n=-1) == B.E2V2_ERR_ARG
     assert call(rc=0.0) == B.E2V2_ERR_ARG
     assert call(rc=float("inf")) == B.E2V2_ERR_ARG
