@@ -29,8 +29,9 @@
 //     the channel set at each step (reduce-scatter), leaving every lane whole
 //     channels: the target EAAS coupling then runs lane-locally and the lane
 //     writes its channels of hhat.
-// Value rows are read as 8-byte (fp16) or 16-byte (fp32) pieces; the 2H lanes of
-// a slot cover one contiguous component row of the neighbour.  A 16-bit h'_j row
+// Value rows are read as 16-byte pieces (4 channels of one fp32 component, or of
+// two interleaved fp16 components); the 2H lanes of a slot cover a contiguous
+// stretch of the neighbour's row.  A 16-bit h'_j row
 // carries one power-of-two scale (in pos4[j].w), folded into the softmax weight
 // of the pair, so each element costs one mixed-precision FMA.
 #include "e2v2_internal.h"
@@ -39,29 +40,49 @@ namespace e2v2 {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-template <bool HB> struct HpRow;
-template <> struct HpRow<true> {     // scaled fp16: 4 channels in one 8-byte load
-    uint2 v;
-    __device__ __forceinline__ void load(const void *base, size_t elem)
+// One neighbour's value pieces for this lane's 4 channels, all components.
+// fp32 h' is [node][comp][C]: one 16-byte load per component.  16-bit h' is
+// stored with components interleaved in pairs (hp_f16_offset): one 16-byte load
+// covers 4 channels of two components, plus an 8-byte load for an odd last
+// component -- half the load instructions of a per-component layout.
+template <bool HB, int NC> struct HpStep;
+template <int NC> struct HpStep<true, NC> {
+    static constexpr int NPR = NC / 2;
+    uint4 pr[NPR > 0 ? NPR : 1];
+    uint2 tl;
+    __device__ __forceinline__ void load(const void *base, int node, int cb, int C)
     {
-        v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(base) + elem);
+        const uint16_t *nb = reinterpret_cast<const uint16_t *>(base) + (size_t)node * NC * C;
+#pragma unroll
+        for (int p = 0; p < NPR; ++p) pr[p] = *reinterpret_cast<const uint4 *>(nb + p * 2 * C + (cb >> 2) * 8);
+        if (NC & 1) tl = *reinterpret_cast<const uint2 *>(nb + (NC - 1) * C + cb);
     }
-    __device__ __forceinline__ float get(int c) const
+    __device__ __forceinline__ float get(int e, int c) const
     {
-        const uint32_t w = (c >> 1) == 0 ? v.x : v.y;
+        uint32_t w;
+        if (e < 2 * NPR) {
+            const uint4 &v = pr[e >> 1];
+            const int k = (e & 1) * 2 + (c >> 1);
+            w = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+        } else {
+            w = (c >> 1) == 0 ? tl.x : tl.y;
+        }
         const uint16_t b = (c & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xffffu);
         return (float)__builtin_bit_cast(_Float16, b);
     }
 };
-template <> struct HpRow<false> {    // fp32: 4 channels in one 16-byte load
-    float4 a;
-    __device__ __forceinline__ void load(const void *base, size_t elem)
+template <int NC> struct HpStep<false, NC> {
+    float4 a[NC];
+    __device__ __forceinline__ void load(const void *base, int node, int cb, int C)
     {
-        a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + elem);
+        const float *nb = reinterpret_cast<const float *>(base) + (size_t)node * NC * C + cb;
+#pragma unroll
+        for (int e = 0; e < NC; ++e) a[e] = *reinterpret_cast<const float4 *>(nb + e * C);
     }
-    __device__ __forceinline__ float get(int c) const
+    __device__ __forceinline__ float get(int e, int c) const
     {
-        return c == 0 ? a.x : c == 1 ? a.y : c == 2 ? a.z : a.w;
+        const float4 &v = a[e];
+        return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
     }
 };
 
@@ -160,13 +181,9 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
 #pragma unroll
         for (int s = 0; s < S; ++s)
             kv[s] = *reinterpret_cast<const float4 *>(A.k + (size_t)(js[s] >= 0 ? js[s] : i) * C + cb);
-        HpRow<HB> hv[SP][NC];
+        HpStep<HB, NC> hv[SP];
 #pragma unroll
-        for (int s = 0; s < SP; ++s) {
-            const size_t rowe = (size_t)(js[s] >= 0 ? js[s] : i) * NC * C + cb;
-#pragma unroll
-            for (int e = 0; e < NC; ++e) hv[s][e].load(A.hp, rowe + (size_t)e * C);
-        }
+        for (int s = 0; s < SP; ++s) hv[s].load(A.hp, js[s] >= 0 ? js[s] : i, cb, C);
         // ---- (c) prefetch the next chunk's index for pair pm
         int jn = -1;
         if (c0 + 16 + pm < len) jn = A.nbr_idx[start + c0 + 16 + pm];
@@ -178,12 +195,27 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
         const float t0 = d * inv_delta - (float)kq;      // (d - mu_k) / Delta for k = kq
         const float *wrow = sW + kq * 16 + pm;
         floatx4 bias = {0.f, 0.f, 0.f, 0.f};
+        // Branch-free product over 8 (up to 32 RBFs) or 16 steps of 4 RBFs; the
+        // padded LDS rows are zero, so surplus Gaussians contribute nothing.
+        if (KK <= 8) {
+            float wk[8];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            if (kk < KK) {
+            for (int kk = 0; kk < 8; ++kk) wk[kk] = wrow[64 * kk];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
                 const float tk = t0 - 4.0f * (float)kk;
                 const float phi = fc * __builtin_amdgcn_exp2f(gexp * tk * tk);
-                bias = __builtin_amdgcn_mfma_f32_16x16x4f32(phi, wrow[64 * kk], bias, 0, 0, 0);
+                bias = __builtin_amdgcn_mfma_f32_16x16x4f32(phi, wk[kk], bias, 0, 0, 0);
+            }
+        } else {
+            float wk[16];
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) wk[kk] = wrow[64 * kk];
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                const float tk = t0 - 4.0f * (float)kk;
+                const float phi = fc * __builtin_amdgcn_exp2f(gexp * tk * tk);
+                bias = __builtin_amdgcn_mfma_f32_16x16x4f32(phi, wk[kk], bias, 0, 0, 0);
             }
         }
         // bias[r] holds pair 4 (lane / 16) + r for head (lane % 16) % H.
@@ -237,12 +269,7 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
             if (ph > 0) {
                 __builtin_amdgcn_sched_barrier(0);     // this phase reuses the previous phase's registers
 #pragma unroll
-                for (int s = 0; s < SP; ++s) {
-                    const int st = ph * SP + s;
-                    const size_t rowe = (size_t)(js[st] >= 0 ? js[st] : i) * NC * C + cb;
-#pragma unroll
-                    for (int e = 0; e < NC; ++e) hv[s][e].load(A.hp, rowe + (size_t)e * C);
-                }
+                for (int s = 0; s < SP; ++s) hv[s].load(A.hp, js[ph * SP + s] >= 0 ? js[ph * SP + s] : i, cb, C);
             }
             if (ph == NPH - 1 && jn >= 0 && jn < n) pjn = A.pos4[jn];
 #pragma unroll
@@ -251,7 +278,7 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
                 for (int c = 0; c < 4; ++c) {
                     float a = acc[e][c];
 #pragma unroll
-                    for (int s = 0; s < SP; ++s) a = fmaf(ps[ph * SP + s], hv[s][e].get(c), a);
+                    for (int s = 0; s < SP; ++s) a = fmaf(ps[ph * SP + s], hv[s].get(e, c), a);
                     acc[e][c] = a;
                 }
         }

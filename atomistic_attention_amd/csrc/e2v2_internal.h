@@ -252,6 +252,17 @@ __device__ __forceinline__ void eaas_channel(const float *__restrict__ D, const 
 }
 
 // ----------------------------------------------------------------------------
+// Layout of 16-bit h' in the workspace: per node NC * C elements; components are
+// interleaved in pairs at 4-channel granularity, so element (e, c) of a pair
+// (e < 2 * (NC / 2)) sits at (e / 2) * 2C + (c / 4) * 8 + (e % 2) * 4 + c % 4, and an
+// odd last component is stored plainly at (NC - 1) * C + c.
+__host__ __device__ inline int hp_f16_offset(int e, int c, int NC, int C)
+{
+    if (e < 2 * (NC / 2)) return (e >> 1) * 2 * C + (c >> 2) * 8 + (e & 1) * 4 + (c & 3);
+    return (NC - 1) * C + c;
+}
+
+// ----------------------------------------------------------------------------
 // bf16 helpers (bit patterns in uint16_t / packed in uint32_t).
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -288,7 +299,7 @@ hipError_t launch_proj(const ProjJob *jobs, int njobs, int a_bf16, int b_bf16, i
 
 struct AttnArgs {
     const float *q, *k;              // [n][C] fp32
-    const void *hp;                  // [n][NC][C] fp32, or fp16 scaled by pos4[j].w
+    const void *hp;                  // [n][NC][C] fp32, or fp16 (hp_f16_offset layout) scaled by pos4[j].w
     const float4 *pos4;              // [n] (x, y, z, scale of h'_j)
     const float *dmat;               // [n][n_dmat(L)]
     const int32_t *nbr_start, *nbr_len, *nbr_idx;

@@ -16,7 +16,7 @@ template <> __device__ __forceinline__ float ld_elem<float>(const float *p, size
 template <> __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t *p, size_t i) { return bf16_to_f(p[i]); }
 
 // Output formats: fp32, bf16, or fp16 with one power-of-two scale per node
-// (kHpF16S).  The scaled-fp16 form keeps 16 bits per element like bf16 but with
+// (kYF16S, stored in the component-pair interleaved layout of hp_f16_offset).  The scaled-fp16 form keeps 16 bits per element like bf16 but with
 // an 11-bit significand; the per-node scale s (stored in pos4[node].w) keeps
 // fp32 range: the node's largest magnitude M maps below 2^14, so no element
 // overflows and every element within 2^28 of M stays a normal fp16 number.
@@ -89,11 +89,11 @@ __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos
             ib = 254u - sb;
         }
         const float sc = __uint_as_float(sb << 23), inv = __uint_as_float(ib << 23);
-        uint16_t *y = reinterpret_cast<uint16_t *>(y_);
+        uint16_t *y = reinterpret_cast<uint16_t *>(y_) + (size_t)node * NC * C;
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
             const uint16_t hb = f_to_f16(yv[e] * inv);
-            y[base + (size_t)e * C] = hb;
+            y[hp_f16_offset(e, c, NC, C)] = hb;
             if (y_deq) y_deq[base + (size_t)e * C] = f16_to_f(hb) * sc;
         }
         if (c == 0 && pos4_out)
