@@ -230,6 +230,9 @@ def main():
             "bytes_per_pair": ab["per_pair"],
             "bytes_per_target": ab["per_node"],
             "avg_launch_ms": float(mean[3]),
+            "note": "achieved counts every gathered neighbour row (algorithmic bytes); rows shared by nearby "
+                    "targets are served from L2/MALL, so HBM traffic is a small part of it (see traffic) and "
+                    "frac can exceed 1; the hardware counters show the vector-memory issue path as the limiter",
         },
         "cpu_baseline": None,
     }

@@ -6,8 +6,9 @@ cpu_baseline leg may import this module; the product path never does.
 The layer, step by step (O1..O8), each written as its plain definition:
 
 O1 neighbours  -- brute force over all pairs with the fp64 predicate of
-                  brute_neighbors.c; with a cap K, keep the K nearest by
-                  (d^2, j); rows sorted by j.  (Explainer section 5.2: verify
+                  brute_neighbors.c against the square of the cutoff's fp32
+                  value; with a cap K, keep the K nearest by (d^2, j); rows
+                  sorted by j.  (Explainer section 5.2: verify
                   the neighbour list; section 3.2: K = 256 with masked padding.)
 O2 encoding    -- real spherical harmonics of the unit position vector
                   (so3.real_sh; explainer section 2.3).
@@ -92,7 +93,8 @@ def neighbors(pos: np.ndarray, cutoff: float, max_neighbors: int = 0, targets=No
     pos32 = np.ascontiguousarray(np.asarray(pos, dtype=np.float64).astype(np.float32))
     n = pos32.shape[0]
     tg = np.arange(n, dtype=np.int32) if targets is None else np.ascontiguousarray(targets, dtype=np.int32)
-    rc2 = float(cutoff) * float(cutoff)
+    rc = float(np.float32(cutoff))          # the cutoff is given as an fp32 value
+    rc2 = rc * rc
     lib = _load()
     counts = np.zeros(tg.size, dtype=np.int64)
     total = lib.oracle_nbr_count(pos32.ctypes.data, n, tg.ctypes.data, tg.size, rc2, counts.ctypes.data)
@@ -111,7 +113,8 @@ def neighbors_numpy(pos: np.ndarray, cutoff: float, max_neighbors: int = 0, targ
     p = np.asarray(pos, dtype=np.float64).astype(np.float32).astype(np.float64)
     n = p.shape[0]
     tg = np.arange(n) if targets is None else np.asarray(targets)
-    rc2 = float(cutoff) * float(cutoff)
+    rc = float(np.float32(cutoff))
+    rc2 = rc * rc
     rows = []
     for i in tg:
         dx = p[:, 0] - p[i, 0]
@@ -194,6 +197,7 @@ def layer_forward(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, *, lmax: int,
     """
     pos = np.asarray(pos, dtype=np.float64)
     h = np.asarray(h, dtype=np.float64)
+    cutoff = float(np.float32(cutoff))       # the cutoff is given as an fp32 value
     n = pos.shape[0]
     tg = np.arange(n) if targets is None else np.asarray(targets, dtype=np.int64)
     if rows is None:
