@@ -249,7 +249,7 @@ size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Attention workspace layout.
 struct AttnWs {
-    size_t q, k, v, hp, dmat, pos4, hhat, total;
+    size_t q, k, v, hp, dmat, pos4, hhat, wpack, total;
 };
 AttnWs attn_ws(const e2v2_layer_desc &d, int n)
 {
@@ -265,6 +265,8 @@ AttnWs attn_ws(const e2v2_layer_desc &d, int n)
     w.dmat = o; o += al256(N * nd * 4);
     w.pos4 = o; o += al256(N * 16);
     w.hhat = o; o += al256(N * NC * C * 4);
+    // bf16 weights packed into MFMA fragments: W_V[0..L], W_Q, W_K, W_O[0..L]
+    w.wpack = o; o += al256(d.storage == E2V2_BF16 ? (size_t)(2 * (d.lmax + 1) + 2) * C * C * 2 : 0);
     w.total = o + 256;   // slack for re-aligning an unaligned base
     return w;
 }
@@ -468,13 +470,31 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
     // Step 2: projections (q, k from the l = 0 block; v per component with W_V[l]).
     ProjJob jobs[kMaxL * kMaxL + 2 * kMaxL + 1 + 2];
     int nj = 0;
+    uint16_t *wp = reinterpret_cast<uint16_t *>(ws + L.wpack);
+    const size_t wsz = (size_t)C * C;                 // elements per packed matrix
+    auto wv = [&](int l) -> const void * {            // weights as the projection kernel reads them
+        return bf ? (const void *)(wp + (size_t)l * wsz) : (const void *)(reinterpret_cast<const char *>(w->w_v) + l * wstride);
+    };
+    auto wo = [&](int l) -> const void * {
+        return bf ? (const void *)(wp + (size_t)(lmax + 3 + l) * wsz) : (const void *)(reinterpret_cast<const char *>(w->w_o) + l * wstride);
+    };
+    if (bf) {
+        const uint16_t *src[2 * kMaxL + 4];
+        uint16_t *dst[2 * kMaxL + 4];
+        int cnt = 0;
+        for (int l = 0; l <= lmax; ++l) { src[cnt] = reinterpret_cast<const uint16_t *>(w->w_v) + l * wsz; dst[cnt] = wp + cnt * wsz; ++cnt; }
+        src[cnt] = reinterpret_cast<const uint16_t *>(w->w_q); dst[cnt] = wp + cnt * wsz; ++cnt;
+        src[cnt] = reinterpret_cast<const uint16_t *>(w->w_k); dst[cnt] = wp + cnt * wsz; ++cnt;
+        for (int l = 0; l <= lmax; ++l) { src[cnt] = reinterpret_cast<const uint16_t *>(w->w_o) + l * wsz; dst[cnt] = wp + cnt * wsz; ++cnt; }
+        e = launch_pack_weights(src, dst, cnt, C, stream);
+        if (e != hipSuccess) return hip_fail(e, "weight packing kernel");
+    }
     for (int l = 0; l <= lmax; ++l)
         for (int m = 0; m < 2 * l + 1; ++m)
-            jobs[nj++] = ProjJob{h, (long long)NC * C, reinterpret_cast<const char *>(w->w_v) + l * wstride, v,
-                                 (long long)NC * C, l * l + m};
-    jobs[nj++] = ProjJob{h, (long long)NC * C, w->w_q, q, (long long)C, 0};
-    jobs[nj++] = ProjJob{h, (long long)NC * C, w->w_k, k, (long long)C, 0};
-    e = launch_proj(jobs, nj, bf, bf, n, C, stream);
+            jobs[nj++] = ProjJob{h, (long long)NC * C, wv(l), v, (long long)NC * C, l * l + m};
+    jobs[nj++] = ProjJob{h, (long long)NC * C, bf ? (const void *)(wp + (size_t)(lmax + 1) * wsz) : w->w_q, q, (long long)C, 0};
+    jobs[nj++] = ProjJob{h, (long long)NC * C, bf ? (const void *)(wp + (size_t)(lmax + 2) * wsz) : w->w_k, k, (long long)C, 0};
+    e = bf ? launch_proj_bf16(jobs, nj, 0, n, C, stream) : launch_proj(jobs, nj, 0, 0, n, C, stream);
     if (e == hipSuccess) e = mark(1);
     if (e != hipSuccess) return hip_fail(e, "projection kernel");
     // Step 3: source coupling h' (EAAS), per-node D blocks and padded positions.
@@ -496,9 +516,8 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
     nj = 0;
     for (int l = 0; l <= lmax; ++l)
         for (int m = 0; m < 2 * l + 1; ++m)
-            jobs[nj++] = ProjJob{hhat, (long long)NC * C, reinterpret_cast<const char *>(w->w_o) + l * wstride, out,
-                                 (long long)NC * C, l * l + m};
-    e = launch_proj(jobs, nj, 0, bf, n, C, stream);
+            jobs[nj++] = ProjJob{hhat, (long long)NC * C, wo(l), out, (long long)NC * C, l * l + m};
+    e = bf ? launch_proj_bf16(jobs, nj, 1, n, C, stream) : launch_proj(jobs, nj, 0, 0, n, C, stream);
     if (e == hipSuccess) e = mark(4);
     if (e != hipSuccess) return hip_fail(e, "output projection kernel");
     if (taps) {

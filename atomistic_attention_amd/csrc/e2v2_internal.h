@@ -296,6 +296,10 @@ struct ProjJob {
     int comp;               // component index of the rows
 };
 hipError_t launch_proj(const ProjJob *jobs, int njobs, int a_bf16, int b_bf16, int n, int C, hipStream_t stream);
+// bf16 weights on bf16 MFMA: job.b points at weights packed by launch_pack_weights;
+// a_f32 selects fp32 input rows (split into bf16 hi + lo), else bf16 rows.
+hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, int count, int C, hipStream_t stream);
+hipError_t launch_proj_bf16(const ProjJob *jobs, int njobs, int a_f32, int n, int C, hipStream_t stream);
 
 struct AttnArgs {
     const float *q, *k;              // [n][C] fp32

@@ -1,8 +1,8 @@
 // Per-node linear projections on the matrix cores: q = h^0 W_Q, k = h^0 W_K,
 // v^l = h^l W_V[l] and out^l = hhat^l W_O[l] -- the layer's only dense
 // contractions.  Each (component, weight) pair is one "job"; rows of a job are
-// nodes.  One wave computes a 16-node x C tile with v_mfma_f32_16x16x4_f32
-// (fp32 accumulate; bf16 operands are widened exactly on load).
+// nodes.  bf16 weights use the bf16 kernel below; fp32 weights use
+// v_mfma_f32_16x16x4_f32 with one wave per 16-node x C tile.
 //
 // The contraction index is permuted so that each lane's 16 x 4 A fragment
 // comes from one contiguous stretch of its row: in MFMA step s, lane group g
@@ -71,6 +71,130 @@ __global__ __launch_bounds__(64) void proj_kernel(const ProjJobs jobs, int n)
             if (orow < n) job.out[orow * job.o_node_stride + (long long)job.comp * C + nb * 16 + m] = acc[r];
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 path on v_mfma_f32_16x16x32_bf16, in the transposed orientation
+// out^T = W^T . in^T: the 16 x 32 A operand is a fragment of W^T, pre-packed so a
+// wave reads it as one coalesced 1 KB load; the 32 x 16 B operand is 16 nodes'
+// input rows (8 consecutive contraction indices per lane, one 16-byte load);
+// each lane of the 16 x 16 result holds 4 consecutive output channels of one
+// node and writes them as one 16-byte store.  fp32 inputs (hhat) are split into
+// bf16 hi + lo, two products, which keeps about 16 significant bits of the
+// input against exact bf16 weights.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// W [C][C] (in, out) bf16 -> fragments: for output block nb (16 channels) and
+// contraction block kb (32 indices), lane l holds W[32 kb + 8 (l / 16) + e][16 nb + l % 16], e < 8.
+struct PackJobs {
+    const uint16_t *w[kMaxJobs];
+    uint16_t *out[kMaxJobs];
+};
+__global__ void k_pack_wt(const PackJobs pj, int C)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int KB = C / 32, NB = C / 16;
+    if (t >= NB * KB * 64) return;
+    const int lane = t & 63, frag = t >> 6, nb = frag / KB, kb = frag - nb * KB;
+    const int nn = 16 * nb + (lane & 15), k0 = 32 * kb + 8 * (lane >> 4);
+    const uint16_t *w = pj.w[blockIdx.y];
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = w[(size_t)(k0 + e) * C + nn];
+    uint4 o;
+    o.x = v[0] | (uint32_t(v[1]) << 16);
+    o.y = v[2] | (uint32_t(v[3]) << 16);
+    o.z = v[4] | (uint32_t(v[5]) << 16);
+    o.w = v[6] | (uint32_t(v[7]) << 16);
+    reinterpret_cast<uint4 *>(pj.out[blockIdx.y])[t] = o;
+}
+
+template <bool AF32, int C>
+__global__ __launch_bounds__(256) void proj_bf16_kernel(const ProjJobs jobs, int n)
+{
+    constexpr int KB = C / 32, NB = C / 16;
+    const ProjJob &job = jobs.j[blockIdx.y];
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long node = tile * 16 + (lane & 15);
+    const bool valid = node < n;
+    bf16x8 bhi[KB], blo[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        uint4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+        if (valid) {
+            if constexpr (AF32) {
+                const float *ap = reinterpret_cast<const float *>(job.a) + node * job.a_node_stride +
+                                  (long long)job.comp * C + 32 * kb + 8 * g;
+                const float4 x0 = reinterpret_cast<const float4 *>(ap)[0];
+                const float4 x1 = reinterpret_cast<const float4 *>(ap)[1];
+                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                uint16_t h16[8], l16[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    h16[e] = f_to_bf16(xs[e]);
+                    l16[e] = f_to_bf16(xs[e] - bf16_to_f(h16[e]));
+                }
+                hi = make_uint4(h16[0] | (uint32_t(h16[1]) << 16), h16[2] | (uint32_t(h16[3]) << 16),
+                                h16[4] | (uint32_t(h16[5]) << 16), h16[6] | (uint32_t(h16[7]) << 16));
+                lo = make_uint4(l16[0] | (uint32_t(l16[1]) << 16), l16[2] | (uint32_t(l16[3]) << 16),
+                                l16[4] | (uint32_t(l16[5]) << 16), l16[6] | (uint32_t(l16[7]) << 16));
+            } else {
+                hi = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(job.a) +
+                                                      node * job.a_node_stride + (long long)job.comp * C +
+                                                      32 * kb + 8 * g);
+            }
+        }
+        bhi[kb] = __builtin_bit_cast(bf16x8, hi);
+        blo[kb] = __builtin_bit_cast(bf16x8, lo);
+    }
+    const uint4 *wp = reinterpret_cast<const uint4 *>(job.b);
+    float *op = job.out + node * job.o_node_stride + (long long)job.comp * C + 4 * g;
+#pragma unroll 2
+    for (int nb = 0; nb < NB; ++nb) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 wf = __builtin_bit_cast(bf16x8, wp[(nb * KB + kb) * 64 + lane]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, bhi[kb], acc, 0, 0, 0);
+            if constexpr (AF32) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, blo[kb], acc, 0, 0, 0);
+        }
+        if (valid) *reinterpret_cast<float4 *>(op + 16 * nb) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, int count, int C, hipStream_t stream)
+{
+    if (count <= 0) return hipSuccess;
+    if (count > kMaxJobs || C % 32 != 0) return hipErrorInvalidValue;
+    PackJobs pj{};
+    for (int i = 0; i < count; ++i) {
+        pj.w[i] = w[i];
+        pj.out[i] = out[i];
+    }
+    const int threads = (C / 16) * (C / 32) * 64;
+    k_pack_wt<<<dim3((unsigned)((threads + 255) / 256), (unsigned)count), 256, 0, stream>>>(pj, C);
+    return hipGetLastError();
+}
+
+hipError_t launch_proj_bf16(const ProjJob *jobs, int njobs, int a_f32, int n, int C, hipStream_t stream)
+{
+    if (n <= 0 || njobs <= 0) return hipSuccess;
+    if (njobs > kMaxJobs) return hipErrorInvalidValue;
+    ProjJobs pj{};
+    for (int i = 0; i < njobs; ++i) pj.j[i] = jobs[i];
+    dim3 grid((unsigned)((n + 63) / 64), (unsigned)njobs), block(256);
+#define E2V2_PROJ_BF16(CC)                                                                         \
+    (a_f32 ? (proj_bf16_kernel<true, CC><<<grid, block, 0, stream>>>(pj, n), 0)                   \
+           : (proj_bf16_kernel<false, CC><<<grid, block, 0, stream>>>(pj, n), 0))
+    switch (C) {
+    case 32: E2V2_PROJ_BF16(32); break;
+    case 64: E2V2_PROJ_BF16(64); break;
+    case 128: E2V2_PROJ_BF16(128); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef E2V2_PROJ_BF16
+    return hipGetLastError();
 }
 
 template <typename TA, typename TB>
