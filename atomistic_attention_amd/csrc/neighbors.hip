@@ -23,6 +23,8 @@
 // K-nearest choice uses a total order, so results are deterministic.
 #include "e2v2_internal.h"
 
+#include <algorithm>
+
 #pragma clang fp contract(off)
 
 namespace e2v2 {
@@ -36,6 +38,7 @@ struct GridInfo {
 
 struct NbrLayout {
     GridInfo *grid;
+    float *box_part;       // [kBoxBlocks][8] partial bounding boxes
     int32_t *cell_of;
     int32_t *cell_cnt;     // [maxc + 1]
     int32_t *cell_start;   // [maxc + 1]
@@ -56,6 +59,7 @@ static NbrLayout nbr_layout(void *ws, int n)
     size_t o = 0;
     const size_t mc = (size_t)max_cells(n);
     L.grid = reinterpret_cast<GridInfo *>(p + o); o += al256(sizeof(GridInfo));
+    L.box_part = reinterpret_cast<float *>(p + o); o += al256(sizeof(float) * 8 * 256);
     L.nnz = reinterpret_cast<int64_t *>(p + o); o += al256(sizeof(int64_t));
     L.cell_of = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (size_t)n);
     L.cell_cnt = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (mc + 1));
@@ -71,13 +75,16 @@ size_t neighbors_ws_bytes(int n, int /*K*/) { return nbr_layout(nullptr, n).byte
 int64_t *neighbors_nnz_slot(void *ws, int n) { return nbr_layout(ws, n).nnz; }
 
 // ---------------------------------------------------------------- step 1
-__global__ __launch_bounds__(1024) void k_bbox(const float *__restrict__ pos, int n, float cutoff, int maxc,
-                                               GridInfo *grid, int32_t *cell_cnt)
+// Bounding box in two stages: kBoxBlocks blocks reduce strided slices into
+// partial (min, max) records, one block combines them and sizes the grid.
+constexpr int kBoxBlocks = 256;
+
+__global__ __launch_bounds__(256) void k_bbox_partial(const float *__restrict__ pos, int n, float *part)
 {
-    __shared__ float smin[3][1024], smax[3][1024];
+    __shared__ float smin[3][256], smax[3][256];
     const int t = threadIdx.x;
     float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
-    for (long long i = t; i < n; i += 1024)
+    for (long long i = (long long)blockIdx.x * 256 + t; i < n; i += (long long)gridDim.x * 256)
         for (int d = 0; d < 3; ++d) {
             const float v = pos[3 * i + d];
             mn[d] = fminf(mn[d], v);     // fminf/fmaxf ignore NaN
@@ -85,7 +92,31 @@ __global__ __launch_bounds__(1024) void k_bbox(const float *__restrict__ pos, in
         }
     for (int d = 0; d < 3; ++d) { smin[d][t] = mn[d]; smax[d][t] = mx[d]; }
     __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
+    for (int s = 128; s > 0; s >>= 1) {
+        if (t < s)
+            for (int d = 0; d < 3; ++d) {
+                smin[d][t] = fminf(smin[d][t], smin[d][t + s]);
+                smax[d][t] = fmaxf(smax[d][t], smax[d][t + s]);
+            }
+        __syncthreads();
+    }
+    if (t < 3) {
+        part[blockIdx.x * 8 + t] = smin[t][0];
+        part[blockIdx.x * 8 + 4 + t] = smax[t][0];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_bbox(const float *__restrict__ part, int nparts, float cutoff, int maxc,
+                                              GridInfo *grid, int32_t *cell_cnt)
+{
+    __shared__ float smin[3][256], smax[3][256];
+    const int t = threadIdx.x;
+    for (int d = 0; d < 3; ++d) {
+        smin[d][t] = t < nparts ? part[t * 8 + d] : INFINITY;
+        smax[d][t] = t < nparts ? part[t * 8 + 4 + d] : -INFINITY;
+    }
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
         if (t < s)
             for (int d = 0; d < 3; ++d) {
                 smin[d][t] = fminf(smin[d][t], smin[d][t + s]);
@@ -94,7 +125,7 @@ __global__ __launch_bounds__(1024) void k_bbox(const float *__restrict__ pos, in
         __syncthreads();
     }
     // clear the cell counters for step 2
-    for (long long c = t; c <= maxc; c += 1024) cell_cnt[c] = 0;
+    for (long long c = t; c <= maxc; c += 256) cell_cnt[c] = 0;
     if (t == 0) {
         const float cmin = cutoff * 1.00001f;
         int dims[3];
@@ -352,61 +383,157 @@ __device__ __forceinline__ void wave_lds_sync()
 
 // Number of neighbours of the target at cell-order slot t; with COLLECT the first
 // kWaveCap of them land in cj / cd (unordered).  Returns a wave-uniform count.
+// The 9 row ranges of the stencil are resolved first and flattened into one
+// candidate index space; candidate positions are then fetched 4 x 64 at a time,
+// so a target costs a few memory round trips rather than one per 64 candidates.
 template <bool COLLECT>
 __device__ __forceinline__ int wave_scan(int i, float4 pi, double rc2, const GridInfo &gi,
                                          const int32_t *__restrict__ cell_start, const float4 *__restrict__ spos,
                                          int32_t *cj, double *cd, int lane)
 {
+    constexpr int U = 4;
     const double xi = pi.x, yi = pi.y, zi = pi.z;
     const int cx = cell_coord(pi.x, gi.lo[0], gi.inv[0], gi.dims[0]);
     const int cy = cell_coord(pi.y, gi.lo[1], gi.inv[1], gi.dims[1]);
     const int cz = cell_coord(pi.z, gi.lo[2], gi.inv[2], gi.dims[2]);
     const int x0 = cx > 0 ? cx - 1 : 0, x1 = cx + 1 < gi.dims[0] ? cx + 1 : gi.dims[0] - 1;
+    // ranges r = 0..8 over (z, y); an out-of-grid row is an empty range
+    int pre[10], off[9];
+    pre[0] = 0;
+#pragma unroll
+    for (int r = 0; r < 9; ++r) {
+        const int z = cz - 1 + r / 3, y = cy - 1 + r % 3;
+        int a = 0, b = 0;
+        if (z >= 0 && z < gi.dims[2] && y >= 0 && y < gi.dims[1]) {
+            const int rowc = (z * gi.dims[1] + y) * gi.dims[0];
+            a = cell_start[rowc + x0];
+            b = cell_start[rowc + x1 + 1];
+        }
+        off[r] = a - pre[r];                      // candidate f of range r is spos[f + off[r]]
+        pre[r + 1] = pre[r] + (b - a);
+    }
+    const int total = pre[9];
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     int count = 0;
-    for (int z = cz - 1; z <= cz + 1; ++z) {
-        if (z < 0 || z >= gi.dims[2]) continue;
-        for (int y = cy - 1; y <= cy + 1; ++y) {
-            if (y < 0 || y >= gi.dims[1]) continue;
-            const int rowc = (z * gi.dims[1] + y) * gi.dims[0];
-            const int s0 = cell_start[rowc + x0], s1 = cell_start[rowc + x1 + 1];
-            for (int base = s0; base < s1; base += 64) {
-                const int sidx = base + lane;
-                bool pass = false;
-                int j = -1;
-                double d2 = 0.0;
-                if (sidx < s1) {
-                    const float4 pj = spos[sidx];
-                    j = __float_as_int(pj.w);
-                    if (j != i) {
-                        d2 = pair_d2(xi, yi, zi, pj);
-                        pass = d2 < rc2;
-                    }
+    for (int c0 = 0; c0 < total; c0 += 64 * U) {
+        float4 pj[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int f = c0 + 64 * u + lane;
+            ok[u] = f < total;
+            int o = off[0];
+#pragma unroll
+            for (int r = 1; r < 9; ++r) o = f >= pre[r] ? off[r] : o;
+            pj[u] = ok[u] ? spos[f + o] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            bool pass = false;
+            int j = -1;
+            double d2 = 0.0;
+            if (ok[u]) {
+                j = __float_as_int(pj[u].w);
+                if (j != i) {
+                    d2 = pair_d2(xi, yi, zi, pj[u]);
+                    pass = d2 < rc2;
                 }
-                const uint64_t m = __ballot(pass);
-                if (COLLECT && pass) {
-                    const int slot = count + __popcll(m & below);
-                    if (slot < kWaveCap) {
-                        cj[slot] = j;
-                        cd[slot] = d2;
-                    }
-                }
-                count += __popcll(m);
             }
+            const uint64_t m = __ballot(pass);
+            if (COLLECT && pass) {
+                const int slot = count + __popcll(m & below);
+                if (slot < kWaveCap) {
+                    cj[slot] = j;
+                    cd[slot] = d2;
+                }
+            }
+            count += __popcll(m);
         }
     }
     return count;
 }
 
-// row[rank by j] = j for the first cnt entries of cj (distinct j).
+// Rank counting with broadcast LDS reads: the keys are read 4 (or 2 doubles) at
+// a time as one 16-byte load that every lane shares, and each lane ranks all of
+// its elements (e = lane + 64 c, c < NCH) against them.  Arrays are padded to a
+// multiple of 4 entries with keys that rank after every real key.
+
+// row[rank by j] = j for the cnt distinct keys of cj.
+template <int NCH>
+__device__ __forceinline__ void wave_write_sorted_n(const int32_t *cj, int cnt, int32_t *row, int lane)
+{
+    int je[NCH], r[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = lane + 64 * c;
+        je[c] = e < cnt ? cj[e] : INT_MAX;
+        r[c] = 0;
+    }
+    const int4 *k4 = reinterpret_cast<const int4 *>(cj);
+    const int nb4 = (cnt + 3) >> 2;
+    for (int t = 0; t < nb4; ++t) {
+        const int4 k = k4[t];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            r[c] += (k.x < je[c] ? 1 : 0) + (k.y < je[c] ? 1 : 0) + (k.z < je[c] ? 1 : 0) + (k.w < je[c] ? 1 : 0);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if (lane + 64 * c < cnt) row[r[c]] = je[c];
+}
 __device__ __forceinline__ void wave_write_sorted(const int32_t *cj, int cnt, int32_t *row, int lane)
 {
-    for (int e0 = 0; e0 < cnt; e0 += 64) {
-        const int e = e0 + lane;
-        const int je = e < cnt ? cj[e] : INT_MAX;
-        int r = 0;
-        for (int t = 0; t < cnt; ++t) r += cj[t] < je ? 1 : 0;
-        if (e < cnt) row[r] = je;
+    if (cnt <= 256) wave_write_sorted_n<4>(cj, cnt, row, lane);
+    else if (cnt <= 512) wave_write_sorted_n<8>(cj, cnt, row, lane);
+    else wave_write_sorted_n<16>(cj, cnt, row, lane);
+}
+
+// The K nearest by (d2, j): kj[rank] = j for every candidate of rank < K.
+template <int NCH>
+__device__ __forceinline__ void wave_select_nearest_n(const double *cd, const int32_t *cj, int cnt, int K,
+                                                      int32_t *kj, int lane)
+{
+    double de[NCH];
+    int je[NCH], r[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = lane + 64 * c;
+        de[c] = e < cnt ? cd[e] : INFINITY;
+        je[c] = e < cnt ? cj[e] : INT_MAX;
+        r[c] = 0;
+    }
+    const double2 *d2 = reinterpret_cast<const double2 *>(cd);
+    const int2 *j2 = reinterpret_cast<const int2 *>(cj);
+    const int nb2 = (cnt + 1) >> 1;
+    for (int t = 0; t < nb2; ++t) {
+        const double2 dv = d2[t];
+        const int2 jv = j2[t];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            r[c] += (dv.x < de[c] || (dv.x == de[c] && jv.x < je[c])) ? 1 : 0;
+            r[c] += (dv.y < de[c] || (dv.y == de[c] && jv.y < je[c])) ? 1 : 0;
+        }
+    }
+    wave_lds_sync();                                      // kj may alias cd
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if (lane + 64 * c < cnt && r[c] < K) kj[r[c]] = je[c];
+}
+__device__ __forceinline__ void wave_select_nearest(const double *cd, const int32_t *cj, int cnt, int K, int32_t *kj,
+                                                    int lane)
+{
+    if (cnt <= 256) wave_select_nearest_n<4>(cd, cj, cnt, K, kj, lane);
+    else if (cnt <= 512) wave_select_nearest_n<8>(cd, cj, cnt, K, kj, lane);
+    else wave_select_nearest_n<16>(cd, cj, cnt, K, kj, lane);
+}
+
+// Pads keys [cnt, cnt rounded up to 4) so that they rank after every real key.
+__device__ __forceinline__ void wave_pad_keys(int32_t *cj, double *cd, int cnt, int lane)
+{
+    const int e = cnt + lane;
+    if (lane < 4 && e < ((cnt + 3) & ~3)) {
+        cj[e] = INT_MAX;
+        if (cd) cd[e] = INFINITY;
     }
 }
 
@@ -432,8 +559,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, do
                                                                        const int32_t *__restrict__ nbr_start,
                                                                        const int32_t *__restrict__ nbr_len, int32_t *nbr_idx)
 {
-    __shared__ int32_t sj[kWavesPerBlock][kWaveCap];
-    __shared__ double sd[kWavesPerBlock][kWaveCap];
+    __shared__ __align__(16) int32_t sj[kWavesPerBlock][kWaveCap + 4];
+    __shared__ __align__(16) double sd[kWavesPerBlock][kWaveCap + 4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerBlock + w));
     if (t >= n) return;
@@ -441,6 +568,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, do
     if (nbr_len[i] > kWaveCap) return;
     const GridInfo gi = *grid;
     const int cnt = wave_scan<true>(i, spos[t], rc2, gi, cell_start, spos, sj[w], sd[w], lane);
+    wave_pad_keys(sj[w], nullptr, cnt, lane);
     wave_lds_sync();
     wave_write_sorted(sj[w], cnt, nbr_idx + nbr_start[i], lane);
 }
@@ -455,8 +583,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
                                                                           int32_t *nbr_start, int32_t *nbr_len,
                                                                           int32_t *nbr_idx)
 {
-    __shared__ int32_t sj[kWavesPerBlock][kWaveCap];
-    __shared__ double sd[kWavesPerBlock][kWaveCap];
+    __shared__ __align__(16) int32_t sj[kWavesPerBlock][kWaveCap + 4];
+    __shared__ __align__(16) double sd[kWavesPerBlock][kWaveCap + 4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerBlock + w));
     if (t >= n) return;
@@ -471,36 +599,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
         if (lane == 0) nbr_len[i] = -1;
         return;
     }
+    wave_pad_keys(cj, cd, cnt, lane);
     wave_lds_sync();
     int len = cnt;
     if (cnt <= K) {
         wave_write_sorted(cj, cnt, row, lane);
     } else {
-        // (d2, j) rank of every candidate; the K smallest go to slots 0..K-1 of kj
-        int rk[kWaveCap / 64];
-#pragma unroll
-        for (int c = 0; c < kWaveCap / 64; ++c) {
-            rk[c] = K;
-            const int e = c * 64 + lane;
-            if (c * 64 < cnt) {
-                const double de = e < cnt ? cd[e] : INFINITY;
-                const int je = e < cnt ? cj[e] : INT_MAX;
-                int r = 0;
-                for (int tt = 0; tt < cnt; ++tt) {
-                    const double dt = cd[tt];
-                    const int jt = cj[tt];
-                    r += (dt < de || (dt == de && jt < je)) ? 1 : 0;
-                }
-                rk[c] = e < cnt ? r : K;
-            }
-        }
-        wave_lds_sync();
-        int32_t *kj = reinterpret_cast<int32_t *>(cd);   // the distances are no longer needed
-#pragma unroll
-        for (int c = 0; c < kWaveCap / 64; ++c) {
-            const int e = c * 64 + lane;
-            if (e < cnt && rk[c] < K) kj[rk[c]] = cj[e];
-        }
+        int32_t *kj = reinterpret_cast<int32_t *>(cd);   // the distances are no longer needed after ranking
+        wave_select_nearest(cd, cj, cnt, K, kj, lane);
+        wave_pad_keys(kj, nullptr, K, lane);
         wave_lds_sync();
         wave_write_sorted(kj, K, row, lane);
         len = K;
@@ -517,7 +624,9 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
 {
     NbrLayout L = nbr_layout(ws, n);
     const int maxc = max_cells(n);
-    k_bbox<<<1, 1024, 0, stream>>>(pos, n, cutoff, maxc, L.grid, L.cell_cnt);
+    const int nparts = (int)std::min<long long>(kBoxBlocks, ((long long)n + 255) / 256);
+    k_bbox_partial<<<nparts, 256, 0, stream>>>(pos, n, L.box_part);
+    k_bbox<<<1, 256, 0, stream>>>(L.box_part, nparts, cutoff, maxc, L.grid, L.cell_cnt);
     k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt);
     k_scan<<<1, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, 0, L.cell_start, L.cell_cur, nullptr);
     k_scatter<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_cur, L.order, L.spos, order_out);
