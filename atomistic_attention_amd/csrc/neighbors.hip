@@ -386,13 +386,39 @@ __device__ __forceinline__ void wave_lds_sync()
 // The 9 row ranges of the stencil are resolved first and flattened into one
 // candidate index space; candidate positions are then fetched 4 x 64 at a time,
 // so a target costs a few memory round trips rather than one per 64 candidates.
+// Decides d2 < rc2 exactly.  An fp32 estimate settles every pair whose squared
+// distance is not within a relative 1e-5 of rc2 (its own error is below 4e-7
+// relative: one rounding per difference, product and sum); the rest take the
+// exact fp64 predicate.  The decision is therefore the fp64 one in every case.
+struct CutoffTest {
+    double rc2;
+    float lo, hi;           // rc2 * (1 - 1e-5), rc2 * (1 + 1e-5) in fp32
+    __device__ __forceinline__ CutoffTest(double r2)
+        : rc2(r2), lo((float)(r2 * (1.0 - 1e-5))), hi((float)(r2 * (1.0 + 1e-5)))
+    {
+        if (!(lo > 1e-30f && hi < 1e30f)) {  // cutoffs outside fp32's comfortable range: always exact
+            lo = -1.f;
+            hi = INFINITY;
+        }
+    }
+    __device__ __forceinline__ bool inside(double xi, double yi, double zi, float4 pi, float4 pj) const
+    {
+        const float dx = pj.x - pi.x, dy = pj.y - pi.y, dz = pj.z - pi.z;
+        const float e = dx * dx + dy * dy + dz * dz;
+        if (e < lo) return true;
+        if (e > hi) return false;             // a NaN estimate falls through to the exact test
+        return pair_d2(xi, yi, zi, pj) < rc2;
+    }
+};
+
 template <bool COLLECT>
 __device__ __forceinline__ int wave_scan(int i, float4 pi, double rc2, const GridInfo &gi,
                                          const int32_t *__restrict__ cell_start, const float4 *__restrict__ spos,
-                                         int32_t *cj, double *cd, int lane)
+                                         int32_t *cj, int lane)
 {
     constexpr int U = 4;
     const double xi = pi.x, yi = pi.y, zi = pi.z;
+    const CutoffTest test(rc2);
     const int cx = cell_coord(pi.x, gi.lo[0], gi.inv[0], gi.dims[0]);
     const int cy = cell_coord(pi.y, gi.lo[1], gi.inv[1], gi.dims[1]);
     const int cz = cell_coord(pi.z, gi.lo[2], gi.inv[2], gi.dims[2]);
@@ -429,23 +455,12 @@ __device__ __forceinline__ int wave_scan(int i, float4 pi, double rc2, const Gri
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            bool pass = false;
-            int j = -1;
-            double d2 = 0.0;
-            if (ok[u]) {
-                j = __float_as_int(pj[u].w);
-                if (j != i) {
-                    d2 = pair_d2(xi, yi, zi, pj[u]);
-                    pass = d2 < rc2;
-                }
-            }
+            const int j = __float_as_int(pj[u].w);
+            const bool pass = ok[u] && j != i && test.inside(xi, yi, zi, pi, pj[u]);
             const uint64_t m = __ballot(pass);
             if (COLLECT && pass) {
                 const int slot = count + __popcll(m & below);
-                if (slot < kWaveCap) {
-                    cj[slot] = j;
-                    cd[slot] = d2;
-                }
+                if (slot < kWaveCap) cj[slot] = j;
             }
             count += __popcll(m);
         }
@@ -483,7 +498,11 @@ __device__ __forceinline__ void wave_write_sorted_n(const int32_t *cj, int cnt, 
 }
 __device__ __forceinline__ void wave_write_sorted(const int32_t *cj, int cnt, int32_t *row, int lane)
 {
-    if (cnt <= 256) wave_write_sorted_n<4>(cj, cnt, row, lane);
+    if (cnt <= 64) wave_write_sorted_n<1>(cj, cnt, row, lane);
+    else if (cnt <= 128) wave_write_sorted_n<2>(cj, cnt, row, lane);
+    else if (cnt <= 192) wave_write_sorted_n<3>(cj, cnt, row, lane);
+    else if (cnt <= 256) wave_write_sorted_n<4>(cj, cnt, row, lane);
+    else if (cnt <= 384) wave_write_sorted_n<6>(cj, cnt, row, lane);
     else if (cnt <= 512) wave_write_sorted_n<8>(cj, cnt, row, lane);
     else wave_write_sorted_n<16>(cj, cnt, row, lane);
 }
@@ -523,6 +542,7 @@ __device__ __forceinline__ void wave_select_nearest(const double *cd, const int3
                                                     int lane)
 {
     if (cnt <= 256) wave_select_nearest_n<4>(cd, cj, cnt, K, kj, lane);
+    else if (cnt <= 384) wave_select_nearest_n<6>(cd, cj, cnt, K, kj, lane);
     else if (cnt <= 512) wave_select_nearest_n<8>(cd, cj, cnt, K, kj, lane);
     else wave_select_nearest_n<16>(cd, cj, cnt, K, kj, lane);
 }
@@ -547,7 +567,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_count_wave(int n, doubl
     if (t >= n) return;
     const GridInfo gi = *grid;
     const int i = order[t];
-    const int cnt = wave_scan<false>(i, spos[t], rc2, gi, cell_start, spos, nullptr, nullptr, lane);
+    const int cnt = wave_scan<false>(i, spos[t], rc2, gi, cell_start, spos, nullptr, lane);
     if (lane == 0) nbr_len[i] = cnt;
 }
 
@@ -560,14 +580,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, do
                                                                        const int32_t *__restrict__ nbr_len, int32_t *nbr_idx)
 {
     __shared__ __align__(16) int32_t sj[kWavesPerBlock][kWaveCap + 4];
-    __shared__ __align__(16) double sd[kWavesPerBlock][kWaveCap + 4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerBlock + w));
     if (t >= n) return;
     const int i = order[t];
     if (nbr_len[i] > kWaveCap) return;
     const GridInfo gi = *grid;
-    const int cnt = wave_scan<true>(i, spos[t], rc2, gi, cell_start, spos, sj[w], sd[w], lane);
+    const int cnt = wave_scan<true>(i, spos[t], rc2, gi, cell_start, spos, sj[w], lane);
     wave_pad_keys(sj[w], nullptr, cnt, lane);
     wave_lds_sync();
     wave_write_sorted(sj[w], cnt, nbr_idx + nbr_start[i], lane);
@@ -576,6 +595,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, do
 // Capped rows: keep the K nearest by (d2, j), written sorted by j and padded with -1.
 // Targets with more than kWaveCap candidates get nbr_len = -1 for k_fill_capped.
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n, int K, double rc2,
+                                                                          const float *__restrict__ pos,
                                                                           const GridInfo *__restrict__ grid,
                                                                           const int32_t *__restrict__ cell_start,
                                                                           const int32_t *__restrict__ order,
@@ -592,7 +612,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
     const GridInfo gi = *grid;
     int32_t *cj = sj[w];
     double *cd = sd[w];
-    const int cnt = wave_scan<true>(i, spos[t], rc2, gi, cell_start, spos, cj, cd, lane);
+    const float4 pi = spos[t];
+    const int cnt = wave_scan<true>(i, pi, rc2, gi, cell_start, spos, cj, lane);
     int32_t *row = nbr_idx + (size_t)i * K;
     if (lane == 0) nbr_start[i] = (int32_t)((size_t)i * K);
     if (cnt > kWaveCap) {
@@ -605,6 +626,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
     if (cnt <= K) {
         wave_write_sorted(cj, cnt, row, lane);
     } else {
+        // exact squared distances of the candidates, for the (d2, j) order
+        for (int e = lane; e < cnt; e += 64) {
+            const int j = cj[e];
+            cd[e] = pair_d2((double)pi.x, (double)pi.y, (double)pi.z,
+                            make_float4(pos[3 * (size_t)j], pos[3 * (size_t)j + 1], pos[3 * (size_t)j + 2], 0.f));
+        }
+        wave_lds_sync();
         int32_t *kj = reinterpret_cast<int32_t *>(cd);   // the distances are no longer needed after ranking
         wave_select_nearest(cd, cj, cnt, K, kj, lane);
         wave_pad_keys(kj, nullptr, K, lane);
@@ -660,7 +688,7 @@ hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, v
                                                       nbr_start, nbr_len, nbr_idx);
     } else {
         k_fill_capped_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(
-            n, K, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
+            n, K, rc2, pos, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
         k_fill_capped<<<nblk(n, 128), 128, 0, stream>>>(n, K, rc2, pos, L.grid, L.cell_start, L.order, L.spos,
                                                          nbr_start, nbr_len, nbr_idx);
     }
