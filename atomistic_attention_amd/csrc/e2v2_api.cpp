@@ -260,7 +260,7 @@ AttnWs attn_ws(const e2v2_layer_desc &d, int n)
     size_t o = 0;
     w.q = o; o += al256(N * C * 4);
     w.k = o; o += al256(N * C * 4);
-    w.v = o; o += al256(N * NC * C * 4);
+    w.v = o; o += al256(d.storage == E2V2_BF16 ? 0 : N * NC * C * 4);   // bf16: v stays in registers
     w.hp = o; o += al256(N * NC * C * s);
     w.dmat = o; o += al256(N * nd * 4);
     w.pos4 = o; o += al256(N * 16);
@@ -449,6 +449,10 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
     }
     if (target_order && !aligned16(target_order)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    if (taps)
+        for (const void *p : {(const void *)taps->q, (const void *)taps->k, (const void *)taps->v,
+                              (const void *)taps->hprime, (const void *)taps->m, (const void *)taps->hhat})
+            if (p && !aligned16(p)) return fail(E2V2_ERR_ARG, "tap pointers must be 16-byte aligned");
     const AttnWs L = attn_ws(*desc, n);
     if (workspace_bytes < L.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, L.total);
     char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
@@ -489,19 +493,37 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         e = launch_pack_weights(src, dst, cnt, C, stream);
         if (e != hipSuccess) return hip_fail(e, "weight packing kernel");
     }
-    for (int l = 0; l <= lmax; ++l)
-        for (int m = 0; m < 2 * l + 1; ++m)
-            jobs[nj++] = ProjJob{h, (long long)NC * C, wv(l), v, (long long)NC * C, l * l + m};
-    jobs[nj++] = ProjJob{h, (long long)NC * C, bf ? (const void *)(wp + (size_t)(lmax + 1) * wsz) : w->w_q, q, (long long)C, 0};
-    jobs[nj++] = ProjJob{h, (long long)NC * C, bf ? (const void *)(wp + (size_t)(lmax + 2) * wsz) : w->w_k, k, (long long)C, 0};
-    e = bf ? launch_proj_bf16(jobs, nj, 0, n, C, stream) : launch_proj(jobs, nj, 0, 0, n, C, stream);
-    if (e == hipSuccess) e = mark(1);
-    if (e != hipSuccess) return hip_fail(e, "projection kernel");
-    // Step 3: source coupling h' (EAAS), per-node D blocks and padded positions.
-    e = launch_eaas(lmax, pos, v, 0, w->w_src, n, C, hp, bf ? 2 : 0, taps ? taps->hprime : nullptr, dmat, pos4,
-                    stream);
-    if (e == hipSuccess) e = mark(2);
-    if (e != hipSuccess) return hip_fail(e, "source EAAS kernel");
+    if (bf) {
+        // Steps 2-3 fused: q, k, v on bf16 MFMA with the source EAAS applied to v in
+        // registers (v itself is never stored unless tapped).
+        QkvEaasArgs qa{};
+        qa.h = reinterpret_cast<const uint16_t *>(h);
+        qa.wv = reinterpret_cast<const uint4 *>(wp);
+        qa.wq = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 1) * wsz);
+        qa.wk = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 2) * wsz);
+        qa.w_src = w->w_src; qa.pos = pos;
+        qa.q = q; qa.k = k; qa.hp = reinterpret_cast<uint16_t *>(hp); qa.pos4 = pos4; qa.dmat = dmat;
+        qa.v_tap = taps ? taps->v : nullptr;
+        qa.hp_tap = taps ? taps->hprime : nullptr;
+        qa.n = n;
+        e = launch_qkv_eaas(lmax, qa, C, stream);
+        if (e == hipSuccess) e = mark(1);
+        if (e == hipSuccess) e = mark(2);
+        if (e != hipSuccess) return hip_fail(e, "projection + source EAAS kernel");
+    } else {
+        for (int l = 0; l <= lmax; ++l)
+            for (int m = 0; m < 2 * l + 1; ++m)
+                jobs[nj++] = ProjJob{h, (long long)NC * C, wv(l), v, (long long)NC * C, l * l + m};
+        jobs[nj++] = ProjJob{h, (long long)NC * C, w->w_q, q, (long long)C, 0};
+        jobs[nj++] = ProjJob{h, (long long)NC * C, w->w_k, k, (long long)C, 0};
+        e = launch_proj(jobs, nj, 0, 0, n, C, stream);
+        if (e == hipSuccess) e = mark(1);
+        if (e != hipSuccess) return hip_fail(e, "projection kernel");
+        // Step 3: source coupling h' (EAAS), per-node D blocks and padded positions.
+        e = launch_eaas(lmax, pos, v, 0, w->w_src, n, C, hp, 0, taps ? taps->hprime : nullptr, dmat, pos4, stream);
+        if (e == hipSuccess) e = mark(2);
+        if (e != hipSuccess) return hip_fail(e, "source EAAS kernel");
+    }
     // Steps 4-5: streaming attention + target coupling.
     AttnArgs a{};
     a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dmat = dmat;
@@ -523,7 +545,7 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
     if (taps) {
         const size_t N = (size_t)n;
         struct { void *dst; const void *src; size_t bytes; } cp[] = {
-            {taps->q, q, N * C * 4}, {taps->k, k, N * C * 4}, {taps->v, v, N * NC * C * 4},
+            {taps->q, q, N * C * 4}, {taps->k, k, N * C * 4}, {bf ? nullptr : taps->v, v, N * NC * C * 4},
             {taps->hhat, hhat, N * NC * C * 4}};
         for (auto &c : cp)
             if (c.dst) {

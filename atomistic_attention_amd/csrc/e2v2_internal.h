@@ -301,6 +301,24 @@ hipError_t launch_proj(const ProjJob *jobs, int njobs, int a_bf16, int b_bf16, i
 hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, int count, int C, hipStream_t stream);
 hipError_t launch_proj_bf16(const ProjJob *jobs, int njobs, int a_f32, int n, int C, hipStream_t stream);
 
+// Fused q / k / v projections and source EAAS for bf16 storage: h bf16
+// [n][NC][C]; wv = packed W_V[0..L] (C*C/8 uint4 each), wq, wk packed W_Q, W_K;
+// w_src [P][C].  Outputs q, k [n][C] fp32; hp fp16 in the hp_f16_offset layout
+// with the node's scale in pos4[node].w; dmat [n][n_dmat(L)].  v_tap and hp_tap
+// (optional, fp32 [n][NC][C]) receive v and h' as stored (dequantised).
+struct QkvEaasArgs {
+    const uint16_t *h;
+    const uint4 *wv, *wq, *wk;
+    const float *w_src, *pos;
+    float *q, *k;
+    uint16_t *hp;
+    float4 *pos4;
+    float *dmat;
+    float *v_tap, *hp_tap;
+    int n;
+};
+hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t stream);
+
 struct AttnArgs {
     const float *q, *k;              // [n][C] fp32
     const void *hp;                  // [n][NC][C] fp32, or fp16 (hp_f16_offset layout) scaled by pos4[j].w

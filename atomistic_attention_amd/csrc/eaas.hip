@@ -3,10 +3,9 @@
 // rotate features, sparse re-index, inverse rotation; section 2.3 Proposition
 // 4.3: the result equals the dense SO(3) tensor product).
 //
-// One block of 256 threads covers 256 / C nodes.  The first threads build each
-// node's Wigner-D blocks in fp64 (once per node, shared through LDS); then one
-// thread per (node, channel) applies rotate-in, the m re-index and rotate-out
-// entirely in registers.  Reads and writes are channel-contiguous.
+// Each node's Wigner-D blocks are built once in fp64 and shared through LDS;
+// each (node, channel) pair then applies rotate-in, the m re-index and
+// rotate-out entirely in registers.  Reads and writes are channel-contiguous.
 #include "e2v2_internal.h"
 
 namespace e2v2 {
@@ -25,6 +24,16 @@ enum { kYF32 = 0, kYBF16 = 1, kYF16S = 2 };
 __device__ __forceinline__ uint16_t f_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 __device__ __forceinline__ float f16_to_f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// One block of 256 threads covers NPB = min(32, 256 * PPT / C) nodes.  Threads
+// 0..NPB-1 build one node's Wigner-D blocks each (fp64), shared through LDS; then
+// every thread handles up to PPT (node, channel) pairs, all in registers.  For
+// the scaled-fp16 output the node's largest magnitude is reduced in LDS first.
+template <int L> constexpr int eaas_pairs() { return L >= 3 ? 4 : 8; }
+template <int L> __host__ __device__ inline int eaas_nodes_per_block(int C)
+{
+    return (256 * eaas_pairs<L>() / C) < 32 ? (256 * eaas_pairs<L>() / C) : 32;
+}
+
 template <int L, typename TX, int YF>
 __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos, const TX *__restrict__ x,
                                                    const float *__restrict__ path_w, int n, int C,
@@ -39,7 +48,8 @@ __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos
     __shared__ int sDir[32];
     __shared__ unsigned sMax[32];
 
-    const int npb = 256 / C;
+    constexpr int kEaasPairs = eaas_pairs<L>();
+    const int npb = eaas_nodes_per_block<L>(C);
     const int t = threadIdx.x;
     const long long node0 = (long long)blockIdx.x * npb;
     if (t < 32) sMax[t] = 0u;
@@ -59,57 +69,68 @@ __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos
         }
     }
     __syncthreads();
-    const int ln = t / C, c = t - ln * C;
-    const long long node = node0 + ln;
-    const bool active = ln < npb && node < n;
-    float yv[NC];
-    const size_t base = (size_t)node * NC * C + c;
-    if (active) {
+    // pairs idx = t + 256 q: node ln = idx / C, channel c = idx % C
+    constexpr int KEEP = YF == kYF16S ? kEaasPairs : 1;   // fp16 output waits for the node's scale
+    float yv[KEEP][NC];
+#pragma unroll
+    for (int q = 0; q < kEaasPairs; ++q) {
+        const int idx = t + 256 * q;
+        const int ln = idx / C, c = idx - ln * C;
+        const long long node = node0 + ln;
+        if (ln >= npb || node >= n) continue;
+        const size_t base = (size_t)node * NC * C + c;
         float xv[NC], w[P];
 #pragma unroll
         for (int e = 0; e < NC; ++e) xv[e] = ld_elem<TX>(x, base + (size_t)e * C);
 #pragma unroll
         for (int p = 0; p < P; ++p) w[p] = path_w[p * C + c];
-        eaas_channel<L>(&sD[ln][0], xv, yv, w, tabs.eaas, sDir[ln] != 0);
-    }
-    if constexpr (YF == kYF16S) {
-        if (active) {
+        float (&yq)[NC] = yv[YF == kYF16S ? q : 0];
+        eaas_channel<L>(&sD[ln][0], xv, yq, w, tabs.eaas, sDir[ln] != 0);
+        if constexpr (YF == kYF16S) {
             float m = 0.f;
 #pragma unroll
-            for (int e = 0; e < NC; ++e) m = fmaxf(m, fabsf(yv[e]));
-            atomicMax(&sMax[ln], __float_as_uint(m));       // non-negative floats order like their bits
-        }
-        __syncthreads();
-        if (!active) return;
-        const unsigned mb = sMax[ln];
-        unsigned sb = 127u, ib = 127u;                      // scale 1 for zero or non-finite rows
-        if (mb != 0u && mb < 0x7f800000u) {
-            const unsigned b = mb >> 23;                    // M < 2^(b-126); s = 2^(b-140)
-            sb = b > 13u ? b - 13u : 1u;
-            ib = 254u - sb;
-        }
-        const float sc = __uint_as_float(sb << 23), inv = __uint_as_float(ib << 23);
-        uint16_t *y = reinterpret_cast<uint16_t *>(y_) + (size_t)node * NC * C;
+            for (int e = 0; e < NC; ++e) m = fmaxf(m, fabsf(yq[e]));
+            atomicMax(&sMax[ln], __float_as_uint(m));   // non-negative floats order like their bits
+        } else {
 #pragma unroll
-        for (int e = 0; e < NC; ++e) {
-            const uint16_t hb = f_to_f16(yv[e] * inv);
-            y[hp_f16_offset(e, c, NC, C)] = hb;
-            if (y_deq) y_deq[base + (size_t)e * C] = f16_to_f(hb) * sc;
-        }
-        if (c == 0 && pos4_out)
-            pos4_out[node] = make_float4(pos[3 * node], pos[3 * node + 1], pos[3 * node + 2], sc);
-    } else {
-        if (!active) return;
-#pragma unroll
-        for (int e = 0; e < NC; ++e) {
-            if (YF == kYBF16) {
-                const uint16_t hb = f_to_bf16(yv[e]);
-                reinterpret_cast<uint16_t *>(y_)[base + (size_t)e * C] = hb;
-                if (y_deq) y_deq[base + (size_t)e * C] = bf16_to_f(hb);
-            } else {
-                reinterpret_cast<float *>(y_)[base + (size_t)e * C] = yv[e];
-                if (y_deq) y_deq[base + (size_t)e * C] = yv[e];
+            for (int e = 0; e < NC; ++e) {
+                if (YF == kYBF16) {
+                    const uint16_t hb = f_to_bf16(yq[e]);
+                    reinterpret_cast<uint16_t *>(y_)[base + (size_t)e * C] = hb;
+                    if (y_deq) y_deq[base + (size_t)e * C] = bf16_to_f(hb);
+                } else {
+                    reinterpret_cast<float *>(y_)[base + (size_t)e * C] = yq[e];
+                    if (y_deq) y_deq[base + (size_t)e * C] = yq[e];
+                }
             }
+        }
+    }
+    if constexpr (YF == kYF16S) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kEaasPairs; ++q) {
+            const int idx = t + 256 * q;
+            const int ln = idx / C, c = idx - ln * C;
+            const long long node = node0 + ln;
+            if (ln >= npb || node >= n) continue;
+            const unsigned mb = sMax[ln];
+            unsigned sb = 127u, ib = 127u;                      // scale 1 for zero or non-finite rows
+            if (mb != 0u && mb < 0x7f800000u) {
+                const unsigned b = mb >> 23;                    // M < 2^(b-126); s = 2^(b-140)
+                sb = b > 13u ? b - 13u : 1u;
+                ib = 254u - sb;
+            }
+            const float sc = __uint_as_float(sb << 23), inv = __uint_as_float(ib << 23);
+            uint16_t *y = reinterpret_cast<uint16_t *>(y_) + (size_t)node * NC * C;
+            const size_t base = (size_t)node * NC * C + c;
+#pragma unroll
+            for (int e = 0; e < NC; ++e) {
+                const uint16_t hb = f_to_f16(yv[q][e] * inv);
+                y[hp_f16_offset(e, c, NC, C)] = hb;
+                if (y_deq) y_deq[base + (size_t)e * C] = f16_to_f(hb) * sc;
+            }
+            if (c == 0 && pos4_out)
+                pos4_out[node] = make_float4(pos[3 * node], pos[3 * node + 1], pos[3 * node + 2], sc);
         }
     }
 }
@@ -131,7 +152,7 @@ template <int L>
 static hipError_t launch_eaas_l(const float *pos, const void *x, int x_bf16, const float *path_w, int n, int C,
                                 void *y, int yf, float *y_deq, float *dmat_out, float4 *pos4_out, hipStream_t stream)
 {
-    const int npb = 256 / C;
+    const int npb = eaas_nodes_per_block<L>(C);
     dim3 grid((unsigned)((n + npb - 1) / npb));
     Tables tb = host_tables();
     tb.eaas = eaas_table(L);

@@ -1,0 +1,364 @@
+// Fused projections + source coupling for bf16 storage (E2Former-V2 explainer,
+// section 2.3: q and k from the invariant block, v = W_V[l] h per degree, then the
+// source-side EAAS h'_j = EAAS(v_j) of section 2.2 / Proposition 4.3).
+//
+// One block covers 16 nodes and all C channels.  The 16 nodes' bf16 input rows
+// (contiguous in HBM) are staged once in LDS; wave nb owns output channels
+// 16 nb .. 16 nb + 15 and runs v_mfma_f32_16x16x32_bf16 in the transposed
+// orientation (A = packed W^T fragment, B = 16 nodes' input rows), one
+// accumulator per component.  Each lane then holds all NC components of 4
+// consecutive channels of one node, so the EAAS (rotate in, sparse re-index,
+// rotate out) runs in registers on the accumulators, with the node's Wigner-D
+// blocks (built beforehand in fp64 by k_node_frames) and the path weights staged
+// in LDS.
+// v never reaches HBM: the only outputs are q, k, h' (fp16 with a per-node
+// power-of-two scale, component-pair interleaved), the D blocks and pos4.
+#include "e2v2_internal.h"
+
+namespace e2v2 {
+
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
+{
+    return uint32_t(__builtin_bit_cast(uint16_t, (_Float16)a)) |
+           (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)b)) << 16);
+}
+__device__ __forceinline__ float f16lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, uint16_t(u & 0xffffu)); }
+__device__ __forceinline__ float f16hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, uint16_t(u >> 16)); }
+
+}  // namespace
+
+// One multiply-add of the aligned-frame coupling: output component `out`
+// receives coefficient c[p][cc] times path weight p times input component `in`;
+// lf > 0 terms vanish for a node at the origin.
+struct CTerm {
+    int p, out, in, cc, lf;
+};
+template <int L>
+struct CTerms {
+    int n;
+    CTerm t[(2 * kMaxL + 1) * kMaxPaths];
+};
+template <int L>
+constexpr CTerms<L> couple_terms()
+{
+    CTerms<L> r = {};
+    int n = 0;
+    for (int lo = 0; lo <= L; ++lo)
+        for (int li = 0; li <= L; ++li)
+            for (int lf = 0; lf <= L; ++lf) {
+                if (!is_path(li, lf, lo)) continue;
+                const int p = path_index(L, li, lf, lo);
+                const bool odd = ((li + lf + lo) & 1) != 0;
+                const int mm = li < lo ? li : lo;
+                for (int mo = -mm; mo <= mm; ++mo) {
+                    if (odd && mo == 0) continue;
+                    const int mi = odd ? -mo : mo;
+                    r.t[n++] = CTerm{p, lo * lo + lo + mo, li * li + li + mi, mo + lo, lf};
+                }
+            }
+    r.n = n;
+    return r;
+}
+
+// Per-node Wigner-D blocks of the alignment rotation, fp64, stored as fp32.
+template <int L>
+__global__ __launch_bounds__(256) void k_node_frames(const float *__restrict__ pos, int n, float *__restrict__ dmat,
+                                                     const DSample ds)
+{
+    const long long node = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (node >= n) return;
+    double Dd[n_dmat(L)];
+    wigner_blocks<L>(pos[3 * node], pos[3 * node + 1], pos[3 * node + 2], ds, Dd);
+#pragma unroll
+    for (int e = 0; e < n_dmat(L); ++e) dmat[node * n_dmat(L) + e] = (float)Dd[e];
+}
+
+template <int L, int C>
+__global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, const EaasCoef tab)
+{
+    constexpr int NC = n_comp(L), NB = C / 16, KB = C / 32, P = path_count(L);
+    constexpr int NDM = n_dmat(L);
+    constexpr int ND = NDM > 0 ? NDM : 1;
+    constexpr int U = NC * C / 8;                 // 16-byte units per node row
+    constexpr int ROW = NC * C * 2 + 16;          // LDS bytes per node row (pad spreads banks)
+    constexpr int WS = (P & 1) ? P : P + 1;       // LDS stride of one channel's path weights (odd)
+    constexpr int NT = 64 * NB;
+    constexpr int PER = (16 * U + NT - 1) / NT;   // staged units per thread
+    constexpr int PW = (P * C + NT - 1) / NT;     // staged path weights per thread
+    constexpr int PD = (16 * ND + NT - 1) / NT;   // staged D entries per thread
+    __shared__ __align__(16) unsigned char sH[16 * ROW];
+    __shared__ float sD[16 * ND];
+    __shared__ float sW[C * WS];
+    __shared__ unsigned sMax[NB][16];
+
+    const int t = threadIdx.x, lane = t & 63, nb = t >> 6, g = lane >> 4, nl = lane & 15;
+    const long long node0 = (long long)blockIdx.x * 16;
+    const int nvalid = (a.n - node0) < 16 ? (int)(a.n - node0) : 16;
+
+    // Stage the input rows, D blocks and path weights: all loads are issued
+    // before the first LDS write.
+    uint4 st[PER];
+    const uint4 *hsrc = reinterpret_cast<const uint4 *>(a.h) + node0 * U;
+    if (nvalid == 16) {
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int u = t + r * NT;
+            if (r + 1 < PER || u < 16 * U) st[r] = hsrc[u];
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int u = t + r * NT;
+            st[r] = (u < 16 * U && u / U < nvalid) ? hsrc[u] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    float wst[PW], dst[PD];
+#pragma unroll
+    for (int r = 0; r < PW; ++r) {
+        const int u = t + r * NT;
+        wst[r] = u < P * C ? a.w_src[u] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < PD; ++r) {
+        const int u = t + r * NT;
+        dst[r] = (NDM > 0 && u < 16 * ND && u / ND < nvalid) ? a.dmat[node0 * ND + u] : 0.f;
+    }
+    auto afrag = [&](const uint4 *w, int kb) { return __builtin_bit_cast(bf16x8, w[(nb * KB + kb) * 64 + lane]); };
+    bf16x8 wv0[KB], wq[KB], wk[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        wv0[kb] = afrag(a.wv, kb);
+        wq[kb] = afrag(a.wq, kb);
+        wk[kb] = afrag(a.wk, kb);
+    }
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int u = t + r * NT;
+        if (r + 1 < PER || u < 16 * U) {
+            const int nd = u / U;
+            *reinterpret_cast<uint4 *>(sH + nd * ROW + (u - nd * U) * 16) = st[r];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < PW; ++r) {
+        const int u = t + r * NT;
+        if (u < P * C) {
+            const int p = u / C, c = u - p * C;
+            sW[c * WS + p] = wst[r];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < PD; ++r) {
+        const int u = t + r * NT;
+        if (u < 16 * ND) sD[u] = dst[r];
+    }
+    __syncthreads();
+
+    // Projections: lane (g, nl) accumulates channels 16 nb + 4 g + (0..3) of node nl.
+    const unsigned char *brow = sH + nl * ROW + g * 16;
+    auto bfrag = [&](int e, int kb) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(brow + e * (C * 2) + kb * 64));
+    };
+    const long long node = node0 + nl;
+    const bool valid = nl < nvalid;
+    const int c0 = 16 * nb + 4 * g;
+    floatx4 acc[NC];
+    bf16x8 wnext[KB];
+    if constexpr (L >= 1) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) wnext[kb] = afrag(a.wv + (size_t)(C * C / 8), kb);
+    }
+    {
+        floatx4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, av = aq;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 b = bfrag(0, kb);
+            av = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv0[kb], b, av, 0, 0, 0);
+            aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wq[kb], b, aq, 0, 0, 0);
+            ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wk[kb], b, ak, 0, 0, 0);
+        }
+        acc[0] = av;
+        if (valid) {
+            *reinterpret_cast<float4 *>(a.q + node * C + c0) = make_float4(aq[0], aq[1], aq[2], aq[3]);
+            *reinterpret_cast<float4 *>(a.k + node * C + c0) = make_float4(ak[0], ak[1], ak[2], ak[3]);
+        }
+    }
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        bf16x8 wf[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) wf[kb] = wnext[kb];
+        if (l < L) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) wnext[kb] = afrag(a.wv + (size_t)(l + 1) * (C * C / 8), kb);
+        }
+#pragma unroll
+        for (int m = 0; m < 2 * l + 1; ++m) {
+            floatx4 ac = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[kb], bfrag(l * l + m, kb), ac, 0, 0, 0);
+            acc[l * l + m] = ac;
+        }
+    }
+    if (a.v_tap && valid) {
+#pragma unroll
+        for (int e = 0; e < NC; ++e)
+            *reinterpret_cast<float4 *>(a.v_tap + (node * NC + e) * C + c0) =
+                make_float4(acc[e][0], acc[e][1], acc[e][2], acc[e][3]);
+    }
+
+    // Source EAAS on the accumulators, in three passes over the lane's 4 channels
+    // so that only one D^l block is live at a time: rotate into the aligned frame
+    // (D^T x), the sparse m re-index with the path weights, rotate back (D y).
+    const float *Dn = sD + nl * ND;
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        constexpr int KM = 2 * L + 1;
+        const int k = 2 * l + 1, o = l * l;
+        float Dl[KM * KM];
+#pragma unroll
+        for (int r = 0; r < k * k; ++r) Dl[r] = Dn[dmat_offset(l) + r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float tmp[KM];
+#pragma unroll
+            for (int b = 0; b < k; ++b) {
+                float s2 = 0.f;
+#pragma unroll
+                for (int aa = 0; aa < k; ++aa) s2 = fmaf(Dl[aa * k + b], acc[o + aa][i], s2);
+                tmp[b] = s2;
+            }
+#pragma unroll
+            for (int b = 0; b < k; ++b) acc[o + b][i] = tmp[b];
+        }
+    }
+    {
+        // the encoding of r = 0 is Y_0 only: paths with l_f > 0 drop out
+        const long long nc = valid ? node : node0;
+        const double px = a.pos[3 * nc], py = a.pos[3 * nc + 1], pz = a.pos[3 * nc + 2];
+        const float fdir = (px * px + py * py + pz * pz > 0.0) ? 1.f : 0.f;
+        constexpr CTerms<L> T = couple_terms<L>();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float *w = &sW[(c0 + i) * WS];
+            float loc[NC];
+#pragma unroll
+            for (int e = 0; e < NC; ++e) loc[e] = 0.f;
+#pragma unroll
+            for (int q = 0; q < T.n; ++q) {
+                const float wp = T.t[q].lf > 0 ? w[T.t[q].p] * fdir : w[T.t[q].p];
+                loc[T.t[q].out] = fmaf(wp * tab.c[T.t[q].p][T.t[q].cc], acc[T.t[q].in][i], loc[T.t[q].out]);
+            }
+#pragma unroll
+            for (int e = 0; e < NC; ++e) acc[e][i] = loc[e];
+        }
+    }
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        constexpr int KM = 2 * L + 1;
+        const int k = 2 * l + 1, o = l * l;
+        float Dl[KM * KM];
+#pragma unroll
+        for (int r = 0; r < k * k; ++r) Dl[r] = Dn[dmat_offset(l) + r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float tmp[KM];
+#pragma unroll
+            for (int aa = 0; aa < k; ++aa) {
+                float s2 = 0.f;
+#pragma unroll
+                for (int b = 0; b < k; ++b) s2 = fmaf(Dl[aa * k + b], acc[o + b][i], s2);
+                tmp[aa] = s2;
+            }
+#pragma unroll
+            for (int aa = 0; aa < k; ++aa) acc[o + aa][i] = tmp[aa];
+        }
+    }
+
+    // Per-node scale: largest |h'| over all components and channels.  Magnitude
+    // bit patterns order like the values; NaN sorts above inf and selects scale 1.
+    unsigned mb = 0u;
+#pragma unroll
+    for (int e = 0; e < NC; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mb = max(mb, __float_as_uint(acc[e][i]) & 0x7fffffffu);
+    mb = max(mb, (unsigned)__shfl_xor((int)mb, 16));
+    mb = max(mb, (unsigned)__shfl_xor((int)mb, 32));
+    if (g == 0) sMax[nb][nl] = mb;
+    __syncthreads();
+    mb = 0u;
+#pragma unroll
+    for (int w = 0; w < NB; ++w) mb = max(mb, sMax[w][nl]);
+    unsigned sb = 127u, ib = 127u;                        // scale 1 for zero or non-finite rows
+    if (mb != 0u && mb < 0x7f800000u) {
+        const unsigned b = mb >> 23;                      // M < 2^(b-126); s = 2^(b-140)
+        sb = b > 13u ? b - 13u : 1u;
+        ib = 254u - sb;
+    }
+    const float sc = __uint_as_float(sb << 23), inv = __uint_as_float(ib << 23);
+    if (!valid) return;
+    uint16_t *hp = a.hp + node * (NC * C);
+#pragma unroll
+    for (int j = 0; j < NC / 2; ++j) {
+        const floatx4 y0 = acc[2 * j], y1 = acc[2 * j + 1];
+        const uint4 o = make_uint4(pack_f16x2(y0[0] * inv, y0[1] * inv), pack_f16x2(y0[2] * inv, y0[3] * inv),
+                                   pack_f16x2(y1[0] * inv, y1[1] * inv), pack_f16x2(y1[2] * inv, y1[3] * inv));
+        *reinterpret_cast<uint4 *>(hp + j * 2 * C + (c0 >> 2) * 8) = o;
+        if (a.hp_tap) {
+            float *d0 = a.hp_tap + (node * NC + 2 * j) * C + c0;
+            *reinterpret_cast<float4 *>(d0) =
+                make_float4(f16lo(o.x) * sc, f16hi(o.x) * sc, f16lo(o.y) * sc, f16hi(o.y) * sc);
+            *reinterpret_cast<float4 *>(d0 + C) =
+                make_float4(f16lo(o.z) * sc, f16hi(o.z) * sc, f16lo(o.w) * sc, f16hi(o.w) * sc);
+        }
+    }
+    if constexpr ((NC & 1) != 0) {
+        const floatx4 y0 = acc[NC - 1];
+        const uint2 o = make_uint2(pack_f16x2(y0[0] * inv, y0[1] * inv), pack_f16x2(y0[2] * inv, y0[3] * inv));
+        *reinterpret_cast<uint2 *>(hp + (NC - 1) * C + c0) = o;
+        if (a.hp_tap)
+            *reinterpret_cast<float4 *>(a.hp_tap + (node * NC + NC - 1) * C + c0) =
+                make_float4(f16lo(o.x) * sc, f16hi(o.x) * sc, f16lo(o.y) * sc, f16hi(o.y) * sc);
+    }
+    if (nb == 0 && g == 0)
+        a.pos4[node] = make_float4(a.pos[3 * node], a.pos[3 * node + 1], a.pos[3 * node + 2], sc);
+}
+
+template <int L>
+static hipError_t launch_qkv_eaas_l(const QkvEaasArgs &a, int C, hipStream_t stream)
+{
+    if constexpr (n_dmat(L) > 0) {
+        k_node_frames<L><<<dim3((unsigned)((a.n + 255) / 256)), 256, 0, stream>>>(a.pos, a.n, a.dmat, host_tables().ds);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const EaasCoef &tab = eaas_table(L);
+    const dim3 grid((unsigned)((a.n + 15) / 16));
+    switch (C) {
+    case 32: qkv_eaas_kernel<L, 32><<<grid, 128, 0, stream>>>(a, tab); break;
+    case 64: qkv_eaas_kernel<L, 64><<<grid, 256, 0, stream>>>(a, tab); break;
+    case 128: qkv_eaas_kernel<L, 128><<<grid, 512, 0, stream>>>(a, tab); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t stream)
+{
+    if (a.n <= 0) return hipSuccess;
+    switch (L) {
+    case 0: return launch_qkv_eaas_l<0>(a, C, stream);
+    case 1: return launch_qkv_eaas_l<1>(a, C, stream);
+    case 2: return launch_qkv_eaas_l<2>(a, C, stream);
+    case 3: return launch_qkv_eaas_l<3>(a, C, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace e2v2

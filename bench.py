@@ -178,7 +178,7 @@ def main():
     wall = time.perf_counter() - t0
 
     stages = np.array([[events[k][a].elapsed_time(events[k][a + 1]) for a in range(5)] for k in range(args.steps)])
-    mean = stages.mean(axis=0)          # ms: neighbours, projections, source EAAS, attention, output projection
+    mean = stages.mean(axis=0)          # ms per stage between consecutive events
     ms_step = wall * 1e3 / args.steps
     nnz = int(length.sum().item())
     ab = algorithmic_bytes(cfg, nnz)
@@ -188,10 +188,24 @@ def main():
     layer_ms = float(mean[1:].sum())
     C, nc, s = cfg.channels, cfg.n_comp, (2 if cfg.storage == "bf16" else 4)
     nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
-    layer_bytes = (N * nc * C * s + N * C * 8 + N * nc * C * 4            # projections: h in; q, k, v out
-                   + N * nc * C * 4 + N * 12 + N * nc * C * s + N * (4 * nd + 16)   # source EAAS
+    if cfg.storage == "bf16":
+        # fused projections + source EAAS: h in; q, k, h' (16-bit), D blocks, pos4 out
+        front = N * nc * C * 2 + N * C * 8 + N * 12 + N * nc * C * 2 + N * (4 * nd + 16)
+        stage_names = ("neighbours", "projections+source_eaas", None, "attention", "output_projection")
+    else:
+        front = (N * nc * C * s + N * C * 8 + N * nc * C * 4                          # projections
+                 + N * nc * C * 4 + N * 12 + N * nc * C * s + N * (4 * nd + 16))    # source EAAS
+        stage_names = ("neighbours", "projections", "source_eaas", "attention", "output_projection")
+    layer_bytes = (front
                    + ab["total"]                                          # streaming attention + target EAAS
                    + 2 * N * nc * C * 4)                                  # output projection
+    stage_ms = {}
+    for name, v in zip(stage_names, mean):
+        if name is None:
+            stage_ms[prev] += float(v)      # the two events of a fused stage are recorded back to back
+        else:
+            stage_ms[name] = float(v)
+            prev = name
 
     rec = {
         "metric": METRIC,
@@ -212,8 +226,7 @@ def main():
                         f"{cfg.storage} storage, fp32 arithmetic",
             "nnz": nnz,
             "steps_per_s": 1e3 / ms_step,
-            "stage_ms": {"neighbours": float(mean[0]), "projections": float(mean[1]), "source_eaas": float(mean[2]),
-                         "attention": float(mean[3]), "output_projection": float(mean[4])},
+            "stage_ms": stage_ms,
             "layer_ms_excl_neighbours": layer_ms,
             "layer_pairs_per_s_excl_neighbours": nnz / (layer_ms * 1e-3),
             "layer_hbm_frac_excl_neighbours": layer_bytes / (layer_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),

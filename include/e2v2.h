@@ -86,9 +86,11 @@ typedef struct {
     const float *w_src, *w_tgt;
 } e2v2_weights;
 
-/* Optional copies of the layer's intermediates (device pointers; any may be NULL)
- * and optional stage timing.  Intended for validation and measurement;
- * production callers pass NULL taps. */
+/* Optional copies of the layer's intermediates (device pointers, 16-byte
+ * aligned; any may be NULL) and optional stage timing.  Intended for validation
+ * and measurement; production callers pass NULL taps.  For bf16 storage steps 2
+ * and 3 run as one kernel (v is projected and coupled in registers), so the
+ * events after step 2 and after step 3 are recorded back to back. */
 typedef struct {
     float *q;        /* [n][C] fp32                                         */
     float *k;        /* [n][C] fp32                                         */

@@ -101,8 +101,14 @@ def test_workspace_sizes(lib):
     d = _desc()
     a, b = lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 1000), lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 2000)
     assert 0 < a < b
-    # q, k fp32 + v fp32 + h' bf16 + D blocks + padded positions + hhat fp32 per node
-    per_node = 128 * 4 * 2 + 9 * 128 * 4 + 9 * 128 * 2 + 34 * 4 + 16 + 9 * 128 * 4
+    # bf16 storage: q, k fp32 + h' 16-bit + D blocks + padded positions + hhat fp32
+    # per node (v is projected and coupled in registers, never stored)
+    per_node = 128 * 4 * 2 + 9 * 128 * 2 + 34 * 4 + 16 + 9 * 128 * 4
+    assert abs((b - a) / 1000 - per_node) < 2
+    # fp32 storage adds v and stores h' in fp32
+    d32 = _desc(storage=B.E2V2_FP32)
+    a, b = lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 1000), lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 2000)
+    per_node = 128 * 4 * 2 + 9 * 128 * 4 + 9 * 128 * 4 + 34 * 4 + 16 + 9 * 128 * 4
     assert abs((b - a) / 1000 - per_node) < 2
     assert lib.e2v2_build_neighbors_workspace_bytes(1000, 0) > 0
 
