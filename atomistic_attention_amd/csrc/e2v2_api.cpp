@@ -535,11 +535,21 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
     if (e == hipSuccess) e = mark(3);
     if (e != hipSuccess) return hip_fail(e, "attention kernel");
     // Step 6: output projection.
-    nj = 0;
-    for (int l = 0; l <= lmax; ++l)
-        for (int m = 0; m < 2 * l + 1; ++m)
-            jobs[nj++] = ProjJob{hhat, (long long)NC * C, wo(l), out, (long long)NC * C, l * l + m};
-    e = bf ? launch_proj_bf16(jobs, nj, 1, n, C, stream) : launch_proj(jobs, nj, 0, 0, n, C, stream);
+    if (bf) {
+        OutProjArgs oa{};
+        oa.hhat = hhat;
+        oa.wo = reinterpret_cast<const uint4 *>(wo(0));
+        oa.out = out;
+        oa.n = n;
+        oa.lmax = lmax;
+        e = launch_outproj_bf16(oa, C, stream);
+    } else {
+        nj = 0;
+        for (int l = 0; l <= lmax; ++l)
+            for (int m = 0; m < 2 * l + 1; ++m)
+                jobs[nj++] = ProjJob{hhat, (long long)NC * C, wo(l), out, (long long)NC * C, l * l + m};
+        e = launch_proj(jobs, nj, 0, 0, n, C, stream);
+    }
     if (e == hipSuccess) e = mark(4);
     if (e != hipSuccess) return hip_fail(e, "output projection kernel");
     if (taps) {

@@ -319,6 +319,18 @@ struct QkvEaasArgs {
 };
 hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t stream);
 
+// Output projection out^l = hhat^l W_O[l]: hhat, out fp32 [n][(lmax+1)^2][C],
+// wo = packed W_O[0..lmax].  tpb and blk_start are filled in by the launcher.
+struct OutProjArgs {
+    const float *hhat;
+    const uint4 *wo;
+    float *out;
+    int n, lmax;
+    int tpb;
+    int blk_start[kMaxL + 2];
+};
+hipError_t launch_outproj_bf16(const OutProjArgs &a, int C, hipStream_t stream);
+
 struct AttnArgs {
     const float *q, *k;              // [n][C] fp32
     const void *hp;                  // [n][NC][C] fp32, or fp16 (hp_f16_offset layout) scaled by pos4[j].w

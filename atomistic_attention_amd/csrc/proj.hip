@@ -163,6 +163,156 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(const ProjJobs jobs, int
     }
 }
 
+// ---------------------------------------------------------------------------
+// Output projection out^l = hhat^l W_O[l] for fp32 hhat and packed bf16 weights,
+// weight-stationary and persistent: a block owns one degree l, keeps its waves'
+// W_O[l] fragments in registers for its whole run and streams tiles (16 nodes x
+// one component of degree l) through a double-buffered LDS copy of the input
+// rows, split once into bf16 hi + lo.  Tile loads run two tiles ahead.
+template <int C>
+__global__ __launch_bounds__(64 * (C >= 64 ? 4 : 2)) void outproj_kernel(const OutProjArgs a)
+{
+    constexpr int NW = C >= 64 ? 4 : 2;            // waves per block
+    constexpr int NB = C / 16, KB = C / 32, NBW = NB / NW;
+    constexpr int NT = 64 * NW;
+    constexpr int UNITS = 2 * C;                   // 8-float units per tile (16 rows x C / 8)
+    constexpr int UPT = (UNITS + NT - 1) / NT;
+    constexpr int RS = C * 2 + 16;                 // LDS bytes per bf16 row (pad spreads banks)
+    __shared__ __align__(16) unsigned char sA[2][2][16 * RS];   // [buffer][hi, lo][row]
+
+    int l = 0;
+    while (l < a.lmax && (int)blockIdx.x >= a.blk_start[l + 1]) ++l;
+    const int nm = 2 * l + 1, NC = (a.lmax + 1) * (a.lmax + 1);
+    const long long tiles = (long long)((a.n + 15) / 16) * nm;
+    const long long tbase = (long long)(blockIdx.x - a.blk_start[l]) * a.tpb;
+    const int cnt = (int)((tiles - tbase) < a.tpb ? (tiles - tbase) : a.tpb);
+    if (cnt <= 0) return;
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4, nl = lane & 15;
+    bf16x8 wf[NBW][KB];
+    const uint4 *wl = a.wo + (size_t)l * (C * C / 8);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) wf[j][kb] = __builtin_bit_cast(bf16x8, wl[((w * NBW + j) * KB + kb) * 64 + lane]);
+
+    // tile index -> first input/output element of its rows: node 16 gi + r, component l^2 + m
+    auto tile_row = [&](int it, int r, bool &ok) -> long long {
+        const long long ti = tbase + it;
+        const long long gi = ti / nm;
+        const int m = (int)(ti - gi * nm);
+        const long long node = gi * 16 + r;
+        ok = node < a.n;
+        return (node * NC + l * l + m) * C;
+    };
+    typedef float4 Stage[UPT][2];
+    auto load = [&](int it, Stage &rg) {
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+            const int u = t + j * NT;
+            rg[j][0] = rg[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (u < UNITS) {
+                const int r = u / (C / 8), kc = u - r * (C / 8);
+                bool ok;
+                const long long o = tile_row(it, r, ok);
+                if (ok) {
+                    const float4 *src = reinterpret_cast<const float4 *>(a.hhat + o + 8 * kc);
+                    rg[j][0] = src[0];
+                    rg[j][1] = src[1];
+                }
+            }
+        }
+    };
+    auto stage = [&](int buf, const Stage &rg) {
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+            const int u = t + j * NT;
+            if (u < UNITS) {
+                const int r = u / (C / 8), kc = u - r * (C / 8);
+                const float xs[8] = {rg[j][0].x, rg[j][0].y, rg[j][0].z, rg[j][0].w,
+                                     rg[j][1].x, rg[j][1].y, rg[j][1].z, rg[j][1].w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint16_t h0 = f_to_bf16(xs[2 * e]), h1 = f_to_bf16(xs[2 * e + 1]);
+                    const uint16_t l0 = f_to_bf16(xs[2 * e] - bf16_to_f(h0));
+                    const uint16_t l1 = f_to_bf16(xs[2 * e + 1] - bf16_to_f(h1));
+                    hi[e] = h0 | (uint32_t(h1) << 16);
+                    lo[e] = l0 | (uint32_t(l1) << 16);
+                }
+                *reinterpret_cast<uint4 *>(&sA[buf][0][r * RS + kc * 16]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                *reinterpret_cast<uint4 *>(&sA[buf][1][r * RS + kc * 16]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            }
+        }
+    };
+    auto compute = [&](int it, int buf) {
+        floatx4 acc[NBW];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int off = nl * RS + kb * 64 + g * 16;
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&sA[buf][0][off]));
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&sA[buf][1][off]));
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j][kb], bh, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j][kb], bl, acc[j], 0, 0, 0);
+            }
+        }
+        bool ok;
+        const long long o = tile_row(it, nl, ok);
+        if (ok) {
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+                *reinterpret_cast<float4 *>(a.out + o + 16 * (w * NBW + j) + 4 * g) =
+                    make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        }
+    };
+
+    Stage p0, p1;
+    load(0, p0);
+    if (cnt > 1) load(1, p1);
+    stage(0, p0);
+    __syncthreads();
+    for (int it = 0; it < cnt; it += 2) {
+        // p1 holds tile it + 1; p0 is free
+        if (it + 2 < cnt) load(it + 2, p0);
+        compute(it, 0);
+        if (it + 1 < cnt) stage(1, p1);
+        __syncthreads();
+        if (it + 1 >= cnt) break;
+        // p0 holds tile it + 2; p1 is free
+        if (it + 3 < cnt) load(it + 3, p1);
+        compute(it + 1, 1);
+        if (it + 2 < cnt) stage(0, p0);
+        __syncthreads();
+    }
+}
+
+hipError_t launch_outproj_bf16(const OutProjArgs &in, int C, hipStream_t stream)
+{
+    if (in.n <= 0) return hipSuccess;
+    if (in.lmax < 0 || in.lmax > kMaxL) return hipErrorInvalidValue;
+    OutProjArgs a = in;
+    const long long groups = (a.n + 15) / 16, total = groups * (a.lmax + 1) * (a.lmax + 1);
+    const long long target = 2048;                           // about eight blocks per CU
+    a.tpb = (int)((total + target - 1) / target);
+    a.blk_start[0] = 0;
+    for (int l = 0; l <= a.lmax; ++l) {
+        const long long tl = groups * (2 * l + 1);
+        a.blk_start[l + 1] = a.blk_start[l] + (int)((tl + a.tpb - 1) / a.tpb);
+    }
+    const dim3 grid((unsigned)a.blk_start[a.lmax + 1]);
+    switch (C) {
+    case 32: outproj_kernel<32><<<grid, 128, 0, stream>>>(a); break;
+    case 64: outproj_kernel<64><<<grid, 256, 0, stream>>>(a); break;
+    case 128: outproj_kernel<128><<<grid, 256, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, int count, int C, hipStream_t stream)
 {
     if (count <= 0) return hipSuccess;
