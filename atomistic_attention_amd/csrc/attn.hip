@@ -28,7 +28,9 @@
 //   * at the end the PS partial softmaxes are merged by a butterfly that halves
 //     the channel set at each step (reduce-scatter), leaving every lane whole
 //     channels: the target EAAS coupling then runs lane-locally and the lane
-//     writes its channels of hhat.
+//     writes its channels of hhat (fp32 storage), or the lane writes its channels
+//     of the normalised message m_i, which the output-projection kernel couples
+//     (16-bit storage).
 // Value rows are read as 16-byte pieces (4 channels of one fp32 component, or of
 // two interleaved fp16 components); the 2H lanes of a slot cover a contiguous
 // stretch of the neighbour's row.  A 16-bit h'_j row
@@ -325,6 +327,23 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
     const bool writer = (NB <= 2) || ((u & 1) == 0);
     const float invz = z > 0.f ? 1.f / z : 0.f;
 
+    if constexpr (HB) {
+        // 16-bit storage: store the normalised message m_i; the target coupling runs
+        // in the output-projection kernel, on whole nodes.
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int ch = cb + off + c;
+            if (writer) {
+#pragma unroll
+                for (int e = 0; e < NC; ++e) {
+                    const float mv = acc[e][c] * invz;
+                    A.hhat[((size_t)i * NC + e) * C + ch] = mv;
+                    if (A.m_tap) A.m_tap[((size_t)i * NC + e) * C + ch] = mv;
+                }
+            }
+        }
+        return;
+    }
     // ---- target coupling (EAAS with the target's own rotation) and store
     const float *Di = A.dmat + (size_t)i * (ND > 0 ? ND : 1);
     const bool dir = (pi4.x != 0.f) || (pi4.y != 0.f) || (pi4.z != 0.f);

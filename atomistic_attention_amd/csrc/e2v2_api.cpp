@@ -524,7 +524,8 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         if (e == hipSuccess) e = mark(2);
         if (e != hipSuccess) return hip_fail(e, "source EAAS kernel");
     }
-    // Steps 4-5: streaming attention + target coupling.
+    // Steps 4-5: streaming attention + target coupling (fp32 storage); for bf16
+    // storage the streaming kernel stops at the normalised message m_i.
     AttnArgs a{};
     a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dmat = dmat;
     a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
@@ -536,13 +537,15 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
     if (e != hipSuccess) return hip_fail(e, "attention kernel");
     // Step 6: output projection.
     if (bf) {
-        OutProjArgs oa{};
-        oa.hhat = hhat;
+        // Step 5 (target coupling) + step 6 on whole nodes: the streaming kernel
+        // left the normalised message m in the hhat buffer.
+        EaasOutArgs oa{};
+        oa.m = hhat; oa.dmat = dmat; oa.pos4 = pos4; oa.w_tgt = w->w_tgt;
         oa.wo = reinterpret_cast<const uint4 *>(wo(0));
         oa.out = out;
+        oa.hhat_tap = taps ? taps->hhat : nullptr;
         oa.n = n;
-        oa.lmax = lmax;
-        e = launch_outproj_bf16(oa, C, stream);
+        e = launch_eaas_outproj(lmax, oa, C, stream);
     } else {
         nj = 0;
         for (int l = 0; l <= lmax; ++l)
@@ -556,7 +559,7 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         const size_t N = (size_t)n;
         struct { void *dst; const void *src; size_t bytes; } cp[] = {
             {taps->q, q, N * C * 4}, {taps->k, k, N * C * 4}, {bf ? nullptr : taps->v, v, N * NC * C * 4},
-            {taps->hhat, hhat, N * NC * C * 4}};
+            {bf ? nullptr : taps->hhat, hhat, N * NC * C * 4}};
         for (auto &c : cp)
             if (c.dst) {
                 e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, stream);

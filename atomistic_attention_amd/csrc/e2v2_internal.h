@@ -252,6 +252,108 @@ __device__ __forceinline__ void eaas_channel(const float *__restrict__ D, const 
 }
 
 // ----------------------------------------------------------------------------
+// One multiply-add of the aligned-frame coupling: output component `out`
+// receives coefficient c[p][cc] times path weight p times input component `in`;
+// lf > 0 terms vanish for a node at the origin.
+struct CTerm {
+    int p, out, in, cc, lf;
+};
+template <int L>
+struct CTerms {
+    int n;
+    CTerm t[(2 * kMaxL + 1) * kMaxPaths];
+};
+template <int L>
+constexpr CTerms<L> couple_terms()
+{
+    CTerms<L> r = {};
+    int n = 0;
+    for (int lo = 0; lo <= L; ++lo)
+        for (int li = 0; li <= L; ++li)
+            for (int lf = 0; lf <= L; ++lf) {
+                if (!is_path(li, lf, lo)) continue;
+                const int p = path_index(L, li, lf, lo);
+                const bool odd = ((li + lf + lo) & 1) != 0;
+                const int mm = li < lo ? li : lo;
+                for (int mo = -mm; mo <= mm; ++mo) {
+                    if (odd && mo == 0) continue;
+                    const int mi = odd ? -mo : mo;
+                    r.t[n++] = CTerm{p, lo * lo + lo + mo, li * li + li + mi, mo + lo, lf};
+                }
+            }
+    r.n = n;
+    return r;
+}
+
+// EAAS on NI channels of one node held in registers, v[e][i] (component e,
+// channel i), in place: rotate into the aligned frame (D^T x), the sparse m
+// re-index with the path weights, rotate back (D y).  Dn: the node's D^1..D^L
+// (fp32, may live in LDS); channel i's path weights at w0 + i * wstride; fdir = 0
+// drops the l_f > 0 paths (node at the origin).  Three passes over the channels
+// keep one D^l block live at a time.
+template <int L, int NI, typename Arr>
+__device__ __forceinline__ void eaas_multi(Arr &v, const float *Dn, const float *w0, int wstride, const EaasCoef &tab,
+                                           float fdir)
+{
+    constexpr int NC = n_comp(L), KM = 2 * L + 1;
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        const int k = 2 * l + 1, o = l * l;
+        float Dl[KM * KM];
+#pragma unroll
+        for (int r = 0; r < k * k; ++r) Dl[r] = Dn[dmat_offset(l) + r];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float tmp[KM];
+#pragma unroll
+            for (int b = 0; b < k; ++b) {
+                float s2 = 0.f;
+#pragma unroll
+                for (int a = 0; a < k; ++a) s2 = fmaf(Dl[a * k + b], v[o + a][i], s2);
+                tmp[b] = s2;
+            }
+#pragma unroll
+            for (int b = 0; b < k; ++b) v[o + b][i] = tmp[b];
+        }
+    }
+    constexpr CTerms<L> T = couple_terms<L>();
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const float *w = w0 + i * wstride;
+        float loc[NC];
+#pragma unroll
+        for (int e = 0; e < NC; ++e) loc[e] = 0.f;
+#pragma unroll
+        for (int q = 0; q < T.n; ++q) {
+            const float wp = T.t[q].lf > 0 ? w[T.t[q].p] * fdir : w[T.t[q].p];
+            loc[T.t[q].out] = fmaf(wp * tab.c[T.t[q].p][T.t[q].cc], v[T.t[q].in][i], loc[T.t[q].out]);
+        }
+#pragma unroll
+        for (int e = 0; e < NC; ++e) v[e][i] = loc[e];
+    }
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        const int k = 2 * l + 1, o = l * l;
+        float Dl[KM * KM];
+#pragma unroll
+        for (int r = 0; r < k * k; ++r) Dl[r] = Dn[dmat_offset(l) + r];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float tmp[KM];
+#pragma unroll
+            for (int a = 0; a < k; ++a) {
+                float s2 = 0.f;
+#pragma unroll
+                for (int b = 0; b < k; ++b) s2 = fmaf(Dl[a * k + b], v[o + b][i], s2);
+                tmp[a] = s2;
+            }
+#pragma unroll
+            for (int a = 0; a < k; ++a) v[o + a][i] = tmp[a];
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
 // Layout of 16-bit h' in the workspace: per node NC * C elements; components are
 // interleaved in pairs at 4-channel granularity, so element (e, c) of a pair
 // (e < 2 * (NC / 2)) sits at (e / 2) * 2C + (c / 4) * 8 + (e % 2) * 4 + c % 4, and an
@@ -321,6 +423,7 @@ hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t strea
 
 // Output projection out^l = hhat^l W_O[l]: hhat, out fp32 [n][(lmax+1)^2][C],
 // wo = packed W_O[0..lmax].  tpb and blk_start are filled in by the launcher.
+// (Kept for reference layouts; the bf16 forward uses launch_eaas_outproj.)
 struct OutProjArgs {
     const float *hhat;
     const uint4 *wo;
@@ -331,6 +434,19 @@ struct OutProjArgs {
 };
 hipError_t launch_outproj_bf16(const OutProjArgs &a, int C, hipStream_t stream);
 
+// Target coupling + output projection for bf16 storage: m fp32 [n][NC][C] (the
+// normalised message), dmat [n][n_dmat(L)], pos4 [n] (x, y, z, .), w_tgt [P][C],
+// wo = packed W_O[0..L]; out fp32 [n][NC][C]; hhat_tap optional fp32 [n][NC][C].
+struct EaasOutArgs {
+    const float *m, *dmat;
+    const float4 *pos4;
+    const float *w_tgt;
+    const uint4 *wo;
+    float *out, *hhat_tap;
+    int n;
+};
+hipError_t launch_eaas_outproj(int L, const EaasOutArgs &a, int C, hipStream_t stream);
+
 struct AttnArgs {
     const float *q, *k;              // [n][C] fp32
     const void *hp;                  // [n][NC][C] fp32, or fp16 (hp_f16_offset layout) scaled by pos4[j].w
@@ -340,7 +456,7 @@ struct AttnArgs {
     const int32_t *order;            // optional processing order of the targets
     const float *w_rbf;              // [R][H]
     const float *w_tgt;              // [P][C]
-    float *hhat;                     // [n][NC][C] fp32
+    float *hhat;                     // [n][NC][C] fp32: hhat (fp32 h'), or the message m (16-bit h')
     float *m_tap;                    // optional [n][NC][C]
     int n, C, H, R;
     float cutoff;

@@ -32,39 +32,6 @@ __device__ __forceinline__ float f16hi(uint32_t u) { return (float)__builtin_bit
 
 }  // namespace
 
-// One multiply-add of the aligned-frame coupling: output component `out`
-// receives coefficient c[p][cc] times path weight p times input component `in`;
-// lf > 0 terms vanish for a node at the origin.
-struct CTerm {
-    int p, out, in, cc, lf;
-};
-template <int L>
-struct CTerms {
-    int n;
-    CTerm t[(2 * kMaxL + 1) * kMaxPaths];
-};
-template <int L>
-constexpr CTerms<L> couple_terms()
-{
-    CTerms<L> r = {};
-    int n = 0;
-    for (int lo = 0; lo <= L; ++lo)
-        for (int li = 0; li <= L; ++li)
-            for (int lf = 0; lf <= L; ++lf) {
-                if (!is_path(li, lf, lo)) continue;
-                const int p = path_index(L, li, lf, lo);
-                const bool odd = ((li + lf + lo) & 1) != 0;
-                const int mm = li < lo ? li : lo;
-                for (int mo = -mm; mo <= mm; ++mo) {
-                    if (odd && mo == 0) continue;
-                    const int mi = odd ? -mo : mo;
-                    r.t[n++] = CTerm{p, lo * lo + lo + mo, li * li + li + mi, mo + lo, lf};
-                }
-            }
-    r.n = n;
-    return r;
-}
-
 // Per-node Wigner-D blocks of the alignment rotation, fp64, stored as fp32.
 template <int L>
 __global__ __launch_bounds__(256) void k_node_frames(const float *__restrict__ pos, int n, float *__restrict__ dmat,
@@ -213,72 +180,12 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
                 make_float4(acc[e][0], acc[e][1], acc[e][2], acc[e][3]);
     }
 
-    // Source EAAS on the accumulators, in three passes over the lane's 4 channels
-    // so that only one D^l block is live at a time: rotate into the aligned frame
-    // (D^T x), the sparse m re-index with the path weights, rotate back (D y).
-    const float *Dn = sD + nl * ND;
-#pragma unroll
-    for (int l = 1; l <= L; ++l) {
-        constexpr int KM = 2 * L + 1;
-        const int k = 2 * l + 1, o = l * l;
-        float Dl[KM * KM];
-#pragma unroll
-        for (int r = 0; r < k * k; ++r) Dl[r] = Dn[dmat_offset(l) + r];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float tmp[KM];
-#pragma unroll
-            for (int b = 0; b < k; ++b) {
-                float s2 = 0.f;
-#pragma unroll
-                for (int aa = 0; aa < k; ++aa) s2 = fmaf(Dl[aa * k + b], acc[o + aa][i], s2);
-                tmp[b] = s2;
-            }
-#pragma unroll
-            for (int b = 0; b < k; ++b) acc[o + b][i] = tmp[b];
-        }
-    }
+    // Source EAAS on the accumulators (4 channels of node nl per lane).
     {
-        // the encoding of r = 0 is Y_0 only: paths with l_f > 0 drop out
         const long long nc = valid ? node : node0;
         const double px = a.pos[3 * nc], py = a.pos[3 * nc + 1], pz = a.pos[3 * nc + 2];
         const float fdir = (px * px + py * py + pz * pz > 0.0) ? 1.f : 0.f;
-        constexpr CTerms<L> T = couple_terms<L>();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float *w = &sW[(c0 + i) * WS];
-            float loc[NC];
-#pragma unroll
-            for (int e = 0; e < NC; ++e) loc[e] = 0.f;
-#pragma unroll
-            for (int q = 0; q < T.n; ++q) {
-                const float wp = T.t[q].lf > 0 ? w[T.t[q].p] * fdir : w[T.t[q].p];
-                loc[T.t[q].out] = fmaf(wp * tab.c[T.t[q].p][T.t[q].cc], acc[T.t[q].in][i], loc[T.t[q].out]);
-            }
-#pragma unroll
-            for (int e = 0; e < NC; ++e) acc[e][i] = loc[e];
-        }
-    }
-#pragma unroll
-    for (int l = 1; l <= L; ++l) {
-        constexpr int KM = 2 * L + 1;
-        const int k = 2 * l + 1, o = l * l;
-        float Dl[KM * KM];
-#pragma unroll
-        for (int r = 0; r < k * k; ++r) Dl[r] = Dn[dmat_offset(l) + r];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float tmp[KM];
-#pragma unroll
-            for (int aa = 0; aa < k; ++aa) {
-                float s2 = 0.f;
-#pragma unroll
-                for (int b = 0; b < k; ++b) s2 = fmaf(Dl[aa * k + b], acc[o + b][i], s2);
-                tmp[aa] = s2;
-            }
-#pragma unroll
-            for (int aa = 0; aa < k; ++aa) acc[o + aa][i] = tmp[aa];
-        }
+        eaas_multi<L, 4>(acc, sD + nl * ND, &sW[c0 * WS], WS, tab, fdir);
     }
 
     // Per-node scale: largest |h'| over all components and channels.  Magnitude

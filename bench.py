@@ -191,7 +191,8 @@ def main():
     if cfg.storage == "bf16":
         # fused projections + source EAAS: h in; q, k, h' (16-bit), D blocks, pos4 out
         front = N * nc * C * 2 + N * C * 8 + N * 12 + N * nc * C * 2 + N * (4 * nd + 16)
-        stage_names = ("neighbours", "projections+source_eaas", None, "attention", "output_projection")
+        stage_names = ("neighbours", "projections+source_eaas", None, "attention", "target_eaas+output_projection")
+        front += N * (4 * nd + 16)          # the back end reads the D blocks and pos4 again
     else:
         front = (N * nc * C * s + N * C * 8 + N * nc * C * 4                          # projections
                  + N * nc * C * 4 + N * 12 + N * nc * C * s + N * (4 * nd + 16))    # source EAAS

@@ -90,7 +90,8 @@ typedef struct {
  * aligned; any may be NULL) and optional stage timing.  Intended for validation
  * and measurement; production callers pass NULL taps.  For bf16 storage steps 2
  * and 3 run as one kernel (v is projected and coupled in registers), so the
- * events after step 2 and after step 3 are recorded back to back. */
+ * events after step 2 and after step 3 are recorded back to back, and steps 5
+ * and 6 run as one kernel on whole nodes. */
 typedef struct {
     float *q;        /* [n][C] fp32                                         */
     float *k;        /* [n][C] fp32                                         */
@@ -101,7 +102,8 @@ typedef struct {
     float *hhat;     /* [n][(lmax+1)^2][C] fp32 target-coupled message (step 5) */
     hipEvent_t *events;  /* host array of 5 caller-created events or NULL: recorded on
                             `stream` before step 2, after step 2, after step 3, after
-                            steps 4-5 (the streaming kernel) and after step 6 */
+                            the streaming kernel (steps 4-5; step 4 only for bf16
+                            storage, whose step 5 runs with step 6) and after step 6 */
 } e2v2_taps;
 
 /* ------------------------------------------------------------------------
