@@ -116,10 +116,13 @@ def test_layer_deterministic(gpu_lib):
     assert np.array_equal(a, b)
 
 
-def test_target_order_does_not_change_results(gpu_lib):
+@pytest.mark.parametrize("storage", ["fp32", "bf16"])
+def test_target_order_does_not_change_results(gpu_lib, storage):
     """Targets are independent: any processing order (natural, the neighbour
     builder's cell order, a random permutation) gives bit-identical outputs."""
-    wl = W.make_workload("c4", n=6000)
+    base = W.make_workload("c4", n=6000)
+    cfg = W.LayerConfig(**{**base.cfg.__dict__, "storage": storage})
+    wl = W.make_workload(cfg)
     c = wl.cfg
     d = upload(wl)
     order = torch.empty(c.n, dtype=torch.int32, device="cuda")
@@ -131,3 +134,32 @@ def test_target_order_does_not_change_results(gpu_lib):
     outs = [gpu_lib.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, target_order=o).cpu()
             for o in (None, order, perm)]
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def _sampled_check(gpu_lib, wl, rows, nsample, seed):
+    """Layer output for the given neighbour rows against the oracle on a sample of targets."""
+    out, _ = _run(gpu_lib, wl, nbr=csr_from_rows(rows))
+    tg = np.sort(np.random.default_rng(seed).choice(wl.cfg.n, nsample, replace=False))
+    ref = O.layer_forward_workload(wl, targets=tg, rows=[rows[i] for i in tg])
+    assert rel_err(out[tg], ref["out"]) < tolerance(wl)
+
+
+def test_repeated_neighbour_entries(gpu_lib):
+    """A neighbour listed twice counts twice: the softmax runs over list entries."""
+    wl = _small(700, 2, 16, "bf16", 11, side=20.0, cutoff=5.0)
+    rows = O.neighbors(wl.pos, wl.cfg.cutoff)
+    rng = np.random.default_rng(5)
+    for i in rng.choice(wl.cfg.n, 40, replace=False):
+        r = rows[i]
+        if r.size:
+            rows[i] = np.sort(np.r_[r, rng.choice(r, min(3, r.size), replace=False)]).astype(np.int32)
+    _sampled_check(gpu_lib, wl, rows, 160, 1)
+
+
+def test_very_long_neighbour_lists(gpu_lib):
+    """Uncapped lists of well over a thousand entries per target (a dense box with
+    a long cutoff): many 16-pair chunks per target, online-softmax rescaling."""
+    wl = _small(2600, 2, 16, "bf16", 12, side=13.0, cutoff=12.0)
+    rows = O.neighbors(wl.pos, wl.cfg.cutoff)
+    assert np.mean([r.size for r in rows]) > 1000
+    _sampled_check(gpu_lib, wl, rows, 24, 2)
