@@ -476,12 +476,9 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
     int nj = 0;
     uint16_t *wp = reinterpret_cast<uint16_t *>(ws + L.wpack);
     const size_t wsz = (size_t)C * C;                 // elements per packed matrix
-    auto wv = [&](int l) -> const void * {            // weights as the projection kernel reads them
-        return bf ? (const void *)(wp + (size_t)l * wsz) : (const void *)(reinterpret_cast<const char *>(w->w_v) + l * wstride);
-    };
-    auto wo = [&](int l) -> const void * {
-        return bf ? (const void *)(wp + (size_t)(lmax + 3 + l) * wsz) : (const void *)(reinterpret_cast<const char *>(w->w_o) + l * wstride);
-    };
+    // fp32 weights of degree l (fp32 storage)
+    auto wv32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_v) + l * wstride); };
+    auto wo32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_o) + l * wstride); };
     if (bf) {
         const uint16_t *src[2 * kMaxL + 4];
         uint16_t *dst[2 * kMaxL + 4];
@@ -511,12 +508,13 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         if (e == hipSuccess) e = mark(2);
         if (e != hipSuccess) return hip_fail(e, "projection + source EAAS kernel");
     } else {
+        const float *h32 = reinterpret_cast<const float *>(h);
         for (int l = 0; l <= lmax; ++l)
             for (int m = 0; m < 2 * l + 1; ++m)
-                jobs[nj++] = ProjJob{h, (long long)NC * C, wv(l), v, (long long)NC * C, l * l + m};
-        jobs[nj++] = ProjJob{h, (long long)NC * C, w->w_q, q, (long long)C, 0};
-        jobs[nj++] = ProjJob{h, (long long)NC * C, w->w_k, k, (long long)C, 0};
-        e = launch_proj(jobs, nj, 0, 0, n, C, stream);
+                jobs[nj++] = ProjJob{h32, (long long)NC * C, wv32(l), v, (long long)NC * C, l * l + m};
+        jobs[nj++] = ProjJob{h32, (long long)NC * C, reinterpret_cast<const float *>(w->w_q), q, (long long)C, 0};
+        jobs[nj++] = ProjJob{h32, (long long)NC * C, reinterpret_cast<const float *>(w->w_k), k, (long long)C, 0};
+        e = launch_proj(jobs, nj, n, C, stream);
         if (e == hipSuccess) e = mark(1);
         if (e != hipSuccess) return hip_fail(e, "projection kernel");
         // Step 3: source coupling h' (EAAS), per-node D blocks and padded positions.
@@ -541,7 +539,7 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         // left the normalised message m in the hhat buffer.
         EaasOutArgs oa{};
         oa.m = hhat; oa.dmat = dmat; oa.pos4 = pos4; oa.w_tgt = w->w_tgt;
-        oa.wo = reinterpret_cast<const uint4 *>(wo(0));
+        oa.wo = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 3) * wsz);
         oa.out = out;
         oa.hhat_tap = taps ? taps->hhat : nullptr;
         oa.n = n;
@@ -550,8 +548,8 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         nj = 0;
         for (int l = 0; l <= lmax; ++l)
             for (int m = 0; m < 2 * l + 1; ++m)
-                jobs[nj++] = ProjJob{hhat, (long long)NC * C, wo(l), out, (long long)NC * C, l * l + m};
-        e = launch_proj(jobs, nj, 0, 0, n, C, stream);
+                jobs[nj++] = ProjJob{hhat, (long long)NC * C, wo32(l), out, (long long)NC * C, l * l + m};
+        e = launch_proj(jobs, nj, n, C, stream);
     }
     if (e == hipSuccess) e = mark(4);
     if (e != hipSuccess) return hip_fail(e, "output projection kernel");

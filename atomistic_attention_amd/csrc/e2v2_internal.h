@@ -383,25 +383,23 @@ __device__ __forceinline__ uint16_t f_to_bf16(float f)
 // Launch helpers implemented in the .hip files (all enqueue on `stream`).
 struct NbrWork;   // neighbours.hip
 
-// y_format: 0 fp32, 1 bf16, 2 fp16 with a per-node power-of-two scale written to
-// pos4_out[node].w (pos4_out required).  y_deq (optional) receives the stored
-// values dequantised to fp32.
+// y_format: 0 fp32, 1 bf16.  y_deq (optional) receives the stored values as
+// fp32; dmat_out and pos4_out (optional) the node's D blocks and (x, y, z, 1).
 hipError_t launch_eaas(int L, const float *pos, const void *x, int x_bf16, const float *path_w, int n, int C,
                        void *y, int y_format, float *y_deq, float *dmat_out, float4 *pos4_out, hipStream_t stream);
 
 struct ProjJob {
-    const void *a;          // A rows: a + node*a_node_stride + comp*C (elements)
+    const float *a;         // A rows: a + node*a_node_stride + comp*C (elements)
     long long a_node_stride;
-    const void *b;          // [C][C] weight (in, out)
+    const float *b;         // [C][C] weight (in, out)
     float *out;             // out + node*o_node_stride + comp*C
     long long o_node_stride;
     int comp;               // component index of the rows
 };
-hipError_t launch_proj(const ProjJob *jobs, int njobs, int a_bf16, int b_bf16, int n, int C, hipStream_t stream);
-// bf16 weights on bf16 MFMA: job.b points at weights packed by launch_pack_weights;
-// a_f32 selects fp32 input rows (split into bf16 hi + lo), else bf16 rows.
+// fp32 projections (fp32 storage).
+hipError_t launch_proj(const ProjJob *jobs, int njobs, int n, int C, hipStream_t stream);
+// bf16 weights W [C][C] (in, out) packed into v_mfma_f32_16x16x32_bf16 A fragments.
 hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, int count, int C, hipStream_t stream);
-hipError_t launch_proj_bf16(const ProjJob *jobs, int njobs, int a_f32, int n, int C, hipStream_t stream);
 
 // Fused q / k / v projections and source EAAS for bf16 storage: h bf16
 // [n][NC][C]; wv = packed W_V[0..L] (C*C/8 uint4 each), wq, wk packed W_Q, W_K;
@@ -420,19 +418,6 @@ struct QkvEaasArgs {
     int n;
 };
 hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t stream);
-
-// Output projection out^l = hhat^l W_O[l]: hhat, out fp32 [n][(lmax+1)^2][C],
-// wo = packed W_O[0..lmax].  tpb and blk_start are filled in by the launcher.
-// (Kept for reference layouts; the bf16 forward uses launch_eaas_outproj.)
-struct OutProjArgs {
-    const float *hhat;
-    const uint4 *wo;
-    float *out;
-    int n, lmax;
-    int tpb;
-    int blk_start[kMaxL + 2];
-};
-hipError_t launch_outproj_bf16(const OutProjArgs &a, int C, hipStream_t stream);
 
 // Target coupling + output projection for bf16 storage: m fp32 [n][NC][C] (the
 // normalised message), dmat [n][n_dmat(L)], pos4 [n] (x, y, z, .), w_tgt [P][C],

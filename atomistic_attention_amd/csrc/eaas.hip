@@ -14,20 +14,12 @@ template <typename T> __device__ __forceinline__ float ld_elem(const T *p, size_
 template <> __device__ __forceinline__ float ld_elem<float>(const float *p, size_t i) { return p[i]; }
 template <> __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t *p, size_t i) { return bf16_to_f(p[i]); }
 
-// Output formats: fp32, bf16, or fp16 with one power-of-two scale per node
-// (kYF16S, stored in the component-pair interleaved layout of hp_f16_offset).  The scaled-fp16 form keeps 16 bits per element like bf16 but with
-// an 11-bit significand; the per-node scale s (stored in pos4[node].w) keeps
-// fp32 range: the node's largest magnitude M maps below 2^14, so no element
-// overflows and every element within 2^28 of M stays a normal fp16 number.
-enum { kYF32 = 0, kYBF16 = 1, kYF16S = 2 };
-
-__device__ __forceinline__ uint16_t f_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-__device__ __forceinline__ float f16_to_f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+// Output formats: fp32 or bf16.
+enum { kYF32 = 0, kYBF16 = 1 };
 
 // One block of 256 threads covers NPB = min(32, 256 * PPT / C) nodes.  Threads
 // 0..NPB-1 build one node's Wigner-D blocks each (fp64), shared through LDS; then
-// every thread handles up to PPT (node, channel) pairs, all in registers.  For
-// the scaled-fp16 output the node's largest magnitude is reduced in LDS first.
+// every thread handles up to PPT (node, channel) pairs, all in registers.
 template <int L> constexpr int eaas_pairs() { return L >= 3 ? 4 : 8; }
 template <int L> __host__ __device__ inline int eaas_nodes_per_block(int C)
 {
@@ -46,13 +38,11 @@ __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos
     constexpr int P = path_count(L);
     __shared__ float sD[32][ND];
     __shared__ int sDir[32];
-    __shared__ unsigned sMax[32];
 
     constexpr int kEaasPairs = eaas_pairs<L>();
     const int npb = eaas_nodes_per_block<L>(C);
     const int t = threadIdx.x;
     const long long node0 = (long long)blockIdx.x * npb;
-    if (t < 32) sMax[t] = 0u;
     if (t < npb) {
         const long long node = node0 + t;
         if (node < n) {
@@ -65,13 +55,11 @@ __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos
                 if (dmat_out) dmat_out[node * n_dmat(L) + e] = (float)Dd[e];
             }
             sDir[t] = dir ? 1 : 0;
-            if (pos4_out && YF != kYF16S) pos4_out[node] = make_float4((float)px, (float)py, (float)pz, 1.f);
+            if (pos4_out) pos4_out[node] = make_float4((float)px, (float)py, (float)pz, 1.f);
         }
     }
     __syncthreads();
     // pairs idx = t + 256 q: node ln = idx / C, channel c = idx % C
-    constexpr int KEEP = YF == kYF16S ? kEaasPairs : 1;   // fp16 output waits for the node's scale
-    float yv[KEEP][NC];
 #pragma unroll
     for (int q = 0; q < kEaasPairs; ++q) {
         const int idx = t + 256 * q;
@@ -79,58 +67,22 @@ __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos
         const long long node = node0 + ln;
         if (ln >= npb || node >= n) continue;
         const size_t base = (size_t)node * NC * C + c;
-        float xv[NC], w[P];
+        float xv[NC], yv[NC], w[P];
 #pragma unroll
         for (int e = 0; e < NC; ++e) xv[e] = ld_elem<TX>(x, base + (size_t)e * C);
 #pragma unroll
         for (int p = 0; p < P; ++p) w[p] = path_w[p * C + c];
-        float (&yq)[NC] = yv[YF == kYF16S ? q : 0];
-        eaas_channel<L>(&sD[ln][0], xv, yq, w, tabs.eaas, sDir[ln] != 0);
-        if constexpr (YF == kYF16S) {
-            float m = 0.f;
+        eaas_channel<L>(&sD[ln][0], xv, yv, w, tabs.eaas, sDir[ln] != 0);
 #pragma unroll
-            for (int e = 0; e < NC; ++e) m = fmaxf(m, fabsf(yq[e]));
-            atomicMax(&sMax[ln], __float_as_uint(m));   // non-negative floats order like their bits
-        } else {
-#pragma unroll
-            for (int e = 0; e < NC; ++e) {
-                if (YF == kYBF16) {
-                    const uint16_t hb = f_to_bf16(yq[e]);
-                    reinterpret_cast<uint16_t *>(y_)[base + (size_t)e * C] = hb;
-                    if (y_deq) y_deq[base + (size_t)e * C] = bf16_to_f(hb);
-                } else {
-                    reinterpret_cast<float *>(y_)[base + (size_t)e * C] = yq[e];
-                    if (y_deq) y_deq[base + (size_t)e * C] = yq[e];
-                }
+        for (int e = 0; e < NC; ++e) {
+            if (YF == kYBF16) {
+                const uint16_t hb = f_to_bf16(yv[e]);
+                reinterpret_cast<uint16_t *>(y_)[base + (size_t)e * C] = hb;
+                if (y_deq) y_deq[base + (size_t)e * C] = bf16_to_f(hb);
+            } else {
+                reinterpret_cast<float *>(y_)[base + (size_t)e * C] = yv[e];
+                if (y_deq) y_deq[base + (size_t)e * C] = yv[e];
             }
-        }
-    }
-    if constexpr (YF == kYF16S) {
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < kEaasPairs; ++q) {
-            const int idx = t + 256 * q;
-            const int ln = idx / C, c = idx - ln * C;
-            const long long node = node0 + ln;
-            if (ln >= npb || node >= n) continue;
-            const unsigned mb = sMax[ln];
-            unsigned sb = 127u, ib = 127u;                      // scale 1 for zero or non-finite rows
-            if (mb != 0u && mb < 0x7f800000u) {
-                const unsigned b = mb >> 23;                    // M < 2^(b-126); s = 2^(b-140)
-                sb = b > 13u ? b - 13u : 1u;
-                ib = 254u - sb;
-            }
-            const float sc = __uint_as_float(sb << 23), inv = __uint_as_float(ib << 23);
-            uint16_t *y = reinterpret_cast<uint16_t *>(y_) + (size_t)node * NC * C;
-            const size_t base = (size_t)node * NC * C + c;
-#pragma unroll
-            for (int e = 0; e < NC; ++e) {
-                const uint16_t hb = f_to_f16(yv[q][e] * inv);
-                y[hp_f16_offset(e, c, NC, C)] = hb;
-                if (y_deq) y_deq[base + (size_t)e * C] = f16_to_f(hb) * sc;
-            }
-            if (c == 0 && pos4_out)
-                pos4_out[node] = make_float4(pos[3 * node], pos[3 * node + 1], pos[3 * node + 2], sc);
         }
     }
 }
@@ -140,9 +92,7 @@ static void launch_eaas_x(dim3 grid, const float *pos, const void *x, const floa
                           int yf, float *y_deq, float *dmat_out, float4 *pos4_out, const Tables &tb, hipStream_t stream)
 {
     const TX *xp = reinterpret_cast<const TX *>(x);
-    if (yf == kYF16S)
-        eaas_kernel<L, TX, kYF16S><<<grid, 256, 0, stream>>>(pos, xp, path_w, n, C, y, y_deq, dmat_out, pos4_out, tb);
-    else if (yf == kYBF16)
+    if (yf == kYBF16)
         eaas_kernel<L, TX, kYBF16><<<grid, 256, 0, stream>>>(pos, xp, path_w, n, C, y, y_deq, dmat_out, pos4_out, tb);
     else
         eaas_kernel<L, TX, kYF32><<<grid, 256, 0, stream>>>(pos, xp, path_w, n, C, y, y_deq, dmat_out, pos4_out, tb);

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
         const floatx4 y0 = acc[2 * j], y1 = acc[2 * j + 1];
         const uint4 o = make_uint4(pack_f16x2(y0[0] * inv, y0[1] * inv), pack_f16x2(y0[2] * inv, y0[3] * inv),
                                    pack_f16x2(y1[0] * inv, y1[1] * inv), pack_f16x2(y1[2] * inv, y1[3] * inv));
-        *reinterpret_cast<uint4 *>(hp + j * 2 * C + (c0 >> 2) * 8) = o;
+        *reinterpret_cast<uint4 *>(hp + hp_f16_offset(2 * j, c0, NC, C)) = o;   // 4 channels of components 2j, 2j+1
         if (a.hp_tap) {
             float *d0 = a.hp_tap + (node * NC + 2 * j) * C + c0;
             *reinterpret_cast<float4 *>(d0) =
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
     if constexpr ((NC & 1) != 0) {
         const floatx4 y0 = acc[NC - 1];
         const uint2 o = make_uint2(pack_f16x2(y0[0] * inv, y0[1] * inv), pack_f16x2(y0[2] * inv, y0[3] * inv));
-        *reinterpret_cast<uint2 *>(hp + (NC - 1) * C + c0) = o;
+        *reinterpret_cast<uint2 *>(hp + hp_f16_offset(NC - 1, c0, NC, C)) = o;
         if (a.hp_tap)
             *reinterpret_cast<float4 *>(a.hp_tap + (node * NC + NC - 1) * C + c0) =
                 make_float4(f16lo(o.x) * sc, f16hi(o.x) * sc, f16lo(o.y) * sc, f16hi(o.y) * sc);
