@@ -38,13 +38,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 def algorithmic_bytes(cfg, nnz: int) -> dict:
     """Bytes the streaming kernel must move: per pair the neighbour's coupled value
     row h'_j (storage dtype), its fp32 key row, its index and its position; per
-    target its query, its D blocks, its position, its row bounds and the fp32
-    coupled output row."""
+    target its query, its position, its row bounds and one fp32 output row -- the
+    message m_i for bf16 storage (the target coupling runs in the output kernel),
+    the coupled hhat_i for fp32 storage, which also reads the target's D blocks."""
     C, nc = cfg.channels, cfg.n_comp
     s = 2 if cfg.storage == "bf16" else 4
     nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
     per_pair = nc * C * s + 4 * C + 4 + 12
-    per_node = 4 * C + 4 * nd + 12 + 8 + 4 * nc * C
+    per_node = 4 * C + 12 + 8 + 4 * nc * C + (0 if cfg.storage == "bf16" else 4 * nd)
     return {"per_pair": per_pair, "per_node": per_node, "total": nnz * per_pair + cfg.n * per_node}
 
 
@@ -233,7 +234,8 @@ def main():
             "layer_hbm_frac_excl_neighbours": layer_bytes / (layer_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         },
         "roofline": {
-            "kernel": "attn_kernel (fused streaming attention + target EAAS)",
+            "kernel": ("attn_kernel (fused streaming attention; emits the message m_i)" if cfg.storage == "bf16"
+                       else "attn_kernel (fused streaming attention + target EAAS)"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
