@@ -14,7 +14,8 @@
 //   3. exclusive scan of the counts; scatter atoms into cell order;
 //   4. one wave per target (targets taken in cell order, so neighbouring waves
 //      read the same cells) scans the 27-cell stencil, compacts the pairs that
-//      pass into LDS and orders them there by rank counting:
+//      pass into LDS, picks the K nearest there by rank counting and orders the
+//      row by j with a register bitonic sort:
 //        K = 0: count -> scan -> fill, rows sorted by j;
 //        K > 0: the K nearest by (d2, j), sorted by j, padded with -1.
 //      Rows with more candidates than the LDS buffer holds are finished by a
@@ -367,10 +368,11 @@ __global__ void k_fill_capped(int n, int K, double rc2, const float *__restrict_
 // A wave scans its target's stencil 64 candidates at a time: for fixed (z, y) the
 // three x-neighbouring cells are adjacent in cell order, so the stencil is 9
 // contiguous ranges of the cell-sorted arrays.  Passing candidates are compacted
-// into LDS (ballot + prefix count) and ordered there by rank counting: the rank
-// of an element is the number of elements with a smaller key, which gives every
-// element its final slot without any data movement between lanes.  Rows longer
-// than the LDS buffer are marked and left to the per-thread kernels above.
+// into LDS (ballot + prefix count).  Over-cap rows are cut to the K nearest by
+// rank counting (the rank of an element is the number of elements with a smaller
+// (d2, j) key, which is its final slot), and every row is then sorted by j in
+// registers.  Rows longer than the LDS buffer are marked and left to the
+// per-thread kernels above.
 constexpr int kWaveCap = 1024;                 // candidates a wave can hold in LDS
 constexpr int kWavesPerBlock = 4;
 
@@ -468,44 +470,70 @@ __device__ __forceinline__ int wave_scan(int i, float4 pi, double rc2, const Gri
     return count;
 }
 
-// Rank counting with broadcast LDS reads: the keys are read 4 (or 2 doubles) at
-// a time as one 16-byte load that every lane shares, and each lane ranks all of
-// its elements (e = lane + 64 c, c < NCH) against them.  Arrays are padded to a
-// multiple of 4 entries with keys that rank after every real key.
+// Rows are ordered by j with a bitonic sort held in registers: the wave's 64 E
+// keys (key x = lane * E + k in register k of lane x / E) go through the
+// log2(64 E) merge phases; compare-exchange partners closer than E sit in the
+// same lane, farther ones in lane ^ (d / E), reached by one shuffle per key.
+template <int E>
+__device__ __forceinline__ void wave_bitonic_sort(int (&a)[E], int lane)
+{
+    constexpr int N = 64 * E;
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+        for (int d = size >> 1; d >= 1; d >>= 1) {
+            if (d >= E) {
+                const int lx = d / E;
+                // size > d >= E: the direction depends on the lane only
+                const bool asc = ((lane * E) & size) == 0;
+                const bool keep_min = ((lane & lx) == 0) == asc;
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const int o = __shfl_xor(a[k], lx, 64);
+                    a[k] = keep_min ? min(a[k], o) : max(a[k], o);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    if (k & d) continue;
+                    const bool asc = ((lane * E + k) & size) == 0;
+                    const int p = a[k], q = a[k | d];
+                    a[k] = asc ? min(p, q) : max(p, q);
+                    a[k | d] = asc ? max(p, q) : min(p, q);
+                }
+            }
+        }
+    }
+}
 
-// row[rank by j] = j for the cnt distinct keys of cj.
-template <int NCH>
+// row[0 .. cnt) = the cnt distinct keys of cj in increasing order.
+template <int E>
 __device__ __forceinline__ void wave_write_sorted_n(const int32_t *cj, int cnt, int32_t *row, int lane)
 {
-    int je[NCH], r[NCH];
+    int a[E];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int e = lane + 64 * c;
-        je[c] = e < cnt ? cj[e] : INT_MAX;
-        r[c] = 0;
+    for (int k = 0; k < E; ++k) {
+        const int e = lane * E + k;
+        a[k] = e < cnt ? cj[e] : INT_MAX;
     }
-    const int4 *k4 = reinterpret_cast<const int4 *>(cj);
-    const int nb4 = (cnt + 3) >> 2;
-    for (int t = 0; t < nb4; ++t) {
-        const int4 k = k4[t];
+    wave_bitonic_sort<E>(a, lane);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
-            r[c] += (k.x < je[c] ? 1 : 0) + (k.y < je[c] ? 1 : 0) + (k.z < je[c] ? 1 : 0) + (k.w < je[c] ? 1 : 0);
-    }
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-        if (lane + 64 * c < cnt) row[r[c]] = je[c];
+    for (int k = 0; k < E; ++k)
+        if (lane * E + k < cnt) row[lane * E + k] = a[k];
 }
 __device__ __forceinline__ void wave_write_sorted(const int32_t *cj, int cnt, int32_t *row, int lane)
 {
     if (cnt <= 64) wave_write_sorted_n<1>(cj, cnt, row, lane);
     else if (cnt <= 128) wave_write_sorted_n<2>(cj, cnt, row, lane);
-    else if (cnt <= 192) wave_write_sorted_n<3>(cj, cnt, row, lane);
     else if (cnt <= 256) wave_write_sorted_n<4>(cj, cnt, row, lane);
-    else if (cnt <= 384) wave_write_sorted_n<6>(cj, cnt, row, lane);
     else if (cnt <= 512) wave_write_sorted_n<8>(cj, cnt, row, lane);
     else wave_write_sorted_n<16>(cj, cnt, row, lane);
 }
+
+// The over-cap selection ranks by counting, with broadcast LDS reads: the keys are
+// read 2 doubles at a time as one 16-byte load that every lane shares, and each
+// lane ranks all of its elements (e = lane + 64 c, c < NCH) against them.  Arrays
+// are padded to a multiple of 4 entries with keys that rank after every real key.
 
 // The K nearest by (d2, j): kj[rank] = j for every candidate of rank < K.
 template <int NCH>
