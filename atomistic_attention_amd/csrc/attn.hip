@@ -33,46 +33,48 @@
 //     (16-bit storage).
 // Value rows are read as 16-byte pieces (4 channels of one fp32 component, or of
 // two interleaved fp16 components); the 2H lanes of a slot cover a contiguous
-// stretch of the neighbour's row.  A 16-bit h'_j row
-// carries one power-of-two scale (in pos4[j].w), folded into the softmax weight
-// of the pair, so each element costs one mixed-precision FMA.
+// stretch of the neighbour's row.  With 16-bit storage the key arrives in fp16
+// together with an odd last component of h' (one 16-byte piece per pair), and a
+// neighbour's h' and k share one power-of-two scale (pos4[j].w): it is folded into
+// the softmax weight of the pair, so each value element costs one mixed-precision
+// FMA, and it multiplies the pair's dot product.
 #include "e2v2_internal.h"
 
 namespace e2v2 {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// One neighbour's value pieces for this lane's 4 channels, all components.
-// fp32 h' is [node][comp][C]: one 16-byte load per component.  16-bit h' is
-// stored with components interleaved in pairs (hp_f16_offset): one 16-byte load
-// covers 4 channels of two components, plus an 8-byte load for an odd last
-// component -- half the load instructions of a per-component layout.
+// One neighbour's value pieces for this lane's 4 channels.  fp32 h' is
+// [node][comp][C]: one 16-byte load per component.  16-bit h' is stored with
+// components interleaved in pairs (hp_f16_offset): one 16-byte load covers 4
+// channels of two components -- half the load instructions of a per-component
+// layout -- and an odd last component travels with the key (hp_pair_row).
 template <bool HB, int NC> struct HpStep;
 template <int NC> struct HpStep<true, NC> {
     static constexpr int NPR = NC / 2;
     uint4 pr[NPR > 0 ? NPR : 1];
-    uint2 tl;
     __device__ __forceinline__ void load(const void *base, int node, int cb, int C)
     {
-        const uint16_t *nb = reinterpret_cast<const uint16_t *>(base) + (size_t)node * NC * C;
+        const uint16_t *nb = reinterpret_cast<const uint16_t *>(base) + (size_t)node * hp_pair_row(NC, C);
 #pragma unroll
         for (int p = 0; p < NPR; ++p) pr[p] = *reinterpret_cast<const uint4 *>(nb + p * 2 * C + (cb >> 2) * 8);
-        if (NC & 1) tl = *reinterpret_cast<const uint2 *>(nb + (NC - 1) * C + cb);
     }
+    // component e < 2 NPR, channel c of the lane's 4 (the odd last component
+    // comes with the key, see tail())
     __device__ __forceinline__ float get(int e, int c) const
     {
-        uint32_t w;
-        if (e < 2 * NPR) {
-            const uint4 &v = pr[e >> 1];
-            const int k = (e & 1) * 2 + (c >> 1);
-            w = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-        } else {
-            w = (c >> 1) == 0 ? tl.x : tl.y;
-        }
+        const uint4 &v = pr[e >> 1];
+        const int k = (e & 1) * 2 + (c >> 1);
+        const uint32_t w = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
         const uint16_t b = (c & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xffffu);
         return (float)__builtin_bit_cast(_Float16, b);
     }
 };
+// fp16 halves of a key + tail group
+__device__ __forceinline__ float f16_of(uint32_t w, int hi)
+{
+    return (float)__builtin_bit_cast(_Float16, uint16_t(hi ? (w >> 16) : (w & 0xffffu)));
+}
 template <int NC> struct HpStep<false, NC> {
     float4 a[NC];
     __device__ __forceinline__ void load(const void *base, int node, int cb, int C)
@@ -136,11 +138,12 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
     const int KK = (R + 3) >> 2;
     const int cb = 8 * h + 4 * b;       // first channel of this lane
 
-    // B operand of the bias product, W_rbf[k][head] zero-padded to 64 x 16, in LDS.
+    // B operand of the bias product, log2(e) W_rbf[k][head] zero-padded to 64 x 16,
+    // in LDS: the product is the bias in the log2 domain of the softmax.
     __shared__ float sW[64 * 16];
     for (int e = threadIdx.x; e < 64 * 16; e += 256) {
         const int k = e >> 4, hh = (e & 15) % H;
-        sW[e] = (k < R) ? A.w_rbf[k * H + hh] : 0.f;
+        sW[e] = (k < R) ? A.w_rbf[k * H + hh] * LOG2E : 0.f;
     }
     __syncthreads();
     if (slot >= n || i < 0 || i >= n) return;             // whole wave: i is wave-uniform
@@ -170,7 +173,7 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
     for (int c0 = 0; c0 < len; c0 += 16) {
         // ---- (a) this lane's S neighbours of the chunk and their row scales
         int js[S];
-        float scl[S];
+        float scl[S];                  // the neighbours' h' and k scale (16-bit storage)
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int p = u * S + s;
@@ -180,9 +183,18 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
         }
         // ---- (b) issue every key row and the first phase of value rows
         float4 kv[S];
+        uint2 tl[HB ? S : 1];          // 16-bit storage: h' component NC - 1, from the key + tail group
 #pragma unroll
-        for (int s = 0; s < S; ++s)
-            kv[s] = *reinterpret_cast<const float4 *>(A.k + (size_t)(js[s] >= 0 ? js[s] : i) * C + cb);
+        for (int s = 0; s < S; ++s) {
+            const size_t node = (size_t)(js[s] >= 0 ? js[s] : i);
+            if constexpr (HB) {
+                const uint4 g4 = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(A.k) + node * (2 * C) + 2 * cb);
+                kv[s] = make_float4(f16_of(g4.x, 0), f16_of(g4.x, 1), f16_of(g4.y, 0), f16_of(g4.y, 1));
+                tl[s] = make_uint2(g4.z, g4.w);
+            } else {
+                kv[s] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(A.k) + node * C + cb);
+            }
+        }
         HpStep<HB, NC> hv[SP];
 #pragma unroll
         for (int s = 0; s < SP; ++s) hv[s].load(A.hp, js[s] >= 0 ? js[s] : i, cb, C);
@@ -242,7 +254,8 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
             qk = fmaf(qv.z, kv[s].z, qk);
             qk = fmaf(qv.w, kv[s].w, qk);
             qk += __shfl_xor(qk, H, 64);
-            sl[s] = js[s] >= 0 ? fmaf(qk, qscale, bs[s] * LOG2E) : -INFINITY;
+            if constexpr (HB) qk *= scl[s];
+            sl[s] = js[s] >= 0 ? fmaf(qk, qscale, bs[s]) : -INFINITY;
         }
         float mx = sl[0];
 #pragma unroll
@@ -280,7 +293,15 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
                 for (int c = 0; c < 4; ++c) {
                     float a = acc[e][c];
 #pragma unroll
-                    for (int s = 0; s < SP; ++s) a = fmaf(ps[ph * SP + s], hv[s].get(e, c), a);
+                    for (int s = 0; s < SP; ++s) {
+                        float x;
+                        if constexpr (HB && (NC & 1))
+                            x = e == NC - 1 ? f16_of(c < 2 ? tl[ph * SP + s].x : tl[ph * SP + s].y, c & 1)
+                                            : hv[s].get(e, c);
+                        else
+                            x = hv[s].get(e, c);
+                        a = fmaf(ps[ph * SP + s], x, a);
+                    }
                     acc[e][c] = a;
                 }
         }

@@ -261,7 +261,7 @@ AttnWs attn_ws(const e2v2_layer_desc &d, int n)
     w.q = o; o += al256(N * C * 4);
     w.k = o; o += al256(N * C * 4);
     w.v = o; o += al256(d.storage == E2V2_BF16 ? 0 : N * NC * C * 4);   // bf16: v stays in registers
-    w.hp = o; o += al256(N * NC * C * s);
+    w.hp = o; o += al256(d.storage == E2V2_BF16 ? N * hp_pair_row((int)NC, (int)C) * 2 : N * NC * C * s);
     w.dmat = o; o += al256(N * nd * 4);
     w.pos4 = o; o += al256(N * 16);
     w.hhat = o; o += al256(N * NC * C * 4);
@@ -499,7 +499,9 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
         qa.wq = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 1) * wsz);
         qa.wk = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 2) * wsz);
         qa.w_src = w->w_src; qa.pos = pos;
-        qa.q = q; qa.k = k; qa.hp = reinterpret_cast<uint16_t *>(hp); qa.pos4 = pos4; qa.dmat = dmat;
+        qa.q = q; qa.kt = reinterpret_cast<uint16_t *>(k); qa.hp = reinterpret_cast<uint16_t *>(hp);
+        qa.pos4 = pos4; qa.dmat = dmat;
+        qa.k_tap = taps ? taps->k : nullptr;
         qa.v_tap = taps ? taps->v : nullptr;
         qa.hp_tap = taps ? taps->hprime : nullptr;
         qa.n = n;
@@ -556,7 +558,7 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
     if (taps) {
         const size_t N = (size_t)n;
         struct { void *dst; const void *src; size_t bytes; } cp[] = {
-            {taps->q, q, N * C * 4}, {taps->k, k, N * C * 4}, {bf ? nullptr : taps->v, v, N * NC * C * 4},
+            {taps->q, q, N * C * 4}, {bf ? nullptr : taps->k, k, N * C * 4}, {bf ? nullptr : taps->v, v, N * NC * C * 4},
             {bf ? nullptr : taps->hhat, hhat, N * NC * C * 4}};
         for (auto &c : cp)
             if (c.dst) {

@@ -363,6 +363,14 @@ __host__ __device__ inline int hp_f16_offset(int e, int c, int NC, int C)
     if (e < 2 * (NC / 2)) return (e >> 1) * 2 * C + (c >> 2) * 8 + (e & 1) * 4 + (c & 3);
     return (NC - 1) * C + c;
 }
+// With 16-bit storage the streaming kernel reads, per node, the component pairs
+// of h' (hp_pair_row fp16 elements, hp_f16_offset layout) and one "key + tail"
+// row of C/4 16-byte groups: k of the group's 4 channels, then, for odd NC,
+// component NC - 1 of h' for the same channels; zeros otherwise.  One 16-byte
+// load per pair serves the logit and the last component.  h' and k share the
+// node's power-of-two scale s (pos4[node].w): the stored fp16 values times s.
+__host__ __device__ constexpr int hp_pair_row(int NC, int C) { return (NC & ~1) * C; }
+
 
 // ----------------------------------------------------------------------------
 // bf16 helpers (bit patterns in uint16_t / packed in uint32_t).
@@ -403,18 +411,21 @@ hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, i
 
 // Fused q / k / v projections and source EAAS for bf16 storage: h bf16
 // [n][NC][C]; wv = packed W_V[0..L] (C*C/8 uint4 each), wq, wk packed W_Q, W_K;
-// w_src [P][C].  Outputs q, k [n][C] fp32; hp fp16 in the hp_f16_offset layout
-// with the node's scale in pos4[node].w; dmat [n][n_dmat(L)].  v_tap and hp_tap
-// (optional, fp32 [n][NC][C]) receive v and h' as stored (dequantised).
+// w_src [P][C].  Outputs q [n][C] fp32; hp: the component pairs of h' (fp16,
+// hp_f16_offset layout, hp_pair_row elements per node) with the node's scale in
+// pos4[node].w; kt: the key + tail rows ([n][C/4][8] fp16); dmat [n][n_dmat(L)].
+// k_tap (fp32 [n][C]), v_tap and hp_tap (fp32 [n][NC][C]) are optional: k and v
+// as projected, h' as stored (dequantised).
 struct QkvEaasArgs {
     const uint16_t *h;
     const uint4 *wv, *wq, *wk;
     const float *w_src, *pos;
-    float *q, *k;
+    float *q;
+    uint16_t *kt;
     uint16_t *hp;
     float4 *pos4;
     float *dmat;
-    float *v_tap, *hp_tap;
+    float *k_tap, *v_tap, *hp_tap;
     int n;
 };
 hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t stream);
@@ -433,9 +444,10 @@ struct EaasOutArgs {
 hipError_t launch_eaas_outproj(int L, const EaasOutArgs &a, int C, hipStream_t stream);
 
 struct AttnArgs {
-    const float *q, *k;              // [n][C] fp32
-    const void *hp;                  // [n][NC][C] fp32, or fp16 (hp_f16_offset layout) scaled by pos4[j].w
-    const float4 *pos4;              // [n] (x, y, z, scale of h'_j)
+    const float *q;                  // [n][C] fp32
+    const void *k;                   // [n][C] fp32, or (16-bit h') the key + tail rows
+    const void *hp;                  // [n][NC][C] fp32, or fp16 component pairs (hp_pair_row) scaled by pos4[j].w
+    const float4 *pos4;              // [n] (x, y, z, scale of h'_j and, 16-bit storage, of k_j)
     const float *dmat;               // [n][n_dmat(L)]
     const int32_t *nbr_start, *nbr_len, *nbr_idx;
     const int32_t *order;            // optional processing order of the targets

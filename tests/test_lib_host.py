@@ -101,9 +101,10 @@ def test_workspace_sizes(lib):
     d = _desc()
     a, b = lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 1000), lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 2000)
     assert 0 < a < b
-    # bf16 storage: q, k fp32 + h' 16-bit + D blocks + padded positions + hhat fp32
-    # per node (v is projected and coupled in registers, never stored)
-    per_node = 128 * 4 * 2 + 9 * 128 * 2 + 34 * 4 + 16 + 9 * 128 * 4
+    # bf16 storage: q fp32, k + last h' component (16 bytes per 4 channels), the
+    # other h' components as fp16 pairs, D blocks, padded positions, hhat fp32 per
+    # node (v is projected and coupled in registers, never stored)
+    per_node = 128 * 4 + 128 * 4 + 8 * 128 * 2 + 34 * 4 + 16 + 9 * 128 * 4
     assert abs((b - a) / 1000 - per_node) < 2
     # fp32 storage adds v and stores h' in fp32
     d32 = _desc(storage=B.E2V2_FP32)
