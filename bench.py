@@ -37,14 +37,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 
 def algorithmic_bytes(cfg, nnz: int) -> dict:
     """Bytes the streaming kernel must move: per pair the neighbour's coupled value
-    row h'_j (storage dtype), its fp32 key row, its index and its position; per
-    target its query, its position, its row bounds and one fp32 output row -- the
-    message m_i for bf16 storage (the target coupling runs in the output kernel),
-    the coupled hhat_i for fp32 storage, which also reads the target's D blocks."""
+    row h'_j and key row k_j, its index and its position -- fp32 rows for fp32
+    storage; for bf16 storage fp16 rows, the key travelling with h's odd last
+    component in 16-byte pieces (4C bytes) next to h's component pairs; per target
+    its query, its position, its row bounds and one fp32 output row -- the message
+    m_i for bf16 storage (the target coupling runs in the output kernel), the
+    coupled hhat_i for fp32 storage, which also reads the target's D blocks."""
     C, nc = cfg.channels, cfg.n_comp
-    s = 2 if cfg.storage == "bf16" else 4
     nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
-    per_pair = nc * C * s + 4 * C + 4 + 12
+    if cfg.storage == "bf16":
+        per_pair = 2 * (nc & ~1) * C + 4 * C + 4 + 12
+    else:
+        per_pair = 4 * nc * C + 4 * C + 4 + 12
     per_node = 4 * C + 12 + 8 + 4 * nc * C + (0 if cfg.storage == "bf16" else 4 * nd)
     return {"per_pair": per_pair, "per_node": per_node, "total": nnz * per_pair + cfg.n * per_node}
 
@@ -190,8 +194,9 @@ def main():
     C, nc, s = cfg.channels, cfg.n_comp, (2 if cfg.storage == "bf16" else 4)
     nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
     if cfg.storage == "bf16":
-        # fused projections + source EAAS: h in; q, k, h' (16-bit), D blocks, pos4 out
-        front = N * nc * C * 2 + N * C * 8 + N * 12 + N * nc * C * 2 + N * (4 * nd + 16)
+        # fused projections + source EAAS: h and positions in; q, the key + tail rows,
+        # h's component pairs, D blocks, pos4 out
+        front = N * nc * C * 2 + N * 12 + N * C * 4 + N * C * 4 + N * (nc & ~1) * C * 2 + N * (4 * nd + 16)
         stage_names = ("neighbours", "projections+source_eaas", None, "attention", "target_eaas+output_projection")
         front += N * (4 * nd + 16)          # the back end reads the D blocks and pos4 again
     else:
