@@ -153,9 +153,11 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
     const float qscale = LOG2E * 0.35355339059327373f;   // log2(e) / sqrt(8)
     const int start = __builtin_amdgcn_readfirstlane(A.nbr_start[i]);
     const int len = __builtin_amdgcn_readfirstlane(A.nbr_len[i]);
-    const float inv_delta = (float)(R - 1) / A.cutoff;
+    // Gaussians in the log2 domain: exp(-t^2 / 2) = exp2(-(g t)^2) with g^2 = log2(e) / 2,
+    // t = (d - mu_k) / Delta; the envelope joins the exponent as log2(fc).
+    const float gsc = 0.84932180028801904f;              // sqrt(log2(e) / 2)
+    const float inv_delta = gsc * (float)(R - 1) / A.cutoff;
     const float cos_scale = 0.5f / A.cutoff;             // cos(pi d / rc) = cos(2 pi * d / (2 rc))
-    const float gexp = -0.5f * LOG2E;
 
     float mu = -1e30f, z = 0.f;
     float acc[NC][4];
@@ -206,7 +208,8 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
         const float dx = pj.x - pi4.x, dy = pj.y - pi4.y, dz = pj.z - pi4.z;
         const float d = vp ? sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;
         const float fc = vp ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
-        const float t0 = d * inv_delta - (float)kq;      // (d - mu_k) / Delta for k = kq
+        const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
+        const float t0 = fmaf(d, inv_delta, -gsc * (float)kq);   // g (d - mu_k) / Delta for k = kq
         const float *wrow = sW + kq * 16 + pm;
         floatx4 bias = {0.f, 0.f, 0.f, 0.f};
         // Branch-free product over 8 (up to 32 RBFs) or 16 steps of 4 RBFs; the
@@ -217,8 +220,8 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
             for (int kk = 0; kk < 8; ++kk) wk[kk] = wrow[64 * kk];
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                const float tk = t0 - 4.0f * (float)kk;
-                const float phi = fc * __builtin_amdgcn_exp2f(gexp * tk * tk);
+                const float tk = t0 - (4.0f * gsc) * (float)kk;
+                const float phi = __builtin_amdgcn_exp2f(fmaf(-tk, tk, lfc));
                 bias = __builtin_amdgcn_mfma_f32_16x16x4f32(phi, wk[kk], bias, 0, 0, 0);
             }
         } else {
@@ -227,8 +230,8 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
             for (int kk = 0; kk < 16; ++kk) wk[kk] = wrow[64 * kk];
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) {
-                const float tk = t0 - 4.0f * (float)kk;
-                const float phi = fc * __builtin_amdgcn_exp2f(gexp * tk * tk);
+                const float tk = t0 - (4.0f * gsc) * (float)kk;
+                const float phi = __builtin_amdgcn_exp2f(fmaf(-tk, tk, lfc));
                 bias = __builtin_amdgcn_mfma_f32_16x16x4f32(phi, wk[kk], bias, 0, 0, 0);
             }
         }
@@ -257,27 +260,34 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
             if constexpr (HB) qk *= scl[s];
             sl[s] = js[s] >= 0 ? fmaf(qk, qscale, bs[s]) : -INFINITY;
         }
+        // The reference maximum mu moves only when a logit exceeds it by more than 8
+        // (weights up to 2^8 are harmless in fp32), so the rescale of the
+        // accumulators is skipped in most chunks; the branch is wave-uniform.
         float mx = sl[0];
 #pragma unroll
         for (int s = 1; s < S; ++s) mx = fmaxf(mx, sl[s]);
-        const float mun = fmaxf(mu, mx);
-        const float corr = __builtin_amdgcn_exp2f(mu - mun);
+        const bool grow = mx > mu + 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float mun = grow ? mx : mu;
+            const float corr = __builtin_amdgcn_exp2f(mu - mun);
+            z *= corr;
+#pragma unroll
+            for (int e = 0; e < NC; ++e)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[e][c] *= corr;
+            mu = mun;
+        }
         float ps[S];
         float psum = 0.f;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            ps[s] = __builtin_amdgcn_exp2f(sl[s] - mun);
+            ps[s] = __builtin_amdgcn_exp2f(sl[s] - mu);
             psum += ps[s];
             ps[s] *= scl[s];                   // fold the row scale into the weight
         }
-        z = fmaf(z, corr, psum);
-        mu = mun;
-        // ---- (f) rescale, then accumulate phase by phase; the next chunk's position
-        //          is requested with the last phase
-#pragma unroll
-        for (int e = 0; e < NC; ++e)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[e][c] *= corr;
+        z += psum;
+        // ---- (f) accumulate phase by phase; the next chunk's position is requested
+        //          with the last phase
         float4 pjn = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int ph = 0; ph < NPH; ++ph) {
