@@ -7,19 +7,24 @@
 // search with the same arithmetic.
 //
 // Steps (all on the caller's stream):
-//   1. one block reduces the bounding box and sizes a grid whose cells are at
-//      least (1 + 1e-5) * cutoff wide (so a 27-cell stencil covers every pair
-//      even with rounding in the cell index) and holds at most n + 64 cells;
+//   1. one block reduces the bounding box and sizes a grid whose cells are about
+//      half the cutoff wide (at most n + 64 cells);
 //   2. cell index per atom + per-cell counts (integer atomics: counts are exact);
 //   3. exclusive scan of the counts; scatter atoms into cell order;
 //   4. one wave per target (targets taken in cell order, so neighbouring waves
-//      read the same cells) scans the 27-cell stencil, compacts the pairs that
-//      pass into LDS, picks the K nearest there by rank counting and orders the
-//      row by j with a register bitonic sort:
+//      read the same cells) visits the rows of cells that the cutoff sphere can
+//      reach, each row cut along x to the sphere's extent there (so the scan
+//      covers little more than the sphere), compacts the pairs that pass into
+//      LDS and orders the row by j with a register bitonic sort:
 //        K = 0: count -> scan -> fill, rows sorted by j;
-//        K > 0: the K nearest by (d2, j), sorted by j, padded with -1.
+//        K > 0: the K nearest by (d2, j), sorted by j, padded with -1; rows with
+//               more than K candidates are cut by a second wave kernel that ranks
+//               them in LDS.
 //      Rows with more candidates than the LDS buffer holds are finished by a
 //      per-thread kernel (a max-heap held in the row itself, then a heapsort).
+//   The reach of the sphere along each axis is widened by a margin that covers
+//   fp32 rounding in the cell index and the cell bounds, so the rows and cells
+//   visited are always a superset of the ones holding a neighbour.
 // Within-cell order depends on atomics, but rows are sets sorted by j and the
 // K-nearest choice uses a total order, so results are deterministic.
 #include "e2v2_internal.h"
@@ -32,7 +37,9 @@ namespace e2v2 {
 
 struct GridInfo {
     float lo[3];
-    float inv[3];
+    float inv[3];          // cells per unit length (cell index = floor((x - lo) * inv), clamped)
+    float w[3];            // cell width
+    float margin;          // widening of every reach test: covers fp32 rounding of bounds and indices
     int dims[3];
     int ncell;
 };
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(256) void k_bbox(const float *__restrict__ part, in
     // clear the cell counters for step 2
     for (long long c = t; c <= maxc; c += 256) cell_cnt[c] = 0;
     if (t == 0) {
-        const float cmin = cutoff * 1.00001f;
+        const float cmin = 0.5f * cutoff * 1.001f;              // two cells per cutoff
         int dims[3];
         float ext[3];
         for (int d = 0; d < 3; ++d) {
@@ -142,11 +149,18 @@ __global__ __launch_bounds__(256) void k_bbox(const float *__restrict__ part, in
             if (dims[2] > dims[a]) a = 2;
             dims[a] = dims[a] * 7 / 8 > 0 ? dims[a] * 7 / 8 : 1;
         }
+        float mag = 0.f;
         for (int d = 0; d < 3; ++d) {
             grid->lo[d] = (smin[d][0] < 1e30f && smin[d][0] > -1e30f) ? smin[d][0] : 0.f;
             grid->inv[d] = dims[d] > 1 ? (float)dims[d] / ext[d] : 0.f;
+            grid->w[d] = dims[d] > 1 ? ext[d] / (float)dims[d] : INFINITY;
             grid->dims[d] = dims[d];
+            mag = fmaxf(mag, fmaxf(fabsf(smin[d][0]), fabsf(smax[d][0])));
         }
+        // fp32 rounding of a coordinate-sized quantity is below 6e-8 of the largest
+        // coordinate; 1e-5 of it (plus 1e-4 of the cutoff) is a wide bound
+        const float m = 1e-5f * mag + 1e-4f * cutoff;
+        grid->margin = (m < 1e30f) ? m : INFINITY;              // NaN / inf: every cell is in reach
         grid->ncell = dims[0] * dims[1] * dims[2];
     }
 }
@@ -156,6 +170,35 @@ __device__ __forceinline__ int cell_coord(float x, float lo, float inv, int dim)
     const float t = (x - lo) * inv;
     if (!(t > 0.f)) return 0;                                // also NaN
     return t >= (float)(dim - 1) ? dim - 1 : (int)t;
+}
+
+// Cells [c0, c1] along axis d that hold every coordinate within r of p.  Cell
+// indices are monotone in the coordinate, so the ends' cells bound them.
+__device__ __forceinline__ void axis_reach(float p, float r, const GridInfo &gi, int d, int &c0, int &c1)
+{
+    c0 = cell_coord(p - r, gi.lo[d], gi.inv[d], gi.dims[d]);
+    c1 = cell_coord(p + r, gi.lo[d], gi.inv[d], gi.dims[d]);
+}
+
+// Distance along axis d from p to the coordinates of cell c (the first and last
+// cells reach to -inf / +inf), reduced by the margin: never more than the true gap.
+__device__ __forceinline__ float axis_gap(float p, int c, const GridInfo &gi, int d)
+{
+    const float a = c > 0 ? gi.lo[d] + (float)c * gi.w[d] : -INFINITY;
+    const float b = c < gi.dims[d] - 1 ? gi.lo[d] + (float)(c + 1) * gi.w[d] : INFINITY;
+    const float g = fmaxf(fmaxf(a - p, p - b), 0.f);         // fmaxf drops a NaN operand
+    return fmaxf(g - gi.margin, 0.f);
+}
+
+// The x-cells of row (z, y) that a sphere of radius rcm about p can reach, as
+// [x0, x1]; false if the row is out of reach.
+__device__ __forceinline__ bool row_reach(float4 p, float rcm, int z, int y, const GridInfo &gi, int &x0, int &x1)
+{
+    const float gz = axis_gap(p.z, z, gi, 2), gy = axis_gap(p.y, y, gi, 1);
+    const float rem = rcm * rcm - gz * gz - gy * gy;
+    if (!(rem > 0.f)) return false;
+    axis_reach(p.x, sqrtf(rem) + gi.margin, gi, 0, x0, x1);
+    return true;
 }
 
 // ---------------------------------------------------------------- step 2
@@ -235,34 +278,31 @@ __device__ __forceinline__ double d2_of(const float *__restrict__ pos, double xi
     return pair_d2(xi, yi, zi, make_float4(pos[3 * (size_t)j], pos[3 * (size_t)j + 1], pos[3 * (size_t)j + 2], 0.f));
 }
 
-// Visits every candidate j != i in the 27-cell stencil with d2 < rc2.
+// Visits every candidate j != i within reach of the cutoff sphere with d2 < rc2.
 template <typename F>
-__device__ __forceinline__ void for_each_neighbor(int i, double xi, double yi, double zi, float xf, float yf,
-                                                  float zf, double rc2, const GridInfo &gi,
+__device__ __forceinline__ void for_each_neighbor(int i, float4 pi, float rc, double rc2, const GridInfo &gi,
                                                   const int32_t *__restrict__ cell_start,
                                                   const float4 *__restrict__ spos, F &&f)
 {
-    const int cx = cell_coord(xf, gi.lo[0], gi.inv[0], gi.dims[0]);
-    const int cy = cell_coord(yf, gi.lo[1], gi.inv[1], gi.dims[1]);
-    const int cz = cell_coord(zf, gi.lo[2], gi.inv[2], gi.dims[2]);
-    for (int z = cz - 1; z <= cz + 1; ++z) {
-        if (z < 0 || z >= gi.dims[2]) continue;
-        for (int y = cy - 1; y <= cy + 1; ++y) {
-            if (y < 0 || y >= gi.dims[1]) continue;
-            for (int x = cx - 1; x <= cx + 1; ++x) {
-                if (x < 0 || x >= gi.dims[0]) continue;
-                const int c = (z * gi.dims[1] + y) * gi.dims[0] + x;
-                const int e = cell_start[c + 1];
-                for (int s = cell_start[c]; s < e; ++s) {
-                    const float4 pj = spos[s];
-                    const int j = __float_as_int(pj.w);
-                    if (j == i) continue;
-                    const double d2 = pair_d2(xi, yi, zi, pj);
-                    if (d2 < rc2) f(j, d2);
-                }
+    const double xi = pi.x, yi = pi.y, zi = pi.z;
+    const float rcm = rc + gi.margin;
+    int z0, z1, y0, y1;
+    axis_reach(pi.z, rcm, gi, 2, z0, z1);
+    axis_reach(pi.y, rcm, gi, 1, y0, y1);
+    for (int z = z0; z <= z1; ++z)
+        for (int y = y0; y <= y1; ++y) {
+            int x0, x1;
+            if (!row_reach(pi, rcm, z, y, gi, x0, x1)) continue;
+            const int rowc = (z * gi.dims[1] + y) * gi.dims[0];
+            const int e = cell_start[rowc + x1 + 1];
+            for (int s = cell_start[rowc + x0]; s < e; ++s) {
+                const float4 pj = spos[s];
+                const int j = __float_as_int(pj.w);
+                if (j == i) continue;
+                const double d2 = pair_d2(xi, yi, zi, pj);
+                if (d2 < rc2) f(j, d2);
             }
         }
-    }
 }
 
 // In-place heapsort of ints ascending.
@@ -286,7 +326,7 @@ __device__ inline void heapsort_int(int32_t *a, int len)
 }
 
 // Per-thread fills for rows longer than the wave kernels' LDS buffer (kWaveCap).
-__global__ void k_fill_csr(int n, int cap, double rc2, const GridInfo *__restrict__ grid,
+__global__ void k_fill_csr(int n, int cap, float rc, double rc2, const GridInfo *__restrict__ grid,
                            const int32_t *__restrict__ cell_start, const int32_t *__restrict__ order,
                            const float4 *__restrict__ spos, const int32_t *__restrict__ nbr_start,
                            const int32_t *__restrict__ nbr_len, int32_t *nbr_idx)
@@ -299,8 +339,7 @@ __global__ void k_fill_csr(int n, int cap, double rc2, const GridInfo *__restric
     const float4 pi = spos[t];
     int32_t *row = nbr_idx + nbr_start[i];
     int cnt = 0;
-    for_each_neighbor(i, (double)pi.x, (double)pi.y, (double)pi.z, pi.x, pi.y, pi.z, rc2, gi, cell_start, spos,
-                      [&](int j, double) { row[cnt++] = j; });
+    for_each_neighbor(i, pi, rc, rc2, gi, cell_start, spos, [&](int j, double) { row[cnt++] = j; });
     heapsort_int(row, cnt);
 }
 
@@ -310,7 +349,8 @@ __device__ __forceinline__ bool key_less(double da, int ja, double db, int jb)
     return da < db || (da == db && ja < jb);
 }
 
-__global__ void k_fill_capped(int n, int K, double rc2, const float *__restrict__ pos, const GridInfo *__restrict__ grid,
+__global__ void k_fill_capped(int n, int K, float rc, double rc2, const float *__restrict__ pos,
+                              const GridInfo *__restrict__ grid,
                               const int32_t *__restrict__ cell_start, const int32_t *__restrict__ order,
                               const float4 *__restrict__ spos, int32_t *nbr_start, int32_t *nbr_len, int32_t *nbr_idx)
 {
@@ -343,7 +383,7 @@ __global__ void k_fill_capped(int n, int K, double rc2, const float *__restrict_
         row[root] = rj;
     };
     int cnt = 0;
-    for_each_neighbor(i, xi, yi, zi, pi.x, pi.y, pi.z, rc2, gi, cell_start, spos, [&](int j, double d2) {
+    for_each_neighbor(i, pi, rc, rc2, gi, cell_start, spos, [&](int j, double d2) {
         if (cnt < K) {
             row[cnt] = j;
             if (cnt + 1 == K)
@@ -365,14 +405,16 @@ __global__ void k_fill_capped(int n, int K, double rc2, const float *__restrict_
 }
 
 // ---------------------------------------------------------------- step 4, one wave per target
-// A wave scans its target's stencil 64 candidates at a time: for fixed (z, y) the
-// three x-neighbouring cells are adjacent in cell order, so the stencil is 9
-// contiguous ranges of the cell-sorted arrays.  Passing candidates are compacted
-// into LDS (ballot + prefix count).  Over-cap rows are cut to the K nearest by
-// rank counting (the rank of an element is the number of elements with a smaller
-// (d2, j) key, which is its final slot), and every row is then sorted by j in
-// registers.  Rows longer than the LDS buffer are marked and left to the
-// per-thread kernels above.
+// A wave scans its target's reach 64 candidates at a time.  Cells are sorted by
+// (z, y, x), so the x-cells of one (z, y) row that the sphere reaches are one
+// contiguous range of the cell-sorted arrays; lane r resolves row r, and the
+// rows' ranges are flattened into one candidate index space (a candidate finds
+// its row by a binary search over the lanes' running totals).  Passing
+// candidates are compacted into LDS (ballot + prefix count).  Rows are then
+// sorted by j in registers; over-cap rows are cut to the K nearest by rank
+// counting (the rank of an element is the number of elements with a smaller
+// (d2, j) key, which is its final slot).  Rows longer than the LDS buffer are
+// marked and left to the per-thread kernels above.
 constexpr int kWaveCap = 1024;                 // candidates a wave can hold in LDS
 constexpr int kWavesPerBlock = 4;
 
@@ -383,11 +425,6 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Number of neighbours of the target at cell-order slot t; with COLLECT the first
-// kWaveCap of them land in cj / cd (unordered).  Returns a wave-uniform count.
-// The 9 row ranges of the stencil are resolved first and flattened into one
-// candidate index space; candidate positions are then fetched 4 x 64 at a time,
-// so a target costs a few memory round trips rather than one per 64 candidates.
 // Decides d2 < rc2 exactly.  An fp32 estimate settles every pair whose squared
 // distance is not within a relative 1e-5 of rc2 (its own error is below 4e-7
 // relative: one rounding per difference, product and sum); the rest take the
@@ -413,58 +450,72 @@ struct CutoffTest {
     }
 };
 
+// Number of neighbours of target i at position pi; with COLLECT the first kWaveCap
+// of them land in cj (unordered).  Returns a wave-uniform count.  Candidate
+// positions are fetched 4 x 64 at a time, so a target costs a few memory round
+// trips rather than one per 64 candidates.
 template <bool COLLECT>
-__device__ __forceinline__ int wave_scan(int i, float4 pi, double rc2, const GridInfo &gi,
+__device__ __forceinline__ int wave_scan(int i, float4 pi, float rc, double rc2, const GridInfo &gi,
                                          const int32_t *__restrict__ cell_start, const float4 *__restrict__ spos,
                                          int32_t *cj, int lane)
 {
     constexpr int U = 4;
     const double xi = pi.x, yi = pi.y, zi = pi.z;
     const CutoffTest test(rc2);
-    const int cx = cell_coord(pi.x, gi.lo[0], gi.inv[0], gi.dims[0]);
-    const int cy = cell_coord(pi.y, gi.lo[1], gi.inv[1], gi.dims[1]);
-    const int cz = cell_coord(pi.z, gi.lo[2], gi.inv[2], gi.dims[2]);
-    const int x0 = cx > 0 ? cx - 1 : 0, x1 = cx + 1 < gi.dims[0] ? cx + 1 : gi.dims[0] - 1;
-    // ranges r = 0..8 over (z, y); an out-of-grid row is an empty range
-    int pre[10], off[9];
-    pre[0] = 0;
-#pragma unroll
-    for (int r = 0; r < 9; ++r) {
-        const int z = cz - 1 + r / 3, y = cy - 1 + r % 3;
-        int a = 0, b = 0;
-        if (z >= 0 && z < gi.dims[2] && y >= 0 && y < gi.dims[1]) {
-            const int rowc = (z * gi.dims[1] + y) * gi.dims[0];
-            a = cell_start[rowc + x0];
-            b = cell_start[rowc + x1 + 1];
-        }
-        off[r] = a - pre[r];                      // candidate f of range r is spos[f + off[r]]
-        pre[r + 1] = pre[r] + (b - a);
-    }
-    const int total = pre[9];
+    const float rcm = rc + gi.margin;
+    int z0, z1, y0, y1;
+    axis_reach(pi.z, rcm, gi, 2, z0, z1);
+    axis_reach(pi.y, rcm, gi, 1, y0, y1);
+    const int ny = y1 - y0 + 1, nrow = (z1 - z0 + 1) * ny;
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     int count = 0;
-    for (int c0 = 0; c0 < total; c0 += 64 * U) {
-        float4 pj[U];
-        bool ok[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int f = c0 + 64 * u + lane;
-            ok[u] = f < total;
-            int o = off[0];
-#pragma unroll
-            for (int r = 1; r < 9; ++r) o = f >= pre[r] ? off[r] : o;
-            pj[u] = ok[u] ? spos[f + o] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = __float_as_int(pj[u].w);
-            const bool pass = ok[u] && j != i && test.inside(xi, yi, zi, pi, pj[u]);
-            const uint64_t m = __ballot(pass);
-            if (COLLECT && pass) {
-                const int slot = count + __popcll(m & below);
-                if (slot < kWaveCap) cj[slot] = j;
+    for (int rb = 0; rb < nrow; rb += 64) {           // one pass unless the reach spans > 64 rows
+        // lane r: candidate range [a, a + len) of row rb + r
+        int a = 0, len = 0;
+        const int r = rb + lane;
+        if (r < nrow) {
+            const int zr = r / ny;
+            const int z = z0 + zr, y = y0 + (r - zr * ny);
+            int x0, x1;
+            if (row_reach(pi, rcm, z, y, gi, x0, x1)) {
+                const int rowc = (z * gi.dims[1] + y) * gi.dims[0];
+                a = cell_start[rowc + x0];
+                len = cell_start[rowc + x1 + 1] - a;
             }
-            count += __popcll(m);
+        }
+        int incl = len;                               // running total over lanes 0..r
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        const int total = __shfl(incl, 63, 64);
+        const int offr = a - (incl - len);            // candidate f of row r is spos[f + offr]
+        for (int c0 = 0; c0 < total; c0 += 64 * U) {
+            float4 pj[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int f = c0 + 64 * u + lane;
+                ok[u] = f < total;
+                // row of f = the number of rows whose running total is <= f (totals ascend)
+                int k = 0;
+#pragma unroll
+                for (int st = 32; st >= 1; st >>= 1) k += (__shfl(incl, k + st - 1, 64) <= f) ? st : 0;
+                const int o = __shfl(offr, k, 64);
+                pj[u] = ok[u] ? spos[f + o] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = __float_as_int(pj[u].w);
+                const bool pass = ok[u] && j != i && test.inside(xi, yi, zi, pi, pj[u]);
+                const uint64_t m = __ballot(pass);
+                if (COLLECT && pass) {
+                    const int slot = count + __popcll(m & below);
+                    if (slot < kWaveCap) cj[slot] = j;
+                }
+                count += __popcll(m);
+            }
         }
     }
     return count;
@@ -530,49 +581,87 @@ __device__ __forceinline__ void wave_write_sorted(const int32_t *cj, int cnt, in
     else wave_write_sorted_n<16>(cj, cnt, row, lane);
 }
 
-// The over-cap selection ranks by counting, with broadcast LDS reads: the keys are
-// read 2 doubles at a time as one 16-byte load that every lane shares, and each
-// lane ranks all of its elements (e = lane + 64 c, c < NCH) against them.  Arrays
-// are padded to a multiple of 4 entries with keys that rank after every real key.
-
-// The K nearest by (d2, j): kj[rank] = j for every candidate of rank < K.
-template <int NCH>
-__device__ __forceinline__ void wave_select_nearest_n(const double *cd, const int32_t *cj, int cnt, int K,
-                                                      int32_t *kj, int lane)
+// The K nearest of cnt candidates by (d2, j), exactly: every lane computes the
+// fp64 squared distances of its E candidates, the wave sorts the keys (bits of
+// d2, which order like the values for d2 >= 0, then j) with a register bitonic
+// sort, and cj[0 .. K) receives the first K indices (unordered by j).
+constexpr int kSelectCap = 512;                 // largest candidate count ranked in registers
+__device__ __forceinline__ bool key_before(uint64_t da, int ja, uint64_t db, int jb)
 {
-    double de[NCH];
-    int je[NCH], r[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int e = lane + 64 * c;
-        de[c] = e < cnt ? cd[e] : INFINITY;
-        je[c] = e < cnt ? cj[e] : INT_MAX;
-        r[c] = 0;
-    }
-    const double2 *d2 = reinterpret_cast<const double2 *>(cd);
-    const int2 *j2 = reinterpret_cast<const int2 *>(cj);
-    const int nb2 = (cnt + 1) >> 1;
-    for (int t = 0; t < nb2; ++t) {
-        const double2 dv = d2[t];
-        const int2 jv = j2[t];
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            r[c] += (dv.x < de[c] || (dv.x == de[c] && jv.x < je[c])) ? 1 : 0;
-            r[c] += (dv.y < de[c] || (dv.y == de[c] && jv.y < je[c])) ? 1 : 0;
-        }
-    }
-    wave_lds_sync();                                      // kj may alias cd
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-        if (lane + 64 * c < cnt && r[c] < K) kj[r[c]] = je[c];
+    return da < db || (da == db && ja < jb);
 }
-__device__ __forceinline__ void wave_select_nearest(const double *cd, const int32_t *cj, int cnt, int K, int32_t *kj,
+template <int E>
+__device__ __forceinline__ void wave_keep_nearest_n(int32_t *cj, int cnt, int K, float4 pi, const float *__restrict__ pos,
                                                     int lane)
 {
-    if (cnt <= 256) wave_select_nearest_n<4>(cd, cj, cnt, K, kj, lane);
-    else if (cnt <= 384) wave_select_nearest_n<6>(cd, cj, cnt, K, kj, lane);
-    else if (cnt <= 512) wave_select_nearest_n<8>(cd, cj, cnt, K, kj, lane);
-    else wave_select_nearest_n<16>(cd, cj, cnt, K, kj, lane);
+    constexpr int N = 64 * E;
+    uint64_t dk[E];
+    int jk[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int e = lane * E + k;
+        dk[k] = ~0ull;
+        jk[k] = INT_MAX;
+        if (e < cnt) {
+            const int j = cj[e];
+            const double d2 = pair_d2((double)pi.x, (double)pi.y, (double)pi.z,
+                                      make_float4(pos[3 * (size_t)j], pos[3 * (size_t)j + 1], pos[3 * (size_t)j + 2], 0.f));
+            dk[k] = (uint64_t)__double_as_longlong(d2);
+            jk[k] = j;
+        }
+    }
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+        for (int d = size >> 1; d >= 1; d >>= 1) {
+            if (d >= E) {
+                const int lx = d / E;
+                const bool asc = ((lane * E) & size) == 0;
+                const bool keep_min = ((lane & lx) == 0) == asc;
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const uint32_t olo = __shfl_xor((uint32_t)dk[k], lx, 64);
+                    const uint32_t ohi = __shfl_xor((uint32_t)(dk[k] >> 32), lx, 64);
+                    const int oj = __shfl_xor(jk[k], lx, 64);
+                    const uint64_t od = ((uint64_t)ohi << 32) | olo;
+                    const bool other_first = key_before(od, oj, dk[k], jk[k]);
+                    if (other_first == keep_min) {
+                        dk[k] = od;
+                        jk[k] = oj;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    if (k & d) continue;
+                    const bool asc = ((lane * E + k) & size) == 0;
+                    const bool sw = asc ? key_before(dk[k | d], jk[k | d], dk[k], jk[k])
+                                        : key_before(dk[k], jk[k], dk[k | d], jk[k | d]);
+                    if (sw) {
+                        const uint64_t td = dk[k];
+                        const int tj = jk[k];
+                        dk[k] = dk[k | d];
+                        jk[k] = jk[k | d];
+                        dk[k | d] = td;
+                        jk[k | d] = tj;
+                    }
+                }
+            }
+        }
+    }
+    wave_lds_sync();                                  // every lane has read its candidates
+#pragma unroll
+    for (int k = 0; k < E; ++k)
+        if (lane * E + k < K) cj[lane * E + k] = jk[k];
+    wave_lds_sync();
+}
+__device__ __forceinline__ void wave_keep_nearest(int32_t *cj, int cnt, int K, float4 pi, const float *__restrict__ pos,
+                                                  int lane)
+{
+    if (cnt <= 64) wave_keep_nearest_n<1>(cj, cnt, K, pi, pos, lane);
+    else if (cnt <= 128) wave_keep_nearest_n<2>(cj, cnt, K, pi, pos, lane);
+    else if (cnt <= 256) wave_keep_nearest_n<4>(cj, cnt, K, pi, pos, lane);
+    else wave_keep_nearest_n<8>(cj, cnt, K, pi, pos, lane);
 }
 
 // Pads keys [cnt, cnt rounded up to 4) so that they rank after every real key.
@@ -585,7 +674,8 @@ __device__ __forceinline__ void wave_pad_keys(int32_t *cj, double *cd, int cnt, 
     }
 }
 
-__global__ __launch_bounds__(64 * kWavesPerBlock) void k_count_wave(int n, double rc2, const GridInfo *__restrict__ grid,
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_count_wave(int n, float rc, double rc2,
+                                                                    const GridInfo *__restrict__ grid,
                                                                     const int32_t *__restrict__ cell_start,
                                                                     const int32_t *__restrict__ order,
                                                                     const float4 *__restrict__ spos, int32_t *nbr_len)
@@ -595,12 +685,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_count_wave(int n, doubl
     if (t >= n) return;
     const GridInfo gi = *grid;
     const int i = order[t];
-    const int cnt = wave_scan<false>(i, spos[t], rc2, gi, cell_start, spos, nullptr, lane);
+    const int cnt = wave_scan<false>(i, spos[t], rc, rc2, gi, cell_start, spos, nullptr, lane);
     if (lane == 0) nbr_len[i] = cnt;
 }
 
-// CSR rows of at most kWaveCap entries (longer rows: k_fill_csr_long).
-__global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, double rc2, const GridInfo *__restrict__ grid,
+// CSR rows of at most kWaveCap entries (longer rows: k_fill_csr).
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, float rc, double rc2,
+                                                                       const GridInfo *__restrict__ grid,
                                                                        const int32_t *__restrict__ cell_start,
                                                                        const int32_t *__restrict__ order,
                                                                        const float4 *__restrict__ spos,
@@ -614,15 +705,18 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, do
     const int i = order[t];
     if (nbr_len[i] > kWaveCap) return;
     const GridInfo gi = *grid;
-    const int cnt = wave_scan<true>(i, spos[t], rc2, gi, cell_start, spos, sj[w], lane);
+    const int cnt = wave_scan<true>(i, spos[t], rc, rc2, gi, cell_start, spos, sj[w], lane);
     wave_pad_keys(sj[w], nullptr, cnt, lane);
     wave_lds_sync();
     wave_write_sorted(sj[w], cnt, nbr_idx + nbr_start[i], lane);
 }
 
-// Capped rows: keep the K nearest by (d2, j), written sorted by j and padded with -1.
-// Targets with more than kWaveCap candidates get nbr_len = -1 for k_fill_capped.
-__global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n, int K, double rc2,
+// Capped rows: every candidate if there are at most K, else the K nearest by
+// (d2, j); written sorted by j and padded with -1.  Rows with more than
+// kSelectCap candidates over the cap, or more than kWaveCap in all, get
+// nbr_len = -1 and are finished by k_fill_capped.  Only the index buffer sits in
+// LDS, so many waves share a CU.
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n, int K, float rc, double rc2,
                                                                           const float *__restrict__ pos,
                                                                           const GridInfo *__restrict__ grid,
                                                                           const int32_t *__restrict__ cell_start,
@@ -632,42 +726,27 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
                                                                           int32_t *nbr_idx)
 {
     __shared__ __align__(16) int32_t sj[kWavesPerBlock][kWaveCap + 4];
-    __shared__ __align__(16) double sd[kWavesPerBlock][kWaveCap + 4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerBlock + w));
     if (t >= n) return;
     const int i = order[t];
     const GridInfo gi = *grid;
     int32_t *cj = sj[w];
-    double *cd = sd[w];
     const float4 pi = spos[t];
-    const int cnt = wave_scan<true>(i, pi, rc2, gi, cell_start, spos, cj, lane);
+    const int cnt = wave_scan<true>(i, pi, rc, rc2, gi, cell_start, spos, cj, lane);
     int32_t *row = nbr_idx + (size_t)i * K;
     if (lane == 0) nbr_start[i] = (int32_t)((size_t)i * K);
-    if (cnt > kWaveCap) {
+    if (cnt > kWaveCap || (cnt > K && cnt > kSelectCap)) {
         if (lane == 0) nbr_len[i] = -1;
         return;
     }
-    wave_pad_keys(cj, cd, cnt, lane);
     wave_lds_sync();
     int len = cnt;
-    if (cnt <= K) {
-        wave_write_sorted(cj, cnt, row, lane);
-    } else {
-        // exact squared distances of the candidates, for the (d2, j) order
-        for (int e = lane; e < cnt; e += 64) {
-            const int j = cj[e];
-            cd[e] = pair_d2((double)pi.x, (double)pi.y, (double)pi.z,
-                            make_float4(pos[3 * (size_t)j], pos[3 * (size_t)j + 1], pos[3 * (size_t)j + 2], 0.f));
-        }
-        wave_lds_sync();
-        int32_t *kj = reinterpret_cast<int32_t *>(cd);   // the distances are no longer needed after ranking
-        wave_select_nearest(cd, cj, cnt, K, kj, lane);
-        wave_pad_keys(kj, nullptr, K, lane);
-        wave_lds_sync();
-        wave_write_sorted(kj, K, row, lane);
+    if (cnt > K) {
+        wave_keep_nearest(cj, cnt, K, pi, pos, lane);
         len = K;
     }
+    wave_write_sorted(cj, len, row, lane);
     for (int sidx = len + lane; sidx < K; sidx += 64) row[sidx] = -1;
     if (lane == 0) nbr_len[i] = len;
 }
@@ -688,8 +767,8 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
     k_scatter<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_cur, L.order, L.spos, order_out);
     if (K == 0) {
         const double rc2 = (double)cutoff * (double)cutoff;
-        k_count_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(n, rc2, L.grid, L.cell_start, L.order,
-                                                                                L.spos, nbr_len);
+        k_count_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(n, cutoff, rc2, L.grid, L.cell_start,
+                                                                                L.order, L.spos, nbr_len);
     }
     return hipGetLastError();
 }
@@ -711,13 +790,13 @@ hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, v
     const double rc2 = (double)cutoff * (double)cutoff;
     if (K == 0) {
         k_fill_csr_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(
-            n, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
-        k_fill_csr<<<nblk(n, 128), 128, 0, stream>>>(n, kWaveCap, rc2, L.grid, L.cell_start, L.order, L.spos,
+            n, cutoff, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
+        k_fill_csr<<<nblk(n, 128), 128, 0, stream>>>(n, kWaveCap, cutoff, rc2, L.grid, L.cell_start, L.order, L.spos,
                                                       nbr_start, nbr_len, nbr_idx);
     } else {
         k_fill_capped_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(
-            n, K, rc2, pos, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
-        k_fill_capped<<<nblk(n, 128), 128, 0, stream>>>(n, K, rc2, pos, L.grid, L.cell_start, L.order, L.spos,
+            n, K, cutoff, rc2, pos, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
+        k_fill_capped<<<nblk(n, 128), 128, 0, stream>>>(n, K, cutoff, rc2, pos, L.grid, L.cell_start, L.order, L.spos,
                                                          nbr_start, nbr_len, nbr_idx);
     }
     return hipGetLastError();

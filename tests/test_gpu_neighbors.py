@@ -72,6 +72,9 @@ def test_edge_geometries(gpu_lib):
         "line": np.c_[np.zeros(300), np.zeros(300), rng.uniform(0, 90, 300)],
         "sparse_far": np.r_[rng.uniform(-5, 5, (200, 3)), rng.uniform(1e5, 1.00001e5, (50, 3))],
         "nonfinite": np.r_[rng.uniform(-6, 6, (300, 3)), [[np.nan, 0, 0], [np.inf, 1, 1], [0, -np.inf, 2]]],
+        # half-Angstrom lattice: many pairs exactly at the cutoff (excluded) and exact
+        # distance ties at the cap; atoms on cell boundaries
+        "half_lattice": np.stack(np.meshgrid(*(np.arange(12) * 0.5,) * 3, indexing="ij"), -1).reshape(-1, 3),
         # rows longer than a wave's LDS buffer (1024 candidates) take the per-thread path
         "dense_blob": np.r_[rng.uniform(-1, 1, (1300, 3)), rng.uniform(-20, 20, (400, 3))],
     }
