@@ -84,13 +84,16 @@ int64_t *neighbors_nnz_slot(void *ws, int n) { return nbr_layout(ws, n).nnz; }
 
 // ---------------------------------------------------------------- step 1
 // Bounding box in two stages: kBoxBlocks blocks reduce strided slices into
-// partial (min, max) records, one block combines them and sizes the grid.
+// partial (min, max) records (and clear the cell counters for step 2), one block
+// combines them and sizes the grid.
 constexpr int kBoxBlocks = 256;
 
-__global__ __launch_bounds__(256) void k_bbox_partial(const float *__restrict__ pos, int n, float *part)
+__global__ __launch_bounds__(256) void k_bbox_partial(const float *__restrict__ pos, int n, float *part, int maxc,
+                                                      int32_t *cell_cnt)
 {
     __shared__ float smin[3][256], smax[3][256];
     const int t = threadIdx.x;
+    for (long long c = (long long)blockIdx.x * 256 + t; c <= maxc; c += (long long)gridDim.x * 256) cell_cnt[c] = 0;
     float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
     for (long long i = (long long)blockIdx.x * 256 + t; i < n; i += (long long)gridDim.x * 256)
         for (int d = 0; d < 3; ++d) {
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256) void k_bbox_partial(const float *__restrict__ 
 }
 
 __global__ __launch_bounds__(256) void k_bbox(const float *__restrict__ part, int nparts, float cutoff, int maxc,
-                                              GridInfo *grid, int32_t *cell_cnt)
+                                              GridInfo *grid)
 {
     __shared__ float smin[3][256], smax[3][256];
     const int t = threadIdx.x;
@@ -132,8 +135,6 @@ __global__ __launch_bounds__(256) void k_bbox(const float *__restrict__ part, in
             }
         __syncthreads();
     }
-    // clear the cell counters for step 2
-    for (long long c = t; c <= maxc; c += 256) cell_cnt[c] = 0;
     if (t == 0) {
         const float cmin = 0.5f * cutoff * 1.001f;              // two cells per cutoff
         int dims[3];
@@ -217,35 +218,53 @@ __global__ void k_cell_assign(const float *__restrict__ pos, int n, const GridIn
 }
 
 // Exclusive scan of in[0..count) into out[0..count], out[count] = total; one block.
-// If total_out is non-null the total is also stored there as int64.
+// If total_out is non-null the total is also stored there as int64.  The input is
+// taken in tiles of 4096: each thread sums 4 consecutive entries, the wave scans
+// the sums with shuffles, the 16 wave totals meet in LDS, and a carry runs from
+// tile to tile; loads and stores stay coalesced.
 __global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, const int *count_dev, int count_arg,
                                                int32_t *out, int32_t *copy, int64_t *total_out)
 {
-    __shared__ long long part[1024];
-    const int t = threadIdx.x;
+    __shared__ long long wsum[16];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int count = count_dev ? *count_dev : count_arg;
-    const long long seg = ((long long)count + 1023) / 1024;
-    const long long b = t * seg, e = (b + seg < count) ? b + seg : count;
-    long long s = 0;
-    for (long long k = b; k < e; ++k) s += in[k];
-    part[t] = s;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const long long v = (t >= d) ? part[t - d] : 0;
+    long long carry = 0;
+    for (long long base = 0; base < count; base += 4096) {
+        const long long e0 = base + 4 * t;
+        int v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (e0 + k < count) ? in[e0 + k] : 0;
+        const long long sum = (long long)v[0] + v[1] + v[2] + v[3];
+        long long x = sum;                                  // inclusive scan over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const long long y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wsum[w] = x;
         __syncthreads();
-        part[t] += v;
-        __syncthreads();
+        long long before = 0, tile = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const long long ws = wsum[k];
+            before += k < w ? ws : 0;
+            tile += ws;
+        }
+        long long run = carry + before + x - sum;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (e0 + k < count) {
+                out[e0 + k] = (int32_t)run;
+                if (copy) copy[e0 + k] = (int32_t)run;
+            }
+            run += v[k];
+        }
+        carry += tile;
+        __syncthreads();                                    // wsum is rewritten by the next tile
     }
-    long long run = part[t] - s;
-    for (long long k = b; k < e; ++k) {
-        const int32_t v = in[k];
-        out[k] = (int32_t)run;
-        if (copy) copy[k] = (int32_t)run;
-        run += v;
-    }
-    if (t == 1023) {
-        out[count] = (int32_t)part[1023];
-        if (total_out) *total_out = part[1023];
+    if (t == 0) {
+        out[count] = (int32_t)carry;
+        if (total_out) *total_out = carry;
     }
 }
 
@@ -760,8 +779,8 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
     NbrLayout L = nbr_layout(ws, n);
     const int maxc = max_cells(n);
     const int nparts = (int)std::min<long long>(kBoxBlocks, ((long long)n + 255) / 256);
-    k_bbox_partial<<<nparts, 256, 0, stream>>>(pos, n, L.box_part);
-    k_bbox<<<1, 256, 0, stream>>>(L.box_part, nparts, cutoff, maxc, L.grid, L.cell_cnt);
+    k_bbox_partial<<<nparts, 256, 0, stream>>>(pos, n, L.box_part, maxc, L.cell_cnt);
+    k_bbox<<<1, 256, 0, stream>>>(L.box_part, nparts, cutoff, maxc, L.grid);
     k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt);
     k_scan<<<1, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, 0, L.cell_start, L.cell_cur, nullptr);
     k_scatter<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_cur, L.order, L.spos, order_out);
