@@ -389,6 +389,70 @@ __device__ __forceinline__ uint16_t f_to_bf16(float f)
 
 // ----------------------------------------------------------------------------
 // Launch helpers implemented in the .hip files (all enqueue on `stream`).
+// Ascending bitonic sort of a wave's 64 E int keys held in registers: the wave's 64 E
+// keys (key x = lane * E + k in register k of lane x / E) go through the
+// log2(64 E) merge phases; compare-exchange partners closer than E sit in the
+// same lane, farther ones in lane ^ (d / E), reached by one shuffle per key.
+template <int E>
+__device__ __forceinline__ void wave_bitonic_sort(int (&a)[E], int lane)
+{
+    constexpr int N = 64 * E;
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+        for (int d = size >> 1; d >= 1; d >>= 1) {
+            if (d >= E) {
+                const int lx = d / E;
+                // size > d >= E: the direction depends on the lane only
+                const bool asc = ((lane * E) & size) == 0;
+                const bool keep_min = ((lane & lx) == 0) == asc;
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const int o = __shfl_xor(a[k], lx, 64);
+                    a[k] = keep_min ? min(a[k], o) : max(a[k], o);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    if (k & d) continue;
+                    const bool asc = ((lane * E + k) & size) == 0;
+                    const int p = a[k], q = a[k | d];
+                    a[k] = asc ? min(p, q) : max(p, q);
+                    a[k | d] = asc ? max(p, q) : min(p, q);
+                }
+            }
+        }
+    }
+}
+
+// Ascending sort of a bitonic sequence of 64 E keys (same register layout as
+// wave_bitonic_sort): the last merge phase of the network alone.
+template <int E>
+__device__ __forceinline__ void wave_bitonic_merge(int (&a)[E], int lane)
+{
+    constexpr int N = 64 * E;
+#pragma unroll
+    for (int d = N >> 1; d >= 1; d >>= 1) {
+        if (d >= E) {
+            const int lx = d / E;
+            const bool keep_min = (lane & lx) == 0;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int o = __shfl_xor(a[k], lx, 64);
+                a[k] = keep_min ? min(a[k], o) : max(a[k], o);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                if (k & d) continue;
+                const int p = a[k], q = a[k | d];
+                a[k] = min(p, q);
+                a[k | d] = max(p, q);
+            }
+        }
+    }
+}
+
 struct NbrWork;   // neighbours.hip
 
 // y_format: 0 fp32, 1 bf16.  y_deq (optional) receives the stored values as

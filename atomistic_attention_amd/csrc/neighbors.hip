@@ -540,42 +540,7 @@ __device__ __forceinline__ int wave_scan(int i, float4 pi, float rc, double rc2,
     return count;
 }
 
-// Rows are ordered by j with a bitonic sort held in registers: the wave's 64 E
-// keys (key x = lane * E + k in register k of lane x / E) go through the
-// log2(64 E) merge phases; compare-exchange partners closer than E sit in the
-// same lane, farther ones in lane ^ (d / E), reached by one shuffle per key.
-template <int E>
-__device__ __forceinline__ void wave_bitonic_sort(int (&a)[E], int lane)
-{
-    constexpr int N = 64 * E;
-#pragma unroll
-    for (int size = 2; size <= N; size <<= 1) {
-#pragma unroll
-        for (int d = size >> 1; d >= 1; d >>= 1) {
-            if (d >= E) {
-                const int lx = d / E;
-                // size > d >= E: the direction depends on the lane only
-                const bool asc = ((lane * E) & size) == 0;
-                const bool keep_min = ((lane & lx) == 0) == asc;
-#pragma unroll
-                for (int k = 0; k < E; ++k) {
-                    const int o = __shfl_xor(a[k], lx, 64);
-                    a[k] = keep_min ? min(a[k], o) : max(a[k], o);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < E; ++k) {
-                    if (k & d) continue;
-                    const bool asc = ((lane * E + k) & size) == 0;
-                    const int p = a[k], q = a[k | d];
-                    a[k] = asc ? min(p, q) : max(p, q);
-                    a[k | d] = asc ? max(p, q) : min(p, q);
-                }
-            }
-        }
-    }
-}
-
+// Rows are ordered by j with wave_bitonic_sort (e2v2_internal.h).
 // row[0 .. cnt) = the cnt distinct keys of cj in increasing order.
 template <int E>
 __device__ __forceinline__ void wave_write_sorted_n(const int32_t *cj, int cnt, int32_t *row, int lane)

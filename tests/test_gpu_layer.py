@@ -119,7 +119,12 @@ def test_layer_deterministic(gpu_lib):
 @pytest.mark.parametrize("storage", ["fp32", "bf16"])
 def test_target_order_does_not_change_results(gpu_lib, storage):
     """Targets are independent: any processing order (natural, the neighbour
-    builder's cell order, a random permutation) gives bit-identical outputs."""
+    builder's cell order, a random permutation) gives the same outputs.  With fp32
+    storage (one target per wave) they are bit-identical.  With 16-bit storage two
+    consecutive targets share a wave and the chunks of their merged list, so the
+    order changes only the fp32 summation order: every order is deterministic and
+    the orders agree to 5e-4 of the output RMS (measured 5e-5 over 6.9 M values;
+    a wrong pairing would differ by O(1))."""
     base = W.make_workload("c4", n=6000)
     cfg = W.LayerConfig(**{**base.cfg.__dict__, "storage": storage})
     wl = W.make_workload(cfg)
@@ -131,9 +136,15 @@ def test_target_order_does_not_change_results(gpu_lib, storage):
     assert np.array_equal(np.sort(order.cpu().numpy()), np.arange(c.n))
     desc = _desc(gpu_lib, wl, d["dtype"])
     perm = torch.from_numpy(np.random.default_rng(3).permutation(c.n).astype(np.int32)).cuda()
-    outs = [gpu_lib.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, target_order=o).cpu()
-            for o in (None, order, perm)]
-    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    run = lambda o: gpu_lib.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, target_order=o).cpu()
+    outs = [run(o) for o in (None, order, perm)]
+    again = [run(o) for o in (None, order, perm)]
+    assert all(torch.equal(a, b) for a, b in zip(outs, again))
+    if storage == "fp32":
+        assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    else:
+        assert rel_err(outs[1].numpy(), outs[0].numpy()) < 5e-4
+        assert rel_err(outs[2].numpy(), outs[0].numpy()) < 5e-4
 
 
 def _sampled_check(gpu_lib, wl, rows, nsample, seed):
