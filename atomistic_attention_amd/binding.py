@@ -19,7 +19,8 @@ E2V2_FP32, E2V2_BF16 = 0, 1
 
 EXPORTS = [
     "e2v2_build_neighbors", "e2v2_build_neighbors_workspace_bytes", "e2v2_eaas_couple",
-    "e2v2_attn_forward", "e2v2_attn_forward_taps", "e2v2_attn_workspace_bytes", "e2v2_num_paths",
+    "e2v2_attn_forward", "e2v2_attn_forward_taps", "e2v2_attn_prepare", "e2v2_attn_aggregate",
+    "e2v2_attn_workspace_bytes", "e2v2_num_paths",
     "e2v2_path_table", "e2v2_eaas_coefficients", "e2v2_alignment_wigner", "e2v2_status_string",
     "e2v2_last_error",
 ]
@@ -72,6 +73,11 @@ def load(path: str = LIB_PATH):
     lib.e2v2_attn_forward_taps.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp,
                                            vp, i32, vp, vp, sz, ctypes.POINTER(Taps), vp]
     lib.e2v2_attn_forward_taps.restype = ctypes.c_int
+    lib.e2v2_attn_prepare.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), i32, vp, sz, vp]
+    lib.e2v2_attn_prepare.restype = ctypes.c_int
+    lib.e2v2_attn_aggregate.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(Weights), vp, vp, vp, vp, i32, vp,
+                                        vp, sz, vp]
+    lib.e2v2_attn_aggregate.restype = ctypes.c_int
     lib.e2v2_attn_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32]
     lib.e2v2_attn_workspace_bytes.restype = sz
     lib.e2v2_num_paths.argtypes = [i32]
@@ -259,4 +265,38 @@ def e2v2_attn_forward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len
                                         _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), n, _ptr(out),
                                         _ptr(workspace), workspace.numel(), ctypes.byref(tp), _stream(stream))
     _check(st)
+    return out
+
+
+def _weights(weights: dict, sdt) -> Weights:
+    for name in ("w_q", "w_k", "w_v", "w_o"):
+        _dev(weights[name], sdt, name)
+    for name in ("w_rbf", "w_src", "w_tgt"):
+        _dev(weights[name], torch.float32, name)
+    return Weights(*(_ptr(weights[k]) for k in ("w_q", "w_k", "w_v", "w_o", "w_rbf", "w_src", "w_tgt")))
+
+
+def e2v2_attn_prepare(desc: LayerDesc, pos, h, weights: dict, workspace: torch.Tensor, stream=None):
+    """Steps 2-3 of the layer into `workspace` (no neighbour list needed)."""
+    lib = load()
+    _dev(pos, torch.float32, "pos")
+    _dev(h, h.dtype, "h")
+    w = _weights(weights, h.dtype)
+    _check(lib.e2v2_attn_prepare(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), pos.shape[0],
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def e2v2_attn_aggregate(desc: LayerDesc, weights: dict, nbr_start, nbr_len, nbr_idx, out: torch.Tensor,
+                        workspace: torch.Tensor, stream=None, target_order: torch.Tensor | None = None):
+    """Steps 4-6 of the layer on a workspace that e2v2_attn_prepare filled; writes out."""
+    lib = load()
+    for t, nm in ((nbr_start, "nbr_start"), (nbr_len, "nbr_len"), (nbr_idx, "nbr_idx")):
+        _dev(t, torch.int32, nm)
+    if target_order is not None:
+        _dev(target_order, torch.int32, "target_order")
+    _dev(out, torch.float32, "out")
+    w = _weights(weights, weights["w_q"].dtype)
+    _check(lib.e2v2_attn_aggregate(ctypes.byref(desc), ctypes.byref(w), _ptr(nbr_start), _ptr(nbr_len),
+                                   _ptr(nbr_idx), _ptr(target_order), nbr_start.shape[0], _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

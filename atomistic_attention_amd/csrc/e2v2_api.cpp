@@ -431,22 +431,32 @@ size_t e2v2_attn_workspace_bytes(const e2v2_layer_desc *desc, int32_t n)
     return attn_ws(*desc, n).total;
 }
 
-e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos, const void *h,
-                                   const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
-                                   const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
-                                   void *workspace, size_t workspace_bytes, const e2v2_taps *taps,
-                                   hipStream_t stream)
+}  // extern "C"
+
+namespace {
+// The layer forward in two parts that share the workspace: `prep` runs steps 2-3
+// (weight packing, projections, source coupling; no neighbour list needed) and
+// `agg` runs steps 4-6 (streaming attention, target coupling, output
+// projection) on what `prep` left in the workspace.
+e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,
+                     const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
+                     const int32_t *target_order, int32_t n, float *out, void *workspace, size_t workspace_bytes,
+                     const e2v2_taps *taps, hipStream_t stream, bool prep, bool agg)
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
     if (n < 0) return fail(E2V2_ERR_ARG, "n < 0");
     if (n == 0) return E2V2_OK;
     if (!w) return fail(E2V2_ERR_ARG, "weights is NULL");
-    const void *dev[] = {pos, h, w->w_q, w->w_k, w->w_v, w->w_o, w->w_rbf, w->w_src, w->w_tgt,
-                         nbr_start, nbr_len, nbr_idx, out, workspace};
-    for (const void *p : dev) {
-        if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
-        if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    const void *dev_prep[] = {pos, h, w->w_q, w->w_k, w->w_v, w->w_o, w->w_src, workspace};
+    const void *dev_agg[] = {w->w_o, w->w_rbf, w->w_tgt, nbr_start, nbr_len, nbr_idx, out, workspace};
+    for (int part = 0; part < 2; ++part) {
+        if (part == 0 && !prep) continue;
+        if (part == 1 && !agg) continue;
+        for (const void *p : (part == 0 ? dev_prep : dev_agg)) {
+            if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
+            if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+        }
     }
     if (target_order && !aligned16(target_order)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
     if (taps)
@@ -469,104 +479,137 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
 
     hipEvent_t *ev = taps ? taps->events : nullptr;
     auto mark = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], stream) : hipSuccess; };
-    hipError_t e = mark(0);
-    if (e != hipSuccess) return hip_fail(e, "recording stage event");
-    // Step 2: projections (q, k from the l = 0 block; v per component with W_V[l]).
+    hipError_t e = hipSuccess;
+    // fp32 weights of degree l (fp32 storage)
+    auto wv32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_v) + l * wstride); };
+    auto wo32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_o) + l * wstride); };
     ProjJob jobs[kMaxL * kMaxL + 2 * kMaxL + 1 + 2];
     int nj = 0;
     uint16_t *wp = reinterpret_cast<uint16_t *>(ws + L.wpack);
     const size_t wsz = (size_t)C * C;                 // elements per packed matrix
-    // fp32 weights of degree l (fp32 storage)
-    auto wv32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_v) + l * wstride); };
-    auto wo32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_o) + l * wstride); };
-    if (bf) {
-        const uint16_t *src[2 * kMaxL + 4];
-        uint16_t *dst[2 * kMaxL + 4];
-        int cnt = 0;
-        for (int l = 0; l <= lmax; ++l) { src[cnt] = reinterpret_cast<const uint16_t *>(w->w_v) + l * wsz; dst[cnt] = wp + cnt * wsz; ++cnt; }
-        src[cnt] = reinterpret_cast<const uint16_t *>(w->w_q); dst[cnt] = wp + cnt * wsz; ++cnt;
-        src[cnt] = reinterpret_cast<const uint16_t *>(w->w_k); dst[cnt] = wp + cnt * wsz; ++cnt;
-        for (int l = 0; l <= lmax; ++l) { src[cnt] = reinterpret_cast<const uint16_t *>(w->w_o) + l * wsz; dst[cnt] = wp + cnt * wsz; ++cnt; }
-        e = launch_pack_weights(src, dst, cnt, C, stream);
-        if (e != hipSuccess) return hip_fail(e, "weight packing kernel");
+    if (prep) {
+        e = mark(0);
+        if (e != hipSuccess) return hip_fail(e, "recording stage event");
+        // Step 2: projections (q, k from the l = 0 block; v per component with W_V[l]).
+        if (bf) {
+            const uint16_t *src[2 * kMaxL + 4];
+            uint16_t *dst[2 * kMaxL + 4];
+            int cnt = 0;
+            for (int l = 0; l <= lmax; ++l) { src[cnt] = reinterpret_cast<const uint16_t *>(w->w_v) + l * wsz; dst[cnt] = wp + cnt * wsz; ++cnt; }
+            src[cnt] = reinterpret_cast<const uint16_t *>(w->w_q); dst[cnt] = wp + cnt * wsz; ++cnt;
+            src[cnt] = reinterpret_cast<const uint16_t *>(w->w_k); dst[cnt] = wp + cnt * wsz; ++cnt;
+            for (int l = 0; l <= lmax; ++l) { src[cnt] = reinterpret_cast<const uint16_t *>(w->w_o) + l * wsz; dst[cnt] = wp + cnt * wsz; ++cnt; }
+            e = launch_pack_weights(src, dst, cnt, C, stream);
+            if (e != hipSuccess) return hip_fail(e, "weight packing kernel");
+        }
+        if (bf) {
+            // Steps 2-3 fused: q, k, v on bf16 MFMA with the source EAAS applied to v in
+            // registers (v itself is never stored unless tapped).
+            QkvEaasArgs qa{};
+            qa.h = reinterpret_cast<const uint16_t *>(h);
+            qa.wv = reinterpret_cast<const uint4 *>(wp);
+            qa.wq = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 1) * wsz);
+            qa.wk = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 2) * wsz);
+            qa.w_src = w->w_src; qa.pos = pos;
+            qa.q = q; qa.kt = reinterpret_cast<uint16_t *>(k); qa.hp = reinterpret_cast<uint16_t *>(hp);
+            qa.pos4 = pos4; qa.dmat = dmat;
+            qa.k_tap = taps ? taps->k : nullptr;
+            qa.v_tap = taps ? taps->v : nullptr;
+            qa.hp_tap = taps ? taps->hprime : nullptr;
+            qa.n = n;
+            e = launch_qkv_eaas(lmax, qa, C, stream);
+            if (e == hipSuccess) e = mark(1);
+            if (e == hipSuccess) e = mark(2);
+            if (e != hipSuccess) return hip_fail(e, "projection + source EAAS kernel");
+        } else {
+            const float *h32 = reinterpret_cast<const float *>(h);
+            for (int l = 0; l <= lmax; ++l)
+                for (int m = 0; m < 2 * l + 1; ++m)
+                    jobs[nj++] = ProjJob{h32, (long long)NC * C, wv32(l), v, (long long)NC * C, l * l + m};
+            jobs[nj++] = ProjJob{h32, (long long)NC * C, reinterpret_cast<const float *>(w->w_q), q, (long long)C, 0};
+            jobs[nj++] = ProjJob{h32, (long long)NC * C, reinterpret_cast<const float *>(w->w_k), k, (long long)C, 0};
+            e = launch_proj(jobs, nj, n, C, stream);
+            if (e == hipSuccess) e = mark(1);
+            if (e != hipSuccess) return hip_fail(e, "projection kernel");
+            // Step 3: source coupling h' (EAAS), per-node D blocks and padded positions.
+            e = launch_eaas(lmax, pos, v, 0, w->w_src, n, C, hp, 0, taps ? taps->hprime : nullptr, dmat, pos4, stream);
+            if (e == hipSuccess) e = mark(2);
+            if (e != hipSuccess) return hip_fail(e, "source EAAS kernel");
+        }
     }
-    if (bf) {
-        // Steps 2-3 fused: q, k, v on bf16 MFMA with the source EAAS applied to v in
-        // registers (v itself is never stored unless tapped).
-        QkvEaasArgs qa{};
-        qa.h = reinterpret_cast<const uint16_t *>(h);
-        qa.wv = reinterpret_cast<const uint4 *>(wp);
-        qa.wq = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 1) * wsz);
-        qa.wk = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 2) * wsz);
-        qa.w_src = w->w_src; qa.pos = pos;
-        qa.q = q; qa.kt = reinterpret_cast<uint16_t *>(k); qa.hp = reinterpret_cast<uint16_t *>(hp);
-        qa.pos4 = pos4; qa.dmat = dmat;
-        qa.k_tap = taps ? taps->k : nullptr;
-        qa.v_tap = taps ? taps->v : nullptr;
-        qa.hp_tap = taps ? taps->hprime : nullptr;
-        qa.n = n;
-        e = launch_qkv_eaas(lmax, qa, C, stream);
-        if (e == hipSuccess) e = mark(1);
-        if (e == hipSuccess) e = mark(2);
-        if (e != hipSuccess) return hip_fail(e, "projection + source EAAS kernel");
-    } else {
-        const float *h32 = reinterpret_cast<const float *>(h);
-        for (int l = 0; l <= lmax; ++l)
-            for (int m = 0; m < 2 * l + 1; ++m)
-                jobs[nj++] = ProjJob{h32, (long long)NC * C, wv32(l), v, (long long)NC * C, l * l + m};
-        jobs[nj++] = ProjJob{h32, (long long)NC * C, reinterpret_cast<const float *>(w->w_q), q, (long long)C, 0};
-        jobs[nj++] = ProjJob{h32, (long long)NC * C, reinterpret_cast<const float *>(w->w_k), k, (long long)C, 0};
-        e = launch_proj(jobs, nj, n, C, stream);
-        if (e == hipSuccess) e = mark(1);
-        if (e != hipSuccess) return hip_fail(e, "projection kernel");
-        // Step 3: source coupling h' (EAAS), per-node D blocks and padded positions.
-        e = launch_eaas(lmax, pos, v, 0, w->w_src, n, C, hp, 0, taps ? taps->hprime : nullptr, dmat, pos4, stream);
-        if (e == hipSuccess) e = mark(2);
-        if (e != hipSuccess) return hip_fail(e, "source EAAS kernel");
-    }
-    // Steps 4-5: streaming attention + target coupling (fp32 storage); for bf16
-    // storage the streaming kernel stops at the normalised message m_i.
-    AttnArgs a{};
-    a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dmat = dmat;
-    a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
-    a.w_rbf = w->w_rbf; a.w_tgt = w->w_tgt; a.hhat = hhat;
-    a.m_tap = taps ? taps->m : nullptr;
-    a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
-    e = launch_attn(lmax, bf, a, stream);
-    if (e == hipSuccess) e = mark(3);
-    if (e != hipSuccess) return hip_fail(e, "attention kernel");
-    // Step 6: output projection.
-    if (bf) {
-        // Step 5 (target coupling) + step 6 on whole nodes: the streaming kernel
-        // left the normalised message m in the hhat buffer.
-        EaasOutArgs oa{};
-        oa.m = hhat; oa.dmat = dmat; oa.pos4 = pos4; oa.w_tgt = w->w_tgt;
-        oa.wo = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 3) * wsz);
-        oa.out = out;
-        oa.hhat_tap = taps ? taps->hhat : nullptr;
-        oa.n = n;
-        e = launch_eaas_outproj(lmax, oa, C, stream);
-    } else {
-        nj = 0;
-        for (int l = 0; l <= lmax; ++l)
-            for (int m = 0; m < 2 * l + 1; ++m)
-                jobs[nj++] = ProjJob{hhat, (long long)NC * C, wo32(l), out, (long long)NC * C, l * l + m};
-        e = launch_proj(jobs, nj, n, C, stream);
-    }
-    if (e == hipSuccess) e = mark(4);
-    if (e != hipSuccess) return hip_fail(e, "output projection kernel");
-    if (taps) {
-        const size_t N = (size_t)n;
-        struct { void *dst; const void *src; size_t bytes; } cp[] = {
-            {taps->q, q, N * C * 4}, {bf ? nullptr : taps->k, k, N * C * 4}, {bf ? nullptr : taps->v, v, N * NC * C * 4},
-            {bf ? nullptr : taps->hhat, hhat, N * NC * C * 4}};
-        for (auto &c : cp)
-            if (c.dst) {
-                e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, stream);
-                if (e != hipSuccess) return hip_fail(e, "copying taps");
-            }
+    if (agg) {
+        // Steps 4-5: streaming attention + target coupling (fp32 storage); for bf16
+        // storage the streaming kernel stops at the normalised message m_i.
+        AttnArgs a{};
+        a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dmat = dmat;
+        a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
+        a.w_rbf = w->w_rbf; a.w_tgt = w->w_tgt; a.hhat = hhat;
+        a.m_tap = taps ? taps->m : nullptr;
+        a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
+        e = launch_attn(lmax, bf, a, stream);
+        if (e == hipSuccess) e = mark(3);
+        if (e != hipSuccess) return hip_fail(e, "attention kernel");
+        // Step 6: output projection.
+        if (bf) {
+            // Step 5 (target coupling) + step 6 on whole nodes: the streaming kernel
+            // left the normalised message m in the hhat buffer.
+            EaasOutArgs oa{};
+            oa.m = hhat; oa.dmat = dmat; oa.pos4 = pos4; oa.w_tgt = w->w_tgt;
+            oa.wo = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 3) * wsz);
+            oa.out = out;
+            oa.hhat_tap = taps ? taps->hhat : nullptr;
+            oa.n = n;
+            e = launch_eaas_outproj(lmax, oa, C, stream);
+        } else {
+            nj = 0;
+            for (int l = 0; l <= lmax; ++l)
+                for (int m = 0; m < 2 * l + 1; ++m)
+                    jobs[nj++] = ProjJob{hhat, (long long)NC * C, wo32(l), out, (long long)NC * C, l * l + m};
+            e = launch_proj(jobs, nj, n, C, stream);
+        }
+        if (e == hipSuccess) e = mark(4);
+        if (e != hipSuccess) return hip_fail(e, "output projection kernel");
+        if (taps) {
+            const size_t N = (size_t)n;
+            struct { void *dst; const void *src; size_t bytes; } cp[] = {
+                {taps->q, q, N * C * 4}, {bf ? nullptr : taps->k, k, N * C * 4}, {bf ? nullptr : taps->v, v, N * NC * C * 4},
+                {bf ? nullptr : taps->hhat, hhat, N * NC * C * 4}};
+            for (auto &c : cp)
+                if (c.dst) {
+                    e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, stream);
+                    if (e != hipSuccess) return hip_fail(e, "copying taps");
+                }
+        }
     }
     return E2V2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos, const void *h,
+                                   const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
+                                   const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
+                                   void *workspace, size_t workspace_bytes, const e2v2_taps *taps,
+                                   hipStream_t stream)
+{
+    return attn_run(desc, pos, h, w, nbr_start, nbr_len, nbr_idx, target_order, n, out, workspace, workspace_bytes,
+                    taps, stream, true, true);
+}
+
+e2v2_status e2v2_attn_prepare(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,
+                              int32_t n, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return attn_run(desc, pos, h, w, nullptr, nullptr, nullptr, nullptr, n, nullptr, workspace, workspace_bytes,
+                    nullptr, stream, true, false);
+}
+
+e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights *w, const int32_t *nbr_start,
+                                const int32_t *nbr_len, const int32_t *nbr_idx, const int32_t *target_order,
+                                int32_t n, float *out, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return attn_run(desc, nullptr, nullptr, w, nbr_start, nbr_len, nbr_idx, target_order, n, out, workspace,
+                    workspace_bytes, nullptr, stream, false, true);
 }
 
 e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,

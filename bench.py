@@ -167,11 +167,28 @@ def main():
     torch.cuda.synchronize()
 
     def step(ev=None):
+        """One step in stage order on one stream (events mark the stage boundaries)."""
         if ev is not None:
             ev[0].record(stream)
         build()
         B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], start, length, idx, out=out, workspace=aws,
                             taps={"events": ev[1:]} if ev is not None else None, target_order=order)
+
+    # The timed step: the projections and source coupling need no neighbour list,
+    # so they run on a second stream while the list is built, and the streaming
+    # attention + output stage joins both.  The fork waits for the previous step,
+    # whose attention still reads the workspace.
+    side = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    def step_overlapped():
+        fork.record(stream)
+        side.wait_event(fork)
+        B.e2v2_attn_prepare(desc, d["pos"], d["h"], d["weights"], aws, stream=side)
+        join.record(side)
+        build()
+        stream.wait_event(join)
+        B.e2v2_attn_aggregate(desc, d["weights"], start, length, idx, out, aws, stream=stream, target_order=order)
 
     if args.traffic_probe:
         for _ in range(5):
@@ -187,17 +204,23 @@ def main():
         return
 
     for _ in range(args.warmup):
-        step()
+        step_overlapped()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step_overlapped()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
 
+    # Stage times (and the streaming kernel's launch time for the roofline) from the
+    # same number of steps run in stage order on one stream, outside the timed region.
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
     stages = np.array([[events[k][a].elapsed_time(events[k][a + 1]) for a in range(5)] for k in range(args.steps)])
     mean = stages.mean(axis=0)          # ms per stage between consecutive events
-    ms_step = wall * 1e3 / args.steps
+    serial_ms = float(stages.sum(axis=1).mean())
     nnz = int(length.sum().item())
     ab = algorithmic_bytes(cfg, nnz)
     t_attn = mean[3] * 1e-3
@@ -247,6 +270,8 @@ def main():
             "nnz": nnz,
             "steps_per_s": 1e3 / ms_step,
             "stage_ms": stage_ms,
+            "stages_in_order_ms_per_step": serial_ms,
+            "overlap": "projections + source coupling on a second stream during the neighbour build",
             "layer_ms_excl_neighbours": layer_ms,
             "layer_pairs_per_s_excl_neighbours": nnz / (layer_ms * 1e-3),
             "layer_hbm_frac_excl_neighbours": layer_bytes / (layer_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),

@@ -189,6 +189,27 @@ e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos
                                    hipStream_t stream);
 size_t e2v2_attn_workspace_bytes(const e2v2_layer_desc *desc, int32_t n);
 
+/* The same forward in two calls that share the workspace, so that the part that
+ * needs no neighbour list can overlap e2v2_build_neighbors on another stream.
+ * e2v2_attn_prepare runs steps 2-3 (projections q, k, v; source pre-coupling of
+ * v by EAAS: E2Former-V2 explainer sections 2.3 and 3.1) and leaves q, k, h', the
+ * per-node frames and the packed weights in the workspace.  e2v2_attn_aggregate
+ * runs steps 4-6 (streaming attention, target coupling, output projection:
+ * sections 3.1-3.2) on that workspace and writes out.  Arguments mean what they
+ * mean for e2v2_attn_forward.  The two calls must use the same desc, weights, n
+ * and workspace; aggregate must be ordered after prepare (same stream, or an
+ * event), and a prepare must not start while an earlier aggregate on the same
+ * workspace still runs.  The result equals e2v2_attn_forward's bit for bit.
+ * Errors as for e2v2_attn_forward; prepare checks pos, h and the projection
+ * and source weights, aggregate the neighbour list, out, w_o, w_rbf, w_tgt. */
+e2v2_status e2v2_attn_prepare(const e2v2_layer_desc *desc, const float *pos, const void *h,
+                              const e2v2_weights *w, int32_t n, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights *w, const int32_t *nbr_start,
+                                const int32_t *nbr_len, const int32_t *nbr_idx, const int32_t *target_order,
+                                int32_t n, float *out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Host-side tables (no GPU needed). */
 int32_t e2v2_num_paths(int32_t lmax);   /* 1, 5, 15, 34 for lmax 0..3; -1 if out of range */

@@ -174,3 +174,32 @@ def test_very_long_neighbour_lists(gpu_lib):
     rows = O.neighbors(wl.pos, wl.cfg.cutoff)
     assert np.mean([r.size for r in rows]) > 1000
     _sampled_check(gpu_lib, wl, rows, 24, 2)
+
+
+@pytest.mark.parametrize("storage", ["fp32", "bf16"])
+def test_split_forward_on_two_streams(gpu_lib, storage):
+    """e2v2_attn_prepare on a second stream, overlapping the neighbour build, then
+    e2v2_attn_aggregate after an event: the same output as e2v2_attn_forward, bit
+    for bit, on two calls in a row."""
+    base = W.make_workload("c4", n=5000)
+    wl = W.make_workload(W.LayerConfig(**{**base.cfg.__dict__, "storage": storage}))
+    c = wl.cfg
+    d = upload(wl)
+    desc = _desc(gpu_lib, wl, d["dtype"])
+    s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors)
+    ref = gpu_lib.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix)
+    ws = torch.empty(gpu_lib.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(ref)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    for _ in range(2):
+        out.zero_()
+        fork.record(main)
+        side.wait_event(fork)
+        gpu_lib.e2v2_attn_prepare(desc, d["pos"], d["h"], d["weights"], ws, stream=side)
+        join.record(side)
+        s2, ln2, ix2, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors)
+        main.wait_event(join)
+        gpu_lib.e2v2_attn_aggregate(desc, d["weights"], s2, ln2, ix2, out, ws, stream=main)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)

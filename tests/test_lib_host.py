@@ -97,6 +97,31 @@ def test_attn_argument_errors(lib):
     assert _attn(lib, _desc(), n=0) == B.E2V2_OK                       # nothing to do
 
 
+def test_split_forward_argument_errors(lib):
+    """The two halves check what they use; argument errors enqueue nothing."""
+    d = _desc()
+    wsb = lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 10)
+    full = B.Weights(*([FAKE] * 7))
+    prep = lambda desc=d, n=10, pos=FAKE, h=FAKE, w=full, ws=FAKE, b=wsb: lib.e2v2_attn_prepare(
+        ctypes.byref(desc) if desc is not None else None, pos, h, ctypes.byref(w), n, ws, b, None)
+    agg = lambda desc=d, n=10, nbr=FAKE, out=FAKE, w=full, ws=FAKE, b=wsb: lib.e2v2_attn_aggregate(
+        ctypes.byref(desc) if desc is not None else None, ctypes.byref(w), nbr, nbr, nbr, None, n, out, ws, b, None)
+    for call in (prep, agg):
+        assert call(desc=None) == B.E2V2_ERR_ARG
+        assert call(desc=_desc(lmax=4)) == B.E2V2_ERR_ARG
+        assert call(n=-1) == B.E2V2_ERR_ARG
+        assert call(ws=None) == B.E2V2_ERR_ARG
+        assert call(b=100) == B.E2V2_ERR_ARG
+        assert call(n=0) == B.E2V2_OK
+    assert prep(pos=None) == B.E2V2_ERR_ARG and prep(h=FAKE_MIS) == B.E2V2_ERR_ARG
+    assert agg(nbr=None) == B.E2V2_ERR_ARG and agg(out=FAKE_MIS) == B.E2V2_ERR_ARG
+    # prepare does not need the attention weights, aggregate does not need the projection ones
+    no_rbf = B.Weights(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE)
+    no_q = B.Weights(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert agg(w=no_rbf) == B.E2V2_ERR_ARG
+    assert prep(w=no_q) == B.E2V2_ERR_ARG
+
+
 def test_workspace_sizes(lib):
     d = _desc()
     a, b = lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 1000), lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 2000)
