@@ -300,20 +300,9 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
     const float invz = z > 0.f ? 1.f / z : 0.f;
 
     if constexpr (HB) {
-        // 16-bit storage: store the normalised message m_i; the target coupling runs
-        // in the output-projection kernel, on whole nodes.
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int ch = cb + off + c;
-            if (writer) {
-#pragma unroll
-                for (int e = 0; e < NC; ++e) {
-                    const float mv = acc[e][c] * invz;
-                    A.hhat[((size_t)i * NC + e) * C + ch] = mv;
-                    if (A.m_tap) A.m_tap[((size_t)i * NC + e) * C + ch] = mv;
-                }
-            }
-        }
+        // 16-bit storage: store the normalised message m_i (fp16 under a node scale);
+        // the target coupling runs in the output-projection kernel, on whole nodes.
+        store_message_f16<NC, NCH>(A, i, C, z, acc, cb + off, writer, lane);
         return;
     }
     // ---- target coupling (EAAS with the target's own rotation) and store

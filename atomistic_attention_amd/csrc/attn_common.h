@@ -65,6 +65,51 @@ __device__ __forceinline__ float pick4(const floatx4 &v, int r)
     return r == 0 ? v[0] : r == 1 ? v[1] : r == 2 ? v[2] : v[3];
 }
 
+// Stores one target's normalised message m_i after the slot merge (16-bit
+// storage): lane holds channels cb + off + c, c < NCH, of every component in
+// acc (not yet divided by z).  m_i is written in fp16 under one power-of-two
+// scale per node -- the largest |m_i| M below 2^14 s, the rule the source
+// features use -- and s goes to A.msc[i]; the tap receives the stored values.
+template <int NC, int NCH>
+__device__ __forceinline__ void store_message_f16(const AttnArgs &A, int i, int C, float z, const float (&acc)[NC][4],
+                                                  int ch0, bool writer, int lane)
+{
+    const float invz = z > 0.f ? 1.f / z : 0.f;
+    unsigned mb = 0u;
+#pragma unroll
+    for (int e = 0; e < NC; ++e)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) mb = max(mb, __float_as_uint(acc[e][c] * invz) & 0x7fffffffu);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mb = max(mb, (unsigned)__shfl_xor((int)mb, d, 64));
+    unsigned sb = 127u;                                  // scale 1 for zero or non-finite rows
+    if (mb != 0u && mb < 0x7f800000u) {
+        const unsigned b = mb >> 23;
+        sb = b > 13u ? b - 13u : 1u;
+    }
+    const float sc = __uint_as_float(sb << 23), inv = __uint_as_float((254u - sb) << 23);
+    if (lane == 0) A.msc[i] = sc;
+    if (!writer) return;
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+        const size_t o = ((size_t)i * NC + e) * C + ch0;
+        _Float16 hv[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) hv[c] = (_Float16)(acc[e][c] * invz * inv);
+        if constexpr (NCH == 2) {
+            *reinterpret_cast<uint32_t *>(A.mh + o) =
+                uint32_t(__builtin_bit_cast(uint16_t, hv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, hv[1])) << 16);
+        } else {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) A.mh[o + c] = __builtin_bit_cast(uint16_t, hv[c]);
+        }
+        if (A.m_tap) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) A.m_tap[o + c] = (float)hv[c] * sc;
+        }
+    }
+}
+
 // Two targets per wave over the union of their lists (attn_pair.hip): 16-bit
 // storage, l_max <= 2, n < attn_pair_max_atoms().
 hipError_t launch_attn_pair(int L, const AttnArgs &a, hipStream_t stream);

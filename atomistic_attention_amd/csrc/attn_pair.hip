@@ -470,24 +470,10 @@ void attn_pair_kernel(const AttnArgs A)
     for (int st = 0; st < NB && st < 2; ++st) off += ((u >> (NB - 1 - st)) & 1) ? (2 >> st) : 0;
     constexpr int NCH = (NB >= 2) ? 1 : (4 >> NB);
     const bool writer = (NB <= 2) || ((u & 1) == 0);
-    auto store = [&](int i, float z, const float (&acc)[NC][4]) {
-        const float invz = z > 0.f ? 1.f / z : 0.f;
-        if (!writer) return;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int ch = cb + off + c;
-#pragma unroll
-            for (int e = 0; e < NC; ++e) {
-                const float mv = acc[e][c] * invz;
-                A.hhat[((size_t)i * NC + e) * C + ch] = mv;
-                if (A.m_tap) A.m_tap[((size_t)i * NC + e) * C + ch] = mv;
-            }
-        }
-    };
     merge(mua, za, acca);
     merge(mub, zb, accb);
-    if (va) store(ia, za, acca);
-    if (vb) store(ib, zb, accb);
+    if (va) store_message_f16<NC, NCH>(A, ia, C, za, acca, cb + off, writer, lane);
+    if (vb) store_message_f16<NC, NCH>(A, ib, C, zb, accb, cb + off, writer, lane);
 }
 
 template <int L>

@@ -249,7 +249,7 @@ size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Attention workspace layout.
 struct AttnWs {
-    size_t q, k, v, hp, dmat, pos4, hhat, wpack, total;
+    size_t q, k, v, hp, dmat, pos4, hhat, msc, wpack, total;
 };
 AttnWs attn_ws(const e2v2_layer_desc &d, int n)
 {
@@ -264,7 +264,9 @@ AttnWs attn_ws(const e2v2_layer_desc &d, int n)
     w.hp = o; o += al256(d.storage == E2V2_BF16 ? N * hp_pair_row((int)NC, (int)C) * 2 : N * NC * C * s);
     w.dmat = o; o += al256(N * nd * 4);
     w.pos4 = o; o += al256(N * 16);
-    w.hhat = o; o += al256(N * NC * C * 4);
+    // fp32 storage: hhat; 16-bit storage: the message m in fp16 and its node scales
+    w.hhat = o; o += al256(N * NC * C * (d.storage == E2V2_BF16 ? 2 : 4));
+    w.msc = o; o += al256(d.storage == E2V2_BF16 ? N * 4 : 0);
     // bf16 weights packed into MFMA fragments: W_V[0..L], W_Q, W_K, W_O[0..L]
     w.wpack = o; o += al256(d.storage == E2V2_BF16 ? (size_t)(2 * (d.lmax + 1) + 2) * C * C * 2 : 0);
     w.total = o + 256;   // slack for re-aligning an unaligned base
@@ -476,6 +478,8 @@ e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *
     float *dmat = reinterpret_cast<float *>(ws + L.dmat);
     float4 *pos4 = reinterpret_cast<float4 *>(ws + L.pos4);
     float *hhat = reinterpret_cast<float *>(ws + L.hhat);
+    uint16_t *mh = reinterpret_cast<uint16_t *>(ws + L.hhat);    // 16-bit storage: the fp16 message
+    float *msc = reinterpret_cast<float *>(ws + L.msc);
 
     hipEvent_t *ev = taps ? taps->events : nullptr;
     auto mark = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], stream) : hipSuccess; };
@@ -543,7 +547,7 @@ e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *
         AttnArgs a{};
         a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dmat = dmat;
         a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
-        a.w_rbf = w->w_rbf; a.w_tgt = w->w_tgt; a.hhat = hhat;
+        a.w_rbf = w->w_rbf; a.w_tgt = w->w_tgt; a.hhat = hhat; a.mh = mh; a.msc = msc;
         a.m_tap = taps ? taps->m : nullptr;
         a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
         e = launch_attn(lmax, bf, a, stream);
@@ -552,9 +556,9 @@ e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *
         // Step 6: output projection.
         if (bf) {
             // Step 5 (target coupling) + step 6 on whole nodes: the streaming kernel
-            // left the normalised message m in the hhat buffer.
+            // left the normalised message m (fp16, node scales in msc) in the hhat buffer.
             EaasOutArgs oa{};
-            oa.m = hhat; oa.dmat = dmat; oa.pos4 = pos4; oa.w_tgt = w->w_tgt;
+            oa.m = mh; oa.msc = msc; oa.dmat = dmat; oa.pos4 = pos4; oa.w_tgt = w->w_tgt;
             oa.wo = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 3) * wsz);
             oa.out = out;
             oa.hhat_tap = taps ? taps->hhat : nullptr;

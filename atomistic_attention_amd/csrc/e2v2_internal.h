@@ -498,7 +498,9 @@ hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t strea
 // normalised message), dmat [n][n_dmat(L)], pos4 [n] (x, y, z, .), w_tgt [P][C],
 // wo = packed W_O[0..L]; out fp32 [n][NC][C]; hhat_tap optional fp32 [n][NC][C].
 struct EaasOutArgs {
-    const float *m, *dmat;
+    const uint16_t *m;               // [n][NC][C] fp16 message m_i / msc[i]
+    const float *msc;                // [n] power-of-two scale of m_i
+    const float *dmat;
     const float4 *pos4;
     const float *w_tgt;
     const uint4 *wo;
@@ -517,7 +519,9 @@ struct AttnArgs {
     const int32_t *order;            // optional processing order of the targets
     const float *w_rbf;              // [R][H]
     const float *w_tgt;              // [P][C]
-    float *hhat;                     // [n][NC][C] fp32: hhat (fp32 h'), or the message m (16-bit h')
+    float *hhat;                     // [n][NC][C] fp32 hhat (fp32 storage)
+    uint16_t *mh;                    // [n][NC][C] fp16 message m_i / msc[i] (16-bit storage)
+    float *msc;                      // [n] power-of-two scale of m_i (16-bit storage)
     float *m_tap;                    // optional [n][NC][C]
     int n, C, H, R;
     float cutoff;

@@ -1,6 +1,7 @@
 // Target coupling + output projection for 16-bit storage (E2Former-V2 explainer,
 // section 3.1: the aggregated message m_i is coupled with the target's own
-// encoding, hhat_i = EAAS_i(m_i), then out_i = W_O[l] hhat_i per degree).
+// encoding, hhat_i = EAAS_i(m_i), then out_i = W_O[l] hhat_i per degree).  m_i
+// arrives in fp16 under one power-of-two scale per node.
 //
 // One block covers 16 nodes and all C channels, in two halves of C/2 input
 // channels (one for C = 32): each thread couples 2 channels of one node in
@@ -85,12 +86,13 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
         const int en = item / (CH / 2), cp = item - en * (CH / 2);
         const long long enode = node0 + en;
         const int c0 = half * CH + 2 * cp;
+        const float sc = en < nvalid ? a.msc[enode] : 0.f;
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
-            float2 x = make_float2(0.f, 0.f);
-            if (en < nvalid) x = *reinterpret_cast<const float2 *>(a.m + (enode * NC + e) * C + c0);
-            v[e][0] = x.x;
-            v[e][1] = x.y;
+            uint32_t x = 0u;
+            if (en < nvalid) x = *reinterpret_cast<const uint32_t *>(a.m + (enode * NC + e) * C + c0);
+            v[e][0] = (float)__builtin_bit_cast(_Float16, uint16_t(x & 0xffffu)) * sc;
+            v[e][1] = (float)__builtin_bit_cast(_Float16, uint16_t(x >> 16)) * sc;
         }
         eaas_multi<L, 2>(v, sD + en * ND, &sW[c0 * WS], WS, tab, sDir[en]);
         if (a.hhat_tap && en < nvalid) {

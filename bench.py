@@ -41,16 +41,20 @@ def algorithmic_bytes(cfg, nnz: int) -> dict:
     row h'_j and key row k_j, its index and its position -- fp32 rows for fp32
     storage; for bf16 storage fp16 rows, the key travelling with h's odd last
     component in 16-byte pieces (4C bytes) next to h's component pairs; per target
-    its query, its position, its row bounds and one fp32 output row -- the message
-    m_i for bf16 storage (the target coupling runs in the output kernel), the
-    coupled hhat_i for fp32 storage, which also reads the target's D blocks."""
+    its query, its position, its row bounds and one output row -- the message m_i
+    in fp16 with its node scale for bf16 storage (the target coupling runs in the
+    output kernel), the coupled fp32 hhat_i for fp32 storage, which also reads the
+    target's D blocks."""
     C, nc = cfg.channels, cfg.n_comp
     nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
     if cfg.storage == "bf16":
         per_pair = 2 * (nc & ~1) * C + 4 * C + 4 + 12
     else:
         per_pair = 4 * nc * C + 4 * C + 4 + 12
-    per_node = 4 * C + 12 + 8 + 4 * nc * C + (0 if cfg.storage == "bf16" else 4 * nd)
+    if cfg.storage == "bf16":
+        per_node = 4 * C + 12 + 8 + 2 * nc * C + 4
+    else:
+        per_node = 4 * C + 12 + 8 + 4 * nc * C + 4 * nd
     return {"per_pair": per_pair, "per_node": per_node, "total": nnz * per_pair + cfg.n * per_node}
 
 
@@ -239,9 +243,10 @@ def main():
         front = (N * nc * C * s + N * C * 8 + N * nc * C * 4                          # projections
                  + N * nc * C * 4 + N * 12 + N * nc * C * s + N * (4 * nd + 16))    # source EAAS
         stage_names = ("neighbours", "projections", "source_eaas", "attention", "output_projection")
+    back = N * (2 * nc * C + 4) + N * nc * C * 4 if cfg.storage == "bf16" else 2 * N * nc * C * 4
     layer_bytes = (front
                    + ab["total"]                                          # streaming attention + target EAAS
-                   + 2 * N * nc * C * 4)                                  # output projection
+                   + back)                                                # (target EAAS +) output projection
     stage_ms = {}
     for name, v in zip(stage_names, mean):
         if name is None:

@@ -122,9 +122,10 @@ def test_target_order_does_not_change_results(gpu_lib, storage):
     builder's cell order, a random permutation) gives the same outputs.  With fp32
     storage (one target per wave) they are bit-identical.  With 16-bit storage two
     consecutive targets share a wave and the chunks of their merged list, so the
-    order changes only the fp32 summation order: every order is deterministic and
-    the orders agree to 5e-4 of the output RMS (measured 5e-5 over 6.9 M values;
-    a wrong pairing would differ by O(1))."""
+    order changes the fp32 summation order, which can move the fp16-stored message
+    by one rounding step: every order is deterministic and the orders agree to
+    5e-3 of the output RMS (measured 1e-3 over 6.9 M values; a wrong pairing would
+    differ by O(1))."""
     base = W.make_workload("c4", n=6000)
     cfg = W.LayerConfig(**{**base.cfg.__dict__, "storage": storage})
     wl = W.make_workload(cfg)
@@ -143,8 +144,8 @@ def test_target_order_does_not_change_results(gpu_lib, storage):
     if storage == "fp32":
         assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
     else:
-        assert rel_err(outs[1].numpy(), outs[0].numpy()) < 5e-4
-        assert rel_err(outs[2].numpy(), outs[0].numpy()) < 5e-4
+        assert rel_err(outs[1].numpy(), outs[0].numpy()) < 5e-3
+        assert rel_err(outs[2].numpy(), outs[0].numpy()) < 5e-3
 
 
 def _sampled_check(gpu_lib, wl, rows, nsample, seed):
