@@ -67,9 +67,11 @@ typedef struct {
     int32_t heads;
     int32_t n_rbf;
     float cutoff;        /* Angstrom; also the RBF range and the envelope's zero */
-    int32_t storage;     /* e2v2_dtype of h, W_Q, W_K, W_V and W_O.  The coupled values h'
-                            are kept in the workspace as fp32 (fp32 storage) or, for bf16
-                            storage, as fp16 with one power-of-two scale per node */
+    int32_t storage;     /* e2v2_dtype of h, W_Q, W_K, W_V and W_O.  The intermediates
+                            k, h' and the aggregated message m are kept in the
+                            workspace as fp32 (fp32 storage) or, for bf16 storage, as
+                            fp16 under one power-of-two scale per node; arithmetic is
+                            fp32 throughout */
 } e2v2_layer_desc;
 
 /* Layer weights (device pointers).
@@ -94,11 +96,12 @@ typedef struct {
  * and 6 run as one kernel on whole nodes. */
 typedef struct {
     float *q;        /* [n][C] fp32                                         */
-    float *k;        /* [n][C] fp32                                         */
+    float *k;        /* [n][C] fp32 (for bf16 storage: k before its fp16 storage) */
     float *v;        /* [n][(lmax+1)^2][C] fp32                             */
     float *hprime;   /* [n][(lmax+1)^2][C] fp32: h' as the streaming kernel reads it
                         (for bf16 storage: its 16-bit form times the node's scale) */
-    float *m;        /* [n][(lmax+1)^2][C] fp32 aggregated message (step 4) */
+    float *m;        /* [n][(lmax+1)^2][C] fp32 aggregated message (step 4); for
+                        bf16 storage its fp16 form times the node's scale */
     float *hhat;     /* [n][(lmax+1)^2][C] fp32 target-coupled message (step 5) */
     hipEvent_t *events;  /* host array of 5 caller-created events or NULL: recorded on
                             `stream` before step 2, after step 2, after step 3, after
@@ -174,7 +177,8 @@ e2v2_status e2v2_eaas_couple(const float *pos, const void *x, e2v2_dtype x_dtype
  *   out  device [n][(lmax+1)^2][C] fp32
  *   workspace  device scratch of at least e2v2_attn_workspace_bytes(desc, n)
  * No N x K tensor is formed: the streaming kernel reads each neighbour's key
- * and coupled value once per target and accumulates on chip. */
+ * and coupled value at most once per target (for bf16 storage with lmax <= 2,
+ * once for two consecutive targets of target_order) and accumulates on chip. */
 e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, const void *h,
                               const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
                               const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
