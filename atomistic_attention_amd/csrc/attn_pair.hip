@@ -136,6 +136,16 @@ __device__ __forceinline__ int pair_union(const int32_t *__restrict__ idx, int n
     return tot3[0] + tot3[1] + tot3[2];
 }
 
+// v_permlane16_swap_b32 on a and b.  In each pair of 16-lane rows (2 t, 2 t + 1), lane
+// for lane, the even row ends with (a, b) = (its own a, the odd row's a) and the odd row
+// with (the even row's b, its own b).
+__device__ __forceinline__ void row_swap(float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void pair_lds_sync()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -159,6 +169,10 @@ void attn_pair_kernel(const AttnArgs A)
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr int SP = S >= 2 ? 2 : 1;  // value rows per phase
     constexpr int NPH = S / SP;
+    // With H = 16 the two channel halves b of a head sit in adjacent 16-lane rows, and
+    // each half computes the logits and softmax weights of 4 of its slot's 8 entries.
+    constexpr bool ROWHALF = H == 16;
+    constexpr int SO = ROWHALF ? 4 : S;  // entries whose logit this lane computes
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     // Workgroups go to the 8 XCDs round robin; each XCD gets one contiguous run of
@@ -177,6 +191,8 @@ void attn_pair_kernel(const AttnArgs A)
     // B operand of the bias product, log2(e) W_rbf[k][head] zero-padded to 64 x 16.
     __shared__ float sW[64 * 16];
     __shared__ int sU[4][kPairUnionMax];
+    __shared__ __align__(16) int sE[4][16];      // the chunk's entries, per wave
+    __shared__ __align__(16) float sS[4][16];    // and their row scales
     for (int e = threadIdx.x; e < 64 * 16; e += 256) {
         const int k = e >> 4, hh = (e & 15) % H;
         sW[e] = (k < R) ? A.w_rbf[k * H + hh] * LOG2E : 0.f;
@@ -275,26 +291,23 @@ void attn_pair_kernel(const AttnArgs A)
         }
         return bias;
     };
-    // this lane's S pair biases from the product
+    // this lane's S pair biases from the product (H < 16: pairs u S .. u S + S - 1 lie
+    // in this lane's four)
     auto lane_bias = [&](const floatx4 &bias, float (&bs)[S]) {
-        if constexpr (H == 16) {            // pairs 8u .. 8u+7: half b holds 4b .. 4b+3, the partner the rest
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float other = __shfl_xor(bias[r], 16, 64);
-                bs[r] = b ? other : bias[r];
-                bs[4 + r] = b ? bias[r] : other;
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < S; ++s) bs[s] = pick4(bias, ((u * S) & 3) + s);
-        }
+        for (int s = 0; s < S; ++s) bs[s] = pick4(bias, ((u * S) & 3) + s);
     };
     // lazily moved reference maximum (as in attn_kernel), then the chunk's weights
-    auto softmax = [&](const float (&sl)[S], const float (&scl)[S], float &mu, float &z, float (&acc)[NC][4],
+    auto softmax = [&](const float (&sl)[SO], const float (&scl)[SO], float &mu, float &z, float (&acc)[NC][4],
                        float (&p)[S]) {
         float mx = sl[0];
 #pragma unroll
-        for (int s = 1; s < S; ++s) mx = fmaxf(mx, sl[s]);
+        for (int s = 1; s < SO; ++s) mx = fmaxf(mx, sl[s]);
+        if constexpr (ROWHALF) {                // one maximum for both halves of the slot
+            float me = mx, mo = mx;
+            row_swap(me, mo);
+            mx = fmaxf(me, mo);
+        }
         const bool grow = mx > mu + 8.f;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             const float mun = grow ? mx : mu;
@@ -306,14 +319,26 @@ void attn_pair_kernel(const AttnArgs A)
                 for (int c = 0; c < 4; ++c) acc[e][c] *= corr;
             mu = mun;
         }
-        float psum = 0.f;
+        float psum = 0.f, po[SO];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            p[s] = __builtin_amdgcn_exp2f(sl[s] - mu);
-            psum += p[s];
-            p[s] *= scl[s];                    // fold the row scale into the weight
+        for (int s = 0; s < SO; ++s) {
+            po[s] = __builtin_amdgcn_exp2f(sl[s] - mu);
+            psum += po[s];
+            po[s] *= scl[s];                   // fold the row scale into the weight
         }
-        z += psum;
+        z += psum;                             // with row halves: this half's entries only
+        if constexpr (ROWHALF) {               // every lane takes all 8 weights of its slot
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float pe = po[r], pw = po[r];
+                row_swap(pe, pw);
+                p[r] = pe;
+                p[4 + r] = pw;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < S; ++s) p[s] = po[s];
+        }
     };
 
     // Prologue: entry and position of pair pm of the first chunk.
@@ -323,18 +348,30 @@ void attn_pair_kernel(const AttnArgs A)
     if (ep >= 0) pj = A.pos4[ep >> 2];
 
     for (int c0 = 0; c0 < nu; c0 += 16) {
-        // ---- (a) this lane's S entries of the chunk, their lists and row scales
+        // ---- (a) the chunk's entries and row scales pass from the pair lanes through
+        //          LDS; every lane reads the S entries of its slot
+        if (lane < 16) {
+            sE[wv][lane] = ep;
+            sS[wv][lane] = pj.w;
+        }
+        pair_lds_sync();
         int js[S];
-        bool fa[S], fb[S];
-        float scl[S];
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            const int p = u * S + s;
-            const int e = __shfl(ep, p, 64);
+            const int e = sE[wv][u * S + s];
             js[s] = e >= 0 ? (e >> 2) : -1;
-            fa[s] = e >= 0 && (e & 2) != 0;
-            fb[s] = e >= 0 && (e & 1) != 0;
-            scl[s] = __shfl(pj.w, p, 64);
+        }
+        // Entries whose logit and softmax weight this lane computes: all S of the slot,
+        // or with row halves the 4 entries 4 b + r of its half.
+        const int s0o = ROWHALF ? 4 * b : 0;
+        bool fa[SO], fb[SO];
+        float scl[SO];
+#pragma unroll
+        for (int r = 0; r < SO; ++r) {
+            const int e = sE[wv][u * S + s0o + r];
+            fa[r] = e >= 0 && (e & 2) != 0;
+            fb[r] = e >= 0 && (e & 1) != 0;
+            scl[r] = sS[wv][u * S + s0o + r];
         }
         // ---- (b) every key + tail row and the first phase of value rows
         uint4 g4[S];
@@ -356,27 +393,43 @@ void attn_pair_kernel(const AttnArgs A)
         const bool anyb = __builtin_amdgcn_ballot_w64(vp && (ep & 1) != 0) != 0;
         // ---- (e) per target: logits (4-channel partial + the other half) and the
         //          online-softmax update
-        auto logits = [&](float4 pt, bool ok, float4 qv, const bool (&f)[S], float (&sl)[S]) {
-            float bs[S];
-            lane_bias(bias_of(pj, pt, vp && ok), bs);
+        auto logits = [&](float4 pt, bool ok, float4 qv, const bool (&f)[SO], float (&sl)[SO]) {
+            const floatx4 bias = bias_of(pj, pt, vp && ok);
+            float x[S];                         // this half's 4-channel part of q . k
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 float qk = qv.x * f16_of(g4[s].x, 0);
                 qk = fmaf(qv.y, f16_of(g4[s].x, 1), qk);
                 qk = fmaf(qv.z, f16_of(g4[s].y, 0), qk);
-                qk = fmaf(qv.w, f16_of(g4[s].y, 1), qk);
-                qk += __shfl_xor(qk, H, 64);
-                sl[s] = f[s] ? fmaf(qk * scl[s], qscale, bs[s]) : -INFINITY;
+                x[s] = fmaf(qv.w, f16_of(g4[s].y, 1), qk);
+            }
+            if constexpr (ROWHALF) {
+                // Half 0 takes entry r's full dot product and half 1 entry 4 + r's;
+                // the bias product already holds pairs 8 u + 4 b + r in this lane.
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float lo = x[r], hi = x[4 + r];
+                    row_swap(lo, hi);
+                    sl[r] = f[r] ? fmaf((lo + hi) * scl[r], qscale, bias[r]) : -INFINITY;
+                }
+            } else {
+                float bs[S];
+                lane_bias(bias, bs);
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const float qk = x[s] + __shfl_xor(x[s], H, 64);
+                    sl[s] = f[s] ? fmaf(qk * scl[s], qscale, bs[s]) : -INFINITY;
+                }
             }
         };
         float psa[S], psb[S];
         if (anya) {
-            float sl[S];
+            float sl[SO];
             logits(pa, va, qa, fa, sl);
             softmax(sl, scl, mua, za, acca, psa);
         }
         if (anyb) {
-            float sl[S];
+            float sl[SO];
             logits(pb, vb, qb, fb, sl);
             softmax(sl, scl, mub, zb, accb, psb);
         }
@@ -432,6 +485,11 @@ void attn_pair_kernel(const AttnArgs A)
     // ---- merge the PS partial softmaxes of each target (butterfly over the slot
     //      bits of the lane, halving the channel set at each step) and store m
     auto merge = [&](float &mu, float &z, float (&acc)[NC][4]) {
+        if constexpr (ROWHALF) {                // the two halves' normalisers (same maximum)
+            float ze = z, zo = z;
+            row_swap(ze, zo);
+            z = ze + zo;
+        }
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
             const int bit = NB - 1 - st;
