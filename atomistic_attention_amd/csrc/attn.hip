@@ -147,7 +147,7 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
         // ---- (d) pair pm: distance, Gaussians x envelope, bias product on the matrix cores
         const bool vp = (jp >= 0) && (jp < n);
         const float dx = pj.x - pi4.x, dy = pj.y - pi4.y, dz = pj.z - pi4.z;
-        const float d = vp ? sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;
+        const float d = vp ? __builtin_amdgcn_sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;   // v_sqrt_f32, 1 ulp
         const float fc = vp ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
         const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
         const float t0 = fmaf(d, inv_delta, -gsc * (float)kq);   // g (d - mu_k) / Delta for k = kq
@@ -345,7 +345,7 @@ static hipError_t launch_attn_lh(const AttnArgs &a, hipStream_t stream)
 hipError_t launch_attn(int L, int hp_bf16, const AttnArgs &a, hipStream_t stream)
 {
     if (a.n <= 0) return hipSuccess;
-    if (hp_bf16 && L <= 2 && a.n < attn_pair_max_atoms()) return launch_attn_pair(L, a, stream);
+    if (hp_bf16 && L <= 2 && a.n < attn_pair_max_atoms(L, 8 * a.H)) return launch_attn_pair(L, a, stream);
     switch (L * 2 + (hp_bf16 ? 1 : 0)) {
     case 0: return launch_attn_lh<0, false>(a, stream);
     case 1: return launch_attn_lh<0, true>(a, stream);

@@ -23,6 +23,15 @@ template <int NC> struct HpStep<true, NC> {
 #pragma unroll
         for (int p = 0; p < NPR; ++p) pr[p] = *reinterpret_cast<const uint4 *>(nb + p * 2 * C + (cb >> 2) * 8);
     }
+    // The same row addressed by a 32-bit byte offset from base (row * row bytes
+    // must stay below 2^32): one scalar base plus one 32-bit offset per load.
+    __device__ __forceinline__ void load32(const void *base, uint32_t row, int cb, int C)
+    {
+        const unsigned char *nb = reinterpret_cast<const unsigned char *>(base) +
+                                  (row * uint32_t(2 * hp_pair_row(NC, C)) + uint32_t(cb >> 2) * 16u);
+#pragma unroll
+        for (int p = 0; p < NPR; ++p) pr[p] = *reinterpret_cast<const uint4 *>(nb + p * 4 * C);
+    }
     // component e < 2 NPR, channel c of the lane's 4 (the odd last component
     // comes with the key, see tail())
     __device__ __forceinline__ float get(int e, int c) const
@@ -111,8 +120,8 @@ __device__ __forceinline__ void store_message_f16(const AttnArgs &A, int i, int 
 }
 
 // Two targets per wave over the union of their lists (attn_pair.hip): 16-bit
-// storage, l_max <= 2, n < attn_pair_max_atoms().
+// storage, l_max <= 2, n < attn_pair_max_atoms(L, C).
 hipError_t launch_attn_pair(int L, const AttnArgs &a, hipStream_t stream);
-int attn_pair_max_atoms();
+long long attn_pair_max_atoms(int L, int C);
 
 }  // namespace e2v2

@@ -155,7 +155,18 @@ __device__ __forceinline__ void pair_lds_sync()
 
 }  // namespace
 
-int attn_pair_max_atoms() { return 1 << 29; }
+// Entry codes need n < 2^29, and rows are addressed by 32-bit byte offsets: n times
+// the longest row (h' pairs 2 (NC & ~1) C bytes, key + tail 4 C, position 16) stays
+// below 2^32.
+long long attn_pair_max_atoms(int L, int C)
+{
+    const long long nc = (long long)(L + 1) * (L + 1);
+    long long row = 2 * (nc & ~1LL) * C;
+    if (row < 4LL * C) row = 4LL * C;
+    if (row < 16) row = 16;
+    const long long lim = (1LL << 32) / row;
+    return lim < (1LL << 29) ? lim : (1LL << 29);
+}
 
 template <int L, int H>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -268,7 +279,7 @@ void attn_pair_kernel(const AttnArgs A)
     // (4 (lane / 16) + r, head (lane % 16) % H) of the returned product.
     auto bias_of = [&](float4 pj, float4 pt, bool ok) -> floatx4 {
         const float dx = pj.x - pt.x, dy = pj.y - pt.y, dz = pj.z - pt.z;
-        const float d = ok ? sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;
+        const float d = ok ? __builtin_amdgcn_sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;   // v_sqrt_f32, 1 ulp
         const float fc = ok ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
         const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
         const float t0 = fmaf(d, inv_delta, -gsc * (float)kq);     // g (d - mu_k) / Delta for k = kq
@@ -355,11 +366,11 @@ void attn_pair_kernel(const AttnArgs A)
             sS[wv][lane] = pj.w;
         }
         pair_lds_sync();
-        int js[S];
+        uint32_t rw[S];                         // rows to load (an entry of neither target reads ifill's)
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int e = sE[wv][u * S + s];
-            js[s] = e >= 0 ? (e >> 2) : -1;
+            rw[s] = uint32_t(e >= 0 ? (e >> 2) : ifill);
         }
         // Entries whose logit and softmax weight this lane computes: all S of the slot,
         // or with row halves the 4 entries 4 b + r of its half.
@@ -376,13 +387,12 @@ void attn_pair_kernel(const AttnArgs A)
         // ---- (b) every key + tail row and the first phase of value rows
         uint4 g4[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const size_t node = (size_t)(js[s] >= 0 ? js[s] : ifill);
-            g4[s] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(A.k) + node * (2 * C) + 2 * cb);
-        }
+        for (int s = 0; s < S; ++s)
+            g4[s] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(A.k) +
+                                                     (rw[s] * uint32_t(4 * C) + uint32_t(4 * cb)));
         HpStep<true, NC> hv[2][SP];       // value rows, double-buffered across phases
 #pragma unroll
-        for (int s = 0; s < SP; ++s) hv[0][s].load(A.hp, js[s] >= 0 ? js[s] : ifill, cb, C);
+        for (int s = 0; s < SP; ++s) hv[0][s].load32(A.hp, rw[s], cb, C);
         // ---- (c) the next chunk's entry for pair pm
         int en = -1;
         if (c0 + 16 + pm < nu) en = entry(c0 + 16 + pm);
@@ -398,7 +408,7 @@ void attn_pair_kernel(const AttnArgs A)
             float x[S];                         // this half's 4-channel part of q . k
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                float qk = qv.x * f16_of(g4[s].x, 0);
+                float qk = fmaf(qv.x, f16_of(g4[s].x, 0), 0.f);   // one v_fma_mix each
                 qk = fmaf(qv.y, f16_of(g4[s].x, 1), qk);
                 qk = fmaf(qv.z, f16_of(g4[s].y, 0), qk);
                 x[s] = fmaf(qv.w, f16_of(g4[s].y, 1), qk);
@@ -450,12 +460,11 @@ void attn_pair_kernel(const AttnArgs A)
             }
             if (ph + 1 < NPH) {
 #pragma unroll
-                for (int s = 0; s < SP; ++s) {
-                    const int jn2 = js[(ph + 1) * SP + s];
-                    hv[(ph + 1) & 1][s].load(A.hp, jn2 >= 0 ? jn2 : ifill, cb, C);
-                }
+                for (int s = 0; s < SP; ++s) hv[(ph + 1) & 1][s].load32(A.hp, rw[(ph + 1) * SP + s], cb, C);
             }
-            if (ph == NPH - 1 && en >= 0) pjn = A.pos4[en >> 2];
+            if (ph == NPH - 1 && en >= 0)
+                pjn = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(A.pos4) +
+                                                        uint32_t(en >> 2) * 16u);
             auto accumulate = [&](const float (&p)[S], float (&acc)[NC][4]) {
 #pragma unroll
                 for (int e = 0; e < NC; ++e)
@@ -550,7 +559,7 @@ static hipError_t launch_attn_pair_l(const AttnArgs &a, hipStream_t stream)
 hipError_t launch_attn_pair(int L, const AttnArgs &a, hipStream_t stream)
 {
     if (a.n <= 0) return hipSuccess;
-    if (a.n >= attn_pair_max_atoms()) return hipErrorInvalidValue;
+    if (a.n >= attn_pair_max_atoms(L, 8 * a.H)) return hipErrorInvalidValue;
     switch (L) {
     case 0: return launch_attn_pair_l<0>(a, stream);
     case 1: return launch_attn_pair_l<1>(a, stream);
