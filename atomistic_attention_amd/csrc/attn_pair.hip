@@ -146,6 +146,8 @@ __device__ __forceinline__ void row_swap(float &a, float &b)
     b = __uint_as_float(r[1]);
 }
 
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
 __device__ __forceinline__ void pair_lds_sync()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -196,17 +198,19 @@ void attn_pair_kernel(const AttnArgs A)
     const int h = lane % H, b = (lane / H) & 1, u = lane / (2 * H);
     const int kq = lane >> 4, pm = lane & 15;
     const int R = A.R;
-    const int KK = (R + 3) >> 2;
     const int cb = 8 * h + 4 * b;       // first channel of this lane
 
-    // B operand of the bias product, log2(e) W_rbf[k][head] zero-padded to 64 x 16.
-    __shared__ float sW[64 * 16];
+    // B operand of the bias product in fp16, log2(e) W_rbf[k][head] zero-padded to
+    // 64 x 16, as v_mfma_f32_16x16x32_f16 fragments: group g, lane l holds
+    // k = 32 g + 8 (l / 16) + i (i < 8) for head column l % 16.
+    __shared__ __align__(16) _Float16 sWh[2][64][8];
     __shared__ int sU[4][kPairUnionMax];
     __shared__ __align__(16) int sE[4][16];      // the chunk's entries, per wave
     __shared__ __align__(16) float sS[4][16];    // and their row scales
-    for (int e = threadIdx.x; e < 64 * 16; e += 256) {
-        const int k = e >> 4, hh = (e & 15) % H;
-        sW[e] = (k < R) ? A.w_rbf[k * H + hh] * LOG2E : 0.f;
+    for (int e = threadIdx.x; e < 2 * 64 * 8; e += 256) {
+        const int g = e >> 9, l = (e >> 3) & 63, i = e & 7;
+        const int k = 32 * g + 8 * (l >> 4) + i, hh = (l & 15) % H;
+        sWh[g][l][i] = (_Float16)((k < R) ? A.w_rbf[k * H + hh] * LOG2E : 0.f);
     }
     __syncthreads();
 
@@ -282,24 +286,20 @@ void attn_pair_kernel(const AttnArgs A)
         const float d = ok ? __builtin_amdgcn_sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;   // v_sqrt_f32, 1 ulp
         const float fc = ok ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
         const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
-        const float t0 = fmaf(d, inv_delta, -gsc * (float)kq);     // g (d - mu_k) / Delta for k = kq
-        const float *wrow = sW + kq * 16 + pm;
-        floatx4 bias = {0.f, 0.f, 0.f, 0.f};
-        if (KK <= 8) {
+        const float t0 = fmaf(d, inv_delta, -gsc * (float)(8 * kq));   // g (d - mu_k) / Delta for k = 8 kq
+        // A operand: lane (kq, pm) holds phi_k of pair pm for k = 8 kq + i (+ 32)
+        auto group = [&](int g, floatx4 acc) {
+            half8_t a;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const float tk = t0 - (4.0f * gsc) * (float)kk;
-                const float phi = __builtin_amdgcn_exp2f(fmaf(-tk, tk, lfc));
-                bias = __builtin_amdgcn_mfma_f32_16x16x4f32(phi, wrow[64 * kk], bias, 0, 0, 0);
+            for (int i = 0; i < 8; ++i) {
+                const float tk = t0 - gsc * (float)(32 * g + i);
+                a[i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(-tk, tk, lfc));
             }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const float tk = t0 - (4.0f * gsc) * (float)kk;
-                const float phi = __builtin_amdgcn_exp2f(fmaf(-tk, tk, lfc));
-                bias = __builtin_amdgcn_mfma_f32_16x16x4f32(phi, wrow[64 * kk], bias, 0, 0, 0);
-            }
-        }
+            const half8_t w = *reinterpret_cast<const half8_t *>(&sWh[g][lane][0]);
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, w, acc, 0, 0, 0);
+        };
+        floatx4 bias = group(0, floatx4{0.f, 0.f, 0.f, 0.f});
+        if (R > 32) bias = group(1, bias);
         return bias;
     };
     // this lane's S pair biases from the product (H < 16: pairs u S .. u S + S - 1 lie
