@@ -288,12 +288,20 @@ void attn_pair_kernel(const AttnArgs A)
         const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
         const float t0 = fmaf(d, inv_delta, -gsc * (float)(8 * kq));   // g (d - mu_k) / Delta for k = 8 kq
         // A operand: lane (kq, pm) holds phi_k of pair pm for k = 8 kq + i (+ 32)
+        // With t_i = t - g i (g = gsc), phi_{i+1} / phi_i = exp2(2 g t - g^2) e^{-i}: two
+        // exponentials and a product chain give the lane's 8 consecutive Gaussians.
+        // Whenever one of them exceeds 2^-24 the first is above 2^-118, a normal
+        // number, so the chain loses nothing that matters.
         auto group = [&](int g, floatx4 acc) {
+            const float t = t0 - gsc * (float)(32 * g);
+            float phi = __builtin_amdgcn_exp2f(fmaf(-t, t, lfc));
+            float r = __builtin_amdgcn_exp2f(fmaf(2.f * gsc, t, -gsc * gsc));
             half8_t a;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float tk = t0 - gsc * (float)(32 * g + i);
-                a[i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(-tk, tk, lfc));
+                a[i] = (_Float16)phi;
+                phi *= r;
+                r *= 0.36787944117144233f;                      // exp2(-2 g^2) = 1 / e
             }
             const half8_t w = *reinterpret_cast<const half8_t *>(&sWh[g][lane][0]);
             return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, w, acc, 0, 0, 0);
