@@ -22,7 +22,8 @@ import math
 
 import numpy as np
 
-__all__ = ["LayerConfig", "CONFIGS", "Workload", "make_workload", "num_paths",
+__all__ = ["LayerConfig", "CONFIGS", "Workload", "make_workload", "num_paths", "StackConfig", "STACKS",
+           "Stack", "trajectory", "make_stack",
            "path_list", "round_bf16", "bf16_bits", "bf16_from_bits", "device_arrays"]
 
 
@@ -206,3 +207,75 @@ def make_workload(cfg: LayerConfig | str, n: int | None = None, seed: int | None
     w_src = f32(rng.standard_normal((len(paths), C)) * scale)
     w_tgt = f32(rng.standard_normal((len(paths), C)) * scale)
     return Workload(cfg, pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt)
+
+
+# ---------------------------------------------------------------------------
+# Four-layer stacks over a moving system (Tessera article: three short-range
+# layers with a 5 A cutoff and one long-range layer with 8 A; neighbour lists
+# rebuilt every 10 steps, early when an atom has moved more than 0.25 A).
+
+
+@dataclasses.dataclass(frozen=True)
+class StackConfig:
+    name: str
+    base: str           # LayerConfig giving geometry, density, l_max, C, heads, n_rbf, storage
+    n: int
+    cutoffs: tuple      # per layer, in order (A)
+    max_neighbors: int  # K of the list at the largest cutoff
+    seed: int
+    steps: int          # trajectory length
+    sigma: float        # per-step random displacement, per coordinate (A)
+
+
+STACKS = {
+    "s1": StackConfig("s1", "c1", 256, (5.0, 5.0, 5.0, 8.0), 256, 2001, 16, 0.005),
+    "s2": StackConfig("s2", "c3", 4000, (5.0, 5.0, 5.0, 8.0), 256, 2002, 16, 0.005),
+    "s4": StackConfig("s4", "c4", 32768, (5.0, 5.0, 5.0, 8.0), 256, 2004, 100, 0.005),
+}
+
+
+@dataclasses.dataclass
+class Stack:
+    """Inputs of a stack run: one weight set per layer (each a Workload whose
+    cutoff is the layer's), the features h0 fed to the first layer at every
+    step, and positions per step (fp32 values)."""
+    cfg: StackConfig
+    layers: list
+    h0: np.ndarray
+    traj: list
+
+    @property
+    def base(self) -> LayerConfig:
+        return self.layers[0].cfg
+
+
+def trajectory(pos0: np.ndarray, steps: int, sigma: float, seed: int, jumps=()) -> list:
+    """Positions for ``steps`` steps: a random walk with N(0, sigma^2) steps per
+    coordinate, each step rounded to fp32; ``jumps`` adds (step, atom, (dx, dy, dz))
+    offsets at the given steps (kept in later steps)."""
+    rng = np.random.default_rng(seed)
+    p = np.asarray(pos0, dtype=np.float64).astype(np.float32).astype(np.float64)
+    out = [p.copy()]
+    for t in range(1, steps):
+        p = p + rng.standard_normal(p.shape) * sigma
+        for (js, a, v) in jumps:
+            if js == t:
+                p[a] = p[a] + np.asarray(v, dtype=np.float64)
+        p = p.astype(np.float32).astype(np.float64)
+        out.append(p.copy())
+    return out
+
+
+def make_stack(cfg: StackConfig | str, n: int | None = None, steps: int | None = None, jumps=()) -> Stack:
+    """Draw a stack: layer l's weights come from the base config with the layer's
+    cutoff and seed + l; the trajectory starts at the base geometry."""
+    if isinstance(cfg, str):
+        cfg = STACKS[cfg]
+    if n is not None or steps is not None:
+        cfg = dataclasses.replace(cfg, n=cfg.n if n is None else n, steps=cfg.steps if steps is None else steps)
+    base = dataclasses.replace(CONFIGS[cfg.base], n=cfg.n, max_neighbors=cfg.max_neighbors)
+    layers = [make_workload(dataclasses.replace(base, cutoff=rc, seed=cfg.seed + l)) for l, rc in enumerate(cfg.cutoffs)]
+    # the first layer's draw supplies the start geometry and h0
+    pos0, h0 = layers[0].pos, layers[0].h
+    traj = trajectory(pos0, cfg.steps, cfg.sigma, cfg.seed + 1000, jumps)
+    return Stack(cfg, layers, h0, traj)

@@ -18,5 +18,10 @@ tests/test_oracle_*.py):
   layer.attention                 pinned: torch scaled_dot_product_attention (l_max = 0),
                                   one-neighbour and equal-logit special cases
   layer.layer_forward             pinned: rotation equivariance to 1e-10
+  stack.filter_rows               pinned: equals the brute-force search at the smaller cutoff
+  stack.max_displacement2         pinned: exact dyadic displacements, strict threshold
+  stack.StackState (rebuild rule) pinned: trajectories with known rebuild steps
+  stack.stack_step / run_stack    pinned: topology reuse on a two-atom system, rotation
+                                  equivariance of the whole stack to 1e-10
 """
-from . import so3, layer  # noqa: F401
+from . import so3, layer, stack  # noqa: F401
