@@ -22,7 +22,8 @@ EXPORTS = [
     "e2v2_attn_forward", "e2v2_attn_forward_taps", "e2v2_attn_prepare", "e2v2_attn_aggregate",
     "e2v2_attn_workspace_bytes", "e2v2_num_paths",
     "e2v2_path_table", "e2v2_eaas_coefficients", "e2v2_alignment_wigner", "e2v2_status_string",
-    "e2v2_last_error",
+    "e2v2_last_error", "e2v2_filter_neighbors", "e2v2_max_displacement2", "e2v2_stack_state_bytes",
+    "e2v2_stack_workspace_bytes", "e2v2_stack_forward",
 ]
 
 
@@ -41,6 +42,11 @@ class Taps(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("hprime", ctypes.c_void_p), ("m", ctypes.c_void_p), ("hhat", ctypes.c_void_p),
                 ("events", ctypes.c_void_p)]
+
+
+class RebuildPolicy(ctypes.Structure):
+    _fields_ = [("rebuild_every", ctypes.c_int32), ("max_displacement", ctypes.c_float),
+                ("steps_since_rebuild", ctypes.c_int32), ("rebuilt", ctypes.c_int32), ("rebuilds", ctypes.c_int64)]
 
 
 class E2V2Error(RuntimeError):
@@ -88,6 +94,17 @@ def load(path: str = LIB_PATH):
     lib.e2v2_eaas_coefficients.restype = ctypes.c_int
     lib.e2v2_alignment_wigner.argtypes = [i32, vp, vp]
     lib.e2v2_alignment_wigner.restype = ctypes.c_int
+    lib.e2v2_filter_neighbors.argtypes = [vp, i32, f32, vp, vp, vp, vp, vp, vp]
+    lib.e2v2_filter_neighbors.restype = ctypes.c_int
+    lib.e2v2_max_displacement2.argtypes = [vp, vp, i32, vp, vp]
+    lib.e2v2_max_displacement2.restype = ctypes.c_int
+    lib.e2v2_stack_state_bytes.argtypes = [i32, ctypes.POINTER(LayerDesc), i32, i32]
+    lib.e2v2_stack_state_bytes.restype = sz
+    lib.e2v2_stack_workspace_bytes.argtypes = [i32, ctypes.POINTER(LayerDesc), i32, i32]
+    lib.e2v2_stack_workspace_bytes.restype = sz
+    lib.e2v2_stack_forward.argtypes = [i32, ctypes.POINTER(LayerDesc), ctypes.POINTER(Weights), vp, vp, i32, i32,
+                                       ctypes.POINTER(RebuildPolicy), vp, sz, vp, vp, sz, vp]
+    lib.e2v2_stack_forward.restype = ctypes.c_int
     lib.e2v2_status_string.argtypes = [ctypes.c_int]
     lib.e2v2_status_string.restype = ctypes.c_char_p
     lib.e2v2_last_error.argtypes = []
@@ -300,3 +317,65 @@ def e2v2_attn_aggregate(desc: LayerDesc, weights: dict, nbr_start, nbr_len, nbr_
                                    _ptr(nbr_idx), _ptr(target_order), nbr_start.shape[0], _ptr(out),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------------ neighbour reuse and the stack
+def e2v2_filter_neighbors(pos, cutoff: float, nbr_start, nbr_len, nbr_idx, out_len=None, out_idx=None, stream=None):
+    """Entries of each row within `cutoff` (same predicate as the builder), rows at the
+    input's starts.  Returns (out_len, out_idx); pass nbr_len / nbr_idx to filter in place."""
+    lib = load()
+    _dev(pos, torch.float32, "pos")
+    for t, nm in ((nbr_start, "nbr_start"), (nbr_len, "nbr_len"), (nbr_idx, "nbr_idx")):
+        _dev(t, torch.int32, nm)
+    if out_len is None:
+        out_len = torch.empty_like(nbr_len)
+    if out_idx is None:
+        out_idx = torch.empty_like(nbr_idx)
+    _check(lib.e2v2_filter_neighbors(_ptr(pos), pos.shape[0], float(cutoff), _ptr(nbr_start), _ptr(nbr_len),
+                                     _ptr(nbr_idx), _ptr(out_len), _ptr(out_idx), _stream(stream)))
+    return out_len, out_idx
+
+
+def e2v2_max_displacement2(pos, ref, out=None, stream=None) -> torch.Tensor:
+    """Largest squared displacement (fp64) as a one-element device tensor."""
+    lib = load()
+    _dev(pos, torch.float32, "pos")
+    _dev(ref, torch.float32, "ref")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=pos.device)
+    _check(lib.e2v2_max_displacement2(_ptr(pos), _ptr(ref), pos.shape[0], _ptr(out), _stream(stream)))
+    return out
+
+
+class StackRun:
+    """Device state and scratch of one e2v2_stack_forward run (allocated through torch),
+    and the host rebuild policy the calls update."""
+
+    def __init__(self, descs, weights, n: int, max_neighbors: int, device="cuda", rebuild_every: int = 10,
+                 max_displacement: float = 0.25):
+        lib = load()
+        self.L = len(descs)
+        self.descs = (LayerDesc * self.L)(*descs)
+        self.sdt = weights[0]["w_q"].dtype
+        self.weights = (Weights * self.L)(*(_weights(w, self.sdt) for w in weights))
+        self._keep = weights                      # the weight tensors outlive the calls
+        self.n, self.K = n, max_neighbors
+        sb = int(lib.e2v2_stack_state_bytes(self.L, self.descs, n, max_neighbors))
+        wb = int(lib.e2v2_stack_workspace_bytes(self.L, self.descs, n, max_neighbors))
+        if sb == 0 or wb == 0:
+            raise ValueError("invalid stack description")
+        self.state = torch.empty(sb, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(wb, dtype=torch.uint8, device=device)
+        self.policy = RebuildPolicy(rebuild_every, max_displacement, -1, 0, 0)
+
+    def e2v2_stack_forward(self, pos, h, out=None, stream=None) -> torch.Tensor:
+        lib = load()
+        _dev(pos, torch.float32, "pos")
+        _dev(h, self.sdt, "h")
+        if out is None:
+            out = torch.empty(h.shape, dtype=torch.float32, device=h.device)
+        _dev(out, torch.float32, "out")
+        _check(lib.e2v2_stack_forward(self.L, self.descs, self.weights, _ptr(pos), _ptr(h), self.n, self.K,
+                                      ctypes.byref(self.policy), _ptr(self.state), self.state.numel(), _ptr(out),
+                                      _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
+        return out

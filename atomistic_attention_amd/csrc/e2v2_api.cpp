@@ -626,3 +626,225 @@ e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, con
 }
 
 }  // extern "C"
+
+// ============================================================================
+// Neighbour reuse and the layer stack
+// ============================================================================
+namespace {
+constexpr int kMaxStackLayers = 16;
+
+// Distinct layer cutoffs, largest first.
+int distinct_cutoffs(int L, const e2v2_layer_desc *d, float *cut)
+{
+    int nc = 0;
+    for (int l = 0; l < L; ++l) {
+        bool seen = false;
+        for (int k = 0; k < nc; ++k) seen = seen || cut[k] == d[l].cutoff;
+        if (!seen) cut[nc++] = d[l].cutoff;
+    }
+    std::sort(cut, cut + nc, [](float a, float b) { return a > b; });
+    return nc;
+}
+int cutoff_index(int nc, const float *cut, float c)
+{
+    for (int k = 0; k < nc; ++k)
+        if (cut[k] == c) return k;
+    return -1;
+}
+
+// Persistent state: reference positions, target order, row starts, the
+// displacement slot, then per distinct cutoff the row lengths and entries.
+struct StackState {
+    size_t ref, order, start, disp, lists, per_list, len_off, total;
+    int ncut;
+    float cut[kMaxStackLayers];
+};
+StackState stack_state(int L, const e2v2_layer_desc *d, int n, int K)
+{
+    StackState s{};
+    s.ncut = distinct_cutoffs(L, d, s.cut);
+    const size_t N = (size_t)n;
+    size_t o = 0;
+    s.ref = o; o += al256(N * 12);
+    s.order = o; o += al256(N * 4);
+    s.start = o; o += al256(N * 4);
+    s.disp = o; o += 256;
+    s.lists = o;
+    s.len_off = al256(N * 4);
+    s.per_list = s.len_off + al256(N * (size_t)K * 4);
+    o += s.per_list * (size_t)s.ncut;
+    s.total = o + 256;
+    return s;
+}
+
+// Scratch: neighbour build workspace, one layer workspace (the largest), two fp32
+// feature buffers and a bf16 one for the next layer's input.
+struct StackWs {
+    size_t nbws, nbws_bytes, lws, lws_bytes, f0, f1, hb, total;
+};
+StackWs stack_ws(int L, const e2v2_layer_desc *d, int n, int K)
+{
+    StackWs w{};
+    const size_t feat = (size_t)n * (size_t)n_comp(d[0].lmax) * (size_t)d[0].channels;
+    size_t o = 0;
+    w.nbws = o; w.nbws_bytes = e2v2_build_neighbors_workspace_bytes(n, K); o += al256(w.nbws_bytes);
+    size_t lb = 0;
+    for (int l = 0; l < L; ++l) lb = std::max(lb, attn_ws(d[l], n).total);
+    w.lws = o; w.lws_bytes = lb; o += al256(lb);
+    w.f0 = o; o += al256(feat * 4);
+    w.f1 = o; o += al256(L > 2 ? feat * 4 : 0);
+    w.hb = o; o += al256(d[0].storage == E2V2_BF16 ? feat * 2 : 0);
+    w.total = o + 256;
+    return w;
+}
+
+e2v2_status check_stack(int L, const e2v2_layer_desc *descs, const e2v2_weights *weights, int n, int K)
+{
+    if (L < 1 || L > kMaxStackLayers) return fail(E2V2_ERR_ARG, "n_layers %d outside 1..%d", L, kMaxStackLayers);
+    if (!descs) return fail(E2V2_ERR_ARG, "descs is NULL");
+    for (int l = 0; l < L; ++l) {
+        e2v2_status st = check_desc(&descs[l]);
+        if (st != E2V2_OK) return st;
+        if (descs[l].lmax != descs[0].lmax || descs[l].channels != descs[0].channels ||
+            descs[l].storage != descs[0].storage)
+            return fail(E2V2_ERR_ARG, "layer %d differs from layer 0 in lmax, channels or storage", l);
+        if (weights && !weights[l].w_q) return fail(E2V2_ERR_ARG, "weights[%d] has NULL pointers", l);
+    }
+    if (n < 0 || n == INT32_MAX) return fail(E2V2_ERR_ARG, "n = %d out of range", n);
+    if (K < 1 || K > 4096) return fail(E2V2_ERR_ARG, "max_neighbors %d outside 1..4096", K);
+    if ((int64_t)n * K >= INT32_MAX) return fail(E2V2_ERR_ARG, "n*K exceeds int32 offsets");
+    return E2V2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+e2v2_status e2v2_filter_neighbors(const float *pos, int32_t n, float cutoff, const int32_t *nbr_start,
+                                  const int32_t *nbr_len, const int32_t *nbr_idx, int32_t *out_len,
+                                  int32_t *out_idx, hipStream_t stream)
+{
+    if (n < 0 || n == INT32_MAX) return fail(E2V2_ERR_ARG, "n = %d out of range", n);
+    if (!(cutoff > 0.f) || !std::isfinite(cutoff)) return fail(E2V2_ERR_ARG, "cutoff must be finite and > 0");
+    if (n == 0) return E2V2_OK;
+    for (const void *p : {(const void *)pos, (const void *)nbr_start, (const void *)nbr_len, (const void *)nbr_idx,
+                          (const void *)out_len, (const void *)out_idx}) {
+        if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
+        if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    }
+    hipError_t e = launch_filter_rows(pos, n, cutoff, nbr_start, nbr_len, nbr_idx, out_len, out_idx, stream);
+    if (e != hipSuccess) return hip_fail(e, "neighbour filter kernel");
+    return E2V2_OK;
+}
+
+e2v2_status e2v2_max_displacement2(const float *pos, const float *ref, int32_t n, double *max_d2, hipStream_t stream)
+{
+    if (n < 0) return fail(E2V2_ERR_ARG, "n < 0");
+    if (!max_d2 || (n > 0 && (!pos || !ref))) return fail(E2V2_ERR_ARG, "NULL device pointer");
+    if ((n > 0 && (!aligned16(pos) || !aligned16(ref))) || (reinterpret_cast<uintptr_t>(max_d2) & 7u))
+        return fail(E2V2_ERR_ARG, "pos and ref must be 16-byte aligned, max_d2 8-byte aligned");
+    hipError_t e = launch_max_disp2(pos, ref, n, max_d2, stream);
+    if (e != hipSuccess) return hip_fail(e, "displacement kernel");
+    return E2V2_OK;
+}
+
+size_t e2v2_stack_state_bytes(int32_t n_layers, const e2v2_layer_desc *descs, int32_t n, int32_t max_neighbors)
+{
+    if (n_layers < 1 || n_layers > kMaxStackLayers || !descs || n < 0 || max_neighbors < 1) return 0;
+    return stack_state(n_layers, descs, n, max_neighbors).total;
+}
+
+size_t e2v2_stack_workspace_bytes(int32_t n_layers, const e2v2_layer_desc *descs, int32_t n, int32_t max_neighbors)
+{
+    if (n_layers < 1 || n_layers > kMaxStackLayers || !descs || n < 0 || max_neighbors < 1) return 0;
+    for (int l = 0; l < n_layers; ++l)
+        if (descs[l].lmax < 0 || descs[l].lmax > kMaxL || descs[l].channels <= 0) return 0;
+    return stack_ws(n_layers, descs, n, max_neighbors).total;
+}
+
+e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, const e2v2_weights *weights,
+                               const float *pos, const void *h, int32_t n, int32_t K, e2v2_rebuild_policy *policy,
+                               void *state, size_t state_bytes, float *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    e2v2_status st = check_stack(n_layers, descs, weights, n, K);
+    if (st != E2V2_OK) return st;
+    if (!weights) return fail(E2V2_ERR_ARG, "weights is NULL");
+    if (!policy) return fail(E2V2_ERR_ARG, "policy is NULL");
+    if (policy->rebuild_every < 1) return fail(E2V2_ERR_ARG, "rebuild_every %d < 1", policy->rebuild_every);
+    if (!(policy->max_displacement >= 0.f) || !std::isfinite(policy->max_displacement))
+        return fail(E2V2_ERR_ARG, "max_displacement must be finite and >= 0");
+    if (n == 0) return E2V2_OK;
+    for (const void *p : {(const void *)pos, h, (const void *)state, (const void *)out, (const void *)workspace}) {
+        if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
+        if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    }
+    const StackState S = stack_state(n_layers, descs, n, K);
+    const StackWs W = stack_ws(n_layers, descs, n, K);
+    if (state_bytes < S.total) return fail(E2V2_ERR_ARG, "state too small: %zu < %zu", state_bytes, S.total);
+    if (workspace_bytes < W.total)
+        return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, W.total);
+    char *sb = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(state) + 255) & ~uintptr_t(255));
+    char *wb = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+    float *ref = reinterpret_cast<float *>(sb + S.ref);
+    int32_t *order = reinterpret_cast<int32_t *>(sb + S.order);
+    int32_t *start = reinterpret_cast<int32_t *>(sb + S.start);
+    double *disp = reinterpret_cast<double *>(sb + S.disp);
+    auto list_len = [&](int k) { return reinterpret_cast<int32_t *>(sb + S.lists + (size_t)k * S.per_list); };
+    auto list_idx = [&](int k) { return reinterpret_cast<int32_t *>(sb + S.lists + (size_t)k * S.per_list + S.len_off); };
+
+    // 1. rebuild decision
+    bool rebuild = policy->steps_since_rebuild < 0 || policy->steps_since_rebuild >= policy->rebuild_every;
+    hipError_t e = hipSuccess;
+    if (!rebuild) {
+        e = launch_max_disp2(pos, ref, n, disp, stream);
+        double d2 = 0.0;
+        if (e == hipSuccess) e = hipMemcpyAsync(&d2, disp, sizeof d2, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "displacement check");
+        const double lim = (double)policy->max_displacement * (double)policy->max_displacement;
+        rebuild = !(d2 <= lim);
+    }
+    // 2. lists at the largest cutoff, then filtered for each smaller one
+    if (rebuild) {
+        st = e2v2_build_neighbors(pos, n, S.cut[0], K, start, list_len(0), list_idx(0), (int64_t)n * K, nullptr,
+                                  order, wb + W.nbws, W.nbws_bytes, stream);
+        if (st != E2V2_OK) return st;
+        for (int k = 1; k < S.ncut; ++k) {
+            e = launch_filter_rows(pos, n, S.cut[k], start, list_len(0), list_idx(0), list_len(k), list_idx(k), stream);
+            if (e != hipSuccess) return hip_fail(e, "neighbour filter kernel");
+        }
+        e = hipMemcpyAsync(ref, pos, (size_t)n * 12, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "keeping the reference positions");
+    }
+    // 3. the layers
+    const bool bf = descs[0].storage == E2V2_BF16;
+    const long long feat = (long long)n * n_comp(descs[0].lmax) * descs[0].channels;
+    float *fb[2] = {reinterpret_cast<float *>(wb + W.f0), reinterpret_cast<float *>(wb + W.f1)};
+    uint16_t *hb = reinterpret_cast<uint16_t *>(wb + W.hb);
+    const void *x = h;
+    for (int l = 0; l < n_layers; ++l) {
+        const int k = cutoff_index(S.ncut, S.cut, descs[l].cutoff);
+        float *y = l + 1 == n_layers ? out : fb[l & 1];
+        st = e2v2_attn_forward(&descs[l], pos, x, &weights[l], start, list_len(k), list_idx(k), order, n, y,
+                               wb + W.lws, W.lws_bytes, stream);
+        if (st != E2V2_OK) return st;
+        if (l + 1 < n_layers) {
+            if (bf) {
+                e = launch_f32_to_bf16(y, hb, feat, stream);
+                if (e != hipSuccess) return hip_fail(e, "bf16 conversion kernel");
+                x = hb;
+            } else {
+                x = y;
+            }
+        }
+    }
+    if (rebuild) {
+        policy->steps_since_rebuild = 0;
+        policy->rebuilds += 1;
+    }
+    policy->rebuilt = rebuild ? 1 : 0;
+    policy->steps_since_rebuild += 1;
+    return E2V2_OK;
+}
+
+}  // extern "C"

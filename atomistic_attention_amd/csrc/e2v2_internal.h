@@ -533,6 +533,10 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
                                   int32_t *nbr_len, int32_t *order_out, hipStream_t stream);
 hipError_t launch_neighbors_scan(int n, void *ws, int32_t *nbr_start, int32_t *nbr_len, int64_t *nnz_dev,
                                  hipStream_t stream);
+hipError_t launch_filter_rows(const float *pos, int n, float cutoff, const int32_t *start, const int32_t *len,
+                              const int32_t *idx, int32_t *out_len, int32_t *out_idx, hipStream_t stream);
+hipError_t launch_max_disp2(const float *pos, const float *ref, int n, double *out, hipStream_t stream);
+hipError_t launch_f32_to_bf16(const float *x, uint16_t *y, long long count, hipStream_t stream);
 hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, void *ws, int32_t *nbr_start,
                                  int32_t *nbr_len, int32_t *nbr_idx, hipStream_t stream);
 size_t neighbors_ws_bytes(int n, int K);

@@ -735,8 +735,96 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
     if (lane == 0) nbr_len[i] = len;
 }
 
+// ---------------------------------------------------------------- list maintenance
+// Between rebuilds a model reuses the topology (Tessera article, neighbour reuse):
+// lists at smaller cutoffs are the entries of the largest-cutoff list that pass
+// the same fp64 predicate, and the rebuild rule needs the largest displacement
+// since the last rebuild.
+constexpr int kFilterWaves = 4;
+
+// One wave per row: entries j in [0, n) with d2 < rc2, kept in order (ballot
+// compaction), the rest of the row's range set to -1.  A kept entry moves only to
+// an earlier slot of its row, after its chunk has been read, so out may alias in.
+__global__ __launch_bounds__(64 * kFilterWaves) void k_filter_rows(const float *__restrict__ pos, int n, double rc2,
+                                                                   const int32_t *start, const int32_t *len,
+                                                                   const int32_t *idx, int32_t *out_len,
+                                                                   int32_t *out_idx)
+{
+    const int lane = threadIdx.x & 63;
+    const long long i = (long long)blockIdx.x * kFilterWaves + (threadIdx.x >> 6);
+    if (i >= n) return;
+    const long long s0 = start[i];
+    const int L = len[i] > 0 ? len[i] : 0;
+    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    int kept = 0;
+    for (int base = 0; base < L; base += 64) {
+        const int x = base + lane;
+        int j = -1;
+        bool keep = false;
+        if (x < L) {
+            j = idx[s0 + x];
+            if (j >= 0 && j < n) keep = d2_of(pos, xi, yi, zi, j) < rc2;
+        }
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(keep);
+        const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+        if (keep) out_idx[s0 + kept + before] = j;
+        kept += __popcll(m);
+    }
+    for (int x = kept + lane; x < L; x += 64) out_idx[s0 + x] = -1;
+    if (lane == 0) out_len[i] = kept;
+}
+
+// Largest (dx*dx + dy*dy) + dz*dz over atoms, fp64 (dx = x - x_ref of fp32 values is
+// exact), a non-finite value counting as +inf; *out must hold 0 beforehand.  The
+// bit patterns of non-negative doubles order like their values, so blocks combine
+// with an integer atomic max.
+__global__ __launch_bounds__(256) void k_max_disp2(const float *__restrict__ pos, const float *__restrict__ ref, int n,
+                                                   unsigned long long *out)
+{
+    __shared__ double sm[4];
+    double m = 0.0;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+        const double dx = (double)pos[3 * i] - (double)ref[3 * i];
+        const double dy = (double)pos[3 * i + 1] - (double)ref[3 * i + 1];
+        const double dz = (double)pos[3 * i + 2] - (double)ref[3 * i + 2];
+        const double xx = dx * dx, yy = dy * dy, zz = dz * dz;
+        double d2 = (xx + yy) + zz;
+        if (!(d2 <= 1.7976931348623157e308)) d2 = INFINITY;   // NaN and inf
+        m = d2 > m ? d2 : m;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        const double v = __shfl_xor(m, o, 64);
+        m = v > m ? v : m;
+    }
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w) m = sm[w] > m ? sm[w] : m;
+        atomicMax(out, (unsigned long long)__double_as_longlong(m));
+    }
+}
+
 // ---------------------------------------------------------------- host launchers
 static inline unsigned nblk(long long n, int b) { return (unsigned)((n + b - 1) / b); }
+
+hipError_t launch_filter_rows(const float *pos, int n, float cutoff, const int32_t *start, const int32_t *len,
+                              const int32_t *idx, int32_t *out_len, int32_t *out_idx, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    const double rc2 = (double)cutoff * (double)cutoff;
+    k_filter_rows<<<nblk(n, kFilterWaves), 64 * kFilterWaves, 0, stream>>>(pos, n, rc2, start, len, idx, out_len,
+                                                                           out_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_max_disp2(const float *pos, const float *ref, int n, double *out, hipStream_t stream)
+{
+    hipError_t e = hipMemsetAsync(out, 0, sizeof(double), stream);
+    if (e != hipSuccess || n <= 0) return e;
+    const unsigned nb = (unsigned)std::min<long long>(1024, ((long long)n + 255) / 256);
+    k_max_disp2<<<nb, 256, 0, stream>>>(pos, ref, n, reinterpret_cast<unsigned long long *>(out));
+    return hipGetLastError();
+}
 
 hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, void *ws, size_t,
                                   int32_t *nbr_len, int32_t *order_out, hipStream_t stream)

@@ -15,6 +15,8 @@
 // weights out as that instruction's A fragments.
 #include "e2v2_internal.h"
 
+#include <algorithm>
+
 namespace e2v2 {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -102,6 +104,27 @@ hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, i
     }
     const int threads = (C / 16) * (C / 32) * 64;
     k_pack_wt<<<dim3((unsigned)((threads + 255) / 256), (unsigned)count), 256, 0, stream>>>(pj, C);
+    return hipGetLastError();
+}
+
+// fp32 -> bf16 (nearest, ties to even), 4 values per thread; count % 4 == 0.
+// The features a layer writes become the next layer's bf16 input.
+__global__ __launch_bounds__(256) void k_f32_to_bf16(const float4 *__restrict__ x, uint2 *__restrict__ y, long long n4)
+{
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+        const float4 v = x[i];
+        y[i] = make_uint2(uint32_t(f_to_bf16(v.x)) | (uint32_t(f_to_bf16(v.y)) << 16),
+                          uint32_t(f_to_bf16(v.z)) | (uint32_t(f_to_bf16(v.w)) << 16));
+    }
+}
+
+hipError_t launch_f32_to_bf16(const float *x, uint16_t *y, long long count, hipStream_t stream)
+{
+    if (count <= 0) return hipSuccess;
+    if (count % 4 != 0) return hipErrorInvalidValue;
+    const long long n4 = count / 4;
+    const unsigned nb = (unsigned)std::min<long long>(4096, (n4 + 255) / 256);
+    k_f32_to_bf16<<<nb, 256, 0, stream>>>(reinterpret_cast<const float4 *>(x), reinterpret_cast<uint2 *>(y), n4);
     return hipGetLastError();
 }
 

@@ -229,7 +229,7 @@ class StackConfig:
 
 STACKS = {
     "s1": StackConfig("s1", "c1", 256, (5.0, 5.0, 5.0, 8.0), 256, 2001, 16, 0.005),
-    "s2": StackConfig("s2", "c3", 4000, (5.0, 5.0, 5.0, 8.0), 256, 2002, 16, 0.005),
+    "s2": StackConfig("s2", "c3", 2000, (5.0, 5.0, 5.0, 8.0), 256, 2002, 3, 0.005),
     "s4": StackConfig("s4", "c4", 32768, (5.0, 5.0, 5.0, 8.0), 256, 2004, 100, 0.005),
 }
 

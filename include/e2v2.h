@@ -215,6 +215,81 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Lists reused between rebuilds (Tessera article, neighbour reuse: the topology
+ * is kept for several steps while distances come from the latest coordinates;
+ * the short-range lists are taken from the long-range one).
+ *
+ * e2v2_filter_neighbors keeps, in each row i of a list in the layout of
+ * e2v2_build_neighbors, the entries j in [0, n) with d2 < cutoff^2 -- the fp64
+ * predicate of e2v2_build_neighbors, evaluated at `pos` -- in their order.
+ * out_len[i] receives the count; out_idx[nbr_start[i] .. + out_len[i]) the
+ * entries, and the rest of the input row's range, up to nbr_len[i], is set to -1.
+ * Output rows start where input rows start (out_idx has the input's layout), and
+ * out_len / out_idx may be nbr_len / nbr_idx (in place).  Filtering the K-nearest
+ * list at a larger cutoff gives the list at `cutoff` exactly unless some row has
+ * more than K atoms within `cutoff`.
+ *   pos device [n][3] fp32; nbr_start, nbr_len, out_len device [n] int32;
+ *   nbr_idx, out_idx device int32 covering every row's range
+ * Limits: 0 <= n < 2^31 - 1, cutoff > 0 finite. */
+e2v2_status e2v2_filter_neighbors(const float *pos, int32_t n, float cutoff, const int32_t *nbr_start,
+                                  const int32_t *nbr_len, const int32_t *nbr_idx, int32_t *out_len,
+                                  int32_t *out_idx, hipStream_t stream);
+
+/* Largest squared displacement max_i (dx*dx + dy*dy) + dz*dz with dx = pos - ref
+ * per coordinate, in fp64 (dx is exact for fp32 inputs, each further operation
+ * rounded); a non-finite value counts as +inf, and n = 0 gives 0.
+ *   pos, ref device [n][3] fp32;  max_d2 device, one double */
+e2v2_status e2v2_max_displacement2(const float *pos, const float *ref, int32_t n, double *max_d2,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * A stack of layers over a moving system (Tessera article: three short-range
+ * layers with a 5 A cutoff and one long-range layer with 8 A; the neighbour graph
+ * rebuilt every 10 steps, or earlier, by a global synchronisation, when an atom
+ * has moved more than 0.25 A).  One call is one model step at positions `pos`:
+ *   1. Rebuild decision: on the first call (steps_since_rebuild < 0), when
+ *      steps_since_rebuild >= rebuild_every, or when e2v2_max_displacement2(pos,
+ *      positions at the last rebuild) > (double)max_displacement^2 (or is not
+ *      finite).  The displacement test reads one value back and synchronises
+ *      `stream`.
+ *   2. On a rebuild: the K-nearest list at the largest layer cutoff
+ *      (e2v2_build_neighbors), then for every smaller cutoff the entries of that
+ *      list within it (e2v2_filter_neighbors), both at `pos`, which becomes the
+ *      reference.
+ *   3. Layers l = 0 .. n_layers - 1 in order: e2v2_attn_forward with descs[l],
+ *      weights[l] and the list of descs[l].cutoff at the current positions, on h
+ *      (l = 0) or the previous layer's output: fp32 storage takes it as written,
+ *      bf16 storage rounds it to bf16 (nearest, ties to even).  The last layer
+ *      writes out.
+ * Between rebuilds the lists are reused as they are: an atom listed at the last
+ * rebuild stays a neighbour, with its current distance and direction.
+ *   descs, weights   host arrays [n_layers] (1..16); every layer has the same lmax,
+ *                    channels and storage, since features flow from layer to layer
+ *   h                device [n][(lmax+1)^2][C] storage dtype
+ *   out              device [n][(lmax+1)^2][C] fp32
+ *   max_neighbors    K (1..4096) of the list at the largest cutoff
+ *   policy           host; read and updated by every call
+ *   state            device, >= e2v2_stack_state_bytes(...): the lists, the
+ *                    reference positions and the target order, kept from call to
+ *                    call; the caller leaves it untouched during a run
+ *   workspace        device scratch, >= e2v2_stack_workspace_bytes(...)
+ * Errors as for the calls above; on an error the policy is left unchanged. */
+typedef struct {
+    int32_t rebuild_every;        /* rebuild when this many steps have passed since the last one (10) */
+    float max_displacement;       /* rebuild earlier when an atom moved more than this, A (0.25) */
+    int32_t steps_since_rebuild;  /* state: steps since the last rebuild; negative forces one (start at -1) */
+    int32_t rebuilt;              /* out: 1 if this call rebuilt the lists, else 0 */
+    int64_t rebuilds;             /* out: rebuilds so far (the caller sets 0 at the start of a run) */
+} e2v2_rebuild_policy;
+
+size_t e2v2_stack_state_bytes(int32_t n_layers, const e2v2_layer_desc *descs, int32_t n, int32_t max_neighbors);
+size_t e2v2_stack_workspace_bytes(int32_t n_layers, const e2v2_layer_desc *descs, int32_t n, int32_t max_neighbors);
+e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, const e2v2_weights *weights,
+                               const float *pos, const void *h, int32_t n, int32_t max_neighbors,
+                               e2v2_rebuild_policy *policy, void *state, size_t state_bytes, float *out,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Host-side tables (no GPU needed). */
 int32_t e2v2_num_paths(int32_t lmax);   /* 1, 5, 15, 34 for lmax 0..3; -1 if out of range */
 /* li_lf_lo: host [n_paths][3]. */

@@ -25,7 +25,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "e2v2.h")).read()
-    declared = set(re.findall(r"\b(e2v2_[a-z_]+)\s*\(", hdr))
+    declared = set(re.findall(r"\b(e2v2_[a-z0-9_]+)\s*\(", hdr))
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
