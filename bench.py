@@ -13,7 +13,11 @@ times, the streaming kernel's achieved algorithmic bandwidth against the HBM
 peak (roofline), and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host (cpu_baseline).
 
-    python bench.py [--steps K] [--warmup W] [--config c4] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config c4] [--no-cpu-baseline] [--no-stack]
+
+config.stack reports the model level: steps/s of the four-layer stack (three 5 A
+layers, one 8 A layer) with neighbour reuse on the same system moving by a random
+walk (e2v2_stack_forward).
 """
 from __future__ import annotations
 
@@ -107,6 +111,40 @@ def cpu_baseline(wl, budget_targets: int | None = None) -> dict:
                       f"tensor products one thread"}
 
 
+def stack_bench(B, W, torch, steps: int = 60, warmup: int = 10) -> dict:
+    """Model-level steps/s of the four-layer stack (5, 5, 5, 8 A) on the 32,768-atom
+    system moving by a random walk: every call is one model step with the rebuild
+    rule (10 steps, or a move of more than 0.25 A) applied by the library."""
+    st = W.make_stack("s4", steps=warmup + steps)
+    dt = torch.bfloat16 if st.base.storage == "bf16" else torch.float32
+    descs, weights = [], []
+    for wl in st.layers:
+        c = wl.cfg
+        descs.append(B.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, dt))
+        weights.append(W.device_arrays(wl)["weights"])
+    run = B.StackRun(descs, weights, st.cfg.n, st.cfg.max_neighbors)
+    h = W.device_arrays(st.layers[0])["h"]
+    traj = [torch.from_numpy(np.ascontiguousarray(p, dtype=np.float32)).cuda() for p in st.traj]
+    out = torch.empty(st.h0.shape, dtype=torch.float32, device="cuda")
+    for t in range(warmup):
+        run.e2v2_stack_forward(traj[t], h, out=out)
+    torch.cuda.synchronize()
+    r0 = run.policy.rebuilds
+    t0 = time.perf_counter()
+    for t in range(warmup, warmup + steps):
+        run.e2v2_stack_forward(traj[t], h, out=out)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    c = st.base
+    return {"model": f"{len(st.layers)} layers, cutoffs {list(st.cfg.cutoffs)} A, the 8 A list capped at K="
+                     f"{st.cfg.max_neighbors} and the 5 A lists filtered from it; l_max={c.lmax}, C={c.channels}, "
+                     f"{c.heads} heads, {c.n_rbf} RBFs, {c.storage} storage",
+            "atoms": st.cfg.n, "steps": steps, "ms_per_step": ms, "steps_per_s": 1e3 / ms,
+            "rebuilds": int(run.policy.rebuilds - r0),
+            "rebuild_rule": "every 10 steps, or when an atom moved more than 0.25 A since the last rebuild",
+            "trajectory": f"random walk, N(0, {st.cfg.sigma}^2) A per coordinate and step, synthetic"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +152,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the four-layer stack measurement")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: 3 layer forwards, then 3 plain device copies of 1 GiB "
                          "(the copies calibrate the counters' byte units); prints no JSON")
@@ -299,6 +338,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_stack:
+        rec["config"]["stack"] = stack_bench(B, W, torch)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(rec), flush=True)

@@ -170,3 +170,47 @@ def test_eaas_argument_errors(lib):
 def test_status_strings(lib):
     assert lib.e2v2_status_string(0) == b"ok"
     assert lib.e2v2_status_string(2) == b"insufficient neighbour capacity"
+
+
+def test_reuse_argument_errors(lib):
+    """Neighbour filter and displacement: argument errors come before any launch."""
+    flt = lambda n=10, rc=5.0, pos=FAKE, p=FAKE: lib.e2v2_filter_neighbors(pos, n, rc, p, p, p, p, p, None)
+    assert flt(n=-1) == B.E2V2_ERR_ARG and flt(rc=0.0) == B.E2V2_ERR_ARG and flt(rc=float("inf")) == B.E2V2_ERR_ARG
+    assert flt(pos=None) == B.E2V2_ERR_ARG and flt(p=FAKE_MIS) == B.E2V2_ERR_ARG
+    assert flt(n=0) == B.E2V2_OK
+    dsp = lambda n=10, pos=FAKE, out=FAKE: lib.e2v2_max_displacement2(pos, pos, n, out, None)
+    assert dsp(n=-1) == B.E2V2_ERR_ARG and dsp(pos=None) == B.E2V2_ERR_ARG and dsp(out=None) == B.E2V2_ERR_ARG
+    assert dsp(pos=FAKE_MIS) == B.E2V2_ERR_ARG
+
+
+def test_stack_argument_errors(lib):
+    """The stack checks layer shapes, K, the policy and buffer sizes before anything
+    runs, and leaves the policy unchanged on an error."""
+    descs = (B.LayerDesc * 4)(*[_desc(cutoff=c) for c in (5.0, 5.0, 5.0, 8.0)])
+    ws = (B.Weights * 4)(*[B.Weights(*([FAKE] * 7)) for _ in range(4)])
+    n, K = 10, 16
+    sb = lib.e2v2_stack_state_bytes(4, descs, n, K)
+    wb = lib.e2v2_stack_workspace_bytes(4, descs, n, K)
+    assert sb > 0 and wb > 0
+    pol = B.RebuildPolicy(10, 0.25, -1, 0, 0)
+
+    def call(L=4, d=descs, w=ws, n=n, K=K, policy=pol, state=FAKE, s=sb, out=FAKE, work=FAKE, b=wb):
+        return lib.e2v2_stack_forward(L, d, w, FAKE, FAKE, n, K, ctypes.byref(policy) if policy is not None else None,
+                                      state, s, out, work, b, None)
+    assert call(L=0) == B.E2V2_ERR_ARG and call(L=17) == B.E2V2_ERR_ARG
+    assert call(K=0) == B.E2V2_ERR_ARG and call(K=5000) == B.E2V2_ERR_ARG
+    assert call(policy=None) == B.E2V2_ERR_ARG
+    assert call(policy=B.RebuildPolicy(0, 0.25, -1, 0, 0)) == B.E2V2_ERR_ARG
+    assert call(policy=B.RebuildPolicy(10, float("nan"), -1, 0, 0)) == B.E2V2_ERR_ARG
+    assert call(s=sb - 1) == B.E2V2_ERR_ARG and call(b=wb - 1) == B.E2V2_ERR_ARG
+    assert call(state=None) == B.E2V2_ERR_ARG and call(out=FAKE_MIS) == B.E2V2_ERR_ARG
+    mixed = (B.LayerDesc * 2)(_desc(), _desc(lmax=1))
+    assert call(L=2, d=mixed) == B.E2V2_ERR_ARG
+    bad = (B.LayerDesc * 2)(_desc(), _desc(heads=3))
+    assert call(L=2, d=bad) != B.E2V2_OK
+    assert (pol.steps_since_rebuild, pol.rebuilt, pol.rebuilds) == (-1, 0, 0)
+    assert call(n=0) == B.E2V2_OK
+    # one distinct cutoff needs one list, two need two
+    one = (B.LayerDesc * 2)(_desc(cutoff=5.0), _desc(cutoff=5.0))
+    two = (B.LayerDesc * 2)(_desc(cutoff=5.0), _desc(cutoff=8.0))
+    assert lib.e2v2_stack_state_bytes(2, two, 1000, 64) - lib.e2v2_stack_state_bytes(2, one, 1000, 64) >= 1000 * 65 * 4
