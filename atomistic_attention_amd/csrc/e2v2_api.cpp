@@ -843,7 +843,7 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
         policy->rebuilds += 1;
     }
     policy->rebuilt = rebuild ? 1 : 0;
-    policy->steps_since_rebuild += 1;
+    if (policy->steps_since_rebuild < INT32_MAX) policy->steps_since_rebuild += 1;
     return E2V2_OK;
 }
 
