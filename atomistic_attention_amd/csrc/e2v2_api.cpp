@@ -443,7 +443,7 @@ namespace {
 e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,
                      const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
                      const int32_t *target_order, int32_t n, float *out, void *workspace, size_t workspace_bytes,
-                     const e2v2_taps *taps, hipStream_t stream, bool prep, bool agg)
+                     const e2v2_taps *taps, hipStream_t stream, bool prep, bool agg, uint16_t *out_bf16 = nullptr)
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
@@ -451,7 +451,10 @@ e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *
     if (n == 0) return E2V2_OK;
     if (!w) return fail(E2V2_ERR_ARG, "weights is NULL");
     const void *dev_prep[] = {pos, h, w->w_q, w->w_k, w->w_v, w->w_o, w->w_src, workspace};
-    const void *dev_agg[] = {w->w_o, w->w_rbf, w->w_tgt, nbr_start, nbr_len, nbr_idx, out, workspace};
+    // out_bf16 (bf16 storage only, used by the layer stack) replaces out
+    const void *dev_agg[] = {w->w_o, w->w_rbf, w->w_tgt, nbr_start, nbr_len, nbr_idx,
+                             out_bf16 ? (const void *)out_bf16 : (const void *)out, workspace};
+    if (out_bf16 && desc->storage != E2V2_BF16) return fail(E2V2_ERR_ARG, "a bf16 output needs bf16 storage");
     for (int part = 0; part < 2; ++part) {
         if (part == 0 && !prep) continue;
         if (part == 1 && !agg) continue;
@@ -561,6 +564,7 @@ e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *
             oa.m = mh; oa.msc = msc; oa.dmat = dmat; oa.pos4 = pos4; oa.w_tgt = w->w_tgt;
             oa.wo = reinterpret_cast<const uint4 *>(wp + (size_t)(lmax + 3) * wsz);
             oa.out = out;
+            oa.out_bf16 = out_bf16;
             oa.hhat_tap = taps ? taps->hhat : nullptr;
             oa.n = n;
             e = launch_eaas_outproj(lmax, oa, C, stream);
@@ -677,10 +681,10 @@ StackState stack_state(int L, const e2v2_layer_desc *d, int n, int K)
     return s;
 }
 
-// Scratch: neighbour build workspace, one layer workspace (the largest), two fp32
-// feature buffers and a bf16 one for the next layer's input.
+// Scratch: neighbour build workspace, one layer workspace (the largest) and two
+// feature buffers in the storage dtype for the layers' outputs.
 struct StackWs {
-    size_t nbws, nbws_bytes, lws, lws_bytes, f0, f1, hb, total;
+    size_t nbws, nbws_bytes, lws, lws_bytes, f0, f1, total;
 };
 StackWs stack_ws(int L, const e2v2_layer_desc *d, int n, int K)
 {
@@ -691,9 +695,11 @@ StackWs stack_ws(int L, const e2v2_layer_desc *d, int n, int K)
     size_t lb = 0;
     for (int l = 0; l < L; ++l) lb = std::max(lb, attn_ws(d[l], n).total);
     w.lws = o; w.lws_bytes = lb; o += al256(lb);
-    w.f0 = o; o += al256(feat * 4);
-    w.f1 = o; o += al256(L > 2 ? feat * 4 : 0);
-    w.hb = o; o += al256(d[0].storage == E2V2_BF16 ? feat * 2 : 0);
+    // the previous layer's output as the next layer's input, ping-pong: fp32 buffers
+    // for fp32 storage, bf16 buffers (written by the output kernel) for bf16
+    const size_t es = d[0].storage == E2V2_BF16 ? 2 : 4;
+    w.f0 = o; o += al256(L > 1 ? feat * es : 0);
+    w.f1 = o; o += al256(L > 2 ? feat * es : 0);
     w.total = o + 256;
     return w;
 }
@@ -817,26 +823,20 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
         if (e != hipSuccess) return hip_fail(e, "keeping the reference positions");
     }
     // 3. the layers
+    // bf16 storage: the output kernel of every layer but the last writes the next
+    // layer's bf16 input directly (the same rounding of the same fp32 value)
     const bool bf = descs[0].storage == E2V2_BF16;
-    const long long feat = (long long)n * n_comp(descs[0].lmax) * descs[0].channels;
-    float *fb[2] = {reinterpret_cast<float *>(wb + W.f0), reinterpret_cast<float *>(wb + W.f1)};
-    uint16_t *hb = reinterpret_cast<uint16_t *>(wb + W.hb);
+    char *fb[2] = {wb + W.f0, wb + W.f1};
     const void *x = h;
     for (int l = 0; l < n_layers; ++l) {
         const int k = cutoff_index(S.ncut, S.cut, descs[l].cutoff);
-        float *y = l + 1 == n_layers ? out : fb[l & 1];
-        st = e2v2_attn_forward(&descs[l], pos, x, &weights[l], start, list_len(k), list_idx(k), order, n, y,
-                               wb + W.lws, W.lws_bytes, stream);
+        const bool last = l + 1 == n_layers;
+        float *y = last ? out : (bf ? nullptr : reinterpret_cast<float *>(fb[l & 1]));
+        uint16_t *yb = (!last && bf) ? reinterpret_cast<uint16_t *>(fb[l & 1]) : nullptr;
+        st = attn_run(&descs[l], pos, x, &weights[l], start, list_len(k), list_idx(k), order, n, y, wb + W.lws,
+                      W.lws_bytes, nullptr, stream, true, true, yb);
         if (st != E2V2_OK) return st;
-        if (l + 1 < n_layers) {
-            if (bf) {
-                e = launch_f32_to_bf16(y, hb, feat, stream);
-                if (e != hipSuccess) return hip_fail(e, "bf16 conversion kernel");
-                x = hb;
-            } else {
-                x = y;
-            }
-        }
+        x = fb[l & 1];
     }
     if (rebuild) {
         policy->steps_since_rebuild = 0;

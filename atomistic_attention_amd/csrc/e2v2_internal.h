@@ -505,6 +505,7 @@ struct EaasOutArgs {
     const float *w_tgt;
     const uint4 *wo;
     float *out, *hhat_tap;
+    uint16_t *out_bf16;              // if set: the output in bf16 (nearest even) instead of out
     int n;
 };
 hipError_t launch_eaas_outproj(int L, const EaasOutArgs &a, int C, hipStream_t stream);
@@ -536,7 +537,6 @@ hipError_t launch_neighbors_scan(int n, void *ws, int32_t *nbr_start, int32_t *n
 hipError_t launch_filter_rows(const float *pos, int n, float cutoff, const int32_t *start, const int32_t *len,
                               const int32_t *idx, int32_t *out_len, int32_t *out_idx, hipStream_t stream);
 hipError_t launch_max_disp2(const float *pos, const float *ref, int n, double *out, hipStream_t stream);
-hipError_t launch_f32_to_bf16(const float *x, uint16_t *y, long long count, hipStream_t stream);
 hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, void *ws, int32_t *nbr_start,
                                  int32_t *nbr_len, int32_t *nbr_idx, hipStream_t stream);
 size_t neighbors_ws_bytes(int n, int K);

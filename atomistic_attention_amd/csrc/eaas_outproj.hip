@@ -24,7 +24,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 template <int L, int C>
 __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 4 : 1))) void eaas_outproj_kernel(const EaasOutArgs a, const EaasCoef tab)
 {
-    constexpr int NC = n_comp(L), NB = C / 16, KB = C / 32, P = path_count(L);
+    constexpr int NC = n_comp(L), KB = C / 32, P = path_count(L);
     constexpr int NDM = n_dmat(L);
     constexpr int ND = NDM > 0 ? NDM : 1;
     constexpr int NH = C >= 64 ? 2 : 1;           // input-channel halves (one for C = 32)
@@ -156,10 +156,18 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
     }
     if (nl < nvalid) {
         const long long node = node0 + nl;
+        if (a.out_bf16) {                        // the next layer's bf16 input, rounded once
 #pragma unroll
-        for (int e = 0; e < NC; ++e)
-            *reinterpret_cast<float4 *>(a.out + (node * NC + e) * C + 16 * nb + 4 * g) =
-                make_float4(acc[e][0], acc[e][1], acc[e][2], acc[e][3]);
+            for (int e = 0; e < NC; ++e)
+                *reinterpret_cast<uint2 *>(a.out_bf16 + (node * NC + e) * C + 16 * nb + 4 * g) =
+                    make_uint2(uint32_t(f_to_bf16(acc[e][0])) | (uint32_t(f_to_bf16(acc[e][1])) << 16),
+                               uint32_t(f_to_bf16(acc[e][2])) | (uint32_t(f_to_bf16(acc[e][3])) << 16));
+        } else {
+#pragma unroll
+            for (int e = 0; e < NC; ++e)
+                *reinterpret_cast<float4 *>(a.out + (node * NC + e) * C + 16 * nb + 4 * g) =
+                    make_float4(acc[e][0], acc[e][1], acc[e][2], acc[e][3]);
+        }
     }
 }
 

@@ -107,27 +107,6 @@ hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, i
     return hipGetLastError();
 }
 
-// fp32 -> bf16 (nearest, ties to even), 4 values per thread; count % 4 == 0.
-// The features a layer writes become the next layer's bf16 input.
-__global__ __launch_bounds__(256) void k_f32_to_bf16(const float4 *__restrict__ x, uint2 *__restrict__ y, long long n4)
-{
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
-        const float4 v = x[i];
-        y[i] = make_uint2(uint32_t(f_to_bf16(v.x)) | (uint32_t(f_to_bf16(v.y)) << 16),
-                          uint32_t(f_to_bf16(v.z)) | (uint32_t(f_to_bf16(v.w)) << 16));
-    }
-}
-
-hipError_t launch_f32_to_bf16(const float *x, uint16_t *y, long long count, hipStream_t stream)
-{
-    if (count <= 0) return hipSuccess;
-    if (count % 4 != 0) return hipErrorInvalidValue;
-    const long long n4 = count / 4;
-    const unsigned nb = (unsigned)std::min<long long>(4096, (n4 + 255) / 256);
-    k_f32_to_bf16<<<nb, 256, 0, stream>>>(reinterpret_cast<const float4 *>(x), reinterpret_cast<uint2 *>(y), n4);
-    return hipGetLastError();
-}
-
 hipError_t launch_proj(const ProjJob *jobs, int njobs, int n, int C, hipStream_t stream)
 {
     if (n <= 0 || njobs <= 0) return hipSuccess;
