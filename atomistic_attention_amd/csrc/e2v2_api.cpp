@@ -443,7 +443,8 @@ namespace {
 e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,
                      const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
                      const int32_t *target_order, int32_t n, float *out, void *workspace, size_t workspace_bytes,
-                     const e2v2_taps *taps, hipStream_t stream, bool prep, bool agg, uint16_t *out_bf16 = nullptr)
+                     const e2v2_taps *taps, hipStream_t stream, bool prep, bool agg, uint16_t *out_bf16 = nullptr,
+                     const uint16_t *packed_w = nullptr, bool frames_ready = false)
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
@@ -492,13 +493,15 @@ e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *
     auto wo32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_o) + l * wstride); };
     ProjJob jobs[kMaxL * kMaxL + 2 * kMaxL + 1 + 2];
     int nj = 0;
-    uint16_t *wp = reinterpret_cast<uint16_t *>(ws + L.wpack);
+    // bf16 weights as MFMA fragments: packed here, or already packed by the caller
+    // (the layer stack packs every layer's weights in one launch)
+    uint16_t *wp = packed_w ? const_cast<uint16_t *>(packed_w) : reinterpret_cast<uint16_t *>(ws + L.wpack);
     const size_t wsz = (size_t)C * C;                 // elements per packed matrix
     if (prep) {
         e = mark(0);
         if (e != hipSuccess) return hip_fail(e, "recording stage event");
         // Step 2: projections (q, k from the l = 0 block; v per component with W_V[l]).
-        if (bf) {
+        if (bf && !packed_w) {
             const uint16_t *src[2 * kMaxL + 4];
             uint16_t *dst[2 * kMaxL + 4];
             int cnt = 0;
@@ -524,6 +527,7 @@ e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *
             qa.v_tap = taps ? taps->v : nullptr;
             qa.hp_tap = taps ? taps->hprime : nullptr;
             qa.n = n;
+            qa.frames_ready = frames_ready;
             e = launch_qkv_eaas(lmax, qa, C, stream);
             if (e == hipSuccess) e = mark(1);
             if (e == hipSuccess) e = mark(2);
@@ -684,7 +688,7 @@ StackState stack_state(int L, const e2v2_layer_desc *d, int n, int K)
 // Scratch: neighbour build workspace, one layer workspace (the largest) and two
 // feature buffers in the storage dtype for the layers' outputs.
 struct StackWs {
-    size_t nbws, nbws_bytes, lws, lws_bytes, f0, f1, total;
+    size_t nbws, nbws_bytes, lws, lws_bytes, f0, f1, wpk, wpk_layer, total;
 };
 StackWs stack_ws(int L, const e2v2_layer_desc *d, int n, int K)
 {
@@ -700,6 +704,10 @@ StackWs stack_ws(int L, const e2v2_layer_desc *d, int n, int K)
     const size_t es = d[0].storage == E2V2_BF16 ? 2 : 4;
     w.f0 = o; o += al256(L > 1 ? feat * es : 0);
     w.f1 = o; o += al256(L > 2 ? feat * es : 0);
+    // bf16: every layer's weights as MFMA fragments (W_V[0..L], W_Q, W_K, W_O[0..L])
+    const size_t C = (size_t)d[0].channels;
+    w.wpk_layer = d[0].storage == E2V2_BF16 ? al256((size_t)(2 * (d[0].lmax + 1) + 2) * C * C * 2) : 0;
+    w.wpk = o; o += w.wpk_layer * (size_t)L;
     w.total = o + 256;
     return w;
 }
@@ -828,13 +836,36 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
     const bool bf = descs[0].storage == E2V2_BF16;
     char *fb[2] = {wb + W.f0, wb + W.f1};
     const void *x = h;
+    if (bf) {       // all layers' weights packed in one launch
+        const int C = descs[0].channels, lmax = descs[0].lmax;
+        const size_t wsz = (size_t)C * C;
+        const uint16_t *src[kMaxStackLayers * (2 * kMaxL + 4)];
+        uint16_t *dst[kMaxStackLayers * (2 * kMaxL + 4)];
+        int cnt = 0;
+        for (int l = 0; l < n_layers; ++l) {
+            uint16_t *base = reinterpret_cast<uint16_t *>(wb + W.wpk + (size_t)l * W.wpk_layer);
+            const e2v2_weights &wl = weights[l];
+            if (!wl.w_v || !wl.w_q || !wl.w_k || !wl.w_o) return fail(E2V2_ERR_ARG, "NULL weight pointer in layer %d", l);
+            int c = 0;
+            for (int ll = 0; ll <= lmax; ++ll) { src[cnt] = reinterpret_cast<const uint16_t *>(wl.w_v) + ll * wsz; dst[cnt++] = base + (c++) * wsz; }
+            src[cnt] = reinterpret_cast<const uint16_t *>(wl.w_q); dst[cnt++] = base + (c++) * wsz;
+            src[cnt] = reinterpret_cast<const uint16_t *>(wl.w_k); dst[cnt++] = base + (c++) * wsz;
+            for (int ll = 0; ll <= lmax; ++ll) { src[cnt] = reinterpret_cast<const uint16_t *>(wl.w_o) + ll * wsz; dst[cnt++] = base + (c++) * wsz; }
+        }
+        for (int b0 = 0; b0 < cnt; b0 += 64) {
+            e = launch_pack_weights(src + b0, dst + b0, std::min(64, cnt - b0), C, stream);
+            if (e != hipSuccess) return hip_fail(e, "weight packing kernel");
+        }
+    }
     for (int l = 0; l < n_layers; ++l) {
         const int k = cutoff_index(S.ncut, S.cut, descs[l].cutoff);
         const bool last = l + 1 == n_layers;
         float *y = last ? out : (bf ? nullptr : reinterpret_cast<float *>(fb[l & 1]));
         uint16_t *yb = (!last && bf) ? reinterpret_cast<uint16_t *>(fb[l & 1]) : nullptr;
+        // the positions, hence the D blocks in the shared layer workspace, are those of layer 0
+        const uint16_t *pk = bf ? reinterpret_cast<const uint16_t *>(wb + W.wpk + (size_t)l * W.wpk_layer) : nullptr;
         st = attn_run(&descs[l], pos, x, &weights[l], start, list_len(k), list_idx(k), order, n, y, wb + W.lws,
-                      W.lws_bytes, nullptr, stream, true, true, yb);
+                      W.lws_bytes, nullptr, stream, true, true, yb, pk, l > 0);
         if (st != E2V2_OK) return st;
         x = fb[l & 1];
     }

@@ -491,6 +491,7 @@ struct QkvEaasArgs {
     float *dmat;
     float *k_tap, *v_tap, *hp_tap;
     int n;
+    bool frames_ready;               // dmat already holds these positions' D blocks
 };
 hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t stream);
 

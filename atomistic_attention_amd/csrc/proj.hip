@@ -70,9 +70,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // W [C][C] (in, out) bf16 -> fragments: for output block nb (16 channels) and
 // contraction block kb (32 indices), lane l holds W[32 kb + 8 (l / 16) + e][16 nb + l % 16], e < 8.
+constexpr int kMaxPack = 64;          // matrices per packing launch (a whole layer stack)
 struct PackJobs {
-    const uint16_t *w[kMaxJobs];
-    uint16_t *out[kMaxJobs];
+    const uint16_t *w[kMaxPack];
+    uint16_t *out[kMaxPack];
 };
 __global__ void k_pack_wt(const PackJobs pj, int C)
 {
@@ -96,7 +97,7 @@ __global__ void k_pack_wt(const PackJobs pj, int C)
 hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, int count, int C, hipStream_t stream)
 {
     if (count <= 0) return hipSuccess;
-    if (count > kMaxJobs || C % 32 != 0) return hipErrorInvalidValue;
+    if (count > kMaxPack || C % 32 != 0) return hipErrorInvalidValue;
     PackJobs pj{};
     for (int i = 0; i < count; ++i) {
         pj.w[i] = w[i];

@@ -265,9 +265,12 @@ template <int L>
 static hipError_t launch_qkv_eaas_l(const QkvEaasArgs &a, int C, hipStream_t stream)
 {
     if constexpr (n_dmat(L) > 0) {
-        k_node_frames<L><<<dim3((unsigned)((a.n + 255) / 256)), 256, 0, stream>>>(a.pos, a.n, a.dmat, host_tables().ds);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (!a.frames_ready) {
+            k_node_frames<L><<<dim3((unsigned)((a.n + 255) / 256)), 256, 0, stream>>>(a.pos, a.n, a.dmat,
+                                                                                    host_tables().ds);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     const EaasCoef &tab = eaas_table(L);
     const dim3 grid((unsigned)((a.n + 15) / 16));

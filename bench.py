@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--config", default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the four-layer stack measurement")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="run only the four-layer stack measurement and print its record (for profiling)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: 3 layer forwards, then 3 plain device copies of 1 GiB "
                          "(the copies calibrate the counters' byte units); prints no JSON")
@@ -170,6 +172,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     B.load()
+    if args.stack_only:
+        print(json.dumps({"stack": stack_bench(B, W, torch)}), flush=True)
+        return
     wl = W.make_workload(args.config)
     cfg = wl.cfg
     d = W.device_arrays(wl)
