@@ -23,5 +23,8 @@ tests/test_oracle_*.py):
   stack.StackState (rebuild rule) pinned: trajectories with known rebuild steps
   stack.stack_step / run_stack    pinned: topology reuse on a two-atom system, rotation
                                   equivariance of the whole stack to 1e-10
+  backward.grad_h                 pinned: central finite differences of layer.layer_forward
+                                  (directional and element-wise), forward equal to
+                                  layer.layer_forward, one-neighbour and isolated-atom cases
 """
-from . import so3, layer, stack  # noqa: F401
+from . import so3, layer, stack, backward  # noqa: F401

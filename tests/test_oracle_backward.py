@@ -1,0 +1,114 @@
+"""Pins of the feature-gradient oracle (oracle/backward.py).
+
+The torch fp64 layer is checked against the numpy oracle's forward pass, and
+its reverse-mode gradient against central finite differences of the numpy
+forward pass (layer.layer_forward), so a dropped term, a wrong sign or a
+transposed weight in either place fails here.  Special cases: one neighbour
+(softmax weight 1, so q and k receive no gradient), an isolated atom (its
+gradient comes only from other targets through it as a source; with no
+neighbours on either side it is zero), an atom at the origin (l_f > 0 paths
+vanish)."""
+import numpy as np
+import pytest
+
+from oracle import backward, layer, so3
+
+LMAX, C, HEADS, R, CUT = 2, 16, 2, 8, 3.0
+
+
+def _system(seed, n=20, side=5.0, extra=()):
+    rng = np.random.default_rng(seed)
+    pos = rng.uniform(-side / 2, side / 2, (n, 3))
+    if extra:
+        pos = np.concatenate([pos, np.asarray(extra, dtype=np.float64)], axis=0)
+    pos = pos.astype(np.float32).astype(np.float64)
+    nc = (LMAX + 1) ** 2
+    P = len(so3.paths(LMAX))
+    W = dict(
+        w_q=rng.standard_normal((C, C)) / np.sqrt(C),
+        w_k=rng.standard_normal((C, C)) / np.sqrt(C),
+        w_v=rng.standard_normal((LMAX + 1, C, C)) / np.sqrt(C),
+        w_o=rng.standard_normal((LMAX + 1, C, C)) / np.sqrt(C),
+        w_rbf=rng.standard_normal((R, HEADS)) / np.sqrt(R),
+        w_src=rng.standard_normal((P, C)) / np.sqrt(P),
+        w_tgt=rng.standard_normal((P, C)) / np.sqrt(P))
+    h = rng.standard_normal((pos.shape[0], nc, C))
+    g = rng.standard_normal((pos.shape[0], nc, C))
+    return pos, h, W, g
+
+
+def _fwd_np(pos, h, W, rows):
+    return layer.layer_forward(pos, h, **W, lmax=LMAX, heads=HEADS, cutoff=CUT, rows=rows)["out"]
+
+
+def _grad(pos, h, W, g, rows):
+    return backward.grad_h(pos, h, **W, g=g, lmax=LMAX, heads=HEADS, cutoff=CUT, rows=rows)
+
+
+def test_torch_forward_matches_numpy_oracle():
+    import torch
+    pos, h, W, _ = _system(1, extra=[[0.0, 0.0, 0.0], [40.0, 0.0, 0.0]])
+    rows = layer.neighbors(pos, CUT)
+    ref = _fwd_np(pos, h, W, rows)
+    got = backward.layer_forward_torch(pos, torch.tensor(h), **W, lmax=LMAX, heads=HEADS, cutoff=CUT,
+                                       rows=rows).numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("seed", [2, 3])
+def test_gradient_matches_central_differences(seed):
+    """Directional derivatives along random u: (L(h + eps u) - L(h - eps u)) / 2 eps of the
+    numpy forward pass against <dL/dh, u>; also along u restricted to the l = 0 block
+    (the only block feeding q and k) and to the l = 2 block."""
+    pos, h, W, g = _system(seed, extra=[[0.0, 0.0, 0.0]])
+    rows = layer.neighbors(pos, CUT)
+    assert min(r.size for r in rows[:-1]) >= 1 and max(r.size for r in rows) >= 4
+    gr = _grad(pos, h, W, g, rows)
+    rng = np.random.default_rng(seed + 100)
+    eps = 1e-5
+    masks = [np.ones_like(h), np.zeros_like(h), np.zeros_like(h)]
+    masks[1][:, 0, :] = 1.0
+    masks[2][:, 4:9, :] = 1.0
+    for mk in masks:
+        u = rng.standard_normal(h.shape) * mk
+        lp = np.sum(g * _fwd_np(pos, h + eps * u, W, rows))
+        lm = np.sum(g * _fwd_np(pos, h - eps * u, W, rows))
+        fd = (lp - lm) / (2 * eps)
+        an = float(np.sum(gr * u))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (fd, an)
+
+
+def test_single_entries_by_central_differences():
+    """Element-wise finite differences on a few entries of l = 0, 1, 2 at several atoms."""
+    pos, h, W, g = _system(4)
+    rows = layer.neighbors(pos, CUT)
+    gr = _grad(pos, h, W, g, rows)
+    eps = 1e-5
+    for (a, e, c) in [(0, 0, 3), (5, 0, 15), (7, 2, 0), (11, 6, 9), (19, 8, 7)]:
+        d = np.zeros_like(h)
+        d[a, e, c] = eps
+        fd = (np.sum(g * _fwd_np(pos, h + d, W, rows)) - np.sum(g * _fwd_np(pos, h - d, W, rows))) / (2 * eps)
+        assert abs(fd - gr[a, e, c]) <= 1e-7 * max(1.0, abs(gr[a, e, c])), (a, e, c, fd, gr[a, e, c])
+
+
+def test_one_neighbour_pair_has_no_query_key_gradient():
+    """Two atoms within the cutoff, each the other's only neighbour: the softmax
+    weight is 1 whatever q and k are, so the gradient does not depend on W_Q, W_K,
+    and equals that with W_Q = W_K = 0."""
+    pos, h, W, g = _system(5, n=0, extra=[[0.3, -0.2, 0.1], [1.1, 0.4, -0.9]])
+    rows = layer.neighbors(pos, CUT)
+    assert [r.tolist() for r in rows] == [[1], [0]]
+    g1 = _grad(pos, h, W, g, rows)
+    W0 = dict(W, w_q=np.zeros((C, C)), w_k=np.zeros((C, C)))
+    g0 = _grad(pos, h, W0, g, rows)
+    assert np.max(np.abs(g1 - g0)) <= 1e-13 * np.max(np.abs(g1))
+    assert np.max(np.abs(g1)) > 0
+
+
+def test_isolated_atom_has_zero_gradient():
+    pos, h, W, g = _system(6, extra=[[50.0, 50.0, 50.0]])
+    rows = layer.neighbors(pos, CUT)
+    assert rows[-1].size == 0
+    gr = _grad(pos, h, W, g, rows)
+    assert np.all(gr[-1] == 0.0)
+    assert np.max(np.abs(gr[:-1])) > 0
