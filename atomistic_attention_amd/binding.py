@@ -23,7 +23,8 @@ EXPORTS = [
     "e2v2_attn_workspace_bytes", "e2v2_num_paths",
     "e2v2_path_table", "e2v2_eaas_coefficients", "e2v2_alignment_wigner", "e2v2_status_string",
     "e2v2_last_error", "e2v2_filter_neighbors", "e2v2_max_displacement2", "e2v2_stack_state_bytes",
-    "e2v2_stack_workspace_bytes", "e2v2_stack_forward",
+    "e2v2_stack_workspace_bytes", "e2v2_stack_forward", "e2v2_layer_backward_workspace_bytes",
+    "e2v2_layer_backward",
 ]
 
 
@@ -105,6 +106,11 @@ def load(path: str = LIB_PATH):
     lib.e2v2_stack_forward.argtypes = [i32, ctypes.POINTER(LayerDesc), ctypes.POINTER(Weights), vp, vp, i32, i32,
                                        ctypes.POINTER(RebuildPolicy), vp, sz, vp, vp, sz, vp]
     lib.e2v2_stack_forward.restype = ctypes.c_int
+    lib.e2v2_layer_backward_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32]
+    lib.e2v2_layer_backward_workspace_bytes.restype = sz
+    lib.e2v2_layer_backward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, vp,
+                                        i32, vp, vp, vp, sz, vp]
+    lib.e2v2_layer_backward.restype = ctypes.c_int
     lib.e2v2_status_string.argtypes = [ctypes.c_int]
     lib.e2v2_status_string.restype = ctypes.c_char_p
     lib.e2v2_last_error.argtypes = []
@@ -317,6 +323,38 @@ def e2v2_attn_aggregate(desc: LayerDesc, weights: dict, nbr_start, nbr_len, nbr_
                                    _ptr(nbr_idx), _ptr(target_order), nbr_start.shape[0], _ptr(out),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def backward_workspace_bytes(desc: LayerDesc, n: int) -> int:
+    return int(load().e2v2_layer_backward_workspace_bytes(ctypes.byref(desc), n))
+
+
+def e2v2_layer_backward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len, nbr_idx, grad_out,
+                        grad_h=None, workspace=None, stream=None,
+                        target_order: torch.Tensor | None = None) -> torch.Tensor:
+    """dL/dh for L = sum(grad_out * layer(h)) (fp32 storage, symmetric neighbour list)."""
+    lib = load()
+    n = pos.shape[0]
+    _dev(pos, torch.float32, "pos")
+    _dev(h, torch.float32, "h")
+    _dev(grad_out, torch.float32, "grad_out")
+    if tuple(grad_out.shape) != tuple(h.shape):
+        raise ValueError(f"grad_out shape {tuple(grad_out.shape)} != h shape {tuple(h.shape)}")
+    for t, nm in ((nbr_start, "nbr_start"), (nbr_len, "nbr_len"), (nbr_idx, "nbr_idx")):
+        _dev(t, torch.int32, nm)
+    if target_order is not None:
+        _dev(target_order, torch.int32, "target_order")
+    w = _weights(weights, torch.float32)
+    if grad_h is None:
+        grad_h = torch.empty(h.shape, dtype=torch.float32, device=h.device)
+    _dev(grad_h, torch.float32, "grad_h")
+    wsb = backward_workspace_bytes(desc, n)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=h.device)
+    _check(lib.e2v2_layer_backward(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), _ptr(nbr_start),
+                                   _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), n, _ptr(grad_out),
+                                   _ptr(grad_h), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return grad_h
 
 
 # ------------------------------------------------------------------ neighbour reuse and the stack

@@ -636,6 +636,125 @@ e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, con
 }  // extern "C"
 
 // ============================================================================
+// Gradient of the layer with respect to its input features (fp32 storage)
+// ============================================================================
+namespace {
+// The forward workspace (q, k, v, h', frames) followed by the gradient buffers.
+struct BwdWs {
+    size_t fwd, gbuf, dm, mx, rz, dd, dq, dk, total;
+};
+BwdWs bwd_ws(const e2v2_layer_desc &d, int n)
+{
+    const size_t N = (size_t)n, C = (size_t)d.channels, NC = (size_t)n_comp(d.lmax), H = (size_t)d.heads;
+    BwdWs w{};
+    size_t o = 0;
+    w.fwd = o; o += al256(attn_ws(d, n).total);
+    w.gbuf = o; o += al256(N * NC * C * 4);      // dL/dhhat, then dL/dh'
+    w.dm = o; o += al256(N * NC * C * 4);
+    w.mx = o; o += al256(N * H * 4);
+    w.rz = o; o += al256(N * H * 4);
+    w.dd = o; o += al256(N * H * 4);
+    w.dq = o; o += al256(N * C * 4);
+    w.dk = o; o += al256(N * C * 4);
+    w.total = o + 256;
+    return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t n)
+{
+    if (!desc || n < 0 || desc->lmax < 0 || desc->lmax > kMaxL || desc->channels <= 0 || desc->heads <= 0) return 0;
+    return bwd_ws(*desc, n).total;
+}
+
+e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
+                                const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
+                                const int32_t *target_order, int32_t n, const float *grad_out, float *grad_h,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    e2v2_status st = check_desc(desc);
+    if (st != E2V2_OK) return st;
+    if (desc->storage != E2V2_FP32) return fail(E2V2_ERR_UNSUPPORTED, "the feature gradient needs fp32 storage");
+    if (n < 0) return fail(E2V2_ERR_ARG, "n < 0");
+    if (n == 0) return E2V2_OK;
+    if (!w) return fail(E2V2_ERR_ARG, "weights is NULL");
+    for (const void *p : {(const void *)pos, (const void *)h, (const void *)w->w_q, (const void *)w->w_k,
+                          (const void *)w->w_v, (const void *)w->w_o, (const void *)w->w_rbf, (const void *)w->w_src,
+                          (const void *)w->w_tgt, (const void *)nbr_start, (const void *)nbr_len, (const void *)nbr_idx,
+                          (const void *)grad_out, (const void *)grad_h, (const void *)workspace}) {
+        if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
+        if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    }
+    if (target_order && !aligned16(target_order)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    const BwdWs B = bwd_ws(*desc, n);
+    if (workspace_bytes < B.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, B.total);
+    char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+    const AttnWs F = attn_ws(*desc, n);
+    // Steps 2-3 of the forward pass: q, k, v, h' and the per-node frames.
+    st = attn_run(desc, pos, h, w, nullptr, nullptr, nullptr, nullptr, n, nullptr, ws + B.fwd, F.total, nullptr,
+                  stream, true, false);
+    if (st != E2V2_OK) return st;
+    char *fw = ws + B.fwd;          // 256-aligned already, so attn_run used the same base
+    const float *q = reinterpret_cast<const float *>(fw + F.q);
+    const float *k = reinterpret_cast<const float *>(fw + F.k);
+    float *v = reinterpret_cast<float *>(fw + F.v);          // reused for dL/dv
+    const float *hp = reinterpret_cast<const float *>(fw + F.hp);
+    const float4 *pos4 = reinterpret_cast<const float4 *>(fw + F.pos4);
+    float *gbuf = reinterpret_cast<float *>(ws + B.gbuf);
+    float *dm = reinterpret_cast<float *>(ws + B.dm);
+    float *dq = reinterpret_cast<float *>(ws + B.dq);
+    float *dk = reinterpret_cast<float *>(ws + B.dk);
+    const int L = desc->lmax, C = desc->channels, NC = n_comp(L);
+    const size_t wstride = (size_t)C * C * 4;
+    auto wsel = [&](const void *base, int l) {
+        return reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + l * wstride);
+    };
+    ProjJob jobs[kMaxL * kMaxL + 2 * kMaxL + 1];
+    int nj = 0;
+    // Step 6 adjoint: dL/dhhat^l = g^l W_O[l]^T.
+    for (int l = 0; l <= L; ++l)
+        for (int m = 0; m < 2 * l + 1; ++m)
+            jobs[nj++] = ProjJob{grad_out, (long long)NC * C, wsel(w->w_o, l), gbuf, (long long)NC * C, l * l + m, 1, 0};
+    hipError_t e = launch_proj(jobs, nj, n, C, stream);
+    if (e != hipSuccess) return hip_fail(e, "output projection adjoint");
+    // Step 5 adjoint: dL/dm = EAAS^T with the target's own frame and w_tgt.
+    e = launch_eaas_adjoint(L, pos, gbuf, w->w_tgt, n, C, dm, stream);
+    if (e != hipSuccess) return hip_fail(e, "target coupling adjoint");
+    // Step 4 adjoint: dq (target pass), dL/dh' and dk (source pass).
+    AttnBwdArgs a{};
+    a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dm = dm;
+    a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
+    a.w_rbf = w->w_rbf;
+    a.mx = reinterpret_cast<float *>(ws + B.mx);
+    a.rz = reinterpret_cast<float *>(ws + B.rz);
+    a.dd = reinterpret_cast<float *>(ws + B.dd);
+    a.dq = dq; a.dk = dk; a.dhp = gbuf;
+    a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
+    e = launch_attn_bwd(L, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention adjoint");
+    // Step 3 adjoint: dL/dv = EAAS^T with the source's own frame and w_src.
+    e = launch_eaas_adjoint(L, pos, gbuf, w->w_src, n, C, v, stream);
+    if (e != hipSuccess) return hip_fail(e, "source coupling adjoint");
+    // Step 2 adjoint: dh^l = dv^l W_V[l]^T, then dh^0 += dq W_Q^T and dh^0 += dk W_K^T
+    // (launches in stream order: the accumulating jobs write the rows of the first).
+    nj = 0;
+    for (int l = 0; l <= L; ++l)
+        for (int m = 0; m < 2 * l + 1; ++m)
+            jobs[nj++] = ProjJob{v, (long long)NC * C, wsel(w->w_v, l), grad_h, (long long)NC * C, l * l + m, 1, 0};
+    e = launch_proj(jobs, nj, n, C, stream);
+    ProjJob jq{dq, (long long)C, reinterpret_cast<const float *>(w->w_q), grad_h, (long long)NC * C, 0, 1, 1};
+    ProjJob jk{dk, (long long)C, reinterpret_cast<const float *>(w->w_k), grad_h, (long long)NC * C, 0, 1, 1};
+    if (e == hipSuccess) e = launch_proj(&jq, 1, n, C, stream);
+    if (e == hipSuccess) e = launch_proj(&jk, 1, n, C, stream);
+    if (e != hipSuccess) return hip_fail(e, "input projection adjoint");
+    return E2V2_OK;
+}
+
+}  // extern "C"
+
+// ============================================================================
 // Neighbour reuse and the layer stack
 // ============================================================================
 namespace {

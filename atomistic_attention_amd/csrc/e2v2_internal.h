@@ -193,8 +193,10 @@ __host__ __device__ inline bool wigner_blocks(double x, double y, double z, cons
 // ----------------------------------------------------------------------------
 // EAAS on one channel: y = D(R) . P(D(R)^T x) with per-path weights w[p].
 // D: the node's concatenated D^1..D^L (fp32).  `dir` false (r = 0) drops the
-// l_f > 0 paths: the encoding of a zero vector is Y_0 = 1 only.
-template <int L>
+// l_f > 0 paths: the encoding of a zero vector is Y_0 = 1 only.  ADJ gives the
+// adjoint map y = D . P^T (D^T x): the same rotations, each sparse coefficient
+// carrying output component m_o back to input component m_i.
+template <int L, bool ADJ = false>
 __device__ __forceinline__ void eaas_channel(const float *__restrict__ D, const float (&x)[n_comp(L)],
                                              float (&y)[n_comp(L)], const float *w, const EaasCoef &tab,
                                              bool dir)
@@ -233,7 +235,11 @@ __device__ __forceinline__ void eaas_channel(const float *__restrict__ D, const 
                 for (int mo = -mm; mo <= mm; ++mo) {
                     if (odd && mo == 0) continue;
                     const int mi = odd ? -mo : mo;
-                    loc[lo * lo + lo + mo] = fmaf(wp * tab.c[p][mo + lo], xt[li * li + li + mi], loc[lo * lo + lo + mo]);
+                    const int eo = lo * lo + lo + mo, ei = li * li + li + mi;
+                    if constexpr (ADJ)
+                        loc[ei] = fmaf(wp * tab.c[p][mo + lo], xt[eo], loc[ei]);
+                    else
+                        loc[eo] = fmaf(wp * tab.c[p][mo + lo], xt[ei], loc[eo]);
                 }
             }
     y[0] = loc[0];
@@ -467,6 +473,8 @@ struct ProjJob {
     float *out;             // out + node*o_node_stride + comp*C
     long long o_node_stride;
     int comp;               // component index of the rows
+    int b_trans;            // 1: multiply by b^T (the adjoint of the projection)
+    int accumulate;         // 1: out += product (jobs of one launch must write disjoint rows)
 };
 // fp32 projections (fp32 storage).
 hipError_t launch_proj(const ProjJob *jobs, int njobs, int n, int C, hipStream_t stream);
@@ -530,6 +538,32 @@ struct AttnArgs {
 };
 // hp_f16s: h' is fp16 with per-node scales (else fp32).
 hipError_t launch_attn(int L, int hp_f16s, const AttnArgs &a, hipStream_t stream);
+
+// Adjoint of the EAAS coupling with the node's own encoding, fp32 in and out:
+// y = D . P^T (D^T x) per (node, channel), frames built from pos.
+hipError_t launch_eaas_adjoint(int L, const float *pos, const float *x, const float *path_w, int n, int C, float *y,
+                               hipStream_t stream);
+
+// Gradient of the streaming attention (fp32 storage).  Given dm = dL/dm (the
+// gradient of the normalised message), the target pass writes, per target i and
+// head, the running maximum mx of the log2-domain logits and rz = 1 / normaliser
+// (mx = +inf, rz = 0 for an empty row), dd = sum_j alpha_ij dalpha_ij, and dq; the
+// source pass walks row j of the same (symmetric) list as the targets i that read
+// source j and writes dhp = dL/dh' and dk.
+struct AttnBwdArgs {
+    const float *q, *k, *hp;         // [n][C], [n][C], [n][NC][C]
+    const float4 *pos4;              // [n] (x, y, z, .)
+    const float *dm;                 // [n][NC][C]
+    const int32_t *nbr_start, *nbr_len, *nbr_idx;
+    const int32_t *order;            // optional processing order of the nodes
+    const float *w_rbf;              // [R][H]
+    float *mx, *rz, *dd;             // [n][H]
+    float *dq, *dk;                  // [n][C]
+    float *dhp;                      // [n][NC][C]
+    int n, C, H, R;
+    float cutoff;
+};
+hipError_t launch_attn_bwd(int L, const AttnBwdArgs &a, hipStream_t stream);
 
 hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, void *ws, size_t ws_bytes,
                                   int32_t *nbr_len, int32_t *order_out, hipStream_t stream);

@@ -26,7 +26,7 @@ template <int L> __host__ __device__ inline int eaas_nodes_per_block(int C)
     return (256 * eaas_pairs<L>() / C) < 32 ? (256 * eaas_pairs<L>() / C) : 32;
 }
 
-template <int L, typename TX, int YF>
+template <int L, typename TX, int YF, bool ADJ = false>
 __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos, const TX *__restrict__ x,
                                                    const float *__restrict__ path_w, int n, int C,
                                                    void *__restrict__ y_, float *__restrict__ y_deq,
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void eaas_kernel(const float *__restrict__ pos
         for (int e = 0; e < NC; ++e) xv[e] = ld_elem<TX>(x, base + (size_t)e * C);
 #pragma unroll
         for (int p = 0; p < P; ++p) w[p] = path_w[p * C + c];
-        eaas_channel<L>(&sD[ln][0], xv, yv, w, tabs.eaas, sDir[ln] != 0);
+        eaas_channel<L, ADJ>(&sD[ln][0], xv, yv, w, tabs.eaas, sDir[ln] != 0);
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
             if (YF == kYBF16) {
@@ -122,6 +122,31 @@ hipError_t launch_eaas(int L, const float *pos, const void *x, int x_bf16, const
     case 1: return launch_eaas_l<1>(pos, x, x_bf16, path_w, n, C, y, y_format, y_deq, dmat_out, pos4_out, stream);
     case 2: return launch_eaas_l<2>(pos, x, x_bf16, path_w, n, C, y, y_format, y_deq, dmat_out, pos4_out, stream);
     case 3: return launch_eaas_l<3>(pos, x, x_bf16, path_w, n, C, y, y_format, y_deq, dmat_out, pos4_out, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int L>
+static hipError_t launch_eaas_adj_l(const float *pos, const float *x, const float *path_w, int n, int C, float *y,
+                                    hipStream_t stream)
+{
+    const int npb = eaas_nodes_per_block<L>(C);
+    dim3 grid((unsigned)((n + npb - 1) / npb));
+    Tables tb = host_tables();
+    tb.eaas = eaas_table(L);
+    eaas_kernel<L, float, kYF32, true><<<grid, 256, 0, stream>>>(pos, x, path_w, n, C, y, nullptr, nullptr, nullptr, tb);
+    return hipGetLastError();
+}
+
+hipError_t launch_eaas_adjoint(int L, const float *pos, const float *x, const float *path_w, int n, int C, float *y,
+                               hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    switch (L) {
+    case 0: return launch_eaas_adj_l<0>(pos, x, path_w, n, C, y, stream);
+    case 1: return launch_eaas_adj_l<1>(pos, x, path_w, n, C, y, stream);
+    case 2: return launch_eaas_adj_l<2>(pos, x, path_w, n, C, y, stream);
+    case 3: return launch_eaas_adj_l<3>(pos, x, path_w, n, C, y, stream);
     default: return hipErrorInvalidValue;
     }
 }

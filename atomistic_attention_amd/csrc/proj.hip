@@ -47,17 +47,22 @@ __global__ __launch_bounds__(64) void proj_kernel(const ProjJobs jobs, int n)
 #pragma unroll
         for (int e = 0; e < KQ; ++e) a[e] = 0.f;
     }
-    const float *bp = reinterpret_cast<const float *>(job.b) + (long long)(g * KQ) * C + m;
+    // B element (k, n) = b[k][n], or b[n][k] for the transposed weight
+    const int ks = job.b_trans ? 1 : C, ns = job.b_trans ? C : 1;
+    const float *bp = reinterpret_cast<const float *>(job.b) + (long long)(g * KQ) * ks + (long long)m * ns;
     const long long orow0 = (long long)blockIdx.x * 16 + 4 * g;
     for (int nb = 0; nb < C / 16; ++nb) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KQ; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bp[(long long)s * C + nb * 16], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bp[(long long)s * ks + (long long)nb * 16 * ns], acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const long long orow = orow0 + r;
-            if (orow < n) job.out[orow * job.o_node_stride + (long long)job.comp * C + nb * 16 + m] = acc[r];
+            if (orow < n) {
+                float *o = job.out + orow * job.o_node_stride + (long long)job.comp * C + nb * 16 + m;
+                *o = job.accumulate ? *o + acc[r] : acc[r];
+            }
         }
     }
 }

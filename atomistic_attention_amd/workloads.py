@@ -54,6 +54,8 @@ CONFIGS = {
     "c3b": LayerConfig("c3b", 10000, "uniform", 0.1, 5.0, 0, 3, 128, 16, 32, "bf16", 1003),
     "c4": LayerConfig("c4", 32768, "uniform", 0.1, 8.0, 256, 2, 128, 16, 32, "bf16", 1004),
     "c5": LayerConfig("c5", 100000, "blocks", 0.1, 8.0, 256, 2, 128, 16, 32, "bf16", 1005),
+    # feature gradient: fp32 storage and an uncapped (symmetric) 5 A list, c4's atom count
+    "g4": LayerConfig("g4", 32768, "uniform", 0.1, 5.0, 0, 2, 128, 16, 32, "fp32", 1006),
 }
 
 # Block model of the clustered system: the box is cut into 8^3 equal blocks;

@@ -215,6 +215,39 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Gradient of the layer with respect to its input features.
+ *
+ * For L = sum(grad_out * out), with out the layer output of e2v2_attn_forward
+ * for the same arguments, writes grad_h = dL/dh.  Positions, weights and the
+ * neighbour list are held fixed.  The chain runs the forward's steps 2-3 again
+ * (projections, source coupling: E2Former-V2 explainer sections 2.3 and 3.1),
+ * then the adjoint of each step in reverse: the output projection (h-hat^l
+ * gradient = grad_out^l W_O[l]^T), the target coupling (the EAAS map with each
+ * sparse coefficient taken from output to input: D P^T D^T), the softmax
+ * attention of section 3.1 (per-head logit gradient alpha (dalpha - sum alpha
+ * dalpha); the distance bias of the FlashSchNet page, section 2.1, has no h
+ * dependence), the source coupling, and the input projections.
+ *
+ * Storage must be fp32 (E2V2_ERR_UNSUPPORTED otherwise); pos fp32 [n][3], h and
+ * grad_out fp32 [n][(lmax+1)^2][C], grad_h fp32 [n][(lmax+1)^2][C] (written whole).
+ * The neighbour list (layout of e2v2_attn_forward) must be symmetric: j in row
+ * i exactly when i in row j.  Every uncapped list within a cutoff is
+ * (e2v2_build_neighbors with max_neighbors = 0, and e2v2_filter_neighbors of
+ * one); a K-capped list in general is not, and then grad_h is wrong -- the call
+ * does not check.  Row j is walked once as the targets of source j.
+ * target_order (optional, a permutation of 0..n-1) only changes the order in
+ * which nodes are processed.  Workspace: e2v2_layer_backward_workspace_bytes.
+ * All device pointers 16-byte aligned; asynchronous on `stream`.  Errors:
+ * E2V2_ERR_ARG (NULL or misaligned pointer, small workspace, n < 0),
+ * E2V2_ERR_UNSUPPORTED (storage, head shape), E2V2_ERR_HIP (launch failure). */
+size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t n);
+e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h,
+                                const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
+                                const int32_t *nbr_idx, const int32_t *target_order, int32_t n,
+                                const float *grad_out, float *grad_h, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Lists reused between rebuilds (Tessera article, neighbour reuse: the topology
  * is kept for several steps while distances come from the latest coordinates;
  * the short-range lists are taken from the long-range one).

@@ -37,12 +37,14 @@ def _tp(x, Y, w, lmax: int):
 
 
 def layer_forward_torch(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, *, lmax: int, heads: int,
-                        cutoff: float, rows):
-    """The layer for every atom, in torch fp64; h may require grad."""
+                        cutoff: float, rows, targets=None):
+    """The layer in torch fp64 for ``targets`` (default every atom; rows[t] is the
+    row of targets[t]); h [n, (L+1)^2, C] may require grad."""
     t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
     pos = np.asarray(pos, dtype=np.float64)
     cutoff = float(np.float32(cutoff))
     n, nc, C = h.shape
+    tg = np.arange(n) if targets is None else np.asarray(targets, dtype=np.int64)
     d_head = C // heads
     head_of = torch.arange(C) // d_head
     sl = so3.block_slices(lmax)
@@ -52,8 +54,8 @@ def layer_forward_torch(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, *, lmax
     Y = t(so3.real_sh(pos, lmax))
     hp = _tp(v, Y, t(w_src), lmax)
     ms = []
-    for i in range(n):
-        js = np.asarray(rows[i], dtype=np.int64)
+    for ti, i in enumerate(tg):
+        js = np.asarray(rows[ti], dtype=np.int64)
         if js.size == 0:
             ms.append(torch.zeros(nc, C, dtype=torch.float64))
             continue
@@ -65,14 +67,20 @@ def layer_forward_torch(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, *, lmax
         alpha = torch.softmax(qk / math.sqrt(d_head) + bias, dim=0)          # [J, H]
         ms.append(torch.einsum("jc,jkc->kc", alpha[:, head_of], hp[jt]))
     m = torch.stack(ms, dim=0)
-    hhat = _tp(m, Y, t(w_tgt), lmax)
+    hhat = _tp(m, Y[torch.from_numpy(tg)], t(w_tgt), lmax)
     return torch.cat([hhat[:, sl[l], :] @ t(w_o[l]) for l in range(lmax + 1)], dim=1)
 
 
-def grad_h(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, g, *, lmax: int, heads: int, cutoff: float, rows):
-    """dL/dh for L = sum(g * out)."""
+def grad_h(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, g, *, lmax: int, heads: int, cutoff: float, rows,
+           targets=None):
+    """dL/dh for L = sum over ``targets`` (default all) of g[t] * out[t]; g has one
+    row per target.
+
+    B2  Sampling: out_i depends on h_i and on h_j for j in row i only, so for a
+    symmetric list the gradient at atom a is exact when the targets cover a and
+    every member of row a."""
     ht = torch.tensor(np.asarray(h, dtype=np.float64), requires_grad=True)
     out = layer_forward_torch(pos, ht, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, lmax=lmax, heads=heads,
-                              cutoff=cutoff, rows=rows)
+                              cutoff=cutoff, rows=rows, targets=targets)
     (out * torch.as_tensor(np.asarray(g, dtype=np.float64))).sum().backward()
     return ht.grad.numpy()

@@ -1,0 +1,116 @@
+"""Parity of e2v2_layer_backward (dL/dh for L = sum(g * out), fp32 storage)
+against the fp64 oracle (oracle/backward.py, reverse-mode through the layer).
+
+Tolerance: max |gpu - oracle| / RMS(oracle) <= 1e-4, the fp32 bar of the
+forward layer.  Small workloads compare every atom; the 32,768-atom workload,
+in the launch configuration bench.py times, compares a sample of atoms whose
+gradient the oracle computes exactly from the sample's rows (B2 in the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+from atomistic_attention_amd import workloads as W
+from oracle import backward as OB
+from oracle import layer as O
+from tests._helpers import f32, record, rel_err, rows_from_device, upload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _weights(wl):
+    return dict(w_q=wl.w_q, w_k=wl.w_k, w_v=wl.w_v, w_o=wl.w_o, w_rbf=wl.w_rbf, w_src=wl.w_src, w_tgt=wl.w_tgt)
+
+
+def _g(wl, seed=11):
+    return np.random.default_rng(seed).standard_normal(wl.h.shape).astype(np.float32).astype(np.float64)
+
+
+def _gpu_grad(gpu_lib, wl, g, order=None):
+    c = wl.cfg
+    d = upload(wl)
+    s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, 0)
+    desc = gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
+    print(f"backward {c.name} n={c.n} L={c.lmax} H={c.heads}", flush=True)
+    gh = gpu_lib.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, f32(g), target_order=order)
+    torch.cuda.synchronize()
+    return gh.cpu().numpy(), (s, ln, ix)
+
+
+def _oracle(wl, g, rows=None, targets=None):
+    c = wl.cfg
+    if rows is None:
+        rows = O.neighbors(wl.pos, c.cutoff, 0, targets=targets)
+    return OB.grad_h(wl.pos, wl.h, **_weights(wl), g=g if targets is None else g[targets], lmax=c.lmax,
+                     heads=c.heads, cutoff=c.cutoff, rows=rows, targets=targets)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_backward_full_fp32(gpu_lib, name):
+    wl = W.make_workload(name)
+    g = _g(wl)
+    got, _ = _gpu_grad(gpu_lib, wl, g)
+    ref = _oracle(wl, g)
+    e = rel_err(got, ref)
+    record(f"backward_full[{name}]", grad_h=e)
+    assert e < TOL, e
+
+
+def _edge(n, L, heads, seed, nrbf=10):
+    cfg = W.LayerConfig("edge", n, "uniform", n / 14.0 ** 3, 4.5, 0, L, 8 * heads, heads, nrbf, "fp32", seed)
+    wl = W.make_workload(cfg)
+    wl.pos[0] = 0.0                      # at the origin: the l_f > 0 paths vanish
+    wl.pos[1] = (500.0, 500.0, 500.0)    # isolated: empty row, no readers
+    return wl
+
+
+@pytest.mark.parametrize("n,L,heads,seed", [(150, 0, 4, 31), (150, 1, 8, 32), (200, 3, 16, 33), (130, 2, 8, 34)])
+def test_backward_shapes_and_edges(gpu_lib, n, L, heads, seed):
+    wl = _edge(n, L, heads, seed)
+    g = _g(wl, seed)
+    got, _ = _gpu_grad(gpu_lib, wl, g)
+    ref = _oracle(wl, g)
+    e = rel_err(got, ref)
+    record(f"backward_edge[{n},{L},{heads}]", grad_h=e)
+    assert e < TOL, e
+    assert np.all(got[1] == 0.0)
+
+
+def test_backward_order_invariant(gpu_lib):
+    """The processing order changes no value: every node's result is computed by
+    one wave from the same inputs."""
+    wl = W.make_workload("c2")
+    g = _g(wl)
+    a, _ = _gpu_grad(gpu_lib, wl, g)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(wl.cfg.n).astype(np.int32)).cuda()
+    b, _ = _gpu_grad(gpu_lib, wl, g, order=perm)
+    assert np.array_equal(a, b)
+
+
+def test_backward_full_size_sampled(gpu_lib):
+    """32,768 atoms, 5 A uncapped list: the list is symmetric, and the gradient at
+    sampled atoms matches the oracle's exact sampled gradient."""
+    wl = W.make_workload("g4")
+    g = _g(wl)
+    got, (s, ln, ix) = _gpu_grad(gpu_lib, wl, g)
+    rows = rows_from_device(s, ln, ix)
+    pairs = {(i, int(j)) for i, r in enumerate(rows) for j in r}
+    assert all((j, i) in pairs for (i, j) in pairs)
+    rng = np.random.default_rng(9)
+    sample = np.sort(rng.choice(wl.cfg.n, 6, replace=False))
+    c = wl.cfg
+    srows = O.neighbors(wl.pos, c.cutoff, 0, targets=sample)
+    tg = np.unique(np.concatenate([sample] + [r.astype(np.int64) for r in srows]))
+    trows = O.neighbors(wl.pos, c.cutoff, 0, targets=tg)
+    # the targets' outputs read h of the targets and of their rows only: the oracle
+    # runs on that sub-system, re-indexed
+    sub = np.unique(np.concatenate([tg] + [r.astype(np.int64) for r in trows]))
+    loc = np.full(c.n, -1, dtype=np.int64)
+    loc[sub] = np.arange(sub.size)
+    ref = OB.grad_h(wl.pos[sub], wl.h[sub], **_weights(wl), g=g[tg], lmax=c.lmax, heads=c.heads, cutoff=c.cutoff,
+                    rows=[loc[r] for r in trows], targets=loc[tg])
+    ref = ref[loc[sample]]
+    e = rel_err(got[sample], ref)
+    record("backward_sampled[g4]", grad_h=e)
+    assert e < TOL, e

@@ -214,3 +214,29 @@ def test_stack_argument_errors(lib):
     one = (B.LayerDesc * 2)(_desc(cutoff=5.0), _desc(cutoff=5.0))
     two = (B.LayerDesc * 2)(_desc(cutoff=5.0), _desc(cutoff=8.0))
     assert lib.e2v2_stack_state_bytes(2, two, 1000, 64) - lib.e2v2_stack_state_bytes(2, one, 1000, 64) >= 1000 * 65 * 4
+
+
+def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE):
+    w = B.Weights(*([ptr] * 7))
+    wsb = ws_bytes if ws_bytes is not None else lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(desc), max(n, 0))
+    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, None, n, ptr, ptr,
+                                   ptr, wsb, None)
+
+
+def test_backward_argument_errors_and_workspace(lib):
+    d32 = _desc(storage=B.E2V2_FP32)
+    assert _bwd(lib, _desc()) == B.E2V2_ERR_UNSUPPORTED                 # bf16 storage
+    assert "fp32" in lib.e2v2_last_error().decode()
+    assert _bwd(lib, _desc(storage=B.E2V2_FP32, channels=256)) == B.E2V2_ERR_UNSUPPORTED
+    assert _bwd(lib, d32, n=-1) == B.E2V2_ERR_ARG
+    assert _bwd(lib, d32, ptr=None) == B.E2V2_ERR_ARG
+    assert _bwd(lib, d32, ptr=FAKE_MIS) == B.E2V2_ERR_ARG
+    assert _bwd(lib, d32, ws_bytes=100) == B.E2V2_ERR_ARG
+    assert "workspace" in lib.e2v2_last_error().decode()
+    assert _bwd(lib, d32, n=0) == B.E2V2_OK
+    # the forward's fp32 workspace plus dL/dhhat (reused for dL/dh'), dL/dm, three
+    # per-head values and dq, dk per node
+    fa = lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 2000) - lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 1000)
+    ba = (lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 2000)
+          - lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000))
+    assert abs((ba - fa) / 1000 - (2 * 9 * 128 * 4 + 3 * 16 * 4 + 2 * 128 * 4)) < 2

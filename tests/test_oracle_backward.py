@@ -112,3 +112,19 @@ def test_isolated_atom_has_zero_gradient():
     gr = _grad(pos, h, W, g, rows)
     assert np.all(gr[-1] == 0.0)
     assert np.max(np.abs(gr[:-1])) > 0
+
+
+def test_sampled_targets_give_the_full_gradient_at_sampled_atoms():
+    """B2: with targets = sample plus every member of the sample's rows, the
+    gradient at the sampled atoms equals the whole-system gradient."""
+    pos, h, W, g = _system(7, n=40, side=6.0)
+    rows = layer.neighbors(pos, CUT)
+    full = _grad(pos, h, W, g, rows)
+    sample = np.array([3, 17, 29])
+    tg = np.unique(np.concatenate([sample] + [rows[a] for a in sample]))
+    assert tg.size < pos.shape[0]
+    got = backward.grad_h(pos, h, **W, g=g[tg], lmax=LMAX, heads=HEADS, cutoff=CUT, rows=[rows[t] for t in tg],
+                          targets=tg)
+    assert np.max(np.abs(got[sample] - full[sample])) <= 1e-12 * np.max(np.abs(full))
+    other = np.setdiff1d(np.arange(pos.shape[0]), tg)
+    assert np.max(np.abs(got[other] - full[other])) > 1e-6      # elsewhere the sample is incomplete
