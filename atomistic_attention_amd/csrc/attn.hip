@@ -345,16 +345,13 @@ static hipError_t launch_attn_lh(const AttnArgs &a, hipStream_t stream)
 hipError_t launch_attn(int L, int hp_bf16, const AttnArgs &a, hipStream_t stream)
 {
     if (a.n <= 0) return hipSuccess;
-    if (hp_bf16 && L <= 2 && a.n < attn_pair_max_atoms(L, 8 * a.H)) return launch_attn_pair(L, a, stream);
-    switch (L * 2 + (hp_bf16 ? 1 : 0)) {
-    case 0: return launch_attn_lh<0, false>(a, stream);
-    case 1: return launch_attn_lh<0, true>(a, stream);
-    case 2: return launch_attn_lh<1, false>(a, stream);
-    case 3: return launch_attn_lh<1, true>(a, stream);
-    case 4: return launch_attn_lh<2, false>(a, stream);
-    case 5: return launch_attn_lh<2, true>(a, stream);
-    case 6: return launch_attn_lh<3, false>(a, stream);
-    case 7: return launch_attn_lh<3, true>(a, stream);
+    if (!hp_bf16) return launch_attn_f32(L, a, stream);     // fp32 storage: attn_f32.hip
+    if (L <= 2 && a.n < attn_pair_max_atoms(L, 8 * a.H)) return launch_attn_pair(L, a, stream);
+    switch (L) {
+    case 0: return launch_attn_lh<0, true>(a, stream);
+    case 1: return launch_attn_lh<1, true>(a, stream);
+    case 2: return launch_attn_lh<2, true>(a, stream);
+    case 3: return launch_attn_lh<3, true>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

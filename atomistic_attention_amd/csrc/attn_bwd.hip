@@ -27,90 +27,23 @@
 // the 4 lanes of a head reduce by two xor shuffles.  With fewer than 16 heads the
 // lanes past 4H idle.  Each lane of a head evaluates every fourth Gaussian of the
 // distance expansion.
-#include "e2v2_internal.h"
+#include "attn_lane2.h"
 
 namespace e2v2 {
+using namespace lane2;
 
-namespace {
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRsqrt8 = 0.35355339059327373f;
-constexpr float kGsc = 0.84932180028801904f;    // sqrt(log2(e) / 2): exp(-t^2 / 2) = exp2(-(kGsc t)^2)
-
-__device__ __forceinline__ float quad_sum(float x)
-{
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    return x;
-}
-
-// Per-lane share of the distance bias of the lane's head, log2 domain.
-struct BiasLane {
-    float w[16];        // log2(e) W_rbf[4 kk + r][head], zero past R
-    float inv_delta;    // kGsc (R - 1) / cutoff
-    float cos_scale;    // 1 / (2 cutoff): cos(pi d / rc) = cos(2 pi * d cos_scale)
-    float t_off;        // kGsc * r
-    int kk_n;           // ceil(R / 4)
-
-    __device__ __forceinline__ void init(const AttnBwdArgs &A, int head, int r)
-    {
-        const int R = A.R;
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            const int k = 4 * kk + r;
-            w[kk] = k < R ? A.w_rbf[k * A.H + head] * kLog2e : 0.f;
-        }
-        inv_delta = kGsc * (float)(R - 1) / A.cutoff;
-        cos_scale = 0.5f / A.cutoff;
-        t_off = kGsc * (float)r;
-        kk_n = (R + 3) >> 2;
-    }
-    // b_h(d) * log2(e), summed over the head's 4 lanes
-    __device__ __forceinline__ float bias2(float d) const
-    {
-        const float fc = 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f);
-        const float t0 = fmaf(d, inv_delta, -t_off);
-        float s = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
-            if (kk < kk_n) {
-                const float tk = t0 - (4.f * kGsc) * (float)kk;
-                s = fmaf(w[kk], __builtin_amdgcn_exp2f(-tk * tk), s);
-            }
-        return fc * quad_sum(s);
-    }
-};
-
-__device__ __forceinline__ float pair_dist(const float4 &pt, const float4 &ps)
-{
-    const float dx = ps.x - pt.x, dy = ps.y - pt.y, dz = ps.z - pt.z;
-    return __builtin_amdgcn_sqrtf(fmaf(dz, dz, fmaf(dy, dy, dx * dx)));
-}
-
-__device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
-
-// Slot -> node with one contiguous run of slots per XCD (workgroups go to the 8
-// XCDs round robin), then through the optional processing order.
-__device__ __forceinline__ int node_of_wave(const AttnBwdArgs &A)
-{
-    const int nb = gridDim.x, xcd = blockIdx.x & 7, kth = blockIdx.x >> 3;
-    const int lb = xcd * (nb >> 3) + (xcd < (nb & 7) ? xcd : (nb & 7)) + kth;
-    const int slot = lb * 4 + (int)(threadIdx.x >> 6);
-    if (slot >= A.n) return -1;
-    return A.order ? A.order[slot] : slot;
-}
-}  // namespace
 
 template <int L, int H>
 __global__ __launch_bounds__(256) void k_attn_bwd_target(const AttnBwdArgs A)
 {
     constexpr int NC = n_comp(L), C = 8 * H;
     const int lane = threadIdx.x & 63;
-    const int i = __builtin_amdgcn_readfirstlane(node_of_wave(A));
+    const int i = __builtin_amdgcn_readfirstlane(node_of_wave(A.n, A.order));
     if (i < 0 || i >= A.n) return;                       // wave-uniform
     const bool act = lane < 4 * H;
     const int c0 = act ? 2 * lane : 0, head = c0 >> 3, r = lane & 3;
     BiasLane bl;
-    bl.init(A, head, r);
+    bl.init(A.w_rbf, A.H, A.R, A.cutoff, head, r);
 
     const float2 q = ld2(A.q + (size_t)i * C + c0);
     float2 dm[NC];
@@ -172,12 +105,12 @@ __global__ __launch_bounds__(256) void k_attn_bwd_source(const AttnBwdArgs A)
 {
     constexpr int NC = n_comp(L), C = 8 * H;
     const int lane = threadIdx.x & 63;
-    const int j = __builtin_amdgcn_readfirstlane(node_of_wave(A));
+    const int j = __builtin_amdgcn_readfirstlane(node_of_wave(A.n, A.order));
     if (j < 0 || j >= A.n) return;                       // wave-uniform
     const bool act = lane < 4 * H;
     const int c0 = act ? 2 * lane : 0, head = c0 >> 3, r = lane & 3;
     BiasLane bl;
-    bl.init(A, head, r);
+    bl.init(A.w_rbf, A.H, A.R, A.cutoff, head, r);
 
     const float2 kj = ld2(A.k + (size_t)j * C + c0);
     float2 hv[NC];

@@ -538,6 +538,8 @@ struct AttnArgs {
 };
 // hp_f16s: h' is fp16 with per-node scales (else fp32).
 hipError_t launch_attn(int L, int hp_f16s, const AttnArgs &a, hipStream_t stream);
+// fp32 storage: one wave per target, the target coupling in the epilogue (writes hhat).
+hipError_t launch_attn_f32(int L, const AttnArgs &a, hipStream_t stream);
 
 // Adjoint of the EAAS coupling with the node's own encoding, fp32 in and out:
 // y = D . P^T (D^T x) per (node, channel), frames built from pos.

@@ -26,44 +26,67 @@ struct ProjJobs {
     ProjJob j[kMaxJobs];
 };
 
-// KQ = C / 4 contraction indices per lane group.
-template <int KQ>
+// KQ = C / 4 contraction indices per lane group.  A wave covers RT tiles of 16
+// rows, so each B value it loads feeds RT matrix-core steps; launches with few
+// jobs take RT = 1 to keep enough waves in flight.
+template <int KQ, int RT>
 __global__ __launch_bounds__(64) void proj_kernel(const ProjJobs jobs, int n)
 {
     constexpr int C = 4 * KQ;
     const ProjJob &job = jobs.j[blockIdx.y];
     const int lane = threadIdx.x;
     const int g = lane >> 4, m = lane & 15;
-    const long long row = (long long)blockIdx.x * 16 + m;
-    float a[KQ];
-    if (row < n) {
-        const float *ap = reinterpret_cast<const float *>(job.a) + row * job.a_node_stride + (long long)job.comp * C + g * KQ;
+    const long long row0 = (long long)blockIdx.x * (16 * RT);
+    float a[RT][KQ];
 #pragma unroll
-        for (int e = 0; e < KQ; e += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(ap + e);
-            a[e] = v.x; a[e + 1] = v.y; a[e + 2] = v.z; a[e + 3] = v.w;
-        }
-    } else {
+    for (int rt = 0; rt < RT; ++rt) {
+        const long long row = row0 + rt * 16 + m;
+        if (row < n) {
+            const float *ap = reinterpret_cast<const float *>(job.a) + row * job.a_node_stride + (long long)job.comp * C + g * KQ;
 #pragma unroll
-        for (int e = 0; e < KQ; ++e) a[e] = 0.f;
-    }
-    // B element (k, n) = b[k][n], or b[n][k] for the transposed weight
-    const int ks = job.b_trans ? 1 : C, ns = job.b_trans ? C : 1;
-    const float *bp = reinterpret_cast<const float *>(job.b) + (long long)(g * KQ) * ks + (long long)m * ns;
-    const long long orow0 = (long long)blockIdx.x * 16 + 4 * g;
-    for (int nb = 0; nb < C / 16; ++nb) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KQ; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bp[(long long)s * ks + (long long)nb * 16 * ns], acc, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const long long orow = orow0 + r;
-            if (orow < n) {
-                float *o = job.out + orow * job.o_node_stride + (long long)job.comp * C + nb * 16 + m;
-                *o = job.accumulate ? *o + acc[r] : acc[r];
+            for (int e = 0; e < KQ; e += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(ap + e);
+                a[rt][e] = v.x; a[rt][e + 1] = v.y; a[rt][e + 2] = v.z; a[rt][e + 3] = v.w;
             }
+        } else {
+#pragma unroll
+            for (int e = 0; e < KQ; ++e) a[rt][e] = 0.f;
         }
+    }
+    for (int nb = 0; nb < C / 16; ++nb) {
+        // B element (k, n) for k = g KQ + s, n = 16 nb + m: b[k][n], or b[n][k] for the
+        // transposed weight (one contiguous stretch of a row, read as 16-byte vectors)
+        float bb[KQ];
+        if (job.b_trans) {
+            const float *bt = reinterpret_cast<const float *>(job.b) + (long long)(nb * 16 + m) * C + g * KQ;
+#pragma unroll
+            for (int e = 0; e < KQ; e += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(bt + e);
+                bb[e] = v.x; bb[e + 1] = v.y; bb[e + 2] = v.z; bb[e + 3] = v.w;
+            }
+        } else {
+            const float *bp = reinterpret_cast<const float *>(job.b) + (long long)(g * KQ) * C + nb * 16 + m;
+#pragma unroll
+            for (int e = 0; e < KQ; ++e) bb[e] = bp[(long long)e * C];
+        }
+        floatx4 acc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < KQ; ++s2)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt][s2], bb[s2], acc[rt], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const long long orow = row0 + rt * 16 + 4 * g + r;
+                if (orow < n) {
+                    float *o = job.out + orow * job.o_node_stride + (long long)job.comp * C + nb * 16 + m;
+                    *o = job.accumulate ? *o + acc[rt][r] : acc[rt][r];
+                }
+            }
     }
 }
 
@@ -119,11 +142,15 @@ hipError_t launch_proj(const ProjJob *jobs, int njobs, int n, int C, hipStream_t
     if (njobs > kMaxJobs) return hipErrorInvalidValue;
     ProjJobs pj{};
     for (int i = 0; i < njobs; ++i) pj.j[i] = jobs[i];
-    dim3 grid((unsigned)((n + 15) / 16), (unsigned)njobs), block(64);
-    switch (C) {
-    case 32: proj_kernel<8><<<grid, block, 0, stream>>>(pj, n); break;
-    case 64: proj_kernel<16><<<grid, block, 0, stream>>>(pj, n); break;
-    case 128: proj_kernel<32><<<grid, block, 0, stream>>>(pj, n); break;
+    const int rt = njobs >= 4 ? 4 : 1;
+    dim3 grid((unsigned)((n + 16 * rt - 1) / (16 * rt)), (unsigned)njobs), block(64);
+    switch (C * 8 + rt) {
+    case 32 * 8 + 1: proj_kernel<8, 1><<<grid, block, 0, stream>>>(pj, n); break;
+    case 32 * 8 + 4: proj_kernel<8, 4><<<grid, block, 0, stream>>>(pj, n); break;
+    case 64 * 8 + 1: proj_kernel<16, 1><<<grid, block, 0, stream>>>(pj, n); break;
+    case 64 * 8 + 4: proj_kernel<16, 4><<<grid, block, 0, stream>>>(pj, n); break;
+    case 128 * 8 + 1: proj_kernel<32, 1><<<grid, block, 0, stream>>>(pj, n); break;
+    case 128 * 8 + 4: proj_kernel<32, 4><<<grid, block, 0, stream>>>(pj, n); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -17,7 +17,9 @@ workload on this host (cpu_baseline).
 
 config.stack reports the model level: steps/s of the four-layer stack (three 5 A
 layers, one 8 A layer) with neighbour reuse on the same system moving by a random
-walk (e2v2_stack_forward).
+walk (e2v2_stack_forward).  config.backward reports the feature gradient of one
+layer (e2v2_layer_backward) on 32,768 atoms with an uncapped 5 A list and fp32
+storage, next to that layer's forward.
 """
 from __future__ import annotations
 
@@ -145,6 +147,59 @@ def stack_bench(B, W, torch, steps: int = 60, warmup: int = 10) -> dict:
             "trajectory": f"random walk, N(0, {st.cfg.sigma}^2) A per coordinate and step, synthetic"}
 
 
+def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g4") -> dict:
+    """Feature gradient dL/dh of one layer (e2v2_layer_backward: the forward's
+    projections and source coupling, then the adjoint chain) on the 32,768-atom
+    system with an uncapped 5 A list and fp32 storage, next to the forward of the
+    same layer.  Both timed on resident inputs and lists built beforehand, in the
+    list's spatial order."""
+    wl = W.make_workload(name)
+    c = wl.cfg
+    d = W.device_arrays(wl)
+    dev = d["pos"].device
+    desc = B.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
+    order = torch.empty(c.n, dtype=torch.int32, device=dev)
+    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, 0, order_out=order)
+    g = torch.from_numpy(np.random.default_rng(11).standard_normal(wl.h.shape).astype(np.float32)).to(dev)
+    gh = torch.empty_like(g)
+    out = torch.empty_like(g)
+    bws = torch.empty(B.backward_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
+    fws = torch.empty(B.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
+
+    def bwd():
+        B.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, g, grad_h=gh, workspace=bws,
+                              target_order=order)
+
+    def fwd():
+        B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, out=out, workspace=fws,
+                            target_order=order)
+
+    res = {}
+    for key, fn in (("backward", bwd), ("forward", fwd)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        res[key] = (time.perf_counter() - t0) * 1e3 / steps
+    nnz = int(nnz)
+    C, nc, H = c.channels, c.n_comp, c.heads
+    # attention adjoint, algorithmic bytes: target pass per pair k_j, h'_j, position,
+    # index; source pass per pair q_i, dm_i, position, index and (mx, rz, dd) of the
+    # 16 heads; per node the own rows in and the gradients out
+    per_pair = 2 * (4 * C + 4 * nc * C + 16 + 4) + 3 * 4 * H
+    per_node = 2 * (4 * C + 4 * nc * C + 16 + 8) + 4 * C + 3 * 4 * H + 4 * nc * C + 4 * C
+    return {"workload": f"{name}: {c.n} atoms, {c.geometry} at {c.density} atoms/A^3, cutoff {c.cutoff} A "
+                        f"uncapped (symmetric list), l_max={c.lmax}, C={C}, {H} heads, {c.n_rbf} RBFs, "
+                        f"fp32 storage",
+            "what": "dL/dh for L = sum(g * out), g fixed; positions and weights held fixed",
+            "nnz": nnz, "steps": steps, "ms_backward": res["backward"], "ms_forward_same_layer": res["forward"],
+            "pairs_per_s_backward": nnz / (res["backward"] * 1e-3),
+            "attention_adjoint_algorithmic_bytes": per_pair * nnz + per_node * c.n}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +210,9 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the four-layer stack measurement")
     ap.add_argument("--stack-only", action="store_true",
                     help="run only the four-layer stack measurement and print its record (for profiling)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the feature-gradient measurement")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="run only the feature-gradient measurement and print its record (for profiling)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: 3 layer forwards, then 3 plain device copies of 1 GiB "
                          "(the copies calibrate the counters' byte units); prints no JSON")
@@ -174,6 +232,9 @@ def main():
     B.load()
     if args.stack_only:
         print(json.dumps({"stack": stack_bench(B, W, torch)}), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps({"backward": backward_bench(B, W, torch)}), flush=True)
         return
     wl = W.make_workload(args.config)
     cfg = wl.cfg
@@ -345,6 +406,8 @@ def main():
     }
     if not args.no_stack:
         rec["config"]["stack"] = stack_bench(B, W, torch)
+    if not args.no_backward:
+        rec["config"]["backward"] = backward_bench(B, W, torch)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(rec), flush=True)
