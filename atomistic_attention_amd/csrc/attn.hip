@@ -1,4 +1,6 @@
-// Fused streaming neighbour attention with the target coupling in its epilogue.
+// Streaming neighbour attention for 16-bit storage (the general kernel: any l_max,
+// any size; attn_pair.hip serves l_max <= 2 below its size limit, attn_f32.hip
+// serves fp32 storage).  It stops at the normalised message m_i.
 //
 // E2Former-V2 explainer, section 3.1 (node-centric message passing: the
 // message m_i = sum_j alpha_ij h'_j is formed on the fly, then coupled with the
@@ -27,13 +29,11 @@
 //     as soon as the first half is consumed;
 //   * at the end the PS partial softmaxes are merged by a butterfly that halves
 //     the channel set at each step (reduce-scatter), leaving every lane whole
-//     channels: the target EAAS coupling then runs lane-locally and the lane
-//     writes its channels of hhat (fp32 storage), or the lane writes its channels
-//     of the normalised message m_i, which the output-projection kernel couples
-//     (16-bit storage).
-// Value rows are read as 16-byte pieces (4 channels of one fp32 component, or of
-// two interleaved fp16 components); the 2H lanes of a slot cover a contiguous
-// stretch of the neighbour's row.  With 16-bit storage the key arrives in fp16
+//     channels, and the lane writes its channels of the normalised message m_i,
+//     which the output-projection kernel couples.
+// Value rows are read as 16-byte pieces (4 channels of two interleaved fp16
+// components); the 2H lanes of a slot cover a contiguous stretch of the
+// neighbour's row.  The key arrives in fp16
 // together with an odd last component of h' (one 16-byte piece per pair), and a
 // neighbour's h' and k share one power-of-two scale (pos4[j].w): it is folded into
 // the softmax weight of the pair, so each value element costs one mixed-precision
@@ -42,22 +42,20 @@
 
 namespace e2v2 {
 
-template <int L, bool HB, int H>
+template <int L, int H>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_kernel(const AttnArgs A, const EaasCoef tab)
+void attn_kernel(const AttnArgs A)
 {
     constexpr int NC = n_comp(L);
     constexpr int C = 8 * H;
     constexpr int PS = 32 / H;          // neighbour slots per wave
     constexpr int S = H / 2;            // pairs per slot per 16-pair chunk
-    constexpr int P = path_count(L);
-    constexpr int ND = n_dmat(L);
     constexpr int NB = Log2<PS>::v;
     constexpr float LOG2E = 1.4426950408889634f;
     // Value rows are fetched in NPH phases of SP steps, each phase sized to about
     // 72 registers (one 8- or 16-byte piece per component and step) when a step's
     // piece is small, else to one step.
-    constexpr int RPR = HB ? 2 : 4;
+    constexpr int RPR = 2;
     constexpr int BUDGET = NC * RPR <= 18 ? 72 : 40;
     constexpr int SPF = BUDGET / (NC * RPR) > 0 ? BUDGET / (NC * RPR) : 1;
     constexpr int SP = SPF >= 8 && S >= 8 ? 8 : SPF >= 4 && S >= 4 ? 4 : SPF >= 2 && S >= 2 ? 2 : 1;
@@ -122,23 +120,19 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
             const int p = u * S + s;
             const int j = __shfl(jp, p, 64);
             js[s] = (j >= 0 && j < n) ? j : -1;
-            scl[s] = HB ? __shfl(pj.w, p, 64) : 1.f;
+            scl[s] = __shfl(pj.w, p, 64);
         }
         // ---- (b) issue every key row and the first phase of value rows
         float4 kv[S];
-        uint2 tl[HB ? S : 1];          // 16-bit storage: h' component NC - 1, from the key + tail group
+        uint2 tl[S];                   // h' component NC - 1, from the key + tail group
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const size_t node = (size_t)(js[s] >= 0 ? js[s] : i);
-            if constexpr (HB) {
-                const uint4 g4 = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(A.k) + node * (2 * C) + 2 * cb);
-                kv[s] = make_float4(f16_of(g4.x, 0), f16_of(g4.x, 1), f16_of(g4.y, 0), f16_of(g4.y, 1));
-                tl[s] = make_uint2(g4.z, g4.w);
-            } else {
-                kv[s] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(A.k) + node * C + cb);
-            }
+            const uint4 g4 = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(A.k) + node * (2 * C) + 2 * cb);
+            kv[s] = make_float4(f16_of(g4.x, 0), f16_of(g4.x, 1), f16_of(g4.y, 0), f16_of(g4.y, 1));
+            tl[s] = make_uint2(g4.z, g4.w);
         }
-        HpStep<HB, NC> hv[SP];
+        HpStep<true, NC> hv[SP];
 #pragma unroll
         for (int s = 0; s < SP; ++s) hv[s].load(A.hp, js[s] >= 0 ? js[s] : i, cb, C);
         // ---- (c) prefetch the next chunk's index for pair pm
@@ -198,7 +192,7 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
             qk = fmaf(qv.z, kv[s].z, qk);
             qk = fmaf(qv.w, kv[s].w, qk);
             qk += __shfl_xor(qk, H, 64);
-            if constexpr (HB) qk *= scl[s];
+            qk *= scl[s];
             sl[s] = js[s] >= 0 ? fmaf(qk, qscale, bs[s]) : -INFINITY;
         }
         // The reference maximum mu moves only when a logit exceeds it by more than 8
@@ -246,7 +240,7 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
 #pragma unroll
                     for (int s = 0; s < SP; ++s) {
                         float x;
-                        if constexpr (HB && (NC & 1))
+                        if constexpr ((NC & 1) != 0)
                             x = e == NC - 1 ? f16_of(c < 2 ? tl[ph * SP + s].x : tl[ph * SP + s].y, c & 1)
                                             : hv[s].get(e, c);
                         else
@@ -297,46 +291,20 @@ void attn_kernel(const AttnArgs A, const EaasCoef tab)
     }
     constexpr int NCH = (NB >= 2) ? 1 : (4 >> NB);
     const bool writer = (NB <= 2) || ((u & 1) == 0);
-    const float invz = z > 0.f ? 1.f / z : 0.f;
 
-    if constexpr (HB) {
-        // 16-bit storage: store the normalised message m_i (fp16 under a node scale);
-        // the target coupling runs in the output-projection kernel, on whole nodes.
-        store_message_f16<NC, NCH>(A, i, C, z, acc, cb + off, writer, lane);
-        return;
-    }
-    // ---- target coupling (EAAS with the target's own rotation) and store
-    const float *Di = A.dmat + (size_t)i * (ND > 0 ? ND : 1);
-    const bool dir = (pi4.x != 0.f) || (pi4.y != 0.f) || (pi4.z != 0.f);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int ch = cb + off + c;
-        float mv[NC], yv[NC], w[P];
-#pragma unroll
-        for (int e = 0; e < NC; ++e) mv[e] = acc[e][c] * invz;
-        if (writer && A.m_tap) {
-#pragma unroll
-            for (int e = 0; e < NC; ++e) A.m_tap[((size_t)i * NC + e) * C + ch] = mv[e];
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p) w[p] = A.w_tgt[p * C + ch];
-        eaas_channel<L>(Di, mv, yv, w, tab, dir);
-        if (writer) {
-#pragma unroll
-            for (int e = 0; e < NC; ++e) A.hhat[((size_t)i * NC + e) * C + ch] = yv[e];
-        }
-    }
+    // store the normalised message m_i (fp16 under a node scale); the target
+    // coupling runs in the output-projection kernel, on whole nodes
+    store_message_f16<NC, NCH>(A, i, C, z, acc, cb + off, writer, lane);
 }
 
-template <int L, bool HB>
+template <int L>
 static hipError_t launch_attn_lh(const AttnArgs &a, hipStream_t stream)
 {
     dim3 grid((unsigned)((a.n + 3) / 4)), block(256);
-    const EaasCoef &tab = eaas_table(L);
     switch (a.H) {
-    case 4: attn_kernel<L, HB, 4><<<grid, block, 0, stream>>>(a, tab); break;
-    case 8: attn_kernel<L, HB, 8><<<grid, block, 0, stream>>>(a, tab); break;
-    case 16: attn_kernel<L, HB, 16><<<grid, block, 0, stream>>>(a, tab); break;
+    case 4: attn_kernel<L, 4><<<grid, block, 0, stream>>>(a); break;
+    case 8: attn_kernel<L, 8><<<grid, block, 0, stream>>>(a); break;
+    case 16: attn_kernel<L, 16><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -348,10 +316,10 @@ hipError_t launch_attn(int L, int hp_bf16, const AttnArgs &a, hipStream_t stream
     if (!hp_bf16) return launch_attn_f32(L, a, stream);     // fp32 storage: attn_f32.hip
     if (L <= 2 && a.n < attn_pair_max_atoms(L, 8 * a.H)) return launch_attn_pair(L, a, stream);
     switch (L) {
-    case 0: return launch_attn_lh<0, true>(a, stream);
-    case 1: return launch_attn_lh<1, true>(a, stream);
-    case 2: return launch_attn_lh<2, true>(a, stream);
-    case 3: return launch_attn_lh<3, true>(a, stream);
+    case 0: return launch_attn_lh<0>(a, stream);
+    case 1: return launch_attn_lh<1>(a, stream);
+    case 2: return launch_attn_lh<2>(a, stream);
+    case 3: return launch_attn_lh<3>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -8,8 +8,7 @@ namespace e2v2 {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// One neighbour's value pieces for this lane's 4 channels.  fp32 h' is
-// [node][comp][C]: one 16-byte load per component.  16-bit h' is stored with
+// One neighbour's value pieces for this lane's 4 channels.  16-bit h' is stored with
 // components interleaved in pairs (hp_f16_offset): one 16-byte load covers 4
 // channels of two components -- half the load instructions of a per-component
 // layout -- and an odd last component travels with the key (hp_pair_row).
@@ -48,20 +47,6 @@ __device__ __forceinline__ float f16_of(uint32_t w, int hi)
 {
     return (float)__builtin_bit_cast(_Float16, uint16_t(hi ? (w >> 16) : (w & 0xffffu)));
 }
-template <int NC> struct HpStep<false, NC> {
-    float4 a[NC];
-    __device__ __forceinline__ void load(const void *base, int node, int cb, int C)
-    {
-        const float *nb = reinterpret_cast<const float *>(base) + (size_t)node * NC * C + cb;
-#pragma unroll
-        for (int e = 0; e < NC; ++e) a[e] = *reinterpret_cast<const float4 *>(nb + e * C);
-    }
-    __device__ __forceinline__ float get(int e, int c) const
-    {
-        const float4 &v = a[e];
-        return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
-    }
-};
 
 template <int N> struct Log2;
 template <> struct Log2<1> { static constexpr int v = 0; };
