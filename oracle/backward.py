@@ -9,9 +9,16 @@ B1  L(h) = sum(g * out(h)) for a fixed upstream gradient g; the oracle returns
     spherical harmonics of each position (held constant: so3.coupling_tensor,
     so3.real_sh), the distance bias (constant: layer.rbf_bias), an explicit
     per-head softmax over each neighbour set -- and reverse-mode differentiation
-    gives the gradient.  Positions, weights and neighbour lists are fixed.
+    gives the gradient.  Weights and neighbour lists are fixed.
     The forward pass here is checked against layer.layer_forward, and the
     gradient against central finite differences of layer.layer_forward.
+
+B3  L(pos, h) as in B1 with the positions free as well: dL/dpos through the
+    encodings Y(r_i) of both couplings and through every pair distance in the
+    bias, with the neighbour lists held fixed (the envelope and its slope vanish
+    at the cutoff, so a pair crossing it contributes nothing either way).  At a
+    zero position vector the direction is undefined: its encoding is held
+    constant, so that atom's position receives only the bias terms.
 """
 from __future__ import annotations
 
@@ -22,7 +29,45 @@ import torch
 
 from . import layer, so3
 
-__all__ = ["layer_forward_torch", "grad_h"]
+__all__ = ["layer_forward_torch", "grad_h", "grad_pos_h", "real_sh_torch", "rbf_bias_torch"]
+
+
+def real_sh_torch(r, lmax: int):
+    """so3.real_sh in torch (differentiable in r): the same closed forms of the
+    direction r / |r|; a zero vector maps to Y_0 = 1, Y_{l>0} = 0, held constant
+    (the direction, and so its derivative, is not defined there: B3)."""
+    nrm = torch.sqrt(torch.sum(r * r, dim=-1))
+    zero = nrm == 0.0
+    safe = torch.where(zero, torch.ones_like(nrm), nrm)
+    u = r / safe[..., None]
+    x, y, z = u[..., 0], u[..., 1], u[..., 2]
+    out = [torch.ones_like(x)]
+    if lmax >= 1:
+        s3 = math.sqrt(3.0)
+        out += [s3 * y, s3 * z, s3 * x]
+    if lmax >= 2:
+        s15, s5 = math.sqrt(15.0), math.sqrt(5.0)
+        out += [s15 * x * y, s15 * y * z, 0.5 * s5 * (3.0 * z * z - 1.0), s15 * x * z, 0.5 * s15 * (x * x - y * y)]
+    if lmax >= 3:
+        a, b, c = math.sqrt(35.0 / 8.0), math.sqrt(105.0), math.sqrt(21.0 / 8.0)
+        out += [a * y * (3 * x * x - y * y), b * x * y * z, c * y * (5 * z * z - 1),
+                0.5 * math.sqrt(7.0) * (5 * z ** 3 - 3 * z), c * x * (5 * z * z - 1),
+                0.5 * b * z * (x * x - y * y), a * x * (x * x - 3 * y * y)]
+    Y = torch.stack(out, dim=-1)
+    keep = torch.ones_like(Y)
+    keep[..., 1:] = (~zero).to(Y.dtype)[..., None]
+    return Y * keep
+
+
+def rbf_bias_torch(d, w_rbf, cutoff: float):
+    """layer.rbf_bias in torch (differentiable in d)."""
+    w = torch.as_tensor(np.asarray(w_rbf, dtype=np.float64))
+    R = w.shape[0]
+    delta = cutoff / (R - 1)
+    mu = torch.arange(R, dtype=torch.float64) * delta
+    phi = torch.exp(-((d[..., None] - mu) ** 2) / (2.0 * delta * delta))
+    fc = 0.5 * (torch.cos(math.pi * d / cutoff) + 1.0)
+    return fc[..., None] * (phi @ w)
 
 
 def _tp(x, Y, w, lmax: int):
@@ -39,9 +84,10 @@ def _tp(x, Y, w, lmax: int):
 def layer_forward_torch(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, *, lmax: int, heads: int,
                         cutoff: float, rows, targets=None):
     """The layer in torch fp64 for ``targets`` (default every atom; rows[t] is the
-    row of targets[t]); h [n, (L+1)^2, C] may require grad."""
+    row of targets[t]); h [n, (L+1)^2, C] may require grad, and so may pos when it
+    is given as a torch tensor (then the encodings and the distance bias follow it)."""
     t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
-    pos = np.asarray(pos, dtype=np.float64)
+    pos_t = pos if torch.is_tensor(pos) else torch.as_tensor(np.asarray(pos, dtype=np.float64))
     cutoff = float(np.float32(cutoff))
     n, nc, C = h.shape
     tg = np.arange(n) if targets is None else np.asarray(targets, dtype=np.int64)
@@ -51,7 +97,7 @@ def layer_forward_torch(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, *, lmax
     q = h[:, 0, :] @ t(w_q)
     k = h[:, 0, :] @ t(w_k)
     v = torch.cat([h[:, sl[l], :] @ t(w_v[l]) for l in range(lmax + 1)], dim=1)
-    Y = t(so3.real_sh(pos, lmax))
+    Y = real_sh_torch(pos_t, lmax)
     hp = _tp(v, Y, t(w_src), lmax)
     ms = []
     for ti, i in enumerate(tg):
@@ -59,16 +105,27 @@ def layer_forward_torch(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, *, lmax
         if js.size == 0:
             ms.append(torch.zeros(nc, C, dtype=torch.float64))
             continue
-        diff = pos[js] - pos[i][None, :]
-        d = np.sqrt(np.sum(diff * diff, axis=1))
-        bias = t(layer.rbf_bias(d, w_rbf, cutoff))                           # [J, H]
         jt = torch.from_numpy(js)
+        diff = pos_t[jt] - pos_t[int(i)][None, :]
+        d = torch.sqrt(torch.sum(diff * diff, dim=1))
+        bias = rbf_bias_torch(d, w_rbf, cutoff)                              # [J, H]
         qk = (k[jt] * q[i][None, :]).reshape(js.size, heads, d_head).sum(dim=2)
         alpha = torch.softmax(qk / math.sqrt(d_head) + bias, dim=0)          # [J, H]
         ms.append(torch.einsum("jc,jkc->kc", alpha[:, head_of], hp[jt]))
     m = torch.stack(ms, dim=0)
     hhat = _tp(m, Y[torch.from_numpy(tg)], t(w_tgt), lmax)
     return torch.cat([hhat[:, sl[l], :] @ t(w_o[l]) for l in range(lmax + 1)], dim=1)
+
+
+def grad_pos_h(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, g, *, lmax: int, heads: int, cutoff: float,
+               rows, targets=None):
+    """(dL/dpos, dL/dh) for L = sum over ``targets`` of g[t] * out[t] (B3)."""
+    pt = torch.tensor(np.asarray(pos, dtype=np.float64), requires_grad=True)
+    ht = torch.tensor(np.asarray(h, dtype=np.float64), requires_grad=True)
+    out = layer_forward_torch(pt, ht, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, lmax=lmax, heads=heads,
+                              cutoff=cutoff, rows=rows, targets=targets)
+    (out * torch.as_tensor(np.asarray(g, dtype=np.float64))).sum().backward()
+    return pt.grad.numpy(), ht.grad.numpy()
 
 
 def grad_h(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, g, *, lmax: int, heads: int, cutoff: float, rows,

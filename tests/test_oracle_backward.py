@@ -128,3 +128,56 @@ def test_sampled_targets_give_the_full_gradient_at_sampled_atoms():
     assert np.max(np.abs(got[sample] - full[sample])) <= 1e-12 * np.max(np.abs(full))
     other = np.setdiff1d(np.arange(pos.shape[0]), tg)
     assert np.max(np.abs(got[other] - full[other])) > 1e-6      # elsewhere the sample is incomplete
+
+
+# ---------------------------------------------------------------- B3: positions
+
+def _gpos(pos, h, W, g, rows, lmax=LMAX):
+    return backward.grad_pos_h(pos, h, **W, g=g, lmax=lmax, heads=HEADS, cutoff=CUT, rows=rows)[0]
+
+
+@pytest.mark.parametrize("seed", [12, 13])
+def test_position_gradient_matches_central_differences(seed):
+    """Directional and element-wise derivatives of the numpy forward pass in the
+    positions (lists held fixed) against dL/dpos."""
+    pos, h, W, g = _system(seed)
+    rows = layer.neighbors(pos, CUT)
+    gp = _gpos(pos, h, W, g, rows)
+    rng = np.random.default_rng(seed + 7)
+    eps = 1e-6
+    L = lambda p: np.sum(g * _fwd_np(p, h, W, rows))
+    u = rng.standard_normal(pos.shape)
+    fd = (L(pos + eps * u) - L(pos - eps * u)) / (2 * eps)
+    an = float(np.sum(gp * u))
+    assert abs(fd - an) <= 2e-6 * max(1.0, abs(an)), (fd, an)
+    for a, k in [(0, 0), (4, 1), (9, 2), (15, 0)]:
+        d = np.zeros_like(pos)
+        d[a, k] = eps
+        fd = (L(pos + d) - L(pos - d)) / (2 * eps)
+        assert abs(fd - gp[a, k]) <= 2e-6 * max(1.0, abs(gp[a, k])), (a, k, fd, gp[a, k])
+
+
+def test_position_gradient_vanishes_without_geometry():
+    """l_max = 0 and W_rbf = 0: the output does not depend on the positions."""
+    pos, h, W, g = _system(14)
+    nc = 1
+    P = len(so3.paths(0))
+    W0 = dict(W, w_v=W["w_v"][:1], w_o=W["w_o"][:1], w_src=W["w_src"][:P], w_tgt=W["w_tgt"][:P],
+              w_rbf=np.zeros_like(W["w_rbf"]))
+    rows = layer.neighbors(pos, CUT)
+    gp = _gpos(pos, h[:, :nc], W0, g[:, :nc], rows, lmax=0)
+    assert np.all(gp == 0.0)
+
+
+def test_bias_only_gradient_is_translation_and_rotation_invariant():
+    """l_max = 0: positions enter through pair distances only, so the gradient sums
+    to zero (no net force) and has no net torque."""
+    pos, h, W, g = _system(15)
+    P = len(so3.paths(0))
+    W0 = dict(W, w_v=W["w_v"][:1], w_o=W["w_o"][:1], w_src=W["w_src"][:P], w_tgt=W["w_tgt"][:P])
+    rows = layer.neighbors(pos, CUT)
+    gp = _gpos(pos, h[:, :1], W0, g[:, :1], rows, lmax=0)
+    scale = np.max(np.abs(gp))
+    assert scale > 1e-3
+    assert np.max(np.abs(gp.sum(axis=0))) <= 1e-12 * scale * pos.shape[0]
+    assert np.max(np.abs(np.cross(pos, gp).sum(axis=0))) <= 1e-12 * scale * pos.shape[0] * 5
