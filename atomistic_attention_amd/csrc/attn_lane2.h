@@ -55,7 +55,39 @@ struct BiasLane {
             }
         return fc * quad_sum(s);
     }
+    // The same bias (log2 domain) and its slope db_h/dd in natural units:
+    // b = fc S0, db/dd = fc' S0 - fc S1 / (kGsc Delta) with S0 = sum W phi_k,
+    // S1 = sum W phi_k t_k, t_k = kGsc (d - mu_k) / Delta (phi_k' = -phi_k (d - mu_k) / Delta^2).
+    __device__ __forceinline__ void bias2_slope(float d, float &b2, float &slope) const
+    {
+        const float fc = 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f);
+        const float fcp = -(0.5f * 3.14159265358979f * 2.f) * cos_scale * __builtin_amdgcn_sinf(d * cos_scale);
+        const float t0 = fmaf(d, inv_delta, -t_off);
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+            if (kk < kk_n) {
+                const float tk = t0 - (4.f * kGsc) * (float)kk;
+                const float wp = w[kk] * __builtin_amdgcn_exp2f(-tk * tk);
+                s0 += wp;
+                s1 = fmaf(wp, tk, s1);
+            }
+        s0 = quad_sum(s0);
+        s1 = quad_sum(s1);
+        b2 = fc * s0;
+        slope = (fcp * s0 - fc * s1 * (inv_delta / (kGsc * kGsc))) * (1.f / kLog2e);
+    }
 };
+
+// Sum over the wave of each lane's value, taking lanes with `take` only; every
+// lane gets the total.
+__device__ __forceinline__ float wave_sum_if(float x, bool take)
+{
+    x = take ? x : 0.f;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
 
 // |r_s - r_t| in fp32, one fixed operation order (target t, source s)
 __device__ __forceinline__ float pair_dist(const float4 &pt, const float4 &ps)

@@ -203,7 +203,56 @@ void eaas_for_lmax(int lmax, EaasCoef &out)
 EaasCoef g_by_lmax[kMaxL + 1];
 std::once_flag g_once_l;
 
+// Real-basis coupling tensor T[m_i, m_f, m_o] = sum conj(U_li) conj(U_lf) U_lo C(l_i mu_i; l_f mu_f | l_o mu_o),
+// real part for even l_i + l_f + l_o, imaginary part for odd.
+double coupling_entry(int li, int lf, int lo, int mi, int mf, int mo)
+{
+    std::complex<double> acc = 0.0;
+    for (int a = -li; a <= li; ++a)
+        for (int b = -lf; b <= lf; ++b) {
+            const int M = a + b;
+            if (std::abs(M) > lo) continue;
+            acc += std::conj(U(li, mi, a)) * std::conj(U(lf, mf, b)) * U(lo, mo, M) * cg(li, a, lf, b, lo, M);
+        }
+    return ((li + lf + lo) & 1) ? acc.imag() : acc.real();
+}
+
+CplTable g_cpl[kMaxL + 1];
+std::once_flag g_once_cpl;
+
+void build_cpl(int lmax, CplTable &t)
+{
+    std::memset(&t, 0, sizeof(t));
+    int n = 0;
+    for (int lf = 1; lf <= lmax; ++lf)
+        for (int mf = -lf; mf <= lf; ++mf) {
+            const int ef = lf * lf + lf + mf;
+            t.off[ef] = n;
+            for (int lo = 0; lo <= lmax; ++lo)
+                for (int li = 0; li <= lmax; ++li) {
+                    if (!is_path(li, lf, lo)) continue;
+                    const int p = path_index(lmax, li, lf, lo);
+                    for (int mi = -li; mi <= li; ++mi)
+                        for (int mo = -lo; mo <= lo; ++mo) {
+                            const double v = coupling_entry(li, lf, lo, mi, mf, mo);
+                            if (std::fabs(v) < 1e-12 || n >= kMaxCpl) continue;
+                            t.e[n++] = CplEntry{(float)v, (uint16_t)p, (uint8_t)(li * li + li + mi),
+                                                (uint8_t)(lo * lo + lo + mo)};
+                        }
+                }
+        }
+    for (int ef = (lmax + 1) * (lmax + 1); ef <= n_comp(kMaxL); ++ef) t.off[ef] = n;
+}
+
 }  // namespace
+
+const CplTable &cpl_table(int lmax)
+{
+    std::call_once(g_once_cpl, [] {
+        for (int l = 0; l <= kMaxL; ++l) build_cpl(l, g_cpl[l]);
+    });
+    return g_cpl[lmax];
+}
 
 const Tables &host_tables()
 {
@@ -641,7 +690,7 @@ e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, con
 namespace {
 // The forward workspace (q, k, v, h', frames) followed by the gradient buffers.
 struct BwdWs {
-    size_t fwd, gbuf, dm, mx, rz, dd, dq, dk, total;
+    size_t fwd, gbuf, dhh, dm, mbuf, mx, rz, dd, dq, dk, tab, total;
 };
 BwdWs bwd_ws(const e2v2_layer_desc &d, int n)
 {
@@ -649,13 +698,16 @@ BwdWs bwd_ws(const e2v2_layer_desc &d, int n)
     BwdWs w{};
     size_t o = 0;
     w.fwd = o; o += al256(attn_ws(d, n).total);
-    w.gbuf = o; o += al256(N * NC * C * 4);      // dL/dhhat, then dL/dh'
+    w.gbuf = o; o += al256(N * NC * C * 4);      // dL/dh'
+    w.dhh = o; o += al256(N * NC * C * 4);       // dL/dhhat
     w.dm = o; o += al256(N * NC * C * 4);
+    w.mbuf = o; o += al256(N * NC * C * 4);      // m (for the position gradient)
     w.mx = o; o += al256(N * H * 4);
     w.rz = o; o += al256(N * H * 4);
     w.dd = o; o += al256(N * H * 4);
     w.dq = o; o += al256(N * C * 4);
     w.dk = o; o += al256(N * C * 4);
+    w.tab = o; o += al256(sizeof(CplTable));
     w.total = o + 256;
     return w;
 }
@@ -672,7 +724,7 @@ size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t 
 e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
                                 const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
                                 const int32_t *target_order, int32_t n, const float *grad_out, float *grad_h,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream)
+                                float *grad_pos, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
@@ -687,7 +739,8 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
         if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
         if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
     }
-    if (target_order && !aligned16(target_order)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    if ((target_order && !aligned16(target_order)) || (grad_pos && !aligned16(grad_pos)))
+        return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
     const BwdWs B = bwd_ws(*desc, n);
     if (workspace_bytes < B.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, B.total);
     char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
@@ -703,6 +756,7 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     const float *hp = reinterpret_cast<const float *>(fw + F.hp);
     const float4 *pos4 = reinterpret_cast<const float4 *>(fw + F.pos4);
     float *gbuf = reinterpret_cast<float *>(ws + B.gbuf);
+    float *dhh = reinterpret_cast<float *>(ws + B.dhh);
     float *dm = reinterpret_cast<float *>(ws + B.dm);
     float *dq = reinterpret_cast<float *>(ws + B.dq);
     float *dk = reinterpret_cast<float *>(ws + B.dk);
@@ -716,11 +770,11 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     // Step 6 adjoint: dL/dhhat^l = g^l W_O[l]^T.
     for (int l = 0; l <= L; ++l)
         for (int m = 0; m < 2 * l + 1; ++m)
-            jobs[nj++] = ProjJob{grad_out, (long long)NC * C, wsel(w->w_o, l), gbuf, (long long)NC * C, l * l + m, 1, 0};
+            jobs[nj++] = ProjJob{grad_out, (long long)NC * C, wsel(w->w_o, l), dhh, (long long)NC * C, l * l + m, 1, 0};
     hipError_t e = launch_proj(jobs, nj, n, C, stream);
     if (e != hipSuccess) return hip_fail(e, "output projection adjoint");
     // Step 5 adjoint: dL/dm = EAAS^T with the target's own frame and w_tgt.
-    e = launch_eaas_adjoint(L, pos, gbuf, w->w_tgt, n, C, dm, stream);
+    e = launch_eaas_adjoint(L, pos, dhh, w->w_tgt, n, C, dm, stream);
     if (e != hipSuccess) return hip_fail(e, "target coupling adjoint");
     // Step 4 adjoint: dq (target pass), dL/dh' and dk (source pass).
     AttnBwdArgs a{};
@@ -731,9 +785,23 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     a.rz = reinterpret_cast<float *>(ws + B.rz);
     a.dd = reinterpret_cast<float *>(ws + B.dd);
     a.dq = dq; a.dk = dk; a.dhp = gbuf;
+    a.grad_pos = grad_pos;
+    a.m = reinterpret_cast<float *>(ws + B.mbuf);
     a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
     e = launch_attn_bwd(L, a, stream);
     if (e != hipSuccess) return hip_fail(e, "attention adjoint");
+    if (grad_pos && L > 0) {
+        // The encoding terms of dL/dpos, before dL/dv overwrites v.
+        CplTable *tab = reinterpret_cast<CplTable *>(ws + B.tab);
+        e = hipMemcpyAsync(tab, &cpl_table(L), sizeof(CplTable), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "copying the coupling table");
+        PosGradArgs pa{};
+        pa.pos = pos; pa.v = v; pa.dhp = gbuf; pa.m = a.m; pa.dhhat = dhh;
+        pa.w_src = w->w_src; pa.w_tgt = w->w_tgt; pa.tab = tab; pa.grad_pos = grad_pos;
+        pa.n = n; pa.C = C;
+        e = launch_pos_grad(L, pa, stream);
+        if (e != hipSuccess) return hip_fail(e, "encoding gradient");
+    }
     // Step 3 adjoint: dL/dv = EAAS^T with the source's own frame and w_src.
     e = launch_eaas_adjoint(L, pos, gbuf, w->w_src, n, C, v, stream);
     if (e != hipSuccess) return hip_fail(e, "source coupling adjoint");

@@ -562,10 +562,38 @@ struct AttnBwdArgs {
     float *mx, *rz, *dd;             // [n][H]
     float *dq, *dk;                  // [n][C]
     float *dhp;                      // [n][NC][C]
+    float *grad_pos;                 // optional [n][3]: the bias terms of dL/dpos (target pass writes, source pass adds)
+    float *m;                        // [n][NC][C] the message m_i, written when grad_pos is set
     int n, C, H, R;
     float cutoff;
 };
 hipError_t launch_attn_bwd(int L, const AttnBwdArgs &a, hipStream_t stream);
+
+// Coupling entries with l_f >= 1 for the encoding gradient: T_p[m_i, m_f, m_o] of path p
+// (real basis), grouped by the encoding component ef = l_f^2 + l_f + m_f.
+struct CplEntry {
+    float v;
+    uint16_t p;
+    uint8_t ei, eo;                  // input component l_i^2 + l_i + m_i, output l_o^2 + l_o + m_o
+};
+constexpr int kMaxCpl = 640;
+struct CplTable {
+    int32_t off[n_comp(kMaxL) + 1];  // entries of component ef: e[off[ef] .. off[ef + 1])
+    CplEntry e[kMaxCpl];
+};
+const CplTable &cpl_table(int lmax);   // host copy, built once
+// dL/dpos += the encoding terms: dL/dY_i = sum over the source coupling (v_i, dh'_i,
+// w_src) and the target coupling (m_i, dhhat_i, w_tgt) of sum_c w_p[c] T_p x[e_i][c]
+// g[e_o][c], through dY(r_i / |r_i|) / dr_i.  tab: a device copy of cpl_table(L).
+struct PosGradArgs {
+    const float *pos;                // [n][3]
+    const float *v, *dhp, *m, *dhhat; // [n][NC][C]
+    const float *w_src, *w_tgt;      // [P][C]
+    const CplTable *tab;
+    float *grad_pos;                 // [n][3], accumulated into
+    int n, C;
+};
+hipError_t launch_pos_grad(int L, const PosGradArgs &a, hipStream_t stream);
 
 hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, void *ws, size_t ws_bytes,
                                   int32_t *nbr_len, int32_t *order_out, hipStream_t stream);

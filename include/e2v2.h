@@ -215,11 +215,11 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Gradient of the layer with respect to its input features.
+ * Gradient of the layer with respect to its input features and positions.
  *
  * For L = sum(grad_out * out), with out the layer output of e2v2_attn_forward
- * for the same arguments, writes grad_h = dL/dh.  Positions, weights and the
- * neighbour list are held fixed.  The chain runs the forward's steps 2-3 again
+ * for the same arguments, writes grad_h = dL/dh.  Weights and the neighbour
+ * list are held fixed.  The chain runs the forward's steps 2-3 again
  * (projections, source coupling: E2Former-V2 explainer sections 2.3 and 3.1),
  * then the adjoint of each step in reverse: the output projection (h-hat^l
  * gradient = grad_out^l W_O[l]^T), the target coupling (the EAAS map with each
@@ -227,6 +227,14 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
  * attention of section 3.1 (per-head logit gradient alpha (dalpha - sum alpha
  * dalpha); the distance bias of the FlashSchNet page, section 2.1, has no h
  * dependence), the source coupling, and the input projections.
+ *
+ * grad_pos (optional, NULL to skip) receives dL/dpos [n][3] fp32 with the
+ * neighbour list held fixed: the terms through each node's encoding Y(r_i / |r_i|)
+ * in both couplings (dL/dY from the dense real Clebsch-Gordan form, which the EAAS
+ * form equals, explainer section 2.3, times the tangent gradient of the
+ * harmonics) and through every pair distance in the bias.  A node at the origin
+ * has no direction; its encoding is held constant there.  For a potential
+ * energy E = L the forces are -grad_pos.
  *
  * Storage must be fp32 (E2V2_ERR_UNSUPPORTED otherwise); pos fp32 [n][3], h and
  * grad_out fp32 [n][(lmax+1)^2][C], grad_h fp32 [n][(lmax+1)^2][C] (written whole).
@@ -244,8 +252,8 @@ size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t 
 e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h,
                                 const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
                                 const int32_t *nbr_idx, const int32_t *target_order, int32_t n,
-                                const float *grad_out, float *grad_h, void *workspace, size_t workspace_bytes,
-                                hipStream_t stream);
+                                const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Lists reused between rebuilds (Tessera article, neighbour reuse: the topology

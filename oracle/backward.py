@@ -36,9 +36,9 @@ def real_sh_torch(r, lmax: int):
     """so3.real_sh in torch (differentiable in r): the same closed forms of the
     direction r / |r|; a zero vector maps to Y_0 = 1, Y_{l>0} = 0, held constant
     (the direction, and so its derivative, is not defined there: B3)."""
-    nrm = torch.sqrt(torch.sum(r * r, dim=-1))
-    zero = nrm == 0.0
-    safe = torch.where(zero, torch.ones_like(nrm), nrm)
+    n2 = torch.sum(r * r, dim=-1)
+    zero = n2 == 0.0
+    safe = torch.sqrt(torch.where(zero, torch.ones_like(n2), n2))     # no sqrt at 0: its slope is infinite
     u = r / safe[..., None]
     x, y, z = u[..., 0], u[..., 1], u[..., 2]
     out = [torch.ones_like(x)]

@@ -1,5 +1,6 @@
-"""Parity of e2v2_layer_backward (dL/dh for L = sum(g * out), fp32 storage)
-against the fp64 oracle (oracle/backward.py, reverse-mode through the layer).
+"""Parity of e2v2_layer_backward (dL/dh and dL/dpos for L = sum(g * out), fp32
+storage) against the fp64 oracle (oracle/backward.py, reverse-mode through the
+layer).
 
 Tolerance: max |gpu - oracle| / RMS(oracle) <= 1e-4, the fp32 bar of the
 forward layer.  Small workloads compare every atom; the 32,768-atom workload,
@@ -27,15 +28,19 @@ def _g(wl, seed=11):
     return np.random.default_rng(seed).standard_normal(wl.h.shape).astype(np.float32).astype(np.float64)
 
 
-def _gpu_grad(gpu_lib, wl, g, order=None):
+def _gpu_grad(gpu_lib, wl, g, order=None, pos_grad=False):
     c = wl.cfg
     d = upload(wl)
     s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, 0)
     desc = gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
-    print(f"backward {c.name} n={c.n} L={c.lmax} H={c.heads}", flush=True)
-    gh = gpu_lib.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, f32(g), target_order=order)
+    print(f"backward {c.name} n={c.n} L={c.lmax} H={c.heads} pos={pos_grad}", flush=True)
+    gp = torch.full((c.n, 3), float("nan"), dtype=torch.float32, device="cuda") if pos_grad else None
+    r = gpu_lib.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, f32(g), target_order=order,
+                                    grad_pos=gp)
     torch.cuda.synchronize()
-    return gh.cpu().numpy(), (s, ln, ix)
+    if pos_grad:
+        return r[0].cpu().numpy(), r[1].cpu().numpy(), (s, ln, ix)
+    return r.cpu().numpy(), (s, ln, ix)
 
 
 def _oracle(wl, g, rows=None, targets=None):
@@ -57,6 +62,26 @@ def test_backward_full_fp32(gpu_lib, name):
     assert e < TOL, e
 
 
+def _oracle_pos(wl, g):
+    c = wl.cfg
+    rows = O.neighbors(wl.pos, c.cutoff, 0)
+    return OB.grad_pos_h(wl.pos, wl.h, **_weights(wl), g=g, lmax=c.lmax, heads=c.heads, cutoff=c.cutoff, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_position_gradient_full_fp32(gpu_lib, name):
+    """dL/dpos against the oracle; dL/dh is bit-identical with and without it."""
+    wl = W.make_workload(name)
+    g = _g(wl)
+    gh, gp, _ = _gpu_grad(gpu_lib, wl, g, pos_grad=True)
+    gh0, _ = _gpu_grad(gpu_lib, wl, g)
+    rp, rh = _oracle_pos(wl, g)
+    ep, eh = rel_err(gp, rp), rel_err(gh, rh)
+    record(f"position_gradient[{name}]", grad_pos=ep, grad_h=eh)
+    assert np.array_equal(gh, gh0)
+    assert ep < TOL and eh < TOL, (ep, eh)
+
+
 def _edge(n, L, heads, seed, nrbf=10):
     cfg = W.LayerConfig("edge", n, "uniform", n / 14.0 ** 3, 4.5, 0, L, 8 * heads, heads, nrbf, "fp32", seed)
     wl = W.make_workload(cfg)
@@ -69,12 +94,12 @@ def _edge(n, L, heads, seed, nrbf=10):
 def test_backward_shapes_and_edges(gpu_lib, n, L, heads, seed):
     wl = _edge(n, L, heads, seed)
     g = _g(wl, seed)
-    got, _ = _gpu_grad(gpu_lib, wl, g)
-    ref = _oracle(wl, g)
-    e = rel_err(got, ref)
-    record(f"backward_edge[{n},{L},{heads}]", grad_h=e)
-    assert e < TOL, e
-    assert np.all(got[1] == 0.0)
+    got, gp, _ = _gpu_grad(gpu_lib, wl, g, pos_grad=True)
+    rp, ref = _oracle_pos(wl, g)
+    e, ep = rel_err(got, ref), rel_err(gp, rp)
+    record(f"backward_edge[{n},{L},{heads}]", grad_h=e, grad_pos=ep)
+    assert e < TOL and ep < TOL, (e, ep)
+    assert np.all(got[1] == 0.0) and np.all(gp[1] == 0.0)
 
 
 def test_backward_order_invariant(gpu_lib):
@@ -89,11 +114,11 @@ def test_backward_order_invariant(gpu_lib):
 
 
 def test_backward_full_size_sampled(gpu_lib):
-    """32,768 atoms, 5 A uncapped list: the list is symmetric, and the gradient at
-    sampled atoms matches the oracle's exact sampled gradient."""
+    """32,768 atoms, 5 A uncapped list: the list is symmetric, and both gradients at
+    sampled atoms match the oracle's exact sampled gradients."""
     wl = W.make_workload("g4")
     g = _g(wl)
-    got, (s, ln, ix) = _gpu_grad(gpu_lib, wl, g)
+    got, gp, (s, ln, ix) = _gpu_grad(gpu_lib, wl, g, pos_grad=True)
     rows = rows_from_device(s, ln, ix)
     pairs = {(i, int(j)) for i, r in enumerate(rows) for j in r}
     assert all((j, i) in pairs for (i, j) in pairs)
@@ -108,9 +133,9 @@ def test_backward_full_size_sampled(gpu_lib):
     sub = np.unique(np.concatenate([tg] + [r.astype(np.int64) for r in trows]))
     loc = np.full(c.n, -1, dtype=np.int64)
     loc[sub] = np.arange(sub.size)
-    ref = OB.grad_h(wl.pos[sub], wl.h[sub], **_weights(wl), g=g[tg], lmax=c.lmax, heads=c.heads, cutoff=c.cutoff,
-                    rows=[loc[r] for r in trows], targets=loc[tg])
-    ref = ref[loc[sample]]
-    e = rel_err(got[sample], ref)
-    record("backward_sampled[g4]", grad_h=e)
-    assert e < TOL, e
+    rp, ref = OB.grad_pos_h(wl.pos[sub], wl.h[sub], **_weights(wl), g=g[tg], lmax=c.lmax, heads=c.heads,
+                            cutoff=c.cutoff, rows=[loc[r] for r in trows], targets=loc[tg])
+    e = rel_err(got[sample], ref[loc[sample]])
+    ep = rel_err(gp[sample], rp[loc[sample]])
+    record("backward_sampled[g4]", grad_h=e, grad_pos=ep)
+    assert e < TOL and ep < TOL, (e, ep)

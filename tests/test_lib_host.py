@@ -216,11 +216,11 @@ def test_stack_argument_errors(lib):
     assert lib.e2v2_stack_state_bytes(2, two, 1000, 64) - lib.e2v2_stack_state_bytes(2, one, 1000, 64) >= 1000 * 65 * 4
 
 
-def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE):
+def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE, gpos=None):
     w = B.Weights(*([ptr] * 7))
     wsb = ws_bytes if ws_bytes is not None else lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(desc), max(n, 0))
     return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, None, n, ptr, ptr,
-                                   ptr, wsb, None)
+                                   gpos, ptr, wsb, None)
 
 
 def test_backward_argument_errors_and_workspace(lib):
@@ -233,10 +233,11 @@ def test_backward_argument_errors_and_workspace(lib):
     assert _bwd(lib, d32, ptr=FAKE_MIS) == B.E2V2_ERR_ARG
     assert _bwd(lib, d32, ws_bytes=100) == B.E2V2_ERR_ARG
     assert "workspace" in lib.e2v2_last_error().decode()
+    assert _bwd(lib, d32, gpos=FAKE_MIS) == B.E2V2_ERR_ARG
     assert _bwd(lib, d32, n=0) == B.E2V2_OK
-    # the forward's fp32 workspace plus dL/dhhat (reused for dL/dh'), dL/dm, three
-    # per-head values and dq, dk per node
+    # the forward's fp32 workspace plus dL/dh', dL/dhhat, dL/dm, m, three per-head
+    # values and dq, dk per node
     fa = lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 2000) - lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 1000)
     ba = (lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 2000)
           - lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000))
-    assert abs((ba - fa) / 1000 - (2 * 9 * 128 * 4 + 3 * 16 * 4 + 2 * 128 * 4)) < 2
+    assert abs((ba - fa) / 1000 - (4 * 9 * 128 * 4 + 3 * 16 * 4 + 2 * 128 * 4)) < 2

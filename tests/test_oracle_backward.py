@@ -181,3 +181,21 @@ def test_bias_only_gradient_is_translation_and_rotation_invariant():
     assert scale > 1e-3
     assert np.max(np.abs(gp.sum(axis=0))) <= 1e-12 * scale * pos.shape[0]
     assert np.max(np.abs(np.cross(pos, gp).sum(axis=0))) <= 1e-12 * scale * pos.shape[0] * 5
+
+
+def test_position_gradient_finite_with_an_atom_at_the_origin():
+    """B3: the atom at the origin gets a finite gradient (bias terms only, its
+    encoding held constant), and every other atom's gradient still matches
+    central differences."""
+    pos, h, W, g = _system(16, extra=[[0.0, 0.0, 0.0]])
+    rows = layer.neighbors(pos, CUT)
+    assert rows[-1].size > 0
+    gp = _gpos(pos, h, W, g, rows)
+    assert np.all(np.isfinite(gp))
+    eps = 1e-6
+    L = lambda p: np.sum(g * _fwd_np(p, h, W, rows))
+    u = np.random.default_rng(3).standard_normal(pos.shape)
+    u[-1] = 0.0
+    fd = (L(pos + eps * u) - L(pos - eps * u)) / (2 * eps)
+    an = float(np.sum(gp * u))
+    assert abs(fd - an) <= 2e-6 * max(1.0, abs(an)), (fd, an)
