@@ -229,6 +229,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_source(const AttnBwdArgs A)
 // w_p[c] x[e_i][c] g[e_o][c] for (x, g, w) = (v, dh', w_src) and (m, dhhat, w_tgt).
 // Then dL/dr = (I - u u^T) grad P(u) / |r|, u = r / |r|, for the polynomial forms P
 // of the real harmonics (any extension off the sphere gives the same tangent part).
+// The entries are those of ygrad_terms (the selection rules of the real basis).
 
 // grad P of each harmonic component ef = 1 .. (L+1)^2 - 1 at (x, y, z), into G[ef - 1]
 template <int L>
@@ -259,37 +260,48 @@ __device__ __forceinline__ void sh_poly_grad(float x, float y, float z, float (*
     }
 }
 
-// One 64-lane block per node; the node's four feature rows are staged in LDS.
-template <int L, int C>
-__global__ __launch_bounds__(64) void k_pos_grad(const PosGradArgs A)
+// One wave per node, lanes as in the attention passes (2 channels each): the
+// node's four feature rows and both path-weight rows sit in registers, and the
+// contraction over the coupling entries is unrolled at compile time.
+template <int L, int H>
+__global__ __launch_bounds__(256) void k_pos_grad(const PosGradArgs A)
 {
-    constexpr int NC = n_comp(L);
-    __shared__ float sx[4][NC * C];
-    const int i = blockIdx.x, lane = threadIdx.x;
-    const size_t base = (size_t)i * NC * C;
-    for (int t = lane; t < NC * C; t += 64) {
-        sx[0][t] = A.v[base + t];
-        sx[1][t] = A.dhp[base + t];
-        sx[2][t] = A.m[base + t];
-        sx[3][t] = A.dhhat[base + t];
+    constexpr int NC = n_comp(L), C = 8 * H, P = path_count(L);
+    constexpr YTerms T = ygrad_terms<L>();
+    const int lane = threadIdx.x & 63;
+    const int i = __builtin_amdgcn_readfirstlane(node_of_wave(A.n, nullptr));
+    if (i < 0) return;
+    const bool act = lane < 4 * H;
+    const int c0 = act ? 2 * lane : 0;
+    float2 xs[NC], gs[NC], xt[NC], gt[NC], ws[P], wt[P];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+        const size_t o = ((size_t)i * NC + e) * C + c0;
+        xs[e] = ld2(A.v + o);
+        gs[e] = ld2(A.dhp + o);
+        xt[e] = ld2(A.m + o);
+        gt[e] = ld2(A.dhhat + o);
     }
-    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        ws[p] = ld2(A.w_src + p * C + c0);
+        wt[p] = ld2(A.w_tgt + p * C + c0);
+    }
+    float acc[NC];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int q = 0; q < T.n; ++q) {
+        const YTerm t = T.t[q];
+        float s = ws[t.p].x * xs[t.ei].x * gs[t.eo].x;
+        s = fmaf(ws[t.p].y * xs[t.ei].y, gs[t.eo].y, s);
+        s = fmaf(wt[t.p].x * xt[t.ei].x, gt[t.eo].x, s);
+        s = fmaf(wt[t.p].y * xt[t.ei].y, gt[t.eo].y, s);
+        acc[t.ef] = fmaf(A.tval[q], s, acc[t.ef]);
+    }
     float gy[NC];
 #pragma unroll
-    for (int ef = 1; ef < NC; ++ef) {
-        float acc = 0.f;
-        const int q0 = A.tab->off[ef], q1 = A.tab->off[ef + 1];
-        for (int qq = q0; qq < q1; ++qq) {
-            const CplEntry e = A.tab->e[qq];
-            const float *ws = A.w_src + (size_t)e.p * C, *wt = A.w_tgt + (size_t)e.p * C;
-            for (int c = lane; c < C; c += 64) {
-                const float src = ws[c] * sx[0][e.ei * C + c] * sx[1][e.eo * C + c];
-                const float tgt = wt[c] * sx[2][e.ei * C + c] * sx[3][e.eo * C + c];
-                acc = fmaf(e.v, src + tgt, acc);
-            }
-        }
-        gy[ef] = wave_sum_if(acc, true);
-    }
+    for (int ef = 1; ef < NC; ++ef) gy[ef] = wave_sum_if(acc[ef], act);
     if (lane != 0) return;
     const float rx = A.pos[3 * (size_t)i], ry = A.pos[3 * (size_t)i + 1], rz = A.pos[3 * (size_t)i + 2];
     const float nrm = sqrtf(fmaf(rz, rz, fmaf(ry, ry, rx * rx)));
@@ -313,11 +325,11 @@ __global__ __launch_bounds__(64) void k_pos_grad(const PosGradArgs A)
 template <int L>
 static hipError_t launch_pos_grad_l(const PosGradArgs &a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)a.n);
-    switch (a.C) {
-    case 32: k_pos_grad<L, 32><<<grid, 64, 0, stream>>>(a); break;
-    case 64: k_pos_grad<L, 64><<<grid, 64, 0, stream>>>(a); break;
-    case 128: k_pos_grad<L, 128><<<grid, 64, 0, stream>>>(a); break;
+    const dim3 grid((unsigned)((a.n + 3) / 4));
+    switch (a.H) {
+    case 4: k_pos_grad<L, 4><<<grid, 256, 0, stream>>>(a); break;
+    case 8: k_pos_grad<L, 8><<<grid, 256, 0, stream>>>(a); break;
+    case 16: k_pos_grad<L, 16><<<grid, 256, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

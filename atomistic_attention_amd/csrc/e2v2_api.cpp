@@ -217,41 +217,36 @@ double coupling_entry(int li, int lf, int lo, int mi, int mf, int mo)
     return ((li + lf + lo) & 1) ? acc.imag() : acc.real();
 }
 
-CplTable g_cpl[kMaxL + 1];
-std::once_flag g_once_cpl;
+float g_yval[kMaxL + 1][kMaxYTerms];
+std::once_flag g_once_yval;
 
-void build_cpl(int lmax, CplTable &t)
+template <int L>
+void build_yval(float *out)
 {
-    std::memset(&t, 0, sizeof(t));
-    int n = 0;
-    for (int lf = 1; lf <= lmax; ++lf)
-        for (int mf = -lf; mf <= lf; ++mf) {
-            const int ef = lf * lf + lf + mf;
-            t.off[ef] = n;
-            for (int lo = 0; lo <= lmax; ++lo)
-                for (int li = 0; li <= lmax; ++li) {
-                    if (!is_path(li, lf, lo)) continue;
-                    const int p = path_index(lmax, li, lf, lo);
-                    for (int mi = -li; mi <= li; ++mi)
-                        for (int mo = -lo; mo <= lo; ++mo) {
-                            const double v = coupling_entry(li, lf, lo, mi, mf, mo);
-                            if (std::fabs(v) < 1e-12 || n >= kMaxCpl) continue;
-                            t.e[n++] = CplEntry{(float)v, (uint16_t)p, (uint8_t)(li * li + li + mi),
-                                                (uint8_t)(lo * lo + lo + mo)};
-                        }
-                }
-        }
-    for (int ef = (lmax + 1) * (lmax + 1); ef <= n_comp(kMaxL); ++ef) t.off[ef] = n;
+    constexpr YTerms T = ygrad_terms<L>();
+    static_assert(T.n <= kMaxYTerms, "coupling entry table too small");
+    for (int q = 0; q < T.n; ++q) {
+        const YTerm &t = T.t[q];
+        auto lm = [](int e, int &l, int &m) { l = 0; while ((l + 1) * (l + 1) <= e) ++l; m = e - l * l - l; };
+        int li, mi, lf, mf, lo, mo;
+        lm(t.ei, li, mi);
+        lm(t.ef, lf, mf);
+        lm(t.eo, lo, mo);
+        out[q] = (float)coupling_entry(li, lf, lo, mi, mf, mo);
+    }
 }
 
 }  // namespace
 
-const CplTable &cpl_table(int lmax)
+const float *ygrad_values(int lmax)
 {
-    std::call_once(g_once_cpl, [] {
-        for (int l = 0; l <= kMaxL; ++l) build_cpl(l, g_cpl[l]);
+    std::call_once(g_once_yval, [] {
+        std::memset(g_yval, 0, sizeof(g_yval));
+        build_yval<1>(g_yval[1]);
+        build_yval<2>(g_yval[2]);
+        build_yval<3>(g_yval[3]);
     });
-    return g_cpl[lmax];
+    return g_yval[lmax];
 }
 
 const Tables &host_tables()
@@ -707,7 +702,7 @@ BwdWs bwd_ws(const e2v2_layer_desc &d, int n)
     w.dd = o; o += al256(N * H * 4);
     w.dq = o; o += al256(N * C * 4);
     w.dk = o; o += al256(N * C * 4);
-    w.tab = o; o += al256(sizeof(CplTable));
+    w.tab = o; o += al256(sizeof(float) * kMaxYTerms);
     w.total = o + 256;
     return w;
 }
@@ -792,13 +787,13 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     if (e != hipSuccess) return hip_fail(e, "attention adjoint");
     if (grad_pos && L > 0) {
         // The encoding terms of dL/dpos, before dL/dv overwrites v.
-        CplTable *tab = reinterpret_cast<CplTable *>(ws + B.tab);
-        e = hipMemcpyAsync(tab, &cpl_table(L), sizeof(CplTable), hipMemcpyHostToDevice, stream);
+        float *tval = reinterpret_cast<float *>(ws + B.tab);
+        e = hipMemcpyAsync(tval, ygrad_values(L), sizeof(float) * kMaxYTerms, hipMemcpyHostToDevice, stream);
         if (e != hipSuccess) return hip_fail(e, "copying the coupling table");
         PosGradArgs pa{};
         pa.pos = pos; pa.v = v; pa.dhp = gbuf; pa.m = a.m; pa.dhhat = dhh;
-        pa.w_src = w->w_src; pa.w_tgt = w->w_tgt; pa.tab = tab; pa.grad_pos = grad_pos;
-        pa.n = n; pa.C = C;
+        pa.w_src = w->w_src; pa.w_tgt = w->w_tgt; pa.tval = tval; pa.grad_pos = grad_pos;
+        pa.n = n; pa.C = C; pa.H = desc->heads;
         e = launch_pos_grad(L, pa, stream);
         if (e != hipSuccess) return hip_fail(e, "encoding gradient");
     }

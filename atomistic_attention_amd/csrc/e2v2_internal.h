@@ -569,29 +569,58 @@ struct AttnBwdArgs {
 };
 hipError_t launch_attn_bwd(int L, const AttnBwdArgs &a, hipStream_t stream);
 
-// Coupling entries with l_f >= 1 for the encoding gradient: T_p[m_i, m_f, m_o] of path p
-// (real basis), grouped by the encoding component ef = l_f^2 + l_f + m_f.
-struct CplEntry {
-    float v;
-    uint16_t p;
-    uint8_t ei, eo;                  // input component l_i^2 + l_i + m_i, output l_o^2 + l_o + m_o
+// Entries of the real coupling tensors T_p[m_i, m_f, m_o] with l_f >= 1 that can be
+// nonzero, for the encoding gradient: in the complex basis M = mu_i + mu_f, so in
+// the real basis |m_o| is |m_i| + |m_f| or ||m_i| - |m_f||, and the numbers of
+// sine-type (m < 0) factors among the three has the parity of l_i + l_f + l_o
+// (real part for even, imaginary part for odd).  For l_max <= 2 this is exactly
+// the nonzero set.  The order is fixed at compile time; the host fills the
+// values in the same order.
+struct YTerm {
+    int p, ei, ef, eo;               // path; components l^2 + l + m of input, encoding, output
 };
-constexpr int kMaxCpl = 640;
-struct CplTable {
-    int32_t off[n_comp(kMaxL) + 1];  // entries of component ef: e[off[ef] .. off[ef + 1])
-    CplEntry e[kMaxCpl];
+constexpr int kMaxYTerms = 640;
+struct YTerms {
+    int n;
+    YTerm t[kMaxYTerms];
 };
-const CplTable &cpl_table(int lmax);   // host copy, built once
+template <int L>
+constexpr YTerms ygrad_terms()
+{
+    YTerms r = {};
+    int n = 0;
+    for (int lf = 1; lf <= L; ++lf)
+        for (int mf = -lf; mf <= lf; ++mf)
+            for (int lo = 0; lo <= L; ++lo)
+                for (int li = 0; li <= L; ++li) {
+                    if (!is_path(li, lf, lo)) continue;
+                    const int odd = (li + lf + lo) & 1;
+                    for (int mi = -li; mi <= li; ++mi)
+                        for (int mo = -lo; mo <= lo; ++mo) {
+                            const int ai = mi < 0 ? -mi : mi, af = mf < 0 ? -mf : mf, ao = mo < 0 ? -mo : mo;
+                            const int df = ai > af ? ai - af : af - ai;
+                            if (ao != ai + af && ao != df) continue;
+                            if (((mi < 0) ^ (mf < 0) ^ (mo < 0)) != odd) continue;
+                            r.t[n++] = YTerm{path_index(L, li, lf, lo), li * li + li + mi, lf * lf + lf + mf,
+                                             lo * lo + lo + mo};
+                        }
+                }
+    r.n = n;
+    return r;
+}
+// Host values T_p[m_i, m_f, m_o] in the order of ygrad_terms<lmax>() (built once).
+const float *ygrad_values(int lmax);
+
 // dL/dpos += the encoding terms: dL/dY_i = sum over the source coupling (v_i, dh'_i,
 // w_src) and the target coupling (m_i, dhhat_i, w_tgt) of sum_c w_p[c] T_p x[e_i][c]
-// g[e_o][c], through dY(r_i / |r_i|) / dr_i.  tab: a device copy of cpl_table(L).
+// g[e_o][c], through dY(r_i / |r_i|) / dr_i.  tval: a device copy of ygrad_values(L).
 struct PosGradArgs {
     const float *pos;                // [n][3]
     const float *v, *dhp, *m, *dhhat; // [n][NC][C]
     const float *w_src, *w_tgt;      // [P][C]
-    const CplTable *tab;
+    const float *tval;
     float *grad_pos;                 // [n][3], accumulated into
-    int n, C;
+    int n, C, H;
 };
 hipError_t launch_pos_grad(int L, const PosGradArgs &a, hipStream_t stream);
 

@@ -148,8 +148,8 @@ def stack_bench(B, W, torch, steps: int = 60, warmup: int = 10) -> dict:
 
 
 def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g4") -> dict:
-    """Feature gradient dL/dh of one layer (e2v2_layer_backward: the forward's
-    projections and source coupling, then the adjoint chain) on the 32,768-atom
+    """Gradient of one layer (e2v2_layer_backward: the forward's projections and
+    source coupling, then the adjoint chain; dL/dh, and dL/dh with dL/dpos) on the 32,768-atom
     system with an uncapped 5 A list and fp32 storage, next to the forward of the
     same layer.  Both timed on resident inputs and lists built beforehand, in the
     list's spatial order."""
@@ -166,16 +166,22 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
     bws = torch.empty(B.backward_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
     fws = torch.empty(B.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
 
+    gp = torch.empty((c.n, 3), dtype=torch.float32, device=dev)
+
     def bwd():
         B.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, g, grad_h=gh, workspace=bws,
                               target_order=order)
+
+    def bwd_pos():
+        B.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, g, grad_h=gh, workspace=bws,
+                              target_order=order, grad_pos=gp)
 
     def fwd():
         B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, out=out, workspace=fws,
                             target_order=order)
 
     res = {}
-    for key, fn in (("backward", bwd), ("forward", fwd)):
+    for key, fn in (("backward", bwd), ("backward_pos", bwd_pos), ("forward", fwd)):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -194,9 +200,12 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
     return {"workload": f"{name}: {c.n} atoms, {c.geometry} at {c.density} atoms/A^3, cutoff {c.cutoff} A "
                         f"uncapped (symmetric list), l_max={c.lmax}, C={C}, {H} heads, {c.n_rbf} RBFs, "
                         f"fp32 storage",
-            "what": "dL/dh for L = sum(g * out), g fixed; positions and weights held fixed",
-            "nnz": nnz, "steps": steps, "ms_backward": res["backward"], "ms_forward_same_layer": res["forward"],
+            "what": "dL/dh for L = sum(g * out), g fixed (ms_backward); dL/dh and dL/dpos together "
+                    "(ms_backward_with_positions); weights and the neighbour list held fixed",
+            "nnz": nnz, "steps": steps, "ms_backward": res["backward"],
+            "ms_backward_with_positions": res["backward_pos"], "ms_forward_same_layer": res["forward"],
             "pairs_per_s_backward": nnz / (res["backward"] * 1e-3),
+            "pairs_per_s_backward_with_positions": nnz / (res["backward_pos"] * 1e-3),
             "attention_adjoint_algorithmic_bytes": per_pair * nnz + per_node * c.n}
 
 
