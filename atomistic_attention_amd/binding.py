@@ -106,10 +106,10 @@ def load(path: str = LIB_PATH):
     lib.e2v2_stack_forward.argtypes = [i32, ctypes.POINTER(LayerDesc), ctypes.POINTER(Weights), vp, vp, i32, i32,
                                        ctypes.POINTER(RebuildPolicy), vp, sz, vp, vp, sz, vp]
     lib.e2v2_stack_forward.restype = ctypes.c_int
-    lib.e2v2_layer_backward_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32]
+    lib.e2v2_layer_backward_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32, i64]
     lib.e2v2_layer_backward_workspace_bytes.restype = sz
-    lib.e2v2_layer_backward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, vp,
-                                        i32, vp, vp, vp, vp, sz, vp]
+    lib.e2v2_layer_backward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, i64,
+                                        vp, i32, vp, vp, vp, vp, sz, vp]
     lib.e2v2_layer_backward.restype = ctypes.c_int
     lib.e2v2_status_string.argtypes = [ctypes.c_int]
     lib.e2v2_status_string.restype = ctypes.c_char_p
@@ -325,14 +325,14 @@ def e2v2_attn_aggregate(desc: LayerDesc, weights: dict, nbr_start, nbr_len, nbr_
     return out
 
 
-def backward_workspace_bytes(desc: LayerDesc, n: int) -> int:
-    return int(load().e2v2_layer_backward_workspace_bytes(ctypes.byref(desc), n))
+def backward_workspace_bytes(desc: LayerDesc, n: int, max_entries: int) -> int:
+    return int(load().e2v2_layer_backward_workspace_bytes(ctypes.byref(desc), n, max_entries))
 
 
 def e2v2_layer_backward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len, nbr_idx, grad_out,
                         grad_h=None, workspace=None, stream=None,
                         target_order: torch.Tensor | None = None, grad_pos: torch.Tensor | None = None):
-    """dL/dh for L = sum(grad_out * layer(pos, h)) (fp32 storage, symmetric neighbour list).
+    """dL/dh for L = sum(grad_out * layer(pos, h)) (fp32 storage; any neighbour list).
     With grad_pos (a [n, 3] fp32 device tensor) also dL/dpos; returns grad_h, or
     (grad_h, grad_pos) when grad_pos is given."""
     lib = load()
@@ -350,7 +350,8 @@ def e2v2_layer_backward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_l
     if grad_h is None:
         grad_h = torch.empty(h.shape, dtype=torch.float32, device=h.device)
     _dev(grad_h, torch.float32, "grad_h")
-    wsb = backward_workspace_bytes(desc, n)
+    max_entries = nbr_idx.numel()
+    wsb = backward_workspace_bytes(desc, n, max_entries)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=h.device)
     if grad_pos is not None:
@@ -358,7 +359,7 @@ def e2v2_layer_backward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_l
         if tuple(grad_pos.shape) != (n, 3):
             raise ValueError(f"grad_pos shape {tuple(grad_pos.shape)} != ({n}, 3)")
     _check(lib.e2v2_layer_backward(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), _ptr(nbr_start),
-                                   _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), n, _ptr(grad_out),
+                                   _ptr(nbr_len), _ptr(nbr_idx), max_entries, _ptr(target_order), n, _ptr(grad_out),
                                    _ptr(grad_h), _ptr(grad_pos), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
     return grad_h if grad_pos is None else (grad_h, grad_pos)

@@ -16,9 +16,9 @@
 // (running maximum M): Z = sum e_j, A = sum e_j dalpha_j, B = sum e_j dalpha_j k_j,
 // K = sum e_j k_j with e_j = 2^(s2_j - M), then dd = A / Z and
 // dq = (B - dd K) / (Z sqrt(8)).  It stores M and 1 / Z per head.
-// Source pass: one wave per source j walks row j of the same list -- for a list
-// within a cutoff, i is in row j exactly when j is in row i, so row j names the
-// targets that read source j -- recomputes s_ij exactly as the target pass did
+// Source pass: one wave per source j walks row j of the transposed list (the
+// targets that read source j, in increasing order), recomputes s_ij exactly as
+// the target pass did
 // (same operations, same order), alpha_ij = 2^(s2_ij - M_i) / Z_i, and
 // accumulates dh'_j and dk_j in registers: every row written by one wave, no
 // atomics (FlashSchNet page, section 2.3: owner-computes rows).
@@ -161,8 +161,9 @@ __global__ __launch_bounds__(256) void k_attn_bwd_source(const AttnBwdArgs A)
 #pragma unroll
     for (int e = 0; e < NC; ++e) hv[e] = ld2(A.hp + ((size_t)j * NC + e) * C + c0);
     const float4 pj4 = A.pos4[j];
-    const int start = __builtin_amdgcn_readfirstlane(A.nbr_start[j]);
-    const int len = __builtin_amdgcn_readfirstlane(A.nbr_len[j]);
+    const long long s0 = A.src_start[j], s1 = A.src_start[j + 1];
+    const int start = __builtin_amdgcn_readfirstlane((int)s0);
+    const int len = __builtin_amdgcn_readfirstlane((int)((s1 < A.src_cap ? s1 : A.src_cap) - s0));
 
     float2 dh[NC];
 #pragma unroll
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_source(const AttnBwdArgs A)
     float2 dk = make_float2(0.f, 0.f);
     float3 Fj = make_float3(0.f, 0.f, 0.f);              // POS: sum_i ds_ij b'(d_ij) (r_j - r_i) / d_ij
     for (int p = 0; p < len; ++p) {
-        const int i = __builtin_amdgcn_readfirstlane(A.nbr_idx[start + p]);
+        const int i = __builtin_amdgcn_readfirstlane(A.src_idx[start + p]);
         if (i < 0 || i >= A.n) continue;                 // wave-uniform
         const float2 qi = ld2(A.q + (size_t)i * C + c0);
         float2 dmi[NC];

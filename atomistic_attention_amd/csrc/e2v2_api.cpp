@@ -685,9 +685,9 @@ e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, con
 namespace {
 // The forward workspace (q, k, v, h', frames) followed by the gradient buffers.
 struct BwdWs {
-    size_t fwd, gbuf, dhh, dm, mbuf, mx, rz, dd, dq, dk, tab, total;
+    size_t fwd, gbuf, dhh, dm, mbuf, mx, rz, dd, dq, dk, tab, tcnt, tstart, tcur, tidx, total;
 };
-BwdWs bwd_ws(const e2v2_layer_desc &d, int n)
+BwdWs bwd_ws(const e2v2_layer_desc &d, int n, long long max_entries)
 {
     const size_t N = (size_t)n, C = (size_t)d.channels, NC = (size_t)n_comp(d.lmax), H = (size_t)d.heads;
     BwdWs w{};
@@ -703,6 +703,10 @@ BwdWs bwd_ws(const e2v2_layer_desc &d, int n)
     w.dq = o; o += al256(N * C * 4);
     w.dk = o; o += al256(N * C * 4);
     w.tab = o; o += al256(sizeof(float) * kMaxYTerms);
+    w.tcnt = o; o += al256((N + 1) * 4);         // the transposed list
+    w.tstart = o; o += al256((N + 1) * 4);
+    w.tcur = o; o += al256((N + 1) * 4);
+    w.tidx = o; o += al256((size_t)(max_entries > 0 ? max_entries : 1) * 4);
     w.total = o + 256;
     return w;
 }
@@ -710,21 +714,26 @@ BwdWs bwd_ws(const e2v2_layer_desc &d, int n)
 
 extern "C" {
 
-size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t n)
+size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t n, int64_t max_entries)
 {
-    if (!desc || n < 0 || desc->lmax < 0 || desc->lmax > kMaxL || desc->channels <= 0 || desc->heads <= 0) return 0;
-    return bwd_ws(*desc, n).total;
+    if (!desc || n < 0 || max_entries < 0 || desc->lmax < 0 || desc->lmax > kMaxL || desc->channels <= 0 ||
+        desc->heads <= 0)
+        return 0;
+    return bwd_ws(*desc, n, max_entries).total;
 }
 
 e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
                                 const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
-                                const int32_t *target_order, int32_t n, const float *grad_out, float *grad_h,
-                                float *grad_pos, void *workspace, size_t workspace_bytes, hipStream_t stream)
+                                int64_t max_entries, const int32_t *target_order, int32_t n,
+                                const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream)
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
     if (desc->storage != E2V2_FP32) return fail(E2V2_ERR_UNSUPPORTED, "the feature gradient needs fp32 storage");
     if (n < 0) return fail(E2V2_ERR_ARG, "n < 0");
+    if (max_entries < 0 || max_entries >= INT32_MAX) return fail(E2V2_ERR_ARG, "max_entries %lld out of range",
+                                                                 (long long)max_entries);
     if (n == 0) return E2V2_OK;
     if (!w) return fail(E2V2_ERR_ARG, "weights is NULL");
     for (const void *p : {(const void *)pos, (const void *)h, (const void *)w->w_q, (const void *)w->w_k,
@@ -736,7 +745,7 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     }
     if ((target_order && !aligned16(target_order)) || (grad_pos && !aligned16(grad_pos)))
         return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
-    const BwdWs B = bwd_ws(*desc, n);
+    const BwdWs B = bwd_ws(*desc, n, max_entries);
     if (workspace_bytes < B.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, B.total);
     char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
     const AttnWs F = attn_ws(*desc, n);
@@ -771,10 +780,16 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     // Step 5 adjoint: dL/dm = EAAS^T with the target's own frame and w_tgt.
     e = launch_eaas_adjoint(L, pos, dhh, w->w_tgt, n, C, dm, stream);
     if (e != hipSuccess) return hip_fail(e, "target coupling adjoint");
-    // Step 4 adjoint: dq (target pass), dL/dh' and dk (source pass).
+    // Step 4 adjoint: dq (target pass), dL/dh' and dk (source pass, over the transposed list).
+    int32_t *tstart = reinterpret_cast<int32_t *>(ws + B.tstart);
+    int32_t *tidx = reinterpret_cast<int32_t *>(ws + B.tidx);
+    e = launch_transpose_list(nbr_start, nbr_len, nbr_idx, n, max_entries, reinterpret_cast<int32_t *>(ws + B.tcnt),
+                              tstart, reinterpret_cast<int32_t *>(ws + B.tcur), tidx, stream);
+    if (e != hipSuccess) return hip_fail(e, "transposed list");
     AttnBwdArgs a{};
     a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dm = dm;
     a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
+    a.src_start = tstart; a.src_idx = tidx; a.src_cap = max_entries;
     a.w_rbf = w->w_rbf;
     a.mx = reinterpret_cast<float *>(ws + B.mx);
     a.rz = reinterpret_cast<float *>(ws + B.rz);

@@ -805,6 +805,78 @@ __global__ __launch_bounds__(256) void k_max_disp2(const float *__restrict__ pos
 }
 
 // ---------------------------------------------------------------- host launchers
+// ---------------------------------------------------------------- transposed list
+// The sources' view of a neighbour list: row j of the transposed list holds every
+// i whose row contains j (an entry listed twice appears twice), in increasing
+// order, so sums over it run in a fixed order.  Entries < 0 or >= n are skipped,
+// as the layer skips them.  Built by count, scan, fill, then a sort per row.
+__global__ void k_tzero(int32_t *cnt, int n)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t <= n) cnt[t] = 0;
+}
+__global__ __launch_bounds__(256) void k_tcount(const int32_t *__restrict__ start, const int32_t *__restrict__ len,
+                                                const int32_t *__restrict__ idx, int n, int32_t *cnt)
+{
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (i >= n) return;
+    const int s0 = start[i], l = len[i];
+    for (int p = lane; p < l; p += 64) {
+        const int j = idx[s0 + p];
+        if (j >= 0 && j < n) atomicAdd(&cnt[j], 1);
+    }
+}
+__global__ __launch_bounds__(256) void k_tfill(const int32_t *__restrict__ start, const int32_t *__restrict__ len,
+                                               const int32_t *__restrict__ idx, int n, long long cap, int32_t *cur,
+                                               int32_t *tidx)
+{
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (i >= n) return;
+    const int s0 = start[i], l = len[i];
+    for (int p = lane; p < l; p += 64) {
+        const int j = idx[s0 + p];
+        if (j < 0 || j >= n) continue;
+        const int slot = atomicAdd(&cur[j], 1);
+        if (slot < cap) tidx[slot] = i;
+    }
+}
+// One 64-lane block per row: a register bitonic sort up to 1024 entries, an
+// odd-even transposition sort in place beyond.
+__global__ __launch_bounds__(64) void k_tsort(const int32_t *__restrict__ tstart, int n, long long cap, int32_t *tidx)
+{
+    const int j = blockIdx.x, lane = threadIdx.x;
+    const long long a = tstart[j], b0 = tstart[j + 1];
+    const long long b = b0 < cap ? b0 : cap;
+    const int cnt = b > a ? (int)(b - a) : 0;
+    int32_t *row = tidx + a;
+    if (cnt <= 1) return;
+    if (cnt <= 1024) {
+        wave_write_sorted(row, cnt, row, lane);
+        return;
+    }
+    for (int ph = 0; ph < cnt; ++ph) {
+        for (int q = 2 * lane + (ph & 1); q + 1 < cnt; q += 128) {
+            const int x = row[q], y = row[q + 1];
+            if (x > y) { row[q] = y; row[q + 1] = x; }
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_transpose_list(const int32_t *start, const int32_t *len, const int32_t *idx, int n,
+                                 long long cap, int32_t *cnt, int32_t *tstart, int32_t *cur, int32_t *tidx,
+                                 hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    k_tzero<<<(unsigned)((n + 256) / 256), 256, 0, stream>>>(cnt, n);
+    const unsigned g4 = (unsigned)((n + 3) / 4);
+    k_tcount<<<g4, 256, 0, stream>>>(start, len, idx, n, cnt);
+    k_scan<<<1, 1024, 0, stream>>>(cnt, nullptr, n, tstart, cur, nullptr);
+    k_tfill<<<g4, 256, 0, stream>>>(start, len, idx, n, cap, cur, tidx);
+    k_tsort<<<(unsigned)n, 64, 0, stream>>>(tstart, n, cap, tidx);
+    return hipGetLastError();
+}
+
 static inline unsigned nblk(long long n, int b) { return (unsigned)((n + b - 1) / b); }
 
 hipError_t launch_filter_rows(const float *pos, int n, float cutoff, const int32_t *start, const int32_t *len,

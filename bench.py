@@ -163,7 +163,7 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
     g = torch.from_numpy(np.random.default_rng(11).standard_normal(wl.h.shape).astype(np.float32)).to(dev)
     gh = torch.empty_like(g)
     out = torch.empty_like(g)
-    bws = torch.empty(B.backward_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
+    bws = torch.empty(B.backward_workspace_bytes(desc, c.n, ix.numel()), dtype=torch.uint8, device=dev)
     fws = torch.empty(B.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
 
     gp = torch.empty((c.n, 3), dtype=torch.float32, device=dev)
@@ -201,7 +201,8 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
                         f"uncapped (symmetric list), l_max={c.lmax}, C={C}, {H} heads, {c.n_rbf} RBFs, "
                         f"fp32 storage",
             "what": "dL/dh for L = sum(g * out), g fixed (ms_backward); dL/dh and dL/dpos together "
-                    "(ms_backward_with_positions); weights and the neighbour list held fixed",
+                    "(ms_backward_with_positions); weights and the neighbour list held fixed; each call builds "
+                    "its transposed list",
             "nnz": nnz, "steps": steps, "ms_backward": res["backward"],
             "ms_backward_with_positions": res["backward_pos"], "ms_forward_same_layer": res["forward"],
             "pairs_per_s_backward": nnz / (res["backward"] * 1e-3),

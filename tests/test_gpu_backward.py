@@ -13,7 +13,7 @@ import torch
 from atomistic_attention_amd import workloads as W
 from oracle import backward as OB
 from oracle import layer as O
-from tests._helpers import f32, record, rel_err, rows_from_device, upload
+from tests._helpers import csr_from_rows, f32, record, rel_err, rows_from_device, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -28,10 +28,13 @@ def _g(wl, seed=11):
     return np.random.default_rng(seed).standard_normal(wl.h.shape).astype(np.float32).astype(np.float64)
 
 
-def _gpu_grad(gpu_lib, wl, g, order=None, pos_grad=False):
+def _gpu_grad(gpu_lib, wl, g, order=None, pos_grad=False, K=0, rows=None):
     c = wl.cfg
     d = upload(wl)
-    s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, 0)
+    if rows is not None:
+        s, ln, ix = csr_from_rows(rows)
+    else:
+        s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, K)
     desc = gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
     print(f"backward {c.name} n={c.n} L={c.lmax} H={c.heads} pos={pos_grad}", flush=True)
     gp = torch.full((c.n, 3), float("nan"), dtype=torch.float32, device="cuda") if pos_grad else None
@@ -100,6 +103,43 @@ def test_backward_shapes_and_edges(gpu_lib, n, L, heads, seed):
     record(f"backward_edge[{n},{L},{heads}]", grad_h=e, grad_pos=ep)
     assert e < TOL and ep < TOL, (e, ep)
     assert np.all(got[1] == 0.0) and np.all(gp[1] == 0.0)
+
+
+def test_backward_capped_asymmetric_list(gpu_lib):
+    """A K-capped list whose cap binds is not symmetric: the source side walks the
+    transposed list the call builds, so both gradients still match the oracle."""
+    cfg = W.LayerConfig("capped", 600, "uniform", 0.1, 5.0, 10, 2, 64, 8, 16, "fp32", 41)
+    wl = W.make_workload(cfg)
+    g = _g(wl, 41)
+    rows = O.neighbors(wl.pos, cfg.cutoff, cfg.max_neighbors)
+    pairs = {(i, int(j)) for i, r in enumerate(rows) for j in r}
+    assert any((j, i) not in pairs for (i, j) in pairs)
+    gh, gp, _ = _gpu_grad(gpu_lib, wl, g, pos_grad=True, K=cfg.max_neighbors)
+    rp, rh = OB.grad_pos_h(wl.pos, wl.h, **_weights(wl), g=g, lmax=cfg.lmax, heads=cfg.heads, cutoff=cfg.cutoff,
+                           rows=rows)
+    e, ep = rel_err(gh, rh), rel_err(gp, rp)
+    record("backward_capped[600,K=10]", grad_h=e, grad_pos=ep)
+    assert e < TOL and ep < TOL, (e, ep)
+
+
+def test_backward_invalid_and_repeated_entries(gpu_lib):
+    """Rows holding -1 and out-of-range entries (skipped) and an atom listed twice
+    (counted twice, as the forward counts it)."""
+    wl = _edge(120, 2, 8, 43)
+    c = wl.cfg
+    g = _g(wl, 43)
+    rows = [r.copy() for r in O.neighbors(wl.pos, c.cutoff, 0)]
+    dirty = list(rows)
+    for i in (2, 5, 9):
+        if rows[i].size:
+            dirty[i] = np.concatenate([rows[i], [-1, c.n + 7, rows[i][0]]]).astype(np.int32)
+            rows[i] = np.concatenate([rows[i], [rows[i][0]]]).astype(np.int32)
+    gh, gp, _ = _gpu_grad(gpu_lib, wl, g, pos_grad=True, rows=dirty)
+    rp, rh = OB.grad_pos_h(wl.pos, wl.h, **_weights(wl), g=g, lmax=c.lmax, heads=c.heads, cutoff=c.cutoff,
+                           rows=rows)
+    e, ep = rel_err(gh, rh), rel_err(gp, rp)
+    record("backward_dirty_rows", grad_h=e, grad_pos=ep)
+    assert e < TOL and ep < TOL, (e, ep)
 
 
 def test_backward_order_invariant(gpu_lib):

@@ -216,11 +216,12 @@ def test_stack_argument_errors(lib):
     assert lib.e2v2_stack_state_bytes(2, two, 1000, 64) - lib.e2v2_stack_state_bytes(2, one, 1000, 64) >= 1000 * 65 * 4
 
 
-def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE, gpos=None):
+def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE, gpos=None, entries=100):
     w = B.Weights(*([ptr] * 7))
-    wsb = ws_bytes if ws_bytes is not None else lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(desc), max(n, 0))
-    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, None, n, ptr, ptr,
-                                   gpos, ptr, wsb, None)
+    wsb = ws_bytes if ws_bytes is not None else lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(desc),
+                                                                                       max(n, 0), entries)
+    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, entries, None, n,
+                                   ptr, ptr, gpos, ptr, wsb, None)
 
 
 def test_backward_argument_errors_and_workspace(lib):
@@ -234,10 +235,15 @@ def test_backward_argument_errors_and_workspace(lib):
     assert _bwd(lib, d32, ws_bytes=100) == B.E2V2_ERR_ARG
     assert "workspace" in lib.e2v2_last_error().decode()
     assert _bwd(lib, d32, gpos=FAKE_MIS) == B.E2V2_ERR_ARG
+    assert _bwd(lib, d32, entries=-1, ws_bytes=1 << 30) == B.E2V2_ERR_ARG
+    assert _bwd(lib, d32, entries=1 << 31, ws_bytes=1 << 30) == B.E2V2_ERR_ARG
     assert _bwd(lib, d32, n=0) == B.E2V2_OK
     # the forward's fp32 workspace plus dL/dh', dL/dhhat, dL/dm, m, three per-head
-    # values and dq, dk per node
+    # values, dq, dk and three counters of the transposed list per node
     fa = lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 2000) - lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 1000)
-    ba = (lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 2000)
-          - lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000))
-    assert abs((ba - fa) / 1000 - (4 * 9 * 128 * 4 + 3 * 16 * 4 + 2 * 128 * 4)) < 2
+    ba = (lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 2000, 0)
+          - lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000, 0))
+    assert abs((ba - fa) / 1000 - (4 * 9 * 128 * 4 + 3 * 16 * 4 + 2 * 128 * 4 + 3 * 4)) < 2
+    # plus 4 bytes per list entry for the transposed list
+    e0 = lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000, 0)
+    assert abs(lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000, 100000) - e0 - 400000) <= 256
