@@ -17,8 +17,8 @@
 // K = sum e_j k_j with e_j = 2^(s2_j - M), then dd = A / Z and
 // dq = (B - dd K) / (Z sqrt(8)).  It stores M and 1 / Z per head.
 // Source pass: one wave per source j walks row j of the transposed list (the
-// targets that read source j, in increasing order), recomputes s_ij exactly as
-// the target pass did
+// targets that read source j; for a symmetric list, the list itself), recomputes
+// s_ij exactly as the target pass did
 // (same operations, same order), alpha_ij = 2^(s2_ij - M_i) / Z_i, and
 // accumulates dh'_j and dk_j in registers: every row written by one wave, no
 // atomics (FlashSchNet page, section 2.3: owner-computes rows).
@@ -161,9 +161,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_source(const AttnBwdArgs A)
 #pragma unroll
     for (int e = 0; e < NC; ++e) hv[e] = ld2(A.hp + ((size_t)j * NC + e) * C + c0);
     const float4 pj4 = A.pos4[j];
-    const long long s0 = A.src_start[j], s1 = A.src_start[j + 1];
-    const int start = __builtin_amdgcn_readfirstlane((int)s0);
-    const int len = __builtin_amdgcn_readfirstlane((int)((s1 < A.src_cap ? s1 : A.src_cap) - s0));
+    const int start = __builtin_amdgcn_readfirstlane(A.src_start[j]);
+    const int len = __builtin_amdgcn_readfirstlane(A.src_len[j]);
 
     float2 dh[NC];
 #pragma unroll

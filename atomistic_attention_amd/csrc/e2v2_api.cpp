@@ -685,7 +685,7 @@ e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, con
 namespace {
 // The forward workspace (q, k, v, h', frames) followed by the gradient buffers.
 struct BwdWs {
-    size_t fwd, gbuf, dhh, dm, mbuf, mx, rz, dd, dq, dk, tab, tcnt, tstart, tcur, tidx, total;
+    size_t fwd, gbuf, dhh, dm, mbuf, mx, rz, dd, dq, dk, tab, tcnt, tstart, tcur, tlen, tidx, total;
 };
 BwdWs bwd_ws(const e2v2_layer_desc &d, int n, long long max_entries)
 {
@@ -706,6 +706,7 @@ BwdWs bwd_ws(const e2v2_layer_desc &d, int n, long long max_entries)
     w.tcnt = o; o += al256((N + 1) * 4);         // the transposed list
     w.tstart = o; o += al256((N + 1) * 4);
     w.tcur = o; o += al256((N + 1) * 4);
+    w.tlen = o; o += al256(N * 4);
     w.tidx = o; o += al256((size_t)(max_entries > 0 ? max_entries : 1) * 4);
     w.total = o + 256;
     return w;
@@ -724,7 +725,7 @@ size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t 
 
 e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
                                 const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
-                                int64_t max_entries, const int32_t *target_order, int32_t n,
+                                int64_t max_entries, int32_t symmetric, const int32_t *target_order, int32_t n,
                                 const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream)
 {
@@ -780,16 +781,23 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     // Step 5 adjoint: dL/dm = EAAS^T with the target's own frame and w_tgt.
     e = launch_eaas_adjoint(L, pos, dhh, w->w_tgt, n, C, dm, stream);
     if (e != hipSuccess) return hip_fail(e, "target coupling adjoint");
-    // Step 4 adjoint: dq (target pass), dL/dh' and dk (source pass, over the transposed list).
-    int32_t *tstart = reinterpret_cast<int32_t *>(ws + B.tstart);
-    int32_t *tidx = reinterpret_cast<int32_t *>(ws + B.tidx);
-    e = launch_transpose_list(nbr_start, nbr_len, nbr_idx, n, max_entries, reinterpret_cast<int32_t *>(ws + B.tcnt),
-                              tstart, reinterpret_cast<int32_t *>(ws + B.tcur), tidx, stream);
-    if (e != hipSuccess) return hip_fail(e, "transposed list");
+    // Step 4 adjoint: dq (target pass), dL/dh' and dk (source pass, over the transposed
+    // list; a symmetric list is its own transpose).
     AttnBwdArgs a{};
+    if (symmetric) {
+        a.src_start = nbr_start; a.src_len = nbr_len; a.src_idx = nbr_idx;
+    } else {
+        int32_t *tstart = reinterpret_cast<int32_t *>(ws + B.tstart);
+        int32_t *tlen = reinterpret_cast<int32_t *>(ws + B.tlen);
+        int32_t *tidx = reinterpret_cast<int32_t *>(ws + B.tidx);
+        e = launch_transpose_list(nbr_start, nbr_len, nbr_idx, n, max_entries,
+                                  reinterpret_cast<int32_t *>(ws + B.tcnt), tstart,
+                                  reinterpret_cast<int32_t *>(ws + B.tcur), tidx, tlen, stream);
+        if (e != hipSuccess) return hip_fail(e, "transposed list");
+        a.src_start = tstart; a.src_len = tlen; a.src_idx = tidx;
+    }
     a.q = q; a.k = k; a.hp = hp; a.pos4 = pos4; a.dm = dm;
     a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
-    a.src_start = tstart; a.src_idx = tidx; a.src_cap = max_entries;
     a.w_rbf = w->w_rbf;
     a.mx = reinterpret_cast<float *>(ws + B.mx);
     a.rz = reinterpret_cast<float *>(ws + B.rz);

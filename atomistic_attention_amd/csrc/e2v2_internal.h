@@ -557,8 +557,7 @@ struct AttnBwdArgs {
     const float4 *pos4;              // [n] (x, y, z, .)
     const float *dm;                 // [n][NC][C]
     const int32_t *nbr_start, *nbr_len, *nbr_idx;
-    const int32_t *src_start, *src_idx;  // transposed list: row j at src_idx[src_start[j] .. src_start[j + 1])
-    long long src_cap;               // entries of src_idx (rows are clipped to it)
+    const int32_t *src_start, *src_len, *src_idx;  // the sources' rows: row j at src_idx[src_start[j] ..] (src_len[j])
     const int32_t *order;            // optional processing order of the nodes
     const float *w_rbf;              // [R][H]
     float *mx, *rz, *dd;             // [n][H]
@@ -626,11 +625,11 @@ struct PosGradArgs {
 };
 hipError_t launch_pos_grad(int L, const PosGradArgs &a, hipStream_t stream);
 
-// Transposed list of (start, len, idx) [n rows]: tstart [n + 1], tidx [cap]; cnt and
-// cur are [n + 1] scratch.  Rows sorted by i; entries past cap are dropped.
+// Transposed list of (start, len, idx) [n rows]: tstart [n + 1], tlen [n], tidx [cap];
+// cnt and cur are [n + 1] scratch.  Rows sorted by i; entries past cap are dropped.
 hipError_t launch_transpose_list(const int32_t *start, const int32_t *len, const int32_t *idx, int n,
                                  long long cap, int32_t *cnt, int32_t *tstart, int32_t *cur, int32_t *tidx,
-                                 hipStream_t stream);
+                                 int32_t *tlen, hipStream_t stream);
 
 hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, void *ws, size_t ws_bytes,
                                   int32_t *nbr_len, int32_t *order_out, hipStream_t stream);

@@ -842,13 +842,15 @@ __global__ __launch_bounds__(256) void k_tfill(const int32_t *__restrict__ start
 }
 // One 64-lane block per row: a register bitonic sort up to 1024 entries, an
 // odd-even transposition sort in place beyond.
-__global__ __launch_bounds__(64) void k_tsort(const int32_t *__restrict__ tstart, int n, long long cap, int32_t *tidx)
+__global__ __launch_bounds__(64) void k_tsort(const int32_t *__restrict__ tstart, int n, long long cap, int32_t *tidx,
+                                              int32_t *tlen)
 {
     const int j = blockIdx.x, lane = threadIdx.x;
     const long long a = tstart[j], b0 = tstart[j + 1];
     const long long b = b0 < cap ? b0 : cap;
     const int cnt = b > a ? (int)(b - a) : 0;
     int32_t *row = tidx + a;
+    if (lane == 0) tlen[j] = cnt;
     if (cnt <= 1) return;
     if (cnt <= 1024) {
         wave_write_sorted(row, cnt, row, lane);
@@ -865,7 +867,7 @@ __global__ __launch_bounds__(64) void k_tsort(const int32_t *__restrict__ tstart
 
 hipError_t launch_transpose_list(const int32_t *start, const int32_t *len, const int32_t *idx, int n,
                                  long long cap, int32_t *cnt, int32_t *tstart, int32_t *cur, int32_t *tidx,
-                                 hipStream_t stream)
+                                 int32_t *tlen, hipStream_t stream)
 {
     if (n <= 0) return hipSuccess;
     k_tzero<<<(unsigned)((n + 256) / 256), 256, 0, stream>>>(cnt, n);
@@ -873,7 +875,7 @@ hipError_t launch_transpose_list(const int32_t *start, const int32_t *len, const
     k_tcount<<<g4, 256, 0, stream>>>(start, len, idx, n, cnt);
     k_scan<<<1, 1024, 0, stream>>>(cnt, nullptr, n, tstart, cur, nullptr);
     k_tfill<<<g4, 256, 0, stream>>>(start, len, idx, n, cap, cur, tidx);
-    k_tsort<<<(unsigned)n, 64, 0, stream>>>(tstart, n, cap, tidx);
+    k_tsort<<<(unsigned)n, 64, 0, stream>>>(tstart, n, cap, tidx, tlen);
     return hipGetLastError();
 }
 

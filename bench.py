@@ -170,11 +170,11 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
 
     def bwd():
         B.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, g, grad_h=gh, workspace=bws,
-                              target_order=order)
+                              target_order=order, symmetric=True)
 
     def bwd_pos():
         B.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, g, grad_h=gh, workspace=bws,
-                              target_order=order, grad_pos=gp)
+                              target_order=order, grad_pos=gp, symmetric=True)
 
     def fwd():
         B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, out=out, workspace=fws,
@@ -201,8 +201,8 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
                         f"uncapped (symmetric list), l_max={c.lmax}, C={C}, {H} heads, {c.n_rbf} RBFs, "
                         f"fp32 storage",
             "what": "dL/dh for L = sum(g * out), g fixed (ms_backward); dL/dh and dL/dpos together "
-                    "(ms_backward_with_positions); weights and the neighbour list held fixed; each call builds "
-                    "its transposed list",
+                    "(ms_backward_with_positions); weights and the neighbour list held fixed; the uncapped list "
+                    "is symmetric and serves as its own transpose",
             "nnz": nnz, "steps": steps, "ms_backward": res["backward"],
             "ms_backward_with_positions": res["backward_pos"], "ms_forward_same_layer": res["forward"],
             "pairs_per_s_backward": nnz / (res["backward"] * 1e-3),

@@ -239,16 +239,24 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
  * Storage must be fp32 (E2V2_ERR_UNSUPPORTED otherwise); pos fp32 [n][3], h and
  * grad_out fp32 [n][(lmax+1)^2][C], grad_h fp32 [n][(lmax+1)^2][C] (written whole).
  * The neighbour list has the layout of e2v2_attn_forward (CSR or K-capped with
- * -1 padding; any list, symmetric or not).  The call builds its transposed list
- * in the workspace (the targets that read each source, in increasing order) and
- * gathers each source's gradient over it, so no result is written by atomics
- * (FlashSchNet page, section 2.3: the backward works by source).  max_entries:
+ * -1 padding; any list, symmetric or not).  Each source's gradient is gathered
+ * over the targets that read it, so no result is written by atomics (FlashSchNet
+ * page, section 2.3: the backward works by source).  symmetric = 0: the call
+ * builds the transposed list in the workspace (the targets that read each
+ * source, in increasing order; about 0.26 ms at 1.6 M entries).  symmetric = 1:
+ * the caller guarantees that j is in row i exactly as often as i is in row j,
+ * with valid entries only, and the list serves as its own transpose (true of
+ * every uncapped list of e2v2_build_neighbors and e2v2_filter_neighbors, whose
+ * fp64 predicate is symmetric in i and j; not of capped lists in general).  The
+ * results of the two modes on a symmetric list with rows sorted by index are
+ * identical.  max_entries:
  * an upper bound on the list's entries (the length of nbr_idx is one); entries
  * beyond it are dropped from the source side, so a smaller value gives a wrong
  * gradient (never an out-of-bounds access).
  * target_order (optional, a permutation of 0..n-1) only changes the order in
  * which nodes are processed.  Workspace: e2v2_layer_backward_workspace_bytes
- * (n, max_entries).
+ * (n, max_entries).  A wrong symmetric = 1 gives a wrong gradient, never an
+ * out-of-bounds access.
  * All device pointers 16-byte aligned; asynchronous on `stream`.  Errors:
  * E2V2_ERR_ARG (NULL or misaligned pointer, small workspace, n < 0, max_entries
  * outside 0 .. 2^31 - 2),
@@ -256,7 +264,8 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
 size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t n, int64_t max_entries);
 e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h,
                                 const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
-                                const int32_t *nbr_idx, int64_t max_entries, const int32_t *target_order, int32_t n,
+                                const int32_t *nbr_idx, int64_t max_entries, int32_t symmetric,
+                                const int32_t *target_order, int32_t n,
                                 const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 

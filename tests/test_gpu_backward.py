@@ -28,7 +28,7 @@ def _g(wl, seed=11):
     return np.random.default_rng(seed).standard_normal(wl.h.shape).astype(np.float32).astype(np.float64)
 
 
-def _gpu_grad(gpu_lib, wl, g, order=None, pos_grad=False, K=0, rows=None):
+def _gpu_grad(gpu_lib, wl, g, order=None, pos_grad=False, K=0, rows=None, symmetric=False):
     c = wl.cfg
     d = upload(wl)
     if rows is not None:
@@ -39,7 +39,7 @@ def _gpu_grad(gpu_lib, wl, g, order=None, pos_grad=False, K=0, rows=None):
     print(f"backward {c.name} n={c.n} L={c.lmax} H={c.heads} pos={pos_grad}", flush=True)
     gp = torch.full((c.n, 3), float("nan"), dtype=torch.float32, device="cuda") if pos_grad else None
     r = gpu_lib.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, f32(g), target_order=order,
-                                    grad_pos=gp)
+                                    grad_pos=gp, symmetric=symmetric)
     torch.cuda.synchronize()
     if pos_grad:
         return r[0].cpu().numpy(), r[1].cpu().numpy(), (s, ln, ix)
@@ -142,6 +142,17 @@ def test_backward_invalid_and_repeated_entries(gpu_lib):
     assert e < TOL and ep < TOL, (e, ep)
 
 
+def test_backward_symmetric_mode_identical(gpu_lib):
+    """On an uncapped list (symmetric, rows sorted by index) the list serves as its
+    own transpose: both gradients are bit-identical to those over the transposed
+    list the call builds."""
+    wl = W.make_workload("c2")
+    g = _g(wl)
+    a_h, a_p, _ = _gpu_grad(gpu_lib, wl, g, pos_grad=True)
+    b_h, b_p, _ = _gpu_grad(gpu_lib, wl, g, pos_grad=True, symmetric=True)
+    assert np.array_equal(a_h, b_h) and np.array_equal(a_p, b_p)
+
+
 def test_backward_order_invariant(gpu_lib):
     """The processing order changes no value: every node's result is computed by
     one wave from the same inputs."""
@@ -158,7 +169,7 @@ def test_backward_full_size_sampled(gpu_lib):
     sampled atoms match the oracle's exact sampled gradients."""
     wl = W.make_workload("g4")
     g = _g(wl)
-    got, gp, (s, ln, ix) = _gpu_grad(gpu_lib, wl, g, pos_grad=True)
+    got, gp, (s, ln, ix) = _gpu_grad(gpu_lib, wl, g, pos_grad=True, symmetric=True)
     rows = rows_from_device(s, ln, ix)
     pairs = {(i, int(j)) for i, r in enumerate(rows) for j in r}
     assert all((j, i) in pairs for (i, j) in pairs)

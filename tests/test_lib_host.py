@@ -220,8 +220,8 @@ def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE, gpos=None, entries=100):
     w = B.Weights(*([ptr] * 7))
     wsb = ws_bytes if ws_bytes is not None else lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(desc),
                                                                                        max(n, 0), entries)
-    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, entries, None, n,
-                                   ptr, ptr, gpos, ptr, wsb, None)
+    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, entries, 0, None,
+                                   n, ptr, ptr, gpos, ptr, wsb, None)
 
 
 def test_backward_argument_errors_and_workspace(lib):
@@ -239,11 +239,11 @@ def test_backward_argument_errors_and_workspace(lib):
     assert _bwd(lib, d32, entries=1 << 31, ws_bytes=1 << 30) == B.E2V2_ERR_ARG
     assert _bwd(lib, d32, n=0) == B.E2V2_OK
     # the forward's fp32 workspace plus dL/dh', dL/dhhat, dL/dm, m, three per-head
-    # values, dq, dk and three counters of the transposed list per node
+    # values, dq, dk and four counters of the transposed list per node
     fa = lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 2000) - lib.e2v2_attn_workspace_bytes(ctypes.byref(d32), 1000)
     ba = (lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 2000, 0)
           - lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000, 0))
-    assert abs((ba - fa) / 1000 - (4 * 9 * 128 * 4 + 3 * 16 * 4 + 2 * 128 * 4 + 3 * 4)) < 2
+    assert abs((ba - fa) / 1000 - (4 * 9 * 128 * 4 + 3 * 16 * 4 + 2 * 128 * 4 + 4 * 4)) < 2
     # plus 4 bytes per list entry for the transposed list
     e0 = lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000, 0)
     assert abs(lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000, 100000) - e0 - 400000) <= 256
