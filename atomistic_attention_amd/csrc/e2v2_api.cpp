@@ -1026,8 +1026,13 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
     // 2. lists at the largest cutoff, then filtered for each smaller one
     if (rebuild) {
         st = e2v2_build_neighbors(pos, n, S.cut[0], K, start, list_len(0), list_idx(0), (int64_t)n * K, nullptr,
-                                  order, wb + W.nbws, W.nbws_bytes, stream);
+                                  nullptr, wb + W.nbws, W.nbws_bytes, stream);
         if (st != E2V2_OK) return st;
+        // the targets' processing order until the next rebuild: a Morton curve (its
+        // sort is paid once per rebuild, its locality on every layer of every step)
+        void *nws = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(wb + W.nbws) + 255) & ~uintptr_t(255));
+        e = launch_morton_order(pos, n, nws, order, stream);
+        if (e != hipSuccess) return hip_fail(e, "processing order");
         for (int k = 1; k < S.ncut; ++k) {
             e = launch_filter_rows(pos, n, S.cut[k], start, list_len(0), list_idx(0), list_len(k), list_idx(k), stream);
             if (e != hipSuccess) return hip_fail(e, "neighbour filter kernel");

@@ -641,6 +641,8 @@ hipError_t launch_max_disp2(const float *pos, const float *ref, int n, double *o
 hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, void *ws, int32_t *nbr_start,
                                  int32_t *nbr_len, int32_t *nbr_idx, hipStream_t stream);
 size_t neighbors_ws_bytes(int n, int K);
+// Morton-curve processing order of the atoms on the grid of the last build in ws.
+hipError_t launch_morton_order(const float *pos, int n, void *ws, int32_t *order_out, hipStream_t stream);
 int64_t *neighbors_nnz_slot(void *ws, int n);
 
 }  // namespace e2v2

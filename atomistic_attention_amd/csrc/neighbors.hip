@@ -30,6 +30,7 @@
 #include "e2v2_internal.h"
 
 #include <algorithm>
+#include <hipcub/hipcub.hpp>
 
 #pragma clang fp contract(off)
 
@@ -54,6 +55,10 @@ struct NbrLayout {
     int32_t *order;        // [n] atom ids in cell order
     float4 *spos;          // [n] positions in cell order, w = atom id bits
     int64_t *nnz;
+    uint32_t *mkey[2];     // [n] Morton keys in / sorted (launch_morton_order)
+    int32_t *mval;         // [n] atom ids 0 .. n-1
+    void *sort_tmp;        // radix-sort scratch
+    size_t sort_bytes;
     size_t bytes;
 };
 
@@ -75,6 +80,15 @@ static NbrLayout nbr_layout(void *ws, int n)
     L.cell_cur = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * mc);
     L.order = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (size_t)n);
     L.spos = reinterpret_cast<float4 *>(p + o); o += al256(sizeof(float4) * (size_t)n);
+    L.mkey[0] = reinterpret_cast<uint32_t *>(p + o); o += al256(sizeof(uint32_t) * (size_t)n);
+    L.mkey[1] = reinterpret_cast<uint32_t *>(p + o); o += al256(sizeof(uint32_t) * (size_t)n);
+    L.mval = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (size_t)n);
+    size_t tb = 0;
+    hipcub::DeviceRadixSort::SortPairs(nullptr, tb, (const uint32_t *)nullptr, (uint32_t *)nullptr,
+                                       (const int32_t *)nullptr, (int32_t *)nullptr, n > 0 ? n : 1, 0, 30);
+    L.sort_tmp = p + o;
+    L.sort_bytes = tb;
+    o += al256(tb);
     L.bytes = o;
     return L;
 }
@@ -278,6 +292,38 @@ __global__ void k_scatter(const float *__restrict__ pos, int n, const int32_t *_
     order[slot] = (int32_t)i;
     if (order_out) order_out[slot] = (int32_t)i;
     spos[slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float((int)i));
+}
+
+// ---------------------------------------------------------------- Morton order
+// A processing order for callers that build the list rarely (the layer stack, at
+// rebuilds): atoms sorted by the Morton code of their position on a grid of half
+// the cell width (10 bits per axis, clamped), a space-filling curve, so a run of
+// consecutive targets fills a compact region and the rows it reads stay close
+// together -- fewer L2 misses than the cells' row-major order.  Stable sort keyed
+// on atom ids 0..n-1: deterministic.  Uses the grid of the last build in ws.
+__device__ __forceinline__ uint32_t spread3(uint32_t v)
+{
+    v &= 0x3ffu;
+    v = (v | (v << 16)) & 0x030000ffu;
+    v = (v | (v << 8)) & 0x0300f00fu;
+    v = (v | (v << 4)) & 0x030c30c3u;
+    v = (v | (v << 2)) & 0x09249249u;
+    return v;
+}
+__global__ void k_morton_keys(const float *__restrict__ pos, int n, const GridInfo *__restrict__ grid, uint32_t *key,
+                              int32_t *val)
+{
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const GridInfo gi = *grid;
+    uint32_t q[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        const float t = (pos[3 * i + a] - gi.lo[a]) * gi.inv[a] * 2.f;
+        q[a] = t >= 1023.f ? 1023u : (t > 0.f ? (uint32_t)t : 0u);     // NaN -> 0
+    }
+    key[i] = spread3(q[0]) | (spread3(q[1]) << 1) | (spread3(q[2]) << 2);
+    val[i] = (int32_t)i;
 }
 
 // ---------------------------------------------------------------- step 4
@@ -916,6 +962,18 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
         k_count_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(n, cutoff, rc2, L.grid, L.cell_start,
                                                                                 L.order, L.spos, nbr_len);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_morton_order(const float *pos, int n, void *ws, int32_t *order_out, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    NbrLayout L = nbr_layout(ws, n);
+    k_morton_keys<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.mkey[0], L.mval);
+    size_t tb = L.sort_bytes;
+    const hipError_t e = hipcub::DeviceRadixSort::SortPairs(L.sort_tmp, tb, L.mkey[0], L.mkey[1], L.mval, order_out, n,
+                                                            0, 30, stream);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 
