@@ -109,7 +109,7 @@ def load(path: str = LIB_PATH):
     lib.e2v2_layer_backward_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32, i64]
     lib.e2v2_layer_backward_workspace_bytes.restype = sz
     lib.e2v2_layer_backward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, i64,
-                                        i32, vp, i32, vp, vp, vp, vp, sz, vp]
+                                        i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.e2v2_layer_backward.restype = ctypes.c_int
     lib.e2v2_status_string.argtypes = [ctypes.c_int]
     lib.e2v2_status_string.restype = ctypes.c_char_p
@@ -332,11 +332,13 @@ def backward_workspace_bytes(desc: LayerDesc, n: int, max_entries: int) -> int:
 def e2v2_layer_backward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len, nbr_idx, grad_out,
                         grad_h=None, workspace=None, stream=None,
                         target_order: torch.Tensor | None = None, grad_pos: torch.Tensor | None = None,
-                        symmetric: bool = False):
+                        symmetric: bool = False, reuse_forward: bool = False):
     """dL/dh for L = sum(grad_out * layer(pos, h)) (fp32 storage; any neighbour list).
     With grad_pos (a [n, 3] fp32 device tensor) also dL/dpos; returns grad_h, or
     (grad_h, grad_pos) when grad_pos is given.  symmetric=True: the list is its own
-    transpose (uncapped lists of e2v2_build_neighbors), so none is built."""
+    transpose (uncapped lists of e2v2_build_neighbors), so none is built.
+    reuse_forward=True: `workspace` holds what e2v2_attn_forward left in it for the
+    same inputs (pass the same tensor to both), so q, k, v, h' are not recomputed."""
     lib = load()
     n = pos.shape[0]
     _dev(pos, torch.float32, "pos")
@@ -355,13 +357,16 @@ def e2v2_layer_backward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_l
     max_entries = nbr_idx.numel()
     wsb = backward_workspace_bytes(desc, n, max_entries)
     if workspace is None or workspace.numel() < wsb:
+        if reuse_forward:
+            raise ValueError("reuse_forward needs the workspace the forward ran on, of backward_workspace_bytes")
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=h.device)
     if grad_pos is not None:
         _dev(grad_pos, torch.float32, "grad_pos")
         if tuple(grad_pos.shape) != (n, 3):
             raise ValueError(f"grad_pos shape {tuple(grad_pos.shape)} != ({n}, 3)")
     _check(lib.e2v2_layer_backward(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), _ptr(nbr_start),
-                                   _ptr(nbr_len), _ptr(nbr_idx), max_entries, int(bool(symmetric)), _ptr(target_order),
+                                   _ptr(nbr_len), _ptr(nbr_idx), max_entries, int(bool(symmetric)),
+                                   int(bool(reuse_forward)), _ptr(target_order),
                                    n, _ptr(grad_out),
                                    _ptr(grad_h), _ptr(grad_pos), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))

@@ -725,7 +725,8 @@ size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t 
 
 e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
                                 const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
-                                int64_t max_entries, int32_t symmetric, const int32_t *target_order, int32_t n,
+                                int64_t max_entries, int32_t symmetric, int32_t reuse_forward,
+                                const int32_t *target_order, int32_t n,
                                 const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream)
 {
@@ -750,10 +751,14 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     if (workspace_bytes < B.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, B.total);
     char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
     const AttnWs F = attn_ws(*desc, n);
-    // Steps 2-3 of the forward pass: q, k, v, h' and the per-node frames.
-    st = attn_run(desc, pos, h, w, nullptr, nullptr, nullptr, nullptr, n, nullptr, ws + B.fwd, F.total, nullptr,
-                  stream, true, false);
-    if (st != E2V2_OK) return st;
+    // Steps 2-3 of the forward pass: q, k, v, h' and the per-node frames -- or, with
+    // reuse_forward, those a forward call with the same arguments left at the
+    // start of this workspace.
+    if (!reuse_forward) {
+        st = attn_run(desc, pos, h, w, nullptr, nullptr, nullptr, nullptr, n, nullptr, ws + B.fwd, F.total, nullptr,
+                      stream, true, false);
+        if (st != E2V2_OK) return st;
+    }
     char *fw = ws + B.fwd;          // 256-aligned already, so attn_run used the same base
     const float *q = reinterpret_cast<const float *>(fw + F.q);
     const float *k = reinterpret_cast<const float *>(fw + F.k);

@@ -180,8 +180,15 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
         B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, out=out, workspace=fws,
                             target_order=order)
 
+    def train_step():
+        # the forward on the gradient's workspace, then both gradients reusing its q, k, v, h'
+        B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, out=out, workspace=bws,
+                            target_order=order)
+        B.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, g, grad_h=gh, workspace=bws,
+                              target_order=order, grad_pos=gp, symmetric=True, reuse_forward=True)
+
     res = {}
-    for key, fn in (("backward", bwd), ("backward_pos", bwd_pos), ("forward", fwd)):
+    for key, fn in (("backward", bwd), ("backward_pos", bwd_pos), ("forward", fwd), ("train", train_step)):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -202,9 +209,11 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
                         f"fp32 storage",
             "what": "dL/dh for L = sum(g * out), g fixed (ms_backward); dL/dh and dL/dpos together "
                     "(ms_backward_with_positions); weights and the neighbour list held fixed; the uncapped list "
-                    "is symmetric and serves as its own transpose",
+                    "is symmetric and serves as its own transpose; ms_forward_then_gradients: the forward, then "
+                    "dL/dh and dL/dpos reusing the forward's q, k, v, h' (one training step of the layer)",
             "nnz": nnz, "steps": steps, "ms_backward": res["backward"],
             "ms_backward_with_positions": res["backward_pos"], "ms_forward_same_layer": res["forward"],
+            "ms_forward_then_gradients": res["train"],
             "pairs_per_s_backward": nnz / (res["backward"] * 1e-3),
             "pairs_per_s_backward_with_positions": nnz / (res["backward_pos"] * 1e-3),
             "attention_adjoint_algorithmic_bytes": per_pair * nnz + per_node * c.n}

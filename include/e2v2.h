@@ -256,7 +256,12 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
  * target_order (optional, a permutation of 0..n-1) only changes the order in
  * which nodes are processed.  Workspace: e2v2_layer_backward_workspace_bytes
  * (n, max_entries).  A wrong symmetric = 1 gives a wrong gradient, never an
- * out-of-bounds access.
+ * out-of-bounds access.  reuse_forward = 1 skips the recomputation of q, k, v, h'
+ * and the frames: the caller guarantees that e2v2_attn_forward (or
+ * e2v2_attn_prepare) last ran with the same desc, pos, h, weights and n on this
+ * same workspace pointer (its layout is the first e2v2_attn_workspace_bytes of
+ * the gradient's workspace), as a training step does when it keeps the forward's
+ * intermediates.
  * All device pointers 16-byte aligned; asynchronous on `stream`.  Errors:
  * E2V2_ERR_ARG (NULL or misaligned pointer, small workspace, n < 0, max_entries
  * outside 0 .. 2^31 - 2),
@@ -265,7 +270,7 @@ size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t 
 e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h,
                                 const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
                                 const int32_t *nbr_idx, int64_t max_entries, int32_t symmetric,
-                                const int32_t *target_order, int32_t n,
+                                int32_t reuse_forward, const int32_t *target_order, int32_t n,
                                 const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 

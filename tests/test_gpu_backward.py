@@ -153,6 +153,26 @@ def test_backward_symmetric_mode_identical(gpu_lib):
     assert np.array_equal(a_h, b_h) and np.array_equal(a_p, b_p)
 
 
+def test_backward_reusing_the_forward_workspace(gpu_lib):
+    """A forward on the same workspace, then the gradients with reuse_forward: the
+    same results bit for bit as the call that recomputes q, k, v, h'."""
+    wl = W.make_workload("c2")
+    c = wl.cfg
+    g = _g(wl)
+    d = upload(wl)
+    s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, 0)
+    desc = gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
+    ws = torch.empty(gpu_lib.backward_workspace_bytes(desc, c.n, ix.numel()), dtype=torch.uint8, device="cuda")
+    gt = f32(g)
+    ref_h, ref_p = gpu_lib.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, gt,
+                                               grad_pos=torch.empty((c.n, 3), device="cuda"))
+    gpu_lib.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, workspace=ws)
+    got_h, got_p = gpu_lib.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, gt, workspace=ws,
+                                               grad_pos=torch.empty((c.n, 3), device="cuda"), reuse_forward=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_h, got_h) and torch.equal(ref_p, got_p)
+
+
 def test_backward_order_invariant(gpu_lib):
     """The processing order changes no value: every node's result is computed by
     one wave from the same inputs."""

@@ -220,8 +220,8 @@ def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE, gpos=None, entries=100):
     w = B.Weights(*([ptr] * 7))
     wsb = ws_bytes if ws_bytes is not None else lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(desc),
                                                                                        max(n, 0), entries)
-    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, entries, 0, None,
-                                   n, ptr, ptr, gpos, ptr, wsb, None)
+    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, entries, 0, 0,
+                                   None, n, ptr, ptr, gpos, ptr, wsb, None)
 
 
 def test_backward_argument_errors_and_workspace(lib):
