@@ -65,7 +65,7 @@ def algorithmic_bytes(cfg, nnz: int) -> dict:
 
 
 def kernel_hash() -> str:
-    """Hash of the streaming kernels' sources (the counters are valid for this build only)."""
+    """Hash of the streaming kernels' sources (the stored counters are valid for those sources only)."""
     h = hashlib.sha256()
     for f in ATTN_SRCS:
         h.update(open(f, "rb").read())
