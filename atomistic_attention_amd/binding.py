@@ -24,7 +24,7 @@ EXPORTS = [
     "e2v2_path_table", "e2v2_eaas_coefficients", "e2v2_alignment_wigner", "e2v2_status_string",
     "e2v2_last_error", "e2v2_filter_neighbors", "e2v2_max_displacement2", "e2v2_stack_state_bytes",
     "e2v2_stack_workspace_bytes", "e2v2_stack_forward", "e2v2_layer_backward_workspace_bytes",
-    "e2v2_layer_backward",
+    "e2v2_layer_backward", "e2v2_stack_backward_workspace_bytes", "e2v2_stack_backward",
 ]
 
 
@@ -111,6 +111,11 @@ def load(path: str = LIB_PATH):
     lib.e2v2_layer_backward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, i64,
                                         i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.e2v2_layer_backward.restype = ctypes.c_int
+    lib.e2v2_stack_backward_workspace_bytes.argtypes = [i32, ctypes.POINTER(LayerDesc), i32, i32]
+    lib.e2v2_stack_backward_workspace_bytes.restype = sz
+    lib.e2v2_stack_backward.argtypes = [i32, ctypes.POINTER(LayerDesc), ctypes.POINTER(Weights), vp, vp, i32, i32,
+                                        vp, sz, vp, vp, vp, vp, sz, vp]
+    lib.e2v2_stack_backward.restype = ctypes.c_int
     lib.e2v2_status_string.argtypes = [ctypes.c_int]
     lib.e2v2_status_string.restype = ctypes.c_char_p
     lib.e2v2_last_error.argtypes = []
@@ -433,3 +438,25 @@ class StackRun:
                                       ctypes.byref(self.policy), _ptr(self.state), self.state.numel(), _ptr(out),
                                       _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
         return out
+
+    def e2v2_stack_backward(self, pos, h, grad_out, grad_h=None, grad_pos=None, stream=None):
+        """dL/dh (and dL/dpos if grad_pos, a [n, 3] fp32 tensor, is given) of L = sum(grad_out * out)
+        for the output of the last e2v2_stack_forward call at (pos, h); fp32 storage."""
+        lib = load()
+        _dev(pos, torch.float32, "pos")
+        _dev(h, torch.float32, "h")
+        _dev(grad_out, torch.float32, "grad_out")
+        if grad_h is None:
+            grad_h = torch.empty(h.shape, dtype=torch.float32, device=h.device)
+        if grad_pos is not None:
+            _dev(grad_pos, torch.float32, "grad_pos")
+        wb = int(lib.e2v2_stack_backward_workspace_bytes(self.L, self.descs, self.n, self.K))
+        if wb == 0:
+            raise ValueError("invalid stack description")
+        if getattr(self, "bworkspace", None) is None or self.bworkspace.numel() < wb:
+            self.bworkspace = torch.empty(wb, dtype=torch.uint8, device=h.device)
+        _check(lib.e2v2_stack_backward(self.L, self.descs, self.weights, _ptr(pos), _ptr(h), self.n, self.K,
+                                       _ptr(self.state), self.state.numel(), _ptr(grad_out), _ptr(grad_h),
+                                       _ptr(grad_pos), _ptr(self.bworkspace), self.bworkspace.numel(),
+                                       _stream(stream)))
+        return grad_h if grad_pos is None else (grad_h, grad_pos)

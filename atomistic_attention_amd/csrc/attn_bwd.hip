@@ -124,9 +124,10 @@ __global__ __launch_bounds__(256) void k_attn_bwd_target(const AttnBwdArgs A)
         const float fy = wave_sum_if((Uf.y - dd * Vf.y) * rz, take);
         const float fz = wave_sum_if((Uf.z - dd * Vf.z) * rz, take);
         if (lane == 0) {
-            A.grad_pos[3 * (size_t)i + 0] = fx;
-            A.grad_pos[3 * (size_t)i + 1] = fy;
-            A.grad_pos[3 * (size_t)i + 2] = fz;
+            float *gpi = A.grad_pos + 3 * (size_t)i;
+            gpi[0] = A.pos_acc ? gpi[0] + fx : fx;
+            gpi[1] = A.pos_acc ? gpi[1] + fy : fy;
+            gpi[2] = A.pos_acc ? gpi[2] + fz : fz;
         }
         if (act) {
 #pragma unroll

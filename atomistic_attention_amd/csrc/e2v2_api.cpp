@@ -723,12 +723,14 @@ size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t 
     return bwd_ws(*desc, n, max_entries).total;
 }
 
-e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
-                                const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
-                                int64_t max_entries, int32_t symmetric, int32_t reuse_forward,
-                                const int32_t *target_order, int32_t n,
-                                const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
-                                size_t workspace_bytes, hipStream_t stream)
+// The layer gradient; pos_acc: add dL/dpos into grad_pos instead of writing it
+// (the layer stack sums it over its layers).
+static e2v2_status layer_bwd(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
+                             const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
+                             int64_t max_entries, int32_t symmetric, int32_t reuse_forward,
+                             const int32_t *target_order, int32_t n, const float *grad_out, float *grad_h,
+                             float *grad_pos, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                             bool pos_acc)
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
@@ -809,6 +811,7 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     a.dd = reinterpret_cast<float *>(ws + B.dd);
     a.dq = dq; a.dk = dk; a.dhp = gbuf;
     a.grad_pos = grad_pos;
+    a.pos_acc = pos_acc;
     a.m = reinterpret_cast<float *>(ws + B.mbuf);
     a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
     e = launch_attn_bwd(L, a, stream);
@@ -841,6 +844,17 @@ e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, c
     if (e == hipSuccess) e = launch_proj(&jk, 1, n, C, stream);
     if (e != hipSuccess) return hip_fail(e, "input projection adjoint");
     return E2V2_OK;
+}
+
+e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
+                                const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
+                                int64_t max_entries, int32_t symmetric, int32_t reuse_forward,
+                                const int32_t *target_order, int32_t n,
+                                const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    return layer_bwd(desc, pos, h, w, nbr_start, nbr_len, nbr_idx, max_entries, symmetric, reuse_forward,
+                     target_order, n, grad_out, grad_h, grad_pos, workspace, workspace_bytes, stream, false);
 }
 
 }  // extern "C"
@@ -939,6 +953,28 @@ e2v2_status check_stack(int L, const e2v2_layer_desc *descs, const e2v2_weights 
     if ((int64_t)n * K >= INT32_MAX) return fail(E2V2_ERR_ARG, "n*K exceeds int32 offsets");
     return E2V2_OK;
 }
+}  // namespace
+
+namespace {
+// Workspace of the stack gradient: one layer-gradient workspace (which also serves
+// the forward recomputation), the fp32 inputs of layers 1..L-1, two gradient buffers.
+struct StackBwdWs {
+    size_t bws, bws_bytes, x, per_x, g0, g1, total;
+};
+StackBwdWs stack_bwd_ws(int L, const e2v2_layer_desc *d, int n, int K)
+{
+    StackBwdWs w{};
+    size_t o = 0, mb = 0;
+    for (int l = 0; l < L; ++l) mb = std::max(mb, bwd_ws(d[l], n, (long long)n * K).total);
+    const size_t feat = al256((size_t)n * n_comp(d[0].lmax) * d[0].channels * 4);
+    w.bws = o; w.bws_bytes = mb; o += al256(mb);
+    w.x = o; w.per_x = feat; o += feat * (size_t)(L > 1 ? L - 1 : 0);
+    w.g0 = o; o += feat;
+    w.g1 = o; o += feat;
+    w.total = o + 256;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1090,6 +1126,69 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
     }
     policy->rebuilt = rebuild ? 1 : 0;
     if (policy->steps_since_rebuild < INT32_MAX) policy->steps_since_rebuild += 1;
+    return E2V2_OK;
+}
+
+size_t e2v2_stack_backward_workspace_bytes(int32_t n_layers, const e2v2_layer_desc *descs, int32_t n,
+                                           int32_t max_neighbors)
+{
+    if (n_layers < 1 || n_layers > kMaxStackLayers || !descs || n < 0 || max_neighbors < 1) return 0;
+    for (int l = 0; l < n_layers; ++l)
+        if (descs[l].lmax < 0 || descs[l].lmax > kMaxL || descs[l].channels <= 0 || descs[l].heads <= 0) return 0;
+    return stack_bwd_ws(n_layers, descs, n, max_neighbors).total;
+}
+
+e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, const e2v2_weights *weights,
+                                const float *pos, const float *h, int32_t n, int32_t K, const void *state,
+                                size_t state_bytes, const float *grad_out, float *grad_h, float *grad_pos,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    e2v2_status st = check_stack(n_layers, descs, weights, n, K);
+    if (st != E2V2_OK) return st;
+    if (descs[0].storage != E2V2_FP32) return fail(E2V2_ERR_UNSUPPORTED, "the stack gradient needs fp32 storage");
+    if (!weights) return fail(E2V2_ERR_ARG, "weights is NULL");
+    if (n == 0) return E2V2_OK;
+    for (const void *p : {(const void *)pos, (const void *)h, state, (const void *)grad_out, (const void *)grad_h,
+                          (const void *)workspace}) {
+        if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
+        if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    }
+    if (grad_pos && !aligned16(grad_pos)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    const StackState S = stack_state(n_layers, descs, n, K);
+    const StackBwdWs W = stack_bwd_ws(n_layers, descs, n, K);
+    if (state_bytes < S.total) return fail(E2V2_ERR_ARG, "state too small: %zu < %zu", state_bytes, S.total);
+    if (workspace_bytes < W.total)
+        return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, W.total);
+    const char *sb = reinterpret_cast<const char *>((reinterpret_cast<uintptr_t>(state) + 255) & ~uintptr_t(255));
+    char *wb = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+    const int32_t *order = reinterpret_cast<const int32_t *>(sb + S.order);
+    const int32_t *start = reinterpret_cast<const int32_t *>(sb + S.start);
+    auto list_len = [&](int k) { return reinterpret_cast<const int32_t *>(sb + S.lists + (size_t)k * S.per_list); };
+    auto list_idx = [&](int k) {
+        return reinterpret_cast<const int32_t *>(sb + S.lists + (size_t)k * S.per_list + S.len_off);
+    };
+    // 1. the layers' inputs, recomputed over the lists of the last e2v2_stack_forward
+    const float *x[kMaxStackLayers];
+    x[0] = h;
+    for (int l = 0; l + 1 < n_layers; ++l) {
+        const int k = cutoff_index(S.ncut, S.cut, descs[l].cutoff);
+        float *xo = reinterpret_cast<float *>(wb + W.x + (size_t)l * W.per_x);
+        st = attn_run(&descs[l], pos, x[l], &weights[l], start, list_len(k), list_idx(k), order, n, xo, wb + W.bws,
+                      W.bws_bytes, nullptr, stream, true, true);
+        if (st != E2V2_OK) return st;
+        x[l + 1] = xo;
+    }
+    // 2. the layers' gradients in reverse; dL/dpos summed over the layers
+    float *gb[2] = {reinterpret_cast<float *>(wb + W.g0), reinterpret_cast<float *>(wb + W.g1)};
+    const float *g = grad_out;
+    for (int l = n_layers - 1; l >= 0; --l) {
+        const int k = cutoff_index(S.ncut, S.cut, descs[l].cutoff);
+        float *go = l == 0 ? grad_h : gb[l & 1];
+        st = layer_bwd(&descs[l], pos, x[l], &weights[l], start, list_len(k), list_idx(k), (int64_t)n * K, 0, 0, order,
+                       n, g, go, grad_pos, wb + W.bws, W.bws_bytes, stream, l != n_layers - 1);
+        if (st != E2V2_OK) return st;
+        g = go;
+    }
     return E2V2_OK;
 }
 

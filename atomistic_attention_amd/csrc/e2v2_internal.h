@@ -564,6 +564,7 @@ struct AttnBwdArgs {
     float *dq, *dk;                  // [n][C]
     float *dhp;                      // [n][NC][C]
     float *grad_pos;                 // optional [n][3]: the bias terms of dL/dpos (target pass writes, source pass adds)
+    bool pos_acc;                    // the target pass adds to grad_pos instead of writing it
     float *m;                        // [n][NC][C] the message m_i, written when grad_pos is set
     int n, C, H, R;
     float cutoff;

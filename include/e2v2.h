@@ -349,6 +349,23 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
                                e2v2_rebuild_policy *policy, void *state, size_t state_bytes, float *out,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Gradient of the layer stack (fp32 storage): for L = sum(grad_out * out), with
+ * out the stack output of the last e2v2_stack_forward call at these positions and
+ * features, writes grad_h = dL/dh [n][(lmax+1)^2][C] and, if grad_pos is not
+ * NULL, grad_pos = dL/dpos [n][3] summed over the layers (the forces of the model
+ * for E = L are -grad_pos).  The neighbour lists and the processing order are
+ * those in `state` (left by that forward call), held fixed; each layer's input is
+ * recomputed over them, then each layer's gradient (e2v2_layer_backward, over its
+ * transposed list) runs in reverse order.  Arguments as for e2v2_stack_forward;
+ * every layer must have fp32 storage (E2V2_ERR_UNSUPPORTED otherwise).  Workspace:
+ * e2v2_stack_backward_workspace_bytes.  Asynchronous on `stream`. */
+size_t e2v2_stack_backward_workspace_bytes(int32_t n_layers, const e2v2_layer_desc *descs, int32_t n,
+                                           int32_t max_neighbors);
+e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, const e2v2_weights *weights,
+                                const float *pos, const float *h, int32_t n, int32_t max_neighbors,
+                                const void *state, size_t state_bytes, const float *grad_out, float *grad_h,
+                                float *grad_pos, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Host-side tables (no GPU needed). */
 int32_t e2v2_num_paths(int32_t lmax);   /* 1, 5, 15, 34 for lmax 0..3; -1 if out of range */

@@ -26,5 +26,7 @@ tests/test_oracle_*.py):
   backward.grad_h                 pinned: central finite differences of layer.layer_forward
                                   (directional and element-wise), forward equal to
                                   layer.layer_forward, one-neighbour and isolated-atom cases
+  backward.stack_grad_pos_h       pinned: central finite differences of the numpy layer
+                                  composition over the stack's fixed lists
 """
 from . import so3, layer, stack, backward  # noqa: F401

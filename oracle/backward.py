@@ -29,7 +29,7 @@ import torch
 
 from . import layer, so3
 
-__all__ = ["layer_forward_torch", "grad_h", "grad_pos_h", "real_sh_torch", "rbf_bias_torch"]
+__all__ = ["layer_forward_torch", "grad_h", "grad_pos_h", "stack_grad_pos_h", "real_sh_torch", "rbf_bias_torch"]
 
 
 def real_sh_torch(r, lmax: int):
@@ -141,3 +141,21 @@ def grad_h(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, g, *, lmax: int, hea
                               cutoff=cutoff, rows=rows, targets=targets)
     (out * torch.as_tensor(np.asarray(g, dtype=np.float64))).sum().backward()
     return ht.grad.numpy()
+
+
+def stack_grad_pos_h(pos, h0, layers, rows_by_cutoff, g):
+    """B4: (dL/dpos, dL/dh0) for L = sum(g * out) of a layer stack: layer l + 1 takes
+    layer l's output (the composition of stack.stack_step, without the rounding
+    between layers: the derivative of the real-valued composition), each layer on
+    the rows of its cutoff, the lists held fixed.  ``layers``: Workload-like weight
+    sets with a cfg (lmax, heads, cutoff); ``rows_by_cutoff``: {fp32 cutoff: rows}."""
+    pt = torch.tensor(np.asarray(pos, dtype=np.float64), requires_grad=True)
+    ht = torch.tensor(np.asarray(h0, dtype=np.float64), requires_grad=True)
+    x = ht
+    for wl in layers:
+        c = wl.cfg
+        rows = rows_by_cutoff[float(np.float32(c.cutoff))]
+        x = layer_forward_torch(pt, x, wl.w_q, wl.w_k, wl.w_v, wl.w_o, wl.w_rbf, wl.w_src, wl.w_tgt, lmax=c.lmax,
+                                heads=c.heads, cutoff=c.cutoff, rows=rows)
+    (x * torch.as_tensor(np.asarray(g, dtype=np.float64))).sum().backward()
+    return pt.grad.numpy(), ht.grad.numpy()

@@ -117,3 +117,34 @@ def test_stack_deterministic_and_reused_lists(gpu_lib):
     b, rb = _run_gpu(gpu_lib, st)
     assert ra == rb == [0]
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("K", [256, 60])
+def test_stack_gradient_matches_oracle(gpu_lib, K):
+    """dL/dh and dL/dpos of the four-layer stack (fp32 storage, 256 atoms) after one
+    forward call, against the oracle's reverse mode through the same lists; K = 60
+    makes the 8 A cap bind, so its list (and the 5 A lists taken from it) are not
+    symmetric."""
+    import dataclasses
+    from oracle import backward as OB
+    cfg = dataclasses.replace(W.STACKS["s1"], steps=1, max_neighbors=K)
+    st = W.make_stack(cfg)
+    descs, weights = [], []
+    for wl in st.layers:
+        c = wl.cfg
+        descs.append(gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32))
+        weights.append(W.device_arrays(wl)["weights"])
+    run = gpu_lib.StackRun(descs, weights, cfg.n, K)
+    pos = f32(st.traj[0])
+    h = f32(st.h0)
+    print(f"stack gradient n={cfg.n} K={K}", flush=True)
+    run.e2v2_stack_forward(pos, h)
+    g = np.random.default_rng(31).standard_normal(st.h0.shape).astype(np.float32).astype(np.float64)
+    gh, gp = run.e2v2_stack_backward(pos, h, f32(g), grad_pos=torch.empty((cfg.n, 3), device="cuda"))
+    torch.cuda.synchronize()
+    state = OS.StackState([wl.cfg.cutoff for wl in st.layers], K)
+    state.rebuild(st.traj[0], 0)
+    rp, rh = OB.stack_grad_pos_h(st.traj[0], st.h0, st.layers, state.rows, g)
+    eh, ep = rel_err(gh.cpu().numpy(), rh), rel_err(gp.cpu().numpy(), rp)
+    record(f"stack_gradient[s1,K={K}]", grad_h=eh, grad_pos=ep)
+    assert eh < 1e-4 and ep < 1e-4, (eh, ep)

@@ -247,3 +247,17 @@ def test_backward_argument_errors_and_workspace(lib):
     # plus 4 bytes per list entry for the transposed list
     e0 = lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000, 0)
     assert abs(lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), 1000, 100000) - e0 - 400000) <= 256
+
+
+def test_stack_backward_argument_errors(lib):
+    descs = (B.LayerDesc * 2)(_desc(), _desc())                        # bf16 storage
+    w = (B.Weights * 2)(B.Weights(*([FAKE] * 7)), B.Weights(*([FAKE] * 7)))
+    st = lib.e2v2_stack_backward(2, descs, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == B.E2V2_ERR_UNSUPPORTED
+    d32 = (B.LayerDesc * 2)(_desc(storage=B.E2V2_FP32), _desc(storage=B.E2V2_FP32, cutoff=8.0))
+    st = lib.e2v2_stack_backward(2, d32, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, FAKE, FAKE, FAKE_MIS, FAKE, 1 << 30, None)
+    assert st == B.E2V2_ERR_ARG
+    st = lib.e2v2_stack_backward(2, d32, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, FAKE, FAKE, None, FAKE, 100, None)
+    assert st == B.E2V2_ERR_ARG and "workspace" in lib.e2v2_last_error().decode()
+    assert lib.e2v2_stack_backward_workspace_bytes(2, d32, 1000, 8) > lib.e2v2_layer_backward_workspace_bytes(
+        ctypes.byref(d32[0]), 1000, 8000)

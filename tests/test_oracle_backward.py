@@ -199,3 +199,36 @@ def test_position_gradient_finite_with_an_atom_at_the_origin():
     fd = (L(pos + eps * u) - L(pos - eps * u)) / (2 * eps)
     an = float(np.sum(gp * u))
     assert abs(fd - an) <= 2e-6 * max(1.0, abs(an)), (fd, an)
+
+
+def test_stack_gradient_matches_central_differences():
+    """B4: the gradients of a two-layer stack (5 A and 8 A lists, the second taken
+    from a capped list) against central differences of the numpy layer
+    composition over the same fixed lists, in h and in pos."""
+    import dataclasses
+    from atomistic_attention_amd import workloads as W
+    from oracle import stack as OS
+    cfg = dataclasses.replace(W.STACKS["s1"], n=48, steps=1, cutoffs=(5.0, 8.0), max_neighbors=20)
+    st = W.make_stack(cfg)
+    pos, h0 = st.traj[0], st.h0
+    state = OS.StackState([wl.cfg.cutoff for wl in st.layers], cfg.max_neighbors)
+    state.rebuild(pos, 0)
+    rng = np.random.default_rng(21)
+    g = rng.standard_normal(h0.shape)
+    gp, gh = backward.stack_grad_pos_h(pos, h0, st.layers, state.rows, g)
+
+    def L(p, h):
+        x = h
+        for wl in st.layers:
+            c = wl.cfg
+            x = layer.layer_forward(p, x, wl.w_q, wl.w_k, wl.w_v, wl.w_o, wl.w_rbf, wl.w_src, wl.w_tgt, lmax=c.lmax,
+                                    heads=c.heads, cutoff=c.cutoff, rows=state.rows[float(np.float32(c.cutoff))])["out"]
+        return float(np.sum(g * x))
+
+    eps = 1e-6
+    u = rng.standard_normal(h0.shape)
+    fd = (L(pos, h0 + eps * u) - L(pos, h0 - eps * u)) / (2 * eps)
+    assert abs(fd - np.sum(gh * u)) <= 1e-6 * max(1.0, abs(fd)), (fd, np.sum(gh * u))
+    v = rng.standard_normal(pos.shape)
+    fd = (L(pos + eps * v, h0) - L(pos - eps * v, h0)) / (2 * eps)
+    assert abs(fd - np.sum(gp * v)) <= 2e-6 * max(1.0, abs(fd)), (fd, np.sum(gp * v))
