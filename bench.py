@@ -197,6 +197,33 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
             fn()
         torch.cuda.synchronize()
         res[key] = (time.perf_counter() - t0) * 1e3 / steps
+    # the four-layer stack in fp32 storage on the same system: one model step forward,
+    # then dL/dh and dL/dpos of the whole model (the forces for E = sum(g * out))
+    import dataclasses
+    sc = dataclasses.replace(W.STACKS["s4"], base=name, steps=1)
+    stk = W.make_stack(sc)
+    sdescs, sweights = [], []
+    for wl in stk.layers:
+        lc = wl.cfg
+        sdescs.append(B.make_desc(lc.lmax, lc.channels, lc.heads, lc.n_rbf, lc.cutoff, torch.float32))
+        sweights.append(W.device_arrays(wl)["weights"])
+    run = B.StackRun(sdescs, sweights, sc.n, sc.max_neighbors, rebuild_every=1 << 30, max_displacement=1e9)
+    spos = torch.from_numpy(np.ascontiguousarray(stk.traj[0], dtype=np.float32)).to(dev)
+    sh = torch.from_numpy(np.ascontiguousarray(stk.h0, dtype=np.float32)).to(dev)
+    sout = torch.empty(stk.h0.shape, dtype=torch.float32, device=dev)
+    sgh = torch.empty_like(sout)
+    sgp = torch.empty((sc.n, 3), dtype=torch.float32, device=dev)
+    run.e2v2_stack_forward(spos, sh, out=sout)                      # builds the lists once
+    for key, fn in (("stack_forward", lambda: run.e2v2_stack_forward(spos, sh, out=sout)),
+                    ("stack_gradients", lambda: run.e2v2_stack_backward(spos, sh, g, grad_h=sgh, grad_pos=sgp))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        res[key] = (time.perf_counter() - t0) * 1e3 / 5
     nnz = int(nnz)
     C, nc, H = c.channels, c.n_comp, c.heads
     # attention adjoint, algorithmic bytes: target pass per pair k_j, h'_j, position,
@@ -214,6 +241,10 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
             "nnz": nnz, "steps": steps, "ms_backward": res["backward"],
             "ms_backward_with_positions": res["backward_pos"], "ms_forward_same_layer": res["forward"],
             "ms_forward_then_gradients": res["train"],
+            "stack_fp32": {"model": "four layers (5, 5, 5, 8 A; the 8 A list capped at K=256, the 5 A lists "
+                                    "filtered from it), fp32 storage, same system, lists reused",
+                           "ms_model_step_forward": res["stack_forward"],
+                           "ms_gradients_dh_dpos": res["stack_gradients"]},
             "pairs_per_s_backward": nnz / (res["backward"] * 1e-3),
             "pairs_per_s_backward_with_positions": nnz / (res["backward_pos"] * 1e-3),
             "attention_adjoint_algorithmic_bytes": per_pair * nnz + per_node * c.n}
