@@ -730,7 +730,8 @@ static e2v2_status layer_bwd(const e2v2_layer_desc *desc, const float *pos, cons
                              int64_t max_entries, int32_t symmetric, int32_t reuse_forward,
                              const int32_t *target_order, int32_t n, const float *grad_out, float *grad_h,
                              float *grad_pos, void *workspace, size_t workspace_bytes, hipStream_t stream,
-                             bool pos_acc)
+                             bool pos_acc, const int32_t *src_start = nullptr, const int32_t *src_len = nullptr,
+                             const int32_t *src_idx = nullptr)
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
@@ -791,7 +792,9 @@ static e2v2_status layer_bwd(const e2v2_layer_desc *desc, const float *pos, cons
     // Step 4 adjoint: dq (target pass), dL/dh' and dk (source pass, over the transposed
     // list; a symmetric list is its own transpose).
     AttnBwdArgs a{};
-    if (symmetric) {
+    if (src_start) {                 // a transposed list the caller built (the stack, once per cutoff)
+        a.src_start = src_start; a.src_len = src_len; a.src_idx = src_idx;
+    } else if (symmetric) {
         a.src_start = nbr_start; a.src_len = nbr_len; a.src_idx = nbr_idx;
     } else {
         int32_t *tstart = reinterpret_cast<int32_t *>(ws + B.tstart);
@@ -959,7 +962,7 @@ namespace {
 // Workspace of the stack gradient: one layer-gradient workspace (which also serves
 // the forward recomputation), the fp32 inputs of layers 1..L-1, two gradient buffers.
 struct StackBwdWs {
-    size_t bws, bws_bytes, x, per_x, g0, g1, total;
+    size_t bws, bws_bytes, x, per_x, g0, g1, tl, per_tl, total;
 };
 StackBwdWs stack_bwd_ws(int L, const e2v2_layer_desc *d, int n, int K)
 {
@@ -971,6 +974,10 @@ StackBwdWs stack_bwd_ws(int L, const e2v2_layer_desc *d, int n, int K)
     w.x = o; w.per_x = feat; o += feat * (size_t)(L > 1 ? L - 1 : 0);
     w.g0 = o; o += feat;
     w.g1 = o; o += feat;
+    // one transposed list per distinct cutoff: cnt, start, cur [n + 1], len [n], idx [n K]
+    const size_t N1 = al256(((size_t)n + 1) * 4);
+    w.tl = o; w.per_tl = 3 * N1 + al256((size_t)n * 4) + al256((size_t)n * K * 4);
+    o += w.per_tl * (size_t)L;
     w.total = o + 256;
     return w;
 }
@@ -1178,14 +1185,27 @@ e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, 
         if (st != E2V2_OK) return st;
         x[l + 1] = xo;
     }
-    // 2. the layers' gradients in reverse; dL/dpos summed over the layers
+    // 2. the transposed list of each distinct cutoff's list, built once
+    const size_t N1 = al256(((size_t)n + 1) * 4);
+    auto tl = [&](int k, int part) -> int32_t * {
+        char *b = wb + W.tl + (size_t)k * W.per_tl;
+        const size_t off[5] = {0, N1, 2 * N1, 3 * N1, 3 * N1 + al256((size_t)n * 4)};
+        return reinterpret_cast<int32_t *>(b + off[part]);
+    };
+    for (int k = 0; k < S.ncut; ++k) {
+        const hipError_t e = launch_transpose_list(start, list_len(k), list_idx(k), n, (long long)n * K, tl(k, 0),
+                                                   tl(k, 1), tl(k, 2), tl(k, 4), tl(k, 3), stream);
+        if (e != hipSuccess) return hip_fail(e, "transposed list");
+    }
+    // 3. the layers' gradients in reverse; dL/dpos summed over the layers
     float *gb[2] = {reinterpret_cast<float *>(wb + W.g0), reinterpret_cast<float *>(wb + W.g1)};
     const float *g = grad_out;
     for (int l = n_layers - 1; l >= 0; --l) {
         const int k = cutoff_index(S.ncut, S.cut, descs[l].cutoff);
         float *go = l == 0 ? grad_h : gb[l & 1];
         st = layer_bwd(&descs[l], pos, x[l], &weights[l], start, list_len(k), list_idx(k), (int64_t)n * K, 0, 0, order,
-                       n, g, go, grad_pos, wb + W.bws, W.bws_bytes, stream, l != n_layers - 1);
+                       n, g, go, grad_pos, wb + W.bws, W.bws_bytes, stream, l != n_layers - 1, tl(k, 1), tl(k, 3),
+                       tl(k, 4));
         if (st != E2V2_OK) return st;
         g = go;
     }
