@@ -210,3 +210,23 @@ def test_backward_full_size_sampled(gpu_lib):
     ep = rel_err(gp[sample], rp[loc[sample]])
     record("backward_sampled[g4]", grad_h=e, grad_pos=ep)
     assert e < TOL and ep < TOL, (e, ep)
+
+
+def test_position_gradient_full_size_invariants(gpu_lib):
+    """32,768 atoms, l_max = 0: the positions enter through pair distances only, so
+    dL/dpos has no net force and no net torque (every pair's two terms come from
+    different waves, so this also checks that the target and source passes agree
+    on every pair)."""
+    cfg = W.LayerConfig("g4l0", 32768, "uniform", 0.1, 5.0, 0, 0, 128, 16, 32, "fp32", 1007)
+    wl = W.make_workload(cfg)
+    g = _g(wl, 7)
+    gh, gp, _ = _gpu_grad(gpu_lib, wl, g, pos_grad=True, symmetric=True)
+    gp = gp.astype(np.float64)
+    r = wl.pos
+    scale = np.sum(np.abs(gp))
+    force = np.abs(gp.sum(axis=0)).max()
+    torque = np.abs(np.cross(r, gp).sum(axis=0)).max()
+    tscale = np.sum(np.linalg.norm(r, axis=1) * np.linalg.norm(gp, axis=1))
+    record("position_gradient_invariants[g4l0]", net_force=force / scale, net_torque=torque / tscale)
+    assert np.all(np.isfinite(gp)) and scale > 0
+    assert force <= 1e-5 * scale and torque <= 1e-5 * tscale, (force / scale, torque / tscale)
