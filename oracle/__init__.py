@@ -9,15 +9,21 @@ Parity status per function (what pins it to something other than itself is in
 tests/test_oracle_*.py):
   so3.real_sh / real_sh_legendre  pinned: scipy complex harmonics, closed forms
   so3.cg_complex                  pinned: sympy, unitarity
+  so3.paths                       pinned: the literal path lists at l_max 0..3
   so3.coupling_tensor             pinned: equivariance, dot/cross closed forms,
-                                  sparsity rule of the explainer section 2.2
+                                  sparsity rule of the explainer section 2.2, the
+                                  closed-form EAAS table at l_max = 2 (odd paths too)
   so3.wigner_d                    pinned: D^1 = P R P^T, orthogonal, det 1, homomorphism
   so3.eaas_couple                 pinned: Proposition 4.3 (equals the full CG product)
   layer.neighbors                 pinned: scipy cKDTree (sets and K-nearest)
-  layer.rbf_bias                  pinned: closed-form values of Gaussians and envelope
+  layer.rbf_bias                  pinned: closed-form values of Gaussians and envelope,
+                                  0 from the cutoff on (value and slope)
   layer.attention                 pinned: torch scaled_dot_product_attention (l_max = 0),
                                   one-neighbour and equal-logit special cases
-  layer.layer_forward             pinned: rotation equivariance to 1e-10
+  layer.layer_forward             pinned: rotation equivariance to 1e-10; per-degree
+                                  W_V / W_O by distinct scalar weights per degree; a
+                                  listed pair beyond the cutoff against a closed-form
+                                  softmax
   stack.filter_rows               pinned: equals the brute-force search at the smaller cutoff
   stack.max_displacement2         pinned: exact dyadic displacements, strict threshold
   stack.StackState (rebuild rule) pinned: trajectories with known rebuild steps

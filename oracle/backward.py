@@ -15,8 +15,10 @@ B1  L(h) = sum(g * out(h)) for a fixed upstream gradient g; the oracle returns
 
 B3  L(pos, h) as in B1 with the positions free as well: dL/dpos through the
     encodings Y(r_i) of both couplings and through every pair distance in the
-    bias, with the neighbour lists held fixed (the envelope and its slope vanish
-    at the cutoff, so a pair crossing it contributes nothing either way).  At a
+    bias, with the neighbour lists held fixed.  The envelope and its slope are 0
+    from the cutoff on (layer.rbf_bias), so a listed pair beyond it -- a reused
+    list after the atoms moved -- adds no bias term to dL/dpos, and a pair
+    crossing the cutoff sees no jump in either.  At a
     zero position vector the direction is undefined: its encoding is held
     constant, so that atom's position receives only the bias terms.
 """
@@ -60,13 +62,13 @@ def real_sh_torch(r, lmax: int):
 
 
 def rbf_bias_torch(d, w_rbf, cutoff: float):
-    """layer.rbf_bias in torch (differentiable in d)."""
+    """layer.rbf_bias in torch (differentiable in d; value and slope 0 from the cutoff on)."""
     w = torch.as_tensor(np.asarray(w_rbf, dtype=np.float64))
     R = w.shape[0]
     delta = cutoff / (R - 1)
     mu = torch.arange(R, dtype=torch.float64) * delta
     phi = torch.exp(-((d[..., None] - mu) ** 2) / (2.0 * delta * delta))
-    fc = 0.5 * (torch.cos(math.pi * d / cutoff) + 1.0)
+    fc = torch.where(d < cutoff, 0.5 * (torch.cos(math.pi * d / cutoff) + 1.0), torch.zeros_like(d))
     return fc[..., None] * (phi @ w)
 
 

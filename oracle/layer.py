@@ -21,8 +21,11 @@ O5 source TP   -- h'_j = sum_p w_src[p] (v_j (x) Y(r_j))_p, full dense CG sum,
 O6 attention   -- b_h(d) = f_c(d) sum_k W_rbf[k, h] phi_k(d), Gaussian RBFs
                   phi_k(d) = exp(-(d - mu_k)^2 / (2 Delta^2)), mu_k = k r_c/(R-1),
                   Delta = r_c/(R-1), cosine envelope f_c(d) = (cos(pi d / r_c) + 1)/2
-                  (FlashSchNet page, section 2.1: distance, Gaussian expansion and
-                  cosine envelope);
+                  for d < r_c and 0 from r_c on (FlashSchNet page, section 2.1:
+                  distance, Gaussian expansion and cosine envelope; section 2.2:
+                  the cutoff mask.  A listed pair beyond r_c -- a reused list after
+                  the atoms moved, Tessera article, neighbour reuse -- gets no bias,
+                  while its q.k term still counts);
                   s_jh = q_i^h . k_j^h / sqrt(C/H) + b_h(d_ij);
                   alpha = explicit softmax over the whole neighbour set;
                   m_i[l, m, c] = sum_j alpha_{j, head(c)} h'_j[l, m, c]
@@ -136,13 +139,14 @@ def rows_to_csr(rows):
 
 
 def rbf_bias(d: np.ndarray, w_rbf: np.ndarray, cutoff: float) -> np.ndarray:
-    """b[..., h] = f_c(d) * sum_k W_rbf[k, h] exp(-(d - mu_k)^2 / (2 Delta^2))."""
+    """b[..., h] = f_c(d) * sum_k W_rbf[k, h] exp(-(d - mu_k)^2 / (2 Delta^2)),
+    f_c(d) = (cos(pi d / r_c) + 1) / 2 below r_c and 0 from r_c on (the cutoff mask)."""
     d = np.asarray(d, dtype=np.float64)
     R = w_rbf.shape[0]
     delta = cutoff / (R - 1)
     mu = np.arange(R, dtype=np.float64) * delta
     phi = np.exp(-((d[..., None] - mu) ** 2) / (2.0 * delta * delta))
-    fc = 0.5 * (np.cos(np.pi * d / cutoff) + 1.0)
+    fc = np.where(d < cutoff, 0.5 * (np.cos(np.pi * d / cutoff) + 1.0), 0.0)
     return fc[..., None] * (phi @ np.asarray(w_rbf, dtype=np.float64))
 
 

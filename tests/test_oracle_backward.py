@@ -157,6 +157,26 @@ def test_position_gradient_matches_central_differences(seed):
         assert abs(fd - gp[a, k]) <= 2e-6 * max(1.0, abs(gp[a, k])), (a, k, fd, gp[a, k])
 
 
+def test_position_gradient_on_a_list_with_pairs_beyond_the_cutoff():
+    """A reused list (Tessera article, neighbour reuse) holds pairs that have moved
+    past r_c.  Their bias and its slope are 0 (the cutoff mask), so the torch
+    gradient must still match central differences of the numpy forward pass; a
+    slope term left on those pairs, or a missing one below r_c, fails here."""
+    pos, h, W, g = _system(14)
+    rows = layer.neighbors(pos, CUT + 0.6)               # the list of a larger radius
+    far = sum(int(np.sum(np.linalg.norm(pos[r] - pos[i], axis=1) >= CUT)) for i, r in enumerate(rows))
+    assert far >= 20
+    gp = _gpos(pos, h, W, g, rows)
+    rng = np.random.default_rng(21)
+    eps = 1e-6
+    L = lambda p: np.sum(g * _fwd_np(p, h, W, rows))
+    for _ in range(2):
+        u = rng.standard_normal(pos.shape)
+        fd = (L(pos + eps * u) - L(pos - eps * u)) / (2 * eps)
+        an = float(np.sum(gp * u))
+        assert abs(fd - an) <= 2e-6 * max(1.0, abs(an)), (fd, an)
+
+
 def test_position_gradient_vanishes_without_geometry():
     """l_max = 0 and W_rbf = 0: the output does not depend on the positions."""
     pos, h, W, g = _system(14)

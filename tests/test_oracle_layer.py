@@ -169,3 +169,79 @@ def test_target_subset_matches_full():
     sub = np.array([0, 17, 100, 255])
     part = layer.layer_forward_workload(wl, targets=sub)
     assert np.max(np.abs(part["out"] - full["out"][sub])) < 1e-13
+
+
+# ---------------------------------------------------------------- envelope beyond the cutoff
+def test_envelope_is_zero_from_the_cutoff_on():
+    """The cosine envelope is the cutoff mask of the FlashSchNet page (section 2.2):
+    f_c(d) = 0 for d >= r_c.  (cos(pi d / r_c) + 1) / 2 itself would rise again
+    beyond r_c (0.0089 at 5.3 A for r_c = 5) and return to 1 at 2 r_c."""
+    rc, R = 5.0, 8
+    w = RNG.standard_normal((R, 3))
+    d = np.array([5.0, 5.0 + 1e-9, 5.3, 5.5, 7.5, 10.0, 12.0])
+    assert np.all(layer.rbf_bias(d, w, rc) == 0.0)
+    below = layer.rbf_bias(np.array([5.0 - 1e-3]), np.ones((R, 1)), rc)[0, 0]
+    assert 0.0 < below < 1e-6                        # continuous at r_c from below
+    # the torch form (gradients) agrees: value and slope 0 beyond r_c
+    from oracle import backward
+    dt = torch.tensor([4.0, 5.3, 6.0], dtype=torch.float64, requires_grad=True)
+    b = backward.rbf_bias_torch(dt, w, rc)
+    assert np.all(b[1:].detach().numpy() == 0.0)
+    b.sum().backward()
+    assert dt.grad[0] != 0.0 and np.all(dt.grad[1:].numpy() == 0.0)
+
+
+def test_listed_pair_beyond_cutoff_gets_no_bias():
+    """Reused list (Tessera article, neighbour reuse): target 0 lists atom 1 at
+    3 A and atom 2 at 5.4 A, past r_c = 5.  With W_Q = W_K = 0 the logits are the
+    biases alone: b(3 A) from the Gaussians and the envelope written out here, and 0
+    for the pair beyond r_c, so alpha = (e^b, 1) / (e^b + 1) per head."""
+    C, H, R, L, rc = 8, 2, 6, 2, 5.0
+    p = _rand_layer(3, C, H, R, L, 1.0, 31)
+    p["pos"] = np.array([[0.2, -0.1, 0.3], [0.2, -0.1, 3.3], [5.6, -0.1, 0.3]])
+    p["w_q"] = np.zeros((C, C))
+    p["w_k"] = np.zeros((C, C))
+    rows = [np.array([1, 2], dtype=np.int32), np.array([0], dtype=np.int32), np.array([0], dtype=np.int32)]
+    o = layer.layer_forward(**p, lmax=L, heads=H, cutoff=rc, rows=rows)
+    delta = rc / (R - 1)
+    d = 3.0
+    fc = 0.5 * (math.cos(math.pi * d / rc) + 1.0)
+    b = np.array([fc * sum(p["w_rbf"][k, h] * math.exp(-((d - k * delta) ** 2) / (2 * delta * delta))
+                           for k in range(R)) for h in range(H)])
+    a1 = np.exp(b) / (np.exp(b) + 1.0)                 # per head
+    head_of = np.arange(C) // (C // H)
+    hp = {int(s): o["hprime"][t] for t, s in enumerate(o["src"])}
+    want = a1[head_of] * hp[1] + (1.0 - a1[head_of]) * hp[2]
+    assert np.max(np.abs(o["m"][0] - want)) < 1e-13
+    # with the unclamped envelope the far pair would carry f_c(5.4 A) = 0.0157 of its sum
+    assert abs(0.5 * (math.cos(math.pi * 5.4 / rc) + 1.0) - 0.0157) < 1e-4
+
+
+# ---------------------------------------------------------------- per-degree weights
+def test_per_degree_value_and_output_weights():
+    """W_V[l] acts on degree l of the input and W_O[l] on degree l of the output
+    (readings R12, R14).  One neighbour (alpha = 1), input nonzero in degree l_i only,
+    W_V[l] = s_l I and W_O[l] = t_l I with distinct s_l, t_l: block l_o of the output
+    is s_{l_i} t_{l_o} times the output with identity weights.  Taking W_V[0] for
+    every degree, or W_O of a neighbouring degree, breaks the factor."""
+    C, H, L, rc = 8, 2, 3, 4.0
+    p = _rand_layer(2, C, H, 5, L, 1.0, 41)
+    p["pos"] = np.array([[0.3, -0.7, 1.1], [-1.2, 0.4, 2.0]])
+    rows = [np.array([1], dtype=np.int32), np.array([0], dtype=np.int32)]
+    s = np.array([0.5, 2.0, -3.0, 7.0])
+    t = np.array([11.0, -0.25, 4.0, 0.125])
+    eye = np.broadcast_to(np.eye(C), (L + 1, C, C))
+    sl = so3.block_slices(L)
+    for li in range(L + 1):
+        h = np.zeros_like(p["h"])
+        h[:, sl[li], :] = p["h"][:, sl[li], :]
+        base = dict(p, h=h, w_v=eye.copy(), w_o=eye.copy())
+        ref = layer.layer_forward(**base, lmax=L, heads=H, cutoff=rc, rows=rows)["out"]
+        scaled = dict(base, w_v=s[:, None, None] * eye, w_o=t[:, None, None] * eye)
+        out = layer.layer_forward(**scaled, lmax=L, heads=H, cutoff=rc, rows=rows)["out"]
+        nonzero = 0
+        for lo in range(L + 1):
+            want = s[li] * t[lo] * ref[:, sl[lo], :]
+            assert np.max(np.abs(out[:, sl[lo], :] - want)) <= 1e-13 * max(1.0, np.max(np.abs(want)))
+            nonzero += np.max(np.abs(want)) > 1e-6
+        assert nonzero >= 2                                # several output degrees are fed

@@ -196,3 +196,68 @@ def test_eaas_equals_full_cg(lmax):
         for g in (0.0, 1.1):
             e = so3.eaas_couple(x, r, w, lmax, gamma=g)
             assert np.max(np.abs(e - full)) < 1e-12
+
+
+# ---------------------------------------------------------------- literal path order and EAAS table
+# Every (l_i, l_f, l_o) with the triangle rule, odd l_i + l_f + l_o included
+# (the odd rule of the explainer's section 2.2 needs them), ordered by l_o, then
+# l_i, then l_f.  Written out by hand from that rule.
+PATHS_L2 = [(0, 0, 0), (1, 1, 0), (2, 2, 0),
+            (0, 1, 1), (1, 0, 1), (1, 1, 1), (1, 2, 1), (2, 1, 1), (2, 2, 1),
+            (0, 2, 2), (1, 1, 2), (1, 2, 2), (2, 0, 2), (2, 1, 2), (2, 2, 2)]
+PATHS_L3 = [(0, 0, 0), (1, 1, 0), (2, 2, 0), (3, 3, 0),
+            (0, 1, 1), (1, 0, 1), (1, 1, 1), (1, 2, 1), (2, 1, 1), (2, 2, 1), (2, 3, 1), (3, 2, 1), (3, 3, 1),
+            (0, 2, 2), (1, 1, 2), (1, 2, 2), (1, 3, 2), (2, 0, 2), (2, 1, 2), (2, 2, 2), (2, 3, 2),
+            (3, 1, 2), (3, 2, 2), (3, 3, 2),
+            (0, 3, 3), (1, 2, 3), (1, 3, 3), (2, 1, 3), (2, 2, 3), (2, 3, 3), (3, 0, 3), (3, 1, 3), (3, 2, 3),
+            (3, 3, 3)]
+
+
+def test_path_order_literal():
+    assert len(PATHS_L2) == 15 and len(PATHS_L3) == 34
+    assert [tuple(p) for p in so3.paths(2)] == PATHS_L2
+    assert [tuple(p) for p in so3.paths(3)] == PATHS_L3
+    assert [tuple(p) for p in so3.paths(1)] == [(0, 0, 0), (1, 1, 0), (0, 1, 1), (1, 0, 1), (1, 1, 1)]
+    assert [tuple(p) for p in so3.paths(0)] == [(0, 0, 0)]
+
+
+def _eaas_table_l2():
+    """The EAAS coefficients E_p(m_i -> m_o) = sqrt(2 l_f + 1) T_p[m_i, 0, m_o] at
+    l_max = 2, as closed forms: the sparse re-index of the explainer's section 2.2
+    (m_i = m_o for even l_i + l_f + l_o; m_i = -m_o with a sign for odd), with the
+    values of the real Condon-Shortley convention (readings R4, R8), derived by
+    hand from the complex Clebsch-Gordan coefficients in the real basis.  37 entries."""
+    r = math.sqrt
+    t = {
+        (0, 0, 0): {(0, 0): 1.0},
+        (0, 1, 1): {(0, 0): r(3)},
+        (0, 2, 2): {(0, 0): r(5)},
+        (1, 0, 1): {(m, m): 1.0 for m in (-1, 0, 1)},
+        (1, 1, 0): {(0, 0): -1.0},
+        (1, 1, 1): {(-1, 1): r(1.5), (1, -1): -r(1.5)},
+        (1, 1, 2): {(-1, -1): r(1.5), (1, 1): r(1.5), (0, 0): r(2)},
+        (1, 2, 1): {(-1, -1): r(0.5), (1, 1): r(0.5), (0, 0): -r(2)},
+        (1, 2, 2): {(-1, 1): r(2.5), (1, -1): -r(2.5)},
+        (2, 0, 2): {(m, m): 1.0 for m in (-2, -1, 0, 1, 2)},
+        (2, 1, 1): {(-1, -1): -r(0.9), (1, 1): -r(0.9), (0, 0): -r(1.2)},
+        (2, 1, 2): {(-2, 2): r(2), (-1, 1): r(0.5), (1, -1): -r(0.5), (2, -2): -r(2)},
+        (2, 2, 0): {(0, 0): 1.0},
+        (2, 2, 1): {(-1, 1): -r(1.5), (1, -1): r(1.5)},
+        (2, 2, 2): {(-2, -2): r(10 / 7), (2, 2): r(10 / 7), (-1, -1): -r(5 / 14), (1, 1): -r(5 / 14),
+                    (0, 0): -r(10 / 7)},
+    }
+    assert sum(len(v) for v in t.values()) == 37
+    return t
+
+
+def test_eaas_table_closed_forms():
+    """Every entry of the m_f = 0 slice, odd paths included, equals the table; all
+    other entries are zero."""
+    table = _eaas_table_l2()
+    assert set(table) == set(PATHS_L2)
+    for (li, lf, lo), ent in table.items():
+        E = math.sqrt(2 * lf + 1) * so3.coupling_tensor(li, lf, lo)[:, lf, :]
+        want = np.zeros_like(E)
+        for (mi, mo), v in ent.items():
+            want[mi + li, mo + lo] = v
+        assert np.max(np.abs(E - want)) < 1e-14, (li, lf, lo)
