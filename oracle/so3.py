@@ -224,7 +224,7 @@ def tensor_product(x: np.ndarray, r: np.ndarray, w: np.ndarray, lmax: int) -> np
     out = np.zeros_like(x)
     for p, (li, lf, lo) in enumerate(paths(lmax)):
         T = coupling_tensor(li, lf, lo)
-        term = np.einsum("ijk,nic,nj->nkc", T, x[:, sl[li], :], Y[:, sl[lf]])
+        term = np.einsum("ijk,nic,nj->nkc", T, x[:, sl[li], :], Y[:, sl[lf]], optimize=True)
         out[:, sl[lo], :] += term * w[p][None, None, :]
     return out
 
