@@ -114,7 +114,7 @@ def load(path: str = LIB_PATH):
     lib.e2v2_stack_backward_workspace_bytes.argtypes = [i32, ctypes.POINTER(LayerDesc), i32, i32]
     lib.e2v2_stack_backward_workspace_bytes.restype = sz
     lib.e2v2_stack_backward.argtypes = [i32, ctypes.POINTER(LayerDesc), ctypes.POINTER(Weights), vp, vp, i32, i32,
-                                        vp, sz, vp, vp, vp, vp, sz, vp]
+                                        vp, sz, ctypes.POINTER(RebuildPolicy), vp, vp, vp, vp, sz, vp]
     lib.e2v2_stack_backward.restype = ctypes.c_int
     lib.e2v2_status_string.argtypes = [ctypes.c_int]
     lib.e2v2_status_string.restype = ctypes.c_char_p
@@ -443,6 +443,8 @@ class StackRun:
         """dL/dh (and dL/dpos if grad_pos, a [n, 3] fp32 tensor, is given) of L = sum(grad_out * out)
         for the output of the last e2v2_stack_forward call at (pos, h); fp32 storage."""
         lib = load()
+        if self.policy.rebuilds < 1:
+            raise E2V2Error(E2V2_ERR_ARG, "e2v2_stack_backward: no e2v2_stack_forward call has filled the state")
         _dev(pos, torch.float32, "pos")
         _dev(h, torch.float32, "h")
         _dev(grad_out, torch.float32, "grad_out")
@@ -456,7 +458,8 @@ class StackRun:
         if getattr(self, "bworkspace", None) is None or self.bworkspace.numel() < wb:
             self.bworkspace = torch.empty(wb, dtype=torch.uint8, device=h.device)
         _check(lib.e2v2_stack_backward(self.L, self.descs, self.weights, _ptr(pos), _ptr(h), self.n, self.K,
-                                       _ptr(self.state), self.state.numel(), _ptr(grad_out), _ptr(grad_h),
+                                       _ptr(self.state), self.state.numel(), ctypes.byref(self.policy),
+                                       _ptr(grad_out), _ptr(grad_h),
                                        _ptr(grad_pos), _ptr(self.bworkspace), self.bworkspace.numel(),
                                        _stream(stream)))
         return grad_h if grad_pos is None else (grad_h, grad_pos)

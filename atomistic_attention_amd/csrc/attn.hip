@@ -142,7 +142,7 @@ void attn_kernel(const AttnArgs A)
         const bool vp = (jp >= 0) && (jp < n);
         const float dx = pj.x - pi4.x, dy = pj.y - pi4.y, dz = pj.z - pi4.z;
         const float d = vp ? __builtin_amdgcn_sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;   // v_sqrt_f32, 1 ulp
-        const float fc = vp ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
+        const float fc = (vp && d < A.cutoff) ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;   // cutoff mask
         const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
         const float t0 = fmaf(d, inv_delta, -gsc * (float)kq);   // g (d - mu_k) / Delta for k = kq
         const float *wrow = sW + kq * 16 + pm;

@@ -26,6 +26,7 @@ struct BiasLane {
     float w[16];        // log2(e) W_rbf[4 kk + r][head], zero past R
     float inv_delta;    // kGsc (R - 1) / cutoff
     float cos_scale;    // 1 / (2 cutoff): cos(pi d / rc) = cos(2 pi * d cos_scale)
+    float cutoff;       // the envelope and its slope are 0 from here on (cutoff mask)
     float t_off;        // kGsc * r
     int kk_n;           // ceil(R / 4)
 
@@ -38,13 +39,14 @@ struct BiasLane {
         }
         inv_delta = kGsc * (float)(R - 1) / cutoff;
         cos_scale = 0.5f / cutoff;
+        this->cutoff = cutoff;
         t_off = kGsc * (float)r;
         kk_n = (R + 3) >> 2;
     }
     // b_h(d) * log2(e), summed over the head's 4 lanes
     __device__ __forceinline__ float bias2(float d) const
     {
-        const float fc = 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f);
+        const float fc = d < cutoff ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
         const float t0 = fmaf(d, inv_delta, -t_off);
         float s = 0.f;
 #pragma unroll
@@ -60,8 +62,9 @@ struct BiasLane {
     // S1 = sum W phi_k t_k, t_k = kGsc (d - mu_k) / Delta (phi_k' = -phi_k (d - mu_k) / Delta^2).
     __device__ __forceinline__ void bias2_slope(float d, float &b2, float &slope) const
     {
-        const float fc = 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f);
-        const float fcp = -(0.5f * 3.14159265358979f * 2.f) * cos_scale * __builtin_amdgcn_sinf(d * cos_scale);
+        const bool in = d < cutoff;
+        const float fc = in ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
+        const float fcp = in ? -(0.5f * 3.14159265358979f * 2.f) * cos_scale * __builtin_amdgcn_sinf(d * cos_scale) : 0.f;
         const float t0 = fmaf(d, inv_delta, -t_off);
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll

@@ -284,7 +284,7 @@ void attn_pair_kernel(const AttnArgs A)
     auto bias_of = [&](float4 pj, float4 pt, bool ok) -> floatx4 {
         const float dx = pj.x - pt.x, dy = pj.y - pt.y, dz = pj.z - pt.z;
         const float d = ok ? __builtin_amdgcn_sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;   // v_sqrt_f32, 1 ulp
-        const float fc = ok ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;
+        const float fc = (ok && d < A.cutoff) ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;   // cutoff mask
         const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
         const float t0 = fmaf(d, inv_delta, -gsc * (float)(8 * kq));   // g (d - mu_k) / Delta for k = 8 kq
         // A operand: lane (kq, pm) holds phi_k of pair pm for k = 8 kq + i (+ 32)

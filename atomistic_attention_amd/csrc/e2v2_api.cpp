@@ -975,9 +975,11 @@ StackBwdWs stack_bwd_ws(int L, const e2v2_layer_desc *d, int n, int K)
     w.g0 = o; o += feat;
     w.g1 = o; o += feat;
     // one transposed list per distinct cutoff: cnt, start, cur [n + 1], len [n], idx [n K]
+    float cut[kMaxStackLayers];
+    const int ncut = distinct_cutoffs(L, d, cut);
     const size_t N1 = al256(((size_t)n + 1) * 4);
     w.tl = o; w.per_tl = 3 * N1 + al256((size_t)n * 4) + al256((size_t)n * K * 4);
-    o += w.per_tl * (size_t)L;
+    o += w.per_tl * (size_t)ncut;
     w.total = o + 256;
     return w;
 }
@@ -1147,13 +1149,18 @@ size_t e2v2_stack_backward_workspace_bytes(int32_t n_layers, const e2v2_layer_de
 
 e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, const e2v2_weights *weights,
                                 const float *pos, const float *h, int32_t n, int32_t K, const void *state,
-                                size_t state_bytes, const float *grad_out, float *grad_h, float *grad_pos,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream)
+                                size_t state_bytes, const e2v2_rebuild_policy *policy, const float *grad_out,
+                                float *grad_h, float *grad_pos, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream)
 {
     e2v2_status st = check_stack(n_layers, descs, weights, n, K);
     if (st != E2V2_OK) return st;
     if (descs[0].storage != E2V2_FP32) return fail(E2V2_ERR_UNSUPPORTED, "the stack gradient needs fp32 storage");
     if (!weights) return fail(E2V2_ERR_ARG, "weights is NULL");
+    // the state holds lists only once a forward call has built them
+    if (!policy) return fail(E2V2_ERR_ARG, "policy is NULL");
+    if (policy->rebuilds < 1 || policy->steps_since_rebuild < 1)
+        return fail(E2V2_ERR_ARG, "no e2v2_stack_forward call has filled the state (policy shows no rebuild)");
     if (n == 0) return E2V2_OK;
     for (const void *p : {(const void *)pos, (const void *)h, state, (const void *)grad_out, (const void *)grad_h,
                           (const void *)workspace}) {

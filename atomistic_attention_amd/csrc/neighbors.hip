@@ -56,7 +56,7 @@ struct NbrLayout {
     float4 *spos;          // [n] positions in cell order, w = atom id bits
     int64_t *nnz;
     uint32_t *mkey[2];     // [n] Morton keys in / sorted (launch_morton_order)
-    int32_t *mval;         // [n] atom ids 0 .. n-1
+    int32_t *mval;         // [n] atom ids 0 .. n-1; before that, the atomic slots of the cell scatter
     void *sort_tmp;        // radix-sort scratch
     size_t sort_bytes;
     size_t bytes;
@@ -283,12 +283,29 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, c
 }
 
 // ---------------------------------------------------------------- step 3
-__global__ void k_scatter(const float *__restrict__ pos, int n, const int32_t *__restrict__ cell_of,
-                          int32_t *cell_cur, int32_t *order, float4 *spos, int32_t *order_out)
+// Two passes, so the order within a cell does not depend on the timing of atomics:
+// k_scatter drops every atom into its cell's range at an atomic slot (scratch),
+// then k_place puts it at its rank by atom index within that range.  The cells'
+// order is row-major (z, y, x), and within a cell atoms ascend: the same order
+// on every call.  A cell of k atoms costs k reads per atom.
+__global__ void k_scatter(int n, const int32_t *__restrict__ cell_of, int32_t *cell_cur, int32_t *tmp)
 {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const int slot = atomicAdd(&cell_cur[cell_of[i]], 1);
+    tmp[slot] = (int32_t)i;
+}
+__global__ void k_place(const float *__restrict__ pos, int n, const int32_t *__restrict__ cell_of,
+                        const int32_t *__restrict__ cell_start, const int32_t *__restrict__ tmp, int32_t *order,
+                        float4 *spos, int32_t *order_out)
+{
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int c = cell_of[i];
+    const int cs = cell_start[c], ce = cell_start[c + 1];
+    int rank = 0;
+    for (int t = cs; t < ce; ++t) rank += tmp[t] < (int32_t)i;
+    const int slot = cs + rank;
     order[slot] = (int32_t)i;
     if (order_out) order_out[slot] = (int32_t)i;
     spos[slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float((int)i));
@@ -956,7 +973,8 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
     k_bbox<<<1, 256, 0, stream>>>(L.box_part, nparts, cutoff, maxc, L.grid);
     k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt);
     k_scan<<<1, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, 0, L.cell_start, L.cell_cur, nullptr);
-    k_scatter<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_cur, L.order, L.spos, order_out);
+    k_scatter<<<nblk(n, 256), 256, 0, stream>>>(n, L.cell_of, L.cell_cur, L.mval);
+    k_place<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_start, L.mval, L.order, L.spos, order_out);
     if (K == 0) {
         const double rc2 = (double)cutoff * (double)cutoff;
         k_count_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(n, cutoff, rc2, L.grid, L.cell_start,

@@ -134,8 +134,9 @@ typedef struct {
  *   nnz_host     host, may be NULL for K > 0; required for K == 0
  *   order        device [n] int32 or NULL: receives the atoms in cell-list order
  *                (a permutation of 0..n-1 in which consecutive atoms are spatial
- *                neighbours); pass it as target_order to e2v2_attn_forward.  The
- *                order within a cell may differ between calls.
+ *                neighbours); pass it as target_order to e2v2_attn_forward.  Cells
+ *                come in row-major (z, y, x) order and atoms ascend within a cell,
+ *                so the order is the same on every call with the same positions.
  *   workspace    device scratch of at least
  *                e2v2_build_neighbors_workspace_bytes(n, max_neighbors) bytes
  * Limits: 0 <= n < 2^31 - 1, cutoff > 0 finite, 0 <= K <= 4096, total entries
@@ -170,8 +171,11 @@ e2v2_status e2v2_eaas_couple(const float *pos, const void *x, e2v2_dtype x_dtype
  * no neighbours gets m = 0 and therefore out = 0.
  *   target_order  device [n] int32 or NULL: the order in which targets are
  *        processed (a permutation of 0..n-1, e.g. the order written by
- *        e2v2_build_neighbors).  Results do not depend on it; a spatially
- *        coherent order lets neighbouring targets share cached neighbour rows.
+ *        e2v2_build_neighbors).  With fp32 storage results do not depend
+ *        on it.  With bf16 storage it decides which two targets share a wave
+ *        and so the summation order, which can move the fp16-stored message by
+ *        a rounding step; a given order always gives bit-identical results.  A
+ *        spatially coherent order lets neighbouring targets share cached rows.
  *        Entries outside [0, n) are skipped.
  *   h    device [n][(lmax+1)^2][C] storage dtype
  *   out  device [n][(lmax+1)^2][C] fp32
@@ -357,14 +361,18 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
  * those in `state` (left by that forward call), held fixed; each layer's input is
  * recomputed over them, then each layer's gradient (e2v2_layer_backward, over its
  * transposed list) runs in reverse order.  Arguments as for e2v2_stack_forward;
- * every layer must have fp32 storage (E2V2_ERR_UNSUPPORTED otherwise).  Workspace:
- * e2v2_stack_backward_workspace_bytes.  Asynchronous on `stream`. */
+ * every layer must have fp32 storage (E2V2_ERR_UNSUPPORTED otherwise).  `policy`
+ * is the host policy that forward call updated: with no rebuild recorded
+ * (rebuilds < 1) the state holds no lists yet, and the call returns E2V2_ERR_ARG
+ * before anything is enqueued.  Workspace: e2v2_stack_backward_workspace_bytes
+ * (one transposed list per distinct cutoff).  Asynchronous on `stream`. */
 size_t e2v2_stack_backward_workspace_bytes(int32_t n_layers, const e2v2_layer_desc *descs, int32_t n,
                                            int32_t max_neighbors);
 e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, const e2v2_weights *weights,
                                 const float *pos, const float *h, int32_t n, int32_t max_neighbors,
-                                const void *state, size_t state_bytes, const float *grad_out, float *grad_h,
-                                float *grad_pos, void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                const void *state, size_t state_bytes, const e2v2_rebuild_policy *policy,
+                                const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Host-side tables (no GPU needed). */

@@ -42,6 +42,18 @@ def bf16_close(got, ref, rms_floor=1e-5) -> bool:
     return bool(np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + rms_floor * rms))
 
 
+def fp16_close(got, ref, rms_floor=1e-5) -> bool:
+    """Element-wise bound for one round-to-nearest fp16 store (under a power-of-two
+    scale, which is exact) of an fp32 result: |got - ref| <= 2^-11 |ref| (half an
+    ulp of an 11-bit significand) plus a small absolute floor, relative to the RMS,
+    for the fp32 arithmetic before the store and for values in fp16's subnormal
+    range below the node's scale."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return bool(np.all(np.abs(got - ref) <= 2.0 ** -11 * np.abs(ref) + rms_floor * rms))
+
+
 def record(test: str, **vals):
     """Append measured parity numbers to $E2V2_PARITY_LOG (JSON lines), if set."""
     import json

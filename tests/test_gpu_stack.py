@@ -148,3 +148,88 @@ def test_stack_gradient_matches_oracle(gpu_lib, K):
     eh, ep = rel_err(gh.cpu().numpy(), rh), rel_err(gp.cpu().numpy(), rp)
     record(f"stack_gradient[s1,K={K}]", grad_h=eh, grad_pos=ep)
     assert eh < 1e-4 and ep < 1e-4, (eh, ep)
+
+
+def _far_pairs(pos, rows, cutoff):
+    """Listed pairs at or beyond ``cutoff`` (fp64 distances of the fp32 positions)."""
+    n = 0
+    for i, r in enumerate(rows):
+        r = np.asarray(r, dtype=np.int64)
+        r = r[(r >= 0) & (r < pos.shape[0])]
+        if r.size:
+            n += int(np.sum(np.linalg.norm(pos[r] - pos[i], axis=1) >= cutoff))
+    return n
+
+
+def _moving_stack(steps):
+    """s1 (256 atoms, fp32) with 24 atoms moved by 0.2 A at step 2: below the 0.25 A
+    rebuild threshold, so the lists built at step 0 are kept while listed pairs of
+    the moved atoms cross 5 A and 8 A."""
+    rng = np.random.default_rng(17)
+    dirs = rng.standard_normal((24, 3))
+    dirs = 0.2 * dirs / np.linalg.norm(dirs, axis=1, keepdims=True)
+    jumps = tuple((2, int(a), tuple(v)) for a, v in zip(rng.choice(256, 24, replace=False), dirs))
+    return W.make_stack("s1", steps=steps, jumps=jumps)
+
+
+def test_stack_reused_lists_with_pairs_beyond_the_cutoff(gpu_lib):
+    """Tessera article, neighbour reuse: between rebuilds the lists stay as built and
+    the layers take distances from the current positions, so listed pairs can lie
+    beyond the cutoff.  Their envelope is 0 (FlashSchNet summary section 2.2: the
+    cutoff mask): no distance bias, while q.k still counts.  Every step of the
+    GPU stack matches the oracle's within 1e-4 of the output RMS."""
+    st = _moving_stack(8)
+    outs, rebuilt = _run_gpu(gpu_lib, st)
+    state = OS.StackState([wl.cfg.cutoff for wl in st.layers], st.cfg.max_neighbors)
+    far, errs = 0, []
+    for t, p in enumerate(st.traj):
+        ref = OS.stack_step(state, p, st.h0, st.layers, t, "fp32")
+        if t not in state.rebuilds:
+            far += sum(_far_pairs(p, rows, c) for c, rows in state.rows.items())
+        errs.append(rel_err(outs[t], ref))
+    assert rebuilt == state.rebuilds == [0]
+    assert far >= 10, far
+    record("stack_far_pairs[s1]", worst=max(errs), far_pairs=far)
+    assert max(errs) < 1e-4, errs
+
+
+def test_stack_gradient_on_reused_lists(gpu_lib):
+    """dL/dh and dL/dpos of the four-layer stack after forward steps that reused
+    the step-0 lists while atoms moved (pairs beyond 5 A and 8 A among them),
+    against the oracle's reverse mode over the rebuild-time lists at the current
+    positions."""
+    from oracle import backward as OB
+    st = _moving_stack(4)
+    descs, weights = [], []
+    for wl in st.layers:
+        c = wl.cfg
+        descs.append(gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32))
+        weights.append(W.device_arrays(wl)["weights"])
+    run = gpu_lib.StackRun(descs, weights, st.cfg.n, st.cfg.max_neighbors)
+    h = f32(st.h0)
+    for p in st.traj:
+        run.e2v2_stack_forward(f32(p), h)
+    torch.cuda.synchronize()
+    assert run.policy.rebuilds == 1
+    pos = st.traj[-1]
+    g = np.random.default_rng(33).standard_normal(st.h0.shape).astype(np.float32).astype(np.float64)
+    gh, gp = run.e2v2_stack_backward(f32(pos), h, f32(g), grad_pos=torch.empty((st.cfg.n, 3), device="cuda"))
+    torch.cuda.synchronize()
+    state = OS.StackState([wl.cfg.cutoff for wl in st.layers], st.cfg.max_neighbors)
+    state.rebuild(st.traj[0], 0)
+    assert sum(_far_pairs(pos, rows, c) for c, rows in state.rows.items()) >= 10
+    rp, rh = OB.stack_grad_pos_h(pos, st.h0, st.layers, state.rows, g)
+    eh, ep = rel_err(gh.cpu().numpy(), rh), rel_err(gp.cpu().numpy(), rp)
+    record("stack_gradient_reused[s1]", grad_h=eh, grad_pos=ep)
+    assert eh < 1e-4 and ep < 1e-4, (eh, ep)
+
+
+def test_stack_backward_before_forward_raises(gpu_lib):
+    """The state holds no lists before the first forward call: the gradient call
+    raises before anything is launched."""
+    st = W.make_stack("s1", steps=1)
+    descs = [gpu_lib.make_desc(wl.cfg.lmax, wl.cfg.channels, wl.cfg.heads, wl.cfg.n_rbf, wl.cfg.cutoff, torch.float32)
+             for wl in st.layers]
+    run = gpu_lib.StackRun(descs, [W.device_arrays(wl)["weights"] for wl in st.layers], st.cfg.n, st.cfg.max_neighbors)
+    with pytest.raises(gpu_lib.E2V2Error):
+        run.e2v2_stack_backward(f32(st.traj[0]), f32(st.h0), f32(np.zeros(st.h0.shape)))

@@ -252,12 +252,33 @@ def test_backward_argument_errors_and_workspace(lib):
 def test_stack_backward_argument_errors(lib):
     descs = (B.LayerDesc * 2)(_desc(), _desc())                        # bf16 storage
     w = (B.Weights * 2)(B.Weights(*([FAKE] * 7)), B.Weights(*([FAKE] * 7)))
-    st = lib.e2v2_stack_backward(2, descs, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    pol = ctypes.byref(B.RebuildPolicy(10, 0.25, 1, 1, 1))            # as left by one forward call
+    st = lib.e2v2_stack_backward(2, descs, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, pol, FAKE, FAKE, None, FAKE, 1 << 30,
+                                 None)
     assert st == B.E2V2_ERR_UNSUPPORTED
     d32 = (B.LayerDesc * 2)(_desc(storage=B.E2V2_FP32), _desc(storage=B.E2V2_FP32, cutoff=8.0))
-    st = lib.e2v2_stack_backward(2, d32, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, FAKE, FAKE, FAKE_MIS, FAKE, 1 << 30, None)
+    st = lib.e2v2_stack_backward(2, d32, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, pol, FAKE, FAKE, FAKE_MIS, FAKE,
+                                 1 << 30, None)
     assert st == B.E2V2_ERR_ARG
-    st = lib.e2v2_stack_backward(2, d32, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, FAKE, FAKE, None, FAKE, 100, None)
+    st = lib.e2v2_stack_backward(2, d32, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, pol, FAKE, FAKE, None, FAKE, 100, None)
     assert st == B.E2V2_ERR_ARG and "workspace" in lib.e2v2_last_error().decode()
+    # no forward call yet: the state holds no lists, so nothing may run
+    for fresh in (B.RebuildPolicy(10, 0.25, -1, 0, 0), None):
+        st = lib.e2v2_stack_backward(2, d32, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20,
+                                     ctypes.byref(fresh) if fresh else None, FAKE, FAKE, None, FAKE, 1 << 30, None)
+        assert st == B.E2V2_ERR_ARG
+    assert "e2v2_stack_forward" in lib.e2v2_last_error().decode() or "policy" in lib.e2v2_last_error().decode()
     assert lib.e2v2_stack_backward_workspace_bytes(2, d32, 1000, 8) > lib.e2v2_layer_backward_workspace_bytes(
         ctypes.byref(d32[0]), 1000, 8000)
+
+
+def test_stack_backward_workspace_has_one_transposed_list_per_cutoff(lib):
+    """Layers 5, 5, 5, 8 A share two distinct lists: the gradient's workspace holds
+    two transposed lists, not four (4 bytes per entry of an n x K list each)."""
+    f = B.E2V2_FP32
+    four = (B.LayerDesc * 4)(*[_desc(storage=f, cutoff=c) for c in (5.0, 5.0, 5.0, 8.0)])
+    two = (B.LayerDesc * 4)(*[_desc(storage=f, cutoff=c) for c in (5.0, 6.0, 7.0, 8.0)])
+    n, K = 4096, 256
+    a = lib.e2v2_stack_backward_workspace_bytes(4, four, n, K)
+    b = lib.e2v2_stack_backward_workspace_bytes(4, two, n, K)
+    assert b - a >= 2 * n * K * 4 and b - a <= 2 * (n * K * 4 + 5 * (n + 1) * 4 + 5 * 256)
