@@ -32,12 +32,11 @@
 //     channels, and the lane writes its channels of the normalised message m_i,
 //     which the output-projection kernel couples.
 // Value rows are read as 16-byte pieces (4 channels of two interleaved fp16
-// components); the 2H lanes of a slot cover a contiguous stretch of the
-// neighbour's row.  The key arrives in fp16
-// together with an odd last component of h' (one 16-byte piece per pair), and a
-// neighbour's h' and k share one power-of-two scale (pos4[j].w): it is folded into
-// the softmax weight of the pair, so each value element costs one mixed-precision
-// FMA, and it multiplies the pair's dot product.
+// components, plus an 8-byte piece of an odd last component); the 2H lanes of a
+// slot cover a contiguous stretch of the neighbour's row.  The key arrives in fp32
+// (16 bytes per lane), so the logits carry no 16-bit rounding, and a neighbour's
+// h' carries one power-of-two scale (pos4[j].w): it is folded into the softmax
+// weight of the pair, so each value element costs one mixed-precision FMA.
 #include "attn_common.h"
 
 namespace e2v2 {
@@ -114,7 +113,7 @@ void attn_kernel(const AttnArgs A)
     for (int c0 = 0; c0 < len; c0 += 16) {
         // ---- (a) this lane's S neighbours of the chunk and their row scales
         int js[S];
-        float scl[S];                  // the neighbours' h' and k scale (16-bit storage)
+        float scl[S];                  // the neighbours' h' scale (16-bit storage)
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int p = u * S + s;
@@ -122,15 +121,12 @@ void attn_kernel(const AttnArgs A)
             js[s] = (j >= 0 && j < n) ? j : -1;
             scl[s] = __shfl(pj.w, p, 64);
         }
-        // ---- (b) issue every key row and the first phase of value rows
+        // ---- (b) issue every key row (fp32) and the first phase of value rows
         float4 kv[S];
-        uint2 tl[S];                   // h' component NC - 1, from the key + tail group
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const size_t node = (size_t)(js[s] >= 0 ? js[s] : i);
-            const uint4 g4 = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(A.k) + node * (2 * C) + 2 * cb);
-            kv[s] = make_float4(f16_of(g4.x, 0), f16_of(g4.x, 1), f16_of(g4.y, 0), f16_of(g4.y, 1));
-            tl[s] = make_uint2(g4.z, g4.w);
+            kv[s] = *reinterpret_cast<const float4 *>(A.k + node * C + cb);
         }
         HpStep<true, NC> hv[SP];
 #pragma unroll
@@ -192,7 +188,6 @@ void attn_kernel(const AttnArgs A)
             qk = fmaf(qv.z, kv[s].z, qk);
             qk = fmaf(qv.w, kv[s].w, qk);
             qk += __shfl_xor(qk, H, 64);
-            qk *= scl[s];
             sl[s] = js[s] >= 0 ? fmaf(qk, qscale, bs[s]) : -INFINITY;
         }
         // The reference maximum mu moves only when a logit exceeds it by more than 8
@@ -238,15 +233,7 @@ void attn_kernel(const AttnArgs A)
                 for (int c = 0; c < 4; ++c) {
                     float a = acc[e][c];
 #pragma unroll
-                    for (int s = 0; s < SP; ++s) {
-                        float x;
-                        if constexpr ((NC & 1) != 0)
-                            x = e == NC - 1 ? f16_of(c < 2 ? tl[ph * SP + s].x : tl[ph * SP + s].y, c & 1)
-                                            : hv[s].get(e, c);
-                        else
-                            x = hv[s].get(e, c);
-                        a = fmaf(ps[ph * SP + s], x, a);
-                    }
+                    for (int s = 0; s < SP; ++s) a = fmaf(ps[ph * SP + s], hv[s].get(e, c), a);
                     acc[e][c] = a;
                 }
         }

@@ -11,30 +11,37 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // One neighbour's value pieces for this lane's 4 channels.  16-bit h' is stored with
 // components interleaved in pairs (hp_f16_offset): one 16-byte load covers 4
 // channels of two components -- half the load instructions of a per-component
-// layout -- and an odd last component travels with the key (hp_pair_row).
+// layout -- and an odd last component is one more 8-byte load (hp_row16).
 template <bool HB, int NC> struct HpStep;
 template <int NC> struct HpStep<true, NC> {
     static constexpr int NPR = NC / 2;
+    static constexpr bool ODD = (NC & 1) != 0;
     uint4 pr[NPR > 0 ? NPR : 1];
+    uint2 tl;                                    // the odd last component (odd NC)
     __device__ __forceinline__ void load(const void *base, int node, int cb, int C)
     {
-        const uint16_t *nb = reinterpret_cast<const uint16_t *>(base) + (size_t)node * hp_pair_row(NC, C);
+        const uint16_t *nb = reinterpret_cast<const uint16_t *>(base) + (size_t)node * hp_row16(NC, C);
 #pragma unroll
         for (int p = 0; p < NPR; ++p) pr[p] = *reinterpret_cast<const uint4 *>(nb + p * 2 * C + (cb >> 2) * 8);
+        if constexpr (ODD) tl = *reinterpret_cast<const uint2 *>(nb + (NC - 1) * C + cb);
     }
     // The same row addressed by a 32-bit byte offset from base (row * row bytes
     // must stay below 2^32): one scalar base plus one 32-bit offset per load.
     __device__ __forceinline__ void load32(const void *base, uint32_t row, int cb, int C)
     {
-        const unsigned char *nb = reinterpret_cast<const unsigned char *>(base) +
-                                  (row * uint32_t(2 * hp_pair_row(NC, C)) + uint32_t(cb >> 2) * 16u);
+        const unsigned char *rb = reinterpret_cast<const unsigned char *>(base) + row * uint32_t(2 * hp_row16(NC, C));
+        const unsigned char *nb = rb + uint32_t(cb >> 2) * 16u;
 #pragma unroll
         for (int p = 0; p < NPR; ++p) pr[p] = *reinterpret_cast<const uint4 *>(nb + p * 4 * C);
+        if constexpr (ODD) tl = *reinterpret_cast<const uint2 *>(rb + uint32_t(2 * (NC - 1) * C + 2 * cb));
     }
-    // component e < 2 NPR, channel c of the lane's 4 (the odd last component
-    // comes with the key, see tail())
+    // component e, channel c of the lane's 4
     __device__ __forceinline__ float get(int e, int c) const
     {
+        if (ODD && e == NC - 1) {
+            const uint32_t w = c < 2 ? tl.x : tl.y;
+            return (float)__builtin_bit_cast(_Float16, uint16_t((c & 1) ? (w >> 16) : (w & 0xffffu)));
+        }
         const uint4 &v = pr[e >> 1];
         const int k = (e & 1) * 2 + (c >> 1);
         const uint32_t w = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
@@ -42,7 +49,7 @@ template <int NC> struct HpStep<true, NC> {
         return (float)__builtin_bit_cast(_Float16, b);
     }
 };
-// fp16 halves of a key + tail group
+// fp16 halves of a 32-bit word
 __device__ __forceinline__ float f16_of(uint32_t w, int hi)
 {
     return (float)__builtin_bit_cast(_Float16, uint16_t(hi ? (w >> 16) : (w & 0xffffu)));

@@ -158,12 +158,11 @@ __device__ __forceinline__ void pair_lds_sync()
 }  // namespace
 
 // Entry codes need n < 2^29, and rows are addressed by 32-bit byte offsets: n times
-// the longest row (h' pairs 2 (NC & ~1) C bytes, key + tail 4 C, position 16) stays
-// below 2^32.
+// the longest row (h' 2 NC C bytes, k 4 C, position 16) stays below 2^32.
 long long attn_pair_max_atoms(int L, int C)
 {
     const long long nc = (long long)(L + 1) * (L + 1);
-    long long row = 2 * (nc & ~1LL) * C;
+    long long row = 2 * nc * C;
     if (row < 4LL * C) row = 4LL * C;
     if (row < 16) row = 16;
     const long long lim = (1LL << 32) / row;
@@ -392,12 +391,12 @@ void attn_pair_kernel(const AttnArgs A)
             fb[r] = e >= 0 && (e & 1) != 0;
             scl[r] = sS[wv][u * S + s0o + r];
         }
-        // ---- (b) every key + tail row and the first phase of value rows
-        uint4 g4[S];
+        // ---- (b) every key row (fp32) and the first phase of value rows
+        float4 kf[S];
 #pragma unroll
         for (int s = 0; s < S; ++s)
-            g4[s] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const unsigned char *>(A.k) +
-                                                     (rw[s] * uint32_t(4 * C) + uint32_t(4 * cb)));
+            kf[s] = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(A.k) +
+                                                      (rw[s] * uint32_t(4 * C) + uint32_t(4 * cb)));
         HpStep<true, NC> hv[2][SP];       // value rows, double-buffered across phases
 #pragma unroll
         for (int s = 0; s < SP; ++s) hv[0][s].load32(A.hp, rw[s], cb, C);
@@ -416,10 +415,10 @@ void attn_pair_kernel(const AttnArgs A)
             float x[S];                         // this half's 4-channel part of q . k
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                float qk = fmaf(qv.x, f16_of(g4[s].x, 0), 0.f);   // one v_fma_mix each
-                qk = fmaf(qv.y, f16_of(g4[s].x, 1), qk);
-                qk = fmaf(qv.z, f16_of(g4[s].y, 0), qk);
-                x[s] = fmaf(qv.w, f16_of(g4[s].y, 1), qk);
+                float qk = qv.x * kf[s].x;
+                qk = fmaf(qv.y, kf[s].y, qk);
+                qk = fmaf(qv.z, kf[s].z, qk);
+                x[s] = fmaf(qv.w, kf[s].w, qk);
             }
             if constexpr (ROWHALF) {
                 // Half 0 takes entry r's full dot product and half 1 entry 4 + r's;
@@ -428,7 +427,7 @@ void attn_pair_kernel(const AttnArgs A)
                 for (int r = 0; r < 4; ++r) {
                     float lo = x[r], hi = x[4 + r];
                     row_swap(lo, hi);
-                    sl[r] = f[r] ? fmaf((lo + hi) * scl[r], qscale, bias[r]) : -INFINITY;
+                    sl[r] = f[r] ? fmaf(lo + hi, qscale, bias[r]) : -INFINITY;
                 }
             } else {
                 float bs[S];
@@ -436,7 +435,7 @@ void attn_pair_kernel(const AttnArgs A)
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
                     const float qk = x[s] + __shfl_xor(x[s], H, 64);
-                    sl[s] = f[s] ? fmaf(qk * scl[s], qscale, bs[s]) : -INFINITY;
+                    sl[s] = f[s] ? fmaf(qk, qscale, bs[s]) : -INFINITY;
                 }
             }
         };
@@ -480,15 +479,7 @@ void attn_pair_kernel(const AttnArgs A)
                     for (int c = 0; c < 4; ++c) {
                         float a = acc[e][c];
 #pragma unroll
-                        for (int s = 0; s < SP; ++s) {
-                            const uint4 &t4 = g4[ph * SP + s];
-                            float x;
-                            if constexpr (NC & 1)
-                                x = e == NC - 1 ? f16_of(c < 2 ? t4.z : t4.w, c & 1) : hv[ph & 1][s].get(e, c);
-                            else
-                                x = hv[ph & 1][s].get(e, c);
-                            a = fmaf(p[ph * SP + s], x, a);
-                        }
+                        for (int s = 0; s < SP; ++s) a = fmaf(p[ph * SP + s], hv[ph & 1][s].get(e, c), a);
                         acc[e][c] = a;
                     }
             };

@@ -11,9 +11,9 @@
 // rotate out) runs in registers on the accumulators, with the node's Wigner-D
 // blocks (built beforehand in fp64 by k_node_frames) and the path weights staged
 // in LDS.
-// v never reaches HBM: the only outputs are q, the key + tail rows (k in fp16
-// with h's last component when the count is odd), the component pairs of h' (fp16
-// with a per-node power-of-two scale, interleaved), the D blocks and pos4.
+// v never reaches HBM: the only outputs are q and k (fp32), h' (fp16 with a
+// per-node power-of-two scale, components interleaved in pairs), the D blocks
+// and pos4.
 #include "e2v2_internal.h"
 
 namespace e2v2 {
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
     __shared__ __align__(16) unsigned char sH[16 * ROW];
     __shared__ float sD[16 * ND];
     __shared__ float sW[C * WS];
-    __shared__ unsigned sMax[NB][16], sMaxK[NB][16];
+    __shared__ unsigned sMax[NB][16];
 
     const int t = threadIdx.x, lane = t & 63, nb = t >> 6, g = lane >> 4, nl = lane & 15;
     const long long node0 = (long long)blockIdx.x * 16;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
     const long long node = node0 + nl;
     const bool valid = nl < nvalid;
     const int c0 = 16 * nb + 4 * g;
-    floatx4 acc[NC], kacc;
+    floatx4 acc[NC];
     bf16x8 wnext[KB];
     if constexpr (L >= 1) {
 #pragma unroll
@@ -151,9 +151,9 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
             ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wk[kb], b, ak, 0, 0, 0);
         }
         acc[0] = av;
-        kacc = ak;
         if (valid) {
             *reinterpret_cast<float4 *>(a.q + node * C + c0) = make_float4(aq[0], aq[1], aq[2], aq[3]);
+            *reinterpret_cast<float4 *>(a.k + node * C + c0) = make_float4(ak[0], ak[1], ak[2], ak[3]);
             if (a.k_tap)
                 *reinterpret_cast<float4 *>(a.k_tap + node * C + c0) = make_float4(ak[0], ak[1], ak[2], ak[3]);
         }
@@ -193,35 +193,21 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
 
     // Per-node scale: largest |h'| over all components and channels.  Magnitude
     // bit patterns order like the values; NaN sorts above inf and selects scale 1.
-    // ... and of |k| over the node's channels.
-    unsigned mb = 0u, mk = 0u;
+    unsigned mb = 0u;
 #pragma unroll
     for (int e = 0; e < NC; ++e)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mb = max(mb, __float_as_uint(acc[e][i]) & 0x7fffffffu);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mk = max(mk, __float_as_uint(kacc[i]) & 0x7fffffffu);
     mb = max(mb, (unsigned)__shfl_xor((int)mb, 16));
     mb = max(mb, (unsigned)__shfl_xor((int)mb, 32));
-    mk = max(mk, (unsigned)__shfl_xor((int)mk, 16));
-    mk = max(mk, (unsigned)__shfl_xor((int)mk, 32));
-    if (g == 0) {
-        sMax[nb][nl] = mb;
-        sMaxK[nb][nl] = mk;
-    }
+    if (g == 0) sMax[nb][nl] = mb;
     __syncthreads();
     mb = 0u;
-    mk = 0u;
 #pragma unroll
-    for (int w = 0; w < NB; ++w) {
-        mb = max(mb, sMax[w][nl]);
-        mk = max(mk, sMaxK[w][nl]);
-    }
-    // One power-of-two scale s per node for h' and k, with the larger of their
-    // largest magnitudes M below 2^14 s: no element overflows fp16 and every
-    // element within 2^28 of M stays a normal fp16 number; scale 1 for zero or
-    // non-finite rows.
-    mb = max(mb, mk);
+    for (int w = 0; w < NB; ++w) mb = max(mb, sMax[w][nl]);
+    // One power-of-two scale s per node for h', with its largest magnitude M below
+    // 2^14 s: no element overflows fp16 and every element within 2^28 of M stays a
+    // normal fp16 number; scale 1 for zero or non-finite rows.
     unsigned sb = 127u;
     if (mb != 0u && mb < 0x7f800000u) {
         const unsigned b = mb >> 23;                      // M < 2^(b-126); s = 2^(b-140)
@@ -229,10 +215,7 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
     }
     const float sc = __uint_as_float(sb << 23), inv = __uint_as_float((254u - sb) << 23);
     if (!valid) return;
-    // key half of the node's key + tail group c0 / 4 (k / s in fp16)
-    *reinterpret_cast<uint2 *>(a.kt + node * (2 * C) + 2 * c0) =
-        make_uint2(pack_f16x2(kacc[0] * inv, kacc[1] * inv), pack_f16x2(kacc[2] * inv, kacc[3] * inv));
-    uint16_t *hp = a.hp + node * hp_pair_row(NC, C);
+    uint16_t *hp = a.hp + node * hp_row16(NC, C);
 #pragma unroll
     for (int j = 0; j < NC / 2; ++j) {
         const floatx4 y0 = acc[2 * j], y1 = acc[2 * j + 1];
@@ -250,13 +233,11 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
     if constexpr ((NC & 1) != 0) {
         const floatx4 y0 = acc[NC - 1];
         const uint2 o = make_uint2(pack_f16x2(y0[0] * inv, y0[1] * inv), pack_f16x2(y0[2] * inv, y0[3] * inv));
-        *reinterpret_cast<uint2 *>(a.kt + node * (2 * C) + 2 * c0 + 4) = o;   // tail half of the group
+        *reinterpret_cast<uint2 *>(hp + hp_f16_offset(NC - 1, c0, NC, C)) = o;   // 4 channels of the last component
         if (a.hp_tap)
             *reinterpret_cast<float4 *>(a.hp_tap + (node * NC + NC - 1) * C + c0) =
                 make_float4(f16lo(o.x) * sc, f16hi(o.x) * sc, f16lo(o.y) * sc, f16hi(o.y) * sc);
     }
-    if constexpr ((NC & 1) == 0)
-        *reinterpret_cast<uint2 *>(a.kt + node * (2 * C) + 2 * c0 + 4) = make_uint2(0u, 0u);
     if (nb == 0 && g == 0)
         a.pos4[node] = make_float4(a.pos[3 * node], a.pos[3 * node + 1], a.pos[3 * node + 2], sc);
 }

@@ -68,10 +68,10 @@ typedef struct {
     int32_t n_rbf;
     float cutoff;        /* Angstrom; also the RBF range and the envelope's zero */
     int32_t storage;     /* e2v2_dtype of h, W_Q, W_K, W_V and W_O.  The intermediates
-                            k, h' and the aggregated message m are kept in the
-                            workspace as fp32 (fp32 storage) or, for bf16 storage, as
-                            fp16 under one power-of-two scale per node; arithmetic is
-                            fp32 throughout */
+                            q and k are fp32; h' and the aggregated message m are
+                            fp32 (fp32 storage) or, for bf16 storage, fp16 under one
+                            power-of-two scale per node; arithmetic is fp32
+                            throughout */
 } e2v2_layer_desc;
 
 /* Layer weights (device pointers).
@@ -96,7 +96,7 @@ typedef struct {
  * and 6 run as one kernel on whole nodes. */
 typedef struct {
     float *q;        /* [n][C] fp32                                         */
-    float *k;        /* [n][C] fp32 (for bf16 storage: k before its fp16 storage) */
+    float *k;        /* [n][C] fp32 */
     float *v;        /* [n][(lmax+1)^2][C] fp32                             */
     float *hprime;   /* [n][(lmax+1)^2][C] fp32: h' as the streaming kernel reads it
                         (for bf16 storage: its 16-bit form times the node's scale) */

@@ -126,10 +126,9 @@ def test_workspace_sizes(lib):
     d = _desc()
     a, b = lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 1000), lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 2000)
     assert 0 < a < b
-    # bf16 storage: q fp32, k + last h' component (16 bytes per 4 channels), the
-    # other h' components as fp16 pairs, D blocks, padded positions, the message m
+    # bf16 storage: q and k fp32, h' in fp16, D blocks, padded positions, the message m
     # in fp16 and its node scale (v is projected and coupled in registers, never stored)
-    per_node = 128 * 4 + 128 * 4 + 8 * 128 * 2 + 34 * 4 + 16 + 9 * 128 * 2 + 4
+    per_node = 128 * 4 + 128 * 4 + 9 * 128 * 2 + 34 * 4 + 16 + 9 * 128 * 2 + 4
     assert abs((b - a) / 1000 - per_node) < 2
     # fp32 storage adds v and stores h' in fp32
     d32 = _desc(storage=B.E2V2_FP32)
