@@ -160,6 +160,25 @@ def _box_side(cfg: LayerConfig) -> float:
     return (cfg.n / mean_density) ** (1.0 / 3.0)
 
 
+def _dense_blocks(rng: np.random.Generator) -> np.ndarray:
+    """Which of the 8^3 blocks are dense: the first draw of the workload's generator."""
+    dense = np.zeros(BLOCKS_PER_DIM ** 3, dtype=bool)
+    dense[rng.permutation(BLOCKS_PER_DIM ** 3)[:DENSE_BLOCKS]] = True
+    return dense
+
+
+def dense_block_mask(wl) -> np.ndarray:
+    """For a block-geometry workload: True for the atoms that lie in a dense block."""
+    cfg = wl.cfg
+    if cfg.geometry != "blocks":
+        return np.zeros(cfg.n, dtype=bool)
+    dense = _dense_blocks(np.random.default_rng(cfg.seed))
+    nb = BLOCKS_PER_DIM
+    side = _box_side(cfg)
+    bi = np.clip(np.floor((np.asarray(wl.pos) + 0.5 * side) / (side / nb)).astype(np.int64), 0, nb - 1)
+    return dense[(bi[:, 0] * nb + bi[:, 1]) * nb + bi[:, 2]]
+
+
 def _positions(cfg: LayerConfig, rng: np.random.Generator, n: int) -> np.ndarray:
     side = _box_side(cfg)
     if cfg.geometry == "uniform":
@@ -168,8 +187,7 @@ def _positions(cfg: LayerConfig, rng: np.random.Generator, n: int) -> np.ndarray
     nb = BLOCKS_PER_DIM
     nblk = nb ** 3
     bside = side / nb
-    dense = np.zeros(nblk, dtype=bool)
-    dense[rng.permutation(nblk)[:DENSE_BLOCKS]] = True
+    dense = _dense_blocks(rng)
     dens = np.where(dense, DENSE_DENSITY, cfg.density)
     expect = dens * bside ** 3
     expect = expect * (n / expect.sum())

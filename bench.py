@@ -9,11 +9,15 @@ coupling, output projection).  The default workload is 32,768 atoms at
 128 channels, 16 heads, 32 RBFs, bf16 storage with fp32 arithmetic.
 
 Prints one JSON line: pairs/s over the whole step (value), steps/s, per-stage
-times, the streaming kernel's achieved algorithmic bandwidth against the HBM
-peak (roofline), and the fp64 CPU oracle timed on a bounded sample of the same
-workload on this host (cpu_baseline).
+times, the streaming kernel against the resource that binds it (roofline: fp32
+ALU on algorithmic flops; beside it the VALU issue share, DRAM and L2-miss bytes
+from committed counter runs, and the algorithmic byte count against the HBM
+peak), records of the other configurations (config.per_config, with the
+clustered system's load balance), and the fp64 CPU oracle timed on a bounded
+sample of the same workload on this host (cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--config c4] [--no-cpu-baseline] [--no-stack]
+                    [--no-backward] [--no-per-config]
 
 config.stack reports the model level: steps/s of the four-layer stack (three 5 A
 layers, one 8 A layer) with neighbour reuse on the same system moving by a random
@@ -36,36 +40,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "atom-neighbour pairs/s & steps/s per attn layer fwd; % HBM peak (1 MI355X)"
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed fp32: two values per lane)
+CLOCK_GHZ = 2.4
+SIMDS = 256 * 4                # 256 CUs x 4 SIMDs
 ATTN_SRCS = [os.path.join(ROOT, "atomistic_attention_amd", "csrc", f)
              for f in ("attn_pair.hip", "attn.hip", "attn_common.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_counters.json")
+PER_CONFIG = ("c1", "c2", "c3", "c3b", "c5")
 
 
-def algorithmic_bytes(cfg, nnz: int) -> dict:
-    """Bytes the streaming kernel must move: per pair the neighbour's coupled value
-    row h'_j and key row k_j, its index and its position -- fp32 rows for fp32
-    storage; for bf16 storage fp16 rows, the key travelling with h's odd last
-    component in 16-byte pieces (4C bytes) next to h's component pairs; per target
-    its query, its position, its row bounds and one output row -- the message m_i
-    in fp16 with its node scale for bf16 storage (the target coupling runs in the
-    output kernel), the coupled fp32 hhat_i for fp32 storage, which also reads the
-    target's D blocks."""
-    C, nc = cfg.channels, cfg.n_comp
-    nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
-    if cfg.storage == "bf16":
-        per_pair = 2 * (nc & ~1) * C + 4 * C + 4 + 12
-    else:
-        per_pair = 4 * nc * C + 4 * C + 4 + 12
-    if cfg.storage == "bf16":
-        per_node = 4 * C + 12 + 8 + 2 * nc * C + 4
-    else:
-        per_node = 4 * C + 12 + 8 + 4 * nc * C + 4 * nd
-    return {"per_pair": per_pair, "per_node": per_node, "total": nnz * per_pair + cfg.n * per_node}
+def algorithmic(cfg, nnz: int) -> dict:
+    """What the streaming step moves and computes by the method's own count, per the
+    survey's measurement section: per (target, neighbour) pair the neighbour's
+    coupled value row h'_j in the storage dtype, its fp32 key row, its index and its
+    position (n_c C s + 4 C + 16 bytes) and 2 (C + R H + n_c C) flops (logit, bias,
+    accumulation); per target its fp32 query and fp32 message plus position and row
+    bounds (4 C + 4 n_c C + 20 bytes).  Rows that nearby targets share are counted
+    once per pair, so this is a gather-byte count: over the launch time it can
+    exceed the HBM peak when the shared rows come from the caches."""
+    C, nc, H, R = cfg.channels, cfg.n_comp, cfg.heads, cfg.n_rbf
+    s = 2 if cfg.storage == "bf16" else 4
+    per_pair = nc * C * s + 4 * C + 16
+    per_node = 4 * C + 4 * nc * C + 20
+    flops_pair = 2 * (C + R * H + nc * C)
+    return {"bytes_per_pair": per_pair, "bytes_per_node": per_node,
+            "bytes": nnz * per_pair + cfg.n * per_node, "flops_per_pair": flops_pair, "flops": nnz * flops_pair}
 
 
 def kernel_hash() -> str:
-    """Hash of the streaming kernels' sources (the stored counters are valid for those sources only)."""
+    """Hash of the streaming kernels' sources (stored counters hold for those sources only)."""
     h = hashlib.sha256()
     for f in ATTN_SRCS:
         h.update(open(f, "rb").read())
@@ -77,40 +81,205 @@ def streaming_kernel(cfg) -> str:
         return "attn_pair_kernel (two neighbouring targets per wave over the union of their lists; emits m_i)"
     if cfg.storage == "bf16":
         return "attn_kernel (one target per wave; emits the message m_i)"
-    return "attn_kernel (one target per wave, + target EAAS)"
+    return "k_attn_f32 (one target per wave, + target EAAS)"
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the streaming kernel from the committed counter runs,
-    if they were taken on the current kernel source; else None."""
+def stored_counters(workload: str):
+    """Hardware counters of the streaming kernel for this workload from the committed
+    rocprofv3 runs (profiles/), if they were taken on the current kernel sources."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
+        rec = json.load(open(COUNTERS_FILE)).get(workload)
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("kernel_sha") != kernel_hash() or rec.get("workload") != workload:
+    if not rec or rec.get("kernel_sha") != kernel_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def roofline(cfg, nnz: int, t_ms: float) -> dict:
+    """The streaming kernel against the resource that binds it.  Its algorithmic
+    bytes exceed the HBM peak over its launch time (shared rows are served by L2
+    and the MALL), and the counters show the SIMDs' instruction issue, not DRAM, as
+    the limit, so the line is the fp32 ALU roofline: algorithmic flops over the
+    measured launch time against the fp32 vector peak.  Next to it: the fraction of
+    the SIMDs' VALU issue slots used (SQ_INSTS_VALU, 4 cycles per wave64
+    instruction), the DRAM bytes (TCC_EA0 request counters) and the L2-miss bytes
+    (FETCH_SIZE + WRITE_SIZE), each calibrated by a 1 GiB copy, and the algorithmic
+    byte count as a fraction of the HBM peak."""
+    a = algorithmic(cfg, nnz)
+    t = t_ms * 1e-3
+    tf = a["flops"] / t / 1e12
+    rec = {"kernel": streaming_kernel(cfg), "bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS,
+           "unit": "TFLOP/s", "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None,
+           "avg_launch_ms": t_ms, "algorithmic_flops_per_launch": a["flops"], "flops_per_pair": a["flops_per_pair"],
+           "algorithmic_bytes_per_launch": a["bytes"], "bytes_per_pair": a["bytes_per_pair"],
+           "bytes_per_target": a["bytes_per_node"],
+           "algorithmic_frac": a["bytes"] / t / (HBM_PEAK_GBS * 1e9),
+           "algorithmic_frac_note": "algorithmic gather bytes per launch / launch time / 8 TB/s: every "
+                                    "(target, neighbour) pair's rows counted, so it exceeds 1 when rows shared by "
+                                    "nearby targets come from L2 and the MALL; not an HBM measurement"}
+    ctr = stored_counters(cfg.name)
+    if ctr:
+        cyc = ctr["launch_ms"] * 1e-3 * CLOCK_GHZ * 1e9
+        rec["traffic"] = ctr["fetch_bytes"] + ctr["write_bytes"]
+        rec["traffic_what"] = ("L2-miss bytes per launch: FETCH_SIZE + WRITE_SIZE calibrated by a 1 GiB copy; "
+                               "reads served by the MALL count too")
+        rec["dram_bytes"] = ctr["dram_read_bytes"] + ctr["dram_write_bytes"]
+        rec["dram_frac"] = rec["dram_bytes"] / (ctr["launch_ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9)
+        rec["valu_issue_frac"] = ctr["valu_insts"] * 4 / (SIMDS * cyc)
+        rec["counters"] = {k: ctr[k] for k in ("kernel_sha", "launch_ms", "valu_insts", "fetch_bytes", "write_bytes",
+                                                 "dram_read_bytes", "dram_write_bytes")}
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, budget_targets: int | None = None) -> dict:
-    """The fp64 oracle on a compact ball of targets around the box centre (all of
-    its steps: brute-force neighbours, projections, dense-CG coupling, explicit
-    softmax, target coupling, output projection)."""
+    """The fp64 oracle on a compact ball of targets around the box centre, every step
+    of it: O1 brute-force neighbours (C, OpenMP), then O2-O8 (projections, dense-CG
+    couplings, explicit softmax, output projection; numpy, its BLAS calls threaded)."""
     from oracle import layer as O
     pos = wl.pos
+    c = wl.cfg
     r = np.linalg.norm(pos, axis=1)
     T = budget_targets or int(os.environ.get("E2V2_CPU_TARGETS", "2500"))
     tg = np.sort(np.argsort(r, kind="stable")[:T])
     t0 = time.perf_counter()
-    res = O.layer_forward_workload(wl, targets=tg)
-    dt = time.perf_counter() - t0
-    pairs = int(sum(x.size for x in res["rows"]))
-    threads = int(os.environ.get("OMP_NUM_THREADS", str(len(os.sched_getaffinity(0)))))
-    return {"value": pairs / dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+    rows = O.neighbors(pos, c.cutoff, c.max_neighbors, targets=tg)
+    t1 = time.perf_counter()
+    res = O.layer_forward_workload(wl, targets=tg, rows=rows)
+    t2 = time.perf_counter()
+    pairs = int(sum(x.size for x in rows))
+    cores = len(os.sched_getaffinity(0))
+    t_layer = t2 - t1
+    return {"value": pairs / t_layer, "unit": "pairs/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{T} targets nearest the box centre of the same workload ({pairs} pairs, "
-                      f"{res['src'].size} coupled sources), whole layer incl. brute-force neighbours; "
-                      f"{dt:.1f} s; the neighbour search uses {threads} OpenMP threads, the numpy "
-                      f"tensor products one thread"}
+                      f"{res['src'].size} coupled sources)",
+            "o1_neighbours_s": t1 - t0, "o2_o8_layer_s": t_layer,
+            "sample_steps_per_s": 1.0 / t_layer,
+            "full_step_s_estimate": t_layer * c.n / T,
+            "threads": f"O1 uses {cores} OpenMP threads; O2-O8 run in numpy with its BLAS threads"}
+
+
+def per_config(B, W, torch, name: str, steps: int = 20) -> dict:
+    """One configuration's layer on its own: the list built once beforehand (in the
+    builder's cell order), then the layer (prepare + aggregate) and its streaming
+    kernel timed with HIP events; nnz, ms, pairs/s, steps/s and the roofline."""
+    wl = W.make_workload(name)
+    c = wl.cfg
+    d = W.device_arrays(wl)
+    dev = d["pos"].device
+    desc = B.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, d["dtype"])
+    order = torch.empty(c.n, dtype=torch.int32, device=dev)
+    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors, order_out=order)
+    aws = torch.empty(B.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
+    out = torch.empty(wl.h.shape, dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for e in ev:
+        e.record()
+    stream = torch.cuda.current_stream()
+    nb_ws = torch.empty(B.load().e2v2_build_neighbors_workspace_bytes(c.n, c.max_neighbors), dtype=torch.uint8,
+                        device=dev)
+    t_layer, t_attn, t_nbr = [], [], []
+    for k in range(steps + 3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        B.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors, workspace=nb_ws, want_nnz=False)
+        e1.record(stream)
+        B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, out=out, workspace=aws,
+                            taps={"events": ev}, target_order=order)
+        torch.cuda.synchronize()
+        if k >= 3:
+            t_nbr.append(e0.elapsed_time(e1))
+            t_layer.append(ev[0].elapsed_time(ev[4]))
+            t_attn.append(ev[2].elapsed_time(ev[3]))
+    ms_layer, ms_attn, ms_nbr = (float(np.median(x)) for x in (t_layer, t_attn, t_nbr))
+    rl = roofline(c, int(nnz), ms_attn)
+    rec = {"workload": f"{name}: {c.n} atoms, {c.geometry} at {c.density} atoms/A^3, cutoff {c.cutoff} A, "
+                       f"K={c.max_neighbors or 'none'}, l_max={c.lmax}, C={c.channels}, {c.heads} heads, "
+                       f"{c.n_rbf} RBFs, {c.storage} storage",
+           "nnz": int(nnz), "steps": steps, "ms_layer": ms_layer, "ms_attention": ms_attn, "ms_neighbours": ms_nbr,
+           "pairs_per_s": nnz / (ms_layer * 1e-3), "steps_per_s": 1e3 / ms_layer,
+           "steps_per_s_with_neighbours": 1e3 / (ms_layer + ms_nbr),
+           "attention_algorithmic_frac": rl["algorithmic_frac"], "attention_alu_frac": rl["frac"],
+           "attention_tflops": rl["achieved"]}
+    for k in ("traffic", "dram_bytes", "dram_frac", "valu_issue_frac"):
+        if k in rl and rl[k] is not None:
+            rec["attention_" + k] = rl[k]
+    if name == "c5":
+        rec["load_balance"] = load_balance(B, W, torch, wl, d, desc, s, ln, ix, order)
+    return rec
+
+
+def xcd_slot_ranges(n: int):
+    """The contiguous runs of processing slots that the pair kernel's XCD-aware
+    workgroup mapping gives each of the 8 XCDs (blocks of 4 waves, 2 targets a wave)."""
+    nb = (n + 7) // 8
+    out, b0 = [], 0
+    for x in range(8):
+        cnt = (nb >> 3) + (1 if x < (nb & 7) else 0)
+        out.append((min(n, 8 * b0), min(n, 8 * (b0 + cnt))))
+        b0 += cnt
+    return out
+
+
+def load_balance(B, W, torch, wl, d, desc, s, ln, ix, order, reps: int = 10) -> dict:
+    """The clustered system's imbalance, two ways.  Static: the share of list entries
+    each XCD's run of processing slots holds (max over mean; the XCDs run their runs
+    side by side).  Measured: the aggregation run on the targets of the dense blocks
+    only and of the sparse blocks only, against all targets, each timed with HIP
+    events; the kept targets go two by two (consecutive in the processing order, as
+    the kernel pairs them) to wave slots spread evenly over the launch, the other
+    slots are -1 and their waves exit at once.  Per-target time and row length show
+    what a dense region costs; the Tessera article reports 13-33 % slower steps for
+    its dense capsid than for its salt solution of similar size."""
+    c = wl.cfg
+    dev = d["pos"].device
+    dense = W.dense_block_mask(wl)
+    o = order.cpu().numpy()
+    lens = ln.cpu().numpy().astype(np.int64)
+    runs = [int(lens[o[a:b]].sum()) for a, b in xcd_slot_ranges(c.n)]
+    dense_runs = [float(dense[o[a:b]].mean()) for a, b in xcd_slot_ranges(c.n)]
+    aws = torch.empty(B.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
+    out = torch.empty(wl.h.shape, dtype=torch.float32, device=dev)
+    B.e2v2_attn_prepare(desc, d["pos"], d["h"], d["weights"], aws)
+    res = {"xcd_entries": runs, "xcd_dense_fraction": dense_runs,
+           "xcd_max_over_mean": max(runs) / (sum(runs) / len(runs))}
+    for key, sel in (("all", np.ones(c.n, bool)), ("dense", dense), ("sparse", ~dense)):
+        kept = o[sel[o]].astype(np.int32)                     # kept targets in processing order
+        npair_slots, npairs = c.n // 2, (kept.size + 1) // 2
+        oo = np.full(c.n, -1, np.int32)
+        w = (np.arange(npairs, dtype=np.int64) * npair_slots) // npairs
+        oo[2 * w] = kept[0::2]
+        oo[2 * w[: kept.size // 2] + 1] = kept[1::2]
+        ot = torch.from_numpy(oo).to(dev)
+        times = []
+        for k in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.e2v2_attn_aggregate(desc, d["weights"], s, ln, ix, out, aws, target_order=ot)
+            e1.record()
+            torch.cuda.synchronize()
+            if k >= 2:
+                times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        nt = int(sel.sum())
+        res[key] = {"targets": nt, "pairs": int(lens[sel].sum()), "mean_row": float(lens[sel].mean()),
+                    "ms": ms, "us_per_target": ms * 1e3 / nt, "ns_per_pair": ms * 1e6 / max(int(lens[sel].sum()), 1)}
+    res["dense_vs_sparse_per_target"] = res["dense"]["us_per_target"] / res["sparse"]["us_per_target"]
+    res["what"] = ("aggregation (attention + target coupling + output projection) over the dense blocks' targets "
+                   "only, the sparse blocks' only, and all, with the kept target pairs spread evenly over the "
+                   "wave slots; xcd_entries: list entries in each XCD's run of the processing order")
+    return res
 
 
 def stack_bench(B, W, torch, steps: int = 60, warmup: int = 10) -> dict:
@@ -263,9 +432,10 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the feature-gradient measurement")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only the feature-gradient measurement and print its record (for profiling)")
+    ap.add_argument("--no-per-config", action="store_true", help="skip the records of the other configurations")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="for hardware-counter runs: 3 layer forwards, then 3 plain device copies of 1 GiB "
-                         "(the copies calibrate the counters' byte units); prints no JSON")
+                    help="for hardware-counter runs: 5 layer steps of --config, then 3 plain device copies of "
+                         "1 GiB (the copies calibrate the counters' byte units); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this layer has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -362,46 +532,38 @@ def main():
               flush=True)
         return
 
+    def timed(fn, steps):
+        """HIP events on the main stream around the whole loop of `steps` calls."""
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
     for _ in range(args.warmup):
         step_overlapped()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step_overlapped()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    ms_step = timed(step_overlapped, args.steps)
 
     # Stage times (and the streaming kernel's launch time for the roofline) from the
     # same number of steps run in stage order on one stream, outside the timed region.
+    for _ in range(args.warmup):
+        step()
+    serial_ms = timed(step, args.steps)
     for k in range(args.steps):
         step(events[k])
     torch.cuda.synchronize()
     stages = np.array([[events[k][a].elapsed_time(events[k][a + 1]) for a in range(5)] for k in range(args.steps)])
     mean = stages.mean(axis=0)          # ms per stage between consecutive events
-    serial_ms = float(stages.sum(axis=1).mean())
     nnz = int(length.sum().item())
-    ab = algorithmic_bytes(cfg, nnz)
-    t_attn = mean[3] * 1e-3
-    achieved = ab["total"] / t_attn / 1e9
-    traffic = measured_traffic(cfg.name)
+    t_attn_ms = float(mean[3])
     layer_ms = float(mean[1:].sum())
-    C, nc, s = cfg.channels, cfg.n_comp, (2 if cfg.storage == "bf16" else 4)
-    nd = sum((2 * l + 1) ** 2 for l in range(1, cfg.lmax + 1))
     if cfg.storage == "bf16":
-        # fused projections + source EAAS: h and positions in; q, the key + tail rows,
-        # h's component pairs, D blocks, pos4 out
-        front = N * nc * C * 2 + N * 12 + N * C * 4 + N * C * 4 + N * (nc & ~1) * C * 2 + N * (4 * nd + 16)
         stage_names = ("neighbours", "projections+source_eaas", None, "attention", "target_eaas+output_projection")
-        front += N * (4 * nd + 16)          # the back end reads the D blocks and pos4 again
     else:
-        front = (N * nc * C * s + N * C * 8 + N * nc * C * 4                          # projections
-                 + N * nc * C * 4 + N * 12 + N * nc * C * s + N * (4 * nd + 16))    # source EAAS
         stage_names = ("neighbours", "projections", "source_eaas", "attention", "output_projection")
-    back = N * (2 * nc * C + 4) + N * nc * C * 4 if cfg.storage == "bf16" else 2 * N * nc * C * 4
-    layer_bytes = (front
-                   + ab["total"]                                          # streaming attention + target EAAS
-                   + back)                                                # (target EAAS +) output projection
     stage_ms = {}
     for name, v in zip(stage_names, mean):
         if name is None:
@@ -409,6 +571,12 @@ def main():
         else:
             stage_ms[name] = float(v)
             prev = name
+    a = algorithmic(cfg, nnz)
+    # the whole layer (A2-A6) by the survey's per-unit count: the streaming bytes above
+    # plus the node kernels' (A3 reads h and writes h' in the storage dtype, A5 reads m
+    # and writes hhat in fp32, A2/A6 read their inputs and write fp32 q, k and out)
+    C, nc, sb = cfg.channels, cfg.n_comp, (2 if cfg.storage == "bf16" else 4)
+    node_bytes = N * (2 * nc * C * sb + 8 * nc * C + 4 * nc * C + 8 * C)
 
     rec = {
         "metric": METRIC,
@@ -426,34 +594,29 @@ def main():
         "config": {
             "workload": f"{cfg.name}: {N} atoms, {cfg.geometry} at {cfg.density} atoms/A^3, cutoff {cfg.cutoff} A, "
                         f"cap K={K}, l_max={cfg.lmax}, C={cfg.channels}, {cfg.heads} heads, {cfg.n_rbf} RBFs, "
-                        f"{cfg.storage} storage, fp32 arithmetic",
+                        f"{cfg.storage} storage (h' and m in fp16 under a per-node scale, q and k fp32), "
+                        f"fp32 arithmetic",
             "nnz": nnz,
             "steps_per_s": 1e3 / ms_step,
+            "timing": "HIP events on the main stream around the whole loop of --steps steps",
             "stage_ms": stage_ms,
             "stages_in_order_ms_per_step": serial_ms,
             "overlap": "projections + source coupling on a second stream during the neighbour build",
             "layer_ms_excl_neighbours": layer_ms,
             "layer_pairs_per_s_excl_neighbours": nnz / (layer_ms * 1e-3),
-            "layer_hbm_frac_excl_neighbours": layer_bytes / (layer_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "layer_steps_per_s_excl_neighbours": 1e3 / layer_ms,
+            "layer_algorithmic_frac_excl_neighbours": (a["bytes"] + node_bytes) / (layer_ms * 1e-3)
+                                                      / (HBM_PEAK_GBS * 1e9),
         },
-        "roofline": {
-            "kernel": streaming_kernel(cfg),
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": ab["total"],
-            "bytes_per_pair": ab["per_pair"],
-            "bytes_per_target": ab["per_node"],
-            "avg_launch_ms": float(mean[3]),
-            "note": "achieved counts every (target, neighbour) pair's row (algorithmic bytes); rows shared by "
-                    "the two targets of a wave are loaded once, and rows shared by nearby targets are served "
-                    "from L2/MALL, so HBM traffic is a small part of it (see traffic) and frac can exceed 1",
-        },
+        "roofline": roofline(cfg, nnz, t_attn_ms),
         "cpu_baseline": None,
     }
+    if not args.no_per_config:
+        rec["config"]["per_config"] = {}
+        for name in PER_CONFIG:
+            if name != cfg.name:
+                rec["config"]["per_config"][name] = per_config(B, W, torch, name)
+                torch.cuda.empty_cache()
     if not args.no_stack:
         rec["config"]["stack"] = stack_bench(B, W, torch)
     if not args.no_backward:
