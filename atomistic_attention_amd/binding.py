@@ -24,7 +24,7 @@ EXPORTS = [
     "e2v2_path_table", "e2v2_eaas_coefficients", "e2v2_alignment_wigner", "e2v2_status_string",
     "e2v2_last_error", "e2v2_filter_neighbors", "e2v2_max_displacement2", "e2v2_stack_state_bytes",
     "e2v2_stack_workspace_bytes", "e2v2_stack_forward", "e2v2_layer_backward_workspace_bytes",
-    "e2v2_layer_backward", "e2v2_stack_backward_workspace_bytes", "e2v2_stack_backward",
+    "e2v2_layer_backward", "e2v2_stack_backward_workspace_bytes", "e2v2_stack_backward", "e2v2_attn_forward_noalloc",
 ]
 
 
@@ -116,6 +116,9 @@ def load(path: str = LIB_PATH):
     lib.e2v2_stack_backward.argtypes = [i32, ctypes.POINTER(LayerDesc), ctypes.POINTER(Weights), vp, vp, i32, i32,
                                         vp, sz, ctypes.POINTER(RebuildPolicy), vp, vp, vp, vp, sz, vp]
     lib.e2v2_stack_backward.restype = ctypes.c_int
+    lib.e2v2_attn_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp,
+                                              vp, i32, vp, vp]
+    lib.e2v2_attn_forward_noalloc.restype = ctypes.c_int
     lib.e2v2_status_string.argtypes = [ctypes.c_int]
     lib.e2v2_status_string.restype = ctypes.c_char_p
     lib.e2v2_last_error.argtypes = []
@@ -293,6 +296,25 @@ def e2v2_attn_forward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len
                                         _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), n, _ptr(out),
                                         _ptr(workspace), workspace.numel(), ctypes.byref(tp), _stream(stream))
     _check(st)
+    return out
+
+
+def e2v2_attn_forward_noalloc(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_len, nbr_idx, out: torch.Tensor,
+                              stream=None, target_order: torch.Tensor | None = None) -> torch.Tensor:
+    """e2v2_attn_forward with the library's own device array as workspace (no
+    allocation in the call; `out` is the caller's)."""
+    lib = load()
+    _dev(pos, torch.float32, "pos")
+    _dev(h, h.dtype, "h")
+    for t, nm in ((nbr_start, "nbr_start"), (nbr_len, "nbr_len"), (nbr_idx, "nbr_idx")):
+        _dev(t, torch.int32, nm)
+    if target_order is not None:
+        _dev(target_order, torch.int32, "target_order")
+    _dev(out, torch.float32, "out")
+    w = _weights(weights, h.dtype)
+    _check(lib.e2v2_attn_forward_noalloc(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), _ptr(nbr_start),
+                                         _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), pos.shape[0], _ptr(out),
+                                         _stream(stream)))
     return out
 
 

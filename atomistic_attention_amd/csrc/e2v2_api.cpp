@@ -680,6 +680,69 @@ e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, con
 }  // extern "C"
 
 // ============================================================================
+// The forward without a caller workspace, for callers that cannot allocate
+// ============================================================================
+namespace {
+// The workspace of e2v2_attn_forward_noalloc: one array per device, held from
+// the library's load to the end of the process.  In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;      // 64 MiB
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices];                // device address of `scratch`, per device
+
+// This device's scratch address, looked up once per device with that device current.
+e2v2_status scratch_address(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(E2V2_ERR_UNSUPPORTED, "device %d: the scratch array serves devices 0..%d", dev,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(E2V2_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return E2V2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+e2v2_status e2v2_attn_forward_noalloc(const e2v2_layer_desc *desc, const float *pos, const void *h,
+                                      const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
+                                      const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
+                                      hipStream_t stream)
+{
+    if (!desc) return fail(E2V2_ERR_ARG, "desc is NULL");
+    e2v2_status st = check_desc(desc);
+    if (st != E2V2_OK) return st;
+    if (n < 0 || n == INT32_MAX) return fail(E2V2_ERR_ARG, "n = %d out of range", n);
+    const size_t need = attn_ws(*desc, n).total;
+    if (need > kScratchBytes)
+        return fail(E2V2_ERR_CAPACITY, "n = %d needs %zu bytes of workspace; the allocation-free forward holds %zu "
+                    "(use e2v2_attn_forward with a caller workspace)", n, need, kScratchBytes);
+    if (n == 0) return E2V2_OK;
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != E2V2_OK) return st;
+    // Nothing in the workspace needs to start at zero: every region is written
+    // before it is read within the call.
+    return attn_run(desc, pos, h, w, nbr_start, nbr_len, nbr_idx, target_order, n, out, ws, kScratchBytes, nullptr,
+                    stream, true, true);
+}
+
+}  // extern "C"
+
+// ============================================================================
 // Gradient of the layer with respect to its input features (fp32 storage)
 // ============================================================================
 namespace {

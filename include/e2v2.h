@@ -188,6 +188,23 @@ e2v2_status e2v2_attn_forward(const e2v2_layer_desc *desc, const float *pos, con
                               const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): e2v2_attn_forward with
+ * no workspace argument.  The workspace is a 64 MiB array inside the library,
+ * one per device, held until the process ends; its device address is looked up
+ * once per device on the first call with that device current.  The call makes
+ * no hipMalloc, hipFree or other allocating call.  Arguments, results and errors
+ * as for e2v2_attn_forward, plus E2V2_ERR_CAPACITY (nothing enqueued) when
+ * e2v2_attn_workspace_bytes(desc, n) exceeds 64 MiB: about 11,000 atoms at
+ * l_max = 2, C = 128 with bf16 storage, about 4,000 with fp32 storage.  All
+ * calls on one device share its array: calls that overlap on one device (two
+ * streams, two host threads) race and must be ordered by the caller.  Nothing
+ * in the array needs to start at zero. */
+e2v2_status e2v2_attn_forward_noalloc(const e2v2_layer_desc *desc, const float *pos, const void *h,
+                                      const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
+                                      const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
+                                      hipStream_t stream);
+
 /* Same as e2v2_attn_forward, also copying intermediates into `taps` (host
  * pointer to a struct of device pointers; NULL behaves like e2v2_attn_forward). */
 e2v2_status e2v2_attn_forward_taps(const e2v2_layer_desc *desc, const float *pos, const void *h,

@@ -281,3 +281,21 @@ def test_stack_backward_workspace_has_one_transposed_list_per_cutoff(lib):
     a = lib.e2v2_stack_backward_workspace_bytes(4, four, n, K)
     b = lib.e2v2_stack_backward_workspace_bytes(4, two, n, K)
     assert b - a >= 2 * n * K * 4 and b - a <= 2 * (n * K * 4 + 5 * (n + 1) * 4 + 5 * 256)
+
+
+def test_noalloc_forward_rejects_sizes_beyond_its_array(lib):
+    """The allocation-free forward refuses, before any HIP call, an input whose
+    workspace exceeds its 64 MiB device array; argument errors come first."""
+    d = _desc()
+    w = B.Weights(*([FAKE] * 7))
+    need = lib.e2v2_attn_workspace_bytes(ctypes.byref(d), 100000)
+    assert need > 64 << 20
+    st = lib.e2v2_attn_forward_noalloc(ctypes.byref(d), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, None, 100000,
+                                       FAKE, None)
+    assert st == B.E2V2_ERR_CAPACITY and "workspace" in lib.e2v2_last_error().decode()
+    assert lib.e2v2_attn_forward_noalloc(None, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, None, 10, FAKE,
+                                         None) == B.E2V2_ERR_ARG
+    assert lib.e2v2_attn_forward_noalloc(ctypes.byref(d), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, None, -1,
+                                         FAKE, None) == B.E2V2_ERR_ARG
+    assert lib.e2v2_attn_forward_noalloc(ctypes.byref(d), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, None, 0,
+                                         FAKE, None) == B.E2V2_OK
