@@ -32,7 +32,11 @@ tests/test_oracle_*.py):
   backward.grad_h                 pinned: central finite differences of layer.layer_forward
                                   (directional and element-wise), forward equal to
                                   layer.layer_forward, one-neighbour and isolated-atom cases
+  edge.solid_sh                   pinned: polynomial closed forms to l = 2, homogeneity, parity
+  edge.edge_forward               pinned: invariance under a common translation, rotation
+                                  equivariance (l_max 1..3), the l <= 1 paths by hand (dot
+                                  and cross products), alpha from a closed-form bias
   backward.stack_grad_pos_h       pinned: central finite differences of the numpy layer
                                   composition over the stack's fixed lists
 """
-from . import so3, layer, stack, backward  # noqa: F401
+from . import so3, layer, stack, backward, edge  # noqa: F401
