@@ -25,6 +25,7 @@ EXPORTS = [
     "e2v2_last_error", "e2v2_filter_neighbors", "e2v2_max_displacement2", "e2v2_stack_state_bytes",
     "e2v2_stack_workspace_bytes", "e2v2_stack_forward", "e2v2_layer_backward_workspace_bytes",
     "e2v2_layer_backward", "e2v2_stack_backward_workspace_bytes", "e2v2_stack_backward", "e2v2_attn_forward_noalloc",
+    "e2v2_edge_forward", "e2v2_edge_workspace_bytes", "e2v2_edge_coefficients",
 ]
 
 
@@ -119,6 +120,13 @@ def load(path: str = LIB_PATH):
     lib.e2v2_attn_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp,
                                               vp, i32, vp, vp]
     lib.e2v2_attn_forward_noalloc.restype = ctypes.c_int
+    lib.e2v2_edge_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, vp,
+                                      i32, vp, vp, sz, vp]
+    lib.e2v2_edge_forward.restype = ctypes.c_int
+    lib.e2v2_edge_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32]
+    lib.e2v2_edge_workspace_bytes.restype = sz
+    lib.e2v2_edge_coefficients.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), i32]
+    lib.e2v2_edge_coefficients.restype = i32
     lib.e2v2_status_string.argtypes = [ctypes.c_int]
     lib.e2v2_status_string.restype = ctypes.c_char_p
     lib.e2v2_last_error.argtypes = []
@@ -315,6 +323,36 @@ def e2v2_attn_forward_noalloc(desc: LayerDesc, pos, h, weights: dict, nbr_start,
     _check(lib.e2v2_attn_forward_noalloc(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), _ptr(nbr_start),
                                          _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), pos.shape[0], _ptr(out),
                                          _stream(stream)))
+    return out
+
+
+def edge_workspace_bytes(desc: LayerDesc, n: int) -> int:
+    return int(load().e2v2_edge_workspace_bytes(ctypes.byref(desc), n))
+
+
+def e2v2_edge_forward(desc: LayerDesc, pos, h, weights: dict, w_edge, nbr_start, nbr_len, nbr_idx, out=None,
+                      workspace=None, stream=None, target_order: torch.Tensor | None = None) -> torch.Tensor:
+    """The exact edge-equivalent form (fp32 storage, l_max <= 2): weights as for the
+    layer (w_q, w_k, w_v, w_o, w_rbf), w_edge [n_paths][C] fp32 the edge weights."""
+    lib = load()
+    n = pos.shape[0]
+    _dev(pos, torch.float32, "pos")
+    _dev(h, torch.float32, "h")
+    _dev(w_edge, torch.float32, "w_edge")
+    for t, nm in ((nbr_start, "nbr_start"), (nbr_len, "nbr_len"), (nbr_idx, "nbr_idx")):
+        _dev(t, torch.int32, nm)
+    if target_order is not None:
+        _dev(target_order, torch.int32, "target_order")
+    if out is None:
+        out = torch.empty(h.shape, dtype=torch.float32, device=h.device)
+    wsb = edge_workspace_bytes(desc, n)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=h.device)
+    wd = dict(weights, w_src=w_edge, w_tgt=w_edge)
+    w = _weights(wd, torch.float32)
+    _check(lib.e2v2_edge_forward(ctypes.byref(desc), _ptr(pos), _ptr(h), ctypes.byref(w), _ptr(nbr_start),
+                                 _ptr(nbr_len), _ptr(nbr_idx), _ptr(target_order), n, _ptr(out), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
     return out
 
 

@@ -19,11 +19,14 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/e2v2.h"
 #include "e2v2_internal.h"
+#include "edge_terms.h"
 
 namespace e2v2 {
 namespace {
@@ -248,6 +251,201 @@ const float *ygrad_values(int lmax)
     });
     return g_yval[lmax];
 }
+
+// ---------------------------------------------------------------- edge-form tables
+namespace {
+double binom(int a, int b)
+{
+    double r = 1.0;
+    for (int k = 1; k <= b; ++k) r = r * (a - b + k) / k;
+    return r;
+}
+// Addition theorem of the component-normalised solid harmonics:
+// S^lf(x + y) = sum_lam a (S^lam(x) (x) S^(lf - lam)(y))^lf.
+double addition_coef(int lf, int lam)
+{
+    const int mu = lf - lam;
+    return std::sqrt(binom(2 * lf, 2 * lam) * (2.0 * lf + 1.0) / ((2.0 * lam + 1.0) * (2.0 * mu + 1.0)));
+}
+// 6j recoupling coefficients U(lp) in
+//   (v^li (x) (a^lam (x) b^mu)^lf)^lo = sum_lp U(lp) ((v^li (x) a^lam)^lp (x) b^mu)^lo,
+// from their definition as contractions of four coupling tensors: the left side
+// and each term of the right side are 4-index tensors [m_i, m_lam, m_mu, m_o];
+// U solves the least-squares fit of the left side by the right-side terms, which
+// must be exact (residual below 1e-9 of the left side, else false).
+bool recouple(int li, int lam, int mu, int lf, int lo, std::vector<int> &lps, std::vector<double> &U)
+{
+    const int ni = 2 * li + 1, na = 2 * lam + 1, nb = 2 * mu + 1, nf = 2 * lf + 1, no = 2 * lo + 1;
+    const int sz = ni * na * nb * no;
+    auto at = [&](int i, int a, int b, int o) { return ((i * na + a) * nb + b) * no + o; };
+    std::vector<double> Lt(sz, 0.0);
+    for (int i = 0; i < ni; ++i)
+        for (int a = 0; a < na; ++a)
+            for (int b = 0; b < nb; ++b)
+                for (int o = 0; o < no; ++o) {
+                    double acc = 0.0;
+                    for (int f = 0; f < nf; ++f)
+                        acc += coupling_entry(lam, mu, lf, a - lam, b - mu, f - lf) *
+                               coupling_entry(li, lf, lo, i - li, f - lf, o - lo);
+                    Lt[at(i, a, b, o)] = acc;
+                }
+    lps.clear();
+    std::vector<std::vector<double>> Bs;
+    for (int lp = std::abs(li - lam); lp <= li + lam; ++lp) {
+        if (!is_path(lp, mu, lo)) continue;
+        const int np = 2 * lp + 1;
+        std::vector<double> B(sz, 0.0);
+        for (int i = 0; i < ni; ++i)
+            for (int a = 0; a < na; ++a)
+                for (int b = 0; b < nb; ++b)
+                    for (int o = 0; o < no; ++o) {
+                        double acc = 0.0;
+                        for (int m = 0; m < np; ++m)
+                            acc += coupling_entry(li, lam, lp, i - li, a - lam, m - lp) *
+                                   coupling_entry(lp, mu, lo, m - lp, b - mu, o - lo);
+                        B[at(i, a, b, o)] = acc;
+                    }
+        lps.push_back(lp);
+        Bs.push_back(B);
+    }
+    const int k = (int)lps.size();
+    double Gm[8][9] = {};
+    for (int r = 0; r < k; ++r) {
+        for (int c = 0; c < k; ++c) {
+            double g = 0.0;
+            for (int e = 0; e < sz; ++e) g += Bs[r][e] * Bs[c][e];
+            Gm[r][c] = g;
+        }
+        double rhs = 0.0;
+        for (int e = 0; e < sz; ++e) rhs += Bs[r][e] * Lt[e];
+        Gm[r][k] = rhs;
+    }
+    for (int c = 0; c < k; ++c) {                       // Gauss-Jordan on the Gram system
+        int piv = c;
+        for (int r = c + 1; r < k; ++r)
+            if (std::fabs(Gm[r][c]) > std::fabs(Gm[piv][c])) piv = r;
+        if (std::fabs(Gm[piv][c]) < 1e-14) return false;
+        for (int cc = 0; cc <= k; ++cc) std::swap(Gm[c][cc], Gm[piv][cc]);
+        for (int r = 0; r < k; ++r)
+            if (r != c) {
+                const double f = Gm[r][c] / Gm[c][c];
+                for (int cc = 0; cc <= k; ++cc) Gm[r][cc] -= f * Gm[c][cc];
+            }
+    }
+    U.assign(k, 0.0);
+    for (int r = 0; r < k; ++r) U[r] = Gm[r][k] / Gm[r][r];
+    double res = 0.0, nrm = 0.0;
+    for (int e = 0; e < sz; ++e) {
+        double fit = 0.0;
+        for (int r = 0; r < k; ++r) fit += U[r] * Bs[r][e];
+        res += (Lt[e] - fit) * (Lt[e] - fit);
+        nrm += Lt[e] * Lt[e];
+    }
+    return res <= 1e-18 * std::max(nrm, 1e-300) || nrm == 0.0;
+}
+
+struct EdgeTables {
+    bool ok[edge::kMaxEdgeL + 1];
+    double src[edge::kMaxEdgeL + 1][edge::kMaxSrcTerms];
+    double tgt[edge::kMaxEdgeL + 1][edge::kMaxTgtTerms];
+    float srcf[edge::kMaxEdgeL + 1][edge::kMaxSrcTerms];
+    float tgtf[edge::kMaxEdgeL + 1][edge::kMaxTgtTerms];
+};
+EdgeTables g_edge;
+std::once_flag g_once_edge;
+
+void comp_lm(int e, int &l, int &m)
+{
+    l = 0;
+    while ((l + 1) * (l + 1) <= e) ++l;
+    m = e - l * l - l;
+}
+
+template <int L>
+bool build_edge(double *src, double *tgt)
+{
+    constexpr edge::Blocks B = edge::blocks<L>();
+    constexpr edge::SrcTerms S = edge::src_terms<L>();
+    constexpr edge::TgtTerms T = edge::tgt_terms<L>();
+    static_assert(B.n <= edge::kMaxBlocks && S.n <= edge::kMaxSrcTerms && T.n <= edge::kMaxTgtTerms, "edge tables");
+    auto block_of = [&](int eg) -> const edge::Block & {
+        int k = 0;
+        while (!(eg >= B.b[k].off && eg < B.b[k].off + 2 * B.b[k].lp + 1)) ++k;
+        return B.b[k];
+    };
+    // every nonzero coupling entry of a used block or a target triple obeys the selection rule
+    for (int k = 0; k < B.n; ++k) {
+        const edge::Block &b = B.b[k];
+        for (int mi = -b.li; mi <= b.li; ++mi)
+            for (int ml = -b.lam; ml <= b.lam; ++ml)
+                for (int mp = -b.lp; mp <= b.lp; ++mp)
+                    if (!edge::real_allowed(b.li, b.lam, b.lp, mi, ml, mp) &&
+                        std::fabs(coupling_entry(b.li, b.lam, b.lp, mi, ml, mp)) > 1e-12)
+                        return false;
+    }
+    for (int q = 0; q < S.n; ++q) {
+        const edge::SrcTerm &t = S.t[q];
+        int li, mi, lam, ml;
+        comp_lm(t.ei, li, mi);
+        comp_lm(t.el, lam, ml);
+        const edge::Block &b = block_of(t.eg);
+        src[q] = coupling_entry(li, lam, b.lp, mi, ml, t.eg - b.off - b.lp);
+    }
+    int paths[64][3], np = 0;
+    for (int lo = 0; lo <= L; ++lo)
+        for (int li = 0; li <= L; ++li)
+            for (int lf = 0; lf <= L; ++lf)
+                if (is_path(li, lf, lo)) {
+                    paths[np][0] = li; paths[np][1] = lf; paths[np][2] = lo;
+                    ++np;
+                }
+    std::vector<int> lps;
+    std::vector<double> U;
+    for (int q = 0; q < T.n; ++q) {
+        const edge::TgtTerm &t = T.t[q];
+        const int li = paths[t.p][0], lf = paths[t.p][1], lo = paths[t.p][2];
+        const edge::Block &b = block_of(t.eg);
+        int mu, mm, lo2, mo;
+        comp_lm(t.em, mu, mm);
+        comp_lm(t.eo, lo2, mo);
+        if (b.li != li || b.lam + mu != lf || lo2 != lo) return false;
+        if (!recouple(li, b.lam, mu, lf, lo, lps, U)) return false;
+        double u = 0.0;
+        for (size_t r = 0; r < lps.size(); ++r)
+            if (lps[r] == b.lp) u = U[r];
+        tgt[q] = addition_coef(lf, b.lam) * u * coupling_entry(b.lp, mu, lo, t.eg - b.off - b.lp, mm, mo);
+    }
+    return true;
+}
+
+const EdgeTables &edge_tables()
+{
+    std::call_once(g_once_edge, [] {
+        std::memset(&g_edge, 0, sizeof(g_edge));
+        g_edge.ok[0] = build_edge<0>(g_edge.src[0], g_edge.tgt[0]);
+        g_edge.ok[1] = build_edge<1>(g_edge.src[1], g_edge.tgt[1]);
+        g_edge.ok[2] = build_edge<2>(g_edge.src[2], g_edge.tgt[2]);
+        for (int l = 0; l <= edge::kMaxEdgeL; ++l) {
+            for (int q = 0; q < edge::kMaxSrcTerms; ++q) g_edge.srcf[l][q] = (float)g_edge.src[l][q];
+            for (int q = 0; q < edge::kMaxTgtTerms; ++q) g_edge.tgtf[l][q] = (float)g_edge.tgt[l][q];
+        }
+    });
+    return g_edge;
+}
+}  // namespace
+
+namespace edge {
+const float *src_values(int lmax)
+{
+    if (lmax < 0 || lmax > kMaxEdgeL || !edge_tables().ok[lmax]) return nullptr;
+    return edge_tables().srcf[lmax];
+}
+const float *tgt_values(int lmax)
+{
+    if (lmax < 0 || lmax > kMaxEdgeL || !edge_tables().ok[lmax]) return nullptr;
+    return edge_tables().tgtf[lmax];
+}
+}  // namespace edge
 
 const Tables &host_tables()
 {
@@ -738,6 +936,138 @@ e2v2_status e2v2_attn_forward_noalloc(const e2v2_layer_desc *desc, const float *
     // before it is read within the call.
     return attn_run(desc, pos, h, w, nbr_start, nbr_len, nbr_idx, target_order, n, out, ws, kScratchBytes, nullptr,
                     stream, true, true);
+}
+
+}  // extern "C"
+
+// ============================================================================
+// The exact edge-equivalent form (fp32 storage, l_max <= 2)
+// ============================================================================
+namespace {
+struct EdgeWs {
+    size_t q, k, v, G, M, medge, pos4, origin, sval, tval, total;
+};
+EdgeWs edge_ws(const e2v2_layer_desc &d, int n)
+{
+    const size_t N = (size_t)n, C = (size_t)d.channels, NC = (size_t)n_comp(d.lmax);
+    const int ngp = edge_padded_comps(d.lmax);
+    const size_t NGP = ngp > 0 ? (size_t)ngp : 0;
+    EdgeWs w{};
+    size_t o = 0;
+    w.q = o; o += al256(N * C * 4);
+    w.k = o; o += al256(N * C * 4);
+    w.v = o; o += al256(N * NC * C * 4);
+    w.G = o; o += al256(N * NGP * C * 4);
+    w.M = o; o += al256(N * NGP * C * 4);
+    w.medge = o; o += al256(N * NC * C * 4);
+    w.pos4 = o; o += al256(N * 16);
+    w.origin = o; o += 256;
+    w.sval = o; o += al256(sizeof(float) * edge::kMaxSrcTerms);
+    w.tval = o; o += al256(sizeof(float) * edge::kMaxTgtTerms);
+    w.total = o + 256;
+    return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t e2v2_edge_workspace_bytes(const e2v2_layer_desc *desc, int32_t n)
+{
+    if (!desc || n < 0 || desc->lmax < 0 || desc->lmax > edge::kMaxEdgeL || desc->channels <= 0) return 0;
+    return edge_ws(*desc, n).total;
+}
+
+e2v2_status e2v2_edge_forward(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,
+                              const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
+                              const int32_t *target_order, int32_t n, float *out, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream)
+{
+    e2v2_status st = check_desc(desc);
+    if (st != E2V2_OK) return st;
+    if (desc->storage != E2V2_FP32) return fail(E2V2_ERR_UNSUPPORTED, "the edge form needs fp32 storage");
+    if (desc->lmax > edge::kMaxEdgeL) return fail(E2V2_ERR_UNSUPPORTED, "the edge form serves l_max <= 2");
+    if (n < 0 || n == INT32_MAX) return fail(E2V2_ERR_ARG, "n = %d out of range", n);
+    if (n == 0) return E2V2_OK;
+    if (!w) return fail(E2V2_ERR_ARG, "weights is NULL");
+    for (const void *p : {(const void *)pos, h, (const void *)w->w_q, (const void *)w->w_k, (const void *)w->w_v,
+                          (const void *)w->w_o, (const void *)w->w_rbf, (const void *)w->w_src,
+                          (const void *)nbr_start, (const void *)nbr_len, (const void *)nbr_idx, (const void *)out,
+                          (const void *)workspace}) {
+        if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
+        if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    }
+    if (target_order && !aligned16(target_order)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
+    const EdgeWs L = edge_ws(*desc, n);
+    if (workspace_bytes < L.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, L.total);
+    const float *sv = edge::src_values(desc->lmax), *tv = edge::tgt_values(desc->lmax);
+    if (!sv || !tv) return fail(E2V2_ERR_HIP, "edge-form coefficient tables failed their exactness check");
+    char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+    const int lmax = desc->lmax, C = desc->channels, NC = n_comp(lmax);
+    const size_t wstride = (size_t)C * C * 4;
+    float *q = reinterpret_cast<float *>(ws + L.q), *k = reinterpret_cast<float *>(ws + L.k);
+    float *v = reinterpret_cast<float *>(ws + L.v), *medge = reinterpret_cast<float *>(ws + L.medge);
+    auto wv32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_v) + l * wstride); };
+    auto wo32 = [&](int l) { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(w->w_o) + l * wstride); };
+    const float *h32 = reinterpret_cast<const float *>(h);
+    ProjJob jobs[kMaxL * kMaxL + 2 * kMaxL + 1 + 2];
+    int nj = 0;
+    for (int l = 0; l <= lmax; ++l)
+        for (int m = 0; m < 2 * l + 1; ++m)
+            jobs[nj++] = ProjJob{h32, (long long)NC * C, wv32(l), v, (long long)NC * C, l * l + m};
+    jobs[nj++] = ProjJob{h32, (long long)NC * C, reinterpret_cast<const float *>(w->w_q), q, (long long)C, 0};
+    jobs[nj++] = ProjJob{h32, (long long)NC * C, reinterpret_cast<const float *>(w->w_k), k, (long long)C, 0};
+    hipError_t e = launch_proj(jobs, nj, n, C, stream);
+    if (e != hipSuccess) return hip_fail(e, "projection kernel");
+    e = hipMemcpyAsync(ws + L.sval, sv, sizeof(float) * edge::kMaxSrcTerms, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(ws + L.tval, tv, sizeof(float) * edge::kMaxTgtTerms, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "copying the edge-form tables");
+    EdgeArgs a{};
+    a.pos = pos; a.q = q; a.k = k; a.v = v; a.w_rbf = w->w_rbf; a.w_e = w->w_src;
+    a.src_val = reinterpret_cast<const float *>(ws + L.sval);
+    a.tgt_val = reinterpret_cast<const float *>(ws + L.tval);
+    a.nbr_start = nbr_start; a.nbr_len = nbr_len; a.nbr_idx = nbr_idx; a.order = target_order;
+    a.G = reinterpret_cast<float *>(ws + L.G); a.M = reinterpret_cast<float *>(ws + L.M); a.medge = medge;
+    a.pos4 = reinterpret_cast<float4 *>(ws + L.pos4); a.origin = reinterpret_cast<float4 *>(ws + L.origin);
+    a.n = n; a.C = C; a.H = desc->heads; a.R = desc->n_rbf; a.cutoff = desc->cutoff;
+    e = launch_edge(lmax, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "edge-form kernels");
+    nj = 0;
+    for (int l = 0; l <= lmax; ++l)
+        for (int m = 0; m < 2 * l + 1; ++m)
+            jobs[nj++] = ProjJob{medge, (long long)NC * C, wo32(l), out, (long long)NC * C, l * l + m};
+    e = launch_proj(jobs, nj, n, C, stream);
+    if (e != hipSuccess) return hip_fail(e, "output projection kernel");
+    return E2V2_OK;
+}
+
+int32_t e2v2_edge_coefficients(int32_t lmax, int32_t which, int32_t *idx, double *val, int32_t cap)
+{
+    if (lmax < 0 || lmax > edge::kMaxEdgeL || which < 0 || which > 2) return -1;
+    const EdgeTables &t = edge_tables();
+    if (!t.ok[lmax]) return -1;
+    int cnt = 0;
+    auto put = [&](std::initializer_list<int> ix, double v) {
+        if (cnt < cap && idx) {
+            int k = 0;
+            for (int x : ix) idx[4 * cnt + k++] = x;
+            while (k < 4) idx[4 * cnt + k++] = -1;
+            if (val) val[cnt] = v;
+        }
+        ++cnt;
+    };
+    auto emit = [&](auto B, auto S, auto T) {
+        if (which == 0)
+            for (int q = 0; q < S.n; ++q) put({S.t[q].ei, S.t[q].el, S.t[q].eg}, t.src[lmax][q]);
+        else if (which == 1)
+            for (int q = 0; q < T.n; ++q) put({T.t[q].p, T.t[q].eg, T.t[q].em, T.t[q].eo}, t.tgt[lmax][q]);
+        else
+            for (int k = 0; k < B.n; ++k) put({B.b[k].li, B.b[k].lam, B.b[k].lp, B.b[k].off}, 0.0);
+    };
+    if (lmax == 0) emit(edge::blocks<0>(), edge::src_terms<0>(), edge::tgt_terms<0>());
+    else if (lmax == 1) emit(edge::blocks<1>(), edge::src_terms<1>(), edge::tgt_terms<1>());
+    else emit(edge::blocks<2>(), edge::src_terms<2>(), edge::tgt_terms<2>());
+    return cnt;
 }
 
 }  // extern "C"

@@ -570,6 +570,24 @@ struct AttnBwdArgs {
 };
 hipError_t launch_attn_bwd(int L, const AttnBwdArgs &a, hipStream_t stream);
 
+// The exact edge-equivalent form (edge.hip, edge_terms.h): fp32 storage, l_max <= 2.
+// q, k [n][C] and v [n][NC][C] from the projections; G and M [n][NGP][C] (NGP =
+// edge_padded_comps(L)); medge [n][NC][C] the aggregated edge products before W_O;
+// pos4 [n]; origin one float4; src_val / tgt_val device copies of the host tables.
+struct EdgeArgs {
+    const float *pos;
+    const float *q, *k, *v;
+    const float *w_rbf, *w_e;
+    const float *src_val, *tgt_val;
+    const int32_t *nbr_start, *nbr_len, *nbr_idx, *order;
+    float *G, *M, *medge;
+    float4 *pos4, *origin;
+    int n, C, H, R;
+    float cutoff;
+};
+hipError_t launch_edge(int L, const EdgeArgs &a, hipStream_t stream);
+int edge_padded_comps(int L);
+
 // Entries of the real coupling tensors T_p[m_i, m_f, m_o] with l_f >= 1 that can be
 // nonzero, for the encoding gradient: in the complex basis M = mu_i + mu_f, so in
 // the real basis |m_o| is |m_i| + |m_f| or ||m_i| - |m_f||, and the numbers of

@@ -419,6 +419,52 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
             "attention_adjoint_algorithmic_bytes": per_pair * nnz + per_node * c.n}
 
 
+def edge_bench(B, W, torch, steps: int = 10, warmup: int = 2, name: str = "g4") -> dict:
+    """The exact edge-equivalent form (e2v2_edge_forward: per-edge tensor products with
+    solid harmonics of r_j - r_i, evaluated node by node through 6j recoupling) on the
+    32,768-atom system with an uncapped 5 A list, fp32 storage, next to the layer's
+    forward on the same system and list; both timed with HIP events."""
+    from atomistic_attention_amd.workloads import num_paths
+    wl = W.make_workload(name)
+    c = wl.cfg
+    d = W.device_arrays(wl)
+    dev = d["pos"].device
+    desc = B.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
+    order = torch.empty(c.n, dtype=torch.int32, device=dev)
+    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, 0, order_out=order)
+    w_e = torch.from_numpy(np.random.default_rng(9).standard_normal((num_paths(c.lmax), c.channels))
+                           .astype(np.float32)).to(dev)
+    out = torch.empty(wl.h.shape, dtype=torch.float32, device=dev)
+    ews = torch.empty(B.edge_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
+    aws = torch.empty(B.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms_edge = timed(lambda: B.e2v2_edge_forward(desc, d["pos"], d["h"], d["weights"], w_e, s, ln, ix, out=out,
+                                                workspace=ews, target_order=order))
+    ms_layer = timed(lambda: B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, out=out,
+                                                 workspace=aws, target_order=order))
+    ngp = {0: 20, 1: 20, 2: 60}[c.lmax]
+    return {"workload": f"{name}: {c.n} atoms, {c.geometry} at {c.density} atoms/A^3, cutoff {c.cutoff} A uncapped, "
+                        f"l_max={c.lmax}, C={c.channels}, {c.heads} heads, {c.n_rbf} RBFs, fp32 storage",
+            "nnz": int(nnz), "steps": steps, "ms_edge_forward": ms_edge, "ms_layer_forward_same_system": ms_layer,
+            "pairs_per_s": nnz / (ms_edge * 1e-3), "steps_per_s": 1e3 / ms_edge,
+            "source_row_bytes": ngp * c.channels * 4,
+            "what": "out = W_O sum_j alpha_ij sum_p w_e[p] (v_j (x) S((r_j - r_i) / r_c))_p evaluated node by node: "
+                    "sources coupled with S of their own position (58 components per channel, padded to 60), "
+                    "the stream sums alpha-weighted rows, targets recouple with S of their own position"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -433,6 +479,7 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="run only the feature-gradient measurement and print its record (for profiling)")
     ap.add_argument("--no-per-config", action="store_true", help="skip the records of the other configurations")
+    ap.add_argument("--no-edge", action="store_true", help="skip the edge-form measurement")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: 5 layer steps of --config, then 3 plain device copies of "
                          "1 GiB (the copies calibrate the counters' byte units); prints no JSON")
@@ -621,6 +668,8 @@ def main():
         rec["config"]["stack"] = stack_bench(B, W, torch)
     if not args.no_backward:
         rec["config"]["backward"] = backward_bench(B, W, torch)
+    if not args.no_edge:
+        rec["config"]["edge_form"] = edge_bench(B, W, torch)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(rec), flush=True)

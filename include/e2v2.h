@@ -392,6 +392,42 @@ e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, 
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The exact edge-equivalent form (E2Former-V2 explainer, section 1.2: the
+ * Wigner-6j recoupling identity that lets a node-centric evaluation reproduce
+ * an edge-centric one).  For each target i:
+ *   out_i^l = W_O[l] m_i^l,  m_i = sum_j alpha_ij sum_p w_e[p] (v_j (x) S(x_ij))_p,
+ * with x_ij = (r_j - r_i) / cutoff, S^l(x) = |x|^l Y^l(x / |x|) the component-
+ * normalised real solid harmonics (S^0 = 1), p = (l_i, l_f, l_o) over the paths
+ * of e2v2_path_table, v^l = h^l W_V[l], and alpha_ij the layer's attention
+ * weights (q.k / sqrt(C / heads) plus the distance bias, softmax over the row).
+ * The result depends on r_j - r_i only (translation invariant).  It is
+ * evaluated node by node: each source is coupled once with S of its own
+ * position relative to an origin (the centroid of the positions),
+ * the stream sums those rows with alpha, and each target couples the sum with S
+ * of its own position through the addition theorem of S and 6j recoupling
+ * coefficients; the per-edge products are never formed.
+ *   w    as for e2v2_attn_forward, except that w->w_src holds the edge weights
+ *        w_e [n_paths(lmax)][C] fp32 and w->w_tgt is not read
+ *   desc storage must be E2V2_FP32 and lmax <= 2 (E2V2_ERR_UNSUPPORTED
+ *        otherwise): the node terms grow like (|r - o| / cutoff)^l_f and cancel
+ *        to the edge term, so the fp32 rounding of the result grows like
+ *        (R / cutoff)^lmax for atoms R from the centroid (measured: 2e-5 of
+ *        the output RMS at R / cutoff = 4, 1,000 atoms)
+ *   other arguments as for e2v2_attn_forward; workspace of at least
+ *   e2v2_edge_workspace_bytes(desc, n) bytes. */
+e2v2_status e2v2_edge_forward(const e2v2_layer_desc *desc, const float *pos, const void *h,
+                              const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
+                              const int32_t *nbr_idx, const int32_t *target_order, int32_t n, float *out,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t e2v2_edge_workspace_bytes(const e2v2_layer_desc *desc, int32_t n);
+/* Host copy of the edge form's tables, for checking: which = 0 the source terms
+ * (idx [k][4] = component of v, of S, of the source row, -1), which = 1 the target
+ * terms (path, component of the summed row, of S, of the output), which = 2 the
+ * blocks of the source row (l_i, lam, l', first component; val unused).  Writes
+ * up to cap entries; returns the count, -1 for lmax outside 0..2. */
+int32_t e2v2_edge_coefficients(int32_t lmax, int32_t which, int32_t *idx, double *val, int32_t cap);
+
+/* ------------------------------------------------------------------------
  * Host-side tables (no GPU needed). */
 int32_t e2v2_num_paths(int32_t lmax);   /* 1, 5, 15, 34 for lmax 0..3; -1 if out of range */
 /* li_lf_lo: host [n_paths][3]. */
