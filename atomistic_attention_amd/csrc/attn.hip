@@ -301,6 +301,7 @@ hipError_t launch_attn(int L, int hp_bf16, const AttnArgs &a, hipStream_t stream
 {
     if (a.n <= 0) return hipSuccess;
     if (!hp_bf16) return launch_attn_f32(L, a, stream);     // fp32 storage: attn_f32.hip
+    if (hp_quad_layout(L, a.H, a.C, a.n)) return launch_attn_quad(L, a, stream);
     if (L <= 2 && a.n < attn_pair_max_atoms(L, 8 * a.H)) return launch_attn_pair(L, a, stream);
     switch (L) {
     case 0: return launch_attn_lh<0>(a, stream);

@@ -115,5 +115,8 @@ __device__ __forceinline__ void store_message_f16(const AttnArgs &A, int i, int 
 // storage, l_max <= 2, n < attn_pair_max_atoms(L, C).
 hipError_t launch_attn_pair(int L, const AttnArgs &a, hipStream_t stream);
 long long attn_pair_max_atoms(int L, int C);
+// Four targets per wave, weighted sums on the matrix cores (attn_quad.hip): h' in
+// hp_quad_offset layout, hp_quad_layout(L, H, C, n) must hold.
+hipError_t launch_attn_quad(int L, const AttnArgs &a, hipStream_t stream);
 
 }  // namespace e2v2

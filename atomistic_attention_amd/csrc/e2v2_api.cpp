@@ -770,6 +770,7 @@ e2v2_status attn_run(const e2v2_layer_desc *desc, const float *pos, const void *
             qa.hp_tap = taps ? taps->hprime : nullptr;
             qa.n = n;
             qa.frames_ready = frames_ready;
+            qa.quad = hp_quad_layout(lmax, desc->heads, (int)C, n);
             e = launch_qkv_eaas(lmax, qa, C, stream);
             if (e == hipSuccess) e = mark(1);
             if (e == hipSuccess) e = mark(2);

@@ -375,6 +375,26 @@ __host__ __device__ inline int hp_f16_offset(int e, int c, int NC, int C)
 // piece) and the key row k, fp32 [C].  h' carries the node's power-of-two scale s
 // (pos4[node].w): the stored fp16 values times s.
 __host__ __device__ constexpr int hp_row16(int NC, int C) { return NC * C; }
+// The layout read by the four-targets-per-wave kernel (attn_quad.hip), C = 128 and
+// NC = 1, 4 or 9: lane a = 4 h + c (head h, c < 4) of that kernel owns, per
+// component e, the dword (h'[e][8 h + c], h'[e][8 h + 4 + c]); each lane's first
+// D1 = 4 floor(NC / 4) dwords lie together (lane a at 4 D1 a bytes), the
+// remaining NC - D1 in a tail region after all 64 lanes' first parts.  Offset in
+// fp16 elements of (e, channel ch).
+__host__ __device__ inline int hp_quad_offset(int e, int ch, int NC)
+{
+    const int d1 = 4 * (NC / 4), d2 = NC - d1;
+    const int a = 4 * (ch >> 3) + (ch & 3), f = (ch >> 2) & 1;
+    return e < d1 ? a * 2 * d1 + 2 * e + f : 128 * d1 + a * 2 * d2 + 2 * (e - d1) + f;
+}
+// Four targets per wave with the weighted sums on the matrix cores (attn_quad.hip):
+// 16-bit storage, l_max <= 2, 16 heads of 8 channels, n < attn_quad_max_atoms(L).
+// Whenever it applies, the projection kernel writes h' in hp_quad_offset layout.
+long long attn_quad_max_atoms(int L);
+inline bool hp_quad_layout(int L, int H, int C, long long n)
+{
+    return L <= 2 && H == 16 && C == 128 && n < attn_quad_max_atoms(L);
+}
 
 
 // ----------------------------------------------------------------------------
@@ -398,12 +418,14 @@ __device__ __forceinline__ uint16_t f_to_bf16(float f)
 // keys (key x = lane * E + k in register k of lane x / E) go through the
 // log2(64 E) merge phases; compare-exchange partners closer than E sit in the
 // same lane, farther ones in lane ^ (d / E), reached by one shuffle per key.
-template <int E>
+// FIRST > 2 starts at the phase that merges runs of FIRST / 2: the keys must then
+// already form such runs, ascending where (x & FIRST / 2) == 0, else descending.
+template <int E, int FIRST = 2>
 __device__ __forceinline__ void wave_bitonic_sort(int (&a)[E], int lane)
 {
     constexpr int N = 64 * E;
 #pragma unroll
-    for (int size = 2; size <= N; size <<= 1) {
+    for (int size = FIRST; size <= N; size <<= 1) {
 #pragma unroll
         for (int d = size >> 1; d >= 1; d >>= 1) {
             if (d >= E) {
@@ -499,6 +521,7 @@ struct QkvEaasArgs {
     float *k_tap, *v_tap, *hp_tap;
     int n;
     bool frames_ready;               // dmat already holds these positions' D blocks
+    bool quad;                       // h' in hp_quad_offset layout (else hp_f16_offset)
 };
 hipError_t launch_qkv_eaas(int L, const QkvEaasArgs &a, int C, hipStream_t stream);
 

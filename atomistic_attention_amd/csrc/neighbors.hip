@@ -216,6 +216,33 @@ __device__ __forceinline__ bool row_reach(float4 p, float rcm, int z, int y, con
     return true;
 }
 
+// Cells are numbered in serpentine order: z-planes in turn, the rows of every odd
+// plane in reverse y order, and every odd row (counting rows globally) in reverse
+// x order.  Consecutive cells stay adjacent in space across row and plane ends,
+// so the cell order is a processing order whose runs of targets are compact, and
+// every row of cells is still one contiguous index range.
+__device__ __forceinline__ int row_base(const GridInfo &gi, int z, int y, bool &rev)
+{
+    const int ys = (z & 1) ? gi.dims[1] - 1 - y : y;
+    const int row = z * gi.dims[1] + ys;
+    rev = (row & 1) != 0;
+    return row * gi.dims[0];
+}
+__device__ __forceinline__ int cell_index(const GridInfo &gi, int cx, int cy, int cz)
+{
+    bool rev;
+    const int b = row_base(gi, cz, cy, rev);
+    return b + (rev ? gi.dims[0] - 1 - cx : cx);
+}
+// Cells [lo, hi] (inclusive) holding x-cells x0 .. x1 of row (z, y).
+__device__ __forceinline__ void row_cells(const GridInfo &gi, int z, int y, int x0, int x1, int &lo, int &hi)
+{
+    bool rev;
+    const int b = row_base(gi, z, y, rev);
+    lo = b + (rev ? gi.dims[0] - 1 - x1 : x0);
+    hi = b + (rev ? gi.dims[0] - 1 - x0 : x1);
+}
+
 // ---------------------------------------------------------------- step 2
 __global__ void k_cell_assign(const float *__restrict__ pos, int n, const GridInfo *__restrict__ grid,
                               int32_t *cell_of, int32_t *cell_cnt)
@@ -226,7 +253,7 @@ __global__ void k_cell_assign(const float *__restrict__ pos, int n, const GridIn
     const int cx = cell_coord(pos[3 * i + 0], gi.lo[0], gi.inv[0], gi.dims[0]);
     const int cy = cell_coord(pos[3 * i + 1], gi.lo[1], gi.inv[1], gi.dims[1]);
     const int cz = cell_coord(pos[3 * i + 2], gi.lo[2], gi.inv[2], gi.dims[2]);
-    const int c = (cz * gi.dims[1] + cy) * gi.dims[0] + cx;
+    const int c = cell_index(gi, cx, cy, cz);
     cell_of[i] = c;
     atomicAdd(&cell_cnt[c], 1);
 }
@@ -285,9 +312,9 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, c
 // ---------------------------------------------------------------- step 3
 // Two passes, so the order within a cell does not depend on the timing of atomics:
 // k_scatter drops every atom into its cell's range at an atomic slot (scratch),
-// then k_place puts it at its rank by atom index within that range.  The cells'
-// order is row-major (z, y, x), and within a cell atoms ascend: the same order
-// on every call.  A cell of k atoms costs k reads per atom.
+// then k_place puts it at its rank by atom index within that range.  The cells
+// follow the serpentine order of cell_index, and within a cell atoms ascend: the
+// same order on every call.  A cell of k atoms costs k reads per atom.
 __global__ void k_scatter(int n, const int32_t *__restrict__ cell_of, int32_t *cell_cur, int32_t *tmp)
 {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -316,7 +343,7 @@ __global__ void k_place(const float *__restrict__ pos, int n, const int32_t *__r
 // rebuilds): atoms sorted by the Morton code of their position on a grid of half
 // the cell width (10 bits per axis, clamped), a space-filling curve, so a run of
 // consecutive targets fills a compact region and the rows it reads stay close
-// together -- fewer L2 misses than the cells' row-major order.  Stable sort keyed
+// together -- fewer L2 misses than the cells' own order.  Stable sort keyed
 // on atom ids 0..n-1: deterministic.  Uses the grid of the last build in ws.
 __device__ __forceinline__ uint32_t spread3(uint32_t v)
 {
@@ -375,9 +402,10 @@ __device__ __forceinline__ void for_each_neighbor(int i, float4 pi, float rc, do
         for (int y = y0; y <= y1; ++y) {
             int x0, x1;
             if (!row_reach(pi, rcm, z, y, gi, x0, x1)) continue;
-            const int rowc = (z * gi.dims[1] + y) * gi.dims[0];
-            const int e = cell_start[rowc + x1 + 1];
-            for (int s = cell_start[rowc + x0]; s < e; ++s) {
+            int lo, hi;
+            row_cells(gi, z, y, x0, x1, lo, hi);
+            const int e = cell_start[hi + 1];
+            for (int s = cell_start[lo]; s < e; ++s) {
                 const float4 pj = spos[s];
                 const int j = __float_as_int(pj.w);
                 if (j == i) continue;
@@ -560,9 +588,10 @@ __device__ __forceinline__ int wave_scan(int i, float4 pi, float rc, double rc2,
             const int z = z0 + zr, y = y0 + (r - zr * ny);
             int x0, x1;
             if (row_reach(pi, rcm, z, y, gi, x0, x1)) {
-                const int rowc = (z * gi.dims[1] + y) * gi.dims[0];
-                a = cell_start[rowc + x0];
-                len = cell_start[rowc + x1 + 1] - a;
+                int lo, hi;
+                row_cells(gi, z, y, x0, x1, lo, hi);
+                a = cell_start[lo];
+                len = cell_start[hi + 1] - a;
             }
         }
         int incl = len;                               // running total over lanes 0..r

@@ -214,6 +214,33 @@ __global__ __launch_bounds__(4 * C) void qkv_eaas_kernel(const QkvEaasArgs a, co
         sb = b > 13u ? b - 13u : 1u;
     }
     const float sc = __uint_as_float(sb << 23), inv = __uint_as_float((254u - sb) << 23);
+    if constexpr (C == 128 && (NC == 1 || NC == 4 || NC == 9)) {
+        if (a.quad) {
+            // Rows in the streaming kernel's lane order (hp_quad_offset), assembled in
+            // the staging buffer -- every wave passed the barrier above, so the input
+            // rows are no longer read -- and written out in 16-byte pieces.
+            if (valid) {
+                uint16_t *row = reinterpret_cast<uint16_t *>(sH + nl * ROW);
+#pragma unroll
+                for (int e = 0; e < NC; ++e)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const _Float16 v = (_Float16)(acc[e][i] * inv);
+                        row[hp_quad_offset(e, c0 + i, NC)] = __builtin_bit_cast(uint16_t, v);
+                        if (a.hp_tap) a.hp_tap[(node * NC + e) * C + c0 + i] = (float)v * sc;
+                    }
+                if (nb == 0 && g == 0)
+                    a.pos4[node] = make_float4(a.pos[3 * node], a.pos[3 * node + 1], a.pos[3 * node + 2], sc);
+            }
+            __syncthreads();
+            unsigned char *dst = reinterpret_cast<unsigned char *>(a.hp) + node0 * (2 * NC * C);
+            for (int u = t; u < nvalid * U; u += NT) {
+                const int nd = u / U, o = u - nd * U;
+                *reinterpret_cast<uint4 *>(dst + (size_t)u * 16) = *reinterpret_cast<const uint4 *>(sH + nd * ROW + o * 16);
+            }
+            return;
+        }
+    }
     if (!valid) return;
     uint16_t *hp = a.hp + node * hp_row16(NC, C);
 #pragma unroll

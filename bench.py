@@ -45,7 +45,7 @@ FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed fp
 CLOCK_GHZ = 2.4
 SIMDS = 256 * 4                # 256 CUs x 4 SIMDs
 ATTN_SRCS = [os.path.join(ROOT, "atomistic_attention_amd", "csrc", f)
-             for f in ("attn_pair.hip", "attn.hip", "attn_common.h")]
+             for f in ("attn_quad.hip", "attn_pair.hip", "attn.hip", "attn_common.h")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_counters.json")
 PER_CONFIG = ("c1", "c2", "c3", "c3b", "c5")
 
@@ -77,6 +77,9 @@ def kernel_hash() -> str:
 
 
 def streaming_kernel(cfg) -> str:
+    if cfg.storage == "bf16" and cfg.lmax <= 2 and cfg.heads == 16 and cfg.channels == 128:
+        return ("attn_quad_kernel (four neighbouring targets per wave over the union of their lists, "
+                "logits, bias and weighted sums on the matrix cores; emits m_i)")
     if cfg.storage == "bf16" and cfg.lmax <= 2:
         return "attn_pair_kernel (two neighbouring targets per wave over the union of their lists; emits m_i)"
     if cfg.storage == "bf16":

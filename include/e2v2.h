@@ -135,8 +135,10 @@ typedef struct {
  *   order        device [n] int32 or NULL: receives the atoms in cell-list order
  *                (a permutation of 0..n-1 in which consecutive atoms are spatial
  *                neighbours); pass it as target_order to e2v2_attn_forward.  Cells
- *                come in row-major (z, y, x) order and atoms ascend within a cell,
- *                so the order is the same on every call with the same positions.
+ *                come in serpentine order (z-planes in turn, every other plane's
+ *                rows and every other row reversed, so consecutive cells touch)
+ *                and atoms ascend within a cell, so the order is the same on every
+ *                call with the same positions.
  *   workspace    device scratch of at least
  *                e2v2_build_neighbors_workspace_bytes(n, max_neighbors) bytes
  * Limits: 0 <= n < 2^31 - 1, cutoff > 0 finite, 0 <= K <= 4096, total entries

@@ -219,6 +219,24 @@ def test_isolated_atoms_and_padding(gpu_lib, storage):
         assert rel_err(out, ref["out"]) < tolerance(wl)
 
 
+@pytest.mark.parametrize("n,cutoff,lo,hi", [(300, 2.4, 1, 16), (500, 3.4, 17, 32), (900, 4.5, 33, 64),
+                                             (1600, 5.8, 65, 128), (2600, 7.4, 129, 256)])
+def test_list_length_classes_16_heads(gpu_lib, n, cutoff, lo, hi):
+    """16-bit storage with 16 heads of 8 channels streams four targets per wave over
+    the union of their lists, built by a sort whose width follows the longest of the
+    four lists (up to 16, 32, 64, 128 or 256 entries).  Each case puts the longest
+    list of the system in one of these classes; every target is compared with the
+    oracle, n is not a multiple of 4."""
+    side = (n / 0.1) ** (1.0 / 3.0)
+    wl = W.make_workload(W.LayerConfig("lists", n + 1, "uniform", 0.1, cutoff, 0, 2, 128, 16, 32, "bf16", 70 + n))
+    rows = O.neighbors(wl.pos, wl.cfg.cutoff)
+    longest = max(r.size for r in rows)
+    assert lo <= longest <= hi, (longest, side)
+    out, _ = _run(gpu_lib, wl, nbr=csr_from_rows(rows))
+    ref = O.layer_forward_workload(wl, rows=rows)
+    assert rel_err(out, ref["out"]) < tolerance(wl)
+
+
 def test_layer_deterministic(gpu_lib):
     wl = W.make_workload("c3", n=4000)
     a, _ = _run(gpu_lib, wl)
