@@ -398,16 +398,19 @@ def e2v2_layer_backward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_l
                         grad_h=None, workspace=None, stream=None,
                         target_order: torch.Tensor | None = None, grad_pos: torch.Tensor | None = None,
                         symmetric: bool = False, reuse_forward: bool = False):
-    """dL/dh for L = sum(grad_out * layer(pos, h)) (fp32 storage; any neighbour list).
+    """dL/dh for L = sum(grad_out * layer(pos, h)) (any neighbour list); h and the
+    projection weights in the storage dtype of desc, grad_out and the gradients fp32.
     With grad_pos (a [n, 3] fp32 device tensor) also dL/dpos; returns grad_h, or
     (grad_h, grad_pos) when grad_pos is given.  symmetric=True: the list is its own
     transpose (uncapped lists of e2v2_build_neighbors), so none is built.
-    reuse_forward=True: `workspace` holds what e2v2_attn_forward left in it for the
-    same inputs (pass the same tensor to both), so q, k, v, h' are not recomputed."""
+    reuse_forward=True (fp32 storage): `workspace` holds what e2v2_attn_forward left
+    in it for the same inputs (pass the same tensor to both), so q, k, v, h' are not
+    recomputed."""
     lib = load()
     n = pos.shape[0]
+    sdt = torch.bfloat16 if desc.storage == E2V2_BF16 else torch.float32
     _dev(pos, torch.float32, "pos")
-    _dev(h, torch.float32, "h")
+    _dev(h, sdt, "h")
     _dev(grad_out, torch.float32, "grad_out")
     if tuple(grad_out.shape) != tuple(h.shape):
         raise ValueError(f"grad_out shape {tuple(grad_out.shape)} != h shape {tuple(h.shape)}")
@@ -415,7 +418,7 @@ def e2v2_layer_backward(desc: LayerDesc, pos, h, weights: dict, nbr_start, nbr_l
         _dev(t, torch.int32, nm)
     if target_order is not None:
         _dev(target_order, torch.int32, "target_order")
-    w = _weights(weights, torch.float32)
+    w = _weights(weights, sdt)
     if grad_h is None:
         grad_h = torch.empty(h.shape, dtype=torch.float32, device=h.device)
     _dev(grad_h, torch.float32, "grad_h")
@@ -501,12 +504,13 @@ class StackRun:
 
     def e2v2_stack_backward(self, pos, h, grad_out, grad_h=None, grad_pos=None, stream=None):
         """dL/dh (and dL/dpos if grad_pos, a [n, 3] fp32 tensor, is given) of L = sum(grad_out * out)
-        for the output of the last e2v2_stack_forward call at (pos, h); fp32 storage."""
+        for the output of the last e2v2_stack_forward call at (pos, h); h in the storage
+        dtype, grad_out and the gradients fp32."""
         lib = load()
         if self.policy.rebuilds < 1:
             raise E2V2Error(E2V2_ERR_ARG, "e2v2_stack_backward: no e2v2_stack_forward call has filled the state")
         _dev(pos, torch.float32, "pos")
-        _dev(h, torch.float32, "h")
+        _dev(h, self.sdt, "h")
         _dev(grad_out, torch.float32, "grad_out")
         if grad_h is None:
             grad_h = torch.empty(h.shape, dtype=torch.float32, device=h.device)

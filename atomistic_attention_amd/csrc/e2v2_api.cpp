@@ -14,6 +14,7 @@
 //    harmonic evaluations.  The directions are picked from a Fibonacci sphere
 //    to keep Y^l(X) well conditioned.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <complex>
 #include <cstdarg>
@@ -459,6 +460,22 @@ const EaasCoef &eaas_table(int lmax)
         for (int l = 0; l <= kMaxL; ++l) eaas_for_lmax(l, g_by_lmax[l]);
     });
     return g_by_lmax[lmax];
+}
+
+int device_cus()
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cached[kMaxDev];    // 0: not yet asked
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < kMaxDev) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < kMaxDev) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 }  // namespace e2v2
@@ -1079,14 +1096,23 @@ int32_t e2v2_edge_coefficients(int32_t lmax, int32_t which, int32_t *idx, double
 namespace {
 // The forward workspace (q, k, v, h', frames) followed by the gradient buffers.
 struct BwdWs {
-    size_t fwd, gbuf, dhh, dm, mbuf, mx, rz, dd, dq, dk, tab, tcnt, tstart, tcur, tlen, tidx, total;
+    size_t fwd, gbuf, dhh, dm, mbuf, mx, rz, dd, dq, dk, tab, tcnt, tstart, tcur, tlen, tidx;
+    size_t xh, xq, xk, xv, xo;       // bf16 storage: h and W_Q, W_K, W_V, W_O widened to fp32
+    size_t total;
 };
+// The gradient runs in fp32 storage; for bf16 storage its inputs are widened first.
+e2v2_layer_desc fp32_desc(const e2v2_layer_desc &d)
+{
+    e2v2_layer_desc f = d;
+    f.storage = E2V2_FP32;
+    return f;
+}
 BwdWs bwd_ws(const e2v2_layer_desc &d, int n, long long max_entries)
 {
     const size_t N = (size_t)n, C = (size_t)d.channels, NC = (size_t)n_comp(d.lmax), H = (size_t)d.heads;
     BwdWs w{};
     size_t o = 0;
-    w.fwd = o; o += al256(attn_ws(d, n).total);
+    w.fwd = o; o += al256(attn_ws(fp32_desc(d), n).total);
     w.gbuf = o; o += al256(N * NC * C * 4);      // dL/dh'
     w.dhh = o; o += al256(N * NC * C * 4);       // dL/dhhat
     w.dm = o; o += al256(N * NC * C * 4);
@@ -1102,6 +1128,14 @@ BwdWs bwd_ws(const e2v2_layer_desc &d, int n, long long max_entries)
     w.tcur = o; o += al256((N + 1) * 4);
     w.tlen = o; o += al256(N * 4);
     w.tidx = o; o += al256((size_t)(max_entries > 0 ? max_entries : 1) * 4);
+    if (d.storage == E2V2_BF16) {
+        const size_t L1 = (size_t)d.lmax + 1;
+        w.xh = o; o += al256(N * NC * C * 4);
+        w.xq = o; o += al256(C * C * 4);
+        w.xk = o; o += al256(C * C * 4);
+        w.xv = o; o += al256(L1 * C * C * 4);
+        w.xo = o; o += al256(L1 * C * C * 4);
+    }
     w.total = o + 256;
     return w;
 }
@@ -1119,7 +1153,7 @@ size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t 
 
 // The layer gradient; pos_acc: add dL/dpos into grad_pos instead of writing it
 // (the layer stack sums it over its layers).
-static e2v2_status layer_bwd(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
+static e2v2_status layer_bwd(const e2v2_layer_desc *desc, const float *pos, const void *hin, const e2v2_weights *win,
                              const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
                              int64_t max_entries, int32_t symmetric, int32_t reuse_forward,
                              const int32_t *target_order, int32_t n, const float *grad_out, float *grad_h,
@@ -1129,16 +1163,19 @@ static e2v2_status layer_bwd(const e2v2_layer_desc *desc, const float *pos, cons
 {
     e2v2_status st = check_desc(desc);
     if (st != E2V2_OK) return st;
-    if (desc->storage != E2V2_FP32) return fail(E2V2_ERR_UNSUPPORTED, "the feature gradient needs fp32 storage");
+    const bool bf = desc->storage == E2V2_BF16;
+    if (bf && reuse_forward)
+        return fail(E2V2_ERR_UNSUPPORTED, "reuse_forward needs fp32 storage (a bf16 forward keeps h' in fp16)");
     if (n < 0) return fail(E2V2_ERR_ARG, "n < 0");
     if (max_entries < 0 || max_entries >= INT32_MAX) return fail(E2V2_ERR_ARG, "max_entries %lld out of range",
                                                                  (long long)max_entries);
     if (n == 0) return E2V2_OK;
-    if (!w) return fail(E2V2_ERR_ARG, "weights is NULL");
-    for (const void *p : {(const void *)pos, (const void *)h, (const void *)w->w_q, (const void *)w->w_k,
-                          (const void *)w->w_v, (const void *)w->w_o, (const void *)w->w_rbf, (const void *)w->w_src,
-                          (const void *)w->w_tgt, (const void *)nbr_start, (const void *)nbr_len, (const void *)nbr_idx,
-                          (const void *)grad_out, (const void *)grad_h, (const void *)workspace}) {
+    if (!win) return fail(E2V2_ERR_ARG, "weights is NULL");
+    for (const void *p : {(const void *)pos, hin, (const void *)win->w_q, (const void *)win->w_k,
+                          (const void *)win->w_v, (const void *)win->w_o, (const void *)win->w_rbf,
+                          (const void *)win->w_src, (const void *)win->w_tgt, (const void *)nbr_start,
+                          (const void *)nbr_len, (const void *)nbr_idx, (const void *)grad_out, (const void *)grad_h,
+                          (const void *)workspace}) {
         if (!p) return fail(E2V2_ERR_ARG, "NULL device pointer");
         if (!aligned16(p)) return fail(E2V2_ERR_ARG, "device pointers must be 16-byte aligned");
     }
@@ -1147,6 +1184,27 @@ static e2v2_status layer_bwd(const e2v2_layer_desc *desc, const float *pos, cons
     const BwdWs B = bwd_ws(*desc, n, max_entries);
     if (workspace_bytes < B.total) return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, B.total);
     char *ws = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+    // bf16 storage: the gradient of the same function in fp32 arithmetic, at the
+    // bf16 values of h and of W_Q, W_K, W_V, W_O, widened exactly.
+    const e2v2_layer_desc d32 = fp32_desc(*desc);
+    e2v2_weights w32 = *win;
+    const float *h = reinterpret_cast<const float *>(hin);
+    if (bf) {
+        const long long L1 = desc->lmax + 1, C2 = (long long)desc->channels * desc->channels;
+        float *xh = reinterpret_cast<float *>(ws + B.xh), *xq = reinterpret_cast<float *>(ws + B.xq);
+        float *xk = reinterpret_cast<float *>(ws + B.xk), *xv = reinterpret_cast<float *>(ws + B.xv);
+        float *xo = reinterpret_cast<float *>(ws + B.xo);
+        hipError_t e = launch_widen_bf16(hin, xh, (long long)n * n_comp(desc->lmax) * desc->channels, stream);
+        if (e == hipSuccess) e = launch_widen_bf16(win->w_q, xq, C2, stream);
+        if (e == hipSuccess) e = launch_widen_bf16(win->w_k, xk, C2, stream);
+        if (e == hipSuccess) e = launch_widen_bf16(win->w_v, xv, L1 * C2, stream);
+        if (e == hipSuccess) e = launch_widen_bf16(win->w_o, xo, L1 * C2, stream);
+        if (e != hipSuccess) return hip_fail(e, "widening the bf16 inputs");
+        h = xh;
+        w32.w_q = xq; w32.w_k = xk; w32.w_v = xv; w32.w_o = xo;
+    }
+    desc = &d32;
+    const e2v2_weights *w = &w32;
     const AttnWs F = attn_ws(*desc, n);
     // Steps 2-3 of the forward pass: q, k, v, h' and the per-node frames -- or, with
     // reuse_forward, those a forward call with the same arguments left at the
@@ -1243,7 +1301,7 @@ static e2v2_status layer_bwd(const e2v2_layer_desc *desc, const float *pos, cons
     return E2V2_OK;
 }
 
-e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h, const e2v2_weights *w,
+e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const void *h, const e2v2_weights *w,
                                 const int32_t *nbr_start, const int32_t *nbr_len, const int32_t *nbr_idx,
                                 int64_t max_entries, int32_t symmetric, int32_t reuse_forward,
                                 const int32_t *target_order, int32_t n,
@@ -1542,14 +1600,13 @@ size_t e2v2_stack_backward_workspace_bytes(int32_t n_layers, const e2v2_layer_de
 }
 
 e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, const e2v2_weights *weights,
-                                const float *pos, const float *h, int32_t n, int32_t K, const void *state,
+                                const float *pos, const void *h, int32_t n, int32_t K, const void *state,
                                 size_t state_bytes, const e2v2_rebuild_policy *policy, const float *grad_out,
                                 float *grad_h, float *grad_pos, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream)
 {
     e2v2_status st = check_stack(n_layers, descs, weights, n, K);
     if (st != E2V2_OK) return st;
-    if (descs[0].storage != E2V2_FP32) return fail(E2V2_ERR_UNSUPPORTED, "the stack gradient needs fp32 storage");
     if (!weights) return fail(E2V2_ERR_ARG, "weights is NULL");
     // the state holds lists only once a forward call has built them
     if (!policy) return fail(E2V2_ERR_ARG, "policy is NULL");
@@ -1576,13 +1633,17 @@ e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, 
         return reinterpret_cast<const int32_t *>(sb + S.lists + (size_t)k * S.per_list + S.len_off);
     };
     // 1. the layers' inputs, recomputed over the lists of the last e2v2_stack_forward
-    const float *x[kMaxStackLayers];
+    //    (in the storage dtype, as the forward passed them on: the gradient takes the
+    //    bf16 rounding between layers as the identity)
+    const bool bf = descs[0].storage == E2V2_BF16;
+    const void *x[kMaxStackLayers];
     x[0] = h;
     for (int l = 0; l + 1 < n_layers; ++l) {
         const int k = cutoff_index(S.ncut, S.cut, descs[l].cutoff);
-        float *xo = reinterpret_cast<float *>(wb + W.x + (size_t)l * W.per_x);
-        st = attn_run(&descs[l], pos, x[l], &weights[l], start, list_len(k), list_idx(k), order, n, xo, wb + W.bws,
-                      W.bws_bytes, nullptr, stream, true, true);
+        char *xo = wb + W.x + (size_t)l * W.per_x;
+        st = attn_run(&descs[l], pos, x[l], &weights[l], start, list_len(k), list_idx(k), order, n,
+                      bf ? nullptr : reinterpret_cast<float *>(xo), wb + W.bws, W.bws_bytes, nullptr, stream, true,
+                      true, bf ? reinterpret_cast<uint16_t *>(xo) : nullptr);
         if (st != E2V2_OK) return st;
         x[l + 1] = xo;
     }

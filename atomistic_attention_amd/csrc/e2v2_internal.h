@@ -387,6 +387,9 @@ __host__ __device__ inline int hp_quad_offset(int e, int ch, int NC)
     const int a = 4 * (ch >> 3) + (ch & 3), f = (ch >> 2) & 1;
     return e < d1 ? a * 2 * d1 + 2 * e + f : 128 * d1 + a * 2 * d2 + 2 * (e - d1) + f;
 }
+// Compute units of the current device (cached per device; 256 if the query fails):
+// grid caps of the kernels that loop over tiles.
+int device_cus();
 // Four targets per wave with the weighted sums on the matrix cores (attn_quad.hip):
 // 16-bit storage, l_max <= 2, 16 heads of 8 channels, n < attn_quad_max_atoms(L).
 // Whenever it applies, the projection kernel writes h' in hp_quad_offset layout.
@@ -499,6 +502,8 @@ struct ProjJob {
 };
 // fp32 projections (fp32 storage).
 hipError_t launch_proj(const ProjJob *jobs, int njobs, int n, int C, hipStream_t stream);
+// count bf16 values (16-byte aligned) widened to fp32, exactly.
+hipError_t launch_widen_bf16(const void *in, float *out, long long count, hipStream_t stream);
 // bf16 weights W [C][C] (in, out) packed into v_mfma_f32_16x16x32_bf16 A fragments.
 hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, int count, int C, hipStream_t stream);
 

@@ -136,6 +136,31 @@ hipError_t launch_pack_weights(const uint16_t *const *w, uint16_t *const *out, i
     return hipGetLastError();
 }
 
+// bf16 -> fp32 (exact), 8 values per thread where the count allows, grid-stride.
+__global__ __launch_bounds__(256) void k_widen_bf16(const uint16_t *__restrict__ in, float *__restrict__ out, long long count)
+{
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    const long long n8 = count >> 3;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+        const uint4 v = reinterpret_cast<const uint4 *>(in)[i];
+        float4 *o = reinterpret_cast<float4 *>(out) + 2 * i;
+        o[0] = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+        o[1] = make_float4(bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w));
+    }
+    for (long long i = 8 * n8 + (long long)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+        out[i] = bf16_to_f(in[i]);
+}
+
+hipError_t launch_widen_bf16(const void *in, float *out, long long count, hipStream_t stream)
+{
+    if (count <= 0) return hipSuccess;
+    long long blocks = ((count >> 3) + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    k_widen_bf16<<<dim3((unsigned)blocks), 256, 0, stream>>>(reinterpret_cast<const uint16_t *>(in), out, count);
+    return hipGetLastError();
+}
+
 hipError_t launch_proj(const ProjJob *jobs, int njobs, int n, int C, hipStream_t stream)
 {
     if (n <= 0 || njobs <= 0) return hipSuccess;

@@ -259,8 +259,14 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
  * has no direction; its encoding is held constant there.  For a potential
  * energy E = L the forces are -grad_pos.
  *
- * Storage must be fp32 (E2V2_ERR_UNSUPPORTED otherwise); pos fp32 [n][3], h and
- * grad_out fp32 [n][(lmax+1)^2][C], grad_h fp32 [n][(lmax+1)^2][C] (written whole).
+ * pos fp32 [n][3]; h [n][(lmax+1)^2][C] in the storage dtype; grad_out fp32
+ * [n][(lmax+1)^2][C]; grad_h fp32 [n][(lmax+1)^2][C] (written whole).  With bf16
+ * storage the result is the gradient of the same layer function in fp32
+ * arithmetic at the bf16 values of h, W_Q, W_K, W_V and W_O (widened exactly in
+ * the workspace): the fp16 storage of h' and m inside the forward kernels is
+ * rounding of one evaluation, not part of the function, and is not
+ * differentiated (forces at the benched storage: the inputs and weights are the
+ * bf16 ones, the arithmetic is fp32).
  * The neighbour list has the layout of e2v2_attn_forward (CSR or K-capped with
  * -1 padding; any list, symmetric or not).  Each source's gradient is gathered
  * over the targets that read it, so no result is written by atomics (FlashSchNet
@@ -284,13 +290,14 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
  * e2v2_attn_prepare) last ran with the same desc, pos, h, weights and n on this
  * same workspace pointer (its layout is the first e2v2_attn_workspace_bytes of
  * the gradient's workspace), as a training step does when it keeps the forward's
- * intermediates.
+ * intermediates; fp32 storage only (a bf16 forward keeps h' in fp16).
  * All device pointers 16-byte aligned; asynchronous on `stream`.  Errors:
  * E2V2_ERR_ARG (NULL or misaligned pointer, small workspace, n < 0, max_entries
  * outside 0 .. 2^31 - 2),
- * E2V2_ERR_UNSUPPORTED (storage, head shape), E2V2_ERR_HIP (launch failure). */
+ * E2V2_ERR_UNSUPPORTED (head shape, reuse_forward with bf16 storage),
+ * E2V2_ERR_HIP (launch failure). */
 size_t e2v2_layer_backward_workspace_bytes(const e2v2_layer_desc *desc, int32_t n, int64_t max_entries);
-e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const float *h,
+e2v2_status e2v2_layer_backward(const e2v2_layer_desc *desc, const float *pos, const void *h,
                                 const e2v2_weights *w, const int32_t *nbr_start, const int32_t *nbr_len,
                                 const int32_t *nbr_idx, int64_t max_entries, int32_t symmetric,
                                 int32_t reuse_forward, const int32_t *target_order, int32_t n,
@@ -372,15 +379,17 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
                                e2v2_rebuild_policy *policy, void *state, size_t state_bytes, float *out,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Gradient of the layer stack (fp32 storage): for L = sum(grad_out * out), with
+/* Gradient of the layer stack: for L = sum(grad_out * out), with
  * out the stack output of the last e2v2_stack_forward call at these positions and
  * features, writes grad_h = dL/dh [n][(lmax+1)^2][C] and, if grad_pos is not
  * NULL, grad_pos = dL/dpos [n][3] summed over the layers (the forces of the model
  * for E = L are -grad_pos).  The neighbour lists and the processing order are
  * those in `state` (left by that forward call), held fixed; each layer's input is
  * recomputed over them, then each layer's gradient (e2v2_layer_backward, over its
- * transposed list) runs in reverse order.  Arguments as for e2v2_stack_forward;
- * every layer must have fp32 storage (E2V2_ERR_UNSUPPORTED otherwise).  `policy`
+ * transposed list) runs in reverse order.  Arguments as for e2v2_stack_forward.
+ * With bf16 storage each layer's gradient is taken as in e2v2_layer_backward (fp32
+ * arithmetic at the bf16 inputs and weights) and the rounding of a layer's output
+ * to the next layer's bf16 input passes the gradient through unchanged.  `policy`
  * is the host policy that forward call updated: with no rebuild recorded
  * (rebuilds < 1) the state holds no lists yet, and the call returns E2V2_ERR_ARG
  * before anything is enqueued.  Workspace: e2v2_stack_backward_workspace_bytes
@@ -388,7 +397,7 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
 size_t e2v2_stack_backward_workspace_bytes(int32_t n_layers, const e2v2_layer_desc *descs, int32_t n,
                                            int32_t max_neighbors);
 e2v2_status e2v2_stack_backward(int32_t n_layers, const e2v2_layer_desc *descs, const e2v2_weights *weights,
-                                const float *pos, const float *h, int32_t n, int32_t max_neighbors,
+                                const float *pos, const void *h, int32_t n, int32_t max_neighbors,
                                 const void *state, size_t state_bytes, const e2v2_rebuild_policy *policy,
                                 const float *grad_out, float *grad_h, float *grad_pos, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);

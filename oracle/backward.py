@@ -21,6 +21,13 @@ B3  L(pos, h) as in B1 with the positions free as well: dL/dpos through the
     crossing the cutoff sees no jump in either.  At a
     zero position vector the direction is undefined: its encoding is held
     constant, so that atom's position receives only the bias terms.
+
+B4  A stack of layers (each the B3 function of the previous output) with the
+    lists held fixed; for bf16 storage the outputs between layers are rounded to
+    bf16 as stack.stack_step does and the rounding passes the gradient through
+    unchanged (a step function has no useful derivative; this is the reading the
+    GPU stack gradient follows).  Pinned against the chain rule written out with
+    separate per-layer gradients.
 """
 from __future__ import annotations
 
@@ -29,7 +36,7 @@ import math
 import numpy as np
 import torch
 
-from . import layer, so3
+from . import layer, so3, stack
 
 __all__ = ["layer_forward_torch", "grad_h", "grad_pos_h", "stack_grad_pos_h", "real_sh_torch", "rbf_bias_torch"]
 
@@ -145,18 +152,25 @@ def grad_h(pos, h, w_q, w_k, w_v, w_o, w_rbf, w_src, w_tgt, g, *, lmax: int, hea
     return ht.grad.numpy()
 
 
-def stack_grad_pos_h(pos, h0, layers, rows_by_cutoff, g):
+def stack_grad_pos_h(pos, h0, layers, rows_by_cutoff, g, round_between: bool = False):
     """B4: (dL/dpos, dL/dh0) for L = sum(g * out) of a layer stack: layer l + 1 takes
-    layer l's output (the composition of stack.stack_step, without the rounding
-    between layers: the derivative of the real-valued composition), each layer on
-    the rows of its cutoff, the lists held fixed.  ``layers``: Workload-like weight
-    sets with a cfg (lmax, heads, cutoff); ``rows_by_cutoff``: {fp32 cutoff: rows}."""
+    layer l's output (the composition of stack.stack_step), each layer on the rows
+    of its cutoff, the lists held fixed.  ``layers``: Workload-like weight sets with
+    a cfg (lmax, heads, cutoff); ``rows_by_cutoff``: {fp32 cutoff: rows}.
+    round_between = False: the real-valued composition, no rounding between layers.
+    round_between = True (bf16 storage): each non-final output is rounded to bf16
+    before it feeds the next layer, as in stack.stack_step, and the rounding passes
+    the gradient through unchanged (its derivative taken as the identity), so every
+    layer is differentiated at the input it actually receives."""
     pt = torch.tensor(np.asarray(pos, dtype=np.float64), requires_grad=True)
     ht = torch.tensor(np.asarray(h0, dtype=np.float64), requires_grad=True)
     x = ht
-    for wl in layers:
+    for li, wl in enumerate(layers):
         c = wl.cfg
         rows = rows_by_cutoff[float(np.float32(c.cutoff))]
+        if round_between and li > 0:
+            xr = torch.as_tensor(stack._round_bf16(x.detach().numpy()))
+            x = x + (xr - x).detach()
         x = layer_forward_torch(pt, x, wl.w_q, wl.w_k, wl.w_v, wl.w_o, wl.w_rbf, wl.w_src, wl.w_tgt, lmax=c.lmax,
                                 heads=c.heads, cutoff=c.cutoff, rows=rows)
     (x * torch.as_tensor(np.asarray(g, dtype=np.float64))).sum().backward()

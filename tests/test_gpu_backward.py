@@ -35,7 +35,7 @@ def _gpu_grad(gpu_lib, wl, g, order=None, pos_grad=False, K=0, rows=None, symmet
         s, ln, ix = csr_from_rows(rows)
     else:
         s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, K)
-    desc = gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
+    desc = gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, d["dtype"])
     print(f"backward {c.name} n={c.n} L={c.lmax} H={c.heads} pos={pos_grad}", flush=True)
     gp = torch.full((c.n, 3), float("nan"), dtype=torch.float32, device="cuda") if pos_grad else None
     r = gpu_lib.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, f32(g), target_order=order,
@@ -83,6 +83,40 @@ def test_position_gradient_full_fp32(gpu_lib, name):
     record(f"position_gradient[{name}]", grad_pos=ep, grad_h=eh)
     assert np.array_equal(gh, gh0)
     assert ep < TOL and eh < TOL, (ep, eh)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_backward_bf16_storage(gpu_lib, name):
+    """bf16 storage (E2Former-V2 explainer, section 4.2: forces as the gradient of
+    the energy, here at the benched storage): h and W_Q, W_K, W_V, W_O are bf16,
+    the gradient is that of the layer in fp32 arithmetic at those values, so it
+    meets the fp32 bar against the oracle evaluated at the same bf16 values; dL/dh
+    is bit-identical with and without dL/dpos."""
+    import dataclasses
+    wl = W.make_workload(dataclasses.replace(W.CONFIGS[name], storage="bf16"))
+    g = _g(wl)
+    gh, gp, _ = _gpu_grad(gpu_lib, wl, g, pos_grad=True)
+    gh0, _ = _gpu_grad(gpu_lib, wl, g)
+    rp, rh = _oracle_pos(wl, g)
+    ep, eh = rel_err(gp, rp), rel_err(gh, rh)
+    record(f"backward_bf16[{name}]", grad_pos=ep, grad_h=eh)
+    assert np.array_equal(gh, gh0)
+    assert ep < TOL and eh < TOL, (ep, eh)
+
+
+def test_backward_bf16_storage_refuses_reuse_forward(gpu_lib):
+    """A bf16 forward keeps h' in fp16, so its workspace cannot feed the gradient."""
+    import dataclasses
+    wl = W.make_workload(dataclasses.replace(W.CONFIGS["c1"], storage="bf16"), n=64)
+    c = wl.cfg
+    d = upload(wl)
+    s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, 0)
+    desc = gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, d["dtype"])
+    ws = torch.empty(gpu_lib.backward_workspace_bytes(desc, c.n, ix.numel()), dtype=torch.uint8, device="cuda")
+    with pytest.raises(gpu_lib.E2V2Error) as ei:
+        gpu_lib.e2v2_layer_backward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, f32(_g(wl)), workspace=ws,
+                                    reuse_forward=True)
+    assert ei.value.status == gpu_lib.E2V2_ERR_UNSUPPORTED
 
 
 def _edge(n, L, heads, seed, nrbf=10):

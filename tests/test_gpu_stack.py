@@ -150,6 +150,40 @@ def test_stack_gradient_matches_oracle(gpu_lib, K):
     assert eh < 1e-4 and ep < 1e-4, (eh, ep)
 
 
+def test_stack_gradient_bf16_storage(gpu_lib):
+    """The four-layer stack at bf16 storage (s2's layers: 5 A, 5 A, 5 A, 8 A, 16 heads,
+    l_max = 2), 300 atoms: dL/dh and dL/dpos against the oracle's stack gradient with
+    the outputs rounded to bf16 between layers and the rounding passing the gradient
+    through (B4).  Each layer's gradient is fp32 arithmetic at bf16 values; the
+    inputs of layers 2-4 are the GPU forward's own bf16 outputs, whose 16-bit
+    intermediates move about one element in eight by one bf16 step against the
+    oracle's rounded outputs, so the bar is the bf16-storage bar of the layer
+    output, 2e-2 of the RMS."""
+    import dataclasses
+    from oracle import backward as OB
+    cfg = dataclasses.replace(W.STACKS["s2"], n=300, steps=1)
+    st = W.make_stack(cfg)
+    descs, weights = [], []
+    for wl in st.layers:
+        c = wl.cfg
+        descs.append(gpu_lib.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.bfloat16))
+        weights.append(W.device_arrays(wl)["weights"])
+    run = gpu_lib.StackRun(descs, weights, cfg.n, cfg.max_neighbors)
+    pos = f32(st.traj[0])
+    h = to_storage(st.h0, torch.bfloat16)
+    print(f"stack gradient bf16 n={cfg.n}", flush=True)
+    run.e2v2_stack_forward(pos, h)
+    g = np.random.default_rng(32).standard_normal(st.h0.shape).astype(np.float32).astype(np.float64)
+    gh, gp = run.e2v2_stack_backward(pos, h, f32(g), grad_pos=torch.empty((cfg.n, 3), device="cuda"))
+    torch.cuda.synchronize()
+    state = OS.StackState([wl.cfg.cutoff for wl in st.layers], cfg.max_neighbors)
+    state.rebuild(st.traj[0], 0)
+    rp, rh = OB.stack_grad_pos_h(st.traj[0], st.h0, st.layers, state.rows, g, round_between=True)
+    eh, ep = rel_err(gh.cpu().numpy(), rh), rel_err(gp.cpu().numpy(), rp)
+    record(f"stack_gradient_bf16[s2,n={cfg.n}]", grad_h=eh, grad_pos=ep)
+    assert eh < 2e-2 and ep < 2e-2, (eh, ep)
+
+
 def _far_pairs(pos, rows, cutoff):
     """Listed pairs at or beyond ``cutoff`` (fp64 distances of the fp32 positions)."""
     n = 0

@@ -215,18 +215,26 @@ def test_stack_argument_errors(lib):
     assert lib.e2v2_stack_state_bytes(2, two, 1000, 64) - lib.e2v2_stack_state_bytes(2, one, 1000, 64) >= 1000 * 65 * 4
 
 
-def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE, gpos=None, entries=100):
+def _bwd(lib, desc, n=10, ws_bytes=None, ptr=FAKE, gpos=None, entries=100, reuse=0):
     w = B.Weights(*([ptr] * 7))
     wsb = ws_bytes if ws_bytes is not None else lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(desc),
                                                                                        max(n, 0), entries)
-    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, entries, 0, 0,
+    return lib.e2v2_layer_backward(ctypes.byref(desc), ptr, ptr, ctypes.byref(w), ptr, ptr, ptr, entries, 0, reuse,
                                    None, n, ptr, ptr, gpos, ptr, wsb, None)
 
 
 def test_backward_argument_errors_and_workspace(lib):
     d32 = _desc(storage=B.E2V2_FP32)
-    assert _bwd(lib, _desc()) == B.E2V2_ERR_UNSUPPORTED                 # bf16 storage
+    # bf16 storage: a bf16 forward keeps h' in fp16, so its workspace cannot be reused
+    assert _bwd(lib, _desc(), reuse=1) == B.E2V2_ERR_UNSUPPORTED
     assert "fp32" in lib.e2v2_last_error().decode()
+    assert _bwd(lib, _desc(), ws_bytes=100) == B.E2V2_ERR_ARG
+    # bf16 storage widens h (n x 9 x 128 fp32) and W_Q, W_K, W_V[0..2], W_O[0..2] (8 x 128 x 128 fp32)
+    # into the workspace of the fp32 gradient
+    for n in (1000, 2000):
+        extra = (lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(_desc()), n, 0)
+                 - lib.e2v2_layer_backward_workspace_bytes(ctypes.byref(d32), n, 0))
+        assert abs(extra - (n * 9 * 128 * 4 + 8 * 128 * 128 * 4)) <= 5 * 256
     assert _bwd(lib, _desc(storage=B.E2V2_FP32, channels=256)) == B.E2V2_ERR_UNSUPPORTED
     assert _bwd(lib, d32, n=-1) == B.E2V2_ERR_ARG
     assert _bwd(lib, d32, ptr=None) == B.E2V2_ERR_ARG
@@ -252,9 +260,9 @@ def test_stack_backward_argument_errors(lib):
     descs = (B.LayerDesc * 2)(_desc(), _desc())                        # bf16 storage
     w = (B.Weights * 2)(B.Weights(*([FAKE] * 7)), B.Weights(*([FAKE] * 7)))
     pol = ctypes.byref(B.RebuildPolicy(10, 0.25, 1, 1, 1))            # as left by one forward call
-    st = lib.e2v2_stack_backward(2, descs, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, pol, FAKE, FAKE, None, FAKE, 1 << 30,
+    st = lib.e2v2_stack_backward(2, descs, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, pol, FAKE, FAKE, None, FAKE, 100,
                                  None)
-    assert st == B.E2V2_ERR_UNSUPPORTED
+    assert st == B.E2V2_ERR_ARG and "workspace" in lib.e2v2_last_error().decode()
     d32 = (B.LayerDesc * 2)(_desc(storage=B.E2V2_FP32), _desc(storage=B.E2V2_FP32, cutoff=8.0))
     st = lib.e2v2_stack_backward(2, d32, w, FAKE, FAKE, 10, 8, FAKE, 1 << 20, pol, FAKE, FAKE, FAKE_MIS, FAKE,
                                  1 << 30, None)

@@ -252,3 +252,35 @@ def test_stack_gradient_matches_central_differences():
     v = rng.standard_normal(pos.shape)
     fd = (L(pos + eps * v, h0) - L(pos - eps * v, h0)) / (2 * eps)
     assert abs(fd - np.sum(gp * v)) <= 2e-6 * max(1.0, abs(fd)), (fd, np.sum(gp * v))
+
+
+def test_stack_gradient_with_bf16_rounding_between_layers_is_the_chain_rule():
+    """B4 with bf16 storage: the stack gradient with rounding between layers equals
+    the chain rule written out with separate one-layer gradients -- the second
+    layer's vector-Jacobian product at the rounded first output (B3), then the
+    first layer's at h0 with that result -- and the rounding changes the gradient
+    (it is not silently skipped)."""
+    import dataclasses
+    import torch
+    from atomistic_attention_amd import workloads as W
+    from oracle import stack as OS
+    cfg = dataclasses.replace(W.STACKS["s1"], n=40, steps=1, cutoffs=(5.0, 8.0), max_neighbors=0)
+    st = W.make_stack(cfg)
+    pos, h0 = st.traj[0], st.h0
+    state = OS.StackState([wl.cfg.cutoff for wl in st.layers], 0)
+    state.rebuild(pos, 0)
+    rows = lambda wl: state.rows[float(np.float32(wl.cfg.cutoff))]
+    g = np.random.default_rng(22).standard_normal(h0.shape)
+    gp, gh = backward.stack_grad_pos_h(pos, h0, st.layers, state.rows, g, round_between=True)
+    gp0, gh0 = backward.stack_grad_pos_h(pos, h0, st.layers, state.rows, g)
+    l1, l2 = st.layers
+    kw = lambda wl: dict(w_q=wl.w_q, w_k=wl.w_k, w_v=wl.w_v, w_o=wl.w_o, w_rbf=wl.w_rbf, w_src=wl.w_src,
+                         w_tgt=wl.w_tgt, lmax=wl.cfg.lmax, heads=wl.cfg.heads, cutoff=wl.cfg.cutoff, rows=rows(wl))
+    x1 = layer.layer_forward(pos, h0, **kw(l1))["out"]
+    x1r = OS._round_bf16(x1)
+    assert np.max(np.abs(x1r - x1)) > 0
+    p2, d1 = backward.grad_pos_h(pos, x1r, g=g, **kw(l2))              # layer 2 at its rounded input
+    p1, d0 = backward.grad_pos_h(pos, h0, g=d1, **kw(l1))              # layer 1 with layer 2's dL/dx1
+    assert np.max(np.abs(gh - d0)) <= 1e-10 * np.max(np.abs(d0))
+    assert np.max(np.abs(gp - (p1 + p2))) <= 1e-10 * np.max(np.abs(p1 + p2))
+    assert np.max(np.abs(gh - gh0)) > 1e-6 * np.max(np.abs(gh0))
