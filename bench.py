@@ -396,6 +396,33 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
             fn()
         torch.cuda.synchronize()
         res[key] = (time.perf_counter() - t0) * 1e3 / 5
+    # forces at the benched configuration: the 32,768-atom, 8 A, K = 256 layer with
+    # bf16 storage (gradient in fp32 arithmetic at the bf16 inputs and weights; the
+    # capped list is not symmetric, so the call builds its transpose)
+    wb = W.make_workload("c4")
+    cb = wb.cfg
+    db = W.device_arrays(wb)
+    descb = B.make_desc(cb.lmax, cb.channels, cb.heads, cb.n_rbf, cb.cutoff, db["dtype"])
+    ob = torch.empty(cb.n, dtype=torch.int32, device=dev)
+    sb_, lb_, ib_, nnzb = B.e2v2_build_neighbors(db["pos"], cb.cutoff, cb.max_neighbors, order_out=ob)
+    gb = torch.from_numpy(np.random.default_rng(12).standard_normal(wb.h.shape).astype(np.float32)).to(dev)
+    ghb, gpb = torch.empty_like(gb), torch.empty((cb.n, 3), dtype=torch.float32, device=dev)
+    outb = torch.empty_like(gb)
+    bwsb = torch.empty(B.backward_workspace_bytes(descb, cb.n, ib_.numel()), dtype=torch.uint8, device=dev)
+    fwsb = torch.empty(B.attn_workspace_bytes(descb, cb.n), dtype=torch.uint8, device=dev)
+    for key, fn in (("c4_gradients", lambda: B.e2v2_layer_backward(descb, db["pos"], db["h"], db["weights"], sb_, lb_,
+                                                                    ib_, gb, grad_h=ghb, workspace=bwsb,
+                                                                    target_order=ob, grad_pos=gpb)),
+                    ("c4_forward", lambda: B.e2v2_attn_forward(descb, db["pos"], db["h"], db["weights"], sb_, lb_, ib_,
+                                                               out=outb, workspace=fwsb, target_order=ob))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        res[key] = (time.perf_counter() - t0) * 1e3 / 5
     nnz = int(nnz)
     C, nc, H = c.channels, c.n_comp, c.heads
     # attention adjoint, algorithmic bytes: target pass per pair k_j, h'_j, position,
@@ -417,6 +444,11 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
                                     "filtered from it), fp32 storage, same system, lists reused",
                            "ms_model_step_forward": res["stack_forward"],
                            "ms_gradients_dh_dpos": res["stack_gradients"]},
+            "benched_config_bf16": {"workload": f"c4: {cb.n} atoms, cutoff {cb.cutoff} A, cap K={cb.max_neighbors}, "
+                                                f"bf16 storage", "nnz": int(nnzb),
+                                    "what": "dL/dh and dL/dpos (the forces for E = sum(g * out)) in fp32 arithmetic "
+                                            "at the bf16 inputs and weights, transposed list built in the call",
+                                    "ms_gradients_dh_dpos": res["c4_gradients"], "ms_forward": res["c4_forward"]},
             "pairs_per_s_backward": nnz / (res["backward"] * 1e-3),
             "pairs_per_s_backward_with_positions": nnz / (res["backward_pos"] * 1e-3),
             "attention_adjoint_algorithmic_bytes": per_pair * nnz + per_node * c.n}
