@@ -223,14 +223,14 @@ def per_config(B, W, torch, name: str, steps: int = 20) -> dict:
     return rec
 
 
-def xcd_slot_ranges(n: int):
-    """The contiguous runs of processing slots that the pair kernel's XCD-aware
-    workgroup mapping gives each of the 8 XCDs (blocks of 4 waves, 2 targets a wave)."""
-    nb = (n + 7) // 8
+def xcd_slot_ranges(n: int, per_block: int = 16):
+    """The contiguous runs of processing slots that the streaming kernel's XCD-aware
+    workgroup mapping gives each of the 8 XCDs (blocks of 4 waves, 4 targets a wave)."""
+    nb = (n + per_block - 1) // per_block
     out, b0 = [], 0
     for x in range(8):
         cnt = (nb >> 3) + (1 if x < (nb & 7) else 0)
-        out.append((min(n, 8 * b0), min(n, 8 * (b0 + cnt))))
+        out.append((min(n, per_block * b0), min(n, per_block * (b0 + cnt))))
         b0 += cnt
     return out
 
@@ -240,8 +240,8 @@ def load_balance(B, W, torch, wl, d, desc, s, ln, ix, order, reps: int = 10) -> 
     each XCD's run of processing slots holds (max over mean; the XCDs run their runs
     side by side).  Measured: the aggregation run on the targets of the dense blocks
     only and of the sparse blocks only, against all targets, each timed with HIP
-    events; the kept targets go two by two (consecutive in the processing order, as
-    the kernel pairs them) to wave slots spread evenly over the launch, the other
+    events; the kept targets go four by four (consecutive in the processing order, as
+    the kernel groups them) to wave slots spread evenly over the launch, the other
     slots are -1 and their waves exit at once.  Per-target time and row length show
     what a dense region costs; the Tessera article reports 13-33 % slower steps for
     its dense capsid than for its salt solution of similar size."""
@@ -259,11 +259,14 @@ def load_balance(B, W, torch, wl, d, desc, s, ln, ix, order, reps: int = 10) -> 
            "xcd_max_over_mean": max(runs) / (sum(runs) / len(runs))}
     for key, sel in (("all", np.ones(c.n, bool)), ("dense", dense), ("sparse", ~dense)):
         kept = o[sel[o]].astype(np.int32)                     # kept targets in processing order
-        npair_slots, npairs = c.n // 2, (kept.size + 1) // 2
+        nquad_slots, nquads = c.n // 4, (kept.size + 3) // 4
         oo = np.full(c.n, -1, np.int32)
-        w = (np.arange(npairs, dtype=np.int64) * npair_slots) // npairs
-        oo[2 * w] = kept[0::2]
-        oo[2 * w[: kept.size // 2] + 1] = kept[1::2]
+        w = np.arange(nquads, dtype=np.int64)
+        if nquads <= nquad_slots:                             # spread; else packed (n not a multiple of 4)
+            w = (w * nquad_slots) // nquads
+        for i in range(4):
+            part = kept[i::4]
+            oo[4 * w[: part.size] + i] = part
         ot = torch.from_numpy(oo).to(dev)
         times = []
         for k in range(reps + 2):
@@ -280,7 +283,7 @@ def load_balance(B, W, torch, wl, d, desc, s, ln, ix, order, reps: int = 10) -> 
                     "ms": ms, "us_per_target": ms * 1e3 / nt, "ns_per_pair": ms * 1e6 / max(int(lens[sel].sum()), 1)}
     res["dense_vs_sparse_per_target"] = res["dense"]["us_per_target"] / res["sparse"]["us_per_target"]
     res["what"] = ("aggregation (attention + target coupling + output projection) over the dense blocks' targets "
-                   "only, the sparse blocks' only, and all, with the kept target pairs spread evenly over the "
+                   "only, the sparse blocks' only, and all, with the kept target quads spread evenly over the "
                    "wave slots; xcd_entries: list entries in each XCD's run of the processing order")
     return res
 
