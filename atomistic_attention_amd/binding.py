@@ -25,7 +25,8 @@ EXPORTS = [
     "e2v2_last_error", "e2v2_filter_neighbors", "e2v2_max_displacement2", "e2v2_stack_state_bytes",
     "e2v2_stack_workspace_bytes", "e2v2_stack_forward", "e2v2_layer_backward_workspace_bytes",
     "e2v2_layer_backward", "e2v2_stack_backward_workspace_bytes", "e2v2_stack_backward", "e2v2_attn_forward_noalloc",
-    "e2v2_edge_forward", "e2v2_edge_workspace_bytes", "e2v2_edge_coefficients",
+    "e2v2_edge_forward", "e2v2_edge_workspace_bytes", "e2v2_edge_coefficients", "e2v2_target_order",
+    "e2v2_target_order_workspace_bytes",
 ]
 
 
@@ -73,6 +74,10 @@ def load(path: str = LIB_PATH):
     lib.e2v2_build_neighbors.restype = ctypes.c_int
     lib.e2v2_build_neighbors_workspace_bytes.argtypes = [i32, i32]
     lib.e2v2_build_neighbors_workspace_bytes.restype = sz
+    lib.e2v2_target_order.argtypes = [vp, i32, vp, vp, sz, vp]
+    lib.e2v2_target_order.restype = ctypes.c_int
+    lib.e2v2_target_order_workspace_bytes.argtypes = [i32]
+    lib.e2v2_target_order_workspace_bytes.restype = sz
     lib.e2v2_eaas_couple.argtypes = [vp, vp, ctypes.c_int, vp, i32, i32, i32, vp, ctypes.c_int, vp]
     lib.e2v2_eaas_couple.restype = ctypes.c_int
     lib.e2v2_attn_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.POINTER(Weights), vp, vp, vp, vp,
@@ -236,6 +241,22 @@ def e2v2_build_neighbors(pos: torch.Tensor, cutoff: float, max_neighbors: int = 
     if max_neighbors == 0:
         idx = idx[:int(nnz.value)]
     return start, length, idx, int(nnz.value)
+
+
+def e2v2_target_order(pos: torch.Tensor, order: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Hilbert-curve processing order of pos [n, 3] fp32 (device) as an int32 [n]
+    device tensor (written into `order` when given)."""
+    lib = load()
+    _dev(pos, torch.float32, "pos")
+    n = pos.shape[0]
+    if order is None:
+        order = torch.empty(n, dtype=torch.int32, device=pos.device)
+    wsb = int(lib.e2v2_target_order_workspace_bytes(n))
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=pos.device)
+    _check(lib.e2v2_target_order(_ptr(pos), n, _ptr(order), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return order
 
 
 def e2v2_eaas_couple(pos: torch.Tensor, x: torch.Tensor, path_w: torch.Tensor, lmax: int,

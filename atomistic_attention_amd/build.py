@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libe2v2.so")
 SOURCES = ["e2v2_api.cpp", "eaas.hip", "proj.hip", "qkv_eaas.hip", "eaas_outproj.hip", "attn.hip", "attn_pair.hip", "attn_quad.hip",
-           "neighbors.hip", "attn_bwd.hip", "attn_f32.hip", "edge.hip"]
+           "neighbors.hip", "order.hip", "attn_bwd.hip", "attn_f32.hip", "edge.hip"]
 
 
 def _hipcc() -> str:

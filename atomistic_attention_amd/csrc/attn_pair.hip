@@ -285,7 +285,9 @@ void attn_pair_kernel(const AttnArgs A)
         const float d = ok ? __builtin_amdgcn_sqrtf(dx * dx + dy * dy + dz * dz) : 0.f;   // v_sqrt_f32, 1 ulp
         const float fc = (ok && d < A.cutoff) ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;   // cutoff mask
         const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
-        const float t0 = fmaf(d, inv_delta, -gsc * (float)(8 * kq));   // g (d - mu_k) / Delta for k = 8 kq
+        // g (d - mu_k) / Delta for k = 8 kq; past the cutoff phi is 0 whatever t is, and
+        // the clamp keeps the ratio below finite for listed pairs far beyond it
+        const float t0 = fmaf(fminf(d, A.cutoff), inv_delta, -gsc * (float)(8 * kq));
         // A operand: lane (kq, pm) holds phi_k of pair pm for k = 8 kq + i (+ 32)
         // With t_i = t - g i (g = gsc), phi_{i+1} / phi_i = exp2(2 g t - g^2) e^{-i}: two
         // exponentials and a product chain give the lane's 8 consecutive Gaussians.

@@ -74,12 +74,12 @@ __device__ __forceinline__ int sel4(const int (&v)[4], int i)
 }
 
 // The union of the four lists into su (entries (j << 4) | mask, atom order,
-// followed by 8 to 11 entries of -1); returns the entry count, or -1 when a list
-// holds an atom twice.  sk is scratch for 64 E keys.  Every list must hold at
-// most 16 E entries.
+// followed by 8 to 11 padding entries fill << 4: a valid row that no target
+// uses); returns the entry count, or -1 when a list holds an atom twice.  sk is
+// scratch for 64 E keys.  Every list must hold at most 16 E entries.
 template <int E>
 __device__ __forceinline__ int quad_union(const int32_t *__restrict__ idx, int n, const int (&st)[4],
-                                          const int (&ln)[4], int *sk, int *su, int lane)
+                                          const int (&ln)[4], int fill, int *sk, int *su, int lane)
 {
     constexpr int N = 64 * E, S = 16 * E;
     const int sg = lane >> 4;                       // list of this 16-lane row
@@ -136,8 +136,8 @@ __device__ __forceinline__ int quad_union(const int32_t *__restrict__ idx, int n
         base += __builtin_popcountll(bal);
     }
     if (__builtin_amdgcn_ballot_w64(dup) != 0) return -1;
-    const int padn = ((base + 3) & ~3) + 8 - base;  // two groups of -1 past the last
-    if (lane < padn) su[base + lane] = -1;
+    const int padn = ((base + 3) & ~3) + 8 - base;  // two groups of padding past the last
+    if (lane < padn) su[base + lane] = fill << 4;
     quad_lds_sync();
     return base;
 }
@@ -207,19 +207,20 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
 
     // ---- the stream: the union of the lists, or the lists one after the other
     int nu = -1;
-    if (maxln <= 16) nu = quad_union<1>(A.nbr_idx, n, st, ln, sk, su, lane);
-    else if (maxln <= 32) nu = quad_union<2>(A.nbr_idx, n, st, ln, sk, su, lane);
-    else if (maxln <= 64) nu = quad_union<4>(A.nbr_idx, n, st, ln, sk, su, lane);
-    else if (maxln <= 128) nu = quad_union<8>(A.nbr_idx, n, st, ln, sk, su, lane);
-    else if (maxln <= 256) nu = quad_union<16>(A.nbr_idx, n, st, ln, sk, su, lane);
+    if (maxln <= 16) nu = quad_union<1>(A.nbr_idx, n, st, ln, ifill, sk, su, lane);
+    else if (maxln <= 32) nu = quad_union<2>(A.nbr_idx, n, st, ln, ifill, sk, su, lane);
+    else if (maxln <= 64) nu = quad_union<4>(A.nbr_idx, n, st, ln, ifill, sk, su, lane);
+    else if (maxln <= 128) nu = quad_union<8>(A.nbr_idx, n, st, ln, ifill, sk, su, lane);
+    else if (maxln <= 256) nu = quad_union<16>(A.nbr_idx, n, st, ln, ifill, sk, su, lane);
     nu = __builtin_amdgcn_readfirstlane(nu);
     const bool uni = nu >= 0;
     const long long tot64 = (long long)ln[0] + ln[1] + ln[2] + ln[3];
     const int tot = uni ? nu : (int)(tot64 < INT_MAX - 8 ? tot64 : INT_MAX - 8);
     const int G = (tot + 3) >> 2;
-    // entry x of the sequential stream
+    // entry x of the sequential stream; past the end, or an index out of range, the
+    // fill row with no target
     auto seq_code = [&](int x) -> int {
-        if (x >= tot) return -1;
+        if (x >= tot) return ifill << 4;
         int q = 0, off = x;
         if (off >= ln[0]) {
             off -= ln[0];
@@ -234,9 +235,9 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
             }
         }
         const int j = A.nbr_idx[sel4(st, q) + off];
-        return (j >= 0 && j < n) ? (j << 4) | (1 << q) : -1;
+        return (j >= 0 && j < n) ? (j << 4) | (1 << q) : ifill << 4;
     };
-    // codes of group g (wave-uniform); g may be G or G + 1 (all -1)
+    // codes of group g (wave-uniform); g may be G or G + 1 (padding only)
     auto codes = [&](int g, int (&cd)[4]) {
         if (uni) {
             const int4 v = *reinterpret_cast<const int4 *>(su + 4 * g);
@@ -248,6 +249,14 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
 #pragma unroll
             for (int r = 0; r < 4; ++r) cd[r] = seq_code(4 * g + r);
         }
+    };
+    // code cd[t] in lane 4 h + t: three selects under constant lane masks
+    auto lane_code = [&](const int (&cd)[4]) -> int {
+        int v = cd[0];
+        v = __builtin_amdgcn_inverse_ballot_w64(0x2222222222222222ull) ? cd[1] : v;
+        v = __builtin_amdgcn_inverse_ballot_w64(0x4444444444444444ull) ? cd[2] : v;
+        v = __builtin_amdgcn_inverse_ballot_w64(0x8888888888888888ull) ? cd[3] : v;
+        return v;
     };
 
     // ---- per-lane constants
@@ -282,7 +291,7 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
 
     auto rows_of = [&](const int (&cd)[4], int (&row)[4]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) row[r] = cd[r] >= 0 ? (cd[r] >> 4) : ifill;
+        for (int r = 0; r < 4; ++r) row[r] = cd[r] >> 4;
     };
     // Raw buffer loads: the row offset is a scalar, the lane's offset a constant
     // register, so a row costs no vector address arithmetic.
@@ -302,9 +311,7 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
         }
     };
     auto issue_k = [&](QuadKeys &kb, const int (&cd)[4]) {
-        int row[4];
-        rows_of(cd, row);
-        const int rk = sel4(row, t);
+        const int rk = lane_code(cd) >> 4;
         const unsigned char *kr = reinterpret_cast<const unsigned char *>(A.k) + (uint32_t(rk) * 512u + uint32_t(32 * h));
         kb.k0 = *reinterpret_cast<const float4 *>(kr);
         kb.k1 = *reinterpret_cast<const float4 *>(kr + 16);
@@ -315,10 +322,6 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
 
     // Logits and softmax weights of one group as fp16 pairs.
     auto weights = [&](QuadKeys &kb, const int (&cd)[4], const int (&cn)[4], bool first, half4_t &bh, half4_t &bl) {
-        // bit 4 r + t: entry r feeds target t
-        int mk = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mk |= (cd[r] >= 0 ? (cd[r] & 15) : 0) << (4 * r);
         // log2 of the four rows' scales (lanes 0..3 loaded rows 0..3), exact integers
         int lsi[4];
 #pragma unroll
@@ -336,16 +339,17 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
         S = __builtin_amdgcn_mfma_f32_4x4x1f32(kb.k0.w, qa.w, S, 0, 0, 0);
         S2 = __builtin_amdgcn_mfma_f32_4x4x1f32(kb.k1.w, qb.w, S2, 0, 0, 0);
         S += S2;
-        // bias of pair pm (target pm >> 2, entry pm & 3 = this lane's row)
+        // bias of pair pm (target pm >> 2, entry pm & 3 = this lane's row), also for
+        // pairs that the mask drops below (their logits never enter)
         floatx4 bias;
         {
-            const bool ok = ((mk >> (4 * (pm & 3) + (pm >> 2))) & 1) != 0;
             const float dx = kb.pj.x - pt.x, dy = kb.pj.y - pt.y, dz = kb.pj.z - pt.z;
             const float dl = __builtin_amdgcn_sqrtf(dx * dx + dy * dy + dz * dz);   // v_sqrt_f32, 1 ulp; lanes 0..15
-            const float d = ok ? __int_as_float(__builtin_amdgcn_ds_bpermute(4 * pm, __float_as_int(dl))) : 0.f;
-            const float fc = (ok && d < A.cutoff) ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;   // cutoff mask
+            const float d = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * pm, __float_as_int(dl)));
+            const float fc = d < A.cutoff ? 0.5f * (__builtin_amdgcn_cosf(d * cos_scale) + 1.f) : 0.f;   // cutoff mask
             const float lfc = __builtin_amdgcn_logf(fmaxf(fc, 0.f));   // log2; fc = 0 gives -inf, phi = 0
-            const float t0 = fmaf(d, inv_delta, -gsc * (float)(8 * kq));
+            // past the cutoff phi is 0 whatever u is; the clamp keeps the ratio q below finite
+            const float t0 = fmaf(fminf(d, A.cutoff), inv_delta, -gsc * (float)(8 * kq));
             // kb is read: request the next group's keys and positions into it
             __builtin_amdgcn_sched_barrier(0);
             issue_k(kb, cn);
@@ -375,8 +379,14 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
         float br[4], sc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) br[r] = __int_as_float(__builtin_amdgcn_ds_bpermute(bsrc, __float_as_int(bias[r])));
+        // entry r feeds the targets in bits 0..3 of its code: as a lane mask, the
+        // lanes 4 h + t of those targets
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = ((mk >> (4 * r + t)) & 1) ? S[r] + br[r] + (float)lsi[r] : -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t m32 = uint32_t(cd[r] & 15) * 0x11111111u;
+            const bool on = __builtin_amdgcn_inverse_ballot_w64((uint64_t(m32) << 32) | m32);
+            sc[r] = on ? S[r] + br[r] + (float)lsi[r] : -INFINITY;
+        }
         // lazily raised running maximum, then this group's weights
         const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         const bool grow = mx > mu + 8.f;
@@ -390,14 +400,19 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
                 for (int f = 0; f < 2; ++f) acc[e][f] *= corr;
             mu = mun;
         }
+        // z gains a 2^(zeta - log2 s_r): a product with a power of two built from
+        // its exponent field (clamped to the normal range), exact like ldexp
+        float a[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float a = __builtin_amdgcn_exp2f(sc[r] - mu);
-            z += __builtin_ldexpf(a, zeta - lsi[r]);
-            const _Float16 hi = (_Float16)a;
-            bh[r] = hi;
-            bl[r] = (_Float16)(a - (float)hi);
+            a[r] = __builtin_amdgcn_exp2f(sc[r] - mu);
+            const int ex = min(max(zeta - lsi[r] + 127, 1), 254);
+            z = fmaf(a[r], __uint_as_float(uint32_t(ex) << 23), z);
         }
+        const half4_t hv = __builtin_convertvector(*reinterpret_cast<const floatx4 *>(a), half4_t);
+        const floatx4 hf = __builtin_convertvector(hv, floatx4);
+        bh = hv;
+        bl = __builtin_convertvector(*reinterpret_cast<const floatx4 *>(a) - hf, half4_t);
     };
     // The group's weighted sum into the accumulators.
     auto sums = [&](const QuadRows<NV, D2> &b, const half4_t &bh, const half4_t &bl) {
@@ -498,7 +513,7 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
 }
 
 template <int L>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_quad_kernel(const AttnArgs A)
 {
     const int wv = threadIdx.x >> 6;

@@ -612,6 +612,29 @@ size_t e2v2_build_neighbors_workspace_bytes(int32_t n, int32_t max_neighbors)
     return neighbors_ws_bytes(n, max_neighbors) + 256;
 }
 
+size_t e2v2_target_order_workspace_bytes(int32_t n)
+{
+    if (n < 0) return 0;
+    return target_order_ws_bytes(n) + 256;
+}
+
+e2v2_status e2v2_target_order(const float *pos, int32_t n, int32_t *order, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream)
+{
+    if (n < 0 || n == INT32_MAX) return fail(E2V2_ERR_ARG, "n = %d out of range", n);
+    if (n == 0) return E2V2_OK;
+    if (!pos || !order || !workspace) return fail(E2V2_ERR_ARG, "NULL device pointer");
+    if ((reinterpret_cast<uintptr_t>(pos) | reinterpret_cast<uintptr_t>(order)) & 3u)
+        return fail(E2V2_ERR_ARG, "pos and order must be 4-byte aligned");
+    if (workspace_bytes < e2v2_target_order_workspace_bytes(n))
+        return fail(E2V2_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes,
+                    e2v2_target_order_workspace_bytes(n));
+    void *ws = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+    const hipError_t e = launch_target_order(pos, n, ws, order, stream);
+    if (e != hipSuccess) return hip_fail(e, "target order");
+    return E2V2_OK;
+}
+
 e2v2_status e2v2_build_neighbors(const float *pos, int32_t n, float cutoff, int32_t K, int32_t *nbr_start,
                                  int32_t *nbr_len, int32_t *nbr_idx, int64_t capacity, int64_t *nnz_host,
                                  int32_t *order, void *workspace, size_t workspace_bytes, hipStream_t stream)
@@ -1527,14 +1550,12 @@ e2v2_status e2v2_stack_forward(int32_t n_layers, const e2v2_layer_desc *descs, c
     }
     // 2. lists at the largest cutoff, then filtered for each smaller one
     if (rebuild) {
+        // with the lists, the targets' processing order until the next rebuild: a
+        // Hilbert curve (paid once per rebuild, its locality used by every layer of
+        // every step)
         st = e2v2_build_neighbors(pos, n, S.cut[0], K, start, list_len(0), list_idx(0), (int64_t)n * K, nullptr,
-                                  nullptr, wb + W.nbws, W.nbws_bytes, stream);
+                                  order, wb + W.nbws, W.nbws_bytes, stream);
         if (st != E2V2_OK) return st;
-        // the targets' processing order until the next rebuild: a Morton curve (its
-        // sort is paid once per rebuild, its locality on every layer of every step)
-        void *nws = reinterpret_cast<void *>((reinterpret_cast<uintptr_t>(wb + W.nbws) + 255) & ~uintptr_t(255));
-        e = launch_morton_order(pos, n, nws, order, stream);
-        if (e != hipSuccess) return hip_fail(e, "processing order");
         for (int k = 1; k < S.ncut; ++k) {
             e = launch_filter_rows(pos, n, S.cut[k], start, list_len(0), list_idx(0), list_len(k), list_idx(k), stream);
             if (e != hipSuccess) return hip_fail(e, "neighbour filter kernel");

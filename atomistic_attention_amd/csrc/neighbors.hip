@@ -27,10 +27,10 @@
 //   visited are always a superset of the ones holding a neighbour.
 // Within-cell order depends on atomics, but rows are sets sorted by j and the
 // K-nearest choice uses a total order, so results are deterministic.
+#include "curve.h"
 #include "e2v2_internal.h"
 
 #include <algorithm>
-#include <hipcub/hipcub.hpp>
 
 #pragma clang fp contract(off)
 
@@ -47,7 +47,8 @@ struct GridInfo {
 
 struct NbrLayout {
     GridInfo *grid;
-    float *box_part;       // [kBoxBlocks][8] partial bounding boxes
+    float *box_part;       // [kBoxBlocks][16] partial bounding boxes: all values (min 0..2,
+                           // max 4..6), finite values (min 8..10, max 12..14)
     int32_t *cell_of;
     int32_t *cell_cnt;     // [maxc + 1]
     int32_t *cell_start;   // [maxc + 1]
@@ -55,10 +56,13 @@ struct NbrLayout {
     int32_t *order;        // [n] atom ids in cell order
     float4 *spos;          // [n] positions in cell order, w = atom id bits
     int64_t *nnz;
-    uint32_t *mkey[2];     // [n] Morton keys in / sorted (launch_morton_order)
-    int32_t *mval;         // [n] atom ids 0 .. n-1; before that, the atomic slots of the cell scatter
-    void *sort_tmp;        // radix-sort scratch
-    size_t sort_bytes;
+    int32_t *mval;         // [n] the atomic slots of the cell scatter
+    // the Hilbert processing order (curve.h), when the caller asks for it
+    curve::CurveInfo *curve;
+    int32_t *bcnt, *bstart, *bcursor, *nitems;   // [kBuckets], [kBuckets + 1], [kBuckets], [1]
+    int2 *items;           // [max_items(n)]
+    uint32_t *key;         // [n]
+    uint64_t *ent;         // [n]
     size_t bytes;
 };
 
@@ -72,7 +76,7 @@ static NbrLayout nbr_layout(void *ws, int n)
     size_t o = 0;
     const size_t mc = (size_t)max_cells(n);
     L.grid = reinterpret_cast<GridInfo *>(p + o); o += al256(sizeof(GridInfo));
-    L.box_part = reinterpret_cast<float *>(p + o); o += al256(sizeof(float) * 8 * 256);
+    L.box_part = reinterpret_cast<float *>(p + o); o += al256(sizeof(float) * 16 * 256);
     L.nnz = reinterpret_cast<int64_t *>(p + o); o += al256(sizeof(int64_t));
     L.cell_of = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (size_t)n);
     L.cell_cnt = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (mc + 1));
@@ -80,15 +84,15 @@ static NbrLayout nbr_layout(void *ws, int n)
     L.cell_cur = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * mc);
     L.order = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (size_t)n);
     L.spos = reinterpret_cast<float4 *>(p + o); o += al256(sizeof(float4) * (size_t)n);
-    L.mkey[0] = reinterpret_cast<uint32_t *>(p + o); o += al256(sizeof(uint32_t) * (size_t)n);
-    L.mkey[1] = reinterpret_cast<uint32_t *>(p + o); o += al256(sizeof(uint32_t) * (size_t)n);
     L.mval = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (size_t)n);
-    size_t tb = 0;
-    hipcub::DeviceRadixSort::SortPairs(nullptr, tb, (const uint32_t *)nullptr, (uint32_t *)nullptr,
-                                       (const int32_t *)nullptr, (int32_t *)nullptr, n > 0 ? n : 1, 0, 30);
-    L.sort_tmp = p + o;
-    L.sort_bytes = tb;
-    o += al256(tb);
+    L.curve = reinterpret_cast<curve::CurveInfo *>(p + o); o += al256(sizeof(curve::CurveInfo));
+    L.bcnt = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * curve::kBuckets);
+    L.bstart = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * (curve::kBuckets + 1));
+    L.bcursor = reinterpret_cast<int32_t *>(p + o); o += al256(sizeof(int32_t) * curve::kBuckets);
+    L.nitems = reinterpret_cast<int32_t *>(p + o); o += 256;
+    L.items = reinterpret_cast<int2 *>(p + o); o += al256(sizeof(int2) * (size_t)curve::max_items(n));
+    L.key = reinterpret_cast<uint32_t *>(p + o); o += al256(sizeof(uint32_t) * (size_t)n);
+    L.ent = reinterpret_cast<uint64_t *>(p + o); o += al256(sizeof(uint64_t) * (size_t)n);
     L.bytes = o;
     return L;
 }
@@ -103,58 +107,87 @@ int64_t *neighbors_nnz_slot(void *ws, int n) { return nbr_layout(ws, n).nnz; }
 constexpr int kBoxBlocks = 256;
 
 __global__ __launch_bounds__(256) void k_bbox_partial(const float *__restrict__ pos, int n, float *part, int maxc,
-                                                      int32_t *cell_cnt)
+                                                      int32_t *cell_cnt, int32_t *bcnt)
 {
-    __shared__ float smin[3][256], smax[3][256];
+    __shared__ float sv[12][256];      // min 0..2, max 3..5 over all values; 6..8, 9..11 over finite ones
     const int t = threadIdx.x;
     for (long long c = (long long)blockIdx.x * 256 + t; c <= maxc; c += (long long)gridDim.x * 256) cell_cnt[c] = 0;
-    float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+    if (bcnt)
+        for (int b = blockIdx.x * 256 + t; b < curve::kBuckets; b += gridDim.x * 256) bcnt[b] = 0;
+    float v[12];
+    for (int d = 0; d < 3; ++d) {
+        v[d] = v[6 + d] = INFINITY;
+        v[3 + d] = v[9 + d] = -INFINITY;
+    }
     for (long long i = (long long)blockIdx.x * 256 + t; i < n; i += (long long)gridDim.x * 256)
         for (int d = 0; d < 3; ++d) {
-            const float v = pos[3 * i + d];
-            mn[d] = fminf(mn[d], v);     // fminf/fmaxf ignore NaN
-            mx[d] = fmaxf(mx[d], v);
+            const float x = pos[3 * i + d];
+            v[d] = fminf(v[d], x);       // fminf/fmaxf ignore NaN
+            v[3 + d] = fmaxf(v[3 + d], x);
+            if (std::isfinite(x)) {
+                v[6 + d] = fminf(v[6 + d], x);
+                v[9 + d] = fmaxf(v[9 + d], x);
+            }
         }
-    for (int d = 0; d < 3; ++d) { smin[d][t] = mn[d]; smax[d][t] = mx[d]; }
+    for (int q = 0; q < 12; ++q) sv[q][t] = v[q];
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
         if (t < s)
             for (int d = 0; d < 3; ++d) {
-                smin[d][t] = fminf(smin[d][t], smin[d][t + s]);
-                smax[d][t] = fmaxf(smax[d][t], smax[d][t + s]);
+                sv[d][t] = fminf(sv[d][t], sv[d][t + s]);
+                sv[3 + d][t] = fmaxf(sv[3 + d][t], sv[3 + d][t + s]);
+                sv[6 + d][t] = fminf(sv[6 + d][t], sv[6 + d][t + s]);
+                sv[9 + d][t] = fmaxf(sv[9 + d][t], sv[9 + d][t + s]);
             }
         __syncthreads();
     }
     if (t < 3) {
-        part[blockIdx.x * 8 + t] = smin[t][0];
-        part[blockIdx.x * 8 + 4 + t] = smax[t][0];
+        part[blockIdx.x * 16 + t] = sv[t][0];
+        part[blockIdx.x * 16 + 4 + t] = sv[3 + t][0];
+        part[blockIdx.x * 16 + 8 + t] = sv[6 + t][0];
+        part[blockIdx.x * 16 + 12 + t] = sv[9 + t][0];
     }
 }
 
+// One block: the grid from the partial boxes and, when asked for, the cells of
+// the Hilbert processing order from the finite values' box.
 __global__ __launch_bounds__(256) void k_bbox(const float *__restrict__ part, int nparts, float cutoff, int maxc,
-                                              GridInfo *grid)
+                                              GridInfo *grid, int n, curve::CurveInfo *cinfo)
 {
-    __shared__ float smin[3][256], smax[3][256];
+    __shared__ float sv[12][256];
     const int t = threadIdx.x;
     for (int d = 0; d < 3; ++d) {
-        smin[d][t] = t < nparts ? part[t * 8 + d] : INFINITY;
-        smax[d][t] = t < nparts ? part[t * 8 + 4 + d] : -INFINITY;
+        sv[d][t] = t < nparts ? part[t * 16 + d] : INFINITY;
+        sv[3 + d][t] = t < nparts ? part[t * 16 + 4 + d] : -INFINITY;
+        sv[6 + d][t] = t < nparts ? part[t * 16 + 8 + d] : INFINITY;
+        sv[9 + d][t] = t < nparts ? part[t * 16 + 12 + d] : -INFINITY;
     }
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
         if (t < s)
             for (int d = 0; d < 3; ++d) {
-                smin[d][t] = fminf(smin[d][t], smin[d][t + s]);
-                smax[d][t] = fmaxf(smax[d][t], smax[d][t + s]);
+                sv[d][t] = fminf(sv[d][t], sv[d][t + s]);
+                sv[3 + d][t] = fmaxf(sv[3 + d][t], sv[3 + d][t + s]);
+                sv[6 + d][t] = fminf(sv[6 + d][t], sv[6 + d][t + s]);
+                sv[9 + d][t] = fmaxf(sv[9 + d][t], sv[9 + d][t + s]);
             }
         __syncthreads();
     }
+    if (t == 1 && cinfo) {
+        const float lo[3] = {sv[6][0], sv[7][0], sv[8][0]}, hi[3] = {sv[9][0], sv[10][0], sv[11][0]};
+        *cinfo = curve::curve_setup(lo, hi, n);
+    }
     if (t == 0) {
+        float smin[3], smax[3];
+        for (int d = 0; d < 3; ++d) {
+            smin[d] = sv[d][0];
+            smax[d] = sv[3 + d][0];
+        }
         const float cmin = 0.5f * cutoff * 1.001f;              // two cells per cutoff
         int dims[3];
         float ext[3];
         for (int d = 0; d < 3; ++d) {
-            ext[d] = smax[d][0] - smin[d][0];
+            ext[d] = smax[d] - smin[d];
             float k = (ext[d] < 1e30f) ? floorf(ext[d] / cmin) : 1.f;   // false for NaN / inf
             dims[d] = (k >= 1.f) ? (int)fminf(k, 1024.f) : 1;
         }
@@ -166,11 +199,11 @@ __global__ __launch_bounds__(256) void k_bbox(const float *__restrict__ part, in
         }
         float mag = 0.f;
         for (int d = 0; d < 3; ++d) {
-            grid->lo[d] = (smin[d][0] < 1e30f && smin[d][0] > -1e30f) ? smin[d][0] : 0.f;
+            grid->lo[d] = (smin[d] < 1e30f && smin[d] > -1e30f) ? smin[d] : 0.f;
             grid->inv[d] = dims[d] > 1 ? (float)dims[d] / ext[d] : 0.f;
             grid->w[d] = dims[d] > 1 ? ext[d] / (float)dims[d] : INFINITY;
             grid->dims[d] = dims[d];
-            mag = fmaxf(mag, fmaxf(fabsf(smin[d][0]), fabsf(smax[d][0])));
+            mag = fmaxf(mag, fmaxf(fabsf(smin[d]), fabsf(smax[d])));
         }
         // fp32 rounding of a coordinate-sized quantity is below 6e-8 of the largest
         // coordinate; 1e-5 of it (plus 1e-4 of the cutoff) is a wide bound
@@ -244,18 +277,28 @@ __device__ __forceinline__ void row_cells(const GridInfo &gi, int z, int y, int 
 }
 
 // ---------------------------------------------------------------- step 2
+// Each atom's cell and, when the processing order is asked for, its Hilbert
+// index and bucket count.
 __global__ void k_cell_assign(const float *__restrict__ pos, int n, const GridInfo *__restrict__ grid,
-                              int32_t *cell_of, int32_t *cell_cnt)
+                              int32_t *cell_of, int32_t *cell_cnt, const curve::CurveInfo *__restrict__ cinfo,
+                              uint32_t *key, int32_t *bcnt)
 {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const GridInfo gi = *grid;
-    const int cx = cell_coord(pos[3 * i + 0], gi.lo[0], gi.inv[0], gi.dims[0]);
-    const int cy = cell_coord(pos[3 * i + 1], gi.lo[1], gi.inv[1], gi.dims[1]);
-    const int cz = cell_coord(pos[3 * i + 2], gi.lo[2], gi.inv[2], gi.dims[2]);
+    const float x = pos[3 * i + 0], y = pos[3 * i + 1], z = pos[3 * i + 2];
+    const int cx = cell_coord(x, gi.lo[0], gi.inv[0], gi.dims[0]);
+    const int cy = cell_coord(y, gi.lo[1], gi.inv[1], gi.dims[1]);
+    const int cz = cell_coord(z, gi.lo[2], gi.inv[2], gi.dims[2]);
     const int c = cell_index(gi, cx, cy, cz);
     cell_of[i] = c;
     atomicAdd(&cell_cnt[c], 1);
+    if (cinfo) {
+        const curve::CurveInfo ci = *cinfo;
+        const uint32_t k = curve::curve_key(ci, x, y, z);
+        key[i] = k;
+        atomicAdd(&bcnt[curve::bucket_of(k, ci.shift)], 1);
+    }
 }
 
 // Exclusive scan of in[0..count) into out[0..count], out[count] = total; one block.
@@ -263,8 +306,8 @@ __global__ void k_cell_assign(const float *__restrict__ pos, int n, const GridIn
 // taken in tiles of 4096: each thread sums 4 consecutive entries, the wave scans
 // the sums with shuffles, the 16 wave totals meet in LDS, and a carry runs from
 // tile to tile; loads and stores stay coalesced.
-__global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, const int *count_dev, int count_arg,
-                                               int32_t *out, int32_t *copy, int64_t *total_out)
+__device__ inline void scan_block(const int32_t *__restrict__ in, const int *count_dev, int count_arg, int32_t *out,
+                                  int32_t *copy, int64_t *total_out)
 {
     __shared__ long long wsum[16];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -309,23 +352,61 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, c
     }
 }
 
+__global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, const int *count_dev, int count_arg,
+                                               int32_t *out, int32_t *copy, int64_t *total_out)
+{
+    scan_block(in, count_dev, count_arg, out, copy, total_out);
+}
+
+// The cell scan (block 0) and the processing order's bucket scan (block 1) in one
+// launch.
+__global__ __launch_bounds__(1024) void k_scan_cells_buckets(const int32_t *__restrict__ cell_cnt, const int *ncell,
+                                                             int32_t *cell_start, int32_t *cell_cur,
+                                                             const int32_t *__restrict__ bcnt, int32_t *bstart,
+                                                             int32_t *bcursor, int2 *items, int32_t *nitems)
+{
+    if (blockIdx.x == 0) scan_block(cell_cnt, ncell, 0, cell_start, cell_cur, nullptr);
+    else curve::bucket_scan_block(bcnt, bstart, bcursor, items, nitems);
+}
+
 // ---------------------------------------------------------------- step 3
 // Two passes, so the order within a cell does not depend on the timing of atomics:
 // k_scatter drops every atom into its cell's range at an atomic slot (scratch),
 // then k_place puts it at its rank by atom index within that range.  The cells
 // follow the serpentine order of cell_index, and within a cell atoms ascend: the
 // same order on every call.  A cell of k atoms costs k reads per atom.
-__global__ void k_scatter(int n, const int32_t *__restrict__ cell_of, int32_t *cell_cur, int32_t *tmp)
+__global__ void k_scatter(int n, const int32_t *__restrict__ cell_of, int32_t *cell_cur, int32_t *tmp,
+                          const curve::CurveInfo *__restrict__ cinfo, const uint32_t *__restrict__ key,
+                          int32_t *bcursor, uint64_t *ent)
 {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const int slot = atomicAdd(&cell_cur[cell_of[i]], 1);
     tmp[slot] = (int32_t)i;
+    if (cinfo) {            // the atom's slot in its bucket of the processing order
+        const uint32_t k = key[i];
+        const int b = atomicAdd(&bcursor[curve::bucket_of(k, cinfo->shift)], 1);
+        ent[b] = (uint64_t(k) << 32) | uint32_t(i);
+    }
 }
-__global__ void k_place(const float *__restrict__ pos, int n, const int32_t *__restrict__ cell_of,
-                        const int32_t *__restrict__ cell_start, const int32_t *__restrict__ tmp, int32_t *order,
-                        float4 *spos, int32_t *order_out)
+// Blocks below nplace place the atoms in cell order; the blocks after them, four
+// waves each, rank the work items of the processing order (curve.h) into
+// order_out.
+__global__ __launch_bounds__(256) void k_place(const float *__restrict__ pos, int n,
+                                               const int32_t *__restrict__ cell_of,
+                                               const int32_t *__restrict__ cell_start,
+                                               const int32_t *__restrict__ tmp, int32_t *order, float4 *spos,
+                                               unsigned nplace, const uint64_t *__restrict__ ent,
+                                               const int32_t *__restrict__ bstart, const int2 *__restrict__ items,
+                                               const int32_t *__restrict__ nitems, int32_t *order_out)
 {
+    if (blockIdx.x >= nplace) {
+        __shared__ uint64_t tile[4][curve::kRun];
+        const int w = threadIdx.x >> 6;
+        curve::rank_item(ent, bstart, items, nitems, 4LL * (blockIdx.x - nplace) + w, threadIdx.x & 63, tile[w],
+                         order_out);
+        return;
+    }
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const int c = cell_of[i];
@@ -334,40 +415,7 @@ __global__ void k_place(const float *__restrict__ pos, int n, const int32_t *__r
     for (int t = cs; t < ce; ++t) rank += tmp[t] < (int32_t)i;
     const int slot = cs + rank;
     order[slot] = (int32_t)i;
-    if (order_out) order_out[slot] = (int32_t)i;
     spos[slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float((int)i));
-}
-
-// ---------------------------------------------------------------- Morton order
-// A processing order for callers that build the list rarely (the layer stack, at
-// rebuilds): atoms sorted by the Morton code of their position on a grid of half
-// the cell width (10 bits per axis, clamped), a space-filling curve, so a run of
-// consecutive targets fills a compact region and the rows it reads stay close
-// together -- fewer L2 misses than the cells' own order.  Stable sort keyed
-// on atom ids 0..n-1: deterministic.  Uses the grid of the last build in ws.
-__device__ __forceinline__ uint32_t spread3(uint32_t v)
-{
-    v &= 0x3ffu;
-    v = (v | (v << 16)) & 0x030000ffu;
-    v = (v | (v << 8)) & 0x0300f00fu;
-    v = (v | (v << 4)) & 0x030c30c3u;
-    v = (v | (v << 2)) & 0x09249249u;
-    return v;
-}
-__global__ void k_morton_keys(const float *__restrict__ pos, int n, const GridInfo *__restrict__ grid, uint32_t *key,
-                              int32_t *val)
-{
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const GridInfo gi = *grid;
-    uint32_t q[3];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        const float t = (pos[3 * i + a] - gi.lo[a]) * gi.inv[a] * 2.f;
-        q[a] = t >= 1023.f ? 1023u : (t > 0.f ? (uint32_t)t : 0u);     // NaN -> 0
-    }
-    key[i] = spread3(q[0]) | (spread3(q[1]) << 1) | (spread3(q[2]) << 2);
-    val[i] = (int32_t)i;
 }
 
 // ---------------------------------------------------------------- step 4
@@ -998,29 +1046,28 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
     NbrLayout L = nbr_layout(ws, n);
     const int maxc = max_cells(n);
     const int nparts = (int)std::min<long long>(kBoxBlocks, ((long long)n + 255) / 256);
-    k_bbox_partial<<<nparts, 256, 0, stream>>>(pos, n, L.box_part, maxc, L.cell_cnt);
-    k_bbox<<<1, 256, 0, stream>>>(L.box_part, nparts, cutoff, maxc, L.grid);
-    k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt);
-    k_scan<<<1, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, 0, L.cell_start, L.cell_cur, nullptr);
-    k_scatter<<<nblk(n, 256), 256, 0, stream>>>(n, L.cell_of, L.cell_cur, L.mval);
-    k_place<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.cell_of, L.cell_start, L.mval, L.order, L.spos, order_out);
+    // with order_out the Hilbert processing order (curve.h) rides along in the same
+    // launches: its box, indices and bucket counts, bucket scan, slots and ranks
+    const bool ord = order_out != nullptr;
+    curve::CurveInfo *ci = ord ? L.curve : nullptr;
+    k_bbox_partial<<<nparts, 256, 0, stream>>>(pos, n, L.box_part, maxc, L.cell_cnt, ord ? L.bcnt : nullptr);
+    k_bbox<<<1, 256, 0, stream>>>(L.box_part, nparts, cutoff, maxc, L.grid, n, ci);
+    k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt, ci, L.key, L.bcnt);
+    if (ord)
+        k_scan_cells_buckets<<<2, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, L.cell_start, L.cell_cur, L.bcnt,
+                                                     L.bstart, L.bcursor, L.items, L.nitems);
+    else
+        k_scan<<<1, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, 0, L.cell_start, L.cell_cur, nullptr);
+    k_scatter<<<nblk(n, 256), 256, 0, stream>>>(n, L.cell_of, L.cell_cur, L.mval, ci, L.key, L.bcursor, L.ent);
+    const unsigned nplace = nblk(n, 256);
+    const unsigned nrank = ord ? nblk(curve::max_items(n), 4) : 0u;
+    k_place<<<nplace + nrank, 256, 0, stream>>>(pos, n, L.cell_of, L.cell_start, L.mval, L.order, L.spos, nplace,
+                                                L.ent, L.bstart, L.items, L.nitems, order_out);
     if (K == 0) {
         const double rc2 = (double)cutoff * (double)cutoff;
         k_count_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(n, cutoff, rc2, L.grid, L.cell_start,
                                                                                 L.order, L.spos, nbr_len);
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_morton_order(const float *pos, int n, void *ws, int32_t *order_out, hipStream_t stream)
-{
-    if (n <= 0) return hipSuccess;
-    NbrLayout L = nbr_layout(ws, n);
-    k_morton_keys<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.mkey[0], L.mval);
-    size_t tb = L.sort_bytes;
-    const hipError_t e = hipcub::DeviceRadixSort::SortPairs(L.sort_tmp, tb, L.mkey[0], L.mkey[1], L.mval, order_out, n,
-                                                            0, 30, stream);
-    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

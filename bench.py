@@ -174,16 +174,17 @@ def cpu_baseline(wl, budget_targets: int | None = None) -> dict:
 
 
 def per_config(B, W, torch, name: str, steps: int = 20) -> dict:
-    """One configuration's layer on its own: the list built once beforehand (in the
-    builder's cell order), then the layer (prepare + aggregate) and its streaming
-    kernel timed with HIP events; nnz, ms, pairs/s, steps/s and the roofline."""
+    """One configuration's layer on its own: the list and the Hilbert processing
+    order built once beforehand, then the layer (prepare + aggregate) and its
+    streaming kernel timed with HIP events; nnz, ms, pairs/s, steps/s and the
+    roofline."""
     wl = W.make_workload(name)
     c = wl.cfg
     d = W.device_arrays(wl)
     dev = d["pos"].device
     desc = B.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, d["dtype"])
-    order = torch.empty(c.n, dtype=torch.int32, device=dev)
-    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors, order_out=order)
+    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors)
+    order = B.e2v2_target_order(d["pos"])
     aws = torch.empty(B.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device=dev)
     out = torch.empty(wl.h.shape, dtype=torch.float32, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -333,8 +334,8 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
     d = W.device_arrays(wl)
     dev = d["pos"].device
     desc = B.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
-    order = torch.empty(c.n, dtype=torch.int32, device=dev)
-    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, 0, order_out=order)
+    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, 0)
+    order = B.e2v2_target_order(d["pos"])
     g = torch.from_numpy(np.random.default_rng(11).standard_normal(wl.h.shape).astype(np.float32)).to(dev)
     gh = torch.empty_like(g)
     out = torch.empty_like(g)
@@ -406,8 +407,8 @@ def backward_bench(B, W, torch, steps: int = 20, warmup: int = 3, name: str = "g
     cb = wb.cfg
     db = W.device_arrays(wb)
     descb = B.make_desc(cb.lmax, cb.channels, cb.heads, cb.n_rbf, cb.cutoff, db["dtype"])
-    ob = torch.empty(cb.n, dtype=torch.int32, device=dev)
-    sb_, lb_, ib_, nnzb = B.e2v2_build_neighbors(db["pos"], cb.cutoff, cb.max_neighbors, order_out=ob)
+    sb_, lb_, ib_, nnzb = B.e2v2_build_neighbors(db["pos"], cb.cutoff, cb.max_neighbors)
+    ob = B.e2v2_target_order(db["pos"])
     gb = torch.from_numpy(np.random.default_rng(12).standard_normal(wb.h.shape).astype(np.float32)).to(dev)
     ghb, gpb = torch.empty_like(gb), torch.empty((cb.n, 3), dtype=torch.float32, device=dev)
     outb = torch.empty_like(gb)
@@ -468,8 +469,8 @@ def edge_bench(B, W, torch, steps: int = 10, warmup: int = 2, name: str = "g4") 
     d = W.device_arrays(wl)
     dev = d["pos"].device
     desc = B.make_desc(c.lmax, c.channels, c.heads, c.n_rbf, c.cutoff, torch.float32)
-    order = torch.empty(c.n, dtype=torch.int32, device=dev)
-    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, 0, order_out=order)
+    s, ln, ix, nnz = B.e2v2_build_neighbors(d["pos"], c.cutoff, 0)
+    order = B.e2v2_target_order(d["pos"])
     w_e = torch.from_numpy(np.random.default_rng(9).standard_normal((num_paths(c.lmax), c.channels))
                            .astype(np.float32)).to(dev)
     out = torch.empty(wl.h.shape, dtype=torch.float32, device=dev)
@@ -589,9 +590,10 @@ def main():
                             taps={"events": ev[1:]} if ev is not None else None, target_order=order)
 
     # The timed step: the projections and source coupling need no neighbour list,
-    # so they run on a second stream while the list is built, and the streaming
-    # attention + output stage joins both.  The fork waits for the previous step,
-    # whose attention still reads the workspace.
+    # so they run on a second stream while the list and the targets' Hilbert
+    # processing order are built, and the streaming attention + output stage joins
+    # both.  The fork waits for the previous step, whose attention still reads the
+    # workspace and the order.
     side = torch.cuda.Stream()
     fork, join = torch.cuda.Event(), torch.cuda.Event()
 
@@ -646,9 +648,10 @@ def main():
     t_attn_ms = float(mean[3])
     layer_ms = float(mean[1:].sum())
     if cfg.storage == "bf16":
-        stage_names = ("neighbours", "projections+source_eaas", None, "attention", "target_eaas+output_projection")
+        stage_names = ("neighbours+order", "projections+source_eaas", None, "attention",
+                       "target_eaas+output_projection")
     else:
-        stage_names = ("neighbours", "projections", "source_eaas", "attention", "output_projection")
+        stage_names = ("neighbours+order", "projections", "source_eaas", "attention", "output_projection")
     stage_ms = {}
     for name, v in zip(stage_names, mean):
         if name is None:
@@ -686,7 +689,8 @@ def main():
             "timing": "HIP events on the main stream around the whole loop of --steps steps",
             "stage_ms": stage_ms,
             "stages_in_order_ms_per_step": serial_ms,
-            "overlap": "projections + source coupling on a second stream during the neighbour build",
+            "overlap": "projections + source coupling on a second stream during the neighbour build (which "
+                       "also emits the Hilbert target order)",
             "layer_ms_excl_neighbours": layer_ms,
             "layer_pairs_per_s_excl_neighbours": nnz / (layer_ms * 1e-3),
             "layer_steps_per_s_excl_neighbours": 1e3 / layer_ms,

@@ -132,13 +132,10 @@ typedef struct {
  *   nbr_start    device [n] int32;  nbr_len device [n] int32
  *   nbr_idx      device [capacity] int32
  *   nnz_host     host, may be NULL for K > 0; required for K == 0
- *   order        device [n] int32 or NULL: receives the atoms in cell-list order
- *                (a permutation of 0..n-1 in which consecutive atoms are spatial
- *                neighbours); pass it as target_order to e2v2_attn_forward.  Cells
- *                come in serpentine order (z-planes in turn, every other plane's
- *                rows and every other row reversed, so consecutive cells touch)
- *                and atoms ascend within a cell, so the order is the same on every
- *                call with the same positions.
+ *   order        device [n] int32 or NULL: receives the targets' Hilbert-curve
+ *                processing order, the permutation e2v2_target_order returns
+ *                (computed in the builder's own launches, from the same
+ *                positions); pass it as target_order to the attention calls.
  *   workspace    device scratch of at least
  *                e2v2_build_neighbors_workspace_bytes(n, max_neighbors) bytes
  * Limits: 0 <= n < 2^31 - 1, cutoff > 0 finite, 0 <= K <= 4096, total entries
@@ -148,6 +145,36 @@ e2v2_status e2v2_build_neighbors(const float *pos, int32_t n, float cutoff, int3
                                  int64_t capacity, int64_t *nnz_host, int32_t *order,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t e2v2_build_neighbors_workspace_bytes(int32_t n, int32_t max_neighbors);
+
+/* ------------------------------------------------------------------------
+ * Processing order of the targets along a Hilbert curve, to pass as target_order
+ * to the attention calls.  Targets are independent (FlashSchNet page, section
+ * 2.3: one program writes each target's output, in any order); the order only
+ * decides which targets run together: the four-target streaming kernel reads the
+ * union of four consecutive targets' lists once, and the chip's L2 slices each
+ * work on one run of the order.  A Hilbert curve keeps every run compact.
+ * The curve: cubic cells of side 2^k over the bounding box of the finite
+ * coordinates (lo = its low corner), k the largest integer with
+ * 8 n 2^(3k) <= V, V the product of the box's sides in fp64 (each side at least
+ * 2^-10 of the longest), raised while the longest side spans 1023 cells or more;
+ * cell coordinates q = floor((pos - lo) * 2^-k) in fp32, clamped to 0..1023 (NaN
+ * to 0); each atom's key is the 30-bit Hilbert index of (qx, qy, qz) (J.
+ * Skilling's transposed form, 10 bits per axis, its bits read from the top
+ * level down, first axis first); atoms sorted by key, ties by atom id.  With no extent every key is 0
+ * (the order is 0..n-1).  Deterministic.
+ *   pos        device [n][3] fp32, 4-byte aligned
+ *   order      device [n] int32, 4-byte aligned: receives the permutation
+ *   workspace  device scratch of at least e2v2_target_order_workspace_bytes(n)
+ *              bytes
+ * Runs on `stream` and does not synchronise.  It needs no neighbour list, so it
+ * can run beside e2v2_build_neighbors on a second stream.  Its radix sort clears
+ * counters with hipMemsetAsync: not for stream capture.
+ * Errors: E2V2_ERR_ARG for n < 0 or n = 2^31 - 1, NULL or misaligned pointers, a
+ * workspace below the size; E2V2_ERR_HIP for a failed launch.  n = 0 does
+ * nothing. */
+e2v2_status e2v2_target_order(const float *pos, int32_t n, int32_t *order, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+size_t e2v2_target_order_workspace_bytes(int32_t n);
 
 /* ------------------------------------------------------------------------
  * EAAS tensor product of features with the encoding of each node's position

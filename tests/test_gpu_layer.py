@@ -219,6 +219,30 @@ def test_isolated_atoms_and_padding(gpu_lib, storage):
         assert rel_err(out, ref["out"]) < tolerance(wl)
 
 
+@pytest.mark.parametrize("L,storage", [(2, "bf16"), (3, "bf16"), (2, "fp32")])
+def test_listed_pairs_far_beyond_the_cutoff(gpu_lib, L, storage):
+    """Lists may hold pairs past the cutoff (lists kept while atoms move): their
+    envelope is 0, so their distance bias is 0 and only q . k enters (FlashSchNet
+    page, section 2.2, the cutoff mask on the envelope).  Here every target also
+    lists three atoms of a second cluster 26 A or more away, five cutoffs and
+    beyond, where the Gaussians of the distance expansion underflow completely."""
+    wl = _small(200, L, 16, storage, 21, side=14.0, cutoff=5.0, nrbf=32)
+    wl.pos[150:] += np.array([40.0, 0.0, 0.0], dtype=wl.pos.dtype)
+    rows = O.neighbors(wl.pos, wl.cfg.cutoff)
+    rng = np.random.default_rng(8)
+    far = 0
+    for i in range(wl.cfg.n):
+        other = np.arange(150, 200) if i < 150 else np.arange(0, 150)
+        extra = rng.choice(other, 3, replace=False)
+        far += int(np.sum(np.linalg.norm(wl.pos[extra] - wl.pos[i], axis=1) > 25.0))
+        rows[i] = np.sort(np.r_[rows[i], extra]).astype(np.int32)
+    assert far == 3 * wl.cfg.n
+    out, _ = _run(gpu_lib, wl, nbr=csr_from_rows(rows))
+    ref = O.layer_forward_workload(wl, rows=rows)
+    assert np.all(np.isfinite(out))
+    assert rel_err(out, ref["out"]) < tolerance(wl)
+
+
 @pytest.mark.parametrize("n,cutoff,lo,hi", [(300, 2.4, 1, 16), (500, 3.4, 17, 32), (900, 4.5, 33, 64),
                                              (1600, 5.8, 65, 128), (2600, 7.4, 129, 256)])
 def test_list_length_classes_16_heads(gpu_lib, n, cutoff, lo, hi):
@@ -246,14 +270,14 @@ def test_layer_deterministic(gpu_lib):
 
 @pytest.mark.parametrize("storage", ["fp32", "bf16"])
 def test_target_order_does_not_change_results(gpu_lib, storage):
-    """Targets are independent: any processing order (natural, the neighbour
-    builder's cell order, a random permutation) gives the same outputs.  With fp32
-    storage (one target per wave) they are bit-identical.  With 16-bit storage two
-    consecutive targets share a wave and the chunks of their merged list, so the
-    order changes the fp32 summation order, which can move the fp16-stored message
-    by one rounding step: every order is deterministic and the orders agree to
-    5e-3 of the output RMS (measured 1e-3 over 6.9 M values; a wrong pairing would
-    differ by O(1))."""
+    """Targets are independent: any processing order (natural, slabs along x, a
+    random permutation, the Hilbert order) gives the same outputs.  With fp32
+    storage (one target per wave) they are bit-identical.  With 16-bit storage
+    four consecutive targets share a wave and the groups of the
+    union of their lists, so the order changes the fp32 summation order, which can
+    move the fp16-stored message by one rounding step: every order is deterministic
+    and the orders agree to 5e-3 of the output RMS (measured 1e-3 over 6.9 M values;
+    a wrong pairing would differ by O(1))."""
     base = W.make_workload("c4", n=6000)
     cfg = W.LayerConfig(**{**base.cfg.__dict__, "storage": storage})
     wl = W.make_workload(cfg)
@@ -265,15 +289,19 @@ def test_target_order_does_not_change_results(gpu_lib, storage):
     assert np.array_equal(np.sort(order.cpu().numpy()), np.arange(c.n))
     desc = _desc(gpu_lib, wl, d["dtype"])
     perm = torch.from_numpy(np.random.default_rng(3).permutation(c.n).astype(np.int32)).cuda()
+    hil = gpu_lib.e2v2_target_order(d["pos"])
+    assert torch.equal(hil, order)               # the builder emits the same Hilbert order
+    order = torch.from_numpy(np.lexsort((np.arange(c.n), np.floor(wl.pos[:, 0] / 3.0))).astype(np.int32)).cuda()
     run = lambda o: gpu_lib.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], s, ln, ix, target_order=o).cpu()
-    outs = [run(o) for o in (None, order, perm)]
-    again = [run(o) for o in (None, order, perm)]
+    orders = (None, order, perm, hil)
+    outs = [run(o) for o in orders]
+    again = [run(o) for o in orders]
     assert all(torch.equal(a, b) for a, b in zip(outs, again))
-    if storage == "fp32":
-        assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
-    else:
-        assert rel_err(outs[1].numpy(), outs[0].numpy()) < 5e-3
-        assert rel_err(outs[2].numpy(), outs[0].numpy()) < 5e-3
+    for o in outs[1:]:
+        if storage == "fp32":
+            assert torch.equal(outs[0], o)
+        else:
+            assert rel_err(o.numpy(), outs[0].numpy()) < 5e-3
 
 
 def _sampled_check(gpu_lib, wl, rows, nsample, seed):

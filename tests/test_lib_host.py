@@ -155,6 +155,21 @@ def test_neighbor_argument_errors(lib):
     assert call(n=0) == B.E2V2_OK and nnz.value == 0
 
 
+def test_target_order_argument_errors(lib):
+    ws = lib.e2v2_target_order_workspace_bytes(1000)
+    assert ws >= 3 * 4 * 1000 and lib.e2v2_target_order_workspace_bytes(2000) > ws
+    assert lib.e2v2_target_order_workspace_bytes(-1) == 0
+    call = lambda n=1000, pos=FAKE, order=FAKE, w=FAKE, wsb=ws: lib.e2v2_target_order(pos, n, order, w, wsb, None)
+    assert call(n=-1) == B.E2V2_ERR_ARG
+    assert call(n=2 ** 31 - 1) == B.E2V2_ERR_ARG
+    assert call(pos=None) == B.E2V2_ERR_ARG
+    assert call(order=None) == B.E2V2_ERR_ARG
+    assert call(w=None) == B.E2V2_ERR_ARG
+    assert call(pos=ctypes.c_void_p(0x10002)) == B.E2V2_ERR_ARG
+    assert call(wsb=ws - 1) == B.E2V2_ERR_ARG
+    assert call(n=0, pos=None, order=None, w=None, wsb=0) == B.E2V2_OK
+
+
 def test_eaas_argument_errors(lib):
     f = lambda L=2, C=128, dt=0, n=10, ptr=FAKE: lib.e2v2_eaas_couple(ptr, ptr, dt, ptr, n, L, C, ptr, 0, None)
     assert f(L=4) == B.E2V2_ERR_ARG
