@@ -291,6 +291,48 @@ constexpr CTerms<L> couple_terms()
     return r;
 }
 
+// The re-index terms' products w[p_q][c] * c[p_q][cc_q] of one channel c, in term
+// order (couple_terms), staged by a workgroup of NW waves: wave w takes terms
+// w, w + NW, ..., its lanes channels lane, lane + 64, ..., at dst[c * stride + q].
+// w: [paths][C] fp32.  All loads are issued before the first LDS write.
+template <int L>
+__constant__ CTerms<L> kCoupleTerms = couple_terms<L>();
+template <int L, int C, int NW>
+__device__ __forceinline__ void stage_coupling(const float *__restrict__ w, const EaasCoef &tab, float *dst,
+                                               int stride, int wave, int lane)
+{
+    constexpr int TN = couple_terms<L>().n;
+    constexpr int JM = (TN + NW - 1) / NW > 0 ? (TN + NW - 1) / NW : 1;
+    constexpr int PC = (C + 63) / 64;
+    float x[JM][PC];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        const int q = wave + NW * j;
+        if (q < TN) {
+            const CTerm tq = kCoupleTerms<L>.t[q];
+            const float cq = tab.c[tq.p][tq.cc];
+#pragma unroll
+            for (int k = 0; k < PC; ++k) {
+                const int c = lane + 64 * k;
+                x[j][k] = c < C ? w[tq.p * C + c] * cq : 0.f;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        const int q = wave + NW * j;
+        if (q < TN) {
+#pragma unroll
+            for (int k = 0; k < PC; ++k) {
+                const int c = lane + 64 * k;
+                if (c < C) dst[c * stride + q] = x[j][k];
+            }
+        }
+    }
+}
+template <int L>
+constexpr int coupling_terms() { return couple_terms<L>().n; }
+
 // EAAS on NI channels of one node held in registers, v[e][i] (component e,
 // channel i), in place: rotate into the aligned frame (D^T x), the sparse m
 // re-index with the path weights, rotate back (D y).  Dn: the node's D^1..D^L
@@ -334,6 +376,74 @@ __device__ __forceinline__ void eaas_multi(Arr &v, const float *Dn, const float 
             const float wp = T.t[q].lf > 0 ? w[T.t[q].p] * fdir : w[T.t[q].p];
             loc[T.t[q].out] = fmaf(wp * tab.c[T.t[q].p][T.t[q].cc], v[T.t[q].in][i], loc[T.t[q].out]);
         }
+#pragma unroll
+        for (int e = 0; e < NC; ++e) v[e][i] = loc[e];
+    }
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        const int k = 2 * l + 1, o = l * l;
+        float Dl[KM * KM];
+#pragma unroll
+        for (int r = 0; r < k * k; ++r) Dl[r] = Dn[dmat_offset(l) + r];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float tmp[KM];
+#pragma unroll
+            for (int a = 0; a < k; ++a) {
+                float s2 = 0.f;
+#pragma unroll
+                for (int b = 0; b < k; ++b) s2 = fmaf(Dl[a * k + b], v[o + b][i], s2);
+                tmp[a] = s2;
+            }
+#pragma unroll
+            for (int a = 0; a < k; ++a) v[o + a][i] = tmp[a];
+        }
+    }
+}
+
+// The same with the re-index terms' products staged beforehand (stage_coupling):
+// channel i's products at wc0 + i * wstride, one FMA per term; fdir = 0 drops
+// the l_f > 0 paths (node at the origin): those terms are summed first and the
+// partial sums scaled by fdir.
+template <int L, int NI, typename Arr>
+__device__ __forceinline__ void eaas_multi_pre(Arr &v, const float *Dn, const float *wc0, int wstride, float fdir)
+{
+    constexpr int NC = n_comp(L), KM = 2 * L + 1;
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+        const int k = 2 * l + 1, o = l * l;
+        float Dl[KM * KM];
+#pragma unroll
+        for (int r = 0; r < k * k; ++r) Dl[r] = Dn[dmat_offset(l) + r];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float tmp[KM];
+#pragma unroll
+            for (int b = 0; b < k; ++b) {
+                float s2 = 0.f;
+#pragma unroll
+                for (int a = 0; a < k; ++a) s2 = fmaf(Dl[a * k + b], v[o + a][i], s2);
+                tmp[b] = s2;
+            }
+#pragma unroll
+            for (int b = 0; b < k; ++b) v[o + b][i] = tmp[b];
+        }
+    }
+    constexpr CTerms<L> T = couple_terms<L>();
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const float *w = wc0 + i * wstride;
+        float loc[NC];
+#pragma unroll
+        for (int e = 0; e < NC; ++e) loc[e] = 0.f;
+#pragma unroll
+        for (int q = 0; q < T.n; ++q)
+            if (T.t[q].lf > 0) loc[T.t[q].out] = fmaf(w[q], v[T.t[q].in][i], loc[T.t[q].out]);
+#pragma unroll
+        for (int e = 0; e < NC; ++e) loc[e] *= fdir;
+#pragma unroll
+        for (int q = 0; q < T.n; ++q)
+            if (T.t[q].lf == 0) loc[T.t[q].out] = fmaf(w[q], v[T.t[q].in][i], loc[T.t[q].out]);
 #pragma unroll
         for (int e = 0; e < NC; ++e) v[e][i] = loc[e];
     }

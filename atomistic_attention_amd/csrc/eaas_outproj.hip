@@ -7,7 +7,8 @@
 // channels (one for C = 32): each thread couples 2 channels of one node in
 // registers (the node's
 // Wigner-D blocks and the path weights staged in LDS), splits hhat into bf16
-// hi + lo and writes them to LDS; wave nb then accumulates output channels
+// hi + lo (hi the truncated top half of each fp32 value, lo the exact remainder
+// rounded to bf16) and writes them to LDS; wave nb then accumulates output channels
 // 16 nb .. 16 nb + 15 of every component on v_mfma_f32_16x16x32_bf16 (A = packed
 // W_O^T fragment, B = the 16 nodes' hhat rows), hi and lo as two products.  The
 // coupling is per channel, so each half of the input channels is complete on
@@ -24,16 +25,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 template <int L, int C>
 __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 4 : 1))) void eaas_outproj_kernel(const EaasOutArgs a, const EaasCoef tab)
 {
-    constexpr int NC = n_comp(L), KB = C / 32, P = path_count(L);
+    constexpr int NC = n_comp(L), KB = C / 32;
     constexpr int NDM = n_dmat(L);
     constexpr int ND = NDM > 0 ? NDM : 1;
     constexpr int NH = C >= 64 ? 2 : 1;           // input-channel halves (one for C = 32)
     constexpr int CH = C / NH;                    // input channels per half
     constexpr int KBH = KB / NH;                  // 32-channel contraction blocks per half
     constexpr int ROW = NC * CH * 2 + 16;         // LDS bytes per node row of one half (pad spreads banks)
-    constexpr int WS = (P & 1) ? P : P + 1;       // LDS stride of one channel's path weights (odd)
+    constexpr int TQ = coupling_terms<L>();
+    constexpr int WS = (TQ & 1) ? TQ : TQ + 1;    // LDS stride of one channel's re-index products (odd)
     constexpr int NT = 4 * C;
-    constexpr int PW = (P * C + NT - 1) / NT;
     constexpr int PD = (16 * ND + NT - 1) / NT;
     constexpr int IPT = 16 * (CH / 2) / NT;       // (node, channel pair) items per thread and half
     __shared__ __align__(16) unsigned char sHi[16 * ROW];
@@ -46,15 +47,26 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
     const long long node0 = (long long)blockIdx.x * 16;
     const int nvalid = (a.n - node0) < 16 ? (int)(a.n - node0) : 16;
 
-    // Stage the D blocks, the path weights and the direction flags.
+    // The message's fp16 pairs of the first half are requested before the staging
+    // of the D blocks, the re-index products and the direction flags, so their
+    // latency runs under it.  Item t + r NT covers channels 2 cp, 2 cp + 1 of a
+    // half, node en.
+    uint32_t mraw[NH][IPT][NC];
+    auto request = [&](int half) {
 #pragma unroll
-    for (int r = 0; r < PW; ++r) {
-        const int u = t + r * NT;
-        if (u < P * C) {
-            const int p = u / C, c = u - p * C;
-            sW[c * WS + p] = a.w_tgt[u];
+        for (int r = 0; r < IPT; ++r) {
+            const int item = t + r * NT;
+            const int en = item / (CH / 2), cp = item - en * (CH / 2);
+            const long long enode = node0 + en;
+            const int c0 = half * CH + 2 * cp;
+#pragma unroll
+            for (int e = 0; e < NC; ++e)
+                mraw[half][r][e] = en < nvalid ? *reinterpret_cast<const uint32_t *>(a.m + (enode * NC + e) * C + c0)
+                                               : 0u;
         }
-    }
+    };
+    request(0);
+    stage_coupling<L, C, NT / 64>(a.w_tgt, tab, sW, WS, t >> 6, lane);
 #pragma unroll
     for (int r = 0; r < PD; ++r) {
         const int u = t + r * NT;
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
 
     // Couple every half first (the last half stays in registers), then run one
     // contraction pass per half, so the accumulators are never live during the
-    // coupling.  Item t + r NT covers channels 2 cp, 2 cp + 1 of a half, node en.
+    // coupling.
     auto couple = [&](int half, int r, float (&v)[NC][2]) {
         const int item = t + r * NT;
         const int en = item / (CH / 2), cp = item - en * (CH / 2);
@@ -89,28 +101,35 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
         const float sc = en < nvalid ? a.msc[enode] : 0.f;
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
-            uint32_t x = 0u;
-            if (en < nvalid) x = *reinterpret_cast<const uint32_t *>(a.m + (enode * NC + e) * C + c0);
+            const uint32_t x = mraw[half][r][e];
             v[e][0] = (float)__builtin_bit_cast(_Float16, uint16_t(x & 0xffffu)) * sc;
             v[e][1] = (float)__builtin_bit_cast(_Float16, uint16_t(x >> 16)) * sc;
         }
-        eaas_multi<L, 2>(v, sD + en * ND, &sW[c0 * WS], WS, tab, sDir[en]);
+        eaas_multi_pre<L, 2>(v, sD + en * ND, &sW[c0 * WS], WS, sDir[en]);
         if (a.hhat_tap && en < nvalid) {
 #pragma unroll
             for (int e = 0; e < NC; ++e)
                 *reinterpret_cast<float2 *>(a.hhat_tap + (enode * NC + e) * C + c0) = make_float2(v[e][0], v[e][1]);
         }
     };
+    // hhat = hi + lo in bf16: hi its top 16 bits (truncated), lo the exact
+    // remainder rounded to nearest even (|hi + lo - hhat| <= 2^-16 |hhat|); a NaN
+    // or inf in hhat stays non-finite in hi.  Two values per v_perm_b32.
+    auto rne_hi = [](float x) {                   // finite x: bits whose top half is bf16(x)
+        const uint32_t u = __float_as_uint(x);
+        return u + 0x7fffu + ((u >> 16) & 1u);
+    };
     auto stage = [&](int r, const float (&v)[NC][2]) {
         const int item = t + r * NT;
         const int en = item / (CH / 2), cp = item - en * (CH / 2);
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
-            const uint16_t h0 = f_to_bf16(v[e][0]), h1 = f_to_bf16(v[e][1]);
-            const uint16_t l0 = f_to_bf16(v[e][0] - bf16_to_f(h0)), l1 = f_to_bf16(v[e][1] - bf16_to_f(h1));
+            const uint32_t x0 = __float_as_uint(v[e][0]), x1 = __float_as_uint(v[e][1]);
+            const float r0 = v[e][0] - __uint_as_float(x0 & 0xffff0000u);
+            const float r1 = v[e][1] - __uint_as_float(x1 & 0xffff0000u);
             const int off = en * ROW + (e * CH + 2 * cp) * 2;
-            *reinterpret_cast<uint32_t *>(sHi + off) = h0 | (uint32_t(h1) << 16);
-            *reinterpret_cast<uint32_t *>(sLo + off) = l0 | (uint32_t(l1) << 16);
+            *reinterpret_cast<uint32_t *>(sHi + off) = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+            *reinterpret_cast<uint32_t *>(sLo + off) = __builtin_amdgcn_perm(rne_hi(r1), rne_hi(r0), 0x07060302u);
         }
     };
     auto contract = [&](int half) {
@@ -142,6 +161,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
         stage(r, v);
     }
     if constexpr (NH > 1) {
+        request(1);
 #pragma unroll
         for (int r = 0; r < IPT; ++r) couple(1, r, vlast[r]);
     }
