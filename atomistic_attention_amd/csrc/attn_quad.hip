@@ -320,10 +320,11 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
             kb.pj = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(A.pos4) + uint32_t(rk) * 16u);
     };
 
-    // Logits and softmax weights of one group as fp16 pairs.
-    auto weights = [&](QuadKeys &kb, const int (&cd)[4], const int (&cn)[4], bool first, half4_t &bh, half4_t &bl) {
+    // Masked scores (logit + bias + log2 s_r, base 2) of one group and its rows'
+    // log2 scales; requests the next group's keys once this group's are read.
+    auto scores = [&](QuadKeys &kb, const int (&cd)[4], const int (&cn)[4], bool first, float (&sc)[4],
+                      int (&lsi)[4]) {
         // log2 of the four rows' scales (lanes 0..3 loaded rows 0..3), exact integers
-        int lsi[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) lsi[r] = (int)((__builtin_amdgcn_readlane(__float_as_uint(kb.pj.w), r) >> 23) & 255u) - 127;
         if (first) zeta = lsi[0];
@@ -376,7 +377,7 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
         }
         // lane (kq', pm') of the product holds pairs 4 kq' + i (target kq', entry i) of
         // head pm': move target t, head h to lane 4 h + t
-        float br[4], sc[4];
+        float br[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) br[r] = __int_as_float(__builtin_amdgcn_ds_bpermute(bsrc, __float_as_int(bias[r])));
         // entry r feeds the targets in bits 0..3 of its code: as a lane mask, the
@@ -387,7 +388,9 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
             const bool on = __builtin_amdgcn_inverse_ballot_w64((uint64_t(m32) << 32) | m32);
             sc[r] = on ? S[r] + br[r] + (float)lsi[r] : -INFINITY;
         }
-        // lazily raised running maximum, then this group's weights
+    };
+    // The lazily raised running maximum, then the group's weights as fp16 pairs.
+    auto finish = [&](const float (&sc)[4], const int (&lsi)[4], half4_t &bh, half4_t &bl) {
         const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         const bool grow = mx > mu + 8.f;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -460,7 +463,10 @@ __device__ __forceinline__ void quad_body(const AttnArgs &A, long long s0, const
     for (int g = 0; g < G; ++g) {
         codes(g + 1, c1);
         half4_t bh, bl;
-        weights(kb, c0, c1, g == 0, bh, bl);
+        float sc[4];
+        int lsi[4];
+        scores(kb, c0, c1, g == 0, sc, lsi);
+        finish(sc, lsi, bh, bl);
         sums(b, bh, bl);
         __builtin_amdgcn_sched_barrier(0);
         issue_v(b, c1);
