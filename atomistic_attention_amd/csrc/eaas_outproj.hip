@@ -7,8 +7,8 @@
 // channels (one for C = 32): each thread couples 2 channels of one node in
 // registers (the node's
 // Wigner-D blocks and the path weights staged in LDS), splits hhat into bf16
-// hi + lo (hi the truncated top half of each fp32 value, lo the exact remainder
-// rounded to bf16) and writes them to LDS; wave nb then accumulates output channels
+// hi + lo (both rounded to nearest even, lo from the exact remainder; two
+// values per v_perm_b32) and writes them to LDS; wave nb then accumulates output channels
 // 16 nb .. 16 nb + 15 of every component on v_mfma_f32_16x16x32_bf16 (A = packed
 // W_O^T fragment, B = the 16 nodes' hhat rows), hi and lo as two products.  The
 // coupling is per channel, so each half of the input channels is complete on
@@ -112,23 +112,27 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
                 *reinterpret_cast<float2 *>(a.hhat_tap + (enode * NC + e) * C + c0) = make_float2(v[e][0], v[e][1]);
         }
     };
-    // hhat = hi + lo in bf16: hi its top 16 bits (truncated), lo the exact
-    // remainder rounded to nearest even (|hi + lo - hhat| <= 2^-16 |hhat|); a NaN
-    // or inf in hhat stays non-finite in hi.  Two values per v_perm_b32.
+    // hhat = hi + lo in bf16, each rounded to nearest even: hi of the value, lo of
+    // the exact remainder (|hi + lo - hhat| <= 2^-17 |hhat|); a NaN in hhat stays
+    // a NaN in hi, an inf an inf.  Two values per v_perm_b32.
     auto rne_hi = [](float x) {                   // finite x: bits whose top half is bf16(x)
         const uint32_t u = __float_as_uint(x);
         return u + 0x7fffu + ((u >> 16) & 1u);
+    };
+    auto rne_hi_nan = [&](float x) {              // the same, NaN and inf kept
+        const uint32_t u = __float_as_uint(x);
+        return (u & 0x7f800000u) == 0x7f800000u ? (u | ((u & 0xffffu) ? 0x00400000u : 0u)) : rne_hi(x);
     };
     auto stage = [&](int r, const float (&v)[NC][2]) {
         const int item = t + r * NT;
         const int en = item / (CH / 2), cp = item - en * (CH / 2);
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
-            const uint32_t x0 = __float_as_uint(v[e][0]), x1 = __float_as_uint(v[e][1]);
-            const float r0 = v[e][0] - __uint_as_float(x0 & 0xffff0000u);
-            const float r1 = v[e][1] - __uint_as_float(x1 & 0xffff0000u);
+            const uint32_t h0 = rne_hi_nan(v[e][0]), h1 = rne_hi_nan(v[e][1]);
+            const float r0 = v[e][0] - __uint_as_float(h0 & 0xffff0000u);
+            const float r1 = v[e][1] - __uint_as_float(h1 & 0xffff0000u);
             const int off = en * ROW + (e * CH + 2 * cp) * 2;
-            *reinterpret_cast<uint32_t *>(sHi + off) = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+            *reinterpret_cast<uint32_t *>(sHi + off) = __builtin_amdgcn_perm(h1, h0, 0x07060302u);
             *reinterpret_cast<uint32_t *>(sLo + off) = __builtin_amdgcn_perm(rne_hi(r1), rne_hi(r0), 0x07060302u);
         }
     };

@@ -57,31 +57,25 @@ def test_layer_full_fp32(gpu_lib, name):
 
 
 def _benched_step(gpu_lib, wl, d, desc):
-    """bench.py's timed step: e2v2_attn_prepare on a second stream while the
-    neighbour builder writes the list and its cell order, then
-    e2v2_attn_aggregate over that list in that order."""
+    """bench.py's timed step, on one stream: the neighbour builder writes the list
+    and the Hilbert processing order, e2v2_attn_prepare runs the projections and
+    the source coupling, then e2v2_attn_aggregate streams that list in that order."""
     c = wl.cfg
     order = torch.empty(c.n, dtype=torch.int32, device="cuda")
     ws = torch.empty(gpu_lib.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device="cuda")
     out = torch.empty(wl.h.shape, dtype=torch.float32, device="cuda")
-    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
-    fork, join = torch.cuda.Event(), torch.cuda.Event()
-    fork.record(main)
-    side.wait_event(fork)
-    gpu_lib.e2v2_attn_prepare(desc, d["pos"], d["h"], d["weights"], ws, stream=side)
-    join.record(side)
     s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors, order_out=order)
-    main.wait_event(join)
-    gpu_lib.e2v2_attn_aggregate(desc, d["weights"], s, ln, ix, out, ws, stream=main, target_order=order)
+    gpu_lib.e2v2_attn_prepare(desc, d["pos"], d["h"], d["weights"], ws)
+    gpu_lib.e2v2_attn_aggregate(desc, d["weights"], s, ln, ix, out, ws, target_order=order)
     torch.cuda.synchronize()
     return out, order, (s, ln, ix)
 
 
 def _parity_targets(wl, order, seed):
     """Targets compared at full size: every row the cap cuts (the oracle's uncapped
-    count above K), atoms within the cutoff of a face of the bounding box, both
-    targets of a run of 256 consecutive wave pairs of the processing order and of
-    128 more pairs spread over it, and random atoms up to at least 1,024."""
+    count above K), atoms within the cutoff of a face of the bounding box, the four
+    targets of a run of 128 consecutive wave quads of the processing order and of
+    64 more quads spread over it, and random atoms up to at least 1,024."""
     c = wl.cfg
     rng = np.random.default_rng(seed)
     sel = []
@@ -93,11 +87,11 @@ def _parity_targets(wl, order, seed):
     lo, hi = wl.pos.min(axis=0), wl.pos.max(axis=0)
     face = np.nonzero(np.any((wl.pos - lo < c.cutoff) | (hi - wl.pos < c.cutoff), axis=1))[0]
     sel.append(rng.choice(face, min(256, face.size), replace=False))
-    npair = c.n // 2
-    w0 = int(rng.integers(0, npair - 256))
-    pairs = np.r_[np.arange(w0, w0 + 256), rng.choice(npair, 128, replace=False)]
-    sel.append(order[2 * pairs])
-    sel.append(order[2 * pairs + 1])
+    nquad = c.n // 4
+    w0 = int(rng.integers(0, nquad - 128))
+    quads = np.r_[np.arange(w0, w0 + 128), rng.choice(nquad, 64, replace=False)]
+    for k in range(4):
+        sel.append(order[4 * quads + k])
     tg = np.unique(np.concatenate(sel))
     if tg.size < 1024:
         rest = np.setdiff1d(np.arange(c.n), tg)
@@ -128,7 +122,7 @@ def _message_bound(wl, ref, m_ref):
 def test_layer_benched_sequence_bf16(gpu_lib, name):
     """Full-size parity of the call sequence bench.py times (E2Former-V2 explainer
     section 3.2: K = 256, padded neighbours masked): the split forward over the
-    builder's list in its cell order.  Its output is bit-identical to the one-call
+    builder's list in its Hilbert order.  Its output is bit-identical to the one-call
     forward with taps in the same order, whose intermediates are then checked step
     by step on >= 1,024 targets: q and v (fp32 from bf16 inputs) within 1e-5; h'
     element-wise at the bound of one fp16 store; m element-wise within the bound of
@@ -172,8 +166,9 @@ def test_layer_benched_sequence_bf16(gpu_lib, name):
 
 
 def test_benched_sequence_is_deterministic(gpu_lib):
-    """Two runs of bench.py's step on the 32,768-atom workload give the same cell
-    order and bit-identical outputs (no atomics decide any order or sum)."""
+    """Two runs of bench.py's step on the 32,768-atom workload give the same
+    processing order and bit-identical outputs (no atomics decide any order or
+    sum)."""
     wl = W.make_workload("c4")
     d = upload(wl)
     desc = _desc(gpu_lib, wl, d["dtype"])
