@@ -105,8 +105,8 @@ __device__ __forceinline__ int quad_union(const int32_t *__restrict__ idx, int n
         const int nx = k < E - 1 ? key[k + 1] : nxt0;
         bad |= desc ? key[k] < nx : key[k] > nx;
     }
-    if (__builtin_amdgcn_ballot_w64(bad) == 0) wave_bitonic_sort<E, 2 * S, true>(key, lane);
-    else wave_bitonic_sort<E, 2, true>(key, lane);
+    if (__builtin_amdgcn_ballot_w64(bad) == 0) wave_bitonic_sort<E, 2 * S>(key, lane);
+    else wave_bitonic_sort<E>(key, lane);
 #pragma unroll
     for (int k = 0; k < E; ++k) sk[lane * E + k] = key[k];
     quad_lds_sync();

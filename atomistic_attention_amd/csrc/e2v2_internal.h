@@ -533,23 +533,7 @@ __device__ __forceinline__ uint16_t f_to_bf16(float f)
 // same lane, farther ones in lane ^ (d / E), reached by one shuffle per key.
 // FIRST > 2 starts at the phase that merges runs of FIRST / 2: the keys must then
 // already form such runs, ascending where (x & FIRST / 2) == 0, else descending.
-// The value of lane (lane ^ LX): lane pairs inside a quad by DPP quad permutes,
-// inside 32-lane halves by ds_swizzle's bit-mask mode (no address register),
-// across halves by ds_bpermute.  Every lane of the wave must be active.
-template <int LX>
-__device__ __forceinline__ int lane_xor(int v)
-{
-    static_assert(LX >= 1 && LX <= 32 && (LX & (LX - 1)) == 0, "a power of two below 64");
-    if constexpr (LX == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
-    else if constexpr (LX == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
-    else if constexpr (LX < 32) return __builtin_amdgcn_ds_swizzle(v, (LX << 10) | 0x1F);   // xor_mask, and_mask 31
-    else return __shfl_xor(v, LX, 64);
-}
-
-// XL picks the lane exchange: lane_xor (fewer instructions, more registers held:
-// the streaming kernel's union) or ds_bpermute (the neighbour rows, whose kernel
-// lives on occupancy: lane_xor took it from 56 to 85 VGPRs and twice the time).
-template <int E, int FIRST = 2, bool XL = false>
+template <int E, int FIRST = 2>
 __device__ __forceinline__ void wave_bitonic_sort(int (&a)[E], int lane)
 {
     constexpr int N = 64 * E;
@@ -564,12 +548,7 @@ __device__ __forceinline__ void wave_bitonic_sort(int (&a)[E], int lane)
                 const bool keep_min = ((lane & lx) == 0) == asc;
 #pragma unroll
                 for (int k = 0; k < E; ++k) {
-                    int o;
-                    if constexpr (XL)
-                        o = lx == 1 ? lane_xor<1>(a[k]) : lx == 2 ? lane_xor<2>(a[k]) : lx == 4 ? lane_xor<4>(a[k])
-                          : lx == 8 ? lane_xor<8>(a[k]) : lx == 16 ? lane_xor<16>(a[k]) : lane_xor<32>(a[k]);
-                    else
-                        o = __shfl_xor(a[k], lx, 64);
+                    const int o = __shfl_xor(a[k], lx, 64);
                     a[k] = keep_min ? min(a[k], o) : max(a[k], o);
                 }
             } else {
@@ -588,7 +567,7 @@ __device__ __forceinline__ void wave_bitonic_sort(int (&a)[E], int lane)
 
 // Ascending sort of a bitonic sequence of 64 E keys (same register layout as
 // wave_bitonic_sort): the last merge phase of the network alone.
-template <int E, bool XL = false>
+template <int E>
 __device__ __forceinline__ void wave_bitonic_merge(int (&a)[E], int lane)
 {
     constexpr int N = 64 * E;
@@ -599,12 +578,7 @@ __device__ __forceinline__ void wave_bitonic_merge(int (&a)[E], int lane)
             const bool keep_min = (lane & lx) == 0;
 #pragma unroll
             for (int k = 0; k < E; ++k) {
-                int o;
-                if constexpr (XL)
-                    o = lx == 1 ? lane_xor<1>(a[k]) : lx == 2 ? lane_xor<2>(a[k]) : lx == 4 ? lane_xor<4>(a[k])
-                      : lx == 8 ? lane_xor<8>(a[k]) : lx == 16 ? lane_xor<16>(a[k]) : lane_xor<32>(a[k]);
-                else
-                    o = __shfl_xor(a[k], lx, 64);
+                const int o = __shfl_xor(a[k], lx, 64);
                 a[k] = keep_min ? min(a[k], o) : max(a[k], o);
             }
         } else {
