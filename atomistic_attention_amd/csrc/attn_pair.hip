@@ -17,8 +17,8 @@
 // (target, neighbour) costs 0.64 of the row loads of one target per wave.
 //
 // The union is built in LDS before the stream: the wave sorts the two lists'
-// entries (atom, list) in registers (one bitonic merge when both lists ascend, as
-// the neighbour builder writes them); an entry of the first list directly followed
+// entries (atom, list) in registers (one bitonic merge when both lists ascend, the
+// full sort otherwise); an entry of the first list directly followed
 // by the same atom from the second list becomes one entry for both targets, and
 // invalid indices (negative or >= n) drop out.  An atom listed twice in one list
 // stays two entries, so it counts twice, as in the per-target kernel.  Entries
@@ -54,9 +54,9 @@ __device__ __forceinline__ int entry_code(int j, bool fa, bool fb)
 // The union of the two lists, written to su[0 .. return value).  Keys are
 // (j << 1) | list; invalid entries sort last and are dropped.  The first list
 // fills positions [0, la) and the second, reversed, [64 E - lb, 64 E): when both
-// lists ascend (as the neighbour builder writes them) the keys already form a
-// bitonic sequence and the last merge phase of the network sorts them; any other
-// lists take the full sort.
+// lists ascend the keys already form a bitonic sequence and the last merge phase
+// of the network sorts them; any other lists (the neighbour builder writes its
+// rows in its scan order) take the full sort.
 template <int E>
 __device__ __forceinline__ int pair_union(const int32_t *__restrict__ idx, int n, int sa, int la, int sb, int lb,
                                           int *su, int lane)

@@ -41,8 +41,8 @@
 //
 // The union: the four lists go to the four 16-lane rows of the wave as keys
 // (j << 2) | list, rows 0 and 2 ascending and rows 1 and 3 descending; lists
-// written in ascending order (as the neighbour builder writes them) then need the
-// last two bitonic merge phases only, any other order the full sort.  Equal atoms
+// given in ascending order then need the last two bitonic merge phases only, any
+// other order (the neighbour builder's scan order) the full sort.  Equal atoms
 // fold into one entry (j << 4) | (bit mask of the lists holding it), compacted
 // into LDS in atom order.  A list longer than 256 entries, or an atom listed
 // twice in one list, sends the wave down the general path: the four lists

@@ -15,18 +15,20 @@
 //      read the same cells) visits the rows of cells that the cutoff sphere can
 //      reach, each row cut along x to the sphere's extent there (so the scan
 //      covers little more than the sphere), compacts the pairs that pass into
-//      LDS and orders the row by j with a register bitonic sort:
-//        K = 0: count -> scan -> fill, rows sorted by j;
-//        K > 0: the K nearest by (d2, j), sorted by j, padded with -1; rows with
-//               more than K candidates are cut by a second wave kernel that ranks
-//               them in LDS.
+//      LDS and writes them in the scan's order (rows of cells by z, then y; the
+//      cells of a row in index order; atoms ascending within a cell):
+//        K = 0: count -> scan -> fill;
+//        K > 0: padded with -1; a row with more than K candidates keeps the K
+//               nearest by (d2, j), in that order (a register bitonic sort of the
+//               (d2, j) keys).
 //      Rows with more candidates than the LDS buffer holds are finished by a
-//      per-thread kernel (a max-heap held in the row itself, then a heapsort).
+//      per-thread kernel (a max-heap held in the row itself, then a heapsort: those
+//      rows ascend by j).
 //   The reach of the sphere along each axis is widened by a margin that covers
 //   fp32 rounding in the cell index and the cell bounds, so the rows and cells
 //   visited are always a superset of the ones holding a neighbour.
-// Within-cell order depends on atomics, but rows are sets sorted by j and the
-// K-nearest choice uses a total order, so results are deterministic.
+// Atoms are ranked by index within a cell after the atomic scatter and the
+// K-nearest choice uses a total order, so rows and their order are deterministic.
 #include "curve.h"
 #include "e2v2_internal.h"
 
@@ -568,11 +570,11 @@ __global__ void k_fill_capped(int n, int K, float rc, double rc2, const float *_
 // contiguous range of the cell-sorted arrays; lane r resolves row r, and the
 // rows' ranges are flattened into one candidate index space (a candidate finds
 // its row by a binary search over the lanes' running totals).  Passing
-// candidates are compacted into LDS (ballot + prefix count).  Rows are then
-// sorted by j in registers; over-cap rows are cut to the K nearest by rank
-// counting (the rank of an element is the number of elements with a smaller
-// (d2, j) key, which is its final slot).  Rows longer than the LDS buffer are
-// marked and left to the per-thread kernels above.
+// candidates are compacted into LDS (ballot + prefix count) in the scan's order
+// and written out in it (no consumer needs rows sorted by j: the streaming
+// kernels sort what they merge); over-cap rows are cut to the K nearest by a
+// register bitonic sort of the (d2, j) keys.  Rows longer than the LDS buffer
+// are marked and left to the per-thread kernels above.
 constexpr int kWaveCap = 1024;                 // candidates a wave can hold in LDS
 constexpr int kWavesPerBlock = 4;
 
@@ -788,16 +790,6 @@ __device__ __forceinline__ void wave_keep_nearest(int32_t *cj, int cnt, int K, f
     else wave_keep_nearest_n<8>(cj, cnt, K, pi, pos, lane);
 }
 
-// Pads keys [cnt, cnt rounded up to 4) so that they rank after every real key.
-__device__ __forceinline__ void wave_pad_keys(int32_t *cj, double *cd, int cnt, int lane)
-{
-    const int e = cnt + lane;
-    if (lane < 4 && e < ((cnt + 3) & ~3)) {
-        cj[e] = INT_MAX;
-        if (cd) cd[e] = INFINITY;
-    }
-}
-
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_count_wave(int n, float rc, double rc2,
                                                                     const GridInfo *__restrict__ grid,
                                                                     const int32_t *__restrict__ cell_start,
@@ -830,13 +822,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, fl
     if (nbr_len[i] > kWaveCap) return;
     const GridInfo gi = *grid;
     const int cnt = wave_scan<true>(i, spos[t], rc, rc2, gi, cell_start, spos, sj[w], lane);
-    wave_pad_keys(sj[w], nullptr, cnt, lane);
     wave_lds_sync();
-    wave_write_sorted(sj[w], cnt, nbr_idx + nbr_start[i], lane);
+    int32_t *row = nbr_idx + nbr_start[i];
+    for (int e = lane; e < cnt; e += 64) row[e] = sj[w][e];     // in the scan's order
 }
 
 // Capped rows: every candidate if there are at most K, else the K nearest by
-// (d2, j); written sorted by j and padded with -1.  Rows with more than
+// (d2, j), in that order; written in the scan's order and padded with -1.  Rows with more than
 // kSelectCap candidates over the cap, or more than kWaveCap in all, get
 // nbr_len = -1 and are finished by k_fill_capped.  Only the index buffer sits in
 // LDS, so many waves share a CU.
@@ -870,7 +862,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
         wave_keep_nearest(cj, cnt, K, pi, pos, lane);
         len = K;
     }
-    wave_write_sorted(cj, len, row, lane);
+    for (int e = lane; e < len; e += 64) row[e] = cj[e];         // in the scan's (or the cut's) order
     for (int sidx = len + lane; sidx < K; sidx += 64) row[sidx] = -1;
     if (lane == 0) nbr_len[i] = len;
 }

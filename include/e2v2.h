@@ -127,7 +127,11 @@ typedef struct {
  *                        nbr_len[i] are -1.  nbr_start[i] = i*K.  capacity must
  *                        be >= n*K.  Does not synchronise unless nnz_host is
  *                        non-NULL (then it waits and stores sum(nbr_len)).
- * Rows are sorted by j ascending.  Results are deterministic.
+ * A row lists its neighbours in the builder's scan order (the cell rows the
+ * cutoff sphere reaches, by z then y; the cells of a row in index order; atoms
+ * ascending within a cell), or, when more than K qualify, the K nearest in
+ * (d2, j) order; a row longer than 1,024 candidates comes by ascending j.  The
+ * rows and their order are deterministic (the same for the same positions).
  *   pos          device [n][3] fp32 (the positions' fp32 values are the truth)
  *   nbr_start    device [n] int32;  nbr_len device [n] int32
  *   nbr_idx      device [capacity] int32
@@ -305,7 +309,8 @@ e2v2_status e2v2_attn_aggregate(const e2v2_layer_desc *desc, const e2v2_weights 
  * every uncapped list of e2v2_build_neighbors and e2v2_filter_neighbors, whose
  * fp64 predicate is symmetric in i and j; not of capped lists in general).  The
  * results of the two modes on a symmetric list with rows sorted by index are
- * identical.  max_entries:
+ * identical (the builder's rows come in its scan order, so on them the two
+ * differ only by the order of summation).  max_entries:
  * an upper bound on the list's entries (the length of nbr_idx is one); entries
  * beyond it are dropped from the source side, so a smaller value gives a wrong
  * gradient (never an out-of-bounds access).
