@@ -12,7 +12,12 @@
 // 16 nb .. 16 nb + 15 of every component on v_mfma_f32_16x16x32_bf16 (A = packed
 // W_O^T fragment, B = the 16 nodes' hhat rows), hi and lo as two products.  The
 // coupling is per channel, so each half of the input channels is complete on
-// its own and the contraction is split at the half.
+// its own and the contraction is split at the half.  Each wave then turns its
+// 16-channel x 16-node tile of every component around in LDS, so that four
+// consecutive lanes store one node's 16 channels as 64 contiguous bytes (stored
+// straight from the accumulators, consecutive lanes would hit 16 different rows);
+// the fp32 output is written with non-temporal stores.  Measured at 32,768 atoms,
+// l_max = 2, C = 128: 87 -> 80 us (the layout 3 us, the store hint 4 us).
 #include "e2v2_internal.h"
 
 namespace e2v2 {
@@ -37,10 +42,13 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
     constexpr int NT = 4 * C;
     constexpr int PD = (16 * ND + NT - 1) / NT;
     constexpr int IPT = 16 * (CH / 2) / NT;       // (node, channel pair) items per thread and half
+    constexpr int TB = 20;                        // floats per node row of a wave's output tile (pad spreads banks)
+    constexpr int NWV = NT / 64;
+    constexpr int SWN = C * WS > NWV * 16 * TB ? C * WS : NWV * 16 * TB;
     __shared__ __align__(16) unsigned char sHi[16 * ROW];
     __shared__ __align__(16) unsigned char sLo[16 * ROW];
     __shared__ float sD[16 * ND];
-    __shared__ float sW[C * WS];
+    __shared__ __align__(16) float sW[SWN];       // re-index products; in the epilogue the output tiles
     __shared__ float sDir[16];
 
     const int t = threadIdx.x, lane = t & 63, nb = t >> 6, g = lane >> 4, nl = lane & 15;
@@ -178,19 +186,31 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
         __syncthreads();
         contract(1);
     }
-    if (nl < nvalid) {
-        const long long node = node0 + nl;
-        if (a.out_bf16) {                        // the next layer's bf16 input, rounded once
+    // Every wave has passed a barrier since the last read of the re-index
+    // products, so sW holds the waves' output tiles now: lane (g, nl) writes
+    // channels 4 g .. 4 g + 3 of node nl, lane (kn, kq) reads channels
+    // 4 kq .. 4 kq + 3 of node kn.  The tile is private to the wave.
+    float *tile = sW + nb * (16 * TB);
+    const int kn = lane >> 2, kq = lane & 3;
+    const long long onode = node0 + kn;
+    const size_t obase = (size_t)onode * NC * C + 16 * nb + 4 * kq;
 #pragma unroll
-            for (int e = 0; e < NC; ++e)
-                *reinterpret_cast<uint2 *>(a.out_bf16 + (node * NC + e) * C + 16 * nb + 4 * g) =
-                    make_uint2(uint32_t(f_to_bf16(acc[e][0])) | (uint32_t(f_to_bf16(acc[e][1])) << 16),
-                               uint32_t(f_to_bf16(acc[e][2])) | (uint32_t(f_to_bf16(acc[e][3])) << 16));
-        } else {
-#pragma unroll
-            for (int e = 0; e < NC; ++e)
-                *reinterpret_cast<float4 *>(a.out + (node * NC + e) * C + 16 * nb + 4 * g) =
-                    make_float4(acc[e][0], acc[e][1], acc[e][2], acc[e][3]);
+    for (int e = 0; e < NC; ++e) {
+        *reinterpret_cast<floatx4 *>(tile + nl * TB + 4 * g) = acc[e];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const floatx4 y = *reinterpret_cast<const floatx4 *>(tile + kn * TB + 4 * kq);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (kn < nvalid) {
+            if (a.out_bf16)                       // the next layer's bf16 input, rounded once
+                *reinterpret_cast<uint2 *>(a.out_bf16 + obase + (size_t)e * C) =
+                    make_uint2(uint32_t(f_to_bf16(y[0])) | (uint32_t(f_to_bf16(y[1])) << 16),
+                               uint32_t(f_to_bf16(y[2])) | (uint32_t(f_to_bf16(y[3])) << 16));
+            else                                  // streamed out: nothing in this layer reads it again
+                __builtin_nontemporal_store(y, reinterpret_cast<floatx4 *>(a.out + obase + (size_t)e * C));
         }
     }
 }
