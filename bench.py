@@ -589,12 +589,11 @@ def main():
         B.e2v2_attn_forward(desc, d["pos"], d["h"], d["weights"], start, length, idx, out=out, workspace=aws,
                             taps={"events": ev[1:]} if ev is not None else None, target_order=order)
 
-    # The same step with the projections and source coupling (which need no
-    # neighbour list) on a second stream while the list and the targets' Hilbert
-    # processing order are built; the streaming attention + output stage joins
-    # both.  The fork waits for the previous step, whose attention still reads the
-    # workspace and the order.  Measured beside the timed one-stream step: the
-    # source kernel slows the concurrent neighbour fill about as much as it saves.
+    # The timed step: the projections and source coupling (which need no neighbour
+    # list) on a second stream while the list and the targets' Hilbert processing
+    # order are built; the streaming attention + output stage joins both.  The fork
+    # waits for the previous step, whose attention still reads the workspace and
+    # the order.  The one-stream step in stage order is timed beside it.
     side = torch.cuda.Stream()
     fork, join = torch.cuda.Event(), torch.cuda.Event()
 
@@ -631,13 +630,12 @@ def main():
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps
 
-    # The timed step: stage order on one stream.
     for _ in range(args.warmup):
         step()
-    ms_step = timed(step, args.steps)
+    one_stream_ms = timed(step, args.steps)
     for _ in range(args.warmup):
         step_overlapped()
-    two_stream_ms = timed(step_overlapped, args.steps)
+    ms_step = timed(step_overlapped, args.steps)
 
     # Stage times (and the streaming kernel's launch time for the roofline) from
     # events at the stage boundaries of the same number of steps, outside the timed
@@ -691,9 +689,11 @@ def main():
             "steps_per_s": 1e3 / ms_step,
             "timing": "HIP events on the main stream around the whole loop of --steps steps",
             "stage_ms": stage_ms,
-            "two_stream_ms_per_step": two_stream_ms,
-            "two_stream": "projections + source coupling on a second stream during the neighbour build (which "
-                          "also emits the Hilbert target order); not the timed arrangement",
+            "arrangement": "projections + source coupling on a second stream during the neighbour build (which "
+                           "also emits the Hilbert target order); attention + target coupling + output projection "
+                           "after both",
+            "one_stream_ms_per_step": one_stream_ms,
+            "one_stream": "the same calls in stage order on one stream (stage_ms are taken on this arrangement)",
             "layer_ms_excl_neighbours": layer_ms,
             "layer_pairs_per_s_excl_neighbours": nnz / (layer_ms * 1e-3),
             "layer_steps_per_s_excl_neighbours": 1e3 / layer_ms,

@@ -57,15 +57,22 @@ def test_layer_full_fp32(gpu_lib, name):
 
 
 def _benched_step(gpu_lib, wl, d, desc):
-    """bench.py's timed step, on one stream: the neighbour builder writes the list
-    and the Hilbert processing order, e2v2_attn_prepare runs the projections and
-    the source coupling, then e2v2_attn_aggregate streams that list in that order."""
+    """bench.py's timed step: e2v2_attn_prepare runs the projections and the source
+    coupling on a second stream while the neighbour builder writes the list and the
+    Hilbert processing order on the main one; e2v2_attn_aggregate then streams that
+    list in that order after both."""
     c = wl.cfg
     order = torch.empty(c.n, dtype=torch.int32, device="cuda")
     ws = torch.empty(gpu_lib.attn_workspace_bytes(desc, c.n), dtype=torch.uint8, device="cuda")
     out = torch.empty(wl.h.shape, dtype=torch.float32, device="cuda")
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    fork.record(main)
+    side.wait_event(fork)
+    gpu_lib.e2v2_attn_prepare(desc, d["pos"], d["h"], d["weights"], ws, stream=side)
+    join.record(side)
     s, ln, ix, _ = gpu_lib.e2v2_build_neighbors(d["pos"], c.cutoff, c.max_neighbors, order_out=order)
-    gpu_lib.e2v2_attn_prepare(desc, d["pos"], d["h"], d["weights"], ws)
+    main.wait_event(join)
     gpu_lib.e2v2_attn_aggregate(desc, d["weights"], s, ln, ix, out, ws, target_order=order)
     torch.cuda.synchronize()
     return out, order, (s, ln, ix)
