@@ -12,12 +12,13 @@
 // 16 nb .. 16 nb + 15 of every component on v_mfma_f32_16x16x32_bf16 (A = packed
 // W_O^T fragment, B = the 16 nodes' hhat rows), hi and lo as two products.  The
 // coupling is per channel, so each half of the input channels is complete on
-// its own and the contraction is split at the half.  Each wave then turns its
-// 16-channel x 16-node tile of every component around in LDS, so that four
-// consecutive lanes store one node's 16 channels as 64 contiguous bytes (stored
-// straight from the accumulators, consecutive lanes would hit 16 different rows);
-// the fp32 output is written with non-temporal stores.  Measured at 32,768 atoms,
-// l_max = 2, C = 128: 87 -> 80 us (the layout 3 us, the store hint 4 us).
+// its own and the contraction is split at the half.  The accumulators then go
+// through LDS (the whole staging buffer, a few components at a time), so that
+// each wave stores whole node rows (stored straight from the accumulators,
+// consecutive lanes would hit 16 different rows); the fp32 output is written
+// with non-temporal stores.  Measured at 32,768 atoms, l_max = 2, C = 128:
+// 87 -> 78 us (rows of 64 bytes through a per-wave tile 3 us, the store hint
+// 4 us, whole rows through the block's buffer 2 us).
 #include "e2v2_internal.h"
 
 namespace e2v2 {
@@ -42,13 +43,13 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
     constexpr int NT = 4 * C;
     constexpr int PD = (16 * ND + NT - 1) / NT;
     constexpr int IPT = 16 * (CH / 2) / NT;       // (node, channel pair) items per thread and half
-    constexpr int TB = 20;                        // floats per node row of a wave's output tile (pad spreads banks)
-    constexpr int NWV = NT / 64;
-    constexpr int SWN = C * WS > NWV * 16 * TB ? C * WS : NWV * 16 * TB;
-    __shared__ __align__(16) unsigned char sHi[16 * ROW];
-    __shared__ __align__(16) unsigned char sLo[16 * ROW];
+    constexpr int OTR = C + 4, TILE = 16 * OTR;   // floats per node row / per component of an output tile
+    constexpr int SMB0 = 2 * 16 * ROW + C * WS * 4;
+    constexpr int SMB = SMB0 > 4 * TILE ? SMB0 : 4 * TILE;   // bytes: hi, lo and products; at least one tile
+    __shared__ __align__(16) unsigned char smem[SMB];
+    unsigned char *sHi = smem, *sLo = smem + 16 * ROW;
     __shared__ float sD[16 * ND];
-    __shared__ __align__(16) float sW[SWN];       // re-index products; in the epilogue the output tiles
+    float *sW = reinterpret_cast<float *>(smem + 2 * 16 * ROW);   // re-index products
     __shared__ float sDir[16];
 
     const int t = threadIdx.x, lane = t & 63, nb = t >> 6, g = lane >> 4, nl = lane & 15;
@@ -186,32 +187,34 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
         __syncthreads();
         contract(1);
     }
-    // Every wave has passed a barrier since the last read of the re-index
-    // products, so sW holds the waves' output tiles now: lane (g, nl) writes
-    // channels 4 g .. 4 g + 3 of node nl, lane (kn, kq) reads channels
-    // 4 kq .. 4 kq + 3 of node kn.  The tile is private to the wave.
-    float *tile = sW + nb * (16 * TB);
-    const int kn = lane >> 2, kq = lane & 3;
-    const long long onode = node0 + kn;
-    const size_t obase = (size_t)onode * NC * C + 16 * nb + 4 * kq;
+    // The whole buffer takes the output tiles, CPR components at a time: lane
+    // (g, nl) writes channels 16 nb + 4 g .. + 3 of node nl, then thread u stores
+    // channels 4 (u % (C / 4)) .. + 3 of node u / (C / 4), so a wave writes whole
+    // node rows.
+    constexpr int CPR = (SMB / 4) / TILE < NC ? (SMB / 4) / TILE : NC;
+    static_assert(CPR >= 1, "the buffer holds at least one component's tile");
+    float *ot = reinterpret_cast<float *>(smem);
 #pragma unroll
-    for (int e = 0; e < NC; ++e) {
-        *reinterpret_cast<floatx4 *>(tile + nl * TB + 4 * g) = acc[e];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const floatx4 y = *reinterpret_cast<const floatx4 *>(tile + kn * TB + 4 * kq);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (kn < nvalid) {
-            if (a.out_bf16)                       // the next layer's bf16 input, rounded once
-                *reinterpret_cast<uint2 *>(a.out_bf16 + obase + (size_t)e * C) =
-                    make_uint2(uint32_t(f_to_bf16(y[0])) | (uint32_t(f_to_bf16(y[1])) << 16),
-                               uint32_t(f_to_bf16(y[2])) | (uint32_t(f_to_bf16(y[3])) << 16));
-            else                                  // streamed out: nothing in this layer reads it again
-                __builtin_nontemporal_store(y, reinterpret_cast<floatx4 *>(a.out + obase + (size_t)e * C));
-        }
+    for (int e0 = 0; e0 < NC; e0 += CPR) {
+        __syncthreads();                          // the buffer (or the last round's tiles) is free
+#pragma unroll
+        for (int e = e0; e < (e0 + CPR < NC ? e0 + CPR : NC); ++e)
+            *reinterpret_cast<floatx4 *>(ot + (e - e0) * TILE + nl * OTR + 16 * nb + 4 * g) = acc[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = e0; e < (e0 + CPR < NC ? e0 + CPR : NC); ++e)
+            for (int u = t; u < 16 * (C / 4); u += NT) {
+                const int nd = u / (C / 4), q = u - nd * (C / 4);
+                if (nd >= nvalid) continue;
+                const floatx4 y = *reinterpret_cast<const floatx4 *>(ot + (e - e0) * TILE + nd * OTR + 4 * q);
+                const size_t o = ((size_t)(node0 + nd) * NC + e) * C + 4 * q;
+                if (a.out_bf16)
+                    *reinterpret_cast<uint2 *>(a.out_bf16 + o) =
+                        make_uint2(uint32_t(f_to_bf16(y[0])) | (uint32_t(f_to_bf16(y[1])) << 16),
+                                   uint32_t(f_to_bf16(y[2])) | (uint32_t(f_to_bf16(y[3])) << 16));
+                else
+                    __builtin_nontemporal_store(y, reinterpret_cast<floatx4 *>(a.out + o));
+            }
     }
 }
 
