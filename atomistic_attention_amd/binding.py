@@ -213,7 +213,8 @@ def e2v2_build_neighbors(pos: torch.Tensor, cutoff: float, max_neighbors: int = 
                          workspace: torch.Tensor | None = None, stream=None, want_nnz: bool = True,
                          order_out: torch.Tensor | None = None):
     """Neighbour list of pos [n, 3] fp32 (device).  Returns (start, len, idx, nnz).
-    order_out: optional int32 [n] device tensor receiving the cell-list order."""
+    order_out: optional int32 [n] device tensor receiving the targets' Hilbert-curve processing
+    order (the permutation e2v2_target_order returns)."""
     lib = load()
     _dev(pos, torch.float32, "pos")
     n = pos.shape[0]
