@@ -134,13 +134,15 @@ __device__ __forceinline__ int bucket_of(uint32_t key, int shift)
 }
 
 // Bucket offsets, slot cursors and the work list (bucket, run), by one workgroup
-// of 1024 threads.
+// of NTH threads.
+template <int NTH>
 __device__ inline void bucket_scan_block(const int32_t *__restrict__ cnt, int32_t *__restrict__ bstart,
                                          int32_t *__restrict__ cursor, int2 *__restrict__ items,
                                          int32_t *__restrict__ nitems)
 {
-    constexpr int PER = kBuckets / 1024;
-    __shared__ int sa[1024], sb[1024];
+    static_assert(kBuckets % NTH == 0, "whole buckets per thread");
+    constexpr int PER = kBuckets / NTH;
+    __shared__ int sa[NTH], sb[NTH];
     const int t = threadIdx.x;
     int c[PER], r[PER], ta = 0, tb = 0;
 #pragma unroll
@@ -153,7 +155,7 @@ __device__ inline void bucket_scan_block(const int32_t *__restrict__ cnt, int32_
     sa[t] = ta;
     sb[t] = tb;
     __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {          // inclusive scans of both totals
+    for (int d = 1; d < NTH; d <<= 1) {           // inclusive scans of both totals
         const int xa = t >= d ? sa[t - d] : 0, xb = t >= d ? sb[t - d] : 0;
         __syncthreads();
         sa[t] += xa;
@@ -170,7 +172,7 @@ __device__ inline void bucket_scan_block(const int32_t *__restrict__ cnt, int32_
         oa += c[u];
         ob += r[u];
     }
-    if (t == 1023) {
+    if (t == NTH - 1) {
         bstart[kBuckets] = oa;
         *nitems = ob;
     }

@@ -303,19 +303,21 @@ __global__ void k_cell_assign(const float *__restrict__ pos, int n, const GridIn
     }
 }
 
-// Exclusive scan of in[0..count) into out[0..count], out[count] = total; one block.
-// If total_out is non-null the total is also stored there as int64.  The input is
-// taken in tiles of 4096: each thread sums 4 consecutive entries, the wave scans
-// the sums with shuffles, the 16 wave totals meet in LDS, and a carry runs from
-// tile to tile; loads and stores stay coalesced.
+// Exclusive scan of in[0..count) into out[0..count], out[count] = total; one block
+// of NTH threads.  If total_out is non-null the total is also stored there as
+// int64.  The input is taken in tiles of 4 NTH: each thread sums 4 consecutive
+// entries, the wave scans the sums with shuffles, the wave totals meet in LDS, and
+// a carry runs from tile to tile; loads and stores stay coalesced.
+template <int NTH>
 __device__ inline void scan_block(const int32_t *__restrict__ in, const int *count_dev, int count_arg, int32_t *out,
                                   int32_t *copy, int64_t *total_out)
 {
-    __shared__ long long wsum[16];
+    constexpr int NW = NTH / 64;
+    __shared__ long long wsum[NW];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int count = count_dev ? *count_dev : count_arg;
     long long carry = 0;
-    for (long long base = 0; base < count; base += 4096) {
+    for (long long base = 0; base < count; base += 4 * NTH) {
         const long long e0 = base + 4 * t;
         int v[4];
 #pragma unroll
@@ -331,7 +333,7 @@ __device__ inline void scan_block(const int32_t *__restrict__ in, const int *cou
         __syncthreads();
         long long before = 0, tile = 0;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < NW; ++k) {
             const long long ws = wsum[k];
             before += k < w ? ws : 0;
             tile += ws;
@@ -357,18 +359,20 @@ __device__ inline void scan_block(const int32_t *__restrict__ in, const int *cou
 __global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ in, const int *count_dev, int count_arg,
                                                int32_t *out, int32_t *copy, int64_t *total_out)
 {
-    scan_block(in, count_dev, count_arg, out, copy, total_out);
+    scan_block<1024>(in, count_dev, count_arg, out, copy, total_out);
 }
 
 // The cell scan (block 0) and the processing order's bucket scan (block 1) in one
-// launch.
-__global__ __launch_bounds__(1024) void k_scan_cells_buckets(const int32_t *__restrict__ cell_cnt, const int *ncell,
+// launch, in blocks of 256 threads: they then fit on a CU beside the blocks of a
+// kernel running on another stream (the projections, in the two-stream step).
+constexpr int kScanThreads = 256;
+__global__ __launch_bounds__(kScanThreads) void k_scan_cells_buckets(const int32_t *__restrict__ cell_cnt, const int *ncell,
                                                              int32_t *cell_start, int32_t *cell_cur,
                                                              const int32_t *__restrict__ bcnt, int32_t *bstart,
                                                              int32_t *bcursor, int2 *items, int32_t *nitems)
 {
-    if (blockIdx.x == 0) scan_block(cell_cnt, ncell, 0, cell_start, cell_cur, nullptr);
-    else curve::bucket_scan_block(bcnt, bstart, bcursor, items, nitems);
+    if (blockIdx.x == 0) scan_block<kScanThreads>(cell_cnt, ncell, 0, cell_start, cell_cur, nullptr);
+    else curve::bucket_scan_block<kScanThreads>(bcnt, bstart, bcursor, items, nitems);
 }
 
 // ---------------------------------------------------------------- step 3
@@ -1046,7 +1050,7 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
     k_bbox<<<1, 256, 0, stream>>>(L.box_part, nparts, cutoff, maxc, L.grid, n, ci);
     k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt, ci, L.key, L.bcnt);
     if (ord)
-        k_scan_cells_buckets<<<2, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, L.cell_start, L.cell_cur, L.bcnt,
+        k_scan_cells_buckets<<<2, kScanThreads, 0, stream>>>(L.cell_cnt, &L.grid->ncell, L.cell_start, L.cell_cur, L.bcnt,
                                                      L.bstart, L.bcursor, L.items, L.nitems);
     else
         k_scan<<<1, 1024, 0, stream>>>(L.cell_cnt, &L.grid->ncell, 0, L.cell_start, L.cell_cur, nullptr);

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(1024) void k_order_scan(const int32_t *__restrict__
                                                      int32_t *__restrict__ cursor, int2 *__restrict__ items,
                                                      int32_t *__restrict__ nitems)
 {
-    bucket_scan_block(cnt, bstart, cursor, items, nitems);
+    bucket_scan_block<1024>(cnt, bstart, cursor, items, nitems);
 }
 
 // (4) Each atom takes a slot in its bucket.
