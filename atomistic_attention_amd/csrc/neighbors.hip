@@ -21,9 +21,9 @@
 //        K > 0: padded with -1; a row with more than K candidates keeps the K
 //               nearest by (d2, j), in that order (a register bitonic sort of the
 //               (d2, j) keys).
-//      Rows with more candidates than the LDS buffer holds are finished by a
-//      per-thread kernel (a max-heap held in the row itself, then a heapsort: those
-//      rows ascend by j).
+//      Rows with more candidates than the LDS buffer holds are filled by lane 0
+//      of their wave alone (a max-heap held in the row itself, then a heapsort:
+//      those rows ascend by j).
 //   The reach of the sphere along each axis is widened by a margin that covers
 //   fp32 rounding in the cell index and the cell bounds, so the rows and cells
 //   visited are always a superset of the ones holding a neighbour.
@@ -489,18 +489,13 @@ __device__ inline void heapsort_int(int32_t *a, int len)
     }
 }
 
-// Per-thread fills for rows longer than the wave kernels' LDS buffer (kWaveCap).
-__global__ void k_fill_csr(int n, int cap, float rc, double rc2, const GridInfo *__restrict__ grid,
-                           const int32_t *__restrict__ cell_start, const int32_t *__restrict__ order,
-                           const float4 *__restrict__ spos, const int32_t *__restrict__ nbr_start,
-                           const int32_t *__restrict__ nbr_len, int32_t *nbr_idx)
+// One thread's fill of a row longer than the wave kernels' LDS buffer (kWaveCap),
+// run by lane 0 of the row's wave.
+__device__ __forceinline__ void fill_csr_row(int i, float4 pi, float rc, double rc2, const GridInfo &gi,
+                                             const int32_t *__restrict__ cell_start,
+                                             const float4 *__restrict__ spos,
+                                             const int32_t *__restrict__ nbr_start, int32_t *nbr_idx)
 {
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= n) return;
-    const int i = order[t];
-    if (nbr_len[i] <= cap) return;
-    const GridInfo gi = *grid;
-    const float4 pi = spos[t];
     int32_t *row = nbr_idx + nbr_start[i];
     int cnt = 0;
     for_each_neighbor(i, pi, rc, rc2, gi, cell_start, spos, [&](int j, double) { row[cnt++] = j; });
@@ -513,17 +508,14 @@ __device__ __forceinline__ bool key_less(double da, int ja, double db, int jb)
     return da < db || (da == db && ja < jb);
 }
 
-__global__ void k_fill_capped(int n, int K, float rc, double rc2, const float *__restrict__ pos,
-                              const GridInfo *__restrict__ grid,
-                              const int32_t *__restrict__ cell_start, const int32_t *__restrict__ order,
-                              const float4 *__restrict__ spos, int32_t *nbr_start, int32_t *nbr_len, int32_t *nbr_idx)
+// One thread's fill of a capped row the wave kernel cannot hold or rank, run by
+// lane 0 of the row's wave: a max-heap of the K nearest held in the row itself.
+__device__ __forceinline__ void fill_capped_row(int i, float4 pi, int K, float rc, double rc2,
+                                                const float *__restrict__ pos, const GridInfo &gi,
+                                                const int32_t *__restrict__ cell_start,
+                                                const float4 *__restrict__ spos, int32_t *nbr_start,
+                                                int32_t *nbr_len, int32_t *nbr_idx)
 {
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= n) return;
-    const int i = order[t];
-    if (nbr_len[i] != -1) return;                 // done by k_fill_capped_wave
-    const GridInfo gi = *grid;
-    const float4 pi = spos[t];
     const double xi = pi.x, yi = pi.y, zi = pi.z;
     int32_t *row = nbr_idx + (size_t)i * K;
     // max-heap on (d2, j): row[0] is the farthest kept neighbour
@@ -578,7 +570,7 @@ __global__ void k_fill_capped(int n, int K, float rc, double rc2, const float *_
 // and written out in it (no consumer needs rows sorted by j: the streaming
 // kernels sort what they merge); over-cap rows are cut to the K nearest by a
 // register bitonic sort of the (d2, j) keys.  Rows longer than the LDS buffer
-// are marked and left to the per-thread kernels above.
+// are filled by lane 0 alone with the per-thread code above.
 constexpr int kWaveCap = 1024;                 // candidates a wave can hold in LDS
 constexpr int kWavesPerBlock = 4;
 
@@ -809,7 +801,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_count_wave(int n, float
     if (lane == 0) nbr_len[i] = cnt;
 }
 
-// CSR rows of at most kWaveCap entries (longer rows: k_fill_csr).
+// CSR rows; a row longer than kWaveCap entries is filled by lane 0 alone
+// (fill_csr_row).
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, float rc, double rc2,
                                                                        const GridInfo *__restrict__ grid,
                                                                        const int32_t *__restrict__ cell_start,
@@ -823,8 +816,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, fl
     const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerBlock + w));
     if (t >= n) return;
     const int i = order[t];
-    if (nbr_len[i] > kWaveCap) return;
     const GridInfo gi = *grid;
+    if (nbr_len[i] > kWaveCap) {
+        if (lane == 0) fill_csr_row(i, spos[t], rc, rc2, gi, cell_start, spos, nbr_start, nbr_idx);
+        return;
+    }
     const int cnt = wave_scan<true>(i, spos[t], rc, rc2, gi, cell_start, spos, sj[w], lane);
     wave_lds_sync();
     int32_t *row = nbr_idx + nbr_start[i];
@@ -833,8 +829,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_csr_wave(int n, fl
 
 // Capped rows: every candidate if there are at most K, else the K nearest by
 // (d2, j), in that order; written in the scan's order and padded with -1.  Rows with more than
-// kSelectCap candidates over the cap, or more than kWaveCap in all, get
-// nbr_len = -1 and are finished by k_fill_capped.  Only the index buffer sits in
+// kSelectCap candidates over the cap, or more than kWaveCap in all, are filled by
+// lane 0 alone (fill_capped_row).  Only the index buffer sits in
 // LDS, so many waves share a CU.
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n, int K, float rc, double rc2,
                                                                           const float *__restrict__ pos,
@@ -857,7 +853,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_fill_capped_wave(int n,
     int32_t *row = nbr_idx + (size_t)i * K;
     if (lane == 0) nbr_start[i] = (int32_t)((size_t)i * K);
     if (cnt > kWaveCap || (cnt > K && cnt > kSelectCap)) {
-        if (lane == 0) nbr_len[i] = -1;
+        if (lane == 0) fill_capped_row(i, pi, K, rc, rc2, pos, gi, cell_start, spos, nbr_start, nbr_len, nbr_idx);
         return;
     }
     wave_lds_sync();
@@ -1085,13 +1081,9 @@ hipError_t launch_neighbors_fill(const float *pos, int n, float cutoff, int K, v
     if (K == 0) {
         k_fill_csr_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(
             n, cutoff, rc2, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
-        k_fill_csr<<<nblk(n, 128), 128, 0, stream>>>(n, kWaveCap, cutoff, rc2, L.grid, L.cell_start, L.order, L.spos,
-                                                      nbr_start, nbr_len, nbr_idx);
     } else {
         k_fill_capped_wave<<<nblk(n, kWavesPerBlock), 64 * kWavesPerBlock, 0, stream>>>(
             n, K, cutoff, rc2, pos, L.grid, L.cell_start, L.order, L.spos, nbr_start, nbr_len, nbr_idx);
-        k_fill_capped<<<nblk(n, 128), 128, 0, stream>>>(n, K, cutoff, rc2, pos, L.grid, L.cell_start, L.order, L.spos,
-                                                         nbr_start, nbr_len, nbr_idx);
     }
     return hipGetLastError();
 }
