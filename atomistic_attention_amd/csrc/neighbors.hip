@@ -7,9 +7,10 @@
 // search with the same arithmetic.
 //
 // Steps (all on the caller's stream):
-//   1. one block reduces the bounding box and sizes a grid whose cells are about
-//      half the cutoff wide (at most n + 64 cells);
-//   2. cell index per atom + per-cell counts (integer atomics: counts are exact);
+//   1. partial bounding boxes;
+//   2. every block combines them and sizes a grid whose cells are about half the
+//      cutoff wide (at most n + 64 cells); cell index per atom + per-cell counts
+//      (integer atomics: counts are exact);
 //   3. exclusive scan of the counts; scatter atoms into cell order;
 //   4. one wave per target (targets taken in cell order, so neighbouring waves
 //      read the same cells) visits the rows of cells that the cutoff sphere can
@@ -104,8 +105,8 @@ int64_t *neighbors_nnz_slot(void *ws, int n) { return nbr_layout(ws, n).nnz; }
 
 // ---------------------------------------------------------------- step 1
 // Bounding box in two stages: kBoxBlocks blocks reduce strided slices into
-// partial (min, max) records (and clear the cell counters for step 2), one block
-// combines them and sizes the grid.
+// partial (min, max) records (and clear the cell counters for step 2); every block
+// of step 2 combines them and sizes the grid.
 constexpr int kBoxBlocks = 256;
 
 __global__ __launch_bounds__(256) void k_bbox_partial(const float *__restrict__ pos, int n, float *part, int maxc,
@@ -151,10 +152,11 @@ __global__ __launch_bounds__(256) void k_bbox_partial(const float *__restrict__ 
     }
 }
 
-// One block: the grid from the partial boxes and, when asked for, the cells of
-// the Hilbert processing order from the finite values' box.
-__global__ __launch_bounds__(256) void k_bbox(const float *__restrict__ part, int nparts, float cutoff, int maxc,
-                                              GridInfo *grid, int n, curve::CurveInfo *cinfo)
+// One block of 256 threads: the grid from the partial boxes and, when asked for,
+// the cells of the Hilbert processing order from the finite values' box (grid and
+// cinfo may point to LDS; every block that calls it does the same arithmetic).
+__device__ inline void grid_setup_block(const float *__restrict__ part, int nparts, float cutoff, int maxc,
+                                        GridInfo *grid, int n, curve::CurveInfo *cinfo)
 {
     __shared__ float sv[12][256];
     const int t = threadIdx.x;
@@ -279,15 +281,26 @@ __device__ __forceinline__ void row_cells(const GridInfo &gi, int z, int y, int 
 }
 
 // ---------------------------------------------------------------- step 2
-// Each atom's cell and, when the processing order is asked for, its Hilbert
-// index and bucket count.
-__global__ void k_cell_assign(const float *__restrict__ pos, int n, const GridInfo *__restrict__ grid,
-                              int32_t *cell_of, int32_t *cell_cnt, const curve::CurveInfo *__restrict__ cinfo,
-                              uint32_t *key, int32_t *bcnt)
+// Every block sizes the grid (and the curve's cells) from the partial boxes, block
+// 0 stores them for the later steps; then each atom's cell and, when the
+// processing order is asked for, its Hilbert index and bucket count.
+__global__ __launch_bounds__(256) void k_cell_assign(const float *__restrict__ pos, int n,
+                                                     const float *__restrict__ part, int nparts, float cutoff,
+                                                     int maxc, GridInfo *grid, int32_t *cell_of, int32_t *cell_cnt,
+                                                     curve::CurveInfo *cinfo_out, uint32_t *key, int32_t *bcnt)
 {
+    __shared__ GridInfo sg;
+    __shared__ curve::CurveInfo sc;
+    grid_setup_block(part, nparts, cutoff, maxc, &sg, n, cinfo_out ? &sc : nullptr);
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *grid = sg;
+        if (cinfo_out) *cinfo_out = sc;
+    }
+    const curve::CurveInfo *cinfo = cinfo_out ? &sc : nullptr;
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const GridInfo gi = *grid;
+    const GridInfo gi = sg;
     const float x = pos[3 * i + 0], y = pos[3 * i + 1], z = pos[3 * i + 2];
     const int cx = cell_coord(x, gi.lo[0], gi.inv[0], gi.dims[0]);
     const int cy = cell_coord(y, gi.lo[1], gi.inv[1], gi.dims[1]);
@@ -1043,8 +1056,8 @@ hipError_t launch_neighbors_count(const float *pos, int n, float cutoff, int K, 
     const bool ord = order_out != nullptr;
     curve::CurveInfo *ci = ord ? L.curve : nullptr;
     k_bbox_partial<<<nparts, 256, 0, stream>>>(pos, n, L.box_part, maxc, L.cell_cnt, ord ? L.bcnt : nullptr);
-    k_bbox<<<1, 256, 0, stream>>>(L.box_part, nparts, cutoff, maxc, L.grid, n, ci);
-    k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.grid, L.cell_of, L.cell_cnt, ci, L.key, L.bcnt);
+    k_cell_assign<<<nblk(n, 256), 256, 0, stream>>>(pos, n, L.box_part, nparts, cutoff, maxc, L.grid, L.cell_of,
+                                                    L.cell_cnt, ci, L.key, L.bcnt);
     if (ord)
         k_scan_cells_buckets<<<2, kScanThreads, 0, stream>>>(L.cell_cnt, &L.grid->ncell, L.cell_start, L.cell_cur, L.bcnt,
                                                      L.bstart, L.bcursor, L.items, L.nitems);
