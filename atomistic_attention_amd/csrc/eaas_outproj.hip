@@ -37,7 +37,9 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 
     constexpr int NH = C >= 64 ? 2 : 1;           // input-channel halves (one for C = 32)
     constexpr int CH = C / NH;                    // input channels per half
     constexpr int KBH = KB / NH;                  // 32-channel contraction blocks per half
-    constexpr int ROW = NC * CH * 2 + 16;         // LDS bytes per node row of one half (pad spreads banks)
+    constexpr int ROW = NC * CH * 2 + 32;         // LDS bytes per node row of one half (pad spreads banks:
+                                                  // 32 bytes measured 5.8 -> 1.0 M conflict cycles per launch
+                                                  // at l_max = 2, C = 128, against 16)
     constexpr int TQ = coupling_terms<L>();
     constexpr int WS = (TQ & 1) ? TQ : TQ + 1;    // LDS stride of one channel's re-index products (odd)
     constexpr int NT = 4 * C;
