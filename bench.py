@@ -51,8 +51,8 @@ PER_CONFIG = ("c1", "c2", "c3", "c3b", "c5")
 
 
 def algorithmic(cfg, nnz: int) -> dict:
-    """What the streaming step moves and computes by the method's own count, per the
-    survey's measurement section: per (target, neighbour) pair the neighbour's
+    """What the streaming step moves and computes by the method's own count: per
+    (target, neighbour) pair the neighbour's
     coupled value row h'_j in the storage dtype, its fp32 key row, its index and its
     position (n_c C s + 4 C + 16 bytes) and 2 (C + R H + n_c C) flops (logit, bias,
     accumulation); per target its fp32 query and fp32 message plus position and row
@@ -661,7 +661,7 @@ def main():
             stage_ms[name] = float(v)
             prev = name
     a = algorithmic(cfg, nnz)
-    # the whole layer (A2-A6) by the survey's per-unit count: the streaming bytes above
+    # the whole layer (A2-A6) by the same per-unit count: the streaming bytes above
     # plus the node kernels' (A3 reads h and writes h' in the storage dtype, A5 reads m
     # and writes hhat in fp32, A2/A6 read their inputs and write fp32 q, k and out)
     C, nc, sb = cfg.channels, cfg.n_comp, (2 if cfg.storage == "bf16" else 4)
